@@ -1,0 +1,245 @@
+"""Pins for the oracle's fp16 codec, block decoders and quantizers.
+
+Nothing here compares the oracle with itself.  The decoders are pinned by
+hand-worked blocks (tests/golden/, worked by hand from the GGUF layouts the
+oracle fixes; the ntransformer write-up, GeekNews topic 26894, "Overview",
+names the formats) and by the one number on the pages a layout can be checked
+against (about 670 MB per 70B Q6_K layer, "NVMe direct streaming").  The fp16
+codec is pinned by exhaustive round trips and by numpy's own IEEE conversion.
+The quantizers are pinned by round-trip error bounds derived from the input
+values alone.
+"""
+import glob
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from block_quantized_decode_dequant_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+TYPES = {"q8_0": O.Q8_0, "q4_0": O.Q4_0, "q4_k": O.Q4_K, "q6_k": O.Q6_K}
+
+
+def load_golden(path):
+    t, sets, expects = None, {}, []
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        parts = line.split()
+        if parts[0] == "type":
+            t = TYPES[parts[1]]
+        elif parts[0] == "set":
+            sets[int(parts[1])] = int(parts[2], 16)
+        elif parts[0] == "expect":
+            expects.append((int(parts[1]), float(parts[2])))
+    blk = np.zeros(O.block_bytes(t), np.uint8)
+    for off, v in sets.items():
+        blk[off] = v
+    return t, blk, expects
+
+
+GOLDEN_FILES = sorted(glob.glob(os.path.join(GOLDEN, "*.txt")))
+
+
+def test_golden_files_present():
+    names = {os.path.basename(p) for p in GOLDEN_FILES}
+    for need in ["q8_0_e1.txt", "q8_0_e2.txt", "q4_0_e3.txt", "q4_k_e4.txt", "q6_k_e5.txt"]:
+        assert need in names
+
+
+@pytest.mark.parametrize("path", GOLDEN_FILES, ids=os.path.basename)
+def test_hand_worked_blocks(path):
+    t, blk, expects = load_golden(path)
+    out = O.dequant(t, blk, O.block_elems(t))
+    assert expects
+    for idx, val in expects:
+        assert out[idx] == np.float32(val), (idx, out[idx], val)
+
+
+def test_block_sizes():
+    assert [O.block_elems(t) for t in (O.Q8_0, O.Q4_0, O.Q4_K, O.Q6_K)] == [32, 32, 256, 256]
+    assert [O.block_bytes(t) for t in (O.Q8_0, O.Q4_0, O.Q4_K, O.Q6_K)] == [34, 18, 144, 210]
+    assert O.row_bytes(O.Q4_K, 8192) == 32 * 144
+    assert O.row_bytes(O.Q4_K, 100) == -1
+    assert O.block_elems(99) == -1
+
+
+def test_q6_k_layer_size_matches_the_pages():
+    """NVMe direct streaming: about 670 MB per 70B Q6_K layer (read as MiB)."""
+    H, F, KV = 8192, 28672, 1024
+    shapes = [(H, H), (KV, H), (KV, H), (H, H), (F, H), (F, H), (H, F)]
+    params = sum(r * c for r, c in shapes)
+    assert params == 855_638_016
+    nbytes = sum(r * O.row_bytes(O.Q6_K, c) for r, c in shapes)
+    assert nbytes == 701_890_560
+    assert abs(nbytes / 2**20 - 670) < 1.0
+
+
+# ---- fp16 ------------------------------------------------------------------
+def test_f16_decode_known_values():
+    known = {0x3C00: 1.0, 0x7BFF: 65504.0, 0x0400: 2.0**-14, 0x0001: 2.0**-24, 0x03FF: 1023 * 2.0**-24,
+             0xC000: -2.0, 0x3555: 1365 / 4096, 0x0000: 0.0, 0x7C00: np.inf, 0xFC00: -np.inf}
+    for h, v in known.items():
+        assert O.f16_to_f64(h) == v, hex(h)
+    assert np.isnan(O.f16_to_f64(0x7E00))
+    assert np.signbit(O.f16_to_f64(0x8000))
+
+
+def test_f16_decode_matches_numpy_exhaustively():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    mine = np.array([O.f16_to_f64(int(b)) for b in bits])
+    finite = np.isfinite(ref)
+    assert np.array_equal(mine[finite], ref[finite])
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+
+
+def test_f16_rne_round_trip_and_ties():
+    for h in range(0, 0x7C00, 7):
+        assert O.f64_to_f16_rne(O.f16_to_f64(h)) == h
+        assert O.f64_to_f16_rne(-O.f16_to_f64(h)) == h | 0x8000
+    assert O.f64_to_f16_rne(1 + 2.0**-11) == 0x3C00          # tie -> even (1.0)
+    assert O.f64_to_f16_rne(1 + 3 * 2.0**-11) == 0x3C02      # tie -> even (1 + 2^-9)
+    assert O.f64_to_f16_rne(65519.99) == 0x7BFF
+    assert O.f64_to_f16_rne(65520.0) == 0x7C00                # tie past the top -> inf
+    assert O.f64_to_f16_rne(2.0**-25) == 0x0000               # tie between 0 and 2^-24
+    assert O.f64_to_f16_rne(3 * 2.0**-25) == 0x0002           # tie -> even (2 * 2^-24)
+    assert O.f64_to_f16_rne(1023.5 * 2.0**-24) == 0x0400      # rounds up into the normals
+
+
+def test_f16_rne_matches_numpy_on_random_doubles():
+    g = synth.rng(0, 900)
+    v = np.concatenate([g.standard_normal(4000) * s for s in (1e-6, 1e-4, 1e-2, 1, 100, 3e4)])
+    ref = v.astype(np.float16).view(np.uint16)
+    mine = np.array([O.f64_to_f16_rne(float(x)) for x in v], np.uint16)
+    assert np.array_equal(mine, ref)
+
+
+def test_f16_up_is_smallest_upper_bound():
+    g = synth.rng(0, 901)
+    v = np.abs(np.concatenate([g.standard_normal(3000) * s for s in (1e-7, 1e-4, 1e-1, 10, 1e4)]))
+    for x in v:
+        h = O.f64_to_f16_up(float(x))
+        assert O.f16_to_f64(h) >= x
+        if h > 0:
+            assert O.f16_to_f64(h - 1) < x
+    assert O.f64_to_f16_up(1.0) == 0x3C00
+    assert O.f64_to_f16_up(0.0) == 0
+
+
+# ---- quantizers: round-trip bounds from the input values alone ---------------
+U10, U11, Q16 = 2.0**-10, 2.0**-11, 2.0**-24
+
+
+def _bound_q8_0(x):
+    a = np.abs(x).max(axis=1, keepdims=True)
+    d_hi = a / 127 * (1 + U11) + Q16 / 2
+    return d_hi / 2 + a * U11 + 0 * x
+
+
+def _bound_q4_0(x):
+    a = np.abs(x).max(axis=1, keepdims=True)
+    d_hi = a / 7 * (1 + U11) + Q16 / 2
+    return d_hi / 2 + a * U11 + 0 * x
+
+
+def _bound_q4_k(x):
+    xs = x.reshape(-1, 8, 32)
+    m = np.maximum(0, -xs.min(axis=2))
+    dmin_hi = m.max(axis=1, keepdims=True) / 63 * (1 + U10) + Q16
+    s_hi = (np.maximum(xs.max(axis=2), 0) + m + dmin_hi) / 15
+    d_hi = s_hi.max(axis=1, keepdims=True) / 63 * (1 + U10) + Q16
+    step_hi = s_hi + d_hi
+    return np.repeat(step_hi / 2, 32, axis=1).reshape(x.shape)
+
+
+def _bound_q6_k(x):
+    xs = x.reshape(-1, 16, 16)
+    s = np.abs(xs).max(axis=2) / 31
+    d_hi = s.max(axis=1, keepdims=True) / 127 * (1 + U10) + Q16
+    return np.repeat((s + d_hi) / 2, 16, axis=1).reshape(x.shape)
+
+
+BOUNDS = {O.Q8_0: _bound_q8_0, O.Q4_0: _bound_q4_0, O.Q4_K: _bound_q4_k, O.Q6_K: _bound_q6_k}
+
+
+def _edge_blocks(be):
+    z = np.zeros(be, np.float32)
+    spike = z.copy()
+    spike[be // 3] = 0.7
+    neg = -np.abs(synth.normal_f32(0, 902, be, std=0.02))
+    pos = np.abs(synth.normal_f32(0, 903, be, std=0.02))
+    const = np.full(be, 0.0125, np.float32)
+    ramp = np.linspace(-1, 2, be).astype(np.float32)
+    return np.concatenate([z, spike, neg, pos, const, -const, ramp])
+
+
+@pytest.mark.parametrize("t", [O.Q8_0, O.Q4_0, O.Q4_K, O.Q6_K], ids=["q8_0", "q4_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("std", [0.02, 1.0])
+def test_quantize_round_trip_bound(t, std):
+    be = O.block_elems(t)
+    x = np.concatenate([synth.normal_f32(1, 910 + t, 64 * 256, std=std), _edge_blocks(be)])
+    xh = O.dequant(t, O.quantize(t, x), x.size).astype(np.float64)
+    x64 = x.astype(np.float64).reshape(-1, be)
+    bound = BOUNDS[t](x64).reshape(-1) + np.abs(xh) * Q16
+    err = np.abs(xh - x.astype(np.float64))
+    assert np.all(err <= bound), (err - bound).max()
+
+
+@pytest.mark.parametrize("t", [O.Q8_0, O.Q4_0, O.Q4_K, O.Q6_K], ids=["q8_0", "q4_0", "q4_k", "q6_k"])
+def test_quantize_zero_block(t):
+    be = O.block_elems(t)
+    z = np.zeros(3 * be, np.float32)
+    assert np.all(O.dequant(t, O.quantize(t, z), z.size) == 0)
+
+
+def _grid_input(t, nblocks):
+    """Values on the encoder's own grid, so the round trip must be exact.
+
+    Q8_0: k * 2^-10, k in [-127, 127], one |k| = 127 per block -> d = 2^-10.
+    Q4_0: k * 2^-3, k in [-7, 7], one |k| = 7 per block -> d = 2^-3.
+    Q4_K: k * 63 * 2^-12, k in [0, 15], a 0 and a 15 per sub-block -> dmin = 0,
+          d = 2^-12, every sub-scale 63.
+    Q6_K: k * 127 * 2^-12, k in [-31, 31], one |k| = 31 per sub-block ->
+          d = 2^-12, every sub-scale 127.
+    """
+    g = synth.rng(3, 920 + t)
+    if t == O.Q8_0:
+        k = g.integers(-127, 128, size=(nblocks, 32)); k[:, 5] = -127
+        return (k * 2.0**-10).astype(np.float32).reshape(-1)
+    if t == O.Q4_0:
+        k = g.integers(-7, 8, size=(nblocks, 32)); k[:, 9] = 7
+        return (k * 2.0**-3).astype(np.float32).reshape(-1)
+    if t == O.Q4_K:
+        k = g.integers(0, 16, size=(nblocks * 8, 32)); k[:, 0] = 0; k[:, 31] = 15
+        return (k * 63 * 2.0**-12).astype(np.float32).reshape(-1)
+    k = g.integers(-31, 32, size=(nblocks * 16, 16)); k[:, 7] = 31
+    return (k * 127 * 2.0**-12).astype(np.float32).reshape(-1)
+
+
+@pytest.mark.parametrize("t", [O.Q8_0, O.Q4_0, O.Q4_K, O.Q6_K], ids=["q8_0", "q4_0", "q4_k", "q6_k"])
+def test_quantize_exact_on_grid_values(t):
+    x = _grid_input(t, 16)
+    assert np.array_equal(O.dequant(t, O.quantize(t, x), x.size), x)
+
+
+def test_quantize_rejects_non_finite_and_ragged():
+    x = np.zeros(32, np.float32)
+    x[3] = np.nan
+    with pytest.raises(ValueError):
+        O.quantize(O.Q8_0, x)
+    with pytest.raises(ValueError):
+        O.dequant(O.Q4_K, np.zeros(144, np.uint8), 100)
+
+
+def test_q8_0_packing_matches_generator_layout():
+    d_bits, qs = synth.q8_0_random_parts(0, 4, 64)
+    a = O.pack_q8_0(d_bits, qs)
+    b = synth.q8_0_bytes(d_bits, qs)
+    assert np.array_equal(a, b)
+    vals = O.dequant(O.Q8_0, a, qs.size).astype(np.float64)
+    d = d_bits.view(np.float16).astype(np.float64)
+    assert np.array_equal(vals, np.repeat(d, 32) * qs.astype(np.float64))
