@@ -1,0 +1,99 @@
+"""The C-ABI library loads, exports every call include/nt.h declares, and
+rejects bad arguments before touching the GPU.  CPU-only: nothing here
+launches a kernel.  Calls that pass placeholder addresses run only on hosts
+with no GPU, where the library must stop at NT_ENODEV.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from block_quantized_decode_dequant_amd import nt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nt.h")
+
+
+def _gpu_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+no_gpu_only = pytest.mark.skipif(_gpu_visible(), reason="placeholder addresses are only passed "
+                                 "on hosts without a GPU")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nt_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_call():
+    L = C.CDLL(nt.lib_path())
+    names = declared_functions()
+    assert len(names) >= 18
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_version_status_and_geometry():
+    L = nt.lib()
+    assert L.nt_abi_version() == 1
+    for s in range(8):
+        assert nt.status_str(s).startswith("NT_")
+    assert [L.nt_qtype_block_elems(t) for t in (nt.Q8_0, nt.Q4_0, nt.Q4_K, nt.Q6_K)] == [32, 32, 256, 256]
+    assert [L.nt_qtype_block_bytes(t) for t in (nt.Q8_0, nt.Q4_0, nt.Q4_K, nt.Q6_K)] == [34, 18, 144, 210]
+    assert nt.row_bytes(nt.Q6_K, 8192) == 32 * 210
+    assert nt.row_bytes(nt.Q8_0, 4096) == 128 * 34
+    assert nt.row_bytes(nt.Q4_K, 300) == -1
+    assert L.nt_qtype_block_elems(99) == -1
+
+
+A = 0x10000     # placeholder, 16-byte aligned; never dereferenced
+
+
+def _gemv(t, W, x, y, rows, cols, acc=0):
+    return nt.lib().nt_gemv(t, C.c_void_p(W), C.c_void_p(x), C.c_void_p(y), rows, cols, acc, None)
+
+
+@no_gpu_only
+def test_gemv_argument_errors():
+    assert _gemv(nt.Q4_K, 0, A, A, 4, 256) == nt.NT_EINVAL
+    assert "null" in nt.last_error()
+    assert _gemv(nt.Q4_K, A, A, A, 4, 100) == nt.NT_ESHAPE
+    assert _gemv(nt.Q8_0, A, A, A, -1, 64) == nt.NT_EINVAL
+    assert _gemv(nt.Q8_0, A, A, A, 4, 65536 + 32) == nt.NT_ESHAPE
+    assert _gemv(nt.Q8_0, A + 2, A, A, 4, 64) == nt.NT_EALIGN
+    assert _gemv(nt.Q8_0, A, A + 4, A, 4, 64) == nt.NT_EALIGN
+    assert _gemv(5, A, A, A, 4, 64) == nt.NT_EINVAL
+    assert _gemv(nt.Q8_0, 0, 0, 0, 0, 64) == nt.NT_OK        # nothing to do
+    assert _gemv(nt.Q6_K, A, A, A, 4, 256) == nt.NT_ENODEV   # valid, but no GPU here
+
+
+@no_gpu_only
+def test_dequant_and_calibration_argument_errors():
+    L = nt.lib()
+    v = C.c_void_p
+    assert L.nt_dequant(nt.Q4_0, v(A), v(A), 33, None) == nt.NT_ESHAPE
+    assert L.nt_dequant(nt.Q4_0, v(A + 8), v(A), 32, None) == nt.NT_EALIGN
+    assert L.nt_dequant(nt.Q4_0, v(A), v(A + 2), 32, None) == nt.NT_EALIGN
+    assert L.nt_dequant(nt.F32, v(A), v(A), 32, None) == nt.NT_EINVAL
+    assert L.nt_dequant_q6_k(v(0), v(A), 256, None) == nt.NT_EINVAL
+    assert L.nt_dequant_q8_0(v(A), v(A), 0, None) == nt.NT_OK
+    assert L.nt_dequant_q8_0(v(A), v(A), 64, None) == nt.NT_ENODEV
+    assert L.nt_read_bytes(v(A), 24, v(A), None) == nt.NT_ESHAPE
+    assert L.nt_copy_bytes(v(A), v(A + 4), 32, None) == nt.NT_EALIGN
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    W = torch.zeros(34 * 2, dtype=torch.uint8)
+    x = torch.zeros(64)
+    y = torch.zeros(1)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        nt.nt_gemv_q8_0(W, x, y, 1, 64)
