@@ -162,6 +162,103 @@ NT_GEMV_FN(nt_gemv_q4_k, NT_Q4_K)
 NT_GEMV_FN(nt_gemv_q6_k, NT_Q6_K)
 #undef NT_GEMV_FN
 
+// ---- per-token ops ---------------------------------------------------------------
+#define NT_REQ(cond, st, msg) \
+    do {                      \
+        if (!(cond)) return fail(st, msg); \
+    } while (0)
+
+nt_status nt_rmsnorm(const float *x, const float *gain, float *y, int64_t n, float eps, nt_stream stream) {
+    set_error("");
+    NT_REQ(n >= 0, NT_EINVAL, "nt_rmsnorm: negative n");
+    if (n == 0) return NT_OK;
+    NT_REQ(x && gain && y, NT_EINVAL, "nt_rmsnorm: null pointer");
+    NT_REQ(aligned(x, 4) && aligned(gain, 4) && aligned(y, 4), NT_EALIGN, "nt_rmsnorm: misaligned");
+    NT_REQ(eps >= 0.f, NT_EINVAL, "nt_rmsnorm: negative eps");
+    if (nt_status s = need_device()) return s;
+    return finish(launch_rmsnorm(x, gain, y, n, eps, as_stream(stream)), "nt_rmsnorm");
+}
+
+nt_status nt_rope(float *q, float *k, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                  const int32_t *d_pos, float theta, nt_stream stream) {
+    set_error("");
+    NT_REQ(n_q_heads >= 0 && n_kv_heads >= 0 && head_dim > 0, NT_EINVAL, "nt_rope: bad sizes");
+    NT_REQ(head_dim % 2 == 0, NT_ESHAPE, "nt_rope: head_dim must be even");
+    NT_REQ(theta > 0.f, NT_EINVAL, "nt_rope: theta must be positive");
+    if (n_q_heads + n_kv_heads == 0) return NT_OK;
+    NT_REQ(d_pos && (q || n_q_heads == 0) && (k || n_kv_heads == 0), NT_EINVAL, "nt_rope: null pointer");
+    NT_REQ(aligned(q, 4) && aligned(k, 4) && aligned(d_pos, 4), NT_EALIGN, "nt_rope: misaligned");
+    if (nt_status s = need_device()) return s;
+    return finish(launch_rope(q, k, n_q_heads, n_kv_heads, head_dim, d_pos, theta, as_stream(stream)), "nt_rope");
+}
+
+nt_status nt_softmax(float *x, int64_t n, nt_stream stream) {
+    set_error("");
+    NT_REQ(n >= 0, NT_EINVAL, "nt_softmax: negative n");
+    if (n == 0) return NT_OK;
+    NT_REQ(x, NT_EINVAL, "nt_softmax: null pointer");
+    NT_REQ(aligned(x, 4), NT_EALIGN, "nt_softmax: misaligned");
+    if (nt_status s = need_device()) return s;
+    return finish(launch_softmax(x, n, as_stream(stream)), "nt_softmax");
+}
+
+nt_status nt_swiglu(const float *gate, const float *up, float *out, int64_t n, nt_stream stream) {
+    set_error("");
+    NT_REQ(n >= 0, NT_EINVAL, "nt_swiglu: negative n");
+    if (n == 0) return NT_OK;
+    NT_REQ(gate && up && out, NT_EINVAL, "nt_swiglu: null pointer");
+    NT_REQ(aligned(gate, 4) && aligned(up, 4) && aligned(out, 4), NT_EALIGN, "nt_swiglu: misaligned");
+    if (nt_status s = need_device()) return s;
+    return finish(launch_swiglu(gate, up, out, n, as_stream(stream)), "nt_swiglu");
+}
+
+nt_status nt_argmax(const float *x, int64_t n, int32_t *out, nt_stream stream) {
+    set_error("");
+    NT_REQ(n >= 1 && n < (int64_t(1) << 31), NT_EINVAL, "nt_argmax: need 1 <= n < 2^31");
+    NT_REQ(x && out, NT_EINVAL, "nt_argmax: null pointer");
+    NT_REQ(aligned(x, 4) && aligned(out, 4), NT_EALIGN, "nt_argmax: misaligned");
+    if (nt_status s = need_device()) return s;
+    return finish(launch_argmax(x, n, out, nullptr, as_stream(stream)), "nt_argmax");
+}
+
+nt_status nt_embed(nt_qtype t, const void *table, int64_t vocab, int64_t hidden, const int32_t *d_token,
+                   float *out, nt_stream stream) {
+    set_error("");
+    NT_REQ(is_quant(t), NT_EINVAL, "nt_embed: unsupported type");
+    NT_REQ(vocab > 0 && hidden >= 0 && vocab < (int64_t(1) << 31), NT_EINVAL, "nt_embed: bad sizes");
+    NT_REQ(hidden % block_elems(t) == 0, NT_ESHAPE, "nt_embed: hidden is not a multiple of the block size");
+    if (hidden == 0) return NT_OK;
+    NT_REQ(table && d_token && out, NT_EINVAL, "nt_embed: null pointer");
+    NT_REQ(aligned(table, 16) && aligned(d_token, 4) && aligned(out, 4), NT_EALIGN, "nt_embed: misaligned");
+    if (nt_status s = need_device()) return s;
+    return finish(launch_embed(t, table, vocab, hidden, d_token, out, as_stream(stream)), "nt_embed");
+}
+
+size_t nt_attn_workspace_bytes(const nt_attn_desc *desc) {
+    if (!desc || !attn_shape_ok(*desc)) return 0;
+    return attn_workspace_bytes(*desc);
+}
+
+nt_status nt_attn_decode(const nt_attn_desc *desc, const float *q, const float *k_new, const float *v_new,
+                         uint16_t *k_cache, uint16_t *v_cache, const int32_t *d_pos, float *out,
+                         void *workspace, size_t workspace_bytes, nt_stream stream) {
+    set_error("");
+    NT_REQ(desc, NT_EINVAL, "nt_attn_decode: null descriptor");
+    NT_REQ(desc->n_q_heads > 0 && desc->n_kv_heads > 0 && desc->head_dim > 0 && desc->ctx_cap > 0,
+           NT_EINVAL, "nt_attn_decode: sizes must be positive");
+    NT_REQ(attn_shape_ok(*desc), NT_ESHAPE,
+           "nt_attn_decode: need head_dim 64 or 128 and n_q_heads / n_kv_heads in {1, 2, 4, 8}");
+    NT_REQ(q && k_cache && v_cache && d_pos && out && workspace, NT_EINVAL, "nt_attn_decode: null pointer");
+    NT_REQ((k_new == nullptr) == (v_new == nullptr), NT_EINVAL, "nt_attn_decode: k_new and v_new must both be set or both NULL");
+    NT_REQ(aligned(k_cache, 16) && aligned(v_cache, 16) && aligned(workspace, 16) && aligned(q, 4) &&
+               aligned(out, 4) && aligned(d_pos, 4) && aligned(k_new, 4) && aligned(v_new, 4),
+           NT_EALIGN, "nt_attn_decode: misaligned pointer");
+    NT_REQ(workspace_bytes >= attn_workspace_bytes(*desc), NT_ENOMEM, "nt_attn_decode: workspace too small");
+    if (nt_status s = need_device()) return s;
+    return finish(launch_attn(*desc, q, k_new, v_new, k_cache, v_cache, d_pos, out, workspace, as_stream(stream)),
+                  "nt_attn_decode");
+}
+
 // ---- encode -------------------------------------------------------------------------
 nt_status nt_quantize(nt_qtype t, const float *x, void *blocks, int64_t n, nt_stream stream) {
     set_error("");

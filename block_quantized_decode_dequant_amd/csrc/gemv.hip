@@ -364,6 +364,7 @@ __device__ __forceinline__ void load_x64(const float *x, float *v, float &sum) {
 
 // ---- Q8_0 fast: one lane = blocks 2u, 2u+1 (68 bytes at 68u, word-aligned) --
 struct F80 {
+    static constexpr int kRows = 2;
     struct L { uint32_t off; };
     struct X { float v[64]; float s0, s1; };
     struct Raw { u32x4 a, b, c, d; uint32_t e; };
@@ -410,6 +411,7 @@ struct F80 {
 
 // ---- Q4_0 fast: one lane = blocks 2u, 2u+1 (36 bytes at 36u, word-aligned) --
 struct F40 {
+    static constexpr int kRows = 2;
     struct L { uint32_t off; };
     struct X { float v[64]; float s0, s1; };
     struct Raw { u32x4 a, b; uint32_t c; };
@@ -456,6 +458,7 @@ struct F40 {
 // byte 32p + i: low nibble = value 64p + i (sub-block 2p), high nibble = value
 // 64p + 32 + i (sub-block 2p+1).
 struct F4K {
+    static constexpr int kRows = 2;
     struct L { uint32_t off_h, off_q, p; };
     struct X { float v[64]; float slo, shi; };   // v[i]: value 64p+i (lo: i<32, hi: i>=32)
     struct Raw { u32x4 h, q0, q1; };
@@ -484,16 +487,12 @@ struct F4K {
         for (int m = 0; m < 8; ++m) nib_fma(q[m], xs.v + 4 * m, xs.v + 32 + 4 * m, magic, al, ah);
         const uint32_t p = l.p, sft = 16 * (p & 1);
         const uint32_t y = r.h.y >> sft, z = r.h.z >> sft, w = r.h.w >> sft;
-        uint32_t S0, M0, S1, M1;
-        if (p < 2) {
-            S0 = y & 63; M0 = z & 63;
-            S1 = (y >> 8) & 63; M1 = (z >> 8) & 63;
-        } else {
-            S0 = (w & 15) | (((y >> 6) & 3) << 4);
-            M0 = ((w >> 4) & 15) | (((z >> 6) & 3) << 4);
-            S1 = ((w >> 8) & 15) | (((y >> 14) & 3) << 4);
-            M1 = ((w >> 12) & 15) | (((z >> 14) & 3) << 4);
-        }
+        // both encodings computed, one selected: no divergent branch
+        const bool low = p < 2;
+        const uint32_t S0 = low ? (y & 63) : ((w & 15) | (((y >> 6) & 3) << 4));
+        const uint32_t M0 = low ? (z & 63) : (((w >> 4) & 15) | (((z >> 6) & 3) << 4));
+        const uint32_t S1 = low ? ((y >> 8) & 63) : (((w >> 8) & 15) | (((y >> 14) & 3) << 4));
+        const uint32_t M1 = low ? ((z >> 8) & 63) : (((w >> 12) & 15) | (((z >> 14) & 3) << 4));
         const float d = h2f(r.h.x), dmin = h2f(r.h.x >> 16);
         // sum q x over a sub-block = 16 * (acc - X)
         const float pos = fmaf(float(S0), al - xs.slo, float(S1) * (ah - xs.shi));
@@ -509,6 +508,7 @@ struct F4K {
 // qh[32h + 16j + i] (bits 2k..2k+1), scales[8h + 2k + j] and d.  Odd blocks
 // start 2 bytes into a word: loads are word-aligned and v_perm realigns.
 struct F6K {
+    static constexpr int kRows = 1;
     struct L { uint32_t base, sel, h, j; };
     struct X { float v[4][16]; float s[4]; };
     struct Raw { u32x4 a; uint32_t a4; u32x4 b; uint32_t b4; u32x4 c; uint32_t c4; u32x3 sc; uint32_t d; };
@@ -580,43 +580,74 @@ struct F6K {
     }
 };
 
-// nw waves (one per 64*64-value column slice, up to 8) x R rows at a time.
-template <class Tr, int R>
+// Persistent, software-pipelined fast kernel.  A workgroup of nw waves (one
+// per 4096-value column slice) walks row tiles blockIdx.x, +gridDim.x, ...
+// A tile is G row groups of R rows.  The tile body is fully unrolled with two
+// register buffers: while a wave decodes group g it already has the loads of
+// group g+1 in flight (the last group prefetches the first group of the next
+// tile), so every load is unconditional and the compiler can wait for exactly
+// the group it decodes.  Row sums are reduced over the wave with DPP, kept in
+// one VGPR (lane i = row i of the tile), written to LDS once per tile, and the
+// nw column slices are added in a fixed order.
+template <class Tr, int G>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(3)))
 gemv_fast(const uint8_t *__restrict__ W, const float *__restrict__ x, float *__restrict__ y,
-          int rows, int64_t row_bytes, int units_per_row, int tile, int accumulate) {
-    __shared__ float part[8 * 64];   // [nw][tile], tile <= 64
+          int rows, int64_t row_bytes, int units_per_row, int accumulate) {
+    constexpr int R = Tr::kRows, T = R * G;
+    static_assert(G % 2 == 0 && T <= 64, "tile shape");
+    __shared__ float part[2][8 * T];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int64_t unit = int64_t(wave) * 64 + lane;
     const bool ok = unit < units_per_row;
     const uint32_t magic = opaque(kMagic16);
+    const typename Tr::L L = Tr::lane(ok ? unit : 0);
+    const int ntiles = (rows + T - 1) / T;
+    int t = blockIdx.x;
+    if (t >= ntiles) return;
 
+    // rows past the end re-read the last row; idle lanes read unit 0
+    auto issue = [&](typename Tr::Raw *buf, int tile, int g) {
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+            Tr::load(W + int64_t(min(tile * T + g * R + i, rows - 1)) * row_bytes, L, buf[i]);
+    };
+
+    typename Tr::Raw A[R], B[R];
+    issue(A, t, 0);
+    asm volatile("" ::: "memory");      // the first weight loads go out before the activations
     typename Tr::X xs;
-    typename Tr::L L = Tr::lane(ok ? unit : 0);
-    if (ok) Tr::load_x(x, unit, xs);
+    Tr::load_x(x, ok ? unit : 0, xs);
 
-    const int r0 = blockIdx.x * tile;
-    const int rend = min(rows - r0, tile);
-    for (int rr = 0; rr < rend; rr += R) {
-        typename Tr::Raw raw[R];
+    int pb = 0;
+    for (; t < ntiles; t += gridDim.x) {
+        const int tn = t + int(gridDim.x) < ntiles ? t + int(gridDim.x) : t;
+        float rowsum = 0.f;             // lane i: sum of row i of this tile (this slice)
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-            const int r = r0 + rr + i;
-            if (ok && rr + i < rend) Tr::load(W + int64_t(r) * row_bytes, L, raw[i]);
-        }
+        for (int g = 0; g < G; ++g) {
+            typename Tr::Raw *cur = (g & 1) ? B : A;
+            typename Tr::Raw *nxt = (g & 1) ? A : B;
+            if (g + 1 < G) issue(nxt, t, g + 1);
+            else issue(nxt, tn, 0);
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-            float a = (ok && rr + i < rend) ? Tr::dot(raw[i], xs, L, magic) : 0.f;
-            a = wave_sum_to_lane63(a);
-            if (lane == 63) part[wave * tile + rr + i] = a;
+            for (int i = 0; i < R; ++i) {
+                float a = Tr::dot(cur[i], xs, L, magic);
+                a = ok ? a : 0.f;
+                a = wave_sum_to_lane63(a);
+                const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 63));
+                rowsum = (lane == g * R + i) ? s : rowsum;
+            }
         }
-    }
-    __syncthreads();
-    for (int t = threadIdx.x; t < rend; t += blockDim.x) {
-        float s = 0.f;
-        for (int w = 0; w < nw; ++w) s += part[w * tile + t];
-        const int r = r0 + t;
-        y[r] = accumulate ? y[r] + s : s;
+        if (lane < T) part[pb][wave * T + lane] = rowsum;
+        __syncthreads();
+        if (wave == 0 && lane < T) {
+            const int r = t * T + lane;
+            if (r < rows) {
+                float sum = 0.f;
+                for (int w = 0; w < nw; ++w) sum += part[pb][w * T + lane];
+                y[r] = accumulate ? y[r] + sum : sum;
+            }
+        }
+        pb ^= 1;
     }
 }
 
@@ -652,26 +683,29 @@ hipError_t launch_fast(const void *W, const float *x, float *y, int64_t rows, in
                        int acc, hipStream_t st) {
     const int units = int(cols / 64);
     const int nw = (units + 63) / 64;                 // <= 8 for cols <= 32768
-    static const int tile_env = env_int("NT_GEMV_TILE", 0);
-    static const int r_env = env_int("NT_GEMV_R", 0);
-    int tile = tile_env;
-    if (tile <= 0) {
-        // enough workgroups to keep every CU busy, enough rows per workgroup
-        // to amortize loading its activation slice
-        const int64_t t = rows * nw / 4096;
-        tile = t < 4 ? 4 : t > 32 ? 32 : int(t);
+    static const int waves_env = env_int("NT_GEMV_WAVES", 0);
+    static const int g_env = env_int("NT_GEMV_G", 0);
+    constexpr int R = Tr::kRows;
+    // groups per tile: 8 for tall matrices, 4 (or 2) when that leaves too few tiles
+    int G = g_env;
+    if (G <= 0) {
+        G = 8;
+        while (G > 2 && (rows + R * G - 1) / (R * G) * nw < 2048) G /= 2;
     }
-    const int R = r_env > 0 ? r_env : 2;
-    tile = (tile + R - 1) / R * R;
-    if (tile > 64) tile = 64;
-    const int64_t grid = (rows + tile - 1) / tile;
+    const int T = R * G;
+    const int64_t ntiles = (rows + T - 1) / T;
+    // Persistent grid: about 12 resident waves per CU on 256 CUs.
+    const int64_t waves = waves_env > 0 ? waves_env : 256 * 12;
+    int64_t grid = waves / nw;
+    if (grid > ntiles) grid = ntiles;
+    if (grid < 1) grid = 1;
     const uint8_t *w = static_cast<const uint8_t *>(W);
-    if (R == 4)
-        gemv_fast<Tr, 4><<<dim3(unsigned(grid)), dim3(64 * nw), 0, st>>>(w, x, y, int(rows), row_bytes, units, tile, acc);
-    else if (R == 1)
-        gemv_fast<Tr, 1><<<dim3(unsigned(grid)), dim3(64 * nw), 0, st>>>(w, x, y, int(rows), row_bytes, units, tile, acc);
-    else
-        gemv_fast<Tr, 2><<<dim3(unsigned(grid)), dim3(64 * nw), 0, st>>>(w, x, y, int(rows), row_bytes, units, tile, acc);
+    const dim3 gd = dim3(unsigned(grid)), bd = dim3(unsigned(64 * nw));
+    switch (G) {
+    case 2: gemv_fast<Tr, 2><<<gd, bd, 0, st>>>(w, x, y, int(rows), row_bytes, units, acc); break;
+    case 4: gemv_fast<Tr, 4><<<gd, bd, 0, st>>>(w, x, y, int(rows), row_bytes, units, acc); break;
+    default: gemv_fast<Tr, 8><<<gd, bd, 0, st>>>(w, x, y, int(rows), row_bytes, units, acc); break;
+    }
     return hipGetLastError();
 }
 

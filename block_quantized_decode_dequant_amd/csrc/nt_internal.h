@@ -31,6 +31,19 @@ hipError_t launch_gemv(nt_qtype t, const void *W, const float *x, float *y, int6
                        int64_t cols, int accumulate, hipStream_t st);
 hipError_t launch_quantize(nt_qtype t, const float *x, void *blocks, int64_t n, hipStream_t st);
 hipError_t launch_delay(double us, hipStream_t st);
+hipError_t launch_rmsnorm(const float *x, const float *g, float *y, int64_t n, float eps, hipStream_t st);
+hipError_t launch_rope(float *q, float *k, int n_q_heads, int n_kv_heads, int head_dim, const int32_t *d_pos,
+                       float theta, hipStream_t st);
+hipError_t launch_softmax(float *x, int64_t n, hipStream_t st);
+hipError_t launch_swiglu(const float *g, const float *u, float *out, int64_t n, hipStream_t st);
+hipError_t launch_argmax(const float *x, int64_t n, int32_t *out, int32_t *pos_inc, hipStream_t st);
+hipError_t launch_embed(nt_qtype t, const void *table, int64_t vocab, int64_t hidden, const int32_t *d_token,
+                        float *out, hipStream_t st);
+int attn_chunk(const nt_attn_desc &a);
+size_t attn_workspace_bytes(const nt_attn_desc &a);
+bool attn_shape_ok(const nt_attn_desc &a);
+hipError_t launch_attn(const nt_attn_desc &a, const float *q, const float *k_new, const float *v_new, uint16_t *kc,
+                       uint16_t *vc, const int32_t *d_pos, float *out, void *ws, hipStream_t st);
 hipError_t launch_read_bytes(const void *src, int64_t bytes, float *sink, hipStream_t st);
 hipError_t launch_copy_bytes(void *dst, const void *src, int64_t bytes, hipStream_t st);
 

@@ -20,6 +20,11 @@ BLOCK_ELEMS = {Q8_0: 32, Q4_0: 32, Q4_K: 256, Q6_K: 256}
 BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_K: 144, Q6_K: 210}
 
 
+class AttnDesc(C.Structure):
+    _fields_ = [("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("ctx_cap", C.c_int32), ("scale", C.c_float)]
+
+
 class NTError(RuntimeError):
     def __init__(self, status: int, func: str, message: str):
         super().__init__(f"{func}: status {status}: {message}")
@@ -62,6 +67,14 @@ def _declare(L):
         "nt_read_bytes": (st, [vp, i64, vp, vp]),
         "nt_copy_bytes": (st, [vp, vp, i64, vp]),
         "nt_delay": (st, [C.c_double, vp]),
+        "nt_rmsnorm": (st, [vp, vp, vp, i64, C.c_float, vp]),
+        "nt_rope": (st, [vp, vp, C.c_int32, C.c_int32, C.c_int32, vp, C.c_float, vp]),
+        "nt_softmax": (st, [vp, i64, vp]),
+        "nt_swiglu": (st, [vp, vp, vp, i64, vp]),
+        "nt_argmax": (st, [vp, i64, vp, vp]),
+        "nt_embed": (st, [i32, vp, i64, i64, vp, vp, vp]),
+        "nt_attn_workspace_bytes": (C.c_size_t, [C.POINTER(AttnDesc)]),
+        "nt_attn_decode": (st, [C.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]),
     }
     for t in ("q8_0", "q4_0", "q4_k", "q6_k"):
         sig[f"nt_dequant_{t}"] = (st, [vp, vp, i64, vp])
@@ -167,3 +180,54 @@ def nt_copy_bytes(dst, src, nbytes: int, stream=None):
 
 def nt_delay(microseconds: float, stream=None):
     _check(lib().nt_delay(float(microseconds), _stream(stream)), "nt_delay")
+
+
+# ---- per-token ops --------------------------------------------------------------------
+def nt_rmsnorm(x, gain, y, n: int, eps: float, stream=None):
+    _check(lib().nt_rmsnorm(_ptr(x, 4 * n, "x"), _ptr(gain, 4 * n, "gain"), _ptr(y, 4 * n, "y"), n, eps,
+                            _stream(stream)), "nt_rmsnorm")
+
+
+def nt_rope(q, k, n_q_heads: int, n_kv_heads: int, head_dim: int, d_pos, theta: float, stream=None):
+    _check(lib().nt_rope(_ptr(q, 4 * n_q_heads * head_dim, "q"), _ptr(k, 4 * n_kv_heads * head_dim, "k"),
+                         n_q_heads, n_kv_heads, head_dim, _ptr(d_pos, 4, "d_pos"), theta, _stream(stream)),
+           "nt_rope")
+
+
+def nt_softmax(x, n: int, stream=None):
+    _check(lib().nt_softmax(_ptr(x, 4 * n, "x"), n, _stream(stream)), "nt_softmax")
+
+
+def nt_swiglu(gate, up, out, n: int, stream=None):
+    _check(lib().nt_swiglu(_ptr(gate, 4 * n, "gate"), _ptr(up, 4 * n, "up"), _ptr(out, 4 * n, "out"), n,
+                           _stream(stream)), "nt_swiglu")
+
+
+def nt_argmax(x, n: int, out, stream=None):
+    _check(lib().nt_argmax(_ptr(x, 4 * n, "x"), n, _ptr(out, 4, "out"), _stream(stream)), "nt_argmax")
+
+
+def nt_embed(qtype: int, table, vocab: int, hidden: int, d_token, out, stream=None):
+    rb = row_bytes(qtype, hidden)
+    _check(lib().nt_embed(qtype, _ptr(table, vocab * max(rb, 0), "table"), vocab, hidden,
+                          _ptr(d_token, 4, "d_token"), _ptr(out, 4 * hidden, "out"), _stream(stream)),
+           "nt_embed")
+
+
+def attn_desc(n_q_heads: int, n_kv_heads: int, head_dim: int, ctx_cap: int, scale: float = 0.0) -> AttnDesc:
+    return AttnDesc(n_q_heads, n_kv_heads, head_dim, ctx_cap, scale)
+
+
+def nt_attn_workspace_bytes(desc: AttnDesc) -> int:
+    return lib().nt_attn_workspace_bytes(C.byref(desc))
+
+
+def nt_attn_decode(desc: AttnDesc, q, k_new, v_new, k_cache, v_cache, d_pos, out, workspace, stream=None):
+    kv = desc.n_kv_heads * desc.head_dim
+    cache = 2 * kv * desc.ctx_cap
+    ws_bytes = workspace.numel() * workspace.element_size() if not isinstance(workspace, int) else 0
+    _check(lib().nt_attn_decode(C.byref(desc), _ptr(q, 4 * desc.n_q_heads * desc.head_dim, "q"),
+                                _ptr(k_new, 4 * kv, "k_new"), _ptr(v_new, 4 * kv, "v_new"),
+                                _ptr(k_cache, cache, "k_cache"), _ptr(v_cache, cache, "v_cache"),
+                                _ptr(d_pos, 4, "d_pos"), _ptr(out, 4 * desc.n_q_heads * desc.head_dim, "out"),
+                                _ptr(workspace, 0, "workspace"), ws_bytes, _stream(stream)), "nt_attn_decode")

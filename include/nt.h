@@ -114,6 +114,60 @@ nt_status nt_gemv_q6_k(const void *W, const float *x, float *y, int64_t rows, in
 nt_status nt_gemv(nt_qtype t, const void *W, const float *x, float *y, int64_t rows, int64_t cols,
                   int accumulate, nt_stream stream);
 
+/* ---- per-token ops ("Architecture": RMSNorm, RoPE, SwiGLU, softmax kernels;
+ * "Main features": the Llama block) --------------------------------------
+ * All buffers are device fp32 unless stated, 4-byte aligned, and may not
+ * overlap unless stated.  Reductions run in a fixed order (deterministic). */
+
+/* y[i] = gain[i] * x[i] / sqrt(sum_j x[j]^2 / n + eps), i in [0, n).  y may equal x. */
+nt_status nt_rmsnorm(const float *x, const float *gain, float *y, int64_t n, float eps, nt_stream stream);
+
+/* Rotary embedding in place on q (n_q_heads * head_dim values) and k
+ * (n_kv_heads * head_dim; k may be NULL when n_kv_heads == 0): the adjacent
+ * pair (v[2i], v[2i+1]) of every head turns by angle pos * theta^(-2i/head_dim),
+ * pos = *d_pos (device int32).  head_dim even.  The angle is formed in fp64. */
+nt_status nt_rope(float *q, float *k, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                  const int32_t *d_pos, float theta, nt_stream stream);
+
+/* In place: x[t] <- exp(x[t] - max x) / sum_u exp(x[u] - max x), t in [0, n). */
+nt_status nt_softmax(float *x, int64_t n, nt_stream stream);
+
+/* out[i] = silu(gate[i]) * up[i], silu(a) = a / (1 + exp(-a)).  out may equal gate or up. */
+nt_status nt_swiglu(const float *gate, const float *up, float *out, int64_t n, nt_stream stream);
+
+/* *out (device int32) = index of the largest x[i], the lowest index on ties;
+ * NaNs never win against numbers.  1 <= n < 2^31. */
+nt_status nt_argmax(const float *x, int64_t n, int32_t *out, nt_stream stream);
+
+/* out[0, hidden) = decoded row *d_token of the packed [vocab x hidden] table
+ * (device, 16-byte aligned, format t).  A token outside [0, vocab) yields NaN
+ * values (nothing is read out of bounds). */
+nt_status nt_embed(nt_qtype t, const void *table, int64_t vocab, int64_t hidden, const int32_t *d_token,
+                   float *out, nt_stream stream);
+
+/* ---- decode attention over the fp16 KV cache ("Main features": GQA, KV cache;
+ * "Roadmap": F16 KV cache) ------------------------------------------------
+ * One layer's cache: k_cache and v_cache are device fp16 bit patterns laid out
+ * [n_kv_heads][ctx_cap][head_dim], 16-byte aligned.  With pos = *d_pos:
+ *   1. k_new, v_new (device fp32, n_kv_heads * head_dim) are rounded to fp16
+ *      and stored at slot pos (skipped when k_new and v_new are NULL: the
+ *      caller has stored them already);
+ *   2. q head h (of n_q_heads, q device fp32) attends to slots [0, pos] of kv
+ *      head h / (n_q_heads / n_kv_heads):  s_t = scale * <q_h, k_t>,
+ *      out_h = sum_t softmax(s)_t * v_t   (out: device fp32, n_q_heads * head_dim).
+ * scale <= 0 means 1 / sqrt(head_dim).  head_dim must be 64 or 128 and
+ * n_q_heads / n_kv_heads one of 1, 2, 4, 8 (NT_ESHAPE).  workspace: device,
+ * 16-byte aligned, at least nt_attn_workspace_bytes(desc) bytes (NT_ENOMEM).
+ * A pos outside [0, ctx_cap) makes out NaN and writes nothing to the cache. */
+typedef struct {
+    int32_t n_q_heads, n_kv_heads, head_dim, ctx_cap;
+    float scale;
+} nt_attn_desc;
+size_t    nt_attn_workspace_bytes(const nt_attn_desc *desc);
+nt_status nt_attn_decode(const nt_attn_desc *desc, const float *q, const float *k_new, const float *v_new,
+                         uint16_t *k_cache, uint16_t *v_cache, const int32_t *d_pos, float *out,
+                         void *workspace, size_t workspace_bytes, nt_stream stream);
+
 /* ---- encode (quantize) -------------------------------------------------------
  * blocks <- encoding of x[0, n) (device fp32, 4-byte aligned) into packed
  * blocks (device, 16-byte aligned, n / block_elems * block_bytes bytes).

@@ -97,3 +97,39 @@ def test_binding_refuses_host_tensors():
     y = torch.zeros(1)
     with pytest.raises(ValueError, match="GPU tensor"):
         nt.nt_gemv_q8_0(W, x, y, 1, 64)
+
+
+@no_gpu_only
+def test_op_argument_errors():
+    L = nt.lib()
+    v = C.c_void_p
+    assert L.nt_rmsnorm(v(A), v(A), v(A), -1, 1e-5, None) == nt.NT_EINVAL
+    assert L.nt_rmsnorm(v(A), v(0), v(A), 8, 1e-5, None) == nt.NT_EINVAL
+    assert L.nt_rmsnorm(v(A + 2), v(A), v(A), 8, 1e-5, None) == nt.NT_EALIGN
+    assert L.nt_rope(v(A), v(A), 4, 2, 63, v(A), 1e4, None) == nt.NT_ESHAPE
+    assert L.nt_rope(v(A), v(A), 4, 2, 64, v(0), 1e4, None) == nt.NT_EINVAL
+    assert L.nt_softmax(v(0), 5, None) == nt.NT_EINVAL
+    assert L.nt_swiglu(v(A), v(A), v(A + 1), 5, None) == nt.NT_EALIGN
+    assert L.nt_argmax(v(A), 0, v(A), None) == nt.NT_EINVAL
+    assert L.nt_embed(nt.Q4_K, v(A), 10, 100, v(A), v(A), None) == nt.NT_ESHAPE
+    assert L.nt_embed(nt.Q4_K, v(A + 4), 10, 256, v(A), v(A), None) == nt.NT_EALIGN
+    assert L.nt_rmsnorm(v(A), v(A), v(A), 8, 1e-5, None) == nt.NT_ENODEV
+
+
+@no_gpu_only
+def test_attention_argument_errors():
+    L = nt.lib()
+    v = C.c_void_p
+    good = nt.attn_desc(32, 8, 128, 1152)
+    ws = nt.nt_attn_workspace_bytes(good)
+    assert ws == 32 * 36 * 130 * 4      # chunk 32 -> 36 chunks of (max, sum, o[128]) per q head
+    args = lambda d, wsb=ws, kn=A: (C.byref(d), v(A), v(kn), v(kn), v(A), v(A), v(A), v(A), v(A), wsb, None)
+    assert L.nt_attn_decode(*args(nt.attn_desc(12, 8, 128, 64))) == nt.NT_ESHAPE     # 12 % 8 != 0
+    assert L.nt_attn_decode(*args(nt.attn_desc(32, 8, 96, 64))) == nt.NT_ESHAPE      # head_dim 96
+    assert L.nt_attn_decode(*args(nt.attn_desc(48, 3, 64, 64))) == nt.NT_ESHAPE      # group of 16
+    assert L.nt_attn_decode(*args(nt.attn_desc(32, 8, 128, 0))) == nt.NT_EINVAL
+    assert L.nt_attn_decode(*args(good, ws - 4)) == nt.NT_ENOMEM
+    assert L.nt_attn_decode(C.byref(good), v(A), v(A), v(0), v(A), v(A), v(A), v(A), v(A), ws, None) == nt.NT_EINVAL
+    assert L.nt_attn_decode(*args(good)) == nt.NT_ENODEV
+    assert L.nt_attn_decode(*args(good, ws, 0)) == nt.NT_ENODEV      # both NULL is allowed
+    assert nt.nt_attn_workspace_bytes(nt.attn_desc(32, 8, 96, 64)) == 0
