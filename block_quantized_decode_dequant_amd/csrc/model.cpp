@@ -1,0 +1,534 @@
+// model.cpp -- the decode step: sequencing of the per-token kernels, HIP
+// graph capture and replay, and the host-streamed layer mode.
+//
+// The ntransformer write-up's engine ("Architecture": inference/engine over
+// model/ attention, FFN and normalization) runs one Llama block per layer
+// ("Main features") and keeps some layers resident in GPU memory while the
+// others are copied from pinned host RAM, double buffered so the copy of the
+// next layer overlaps the compute of the current one ("Performance": 3-tier
+// cache; "Main features": streaming that overlaps transfer and compute).
+//
+// Every step is enqueued on the caller's stream.  Token and position live in
+// device memory, so one captured HIP graph replays unchanged for every
+// token; the argmax kernel writes the next token and advances the position.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "nt_internal.h"
+
+namespace nt {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+    size_t x, n, q, k, v, o, g, u, attn, total;
+};
+
+nt_attn_desc attn_of(const nt_model_config &c) {
+    nt_attn_desc a;
+    a.n_q_heads = c.n_q_heads;
+    a.n_kv_heads = c.n_kv_heads;
+    a.head_dim = c.head_dim;
+    a.ctx_cap = c.ctx_cap;
+    a.scale = 0.f;
+    return a;
+}
+
+Layout layout_of(const nt_model_config &c) {
+    Layout L{};
+    const size_t H = size_t(c.hidden), QD = size_t(c.n_q_heads) * c.head_dim,
+                 KD = size_t(c.n_kv_heads) * c.head_dim, F = size_t(c.ffn);
+    size_t off = 0;
+    auto take = [&](size_t bytes) { const size_t at = off; off += align_up(bytes); return at; };
+    L.x = take(4 * H);
+    L.n = take(4 * H);
+    L.q = take(4 * QD);
+    L.k = take(4 * KD);
+    L.v = take(4 * KD);
+    L.o = take(4 * QD);
+    L.g = take(4 * F);
+    L.u = take(4 * F);
+    L.attn = take(attn_workspace_bytes(attn_of(c)));
+    L.total = off;
+    return L;
+}
+
+bool config_ok(const nt_model_config &c, std::string &why) {
+    if (c.n_layers < 0 || c.hidden <= 0 || c.n_q_heads <= 0 || c.n_kv_heads <= 0 || c.head_dim <= 0 ||
+        c.ffn <= 0 || c.vocab <= 0 || c.ctx_cap <= 0) {
+        why = "sizes must be positive";
+        return false;
+    }
+    if (!attn_shape_ok(attn_of(c))) {
+        why = "need head_dim 64 or 128 and n_q_heads / n_kv_heads in {1, 2, 4, 8}";
+        return false;
+    }
+    if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f)) {
+        why = "need rms_eps >= 0 and rope_theta > 0";
+        return false;
+    }
+    return true;
+}
+
+bool tensor_ok(const nt_tensor_ref &t, int64_t cols, bool allow_null, std::string &why, const char *name) {
+    const nt_qtype q = nt_qtype(t.type);
+    if (!is_quant(q)) {
+        why = std::string(name) + ": unsupported weight type";
+        return false;
+    }
+    if (cols % block_elems(q) != 0 || cols > kMaxGemvCols) {
+        why = std::string(name) + ": column count is not a whole number of blocks (or above 65536)";
+        return false;
+    }
+    if (!t.data) {
+        if (allow_null) return true;
+        why = std::string(name) + ": null data";
+        return false;
+    }
+    if (!aligned(t.data, 16)) {
+        why = std::string(name) + ": data not 16-byte aligned";
+        return false;
+    }
+    return true;
+}
+
+const int kBlobOrder = 7;   // wq, wk, wv, wo, w_gate, w_up, w_down
+
+size_t matrix_bytes(const nt_model_config &c, int which, nt_qtype t) {
+    const int64_t H = c.hidden, QD = int64_t(c.n_q_heads) * c.head_dim, KD = int64_t(c.n_kv_heads) * c.head_dim,
+                  F = c.ffn;
+    int64_t rows = 0, cols = 0;
+    switch (which) {
+    case 0: rows = QD; cols = H; break;
+    case 1: case 2: rows = KD; cols = H; break;
+    case 3: rows = H; cols = QD; break;
+    case 4: case 5: rows = F; cols = H; break;
+    default: rows = H; cols = F; break;
+    }
+    return size_t(rows) * size_t(cols / block_elems(t) * block_bytes(t));
+}
+
+}  // namespace
+}  // namespace nt
+
+using namespace nt;
+
+struct nt_model {
+    nt_model_config cfg{};
+    nt_model_weights w{};
+    std::vector<nt_layer_weights> layers;
+    nt_attn_desc attn{};
+    Layout lay{};
+    uint8_t *ws = nullptr;
+
+    bool graph_enabled = true;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    const void *cap_args[4] = {nullptr, nullptr, nullptr, nullptr};
+    hipStream_t cap_stream = nullptr;
+
+    // host-streamed layers
+    bool streaming = false;
+    int32_t first_streamed = 0;
+    std::vector<const void *> blobs;
+    void *d_buf[2] = {nullptr, nullptr};
+    size_t blob_bytes = 0, blob_off[kBlobOrder] = {};
+    int32_t blob_types[kBlobOrder] = {};
+    hipStream_t copy_stream = nullptr;
+    hipEvent_t ready[2] = {nullptr, nullptr}, freed[2] = {nullptr, nullptr};
+    std::vector<hipEvent_t> copy_t0, copy_t1, comp_t0, comp_t1;
+    hipEvent_t step_t0 = nullptr, step_t1 = nullptr;
+    bool have_step = false;
+    uint64_t steps = 0, layers_streamed = 0, h2d_bytes = 0;
+
+    float *f(size_t off) const { return reinterpret_cast<float *>(ws + off); }
+    void drop_graph() {
+        if (exec) (void)hipGraphExecDestroy(exec);
+        if (graph) (void)hipGraphDestroy(graph);
+        exec = nullptr;
+        graph = nullptr;
+    }
+    void drop_events() {
+        auto kill = [](hipEvent_t &e) { if (e) (void)hipEventDestroy(e); e = nullptr; };
+        for (int b = 0; b < 2; ++b) { kill(ready[b]); kill(freed[b]); }
+        for (auto *v : {&copy_t0, &copy_t1, &comp_t0, &comp_t1}) {
+            for (auto &e : *v) kill(e);
+            v->clear();
+        }
+        kill(step_t0);
+        kill(step_t1);
+    }
+};
+
+namespace nt {
+namespace {
+
+#define NT_TRY(expr)                          \
+    do {                                      \
+        hipError_t e_ = (expr);               \
+        if (e_ != hipSuccess) return e_;      \
+    } while (0)
+
+// One transformer block.  mats[i] follow the blob order.
+hipError_t run_layer(nt_model *m, int l, const nt_tensor_ref *mats, const float *attn_norm, const float *ffn_norm,
+                     const int32_t *d_pos, hipStream_t st) {
+    const nt_model_config &c = m->cfg;
+    const int64_t H = c.hidden, QD = int64_t(c.n_q_heads) * c.head_dim, KD = int64_t(c.n_kv_heads) * c.head_dim;
+    float *x = m->f(m->lay.x), *n = m->f(m->lay.n), *q = m->f(m->lay.q), *k = m->f(m->lay.k);
+    float *v = m->f(m->lay.v), *o = m->f(m->lay.o), *g = m->f(m->lay.g), *u = m->f(m->lay.u);
+    const size_t layer_kv = size_t(c.n_kv_heads) * c.ctx_cap * c.head_dim;
+    uint16_t *kc = m->w.k_cache + l * layer_kv, *vc = m->w.v_cache + l * layer_kv;
+
+    NT_TRY(launch_rmsnorm(x, attn_norm, n, H, c.rms_eps, st));
+    NT_TRY(launch_gemv(nt_qtype(mats[0].type), mats[0].data, n, q, QD, H, 0, st));
+    NT_TRY(launch_gemv(nt_qtype(mats[1].type), mats[1].data, n, k, KD, H, 0, st));
+    NT_TRY(launch_gemv(nt_qtype(mats[2].type), mats[2].data, n, v, KD, H, 0, st));
+    NT_TRY(launch_rope(q, k, c.n_q_heads, c.n_kv_heads, c.head_dim, d_pos, c.rope_theta, st));
+    NT_TRY(launch_attn(m->attn, q, k, v, kc, vc, d_pos, o, m->ws + m->lay.attn, st));
+    NT_TRY(launch_gemv(nt_qtype(mats[3].type), mats[3].data, o, x, H, QD, 1, st));
+    NT_TRY(launch_rmsnorm(x, ffn_norm, n, H, c.rms_eps, st));
+    NT_TRY(launch_gemv(nt_qtype(mats[4].type), mats[4].data, n, g, c.ffn, H, 0, st));
+    NT_TRY(launch_gemv(nt_qtype(mats[5].type), mats[5].data, n, u, c.ffn, H, 0, st));
+    NT_TRY(launch_swiglu(g, u, g, c.ffn, st));
+    NT_TRY(launch_gemv(nt_qtype(mats[6].type), mats[6].data, g, x, H, c.ffn, 1, st));
+    return hipSuccess;
+}
+
+void resident_mats(const nt_layer_weights &L, nt_tensor_ref *mats) {
+    mats[0] = L.wq; mats[1] = L.wk; mats[2] = L.wv; mats[3] = L.wo;
+    mats[4] = L.w_gate; mats[5] = L.w_up; mats[6] = L.w_down;
+}
+
+hipError_t head(nt_model *m, int32_t *d_pos, float *logits, int32_t *d_next, hipStream_t st) {
+    const nt_model_config &c = m->cfg;
+    float *x = m->f(m->lay.x), *n = m->f(m->lay.n);
+    NT_TRY(launch_rmsnorm(x, m->w.output_norm, n, c.hidden, c.rms_eps, st));
+    NT_TRY(launch_gemv(nt_qtype(m->w.output.type), m->w.output.data, n, logits, c.vocab, c.hidden, 0, st));
+    NT_TRY(launch_argmax(logits, c.vocab, d_next, d_pos, st));
+    return hipSuccess;
+}
+
+hipError_t enqueue_resident(nt_model *m, const int32_t *d_token, int32_t *d_pos, float *logits, int32_t *d_next,
+                            hipStream_t st) {
+    const nt_model_config &c = m->cfg;
+    NT_TRY(launch_embed(nt_qtype(m->w.tok_embd.type), m->w.tok_embd.data, c.vocab, c.hidden, d_token,
+                        m->f(m->lay.x), st));
+    nt_tensor_ref mats[kBlobOrder];
+    for (int l = 0; l < c.n_layers; ++l) {
+        resident_mats(m->layers[l], mats);
+        NT_TRY(run_layer(m, l, mats, m->layers[l].attn_norm, m->layers[l].ffn_norm, d_pos, st));
+    }
+    return head(m, d_pos, logits, d_next, st);
+}
+
+hipError_t prefetch(nt_model *m, int s) {
+    const int b = s & 1;
+    NT_TRY(hipStreamWaitEvent(m->copy_stream, m->freed[b], 0));
+    NT_TRY(hipEventRecord(m->copy_t0[s], m->copy_stream));
+    NT_TRY(hipMemcpyAsync(m->d_buf[b], m->blobs[s], m->blob_bytes, hipMemcpyHostToDevice, m->copy_stream));
+    NT_TRY(hipEventRecord(m->copy_t1[s], m->copy_stream));
+    NT_TRY(hipEventRecord(m->ready[b], m->copy_stream));
+    return hipSuccess;
+}
+
+hipError_t enqueue_streamed(nt_model *m, const int32_t *d_token, int32_t *d_pos, float *logits, int32_t *d_next,
+                            hipStream_t st) {
+    const nt_model_config &c = m->cfg;
+    const int ns = c.n_layers - m->first_streamed;
+    NT_TRY(hipEventRecord(m->step_t0, st));
+    // the copy side stream must not run ahead of work already queued on the
+    // compute stream that still reads the staging buffers
+    if (ns > 0) NT_TRY(prefetch(m, 0));
+    if (ns > 1) NT_TRY(prefetch(m, 1));
+    NT_TRY(launch_embed(nt_qtype(m->w.tok_embd.type), m->w.tok_embd.data, c.vocab, c.hidden, d_token,
+                        m->f(m->lay.x), st));
+    nt_tensor_ref mats[kBlobOrder];
+    for (int l = 0; l < m->first_streamed; ++l) {
+        resident_mats(m->layers[l], mats);
+        NT_TRY(run_layer(m, l, mats, m->layers[l].attn_norm, m->layers[l].ffn_norm, d_pos, st));
+    }
+    for (int s = 0; s < ns; ++s) {
+        const int l = m->first_streamed + s, b = s & 1;
+        NT_TRY(hipStreamWaitEvent(st, m->ready[b], 0));
+        NT_TRY(hipEventRecord(m->comp_t0[s], st));
+        for (int i = 0; i < kBlobOrder; ++i) {
+            mats[i].type = m->blob_types[i];
+            mats[i].data = static_cast<const uint8_t *>(m->d_buf[b]) + m->blob_off[i];
+        }
+        NT_TRY(run_layer(m, l, mats, m->layers[l].attn_norm, m->layers[l].ffn_norm, d_pos, st));
+        NT_TRY(hipEventRecord(m->comp_t1[s], st));
+        NT_TRY(hipEventRecord(m->freed[b], st));
+        if (s + 2 < ns) NT_TRY(prefetch(m, s + 2));
+    }
+    NT_TRY(head(m, d_pos, logits, d_next, st));
+    NT_TRY(hipEventRecord(m->step_t1, st));
+    m->have_step = true;
+    m->steps += 1;
+    m->layers_streamed += uint64_t(ns);
+    m->h2d_bytes += uint64_t(ns) * m->blob_bytes;
+    return hipSuccess;
+}
+
+nt_status hip_fail(hipError_t e, const char *what) {
+    (void)hipGetLastError();
+    return fail(NT_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+nt_status device_present() {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        return fail(NT_ENODEV, "no HIP device available");
+    }
+    return NT_OK;
+}
+
+}  // namespace
+}  // namespace nt
+
+extern "C" {
+
+size_t nt_model_workspace_bytes(const nt_model_config *cfg) {
+    std::string why;
+    if (!cfg || !config_ok(*cfg, why)) return 0;
+    return layout_of(*cfg).total;
+}
+
+nt_status nt_layer_blob_layout(const nt_model_config *cfg, const int32_t types[7], size_t offsets[7],
+                               size_t *blob_bytes) {
+    set_error("");
+    std::string why;
+    if (!cfg || !types || !offsets || !blob_bytes) return fail(NT_EINVAL, "nt_layer_blob_layout: null pointer");
+    if (!config_ok(*cfg, why)) return fail(NT_ESHAPE, "nt_layer_blob_layout: " + why);
+    size_t off = 0;
+    for (int i = 0; i < kBlobOrder; ++i) {
+        const nt_qtype t = nt_qtype(types[i]);
+        if (!is_quant(t)) return fail(NT_EINVAL, "nt_layer_blob_layout: unsupported type");
+        const int64_t cols = (i == 3) ? int64_t(cfg->n_q_heads) * cfg->head_dim : (i == 6) ? cfg->ffn : cfg->hidden;
+        if (cols % block_elems(t) != 0) return fail(NT_ESHAPE, "nt_layer_blob_layout: columns not a whole number of blocks");
+        offsets[i] = off;
+        off += align_up(matrix_bytes(*cfg, i, t));
+    }
+    *blob_bytes = off;
+    return NT_OK;
+}
+
+nt_status nt_model_create(const nt_model_config *cfg, const nt_model_weights *w, nt_model **out) {
+    set_error("");
+    if (!cfg || !w || !out) return fail(NT_EINVAL, "nt_model_create: null pointer");
+    *out = nullptr;
+    std::string why;
+    if (!config_ok(*cfg, why)) return fail(NT_ESHAPE, "nt_model_create: " + why);
+    const int64_t H = cfg->hidden, QD = int64_t(cfg->n_q_heads) * cfg->head_dim, F = cfg->ffn;
+    if (!tensor_ok(w->tok_embd, H, false, why, "tok_embd") || !tensor_ok(w->output, H, false, why, "output"))
+        return fail(NT_ESHAPE, "nt_model_create: " + why);
+    if (!w->output_norm || !w->k_cache || !w->v_cache || !w->workspace || (cfg->n_layers > 0 && !w->layers))
+        return fail(NT_EINVAL, "nt_model_create: null pointer");
+    if (!aligned(w->k_cache, 16) || !aligned(w->v_cache, 16) || !aligned(w->workspace, kAlign) ||
+        !aligned(w->output_norm, 4))
+        return fail(NT_EALIGN, "nt_model_create: misaligned cache, workspace or gain");
+    const Layout lay = layout_of(*cfg);
+    if (w->workspace_bytes < lay.total) return fail(NT_ENOMEM, "nt_model_create: workspace too small");
+    for (int l = 0; l < cfg->n_layers; ++l) {
+        const nt_layer_weights &L = w->layers[l];
+        const nt_tensor_ref *mats[kBlobOrder] = {&L.wq, &L.wk, &L.wv, &L.wo, &L.w_gate, &L.w_up, &L.w_down};
+        const int64_t cols[kBlobOrder] = {H, H, H, QD, H, H, F};
+        const char *names[kBlobOrder] = {"wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"};
+        for (int i = 0; i < kBlobOrder; ++i)
+            if (!tensor_ok(*mats[i], cols[i], true, why, names[i]))
+                return fail(NT_ESHAPE, "nt_model_create: layer " + std::to_string(l) + " " + why);
+        if (!L.attn_norm || !L.ffn_norm) return fail(NT_EINVAL, "nt_model_create: null norm gain");
+    }
+    if (nt_status s = device_present()) return s;
+    nt_model *m = new nt_model();
+    m->cfg = *cfg;
+    m->w = *w;
+    m->layers.assign(w->layers, w->layers + cfg->n_layers);
+    m->w.layers = nullptr;
+    m->attn = attn_of(*cfg);
+    m->lay = lay;
+    m->ws = static_cast<uint8_t *>(w->workspace);
+    *out = m;
+    return NT_OK;
+}
+
+void nt_model_destroy(nt_model *m) {
+    if (!m) return;
+    m->drop_graph();
+    m->drop_events();
+    delete m;
+}
+
+nt_status nt_model_set_graph(nt_model *m, int enable) {
+    set_error("");
+    if (!m) return fail(NT_EINVAL, "nt_model_set_graph: null model");
+    m->graph_enabled = enable != 0;
+    if (!m->graph_enabled) m->drop_graph();
+    return NT_OK;
+}
+
+nt_status nt_decode_step(nt_model *m, const int32_t *d_token, int32_t *d_pos, float *logits, int32_t *d_next,
+                         nt_stream stream) {
+    set_error("");
+    if (!m || !d_token || !d_pos || !logits || !d_next) return fail(NT_EINVAL, "nt_decode_step: null pointer");
+    if (!aligned(d_token, 4) || !aligned(d_pos, 4) || !aligned(d_next, 4) || !aligned(logits, 4))
+        return fail(NT_EALIGN, "nt_decode_step: misaligned pointer");
+    hipStream_t st = as_stream(stream);
+    if (m->streaming) {
+        hipError_t e = enqueue_streamed(m, d_token, d_pos, logits, d_next, st);
+        return e == hipSuccess ? NT_OK : hip_fail(e, "nt_decode_step (streamed)");
+    }
+    for (int l = 0; l < m->cfg.n_layers; ++l) {
+        const nt_layer_weights &L = m->layers[l];
+        if (!L.wq.data || !L.wk.data || !L.wv.data || !L.wo.data || !L.w_gate.data || !L.w_up.data || !L.w_down.data)
+            return fail(NT_ESTATE, "nt_decode_step: layer " + std::to_string(l) +
+                                       " has no resident weights and streaming is off");
+    }
+    if (!m->graph_enabled || st == nullptr) {
+        hipError_t e = enqueue_resident(m, d_token, d_pos, logits, d_next, st);
+        return e == hipSuccess ? NT_OK : hip_fail(e, "nt_decode_step");
+    }
+    const void *args[4] = {d_token, d_pos, logits, d_next};
+    if (!m->exec || m->cap_stream != st || std::memcmp(args, m->cap_args, sizeof(args)) != 0) {
+        m->drop_graph();
+        hipError_t e = hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal);
+        if (e != hipSuccess) return hip_fail(e, "nt_decode_step: begin capture");
+        hipError_t e2 = enqueue_resident(m, d_token, d_pos, logits, d_next, st);
+        hipGraph_t g = nullptr;
+        e = hipStreamEndCapture(st, &g);
+        if (e2 != hipSuccess || e != hipSuccess) {
+            if (g) (void)hipGraphDestroy(g);
+            return hip_fail(e2 != hipSuccess ? e2 : e, "nt_decode_step: capture");
+        }
+        m->graph = g;
+        e = hipGraphInstantiate(&m->exec, g, nullptr, nullptr, 0);
+        if (e != hipSuccess) {
+            m->drop_graph();
+            return hip_fail(e, "nt_decode_step: instantiate");
+        }
+        std::memcpy(m->cap_args, args, sizeof(args));
+        m->cap_stream = st;
+    }
+    hipError_t e = hipGraphLaunch(m->exec, st);
+    return e == hipSuccess ? NT_OK : hip_fail(e, "nt_decode_step: graph launch");
+}
+
+nt_status nt_stream_layers(nt_model *m, const nt_stream_desc *d) {
+    set_error("");
+    if (!m) return fail(NT_EINVAL, "nt_stream_layers: null model");
+    if (!d) {
+        if (m->streaming) (void)hipStreamSynchronize(m->copy_stream);
+        m->streaming = false;
+        m->drop_events();
+        return NT_OK;
+    }
+    const nt_model_config &c = m->cfg;
+    if (d->first_streamed_layer < 0 || d->first_streamed_layer > c.n_layers)
+        return fail(NT_EINVAL, "nt_stream_layers: first_streamed_layer out of range");
+    const int ns = c.n_layers - d->first_streamed_layer;
+    if (ns > 0 && (!d->h_layer_blobs || !d->d_buf[0] || !d->d_buf[1] || !d->copy_stream))
+        return fail(NT_EINVAL, "nt_stream_layers: null pointer");
+    for (int l = 0; l < d->first_streamed_layer; ++l) {
+        const nt_layer_weights &L = m->layers[l];
+        if (!L.wq.data || !L.wk.data || !L.wv.data || !L.wo.data || !L.w_gate.data || !L.w_up.data || !L.w_down.data)
+            return fail(NT_ESTATE, "nt_stream_layers: resident layer " + std::to_string(l) + " has no weights");
+    }
+    int32_t types[kBlobOrder] = {};
+    size_t offs[kBlobOrder] = {}, bytes = 0;
+    if (ns > 0) {
+        const nt_layer_weights &F0 = m->layers[d->first_streamed_layer];
+        const nt_tensor_ref *mats0[kBlobOrder] = {&F0.wq, &F0.wk, &F0.wv, &F0.wo, &F0.w_gate, &F0.w_up, &F0.w_down};
+        for (int i = 0; i < kBlobOrder; ++i) types[i] = mats0[i]->type;
+        for (int s = 1; s < ns; ++s) {
+            const nt_layer_weights &L = m->layers[d->first_streamed_layer + s];
+            const nt_tensor_ref *mats[kBlobOrder] = {&L.wq, &L.wk, &L.wv, &L.wo, &L.w_gate, &L.w_up, &L.w_down};
+            for (int i = 0; i < kBlobOrder; ++i)
+                if (mats[i]->type != types[i])
+                    return fail(NT_ESHAPE, "nt_stream_layers: streamed layers must share matrix types");
+        }
+        if (nt_status s = nt_layer_blob_layout(&c, types, offs, &bytes)) return s;
+        if (d->buf_bytes < bytes) return fail(NT_ENOMEM, "nt_stream_layers: staging buffers smaller than a blob");
+        if (!aligned(d->d_buf[0], kAlign) || !aligned(d->d_buf[1], kAlign))
+            return fail(NT_EALIGN, "nt_stream_layers: staging buffers must be 256-byte aligned");
+        for (int s = 0; s < ns; ++s) {
+            const void *h = d->h_layer_blobs[s];
+            if (!h) return fail(NT_EINVAL, "nt_stream_layers: null blob");
+            hipPointerAttribute_t attr;
+            if (hipPointerGetAttributes(&attr, h) != hipSuccess || attr.type != hipMemoryTypeHost) {
+                (void)hipGetLastError();
+                return fail(NT_ESTATE, "nt_stream_layers: blob " + std::to_string(s) + " is not pinned host memory");
+            }
+        }
+    }
+    if (nt_status s = device_present()) return s;
+    if (m->streaming) (void)hipStreamSynchronize(m->copy_stream);
+    m->drop_events();
+    m->drop_graph();
+    auto mk = [](hipEvent_t *e) { return hipEventCreate(e); };
+    hipError_t e = hipSuccess;
+    for (int b = 0; b < 2 && e == hipSuccess; ++b) {
+        e = mk(&m->ready[b]);
+        if (e == hipSuccess) e = mk(&m->freed[b]);
+    }
+    m->copy_t0.assign(size_t(ns), nullptr);
+    m->copy_t1.assign(size_t(ns), nullptr);
+    m->comp_t0.assign(size_t(ns), nullptr);
+    m->comp_t1.assign(size_t(ns), nullptr);
+    for (int s = 0; s < ns && e == hipSuccess; ++s) {
+        e = mk(&m->copy_t0[s]);
+        if (e == hipSuccess) e = mk(&m->copy_t1[s]);
+        if (e == hipSuccess) e = mk(&m->comp_t0[s]);
+        if (e == hipSuccess) e = mk(&m->comp_t1[s]);
+    }
+    if (e == hipSuccess) e = mk(&m->step_t0);
+    if (e == hipSuccess) e = mk(&m->step_t1);
+    if (e != hipSuccess) {
+        m->drop_events();
+        return hip_fail(e, "nt_stream_layers: event creation");
+    }
+    m->first_streamed = d->first_streamed_layer;
+    m->blobs.assign(d->h_layer_blobs, d->h_layer_blobs + ns);
+    m->d_buf[0] = d->d_buf[0];
+    m->d_buf[1] = d->d_buf[1];
+    m->blob_bytes = bytes;
+    std::memcpy(m->blob_off, offs, sizeof(offs));
+    std::memcpy(m->blob_types, types, sizeof(types));
+    m->copy_stream = as_stream(d->copy_stream);
+    m->streaming = true;
+    m->have_step = false;
+    m->steps = m->layers_streamed = m->h2d_bytes = 0;
+    return NT_OK;
+}
+
+nt_status nt_stream_stats_get(nt_model *m, nt_stream_stats *out) {
+    set_error("");
+    if (!m || !out) return fail(NT_EINVAL, "nt_stream_stats_get: null pointer");
+    std::memset(out, 0, sizeof(*out));
+    if (!m->streaming) return fail(NT_ESTATE, "nt_stream_stats_get: streaming is off");
+    out->steps = m->steps;
+    out->layers_streamed = m->layers_streamed;
+    out->h2d_bytes = m->h2d_bytes;
+    if (!m->have_step) return NT_OK;
+    hipError_t e = hipEventSynchronize(m->step_t1);
+    if (e != hipSuccess) return hip_fail(e, "nt_stream_stats_get");
+    float ms = 0.f;
+    double copy = 0.0, comp = 0.0;
+    for (size_t s = 0; s < m->copy_t0.size(); ++s) {
+        if (hipEventElapsedTime(&ms, m->copy_t0[s], m->copy_t1[s]) == hipSuccess) copy += ms;
+        if (hipEventElapsedTime(&ms, m->comp_t0[s], m->comp_t1[s]) == hipSuccess) comp += ms;
+    }
+    (void)hipGetLastError();
+    out->copy_ms = copy;
+    out->compute_ms = comp;
+    if (hipEventElapsedTime(&ms, m->step_t0, m->step_t1) == hipSuccess) out->wall_ms = ms;
+    (void)hipGetLastError();
+    return NT_OK;
+}
+
+}  // extern "C"

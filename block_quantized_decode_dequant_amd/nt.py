@@ -231,3 +231,150 @@ def nt_attn_decode(desc: AttnDesc, q, k_new, v_new, k_cache, v_cache, d_pos, out
                                 _ptr(k_cache, cache, "k_cache"), _ptr(v_cache, cache, "v_cache"),
                                 _ptr(d_pos, 4, "d_pos"), _ptr(out, 4 * desc.n_q_heads * desc.head_dim, "out"),
                                 _ptr(workspace, 0, "workspace"), ws_bytes, _stream(stream)), "nt_attn_decode")
+
+
+# ---- decode step and streamed layers ------------------------------------------------
+class ModelConfig(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("hidden", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32),
+                ("vocab", C.c_int32), ("ctx_cap", C.c_int32), ("rms_eps", C.c_float),
+                ("rope_theta", C.c_float)]
+
+
+class TensorRef(C.Structure):
+    _fields_ = [("type", C.c_int32), ("data", C.c_void_p)]
+
+
+class LayerWeights(C.Structure):
+    _fields_ = [("attn_norm", C.c_void_p), ("wq", TensorRef), ("wk", TensorRef), ("wv", TensorRef),
+                ("wo", TensorRef), ("ffn_norm", C.c_void_p), ("w_gate", TensorRef),
+                ("w_up", TensorRef), ("w_down", TensorRef)]
+
+
+class ModelWeights(C.Structure):
+    _fields_ = [("tok_embd", TensorRef), ("output_norm", C.c_void_p), ("output", TensorRef),
+                ("layers", C.POINTER(LayerWeights)), ("k_cache", C.c_void_p), ("v_cache", C.c_void_p),
+                ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
+
+
+class StreamDesc(C.Structure):
+    _fields_ = [("first_streamed_layer", C.c_int32), ("h_layer_blobs", C.POINTER(C.c_void_p)),
+                ("d_buf", C.c_void_p * 2), ("buf_bytes", C.c_size_t), ("copy_stream", C.c_void_p)]
+
+
+class StreamStats(C.Structure):
+    _fields_ = [("steps", C.c_uint64), ("layers_streamed", C.c_uint64), ("h2d_bytes", C.c_uint64),
+                ("copy_ms", C.c_double), ("compute_ms", C.c_double), ("wall_ms", C.c_double)]
+
+
+def _declare_model(L):
+    vp, st = C.c_void_p, C.c_int
+    sig = {
+        "nt_model_workspace_bytes": (C.c_size_t, [C.POINTER(ModelConfig)]),
+        "nt_model_create": (st, [C.POINTER(ModelConfig), C.POINTER(ModelWeights), C.POINTER(vp)]),
+        "nt_model_destroy": (None, [vp]),
+        "nt_model_set_graph": (st, [vp, C.c_int]),
+        "nt_decode_step": (st, [vp, vp, vp, vp, vp, vp]),
+        "nt_layer_blob_layout": (st, [C.POINTER(ModelConfig), C.POINTER(C.c_int32), C.POINTER(C.c_size_t),
+                                      C.POINTER(C.c_size_t)]),
+        "nt_stream_layers": (st, [vp, C.POINTER(StreamDesc)]),
+        "nt_stream_stats_get": (st, [vp, C.POINTER(StreamStats)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+
+
+def model_config(n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, ctx_cap,
+                 rms_eps=1e-5, rope_theta=500000.0) -> ModelConfig:
+    return ModelConfig(n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, ctx_cap,
+                       rms_eps, rope_theta)
+
+
+def nt_model_workspace_bytes(cfg: ModelConfig) -> int:
+    _declare_model(lib())
+    return lib().nt_model_workspace_bytes(C.byref(cfg))
+
+
+def nt_layer_blob_layout(cfg: ModelConfig, types):
+    _declare_model(lib())
+    t = (C.c_int32 * 7)(*types)
+    offs = (C.c_size_t * 7)()
+    nb = C.c_size_t(0)
+    _check(lib().nt_layer_blob_layout(C.byref(cfg), t, offs, C.byref(nb)), "nt_layer_blob_layout")
+    return list(offs), int(nb.value)
+
+
+class Model:
+    """Owns an nt_model handle; keeps the tensors it points at alive.
+
+    weights: dict with tok_embd, output (each (qtype, uint8 tensor)), output_norm
+    (fp32 tensor) and layers: list of dicts with attn_norm, ffn_norm (fp32) and
+    wq, wk, wv, wo, w_gate, w_up, w_down ((qtype, uint8 tensor) or (qtype, None)).
+    """
+
+    MATS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+
+    def __init__(self, cfg: ModelConfig, weights: dict, k_cache, v_cache, workspace):
+        L = lib()
+        _declare_model(L)
+        self.cfg = cfg
+        self._keep = [weights, k_cache, v_cache, workspace]
+
+        def ref(pair):
+            t, tensor = pair
+            return TensorRef(t, None if tensor is None else _ptr(tensor, 0, "weight").value)
+
+        layers = (LayerWeights * cfg.n_layers)()
+        for i, lw in enumerate(weights["layers"]):
+            layers[i] = LayerWeights(_ptr(lw["attn_norm"], 4 * cfg.hidden).value, ref(lw["wq"]), ref(lw["wk"]),
+                                     ref(lw["wv"]), ref(lw["wo"]), _ptr(lw["ffn_norm"], 4 * cfg.hidden).value,
+                                     ref(lw["w_gate"]), ref(lw["w_up"]), ref(lw["w_down"]))
+        self._layers = layers
+        kv = 2 * cfg.n_layers * cfg.n_kv_heads * cfg.ctx_cap * cfg.head_dim
+        ws_bytes = workspace.numel() * workspace.element_size()
+        w = ModelWeights(ref(weights["tok_embd"]), _ptr(weights["output_norm"], 4 * cfg.hidden).value,
+                         ref(weights["output"]), layers, _ptr(k_cache, kv, "k_cache").value,
+                         _ptr(v_cache, kv, "v_cache").value, _ptr(workspace, 0, "workspace").value, ws_bytes)
+        h = C.c_void_p()
+        _check(L.nt_model_create(C.byref(cfg), C.byref(w), C.byref(h)), "nt_model_create")
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None) and self.handle.value:
+            lib().nt_model_destroy(self.handle)
+            self.handle = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_graph(self, enable: bool):
+        _check(lib().nt_model_set_graph(self.handle, int(bool(enable))), "nt_model_set_graph")
+
+    def step(self, d_token, d_pos, logits, d_next, stream=None):
+        _check(lib().nt_decode_step(self.handle, _ptr(d_token, 4, "d_token"), _ptr(d_pos, 4, "d_pos"),
+                                    _ptr(logits, 4 * self.cfg.vocab, "logits"), _ptr(d_next, 4, "d_next"),
+                                    _stream(stream)), "nt_decode_step")
+
+    def stream_layers(self, first_streamed: int, host_blobs, d_buf0, d_buf1, copy_stream):
+        """host_blobs: list of pinned host uint8 tensors (one per streamed layer)."""
+        if host_blobs is None:
+            _check(lib().nt_stream_layers(self.handle, None), "nt_stream_layers")
+            return
+        n = len(host_blobs)
+        arr = (C.c_void_p * max(n, 1))(*[b.data_ptr() for b in host_blobs])
+        self._stream_keep = [host_blobs, d_buf0, d_buf1, arr, copy_stream]
+        bufs = (C.c_void_p * 2)(d_buf0.data_ptr(), d_buf1.data_ptr())
+        nbytes = min(d_buf0.numel(), d_buf1.numel()) * d_buf0.element_size()
+        desc = StreamDesc(first_streamed, C.cast(arr, C.POINTER(C.c_void_p)), bufs, nbytes,
+                          _stream(copy_stream))
+        _check(lib().nt_stream_layers(self.handle, C.byref(desc)), "nt_stream_layers")
+
+    def stream_stats(self) -> dict:
+        s = StreamStats()
+        _check(lib().nt_stream_stats_get(self.handle, C.byref(s)), "nt_stream_stats_get")
+        return {k: getattr(s, k) for k, _ in StreamStats._fields_}

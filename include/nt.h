@@ -168,6 +168,94 @@ nt_status nt_attn_decode(const nt_attn_desc *desc, const float *q, const float *
                          uint16_t *k_cache, uint16_t *v_cache, const int32_t *d_pos, float *out,
                          void *workspace, size_t workspace_bytes, nt_stream stream);
 
+/* ---- one batch-1 Llama decode step ("Main features": RoPE, GQA, SwiGLU,
+ * RMSNorm, KV cache; "Architecture": engine, sampler) ------------------------
+ * Per token, with pos = *d_pos and x the residual stream:
+ *   x = row *d_token of tok_embd
+ *   per layer: n = RMSNorm(x, attn_norm); q = Wq n, k = Wk n, v = Wv n;
+ *              RoPE(q, k, pos); store k, v (fp16) at slot pos; o = Attn(q);
+ *              x += Wo o; m = RMSNorm(x, ffn_norm); x += Wdown (silu(Wgate m) * Wup m)
+ *   logits = Woutput RMSNorm(x, output_norm); *d_next = argmax(logits); ++*d_pos
+ * Weight matrices are packed row-major blocks (any of the four formats, per
+ * tensor); norm gains are fp32.  All pointers are device memory owned by the
+ * caller and must outlive the model.  The model holds only host state, HIP
+ * events and (when enabled) a captured HIP graph. */
+typedef struct {
+    int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, ctx_cap;
+    float rms_eps, rope_theta;
+} nt_model_config;
+
+typedef struct {
+    int32_t type;          /* nt_qtype */
+    const void *data;      /* device, 16-byte aligned packed blocks */
+} nt_tensor_ref;
+
+typedef struct {
+    const float *attn_norm;                    /* fp32[hidden] */
+    nt_tensor_ref wq, wk, wv;                  /* [n_q_heads*head_dim | n_kv_heads*head_dim] x hidden */
+    nt_tensor_ref wo;                          /* hidden x n_q_heads*head_dim */
+    const float *ffn_norm;                     /* fp32[hidden] */
+    nt_tensor_ref w_gate, w_up;                /* ffn x hidden */
+    nt_tensor_ref w_down;                      /* hidden x ffn */
+} nt_layer_weights;
+
+typedef struct {
+    nt_tensor_ref tok_embd;                    /* vocab x hidden */
+    const float *output_norm;                  /* fp32[hidden] */
+    nt_tensor_ref output;                      /* vocab x hidden */
+    const nt_layer_weights *layers;            /* host array of n_layers entries, copied */
+    uint16_t *k_cache, *v_cache;               /* fp16 bits [n_layers][n_kv_heads][ctx_cap][head_dim] */
+    void *workspace;                           /* >= nt_model_workspace_bytes(cfg), 256-byte aligned */
+    size_t workspace_bytes;
+} nt_model_weights;
+
+typedef struct nt_model nt_model;
+
+/* Scratch the step needs (activations and attention partials); 0 if cfg is invalid. */
+size_t nt_model_workspace_bytes(const nt_model_config *cfg);
+/* Validates shapes (head_dim 64 or 128; n_q_heads / n_kv_heads in {1,2,4,8};
+ * every matrix's column count a whole number of its blocks) and pointers.
+ * Layer matrices may be NULL only for layers later served by nt_stream_layers. */
+nt_status nt_model_create(const nt_model_config *cfg, const nt_model_weights *w, nt_model **out);
+void      nt_model_destroy(nt_model *m);
+/* enable != 0 (the default): the first resident step on a stream is captured
+ * into a HIP graph that later steps replay (re-captured when the pointer
+ * arguments change).  Steps on the NULL stream always run eagerly. */
+nt_status nt_model_set_graph(nt_model *m, int enable);
+/* Enqueues one decode step on `stream`.  d_token, d_pos: device int32
+ * (d_next may equal d_token); logits: device fp32[vocab]. */
+nt_status nt_decode_step(nt_model *m, const int32_t *d_token, int32_t *d_pos, float *logits,
+                         int32_t *d_next, nt_stream stream);
+
+/* ---- host-streamed layers ("Performance": 3-tier cache with VRAM-resident
+ * layers and pinned-RAM layers copied host-to-device; "Main features":
+ * double-buffered streaming that overlaps transfer and compute) -------------
+ * A layer blob packs one layer's seven matrices back to back in the order
+ * wq, wk, wv, wo, w_gate, w_up, w_down, each starting on a 256-byte boundary;
+ * types[7] gives their formats. */
+nt_status nt_layer_blob_layout(const nt_model_config *cfg, const int32_t types[7], size_t offsets[7],
+                               size_t *blob_bytes);
+typedef struct {
+    int32_t first_streamed_layer;              /* layers [first, n_layers) are streamed */
+    const void *const *h_layer_blobs;          /* host array: one pinned blob per streamed layer */
+    void *d_buf[2];                            /* device staging buffers, each >= buf_bytes */
+    size_t buf_bytes;                          /* >= the blob size */
+    nt_stream copy_stream;                     /* side stream for host-to-device copies */
+} nt_stream_desc;
+/* Streamed layers take their matrix types from the model's layer weights of
+ * the first streamed layer (all streamed layers must share them).  Each step
+ * then copies blob j into d_buf[j % 2] on copy_stream, and layer j waits for
+ * its copy while the next blob is already in flight.  desc == NULL returns
+ * to fully resident operation (all layer matrices must then be set). */
+nt_status nt_stream_layers(nt_model *m, const nt_stream_desc *desc);
+typedef struct {
+    uint64_t steps, layers_streamed, h2d_bytes;  /* totals since streaming was enabled */
+    double copy_ms, compute_ms, wall_ms;         /* last step: copy-stream busy time, time
+                                                    of the streamed layers' compute, step wall */
+} nt_stream_stats;
+/* Waits for the last step, then reports. */
+nt_status nt_stream_stats_get(nt_model *m, nt_stream_stats *out);
+
 /* ---- encode (quantize) -------------------------------------------------------
  * blocks <- encoding of x[0, n) (device fp32, 4-byte aligned) into packed
  * blocks (device, 16-byte aligned, n / block_elems * block_bytes bytes).
