@@ -13,9 +13,15 @@ kernel with the most time in the timed region gives the `roofline` object.
 The CPU baseline times the oracle (plain fp64 C, test-side code) on a bounded
 sample of the same workload: the first rows of each matrix.
 
+Decode measurements ride along in the same JSON line ("decode"): the
+Llama-3-8B-shaped Q8_0 model (128 greedy tokens from position 1024), the
+Llama-70B-shaped Q4_K/Q6_K model (64 tokens from 4096), each replayed from a
+captured HIP graph, and the 70B all-Q6_K model with 24 GiB of layers resident
+and the rest streamed from pinned host RAM, each as tok/s against the
+weight-bytes / 8 TB/s bound (or the measured pinned H2D rate).
+
 Flags: --gpus N (only 1 is supported: this path runs on one GPU),
---steps K, --warmup W, --no-cpu-baseline, --decode (also time the
-Llama-8B-shaped decode, when the library provides it).
+--steps K, --warmup W, --no-cpu-baseline, --decode none|8b|all.
 """
 from __future__ import annotations
 
@@ -42,7 +48,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--decode", action="store_true")
+    ap.add_argument("--decode", choices=["none", "8b", "all"], default="all",
+                    help="decode measurements: none, the 8B-shaped model, or all (8B, 70B, 70B streamed)")
+    ap.add_argument("--stream-tokens", type=int, default=3)
     return ap.parse_args()
 
 
@@ -138,24 +146,27 @@ def run_gpu(args):
     ms_per_step = wall / args.steps * 1e3
     value = step_bytes / (wall / args.steps) / 1e9
 
-    # Per-kernel durations, measured live: the same steps launched directly,
-    # queued behind a short delay kernel so that every launch is already
-    # waiting on the stream and each event pair brackets one kernel.
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in cases] for _ in range(args.steps)]
+    # Per-kernel durations, measured live: each case launched back to back
+    # `steps` times (rotating weight copies) between one pair of events, all
+    # queued behind a short delay kernel so the GPU never waits for the host.
+    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in cases]
     torch.cuda.synchronize()
-    nt.nt_delay(min(1e6, 2000.0 + 400.0 * args.steps))
-    for s in range(args.steps):
-        step(s, ev[s])
+    nt.nt_delay(min(1e6, 2000.0 + 300.0 * args.steps))
+    for j, c in enumerate(cases):
+        ev[j][0].record()
+        for s_ in range(args.steps):
+            nt.nt_gemv(c["qt"], c["W"][s_ % copies], c["x"], c["y"], c["rows"], c["cols"])
+        ev[j][1].record()
     torch.cuda.synchronize()
-    per_case_ms = [sum(ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)) / args.steps
-                   for j in range(len(cases))]
-    span_ms = ev[0][0][0].elapsed_time(ev[-1][-1][1]) / args.steps
+    per_case_ms = [ev[j][0].elapsed_time(ev[j][1]) / args.steps for j in range(len(cases))]
+    span_ms = ev[0][0].elapsed_time(ev[-1][1]) / args.steps
 
-    # per-kernel (one kernel per block type) totals
+    # per-kernel totals; a kernel is one instantiation (block type, path, tile
+    # rows), as the library reports it, which is what rocprofv3 lists by name
     kern = {}
     for c, ms in zip(cases, per_case_ms):
-        k = f"gemv {c['type']}"
+        li = nt.nt_gemv_launch_info(c["qt"], c["rows"], c["cols"])
+        k = f"gemv {c['type']} {'fast' if li['fast'] else 'generic'} tile{li['tile_rows']}"
         a = kern.setdefault(k, dict(bytes=0, ms=0.0, launches=0))
         a["bytes"] += c["bytes"]
         a["ms"] += ms
@@ -169,6 +180,7 @@ def run_gpu(args):
                 "kernel": dom, "bytes_per_launch": d["bytes"] // d["launches"],
                 "avg_launch_us": round(d["ms"] / d["launches"] * 1e3, 3)}
     detail = [dict(type=c["type"], rows=c["rows"], cols=c["cols"], bytes=c["bytes"],
+                   launch=nt.nt_gemv_launch_info(c["qt"], c["rows"], c["cols"]),
                    us=round(ms * 1e3, 3), gbs=round(c["bytes"] / (ms * 1e-3) / 1e9, 1),
                    frac=round(c["bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
               for c, ms in zip(cases, per_case_ms)]
@@ -178,6 +190,133 @@ def run_gpu(args):
     torch.cuda.empty_cache()
     return dict(value=value, ms_per_step=ms_per_step, roofline=roofline, detail=detail,
                 copies=copies, step_bytes=step_bytes, queued_step_ms=span_ms)
+
+
+def time_decode(model, shape, n_tokens, warmup=8):
+    import torch
+    dev = torch.device("cuda:0")
+    side = torch.cuda.Stream()
+    d_tok = torch.tensor([1], dtype=torch.int32, device=dev)
+    d_pos = torch.tensor([shape.ctx], dtype=torch.int32, device=dev)
+    logits = torch.empty(shape.vocab, dtype=torch.float32, device=dev)
+
+    def run(n):
+        with torch.cuda.stream(side):
+            for _ in range(n):
+                model.step(d_tok, d_pos, logits, d_tok)
+
+    run(warmup)
+    torch.cuda.synchronize()
+    d_pos.fill_(shape.ctx)
+    d_tok.fill_(1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(n_tokens)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert int(d_pos.item()) == shape.ctx + n_tokens
+    return wall
+
+
+def decode_resident(shape):
+    import torch
+
+    from block_quantized_decode_dequant_amd import devmodel
+
+    t0 = time.perf_counter()
+    model, extra = devmodel.build(shape)
+    torch.cuda.synchronize()
+    build_s = time.perf_counter() - t0
+    wall = time_decode(model, shape, shape.n_tokens)
+    tps = shape.n_tokens / wall
+    wbytes = devmodel.weight_bytes_per_token(shape)
+    kv_mid = devmodel.kv_bytes_per_token(shape, shape.ctx + shape.n_tokens // 2)
+    bound = PEAK_HBM_GBS * 1e9 / wbytes
+    bound_kv = PEAK_HBM_GBS * 1e9 / (wbytes + kv_mid)
+    out = {"tok_s": round(tps, 2), "ms_per_token": round(wall / shape.n_tokens * 1e3, 4),
+           "tokens": shape.n_tokens, "start_pos": shape.ctx, "weight_bytes_per_token": wbytes,
+           "bound_tok_s": round(bound, 1), "frac_of_bound": round(tps / bound, 4),
+           "bound_with_kv_tok_s": round(bound_kv, 1), "frac_of_bound_with_kv": round(tps / bound_kv, 4),
+           "achieved_gbs": round((wbytes + kv_mid) * tps / 1e9, 1), "graph": True,
+           "build_s": round(build_s, 1)}
+    model.close()
+    del model, extra
+    torch.cuda.empty_cache()
+    return out
+
+
+def pinned_h2d_ceiling(nbytes=1 << 30, reps=5):
+    import torch
+    h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    d = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    best = 0.0
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        d.copy_(h, non_blocking=True)
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (time.perf_counter() - t0) / 1e9)
+    del h, d
+    return best
+
+
+def decode_streamed(shape, cap_bytes=24 << 30, n_tokens=3):
+    import torch
+
+    from block_quantized_decode_dequant_amd import devmodel, nt
+
+    types = devmodel.tensor_types(shape.weights)
+    cfg = nt.model_config(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                          shape.ffn, shape.vocab, shape.ctx_cap, shape.rms_eps, shape.rope_theta)
+    _, blob = nt.nt_layer_blob_layout(cfg, [types[n] for n in devmodel.MATS])
+    first = min(shape.n_layers, cap_bytes // blob)
+    ceiling = pinned_h2d_ceiling()
+    t0 = time.perf_counter()
+    model, extra = devmodel.build(shape, streamed_from=first)
+    blobs, nbytes = devmodel.fill_streamed_blobs(shape, first)
+    build_s = time.perf_counter() - t0
+    dev = torch.device("cuda:0")
+    dbuf = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(2)]
+    copy_stream = torch.cuda.Stream()
+    model.stream_layers(first, blobs, dbuf[0], dbuf[1], copy_stream)
+    d_tok = torch.tensor([1], dtype=torch.int32, device=dev)
+    d_pos = torch.tensor([shape.ctx], dtype=torch.int32, device=dev)
+    logits = torch.empty(shape.vocab, dtype=torch.float32, device=dev)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        model.step(d_tok, d_pos, logits, d_tok)           # warm-up token
+    torch.cuda.synchronize()
+    walls, copies, comps = [], [], []
+    t0 = time.perf_counter()
+    for _ in range(n_tokens):
+        with torch.cuda.stream(side):
+            model.step(d_tok, d_pos, logits, d_tok)
+        st = model.stream_stats()
+        walls.append(st["wall_ms"])
+        copies.append(st["copy_ms"])
+        comps.append(st["compute_ms"])
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    ns = shape.n_layers - first
+    h2d = ns * nbytes
+    copy_ms, comp_ms, wall_ms = (sum(v) / len(v) for v in (copies, comps, walls))
+    out = {"resident_layers": int(first), "streamed_layers": int(ns), "blob_bytes": int(nbytes),
+           "h2d_bytes_per_token": int(h2d), "tok_s": round(n_tokens / total, 3),
+           "ms_per_token": round(total / n_tokens * 1e3, 2),
+           "h2d_gbs": round(h2d / (copy_ms * 1e-3) / 1e9, 2),
+           "h2d_gbs_wall": round(h2d / (wall_ms * 1e-3) / 1e9, 2),
+           "pinned_h2d_ceiling_gbs": round(ceiling, 2),
+           "frac_of_h2d_ceiling": round(h2d / (copy_ms * 1e-3) / 1e9 / ceiling, 4),
+           "bound_tok_s": round(ceiling * 1e9 / h2d, 3),
+           "copy_ms": round(copy_ms, 2), "streamed_compute_ms": round(comp_ms, 2), "wall_ms": round(wall_ms, 2),
+           "compute_hidden_frac": round(max(0.0, min(1.0, (copy_ms + comp_ms - wall_ms) / comp_ms)), 4)
+           if comp_ms > 0 else None,
+           "tokens": n_tokens, "cap_bytes": int(cap_bytes), "build_s": round(build_s, 1)}
+    model.stream_layers(None, None, None, None, None)
+    model.close()
+    del model, extra, blobs, dbuf
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(seconds: float):
@@ -243,6 +382,13 @@ def main():
         "roofline": g["roofline"],
         "detail": g["detail"],
     }
+    if args.decode != "none":
+        dec = {"llama3_8b_q8_0": decode_resident(workloads.LLAMA_8B_Q8_0)}
+        if args.decode == "all":
+            dec["llama70b_q4_k_q6_k"] = decode_resident(workloads.LLAMA_70B_MIX)
+            dec["llama70b_q6_k_streamed_24gib"] = decode_streamed(workloads.LLAMA_70B_Q6K,
+                                                                  n_tokens=args.stream_tokens)
+        line["decode"] = dec
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -151,6 +151,16 @@ nt_status nt_gemv(nt_qtype t, const void *W, const float *x, float *y, int64_t r
     return finish(launch_gemv(t, W, x, y, rows, cols, accumulate, as_stream(stream)), "nt_gemv");
 }
 
+nt_status nt_gemv_launch_info(nt_qtype t, int64_t rows, int64_t cols, int32_t info[4]) {
+    set_error("");
+    if (!info) return fail(NT_EINVAL, "nt_gemv_launch_info: null pointer");
+    if (!is_quant(t)) return fail(NT_EINVAL, "nt_gemv_launch_info: unsupported type");
+    if (rows <= 0 || cols <= 0 || cols % block_elems(t) != 0 || cols > kMaxGemvCols)
+        return fail(NT_ESHAPE, "nt_gemv_launch_info: bad shape");
+    gemv_launch_info(t, rows, cols, info);
+    return NT_OK;
+}
+
 #define NT_GEMV_FN(name, T)                                                                       \
     nt_status name(const void *W, const float *x, float *y, int64_t rows, int64_t cols, int acc,  \
                    nt_stream s) {                                                                 \

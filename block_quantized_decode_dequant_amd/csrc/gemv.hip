@@ -678,27 +678,40 @@ hipError_t launch_generic(const void *W, const float *x, float *y, int64_t rows,
     return hipGetLastError();
 }
 
+struct FastShape {
+    int nw, G;
+    int64_t grid;
+};
+
+FastShape fast_shape(int R, int64_t rows, int64_t cols) {
+    static const int waves_env = env_int("NT_GEMV_WAVES", 0);
+    static const int g_env = env_int("NT_GEMV_G", 0);
+    FastShape f;
+    const int units = int(cols / 64);
+    f.nw = (units + 63) / 64;                      // <= 8 for cols <= 32768
+    // groups per tile: 8 for tall matrices, 4 (or 2) when that leaves too few tiles
+    f.G = g_env;
+    if (f.G <= 0) {
+        f.G = 8;
+        while (f.G > 2 && (rows + R * f.G - 1) / (R * f.G) * f.nw < 2048) f.G /= 2;
+    }
+    const int T = R * f.G;
+    const int64_t ntiles = (rows + T - 1) / T;
+    // persistent grid: about 12 resident waves per CU on 256 CUs
+    const int64_t waves = waves_env > 0 ? waves_env : 256 * 12;
+    f.grid = waves / f.nw;
+    if (f.grid > ntiles) f.grid = ntiles;
+    if (f.grid < 1) f.grid = 1;
+    return f;
+}
+
 template <class Tr>
 hipError_t launch_fast(const void *W, const float *x, float *y, int64_t rows, int64_t cols, int64_t row_bytes,
                        int acc, hipStream_t st) {
     const int units = int(cols / 64);
-    const int nw = (units + 63) / 64;                 // <= 8 for cols <= 32768
-    static const int waves_env = env_int("NT_GEMV_WAVES", 0);
-    static const int g_env = env_int("NT_GEMV_G", 0);
-    constexpr int R = Tr::kRows;
-    // groups per tile: 8 for tall matrices, 4 (or 2) when that leaves too few tiles
-    int G = g_env;
-    if (G <= 0) {
-        G = 8;
-        while (G > 2 && (rows + R * G - 1) / (R * G) * nw < 2048) G /= 2;
-    }
-    const int T = R * G;
-    const int64_t ntiles = (rows + T - 1) / T;
-    // Persistent grid: about 12 resident waves per CU on 256 CUs.
-    const int64_t waves = waves_env > 0 ? waves_env : 256 * 12;
-    int64_t grid = waves / nw;
-    if (grid > ntiles) grid = ntiles;
-    if (grid < 1) grid = 1;
+    const FastShape fs = fast_shape(Tr::kRows, rows, cols);
+    const int nw = fs.nw, G = fs.G;
+    const int64_t grid = fs.grid;
     const uint8_t *w = static_cast<const uint8_t *>(W);
     const dim3 gd = dim3(unsigned(grid)), bd = dim3(unsigned(64 * nw));
     switch (G) {
@@ -711,13 +724,38 @@ hipError_t launch_fast(const void *W, const float *x, float *y, int64_t rows, in
 
 }  // namespace
 
-hipError_t launch_gemv(nt_qtype t, const void *W, const float *x, float *y, int64_t rows,
-                       int64_t cols, int accumulate, hipStream_t st) {
-    // Fast path: word-aligned rows (an even number of 2-byte-aligned blocks)
-    // and at most 8 slices of 4096 values.
+static bool use_fast(nt_qtype t, int64_t cols) {
+    // fast path: word-aligned rows (an even number of 2-byte-aligned blocks)
+    // and at most 8 slices of 4096 values
     static const bool force_generic = env_int("NT_GEMV_GENERIC", 0) != 0;
     const int64_t rb = cols / block_elems(t) * block_bytes(t);
-    const bool fast = !force_generic && rb % 4 == 0 && cols % 64 == 0 && cols <= 32768;
+    return !force_generic && rb % 4 == 0 && cols % 64 == 0 && cols <= 32768;
+}
+
+void gemv_launch_info(nt_qtype t, int64_t rows, int64_t cols, int32_t info[4]) {
+    if (use_fast(t, cols)) {
+        const int R = t == NT_Q6_K ? F6K::kRows : t == NT_Q8_0 ? F80::kRows : t == NT_Q4_0 ? F40::kRows : F4K::kRows;
+        const FastShape f = fast_shape(R, rows, cols);
+        info[0] = 1;
+        info[1] = R * f.G;
+        info[2] = int32_t(f.grid);
+        info[3] = 64 * f.nw;
+    } else {
+        const int units = int(cols / 32), upl = units <= 1024 ? 1 : 2;
+        const int nw = (units + 64 * upl - 1) / (64 * upl);
+        const int64_t tt = rows * nw / 8192;
+        const int tile = tt < 4 ? 4 : tt > 32 ? 32 : int(tt / 4 * 4);
+        info[0] = 0;
+        info[1] = tile;
+        info[2] = int32_t((rows + tile - 1) / tile);
+        info[3] = 64 * nw;
+    }
+}
+
+hipError_t launch_gemv(nt_qtype t, const void *W, const float *x, float *y, int64_t rows,
+                       int64_t cols, int accumulate, hipStream_t st) {
+    const int64_t rb = cols / block_elems(t) * block_bytes(t);
+    const bool fast = use_fast(t, cols);
     switch (t) {
     case NT_Q8_0: return fast ? launch_fast<F80>(W, x, y, rows, cols, rb, accumulate, st)
                               : launch_generic<Q80>(W, x, y, rows, cols, accumulate, st);

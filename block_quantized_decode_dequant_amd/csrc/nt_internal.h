@@ -29,6 +29,7 @@ bool is_quant(nt_qtype t);
 hipError_t launch_dequant(nt_qtype t, const void *blocks, float *out, int64_t n, hipStream_t st);
 hipError_t launch_gemv(nt_qtype t, const void *W, const float *x, float *y, int64_t rows,
                        int64_t cols, int accumulate, hipStream_t st);
+void gemv_launch_info(nt_qtype t, int64_t rows, int64_t cols, int32_t info[4]);
 hipError_t launch_quantize(nt_qtype t, const float *x, void *blocks, int64_t n, hipStream_t st);
 hipError_t launch_delay(double us, hipStream_t st);
 hipError_t launch_rmsnorm(const float *x, const float *g, float *y, int64_t n, float eps, hipStream_t st);

@@ -64,6 +64,7 @@ def _declare(L):
         "nt_dequant": (st, [i32, vp, vp, i64, vp]),
         "nt_gemv": (st, [i32, vp, vp, vp, i64, i64, i32, vp]),
         "nt_quantize": (st, [i32, vp, vp, i64, vp]),
+        "nt_gemv_launch_info": (st, [i32, i64, i64, C.POINTER(C.c_int32)]),
         "nt_read_bytes": (st, [vp, i64, vp, vp]),
         "nt_copy_bytes": (st, [vp, vp, i64, vp]),
         "nt_delay": (st, [C.c_double, vp]),
@@ -158,6 +159,12 @@ def nt_gemv_q8_0(W, x, y, rows, cols, accumulate=False, stream=None): nt_gemv(Q8
 def nt_gemv_q4_0(W, x, y, rows, cols, accumulate=False, stream=None): nt_gemv(Q4_0, W, x, y, rows, cols, accumulate, stream)
 def nt_gemv_q4_k(W, x, y, rows, cols, accumulate=False, stream=None): nt_gemv(Q4_K, W, x, y, rows, cols, accumulate, stream)
 def nt_gemv_q6_k(W, x, y, rows, cols, accumulate=False, stream=None): nt_gemv(Q6_K, W, x, y, rows, cols, accumulate, stream)
+
+
+def nt_gemv_launch_info(qtype: int, rows: int, cols: int) -> dict:
+    info = (C.c_int32 * 4)()
+    _check(lib().nt_gemv_launch_info(qtype, rows, cols, info), "nt_gemv_launch_info")
+    return {"fast": bool(info[0]), "tile_rows": info[1], "workgroups": info[2], "threads": info[3]}
 
 
 # ---- encode -----------------------------------------------------------------------------

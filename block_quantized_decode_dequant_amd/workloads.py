@@ -59,3 +59,5 @@ LLAMA_8B_Q8_0 = ModelShape("llama3-8b-shaped q8_0", 32, 4096, 32, 8, 128, 14336,
                            1024, 128, "q8_0")
 LLAMA_70B_MIX = ModelShape("llama-70b-shaped q4_k/q6_k", 80, 8192, 64, 8, 128, 28672, 128256,
                            4096, 64, "mix")
+LLAMA_70B_Q6K = ModelShape("llama-70b-shaped q6_k (host-streamed)", 80, 8192, 64, 8, 128, 28672, 128256,
+                           4096, 64, "q6_k")

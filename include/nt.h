@@ -113,6 +113,11 @@ nt_status nt_gemv_q6_k(const void *W, const float *x, float *y, int64_t rows, in
                        int accumulate, nt_stream stream);
 nt_status nt_gemv(nt_qtype t, const void *W, const float *x, float *y, int64_t rows, int64_t cols,
                   int accumulate, nt_stream stream);
+/* The launch the GEMV calls above would use for this shape (no GPU needed):
+ * info[0] = kernel family (1 = fast path: word-aligned rows, cols <= 32768;
+ * 0 = generic path), info[1] = rows per workgroup tile (the kernel
+ * instantiation), info[2] = workgroups, info[3] = threads per workgroup. */
+nt_status nt_gemv_launch_info(nt_qtype t, int64_t rows, int64_t cols, int32_t info[4]);
 
 /* ---- per-token ops ("Architecture": RMSNorm, RoPE, SwiGLU, softmax kernels;
  * "Main features": the Llama block) --------------------------------------
