@@ -166,7 +166,7 @@ def run_gpu(args):
     kern = {}
     for c, ms in zip(cases, per_case_ms):
         li = nt.nt_gemv_launch_info(c["qt"], c["rows"], c["cols"])
-        k = f"gemv {c['type']} {'fast' if li['fast'] else 'generic'} tile{li['tile_rows']}"
+        k = f"gemv {c['type']} lds vec{li['vec']}" if li["fast"] else f"gemv {c['type']} generic"
         a = kern.setdefault(k, dict(bytes=0, ms=0.0, launches=0))
         a["bytes"] += c["bytes"]
         a["ms"] += ms

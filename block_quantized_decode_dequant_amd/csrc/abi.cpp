@@ -161,6 +161,61 @@ nt_status nt_gemv_launch_info(nt_qtype t, int64_t rows, int64_t cols, int32_t in
     return NT_OK;
 }
 
+nt_status nt_gemv_multi(nt_qtype t, int32_t nseg, const void *const *W, const int64_t *rows, float *const *y,
+                        int64_t cols, const float *x, const float *gain, float eps, int accumulate,
+                        nt_stream stream) {
+    set_error("");
+    if (!is_quant(t)) return fail(NT_EINVAL, "nt_gemv_multi: unsupported type");
+    if (nseg < 1 || nseg > 3) return fail(NT_EINVAL, "nt_gemv_multi: nseg must be 1, 2 or 3");
+    if (!W || !rows || !y) return fail(NT_EINVAL, "nt_gemv_multi: null array");
+    if (cols <= 0 || cols % block_elems(t) != 0) return fail(NT_ESHAPE, "nt_gemv_multi: cols not a whole number of blocks");
+    if (!(eps >= 0.f)) return fail(NT_EINVAL, "nt_gemv_multi: negative eps");
+    int64_t total = 0;
+    for (int s = 0; s < nseg; ++s) {
+        if (rows[s] < 0) return fail(NT_EINVAL, "nt_gemv_multi: negative rows");
+        total += rows[s];
+        if (!W[s] || !y[s]) return fail(NT_EINVAL, "nt_gemv_multi: null pointer");
+        if (!aligned(W[s], 16) || !aligned(y[s], 16)) return fail(NT_EALIGN, "nt_gemv_multi: W and y must be 16-byte aligned");
+        if (rows[s] > 0 && !gemv_fast_ok(t, rows[s], cols))
+            return fail(NT_ESHAPE, "nt_gemv_multi: shape not taken by the fused kernels (word-aligned rows, "
+                                   "cols % 64 == 0, cols <= 32768, rows * row_bytes < 2^32)");
+    }
+    if (total > (int64_t(1) << 31) - 1) return fail(NT_ESHAPE, "nt_gemv_multi: more than 2^31 rows");
+    if (!x) return fail(NT_EINVAL, "nt_gemv_multi: null x");
+    if (!aligned(x, 16) || !aligned(gain, 16)) return fail(NT_EALIGN, "nt_gemv_multi: x and gain must be 16-byte aligned");
+    if (total == 0) return NT_OK;
+    if (nt_status s = need_device()) return s;
+    // drop empty matrices (the kernel assumes every listed matrix has rows)
+    const void *Wk[3];
+    int64_t rk[3];
+    float *yk[3];
+    int k = 0;
+    for (int s = 0; s < nseg; ++s)
+        if (rows[s] > 0) { Wk[k] = W[s]; rk[k] = rows[s]; yk[k] = y[s]; ++k; }
+    return finish(launch_gemv_multi(t, k, Wk, rk, yk, cols, x, gain, eps, accumulate, as_stream(stream)),
+                  "nt_gemv_multi");
+}
+
+nt_status nt_gemv_swiglu(nt_qtype t, const void *W_gate, const void *W_up, int64_t rows, int64_t cols,
+                         const float *x, const float *gain, float eps, float *h, nt_stream stream) {
+    set_error("");
+    if (!is_quant(t)) return fail(NT_EINVAL, "nt_gemv_swiglu: unsupported type");
+    if (rows < 0) return fail(NT_EINVAL, "nt_gemv_swiglu: negative rows");
+    if (cols <= 0 || cols % block_elems(t) != 0) return fail(NT_ESHAPE, "nt_gemv_swiglu: cols not a whole number of blocks");
+    if (!(eps >= 0.f)) return fail(NT_EINVAL, "nt_gemv_swiglu: negative eps");
+    if (rows > (int64_t(1) << 30)) return fail(NT_ESHAPE, "nt_gemv_swiglu: more than 2^30 rows");
+    if (rows > 0 && !gemv_fast_ok(t, rows, cols))
+        return fail(NT_ESHAPE, "nt_gemv_swiglu: shape not taken by the fused kernels (word-aligned rows, "
+                               "cols % 64 == 0, cols <= 32768, rows * row_bytes < 2^32)");
+    if (!W_gate || !W_up || !x || !h) return fail(NT_EINVAL, "nt_gemv_swiglu: null pointer");
+    if (!aligned(W_gate, 16) || !aligned(W_up, 16) || !aligned(x, 16) || !aligned(gain, 16) || !aligned(h, 16))
+        return fail(NT_EALIGN, "nt_gemv_swiglu: W_gate, W_up, x, gain and h must be 16-byte aligned");
+    if (rows == 0) return NT_OK;
+    if (nt_status s = need_device()) return s;
+    return finish(launch_gemv_swiglu(t, W_gate, W_up, rows, cols, x, gain, eps, h, as_stream(stream)),
+                  "nt_gemv_swiglu");
+}
+
 #define NT_GEMV_FN(name, T)                                                                       \
     nt_status name(const void *W, const float *x, float *y, int64_t rows, int64_t cols, int acc,  \
                    nt_stream s) {                                                                 \

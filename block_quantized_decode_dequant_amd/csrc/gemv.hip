@@ -28,13 +28,33 @@
 #include "nt_internal.h"
 
 namespace nt {
+
+// Arguments of one fast-path launch: up to three matrices of one format and
+// width read against the same activation vector (their rows concatenated), or
+// in SwiGLU mode a gate and an up matrix whose rows are interleaved.
+struct GemvArgs {
+    const uint8_t *W[3];
+    float *y[3];
+    int32_t seg_end[3];      // cumulative row counts
+    uint32_t seg_lim[3];     // last byte offset a copy may start at, per matrix
+    const float *x;
+    const float *gain;       // RMSNorm gain; null: x is used as is
+    float eps;
+    int cols;
+    int rows;                // rows of all matrices together
+    int units;               // 64-value units per row
+    uint32_t row_bytes;
+    int accumulate;
+    int swiglu;
+};
+
 namespace {
 
 constexpr uint32_t kLo4 = 0x0f0f0f0fu;
 
 // ---- Q8_0: one unit = one 34-byte block ------------------------------------
 struct Q80 {
-    static constexpr int kBlockElems = 32, kBlockBytes = 34;
+    static constexpr int kBlockElems = 32;
     struct Raw { u32x4 a, b; uint32_t c, sh; };
     struct X { float v[32]; float sum; };
 
@@ -77,7 +97,7 @@ struct Q80 {
 
 // ---- Q4_0: one unit = one 18-byte block -------------------------------------
 struct Q40 {
-    static constexpr int kBlockElems = 32, kBlockBytes = 18;
+    static constexpr int kBlockElems = 32;
     struct Raw { u32x4 a; uint32_t c, sh; };
     // v[i]: value i of the block = low nibble of byte i (i < 16) or high
     // nibble of byte i - 16, so the activations load exactly as for Q8_0
@@ -117,7 +137,7 @@ struct Q40 {
 // half hh = t%2; low nibbles are sub-block 2p, values 64p + 16hh + i, high
 // nibbles sub-block 2p+1, values 64p + 32 + 16hh + i (i = 0..15).
 struct Q4K {
-    static constexpr int kBlockElems = 256, kBlockBytes = 144;
+    static constexpr int kBlockElems = 256;
     struct Raw { u32x4 hdr, q; };
     struct X { float lo[16], hi[16]; float slo, shi; uint32_t t; };
 
@@ -185,7 +205,7 @@ struct Q4K {
 // high nibble), ql[64h + 32 + 8m + i] (k = 1 low, k = 3 high), qh[32h + 8m + i]
 // (2 bits per k), scales[8h + 2k + m/2], d.
 struct Q6K {
-    static constexpr int kBlockElems = 256, kBlockBytes = 210;
+    static constexpr int kBlockElems = 256;
     struct Raw { u32x3 qa, qb, qh, sc; uint32_t dd, sh; };
     struct X { float v[4][8]; float s[4]; uint32_t t; };
 
@@ -317,29 +337,43 @@ __global__ void __launch_bounds__(1024) gemv_generic(const uint8_t *__restrict__
 }
 
 // =============================================================================
-// Fast path: 64 values per lane, rows whose byte length is a multiple of 4
-// (an even number of Q8_0 / Q4_0 / Q6_K blocks; any Q4_K row).  A lane's
-// loads are at fixed byte offsets from the row start, so the row pointer is
-// wave-uniform (scalar registers) and the per-lane part a 32-bit offset.
+// Fast path: rows whose byte length is a multiple of 4 (an even number of
+// Q8_0 / Q4_0 blocks, any Q4_K row, Q6_K rows of an even number of
+// super-blocks), cols % 64 == 0, cols <= 32768.
+//
+// Lane l of wave w owns 64 consecutive values of every row ("unit" 64w + l):
+// two Q8_0 / Q4_0 blocks, one 32-byte code pair of a Q4_K super-block, or a
+// quarter of a Q6_K super-block.  The 64 lanes of a wave therefore own one
+// contiguous byte range of each row, its "slice" (kSlice bytes).  The slice
+// is copied from HBM into a per-wave LDS ring by global_load_lds (each
+// instruction moves 64 x VEC contiguous bytes, fully coalesced, straight into
+// LDS without passing through VGPRs); a lane then reads its own unit back
+// from LDS.  The ring keeps kStages - 1 rows in flight per wave, so about
+// 8 waves per CU keep ~100 KB of weight reads outstanding per CU.  Waits are
+// explicit (s_waitcnt vmcnt) because the ring's loads return to LDS, not to
+// registers the compiler could track.
 // =============================================================================
 
-constexpr uint32_t kMagic16 = 0x3c003c00u;   // two fp16 1.0
-constexpr uint32_t kNib16 = 0x03c003c0u;     // a nibble at fp16 fraction bits 6..9
+constexpr uint32_t kMagicQ4 = 0x3c003c00u;   // two fp16 1.0
+constexpr uint32_t kNibQ4 = 0x00f000f0u;     // a nibble at fp16 fraction bits 4..7
+constexpr int kMaxRowsPerWG = 256;           // rows one workgroup reduces (LDS row sums)
 
-// Two fp16 values 1 + q/16 from nibbles already shifted to bits 6..9 and
-// 22..25 (v_and_or_b32 with the magic held in a VGPR).
+// Two fp16 values 1 + q/64 from nibbles already at bits 4..7 and 20..23
+// (v_and_or_b32 with the magic held in a VGPR).  The value keeps q exact; the
+// fp32 sums below carry the leading 1 (removed afterwards), which costs at
+// most 6 bits of the products' precision.
 __device__ __forceinline__ uint32_t nib_pair(uint32_t shifted, uint32_t magic) {
-    return (shifted & kNib16) | magic;
+    return (shifted & kNibQ4) | magic;
 }
 
-// Sum over the 8 nibbles of w of (1 + q/16) * x: low nibbles pair with xl[0..3],
+// Sum over the 8 nibbles of w of (1 + q/64) * x: low nibbles pair with xl[0..3],
 // high nibbles with xh[0..3] (byte k of w <-> index k).
 __device__ __forceinline__ void nib_fma(uint32_t w, const float *xl, const float *xh, uint32_t magic,
                                         float &al, float &ah) {
-    const uint32_t c0 = nib_pair(w << 6, magic);   // low nibbles of bytes 0, 2
-    const uint32_t c1 = nib_pair(w >> 2, magic);   // low nibbles of bytes 1, 3
-    const uint32_t c2 = nib_pair(w << 2, magic);   // high nibbles of bytes 0, 2
-    const uint32_t c3 = nib_pair(w >> 6, magic);   // high nibbles of bytes 1, 3
+    const uint32_t c0 = nib_pair(w << 4, magic);   // low nibbles of bytes 0, 2
+    const uint32_t c1 = nib_pair(w >> 4, magic);   // low nibbles of bytes 1, 3
+    const uint32_t c2 = nib_pair(w, magic);        // high nibbles of bytes 0, 2
+    const uint32_t c3 = nib_pair(w >> 8, magic);   // high nibbles of bytes 1, 3
     al = fmaf(h_lo(c0), xl[0], al);
     al = fmaf(h_lo(c1), xl[1], al);
     al = fmaf(h_hi(c0), xl[2], al);
@@ -350,36 +384,26 @@ __device__ __forceinline__ void nib_fma(uint32_t w, const float *xl, const float
     ah = fmaf(h_hi(c3), xh[3], ah);
 }
 
-__device__ __forceinline__ void load_x64(const float *x, float *v, float &sum) {
-    const float4 *p = reinterpret_cast<const float4 *>(x);
+// Sum of N values: pairwise within groups of four, groups added in order.
+template <int N>
+__device__ __forceinline__ float sum_vals(const float *v) {
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float4 a = p[i];
-        v[4 * i] = a.x; v[4 * i + 1] = a.y; v[4 * i + 2] = a.z; v[4 * i + 3] = a.w;
-        s += (a.x + a.y) + (a.z + a.w);
-    }
-    sum = s;
+    for (int i = 0; i < N / 4; ++i) s += (v[4 * i] + v[4 * i + 1]) + (v[4 * i + 2] + v[4 * i + 3]);
+    return s;
 }
 
 // ---- Q8_0 fast: one lane = blocks 2u, 2u+1 (68 bytes at 68u, word-aligned) --
 struct F80 {
-    static constexpr int kRows = 2;
+    static constexpr int kSlice = 64 * 68, kStages = 4;
     struct L { uint32_t off; };
     struct X { float v[64]; float s0, s1; };
     struct Raw { u32x4 a, b, c, d; uint32_t e; };
-    __device__ static L lane(int64_t u) { return {uint32_t(u * 68)}; }
-    __device__ static void load_x(const float *x, int64_t u, X &xs) {
-        float s;
-        load_x64(x + u * 64, xs.v, s);
-        float s0 = 0.f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) s0 += xs.v[i];
-        xs.s0 = s0;
-        xs.s1 = s - s0;
-    }
-    __device__ static void load(const uint8_t *row, const L &l, Raw &r) {
-        const uint8_t *p = row + l.off;
+    __device__ static L lane(int l) { return {uint32_t(l * 68)}; }
+    __device__ static uint32_t x_chunk(int l, int j) { return uint32_t(16 * l + j); }
+    __device__ static void sums(X &xs) { xs.s0 = sum_vals<32>(xs.v); xs.s1 = sum_vals<32>(xs.v + 32); }
+    __device__ static void load(const uint8_t *base, const L &l, Raw &r) {
+        const uint8_t *p = base + l.off;
         r.a = ld4(p); r.b = ld4(p + 16); r.c = ld4(p + 32); r.d = ld4(p + 48); r.e = ld1(p + 64);
     }
     __device__ static float dot(const Raw &r, const X &xs, const L &, uint32_t) {
@@ -411,25 +435,18 @@ struct F80 {
 
 // ---- Q4_0 fast: one lane = blocks 2u, 2u+1 (36 bytes at 36u, word-aligned) --
 struct F40 {
-    static constexpr int kRows = 2;
+    static constexpr int kSlice = 64 * 36, kStages = 8;
     struct L { uint32_t off; };
     struct X { float v[64]; float s0, s1; };
     struct Raw { u32x4 a, b; uint32_t c; };
-    __device__ static L lane(int64_t u) { return {uint32_t(u * 36)}; }
-    __device__ static void load_x(const float *x, int64_t u, X &xs) {
-        float s;
-        load_x64(x + u * 64, xs.v, s);
-        float s0 = 0.f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) s0 += xs.v[i];
-        xs.s0 = s0;
-        xs.s1 = s - s0;
-    }
-    __device__ static void load(const uint8_t *row, const L &l, Raw &r) {
-        const uint8_t *p = row + l.off;
+    __device__ static L lane(int l) { return {uint32_t(l * 36)}; }
+    __device__ static uint32_t x_chunk(int l, int j) { return uint32_t(16 * l + j); }
+    __device__ static void sums(X &xs) { xs.s0 = sum_vals<32>(xs.v); xs.s1 = sum_vals<32>(xs.v + 32); }
+    __device__ static void load(const uint8_t *base, const L &l, Raw &r) {
+        const uint8_t *p = base + l.off;
         r.a = ld4(p); r.b = ld4(p + 16); r.c = ld1(p + 32);
     }
-    // sum over one block of (1 + q/16) x: byte i holds value i (low) and i+16 (high)
+    // sum over one block of (1 + q/64) x: byte i holds value i (low) and i+16 (high)
     __device__ static float block_acc(const uint32_t *q, const float *v, uint32_t magic) {
         float al = 0.f, ah = 0.f;
 #pragma unroll
@@ -448,9 +465,9 @@ struct F40 {
                                 __builtin_amdgcn_perm(w[4], w[3], 0x05040302u)};
         const uint32_t q1[4] = {w[5], w[6], w[7], w[8]};
         const float a0 = block_acc(q0, xs.v, magic), a1 = block_acc(q1, xs.v + 32, magic);
-        // sum (q-8) x = 16*(acc - X) - 8X = 16 acc - 24 X
+        // sum (q-8) x = 64*(acc - X) - 8X = 64 acc - 72 X
         const float d0 = h2f(w[0]), d1 = h2f(w[4] >> 16);
-        return fmaf(d0, fmaf(16.f, a0, -24.f * xs.s0), d1 * fmaf(16.f, a1, -24.f * xs.s1));
+        return fmaf(d0, fmaf(64.f, a0, -72.f * xs.s0), d1 * fmaf(64.f, a1, -72.f * xs.s1));
     }
 };
 
@@ -458,27 +475,21 @@ struct F40 {
 // byte 32p + i: low nibble = value 64p + i (sub-block 2p), high nibble = value
 // 64p + 32 + i (sub-block 2p+1).
 struct F4K {
-    static constexpr int kRows = 2;
+    static constexpr int kSlice = 16 * 144, kStages = 8;
     struct L { uint32_t off_h, off_q, p; };
     struct X { float v[64]; float slo, shi; };   // v[i]: value 64p+i (lo: i<32, hi: i>=32)
     struct Raw { u32x4 h, q0, q1; };
-    __device__ static L lane(int64_t u) {
-        const uint32_t b = uint32_t(u >> 2), p = uint32_t(u & 3);
+    __device__ static L lane(int l) {
+        const uint32_t b = uint32_t(l >> 2), p = uint32_t(l & 3);
         return {144 * b, 144 * b + 16 + 32 * p, p};
     }
-    __device__ static void load_x(const float *x, int64_t u, X &xs) {
-        const int64_t b = u >> 2, p = u & 3;
-        load_x64(x + b * 256 + 64 * p, xs.v, xs.slo);
-        float sh = 0.f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) sh += xs.v[32 + i];
-        xs.shi = sh;
-        xs.slo -= sh;
-    }
-    __device__ static void load(const uint8_t *row, const L &l, Raw &r) {
-        r.h = ld4(row + l.off_h);
-        r.q0 = ld4(row + l.off_q);
-        r.q1 = ld4(row + l.off_q + 16);
+    // value i of lane l's 64 is x[64 l + i] within the wave's 4096
+    __device__ static uint32_t x_chunk(int l, int j) { return uint32_t(16 * l + j); }
+    __device__ static void sums(X &xs) { xs.slo = sum_vals<32>(xs.v); xs.shi = sum_vals<32>(xs.v + 32); }
+    __device__ static void load(const uint8_t *base, const L &l, Raw &r) {
+        r.h = ld4(base + l.off_h);
+        r.q0 = ld4(base + l.off_q);
+        r.q1 = ld4(base + l.off_q + 16);
     }
     __device__ static float dot(const Raw &r, const X &xs, const L &l, uint32_t magic) {
         const uint32_t q[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
@@ -487,17 +498,17 @@ struct F4K {
         for (int m = 0; m < 8; ++m) nib_fma(q[m], xs.v + 4 * m, xs.v + 32 + 4 * m, magic, al, ah);
         const uint32_t p = l.p, sft = 16 * (p & 1);
         const uint32_t y = r.h.y >> sft, z = r.h.z >> sft, w = r.h.w >> sft;
-        // both encodings computed, one selected: no divergent branch
-        const bool low = p < 2;
-        const uint32_t S0 = low ? (y & 63) : ((w & 15) | (((y >> 6) & 3) << 4));
-        const uint32_t M0 = low ? (z & 63) : (((w >> 4) & 15) | (((z >> 6) & 3) << 4));
-        const uint32_t S1 = low ? ((y >> 8) & 63) : (((w >> 8) & 15) | (((y >> 14) & 3) << 4));
-        const uint32_t M1 = low ? ((z >> 8) & 63) : (((w >> 12) & 15) | (((z >> 14) & 3) << 4));
+        // both encodings computed, one kept by a lane mask: no branch
+        const uint32_t lm = opaque(p < 2 ? 0xffffffffu : 0u), hm = ~lm;
+        const uint32_t S0 = ((y & 63) & lm) | (((w & 15) | (((y >> 6) & 3) << 4)) & hm);
+        const uint32_t M0 = ((z & 63) & lm) | ((((w >> 4) & 15) | (((z >> 6) & 3) << 4)) & hm);
+        const uint32_t S1 = (((y >> 8) & 63) & lm) | ((((w >> 8) & 15) | (((y >> 14) & 3) << 4)) & hm);
+        const uint32_t M1 = (((z >> 8) & 63) & lm) | ((((w >> 12) & 15) | (((z >> 14) & 3) << 4)) & hm);
         const float d = h2f(r.h.x), dmin = h2f(r.h.x >> 16);
-        // sum q x over a sub-block = 16 * (acc - X)
+        // sum q x over a sub-block = 64 * (acc - X)
         const float pos = fmaf(float(S0), al - xs.slo, float(S1) * (ah - xs.shi));
         const float neg = fmaf(float(M0), xs.slo, float(M1) * xs.shi);
-        return fmaf(16.f * d, pos, -dmin * neg);
+        return fmaf(64.f * d, pos, -dmin * neg);
     }
 };
 
@@ -508,32 +519,26 @@ struct F4K {
 // qh[32h + 16j + i] (bits 2k..2k+1), scales[8h + 2k + j] and d.  Odd blocks
 // start 2 bytes into a word: loads are word-aligned and v_perm realigns.
 struct F6K {
-    static constexpr int kRows = 1;
+    static constexpr int kSlice = 16 * 210, kStages = 5;
     struct L { uint32_t base, sel, h, j; };
-    struct X { float v[4][16]; float s[4]; };
+    struct X { float v[64]; float s[4]; };       // v[16k + i]
     struct Raw { u32x4 a; uint32_t a4; u32x4 b; uint32_t b4; u32x4 c; uint32_t c4; u32x3 sc; uint32_t d; };
-    __device__ static L lane(int64_t u) {
-        const uint32_t b = uint32_t(u >> 2), t = uint32_t(u & 3);
+    __device__ static L lane(int l) {
+        const uint32_t b = uint32_t(l >> 2), t = uint32_t(l & 3);
         const uint32_t off = 210 * b, sh = off & 3;
         return {off - sh, sh ? 0x05040302u : 0x03020100u, t >> 1, t & 1};
     }
-    __device__ static void load_x(const float *x, int64_t u, X &xs) {
-        const int64_t b = u >> 2, t = u & 3, h = t >> 1, j = t & 1;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float4 *p = reinterpret_cast<const float4 *>(x + b * 256 + 128 * h + 32 * k + 16 * j);
-            float s = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float4 a = p[i];
-                xs.v[k][4 * i] = a.x; xs.v[k][4 * i + 1] = a.y; xs.v[k][4 * i + 2] = a.z; xs.v[k][4 * i + 3] = a.w;
-                s += (a.x + a.y) + (a.z + a.w);
-            }
-            xs.s[k] = s;
-        }
+    // values v[16k + 4m .. +3] = x[256b + 128h + 32k + 16j + 4m ..] (16-byte chunk 4k + m)
+    __device__ static uint32_t x_chunk(int l, int c) {
+        const int b = l >> 2, t = l & 3, h = t >> 1, j = t & 1, k = c >> 2, m = c & 3;
+        return uint32_t(64 * b + 32 * h + 8 * k + 4 * j + m);
     }
-    __device__ static void load(const uint8_t *row, const L &l, Raw &r) {
-        const uint8_t *p = row + l.base;
+    __device__ static void sums(X &xs) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) xs.s[k] = sum_vals<16>(xs.v + 16 * k);
+    }
+    __device__ static void load(const uint8_t *base, const L &l, Raw &r) {
+        const uint8_t *p = base + l.base;
         const uint32_t oa = 64 * l.h + 16 * l.j, oc = 128 + 32 * l.h + 16 * l.j;
         r.a = ld4(p + oa); r.a4 = ld1(p + oa + 16);
         r.b = ld4(p + oa + 32); r.b4 = ld1(p + oa + 48);
@@ -560,10 +565,10 @@ struct F6K {
             const uint32_t qq[4] = {q0, q1, q2, q3};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                s[k] = fmaf(ubyte<0>(qq[k]), xs.v[k][4 * m + 0], s[k]);
-                s[k] = fmaf(ubyte<1>(qq[k]), xs.v[k][4 * m + 1], s[k]);
-                s[k] = fmaf(ubyte<2>(qq[k]), xs.v[k][4 * m + 2], s[k]);
-                s[k] = fmaf(ubyte<3>(qq[k]), xs.v[k][4 * m + 3], s[k]);
+                s[k] = fmaf(ubyte<0>(qq[k]), xs.v[16 * k + 4 * m + 0], s[k]);
+                s[k] = fmaf(ubyte<1>(qq[k]), xs.v[16 * k + 4 * m + 1], s[k]);
+                s[k] = fmaf(ubyte<2>(qq[k]), xs.v[16 * k + 4 * m + 2], s[k]);
+                s[k] = fmaf(ubyte<3>(qq[k]), xs.v[16 * k + 4 * m + 3], s[k]);
             }
         }
         // int8 scales[8h + 2k + j] = byte 2k + j of the realigned scale words
@@ -580,75 +585,209 @@ struct F6K {
     }
 };
 
-// Persistent, software-pipelined fast kernel.  A workgroup of nw waves (one
-// per 4096-value column slice) walks row tiles blockIdx.x, +gridDim.x, ...
-// A tile is G row groups of R rows.  The tile body is fully unrolled with two
-// register buffers: while a wave decodes group g it already has the loads of
-// group g+1 in flight (the last group prefetches the first group of the next
-// tile), so every load is unconditional and the compiler can wait for exactly
-// the group it decodes.  Row sums are reduced over the wave with DPP, kept in
-// one VGPR (lane i = row i of the tile), written to LDS once per tile, and the
-// nw column slices are added in a fixed order.
-template <class Tr, int G>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(3)))
-gemv_fast(const uint8_t *__restrict__ W, const float *__restrict__ x, float *__restrict__ y,
-          int rows, int64_t row_bytes, int units_per_row, int accumulate) {
-    constexpr int R = Tr::kRows, T = R * G;
-    static_assert(G % 2 == 0 && T <= 64, "tile shape");
-    __shared__ float part[2][8 * T];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    const int64_t unit = int64_t(wave) * 64 + lane;
-    const bool ok = unit < units_per_row;
-    const uint32_t magic = opaque(kMagic16);
-    const typename Tr::L L = Tr::lane(ok ? unit : 0);
-    const int ntiles = (rows + T - 1) / T;
-    int t = blockIdx.x;
-    if (t >= ntiles) return;
+// How one row slice is copied: NFULL instructions of 64 x VEC bytes, then, if
+// the slice is not a whole number of those, one instruction on the first
+// REM / VEC lanes.  VEC = 16 needs 16-byte-aligned rows, VEC = 4 word-aligned.
+template <class Tr, int VEC>
+struct Plan {
+    static constexpr int kPer = 64 * VEC;
+    static constexpr int kFull = Tr::kSlice / kPer;
+    static constexpr int kRem = Tr::kSlice % kPer;
+    static constexpr int kInstr = kFull + (kRem ? 1 : 0);
+    static constexpr int kStages = Tr::kStages;
+    static_assert(kRem % VEC == 0, "slice tail");
+    static_assert((kStages - 1) * kInstr <= 63, "vmcnt holds at most 63 outstanding loads");
+};
 
-    // rows past the end re-read the last row; idle lanes read unit 0
-    auto issue = [&](typename Tr::Raw *buf, int tile, int g) {
-#pragma unroll
-        for (int i = 0; i < R; ++i)
-            Tr::load(W + int64_t(min(tile * T + g * R + i, rows - 1)) * row_bytes, L, buf[i]);
-    };
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt
+// fields at their maxima, i.e. no wait on them).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
-    typename Tr::Raw A[R], B[R];
-    issue(A, t, 0);
-    asm volatile("" ::: "memory");      // the first weight loads go out before the activations
-    typename Tr::X xs;
-    Tr::load_x(x, ok ? unit : 0, xs);
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
 
-    int pb = 0;
-    for (; t < ntiles; t += gridDim.x) {
-        const int tn = t + int(gridDim.x) < ntiles ? t + int(gridDim.x) : t;
-        float rowsum = 0.f;             // lane i: sum of row i of this tile (this slice)
+// One global_load_lds of V bytes per lane: lane i's bytes land at lds + V*i.
+template <int V>
+__device__ __forceinline__ void dma(const uint8_t *g, uint8_t *lds) {
+    if constexpr (V == 16)
+        __builtin_amdgcn_global_load_lds((gbl_void *)g, (lds_void *)lds, 16, 0, 0);
+    else
+        __builtin_amdgcn_global_load_lds((gbl_void *)g, (lds_void *)lds, 4, 0, 0);
+}
+
+// Copy one row slice (this wave's part of one row) into an LDS ring stage.
+template <class Tr, int VEC>
+__device__ __forceinline__ void copy_slice(const uint8_t *W, uint32_t base, uint32_t lim, uint8_t *dst, int lane) {
+    using P = Plan<Tr, VEC>;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            typename Tr::Raw *cur = (g & 1) ? B : A;
-            typename Tr::Raw *nxt = (g & 1) ? A : B;
-            if (g + 1 < G) issue(nxt, t, g + 1);
-            else issue(nxt, tn, 0);
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-                float a = Tr::dot(cur[i], xs, L, magic);
-                a = ok ? a : 0.f;
-                a = wave_sum_to_lane63(a);
-                const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 63));
-                rowsum = (lane == g * R + i) ? s : rowsum;
-            }
-        }
-        if (lane < T) part[pb][wave * T + lane] = rowsum;
-        __syncthreads();
-        if (wave == 0 && lane < T) {
-            const int r = t * T + lane;
-            if (r < rows) {
-                float sum = 0.f;
-                for (int w = 0; w < nw; ++w) sum += part[pb][w * T + lane];
-                y[r] = accumulate ? y[r] + sum : sum;
-            }
-        }
-        pb ^= 1;
+    for (int k = 0; k < P::kFull; ++k) dma<VEC>(W + min(base + uint32_t(k * P::kPer), lim), dst + k * P::kPer);
+    if constexpr (P::kRem > 0) {
+        if (lane < P::kRem / VEC) dma<VEC>(W + min(base + uint32_t(P::kFull * P::kPer), lim), dst + P::kFull * P::kPer);
     }
+}
+
+// s_waitcnt immediate that waits for all LDS operations (lgkmcnt 0) only.
+constexpr int kLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+// A wave's 64 lanes need 64 activations each: 4096 consecutive values, 16 KB
+// (the wave's column slice).  Loading them lane by lane would touch 64 cache
+// lines per instruction; instead the slice is copied into LDS by 16
+// coalesced 1 KB copies and each lane reads its 16 chunks of 16 bytes back.
+// The copy places chunk j of lane l at LDS chunk 16 l + (j + l) mod 16, so a
+// read step j spreads the 64 lanes over all banks; v[4j .. 4j+3] receives
+// chunk Tr::x_chunk(l, j) of the slice.  Past the end of the vector the copy
+// re-reads its last 16 bytes (those values belong to lanes with no columns).
+template <class Tr>
+__device__ __forceinline__ void stage_vec(const float *src, int cols, int wave, int lane, uint8_t *lds, float *v) {
+    const uint8_t *g = reinterpret_cast<const uint8_t *>(src);
+    const uint32_t lim = uint32_t(cols) * 4u - 16u, base = uint32_t(wave) * 16384u;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int p = 64 * k + lane, l = p >> 4, j = ((p & 15) - l) & 15;
+        dma<16>(g + min(base + 16u * Tr::x_chunk(l, j), lim), lds + 1024 * k);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const float4 q = *reinterpret_cast<const float4 *>(lds + 16 * (16 * lane + ((j + lane) & 15)));
+        v[4 * j] = q.x; v[4 * j + 1] = q.y; v[4 * j + 2] = q.z; v[4 * j + 3] = q.w;
+    }
+    // the area is reused as soon as this returns: all reads must be done
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <class Tr, int VEC, bool NORM>
+__global__ void __launch_bounds__(512) gemv_lds(const GemvArgs a) {
+    using P = Plan<Tr, VEC>;
+    constexpr int S = P::kStages, SL = Tr::kSlice, NI = P::kInstr;
+    static_assert(S >= 3, "the ring holds a row being read, one being decoded and one in flight");
+    static_assert(S * SL >= 16384, "the ring must hold a 4096-value activation slice");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    uint8_t *ring = smem + wave * (S * SL);
+    float *part = reinterpret_cast<float *>(smem + nw * (S * SL));   // [nw][kMaxRowsPerWG]
+    float *red = part + nw * kMaxRowsPerWG;                          // [nw]
+
+    // Workgroup b takes items b, b + G, b + 2G, ... (an item is a row, or in
+    // SwiGLU mode a gate row and its up row), so at any moment the workgroups
+    // stream one band of neighbouring rows.
+    const bool pairs = a.swiglu != 0;
+    const int G = gridDim.x, b = blockIdx.x;
+    const int items = pairs ? a.rows / 2 : a.rows;
+    const int nitems = (items - b + G - 1) / G;
+    const int n = pairs ? 2 * nitems : nitems;       // rows, in ring order
+
+    const int u = wave * 64 + lane;
+    const bool ok = u < a.units;
+    const typename Tr::L L = Tr::lane(lane);
+    const uint32_t lane_off = uint32_t(wave) * SL + uint32_t(lane * VEC);
+    const int end0 = a.seg_end[0], end1 = a.seg_end[1];
+    const uint32_t rb = a.row_bytes;
+    const uint8_t *const W0 = a.W[0], *const W1 = a.W[1], *const W2 = a.W[2];
+    const uint32_t lim0 = a.seg_lim[0], lim1 = a.seg_lim[1], lim2 = a.seg_lim[2];
+
+    // row j of this workgroup -> matrix seg_, row local_ within it
+#define NT_LOCATE(j)                                                                        \
+    const int r_ = pairs ? 2 * (b + ((j) >> 1) * G) + ((j) & 1) : b + (j) * G;              \
+    const int seg_ = pairs ? (r_ & 1) : (r_ < end0 ? 0 : (r_ < end1 ? 1 : 2));             \
+    const int local_ = pairs ? (r_ >> 1) : r_ - (seg_ == 0 ? 0 : (seg_ == 1 ? end0 : end1))
+    // copy row j's slice into ring stage st
+#define NT_ISSUE(j, st)                                                                          \
+    do {                                                                                         \
+        NT_LOCATE(j);                                                                            \
+        const uint8_t *W_ = seg_ == 0 ? W0 : (seg_ == 1 ? W1 : W2);                              \
+        const uint32_t lim_ = seg_ == 0 ? lim0 : (seg_ == 1 ? lim1 : lim2);                      \
+        copy_slice<Tr, VEC>(W_, uint32_t(local_) * rb + lane_off, lim_, ring + (st) * SL, lane); \
+    } while (0)
+
+    // activations (and gains) through this wave's ring area, before any row
+    typename Tr::X xs;
+    stage_vec<Tr>(a.x, a.cols, wave, lane, ring, xs.v);
+    if constexpr (NORM) {
+        float gv[64];
+        stage_vec<Tr>(a.gain, a.cols, wave, lane, ring, gv);
+        // RMSNorm of the activation vector: the waves of a workgroup cover
+        // every column, so each workgroup forms 1/rms itself
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 64; ++i) ss = fmaf(xs.v[i], xs.v[i], ss);
+        ss = ok ? ss : 0.f;
+        ss = wave_sum_to_lane63(ss);
+        if (lane == 63) red[wave] = ss;
+        __syncthreads();
+        float tot = 0.f;
+        for (int w = 0; w < nw; ++w) tot += red[w];
+        const float inv = 1.0f / sqrtf(tot / float(a.cols) + a.eps);
+#pragma unroll
+        for (int i = 0; i < 64; ++i) xs.v[i] = gv[i] * (xs.v[i] * inv);
+    }
+    // S - 1 ring slots (placeholders past the last row, so the count is fixed)
+#pragma unroll
+    for (int j = 0; j < S - 1; ++j) {
+        if (j < n) NT_ISSUE(j, j);
+        else copy_slice<Tr, VEC>(W0, uint32_t(lane * VEC), 0u, ring + j * SL, lane);   // placeholder: 16 bytes
+    }
+    Tr::sums(xs);
+    const uint32_t magic = opaque(kMagicQ4);
+
+    // Row j is decoded from registers while row j+1 is read from LDS and rows
+    // up to j+S-1 are in flight.  Row j sits in ring stage j mod S.
+    typename Tr::Raw ra, rb2;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * NI));    // row 0 has landed
+    __builtin_amdgcn_sched_barrier(0);
+    Tr::load(ring, L, ra);
+    int cs = 0;
+#define NT_STEP(j, cur, nxt)                                                                 \
+    {                                                                                        \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        const int sn = cs + 1 == S ? 0 : cs + 1;                /* stage of row j+1 */       \
+        if ((j) + S - 1 < n) {                                                               \
+            NT_ISSUE((j) + S - 1, cs == 0 ? S - 1 : cs - 1);    /* stage of row j-1 */       \
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * NI)); /* row j+1 has landed */    \
+        } else {                                                                             \
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));                                        \
+        }                                                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        if ((j) + 1 < n) Tr::load(ring + sn * SL, L, nxt);                                   \
+        float v_ = Tr::dot(cur, xs, L, magic);                                               \
+        v_ = ok ? v_ : 0.f;                                                                  \
+        v_ = wave_sum_to_lane63(v_);                                                         \
+        if (lane == 63) part[wave * kMaxRowsPerWG + (j)] = v_;                               \
+        cs = sn;                                                                             \
+    }
+    for (int j = 0; j < n; j += 2) {
+        NT_STEP(j, ra, rb2);
+        if (j + 1 >= n) break;
+        NT_STEP(j + 1, rb2, ra);
+    }
+    __syncthreads();
+
+    // combine the column slices in a fixed order
+    if (pairs) {
+        float *h = a.y[0];
+        for (int t = threadIdx.x; t < nitems; t += blockDim.x) {
+            float g = 0.f, up = 0.f;
+            for (int w = 0; w < nw; ++w) {
+                g += part[w * kMaxRowsPerWG + 2 * t];
+                up += part[w * kMaxRowsPerWG + 2 * t + 1];
+            }
+            h[b + t * G] = g / (1.0f + expf(-g)) * up;
+        }
+    } else {
+        for (int t = threadIdx.x; t < n; t += blockDim.x) {
+            float s = 0.f;
+            for (int w = 0; w < nw; ++w) s += part[w * kMaxRowsPerWG + t];
+            NT_LOCATE(t);
+            float *y = (seg_ == 0 ? a.y[0] : (seg_ == 1 ? a.y[1] : a.y[2])) + local_;
+            *y = a.accumulate ? *y + s : s;
+        }
+    }
+#undef NT_STEP
+#undef NT_ISSUE
+#undef NT_LOCATE
 }
 
 int env_int(const char *name, int dflt) {
@@ -678,68 +817,113 @@ hipError_t launch_generic(const void *W, const float *x, float *y, int64_t rows,
     return hipGetLastError();
 }
 
-struct FastShape {
-    int nw, G;
-    int64_t grid;
+// Per-device facts the launch shape depends on.
+struct DevInfo {
+    int cus = 0;
+    int lds_per_cu = 0;
 };
 
-FastShape fast_shape(int R, int64_t rows, int64_t cols) {
-    static const int waves_env = env_int("NT_GEMV_WAVES", 0);
-    static const int g_env = env_int("NT_GEMV_G", 0);
-    FastShape f;
-    const int units = int(cols / 64);
-    f.nw = (units + 63) / 64;                      // <= 8 for cols <= 32768
-    // groups per tile: 8 for tall matrices, 4 (or 2) when that leaves too few tiles
-    f.G = g_env;
-    if (f.G <= 0) {
-        f.G = 8;
-        while (f.G > 2 && (rows + R * f.G - 1) / (R * f.G) * f.nw < 2048) f.G /= 2;
+DevInfo dev_info() {
+    static DevInfo cache[64];
+    int d = 0;
+    if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) d = 0;
+    DevInfo &di = cache[d];
+    if (di.cus == 0) {
+        int cus = 0, lds = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess || cus <= 0) cus = 256;
+        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, d) != hipSuccess ||
+            lds <= 0)
+            lds = 160 * 1024;
+        di.lds_per_cu = lds;
+        di.cus = cus;
     }
-    const int T = R * f.G;
-    const int64_t ntiles = (rows + T - 1) / T;
-    // persistent grid: about 12 resident waves per CU on 256 CUs
-    const int64_t waves = waves_env > 0 ? waves_env : 256 * 12;
-    f.grid = waves / f.nw;
-    if (f.grid > ntiles) f.grid = ntiles;
-    if (f.grid < 1) f.grid = 1;
-    return f;
+    return di;
 }
 
+struct LdsShape {
+    int nw;
+    int64_t grid;
+    size_t lds;
+    int rows_per_wg;
+};
+
+// Workgroups of nw waves (one per 64-unit column slice), as many as fit on
+// the chip at once (LDS ring size and a target of 8 resident waves per CU),
+// each taking an even share of the rows.
 template <class Tr>
-hipError_t launch_fast(const void *W, const float *x, float *y, int64_t rows, int64_t cols, int64_t row_bytes,
-                       int acc, hipStream_t st) {
-    const int units = int(cols / 64);
-    const FastShape fs = fast_shape(Tr::kRows, rows, cols);
-    const int nw = fs.nw, G = fs.G;
-    const int64_t grid = fs.grid;
-    const uint8_t *w = static_cast<const uint8_t *>(W);
-    const dim3 gd = dim3(unsigned(grid)), bd = dim3(unsigned(64 * nw));
-    switch (G) {
-    case 2: gemv_fast<Tr, 2><<<gd, bd, 0, st>>>(w, x, y, int(rows), row_bytes, units, acc); break;
-    case 4: gemv_fast<Tr, 4><<<gd, bd, 0, st>>>(w, x, y, int(rows), row_bytes, units, acc); break;
-    default: gemv_fast<Tr, 8><<<gd, bd, 0, st>>>(w, x, y, int(rows), row_bytes, units, acc); break;
-    }
+LdsShape lds_shape(int64_t items, int64_t cols, bool pairs) {
+    static const int waves_cu_env = env_int("NT_GEMV_WAVES_CU", 0);
+    const DevInfo di = dev_info();
+    LdsShape s;
+    const int64_t units = cols / 64;
+    s.nw = int((units + 63) / 64);
+    s.lds = size_t(s.nw) * (Tr::kStages * Tr::kSlice + kMaxRowsPerWG * 4) + size_t(s.nw) * 4;
+    const int waves_cu = waves_cu_env > 0 ? waves_cu_env : 8;
+    int64_t per_cu = int64_t(di.lds_per_cu) / int64_t(s.lds);
+    const int64_t by_waves = waves_cu / s.nw > 0 ? waves_cu / s.nw : 1;
+    if (per_cu > by_waves) per_cu = by_waves;
+    if (per_cu < 1) per_cu = 1;
+    int64_t grid = int64_t(di.cus) * per_cu;
+    if (grid > items) grid = items;
+    const int64_t cap = pairs ? kMaxRowsPerWG / 2 : kMaxRowsPerWG;
+    if (grid < (items + cap - 1) / cap) grid = (items + cap - 1) / cap;
+    if (grid < 1) grid = 1;
+    s.grid = grid;
+    const int64_t per = (items + grid - 1) / grid;      // items of workgroup 0, the most
+    s.rows_per_wg = int(pairs ? 2 * per : per);
+    return s;
+}
+
+template <class Tr, int VEC, bool NORM>
+hipError_t launch_lds_inst(const GemvArgs &a, bool pairs, hipStream_t st) {
+    const LdsShape s = lds_shape<Tr>(pairs ? a.rows / 2 : a.rows, a.cols, pairs);
+    // allow the large dynamic LDS ring (a launch that still exceeds the
+    // limit fails and is reported by the launch check below)
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_lds<Tr, VEC, NORM>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       dev_info().lds_per_cu);
+    (void)attr;
+    gemv_lds<Tr, VEC, NORM><<<dim3(unsigned(s.grid)), dim3(unsigned(64 * s.nw)), s.lds, st>>>(a);
     return hipGetLastError();
+}
+
+// VEC = 16 when rows are 16-byte aligned (every Q4_K row is), else 4
+template <class Tr, bool WORD_ROWS>
+hipError_t launch_lds(const GemvArgs &a, bool pairs, bool vec16, hipStream_t st) {
+    const bool norm = a.gain != nullptr;
+    if constexpr (WORD_ROWS) {
+        if (!vec16)
+            return norm ? launch_lds_inst<Tr, 4, true>(a, pairs, st) : launch_lds_inst<Tr, 4, false>(a, pairs, st);
+    }
+    return norm ? launch_lds_inst<Tr, 16, true>(a, pairs, st) : launch_lds_inst<Tr, 16, false>(a, pairs, st);
 }
 
 }  // namespace
 
-static bool use_fast(nt_qtype t, int64_t cols) {
-    // fast path: word-aligned rows (an even number of 2-byte-aligned blocks)
-    // and at most 8 slices of 4096 values
+int64_t gemv_row_bytes(nt_qtype t, int64_t cols) { return cols / block_elems(t) * block_bytes(t); }
+
+bool gemv_fast_ok(nt_qtype t, int64_t rows, int64_t cols) {
     static const bool force_generic = env_int("NT_GEMV_GENERIC", 0) != 0;
-    const int64_t rb = cols / block_elems(t) * block_bytes(t);
-    return !force_generic && rb % 4 == 0 && cols % 64 == 0 && cols <= 32768;
+    const int64_t rb = gemv_row_bytes(t, cols);
+    // word-aligned rows, whole 64-value units, at most 8 column slices, and
+    // byte offsets that fit in 32 bits
+    return !force_generic && rb % 4 == 0 && cols % 64 == 0 && cols > 0 && cols <= 32768 &&
+           rows * rb < (int64_t(1) << 32);
 }
 
 void gemv_launch_info(nt_qtype t, int64_t rows, int64_t cols, int32_t info[4]) {
-    if (use_fast(t, cols)) {
-        const int R = t == NT_Q6_K ? F6K::kRows : t == NT_Q8_0 ? F80::kRows : t == NT_Q4_0 ? F40::kRows : F4K::kRows;
-        const FastShape f = fast_shape(R, rows, cols);
-        info[0] = 1;
-        info[1] = R * f.G;
-        info[2] = int32_t(f.grid);
-        info[3] = 64 * f.nw;
+    if (gemv_fast_ok(t, rows, cols)) {
+        LdsShape s{};
+        switch (t) {
+        case NT_Q8_0: s = lds_shape<F80>(rows, cols, false); break;
+        case NT_Q4_0: s = lds_shape<F40>(rows, cols, false); break;
+        case NT_Q4_K: s = lds_shape<F4K>(rows, cols, false); break;
+        default: s = lds_shape<F6K>(rows, cols, false); break;
+        }
+        info[0] = 1 + (gemv_row_bytes(t, cols) % 16 == 0 ? 1 : 0);   // 2: 16-byte copies, 1: 4-byte
+        info[1] = s.rows_per_wg;
+        info[2] = int32_t(s.grid);
+        info[3] = 64 * s.nw;
     } else {
         const int units = int(cols / 32), upl = units <= 1024 ? 1 : 2;
         const int nw = (units + 64 * upl - 1) / (64 * upl);
@@ -752,21 +936,73 @@ void gemv_launch_info(nt_qtype t, int64_t rows, int64_t cols, int32_t info[4]) {
     }
 }
 
-hipError_t launch_gemv(nt_qtype t, const void *W, const float *x, float *y, int64_t rows,
-                       int64_t cols, int accumulate, hipStream_t st) {
-    const int64_t rb = cols / block_elems(t) * block_bytes(t);
-    const bool fast = use_fast(t, cols);
+hipError_t launch_gemv_fused(nt_qtype t, const GemvArgs &a, bool pairs, hipStream_t st) {
+    const bool vec16 = a.row_bytes % 16 == 0;
     switch (t) {
-    case NT_Q8_0: return fast ? launch_fast<F80>(W, x, y, rows, cols, rb, accumulate, st)
-                              : launch_generic<Q80>(W, x, y, rows, cols, accumulate, st);
-    case NT_Q4_0: return fast ? launch_fast<F40>(W, x, y, rows, cols, rb, accumulate, st)
-                              : launch_generic<Q40>(W, x, y, rows, cols, accumulate, st);
-    case NT_Q4_K: return fast ? launch_fast<F4K>(W, x, y, rows, cols, rb, accumulate, st)
-                              : launch_generic<Q4K>(W, x, y, rows, cols, accumulate, st);
-    case NT_Q6_K: return fast ? launch_fast<F6K>(W, x, y, rows, cols, rb, accumulate, st)
-                              : launch_generic<Q6K>(W, x, y, rows, cols, accumulate, st);
+    case NT_Q8_0: return launch_lds<F80, true>(a, pairs, vec16, st);
+    case NT_Q4_0: return launch_lds<F40, true>(a, pairs, vec16, st);
+    case NT_Q4_K: return launch_lds<F4K, false>(a, pairs, true, st);
+    case NT_Q6_K: return launch_lds<F6K, true>(a, pairs, vec16, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+GemvArgs gemv_args(nt_qtype t, int nseg, const void *const *W, const int64_t *rows, float *const *y, int64_t cols,
+                   const float *x, const float *gain, float eps, int accumulate) {
+    GemvArgs a{};
+    const int64_t rb = gemv_row_bytes(t, cols);
+    const int vec = rb % 16 == 0 ? 16 : 4;
+    int64_t end = 0;
+    for (int s = 0; s < 3; ++s) {
+        const int k = s < nseg ? s : nseg - 1;        // unused slots repeat the last matrix
+        a.W[s] = static_cast<const uint8_t *>(W[k]);
+        a.y[s] = y[k];
+        if (s < nseg) end += rows[s];
+        a.seg_end[s] = int32_t(end);
+        a.seg_lim[s] = uint32_t(rows[k] * rb - vec);
+    }
+    a.x = x;
+    a.gain = gain;
+    a.eps = eps;
+    a.cols = int(cols);
+    a.rows = int(end);
+    a.units = int(cols / 64);
+    a.row_bytes = uint32_t(rb);
+    a.accumulate = accumulate;
+    a.swiglu = 0;
+    return a;
+}
+
+hipError_t launch_gemv(nt_qtype t, const void *W, const float *x, float *y, int64_t rows,
+                       int64_t cols, int accumulate, hipStream_t st) {
+    if (gemv_fast_ok(t, rows, cols)) {
+        const GemvArgs a = gemv_args(t, 1, &W, &rows, &y, cols, x, nullptr, 0.f, accumulate);
+        return launch_gemv_fused(t, a, false, st);
+    }
+    switch (t) {
+    case NT_Q8_0: return launch_generic<Q80>(W, x, y, rows, cols, accumulate, st);
+    case NT_Q4_0: return launch_generic<Q40>(W, x, y, rows, cols, accumulate, st);
+    case NT_Q4_K: return launch_generic<Q4K>(W, x, y, rows, cols, accumulate, st);
+    case NT_Q6_K: return launch_generic<Q6K>(W, x, y, rows, cols, accumulate, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gemv_multi(nt_qtype t, int nseg, const void *const *W, const int64_t *rows, float *const *y,
+                             int64_t cols, const float *x, const float *gain, float eps, int accumulate,
+                             hipStream_t st) {
+    const GemvArgs a = gemv_args(t, nseg, W, rows, y, cols, x, gain, eps, accumulate);
+    return launch_gemv_fused(t, a, false, st);
+}
+
+hipError_t launch_gemv_swiglu(nt_qtype t, const void *Wg, const void *Wu, int64_t rows, int64_t cols,
+                              const float *x, const float *gain, float eps, float *h, hipStream_t st) {
+    const void *W[2] = {Wg, Wu};
+    const int64_t r[2] = {rows, rows};
+    float *y[2] = {h, h};
+    GemvArgs a = gemv_args(t, 2, W, r, y, cols, x, gain, eps, 0);
+    a.swiglu = 1;
+    return launch_gemv_fused(t, a, true, st);
 }
 
 }  // namespace nt

@@ -175,6 +175,32 @@ namespace {
         if (e_ != hipSuccess) return e_;      \
     } while (0)
 
+// ys[i] = W_i . RMSNorm(x, gain) for cnt <= 3 matrices of width cols.  Runs
+// of one format whose shape the LDS-ring kernels take go out as one launch
+// that normalizes x itself; any other matrix reads a normalized copy in nbuf,
+// made once.
+hipError_t norm_gemvs(int cnt, const nt_tensor_ref *mats, const int64_t *rows, float *const *ys, int64_t cols,
+                      const float *x, const float *gain, float eps, float *nbuf, hipStream_t st) {
+    bool have_n = false;
+    for (int i = 0; i < cnt;) {
+        const nt_qtype t = nt_qtype(mats[i].type);
+        if (gemv_fast_ok(t, rows[i], cols)) {
+            int j = i + 1;
+            while (j < cnt && mats[j].type == mats[i].type && gemv_fast_ok(t, rows[j], cols)) ++j;
+            const void *W[3] = {nullptr, nullptr, nullptr};
+            for (int s = i; s < j; ++s) W[s - i] = mats[s].data;
+            NT_TRY(launch_gemv_multi(t, j - i, W, rows + i, ys + i, cols, x, gain, eps, 0, st));
+            i = j;
+        } else {
+            if (!have_n) NT_TRY(launch_rmsnorm(x, gain, nbuf, cols, eps, st));
+            have_n = true;
+            NT_TRY(launch_gemv(t, mats[i].data, nbuf, ys[i], rows[i], cols, 0, st));
+            ++i;
+        }
+    }
+    return hipSuccess;
+}
+
 // One transformer block.  mats[i] follow the blob order.
 hipError_t run_layer(nt_model *m, int l, const nt_tensor_ref *mats, const float *attn_norm, const float *ffn_norm,
                      const int32_t *d_pos, hipStream_t st) {
@@ -185,17 +211,24 @@ hipError_t run_layer(nt_model *m, int l, const nt_tensor_ref *mats, const float 
     const size_t layer_kv = size_t(c.n_kv_heads) * c.ctx_cap * c.head_dim;
     uint16_t *kc = m->w.k_cache + l * layer_kv, *vc = m->w.v_cache + l * layer_kv;
 
-    NT_TRY(launch_rmsnorm(x, attn_norm, n, H, c.rms_eps, st));
-    NT_TRY(launch_gemv(nt_qtype(mats[0].type), mats[0].data, n, q, QD, H, 0, st));
-    NT_TRY(launch_gemv(nt_qtype(mats[1].type), mats[1].data, n, k, KD, H, 0, st));
-    NT_TRY(launch_gemv(nt_qtype(mats[2].type), mats[2].data, n, v, KD, H, 0, st));
+    // attention: q, k, v from the normalized residual, RoPE, cache append + attend
+    const int64_t qkv_rows[3] = {QD, KD, KD};
+    float *const qkv_out[3] = {q, k, v};
+    NT_TRY(norm_gemvs(3, mats, qkv_rows, qkv_out, H, x, attn_norm, c.rms_eps, n, st));
     NT_TRY(launch_rope(q, k, c.n_q_heads, c.n_kv_heads, c.head_dim, d_pos, c.rope_theta, st));
     NT_TRY(launch_attn(m->attn, q, k, v, kc, vc, d_pos, o, m->ws + m->lay.attn, st));
     NT_TRY(launch_gemv(nt_qtype(mats[3].type), mats[3].data, o, x, H, QD, 1, st));
-    NT_TRY(launch_rmsnorm(x, ffn_norm, n, H, c.rms_eps, st));
-    NT_TRY(launch_gemv(nt_qtype(mats[4].type), mats[4].data, n, g, c.ffn, H, 0, st));
-    NT_TRY(launch_gemv(nt_qtype(mats[5].type), mats[5].data, n, u, c.ffn, H, 0, st));
-    NT_TRY(launch_swiglu(g, u, g, c.ffn, st));
+
+    // feed-forward: silu(gate) * up from the normalized residual, then down
+    const nt_qtype tg = nt_qtype(mats[4].type);
+    if (mats[4].type == mats[5].type && gemv_fast_ok(tg, c.ffn, H)) {
+        NT_TRY(launch_gemv_swiglu(tg, mats[4].data, mats[5].data, c.ffn, H, x, ffn_norm, c.rms_eps, g, st));
+    } else {
+        const int64_t ff_rows[2] = {c.ffn, c.ffn};
+        float *const ff_out[2] = {g, u};
+        NT_TRY(norm_gemvs(2, mats + 4, ff_rows, ff_out, H, x, ffn_norm, c.rms_eps, n, st));
+        NT_TRY(launch_swiglu(g, u, g, c.ffn, st));
+    }
     NT_TRY(launch_gemv(nt_qtype(mats[6].type), mats[6].data, g, x, H, c.ffn, 1, st));
     return hipSuccess;
 }
@@ -208,8 +241,9 @@ void resident_mats(const nt_layer_weights &L, nt_tensor_ref *mats) {
 hipError_t head(nt_model *m, int32_t *d_pos, float *logits, int32_t *d_next, hipStream_t st) {
     const nt_model_config &c = m->cfg;
     float *x = m->f(m->lay.x), *n = m->f(m->lay.n);
-    NT_TRY(launch_rmsnorm(x, m->w.output_norm, n, c.hidden, c.rms_eps, st));
-    NT_TRY(launch_gemv(nt_qtype(m->w.output.type), m->w.output.data, n, logits, c.vocab, c.hidden, 0, st));
+    const int64_t rows[1] = {c.vocab};
+    float *const out[1] = {logits};
+    NT_TRY(norm_gemvs(1, &m->w.output, rows, out, c.hidden, x, m->w.output_norm, c.rms_eps, n, st));
     NT_TRY(launch_argmax(logits, c.vocab, d_next, d_pos, st));
     return hipSuccess;
 }

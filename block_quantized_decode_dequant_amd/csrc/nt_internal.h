@@ -30,6 +30,14 @@ hipError_t launch_dequant(nt_qtype t, const void *blocks, float *out, int64_t n,
 hipError_t launch_gemv(nt_qtype t, const void *W, const float *x, float *y, int64_t rows,
                        int64_t cols, int accumulate, hipStream_t st);
 void gemv_launch_info(nt_qtype t, int64_t rows, int64_t cols, int32_t info[4]);
+int64_t gemv_row_bytes(nt_qtype t, int64_t cols);
+// shapes the LDS-ring kernels take (and with them the fused variants below)
+bool gemv_fast_ok(nt_qtype t, int64_t rows, int64_t cols);
+hipError_t launch_gemv_multi(nt_qtype t, int nseg, const void *const *W, const int64_t *rows, float *const *y,
+                             int64_t cols, const float *x, const float *gain, float eps, int accumulate,
+                             hipStream_t st);
+hipError_t launch_gemv_swiglu(nt_qtype t, const void *Wg, const void *Wu, int64_t rows, int64_t cols,
+                              const float *x, const float *gain, float eps, float *h, hipStream_t st);
 hipError_t launch_quantize(nt_qtype t, const float *x, void *blocks, int64_t n, hipStream_t st);
 hipError_t launch_delay(double us, hipStream_t st);
 hipError_t launch_rmsnorm(const float *x, const float *g, float *y, int64_t n, float eps, hipStream_t st);

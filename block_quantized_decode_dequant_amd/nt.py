@@ -65,6 +65,9 @@ def _declare(L):
         "nt_gemv": (st, [i32, vp, vp, vp, i64, i64, i32, vp]),
         "nt_quantize": (st, [i32, vp, vp, i64, vp]),
         "nt_gemv_launch_info": (st, [i32, i64, i64, C.POINTER(C.c_int32)]),
+        "nt_gemv_multi": (st, [i32, i32, C.POINTER(vp), C.POINTER(i64), C.POINTER(vp), i64, vp, vp, C.c_float,
+                               i32, vp]),
+        "nt_gemv_swiglu": (st, [i32, vp, vp, i64, i64, vp, vp, C.c_float, vp, vp]),
         "nt_read_bytes": (st, [vp, i64, vp, vp]),
         "nt_copy_bytes": (st, [vp, vp, i64, vp]),
         "nt_delay": (st, [C.c_double, vp]),
@@ -164,7 +167,32 @@ def nt_gemv_q6_k(W, x, y, rows, cols, accumulate=False, stream=None): nt_gemv(Q6
 def nt_gemv_launch_info(qtype: int, rows: int, cols: int) -> dict:
     info = (C.c_int32 * 4)()
     _check(lib().nt_gemv_launch_info(qtype, rows, cols, info), "nt_gemv_launch_info")
-    return {"fast": bool(info[0]), "tile_rows": info[1], "workgroups": info[2], "threads": info[3]}
+    return {"fast": bool(info[0]), "vec": {2: 16, 1: 4}.get(info[0], 0), "rows_per_wg": info[1],
+            "workgroups": info[2], "threads": info[3]}
+
+
+def nt_gemv_multi(qtype: int, Ws, rows, ys, cols: int, x, gain=None, eps: float = 0.0,
+                  accumulate: bool = False, stream=None):
+    """ys[s] (+)= Ws[s] . n, n = x or RMSNorm(x, gain, eps); up to three matrices."""
+    k = len(Ws)
+    if not (len(rows) == k == len(ys)):
+        raise ValueError("Ws, rows and ys must have the same length")
+    rb = row_bytes(qtype, cols)
+    W_arr = (C.c_void_p * k)(*[_ptr(W, r * rb, "W").value for W, r in zip(Ws, rows)])
+    r_arr = (C.c_int64 * k)(*rows)
+    y_arr = (C.c_void_p * k)(*[_ptr(y, 4 * r, "y").value for y, r in zip(ys, rows)])
+    _check(lib().nt_gemv_multi(qtype, k, W_arr, r_arr, y_arr, cols, _ptr(x, 4 * cols, "x"),
+                               _ptr(gain, 4 * cols, "gain"), float(eps), int(bool(accumulate)), _stream(stream)),
+           "nt_gemv_multi")
+
+
+def nt_gemv_swiglu(qtype: int, W_gate, W_up, rows: int, cols: int, x, h, gain=None, eps: float = 0.0,
+                   stream=None):
+    """h = silu(W_gate . n) * (W_up . n), n = x or RMSNorm(x, gain, eps)."""
+    rb = row_bytes(qtype, cols)
+    _check(lib().nt_gemv_swiglu(qtype, _ptr(W_gate, rows * rb, "W_gate"), _ptr(W_up, rows * rb, "W_up"), rows, cols,
+                                _ptr(x, 4 * cols, "x"), _ptr(gain, 4 * cols, "gain"), float(eps),
+                                _ptr(h, 4 * rows, "h"), _stream(stream)), "nt_gemv_swiglu")
 
 
 # ---- encode -----------------------------------------------------------------------------

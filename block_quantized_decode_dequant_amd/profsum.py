@@ -24,14 +24,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 GEMV_SRC = os.path.join(HERE, "csrc", "gemv.hip")
 
 FMT = {"F80": "q8_0", "F40": "q4_0", "F4K": "q4_k", "F6K": "q6_k"}
-ROWS = {"F80": 2, "F40": 2, "F4K": 2, "F6K": 1}
 
 
 def kernel_key(name: str):
     """The benchmark's name for a GEMV kernel instantiation, or None."""
-    m = re.search(r"gemv_fast<nt::\(anonymous namespace\)::(F\w+), (\d+)>", name)
+    m = re.search(r"gemv_lds<nt::\(anonymous namespace\)::(F\w+), (\d+), (true|false)>", name)
     if m:
-        return f"gemv {FMT[m.group(1)]} fast tile{ROWS[m.group(1)] * int(m.group(2))}"
+        return f"gemv {FMT[m.group(1)]} lds vec{m.group(2)}" + (" +norm" if m.group(3) == "true" else "")
     if "gemv_generic" in name:
         return "gemv generic"
     return None

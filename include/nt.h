@@ -114,10 +114,35 @@ nt_status nt_gemv_q6_k(const void *W, const float *x, float *y, int64_t rows, in
 nt_status nt_gemv(nt_qtype t, const void *W, const float *x, float *y, int64_t rows, int64_t cols,
                   int accumulate, nt_stream stream);
 /* The launch the GEMV calls above would use for this shape (no GPU needed):
- * info[0] = kernel family (1 = fast path: word-aligned rows, cols <= 32768;
- * 0 = generic path), info[1] = rows per workgroup tile (the kernel
- * instantiation), info[2] = workgroups, info[3] = threads per workgroup. */
+ * info[0] = kernel family (2 = LDS-ring path copying 16-byte pieces, 1 = the
+ * same with 4-byte pieces (rows only word-aligned), 0 = generic path),
+ * info[1] = largest number of rows one workgroup reduces, info[2] =
+ * workgroups, info[3] = threads per workgroup.  The LDS-ring path takes rows
+ * whose byte length is a multiple of 4, cols % 64 == 0, cols <= 32768 and
+ * rows * row_bytes below 2^32. */
 nt_status nt_gemv_launch_info(nt_qtype t, int64_t rows, int64_t cols, int32_t info[4]);
+
+/* Fused variants for the decode step (one launch where the step would make
+ * several; each needs a shape the LDS-ring path takes, else NT_ESHAPE):
+ *
+ * nt_gemv_multi: for s in [0, nseg), nseg in 1..3, matrices of one format
+ * and width,  y_s[r] = (accumulate ? y_s[r] : 0) + sum_c W_s[r][c] * n[c]
+ * with n = x, or n = RMSNorm(x, gain, eps) as nt_rmsnorm defines it when gain
+ * is not NULL (each workgroup forms 1/rms itself; nothing is written back).
+ * W, rows, y are host arrays of nseg device pointers / row counts.  This is
+ * the Llama block's q/k/v projection from the normalized residual.
+ *
+ * nt_gemv_swiglu: h[r] = silu(W_gate[r] . n) * (W_up[r] . n), r in [0, rows),
+ * n as above: the block's gate and up projections with the SwiGLU
+ * activation applied to the two row sums before they leave the kernel.
+ *
+ * x, gain, every W_s and y_s (h) 16-byte aligned device memory; outputs must
+ * not overlap inputs. */
+nt_status nt_gemv_multi(nt_qtype t, int32_t nseg, const void *const *W, const int64_t *rows, float *const *y,
+                        int64_t cols, const float *x, const float *gain, float eps, int accumulate,
+                        nt_stream stream);
+nt_status nt_gemv_swiglu(nt_qtype t, const void *W_gate, const void *W_up, int64_t rows, int64_t cols,
+                         const float *x, const float *gain, float eps, float *h, nt_stream stream);
 
 /* ---- per-token ops ("Architecture": RMSNorm, RoPE, SwiGLU, softmax kernels;
  * "Main features": the Llama block) --------------------------------------

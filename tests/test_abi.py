@@ -75,6 +75,49 @@ def test_gemv_argument_errors():
     assert _gemv(nt.Q6_K, A, A, A, 4, 256) == nt.NT_ENODEV   # valid, but no GPU here
 
 
+def _multi(t, Ws, rows, ys, cols, x=A, gain=None, eps=1e-5, acc=0):
+    k = len(Ws)
+    W = (C.c_void_p * k)(*Ws)
+    r = (C.c_int64 * k)(*rows)
+    y = (C.c_void_p * k)(*ys)
+    return nt.lib().nt_gemv_multi(t, k, W, r, y, cols, C.c_void_p(x), C.c_void_p(gain), eps, acc, None)
+
+
+def _swiglu(t, Wg, Wu, rows, cols, x=A, gain=None, h=A, eps=1e-5):
+    return nt.lib().nt_gemv_swiglu(t, C.c_void_p(Wg), C.c_void_p(Wu), rows, cols, C.c_void_p(x),
+                                   C.c_void_p(gain), eps, C.c_void_p(h), None)
+
+
+@no_gpu_only
+def test_fused_gemv_argument_errors():
+    assert _multi(nt.Q4_K, [A, A], [4, 4], [A, A], 2048) == nt.NT_ENODEV     # valid
+    assert _multi(nt.Q4_K, [], [], [], 2048) == nt.NT_EINVAL                 # nseg 0
+    assert _multi(nt.Q4_K, [A] * 4, [1] * 4, [A] * 4, 2048) == nt.NT_EINVAL  # nseg 4
+    assert _multi(nt.Q4_K, [A], [4], [A], 300) == nt.NT_ESHAPE
+    assert _multi(nt.Q6_K, [A], [4], [A], 256) == nt.NT_ESHAPE               # 210-byte rows
+    assert _multi(nt.Q8_0, [A], [4], [A], 65536) == nt.NT_ESHAPE             # too wide for the fused path
+    assert _multi(nt.Q4_K, [A + 4], [4], [A], 2048) == nt.NT_EALIGN
+    assert _multi(nt.Q4_K, [A], [4], [A], 2048, gain=A + 4) == nt.NT_EALIGN
+    assert _multi(nt.Q4_K, [0], [4], [A], 2048) == nt.NT_EINVAL
+    assert _multi(nt.Q4_K, [A], [-1], [A], 2048) == nt.NT_EINVAL
+    assert _multi(nt.Q4_K, [A], [4], [A], 2048, eps=-1.0) == nt.NT_EINVAL
+    assert _multi(nt.Q4_K, [A], [0], [A], 2048) == nt.NT_OK                 # nothing to do
+    assert _swiglu(nt.Q8_0, A, A, 64, 4096) == nt.NT_ENODEV                 # valid
+    assert _swiglu(nt.Q8_0, A, 0, 64, 4096) == nt.NT_EINVAL
+    assert _swiglu(nt.Q6_K, A, A, 64, 256) == nt.NT_ESHAPE
+    assert _swiglu(nt.Q8_0, A, A, 64, 4096, h=A + 8) == nt.NT_EALIGN
+    assert _swiglu(nt.Q8_0, A, A, 0, 4096) == nt.NT_OK
+
+
+def test_launch_info_reports_the_copy_width():
+    assert nt.nt_gemv_launch_info(nt.Q4_K, 8192, 8192)["vec"] == 16
+    assert nt.nt_gemv_launch_info(nt.Q6_K, 8192, 8192)["vec"] == 16
+    assert nt.nt_gemv_launch_info(nt.Q6_K, 64, 1536)["vec"] == 4      # 1260-byte rows
+    assert nt.nt_gemv_launch_info(nt.Q8_0, 64, 320)["vec"] == 4       # 340-byte rows
+    assert not nt.nt_gemv_launch_info(nt.Q6_K, 64, 256)["fast"]       # 210-byte rows
+    assert not nt.nt_gemv_launch_info(nt.Q8_0, 8, 40960)["fast"]      # wider than 32768
+
+
 @no_gpu_only
 def test_dequant_and_calibration_argument_errors():
     L = nt.lib()

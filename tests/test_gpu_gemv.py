@@ -158,3 +158,71 @@ def test_gemv_zero_rows_is_a_no_op():
     y = torch.full((4,), 7.0, device=dev)
     nt.nt_gemv_q4_k(W, x, y, 0, 256)
     assert torch.all(y == 7.0)
+
+
+# ---- LDS-ring path: 4-byte copies (rows only word-aligned), many rows per workgroup ----
+VEC4_CASES = [(O.Q8_0, 9, 320), (O.Q8_0, 20000, 320), (O.Q8_0, 130, 2112), (O.Q4_0, 20000, 320),
+              (O.Q4_0, 130, 2112), (O.Q6_K, 70, 1536), (O.Q6_K, 12000, 1536), (O.Q6_K, 33, 6144)]
+
+
+@pytest.mark.parametrize("t,rows,cols", VEC4_CASES,
+                         ids=[f"{TID[TYPES.index(t)]}-{r}x{c}" for t, r, c in VEC4_CASES])
+def test_gemv_word_aligned_rows_and_deep_ring(t, rows, cols):
+    info = nt.nt_gemv_launch_info(t, rows, cols)
+    assert info["fast"], info
+    _gemv_case(t, rows, cols, seed=rows + 7 * cols)
+
+
+# ---- fused variants: several matrices, RMSNorm prologue, SwiGLU epilogue ---------------
+FUSED_COLS = {O.Q8_0: [2048, 2112], O.Q4_0: [2048, 2112], O.Q4_K: [2048, 4096], O.Q6_K: [2048, 1536]}
+
+
+def _norm_inputs(cols, seed):
+    x = synth.normal_f32(seed, 430, cols, std=3.0)
+    g = (1.0 + synth.normal_f32(seed, 431, cols, std=0.1)).astype(np.float32)
+    return x, g
+
+
+@pytest.mark.parametrize("t", TYPES, ids=TID)
+@pytest.mark.parametrize("norm", [True, False], ids=["norm", "plain"])
+def test_gemv_multi_parity(t, norm):
+    eps = 1e-5
+    for cols in FUSED_COLS[t]:
+        rows = [37, 5, 64]
+        Ws = [_blocks(t, r * cols, 50 + i) for i, r in enumerate(rows)]
+        x, g = _norm_inputs(cols, cols)
+        n = O.rmsnorm(x, g, eps) if norm else x.astype(np.float64)
+        y0 = [synth.normal_f32(cols, 440 + i, r) for i, r in enumerate(rows)]
+        acc = not norm                     # the plain variant also checks accumulate
+        ys = [to_dev(y) if acc else torch.full((r,), 9.0, device=device()) for y, r in zip(y0, rows)]
+        nt.nt_gemv_multi(t, [to_dev(W) for W in Ws], rows, ys, cols, to_dev(x), to_dev(g) if norm else None,
+                         eps, accumulate=acc)
+        for i, (W, r) in enumerate(zip(Ws, rows)):
+            ref = O.gemv(t, W, r, cols, n) + (y0[i].astype(np.float64) if acc else 0.0)
+            assert_close(host(ys[i]), ref, what=f"multi {TID[TYPES.index(t)]} seg {i} cols {cols}")
+
+
+@pytest.mark.parametrize("t", TYPES, ids=TID)
+def test_gemv_swiglu_parity(t):
+    eps = 1e-5
+    for cols in FUSED_COLS[t]:
+        rows = 301
+        Wg, Wu = _blocks(t, rows * cols, 60), _blocks(t, rows * cols, 61)
+        x, g = _norm_inputs(cols, cols + 1)
+        n = O.rmsnorm(x, g, eps)
+        h = torch.full((rows + 8,), 5.0, device=device())
+        nt.nt_gemv_swiglu(t, to_dev(Wg), to_dev(Wu), rows, cols, to_dev(x), h, gain=to_dev(g), eps=eps)
+        got = host(h)
+        assert np.all(got[rows:] == 5.0)
+        ref = O.swiglu(O.gemv(t, Wg, rows, cols, n), O.gemv(t, Wu, rows, cols, n))
+        assert_close(got[:rows], ref, what=f"swiglu {TID[TYPES.index(t)]} cols {cols}")
+
+
+def test_fused_gemv_rejects_shapes_outside_the_fast_path():
+    dev = device()
+    W = torch.zeros(210 * 4, dtype=torch.uint8, device=dev)
+    x = torch.zeros(256, dtype=torch.float32, device=dev)
+    y = torch.zeros(4, dtype=torch.float32, device=dev)
+    with pytest.raises(nt.NTError) as e:
+        nt.nt_gemv_multi(O.Q6_K, [W], [4], [y], 256, x)       # 210-byte rows: not word-aligned
+    assert e.value.status == nt.NT_ESHAPE
