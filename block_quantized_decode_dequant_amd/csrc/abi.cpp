@@ -315,7 +315,8 @@ nt_status nt_attn_decode(const nt_attn_desc *desc, const float *q, const float *
            "nt_attn_decode: need head_dim 64 or 128 and n_q_heads / n_kv_heads in {1, 2, 4, 8}");
     NT_REQ(q && k_cache && v_cache && d_pos && out && workspace, NT_EINVAL, "nt_attn_decode: null pointer");
     NT_REQ((k_new == nullptr) == (v_new == nullptr), NT_EINVAL, "nt_attn_decode: k_new and v_new must both be set or both NULL");
-    NT_REQ(aligned(k_cache, 16) && aligned(v_cache, 16) && aligned(workspace, 16) && aligned(q, 4) &&
+    NT_REQ(desc->rope_theta >= 0.f, NT_EINVAL, "nt_attn_decode: rope_theta must be >= 0");
+    NT_REQ(aligned(k_cache, 16) && aligned(v_cache, 16) && aligned(workspace, 16) && aligned(q, 16) &&
                aligned(out, 4) && aligned(d_pos, 4) && aligned(k_new, 4) && aligned(v_new, 4),
            NT_EALIGN, "nt_attn_decode: misaligned pointer");
     NT_REQ(workspace_bytes >= attn_workspace_bytes(*desc), NT_ENOMEM, "nt_attn_decode: workspace too small");

@@ -1,17 +1,23 @@
 // attn.hip -- grouped-query attention for one decode token over an fp16 KV
-// cache (the write-up's "Main features": GQA and the KV cache; "Roadmap":
-// F16 KV cache; softmax among the "Architecture" kernels).
+// cache (the write-up's "Main features": GQA, RoPE and the KV cache;
+// "Roadmap": F16 KV cache; softmax among the "Architecture" kernels).
 //
 // For q head h in kv group g = h / G (G = n_q_heads / n_kv_heads):
 //   s_t = scale * <q_h, k_{g,t}>,  p = softmax(s over t = 0..pos),
 //   o_h = sum_t p_t v_{g,t}
+// Optionally q and the new k are first rotated by RoPE (adjacent pairs, angle
+// pos * theta^(-2i/D) formed in fp64), so the decode step needs no separate
+// rotation kernel.
+//
 // The context is split into chunks of C positions so that n_kv_heads x chunks
-// workgroups fill the chip; each workgroup reads its chunk of K and V once for
-// all G query heads of the group and leaves (max, sum, unnormalized o) per
-// head; a merge kernel combines the chunks with the log-sum-exp rule in a
-// fixed order.  The current token's k and v are stored at slot pos (rounded to
-// fp16) by the workgroup that owns that slot, which attends to the rounded
-// values, so the cache and the attention agree.  A position outside
+// workgroups fill the chip.  A workgroup first issues every load of its
+// chunk's K and V (each thread holds its share in registers), then computes
+// the G heads' scores, their chunk-local softmax statistics and the
+// unnormalized weighted sum of V, and leaves (max, sum, o[D]) per head.  A
+// merge kernel combines the chunks with the log-sum-exp rule in a fixed order
+// (deterministic).  The current token's k and v are stored at slot pos
+// (rounded to fp16) by the workgroup that owns that slot, which attends to the
+// rounded values, so the cache and the attention agree.  A position outside
 // [0, ctx_cap) writes NaN outputs and touches no memory out of bounds.
 #include "device_util.h"
 #include "nt_internal.h"
@@ -20,172 +26,258 @@ namespace nt {
 namespace {
 
 constexpr int kAttnThreads = 256;
+constexpr int kMaxChunk = 128;
+constexpr int kMergeThreads = 512;
 
 __device__ __forceinline__ uint16_t f2h_bits(float v) { return __half_as_ushort(__float2half_rn(v)); }
-__device__ __forceinline__ float hb2f(uint16_t b) { return __half2float(__ushort_as_half(b)); }
 
-// Sum over aligned groups of 16 lanes (every lane of the group gets it).
-__device__ __forceinline__ float sum16(float v) {
+// Sum over aligned groups of N (8 or 16) lanes; every lane of a group gets it.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
     v += dpp<0xb1>(v);    // xor 1
     v += dpp<0x4e>(v);    // xor 2
-    v += dpp<0x141>(v);   // half-row mirror
-    v += dpp<0x140>(v);   // row mirror
+    v += dpp<0x141>(v);   // half-row mirror: the other quad of the 8
+    if constexpr (N == 16) v += dpp<0x140>(v);   // row mirror: the other 8 of the 16
     return v;
 }
 
-// grid (max_chunks, n_kv_heads); D = head_dim, G = q heads per kv head.
+// grid (chunks, n_kv_heads), 256 threads; D = head_dim, G = q heads per kv head.
 template <int D, int G>
 __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
     const float *__restrict__ q, const float *__restrict__ k_new, const float *__restrict__ v_new,
     uint16_t *__restrict__ kc, uint16_t *__restrict__ vc, const int32_t *__restrict__ d_pos, int ctx_cap,
-    int chunk, float scale, float *__restrict__ part) {
-    constexpr int DL = D / 16;          // dims per lane in the score phase
-    extern __shared__ float sm[];       // p[G][chunk] | knew[D] | vnew[D]
-    float *p = sm;
-    float *knew = sm + G * chunk;
-    float *vnew = knew + D;
+    int chunk, float scale, float theta, float *__restrict__ part) {
+    constexpr int LPP = D / 8;                   // score phase: lanes per position (8 dims each)
+    constexpr int NPS = kAttnThreads / LPP;      // position subsets
+    constexpr int NIK = kMaxChunk / NPS;         // positions per thread, at most
+    constexpr int NDP = D / 2;                   // value phase: dim pairs
+    constexpr int NVS = kAttnThreads / NDP;      // position subsets
+    constexpr int NIV = kMaxChunk / NVS;
+    __shared__ float p[G][kMaxChunk];
+    __shared__ float kn[D], vn[D], rc[D / 2], rs[D / 2];
+    __shared__ float stat[G][2];
+    __shared__ float red[NVS][G][D];
 
     const int pos = *d_pos;
     if (pos < 0 || pos >= ctx_cap) return;          // the merge kernel writes NaNs
-    const int c = blockIdx.x, g = blockIdx.y;
+    const int c = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
     const int t0 = c * chunk;
     if (t0 > pos) return;                           // chunk not reached yet
     const int tn = min(chunk, pos + 1 - t0);        // positions in this chunk
     const int64_t head_base = int64_t(g) * ctx_cap * D;
     const bool owns_new = k_new && pos < t0 + chunk;
 
-    if (owns_new) {
-        for (int d = threadIdx.x; d < D; d += blockDim.x) {
-            const uint16_t kb = f2h_bits(k_new[g * D + d]), vb = f2h_bits(v_new[g * D + d]);
-            kc[head_base + int64_t(pos) * D + d] = kb;
-            vc[head_base + int64_t(pos) * D + d] = vb;
-            knew[d] = hb2f(kb);
-            vnew[d] = hb2f(vb);
-        }
+    // ---- every K and V load of the chunk, issued before anything else ----
+    // K: thread (oc, ps) holds dims 8oc..8oc+7 of positions ps*nik + i
+    const int oc = tid % LPP, ps = tid / LPP, nik = chunk / NPS;
+    uint4 kr[NIK];
+#pragma unroll
+    for (int i = 0; i < NIK; ++i) {
+        const int tt = ps * nik + i;
+        if (i < nik && tt < tn)
+            kr[i] = *reinterpret_cast<const uint4 *>(kc + head_base + int64_t(t0 + tt) * D + 8 * oc);
+    }
+    // V: thread (dp, vs) holds dims 2dp, 2dp+1 of positions vs*niv + i
+    const int dp = tid % NDP, vs = tid / NDP, niv = chunk / NVS;
+    uint32_t vr[NIV];
+#pragma unroll
+    for (int i = 0; i < NIV; ++i) {
+        const int tt = vs * niv + i;
+        if (i < niv && tt < tn)
+            vr[i] = *reinterpret_cast<const uint32_t *>(vc + head_base + int64_t(t0 + tt) * D + 2 * dp);
     }
 
-    // ---- scores: 16 lanes per position, DL dims per lane ----
-    const int grp = threadIdx.x >> 4, l16 = threadIdx.x & 15;
-    float qr[G][DL];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int i = 0; i < DL; ++i) qr[h][i] = q[(g * G + h) * D + l16 * DL + i] * scale;
+    // ---- RoPE angles (fp64), then the new k / v of this step ----
+    const bool rope = theta > 0.f;
+    if (rope && tid < D / 2) {
+        const double w = pow(double(theta), -2.0 * double(tid) / double(D));
+        double sn, cn;
+        sincos(double(pos) * w, &sn, &cn);
+        rc[tid] = float(cn);
+        rs[tid] = float(sn);
+    }
     __syncthreads();
-    const int ngrp = blockDim.x >> 4;
-    for (int tt = grp; tt < ((tn + ngrp - 1) / ngrp) * ngrp; tt += ngrp) {
-        const bool live = tt < tn;
-        const int t = t0 + tt;
-        float kv[DL];
-        if (live && owns_new && t == pos) {
+    if (owns_new && tid < D / 2) {
+        float k0 = k_new[g * D + 2 * tid], k1 = k_new[g * D + 2 * tid + 1];
+        if (rope) {
+            const float a = k0, b = k1;
+            k0 = a * rc[tid] - b * rs[tid];
+            k1 = a * rs[tid] + b * rc[tid];
+        }
+        const uint16_t kb0 = f2h_bits(k0), kb1 = f2h_bits(k1);
+        const uint16_t vb0 = f2h_bits(v_new[g * D + 2 * tid]), vb1 = f2h_bits(v_new[g * D + 2 * tid + 1]);
+        const int64_t at = head_base + int64_t(pos) * D + 2 * tid;
+        *reinterpret_cast<uint32_t *>(kc + at) = uint32_t(kb0) | (uint32_t(kb1) << 16);
+        *reinterpret_cast<uint32_t *>(vc + at) = uint32_t(vb0) | (uint32_t(vb1) << 16);
+        kn[2 * tid] = h2f(kb0);
+        kn[2 * tid + 1] = h2f(kb1);
+        vn[2 * tid] = h2f(vb0);
+        vn[2 * tid + 1] = h2f(vb1);
+    }
+
+    // ---- this thread's q octet for the G heads, rotated and scaled ----
+    float qr[G][8];
 #pragma unroll
-            for (int i = 0; i < DL; ++i) kv[i] = knew[l16 * DL + i];
-        } else if (live) {
-            // DL fp16 values = 16 (D = 128) or 8 (D = 64) contiguous bytes
-            const uint16_t *kp = kc + head_base + int64_t(t) * D + l16 * DL;
-            uint32_t wv[DL / 2];
-            if constexpr (DL == 8) {
-                const uint4 w4 = *reinterpret_cast<const uint4 *>(kp);
-                wv[0] = w4.x; wv[1] = w4.y; wv[2] = w4.z; wv[3] = w4.w;
+    for (int h = 0; h < G; ++h) {
+        const float4 *qp = reinterpret_cast<const float4 *>(q + (g * G + h) * D + 8 * oc);
+        const float4 a = qp[0], b = qp[1];
+        float v8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            float x0 = v8[2 * m], x1 = v8[2 * m + 1];
+            if (rope) {
+                const float cs = rc[4 * oc + m], sn = rs[4 * oc + m];
+                const float r0 = x0 * cs - x1 * sn, r1 = x0 * sn + x1 * cs;
+                x0 = r0;
+                x1 = r1;
+            }
+            qr[h][2 * m] = x0 * scale;
+            qr[h][2 * m + 1] = x1 * scale;
+        }
+    }
+    __syncthreads();                               // kn, vn visible
+
+    // ---- scores ----
+#pragma unroll
+    for (int i = 0; i < NIK; ++i) {
+        const int tt = ps * nik + i;
+        if (i < nik && tt < tn) {                  // uniform over the LPP lanes of a position
+            float kv[8];
+            if (owns_new && t0 + tt == pos) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kv[e] = kn[8 * oc + e];
             } else {
-                const uint2 w2 = *reinterpret_cast<const uint2 *>(kp);
-                wv[0] = w2.x; wv[1] = w2.y;
+                const uint32_t w[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    kv[2 * e] = h_lo(w[e]);
+                    kv[2 * e + 1] = h_hi(w[e]);
+                }
             }
 #pragma unroll
-            for (int i = 0; i < DL / 2; ++i) {
-                kv[2 * i] = hb2f(uint16_t(wv[i]));
-                kv[2 * i + 1] = hb2f(uint16_t(wv[i] >> 16));
+            for (int h = 0; h < G; ++h) {
+                float s = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s = fmaf(qr[h][e], kv[e], s);
+                s = group_sum<LPP>(s);
+                if (oc == 0) p[h][tt] = s;
             }
-        } else {
-#pragma unroll
-            for (int i = 0; i < DL; ++i) kv[i] = 0.f;
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float s = 0.f;
-#pragma unroll
-            for (int i = 0; i < DL; ++i) s = fmaf(qr[h][i], kv[i], s);
-            s = sum16(s);
-            if (live && l16 == 0) p[h * chunk + tt] = s;
         }
     }
     __syncthreads();
 
-    // ---- chunk softmax statistics per head (one wave per head) ----
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
-    float *stat = vnew + D;             // [G][2]: max, sum
-    for (int h = wave; h < G; h += nwave) {
+    // ---- chunk softmax statistics, one wave per head ----
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int h = wave; h < G; h += kAttnThreads / 64) {
         float m = -INFINITY;
-        for (int tt = lane; tt < tn; tt += 64) m = fmaxf(m, p[h * chunk + tt]);
+        for (int tt = lane; tt < tn; tt += 64) m = fmaxf(m, p[h][tt]);
         m = wave_max(m);
         float l = 0.f;
         for (int tt = lane; tt < tn; tt += 64) {
-            const float e = expf(p[h * chunk + tt] - m);
-            p[h * chunk + tt] = e;
+            const float e = expf(p[h][tt] - m);
+            p[h][tt] = e;
             l += e;
         }
         l = wave_sum(l);
-        if (lane == 0) { stat[2 * h] = m; stat[2 * h + 1] = l; }
+        if (lane == 0) {
+            stat[h][0] = m;
+            stat[h][1] = l;
+        }
     }
     __syncthreads();
 
-    // ---- unnormalized o = sum_t p_t v_t: threads over (dim pair, head set) ----
-    constexpr int NP = D / 2;                       // dim pairs
-    const int dp = threadIdx.x % NP, hs = threadIdx.x / NP, nhs = blockDim.x / NP;
+    // ---- unnormalized o = sum_t p_t v_t over this thread's positions ----
     float o0[G], o1[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) { o0[h] = 0.f; o1[h] = 0.f; }
-    for (int tt = 0; tt < tn; ++tt) {
-        const int t = t0 + tt;
-        float v0, v1;
-        if (owns_new && t == pos) {
-            v0 = vnew[2 * dp]; v1 = vnew[2 * dp + 1];
-        } else {
-            const uint32_t w = *reinterpret_cast<const uint32_t *>(vc + head_base + int64_t(t) * D + 2 * dp);
-            v0 = hb2f(uint16_t(w)); v1 = hb2f(uint16_t(w >> 16));
-        }
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-            if (h % nhs == hs) {
-                const float pt = p[h * chunk + tt];
+    for (int i = 0; i < NIV; ++i) {
+        const int tt = vs * niv + i;
+        if (i < niv && tt < tn) {
+            float v0, v1;
+            if (owns_new && t0 + tt == pos) {
+                v0 = vn[2 * dp];
+                v1 = vn[2 * dp + 1];
+            } else {
+                v0 = h_lo(vr[i]);
+                v1 = h_hi(vr[i]);
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float pt = p[h][tt];
                 o0[h] = fmaf(pt, v0, o0[h]);
                 o1[h] = fmaf(pt, v1, o1[h]);
             }
-    }
-    // partial record per (g, c, h): [max, sum, o[0..D)]
-    const int nchunks = gridDim.x;
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-        if (h % nhs == hs) {
-            float *rec = part + ((int64_t(g) * G + h) * nchunks + c) * (D + 2);
-            rec[2 + 2 * dp] = o0[h];
-            rec[2 + 2 * dp + 1] = o1[h];
-            if (dp == 0) { rec[0] = stat[2 * h]; rec[1] = stat[2 * h + 1]; }
         }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        red[vs][h][2 * dp] = o0[h];
+        red[vs][h][2 * dp + 1] = o1[h];
+    }
+    __syncthreads();
+
+    // partial record per (g, h, c): [max, sum, o[0..D)], subsets added in order
+    const int nchunks = gridDim.x;
+    for (int k = tid; k < G * D; k += kAttnThreads) {
+        const int h = k / D, d = k % D;
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < NVS; ++j) s += red[j][h][d];
+        float *rec = part + ((int64_t(g) * G + h) * nchunks + c) * (D + 2);
+        rec[2 + d] = s;
+        if (d == 0) {
+            rec[0] = stat[h][0];
+            rec[1] = stat[h][1];
+        }
+    }
 }
 
-// grid n_q_heads, block D: combines the chunks of head h in chunk order.
+// grid n_q_heads, 512 threads: thread (d, grp) adds the chunks c = grp mod NG
+// of head h; the groups are then added in order.
 template <int D>
-__global__ void __launch_bounds__(256) attn_merge_kernel(const float *__restrict__ part, const int32_t *__restrict__ d_pos,
-                                                        int ctx_cap, int chunk, int nchunks, float *__restrict__ out) {
-    const int h = blockIdx.x, d = threadIdx.x;
+__global__ void __launch_bounds__(kMergeThreads) attn_merge_kernel(const float *__restrict__ part,
+                                                                   const int32_t *__restrict__ d_pos, int ctx_cap,
+                                                                   int chunk, int nchunks, float *__restrict__ out) {
+    constexpr int NG = kMergeThreads / D;
+    extern __shared__ float msm[];               // w[nchunks] | ored[NG][D] | scal[2]
+    float *w = msm;
+    float *ored = w + nchunks;
+    float *scal = ored + NG * D;
+    const int h = blockIdx.x, tid = threadIdx.x, d = tid % D, grp = tid / D;
     const int pos = *d_pos;
     if (pos < 0 || pos >= ctx_cap) {
-        out[h * D + d] = __int_as_float(0x7fc00000);
+        if (grp == 0) out[h * D + d] = __int_as_float(0x7fc00000);
         return;
     }
     const int nact = pos / chunk + 1;
     const float *base = part + int64_t(h) * nchunks * (D + 2);
-    float M = -INFINITY;
-    for (int c = 0; c < nact; ++c) M = fmaxf(M, base[c * (D + 2)]);
-    float L = 0.f, o = 0.f;
-    for (int c = 0; c < nact; ++c) {
-        const float *rec = base + c * (D + 2);
-        const float w = expf(rec[0] - M);
-        L = fmaf(rec[1], w, L);
-        o = fmaf(rec[2 + d], w, o);
+    // chunk maxima -> weights (wave 0, lanes strided over the chunks)
+    if (tid < 64) {
+        float m = -INFINITY;
+        for (int c = tid; c < nact; c += 64) m = fmaxf(m, base[int64_t(c) * (D + 2)]);
+        m = wave_max(m);
+        float l = 0.f;
+        for (int c = tid; c < nact; c += 64) {
+            const float e = expf(base[int64_t(c) * (D + 2)] - m);
+            w[c] = e;
+            l = fmaf(base[int64_t(c) * (D + 2) + 1], e, l);
+        }
+        l = wave_sum(l);
+        if (tid == 0) scal[0] = l;
     }
-    out[h * D + d] = o / L;
+    __syncthreads();
+    float o = 0.f;
+#pragma unroll 8
+    for (int c = grp; c < nact; c += NG) o = fmaf(base[int64_t(c) * (D + 2) + 2 + d], w[c], o);
+    ored[grp * D + d] = o;
+    __syncthreads();
+    if (grp == 0) {
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < NG; ++j) s += ored[j * D + d];
+        out[h * D + d] = s / scal[0];
+    }
 }
 
 template <int D, int G>
@@ -193,10 +285,10 @@ hipError_t launch_dg(const nt_attn_desc &a, int chunk, int nchunks, const float 
                      const float *v_new, uint16_t *kc, uint16_t *vc, const int32_t *d_pos, float *out,
                      float *part, hipStream_t st) {
     const float scale = a.scale > 0.f ? a.scale : 1.0f / sqrtf(float(D));
-    const size_t lds = (size_t(G) * chunk + 2 * D + 2 * G) * sizeof(float);
-    attn_split_kernel<D, G><<<dim3(nchunks, a.n_kv_heads), kAttnThreads, lds, st>>>(
-        q, k_new, v_new, kc, vc, d_pos, a.ctx_cap, chunk, scale, part);
-    attn_merge_kernel<D><<<a.n_q_heads, D, 0, st>>>(part, d_pos, a.ctx_cap, chunk, nchunks, out);
+    attn_split_kernel<D, G><<<dim3(nchunks, a.n_kv_heads), kAttnThreads, 0, st>>>(
+        q, k_new, v_new, kc, vc, d_pos, a.ctx_cap, chunk, scale, a.rope_theta, part);
+    const size_t lds = (size_t(nchunks) + size_t(kMergeThreads) + 2) * sizeof(float);
+    attn_merge_kernel<D><<<a.n_q_heads, kMergeThreads, lds, st>>>(part, d_pos, a.ctx_cap, chunk, nchunks, out);
     return hipGetLastError();
 }
 
@@ -216,11 +308,12 @@ hipError_t launch_d(const nt_attn_desc &a, int chunk, int nchunks, const float *
 }  // namespace
 
 int attn_chunk(const nt_attn_desc &a) {
-    // the largest power-of-two chunk (16..256 positions) that still gives at
-    // least 256 (kv head, chunk) workgroups at full context
+    // the largest power-of-two chunk that still gives at least 256 (kv head,
+    // chunk) workgroups at full context; at least one position per score
+    // subset of the split kernel (16 for head_dim 128, 32 for 64), at most 128
     const int64_t want = int64_t(a.ctx_cap) * a.n_kv_heads / 256;
-    int c = 16;
-    while (2 * c <= want && c < 256) c *= 2;
+    int c = a.head_dim == 64 ? 32 : 16;
+    while (2 * c <= want && c < kMaxChunk) c *= 2;
     return c;
 }
 

@@ -37,6 +37,7 @@ nt_attn_desc attn_of(const nt_model_config &c) {
     a.head_dim = c.head_dim;
     a.ctx_cap = c.ctx_cap;
     a.scale = 0.f;
+    a.rope_theta = c.rope_theta;     // the attention kernel rotates q and k itself
     return a;
 }
 
@@ -211,11 +212,11 @@ hipError_t run_layer(nt_model *m, int l, const nt_tensor_ref *mats, const float 
     const size_t layer_kv = size_t(c.n_kv_heads) * c.ctx_cap * c.head_dim;
     uint16_t *kc = m->w.k_cache + l * layer_kv, *vc = m->w.v_cache + l * layer_kv;
 
-    // attention: q, k, v from the normalized residual, RoPE, cache append + attend
+    // attention: q, k, v from the normalized residual; RoPE, cache append and
+    // attend in the attention kernels
     const int64_t qkv_rows[3] = {QD, KD, KD};
     float *const qkv_out[3] = {q, k, v};
     NT_TRY(norm_gemvs(3, mats, qkv_rows, qkv_out, H, x, attn_norm, c.rms_eps, n, st));
-    NT_TRY(launch_rope(q, k, c.n_q_heads, c.n_kv_heads, c.head_dim, d_pos, c.rope_theta, st));
     NT_TRY(launch_attn(m->attn, q, k, v, kc, vc, d_pos, o, m->ws + m->lay.attn, st));
     NT_TRY(launch_gemv(nt_qtype(mats[3].type), mats[3].data, o, x, H, QD, 1, st));
 

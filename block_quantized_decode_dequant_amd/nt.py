@@ -22,7 +22,7 @@ BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_K: 144, Q6_K: 210}
 
 class AttnDesc(C.Structure):
     _fields_ = [("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
-                ("ctx_cap", C.c_int32), ("scale", C.c_float)]
+                ("ctx_cap", C.c_int32), ("scale", C.c_float), ("rope_theta", C.c_float)]
 
 
 class NTError(RuntimeError):
@@ -249,8 +249,9 @@ def nt_embed(qtype: int, table, vocab: int, hidden: int, d_token, out, stream=No
            "nt_embed")
 
 
-def attn_desc(n_q_heads: int, n_kv_heads: int, head_dim: int, ctx_cap: int, scale: float = 0.0) -> AttnDesc:
-    return AttnDesc(n_q_heads, n_kv_heads, head_dim, ctx_cap, scale)
+def attn_desc(n_q_heads: int, n_kv_heads: int, head_dim: int, ctx_cap: int, scale: float = 0.0,
+              rope_theta: float = 0.0) -> AttnDesc:
+    return AttnDesc(n_q_heads, n_kv_heads, head_dim, ctx_cap, scale, rope_theta)
 
 
 def nt_attn_workspace_bytes(desc: AttnDesc) -> int:

@@ -185,13 +185,17 @@ nt_status nt_embed(nt_qtype t, const void *table, int64_t vocab, int64_t hidden,
  *   2. q head h (of n_q_heads, q device fp32) attends to slots [0, pos] of kv
  *      head h / (n_q_heads / n_kv_heads):  s_t = scale * <q_h, k_t>,
  *      out_h = sum_t softmax(s)_t * v_t   (out: device fp32, n_q_heads * head_dim).
- * scale <= 0 means 1 / sqrt(head_dim).  head_dim must be 64 or 128 and
- * n_q_heads / n_kv_heads one of 1, 2, 4, 8 (NT_ESHAPE).  workspace: device,
- * 16-byte aligned, at least nt_attn_workspace_bytes(desc) bytes (NT_ENOMEM).
- * A pos outside [0, ctx_cap) makes out NaN and writes nothing to the cache. */
+ * scale <= 0 means 1 / sqrt(head_dim).  rope_theta > 0 first rotates q and
+ * k_new by RoPE at pos exactly as nt_rope would (q itself is not modified);
+ * 0 uses them as given.  head_dim must be 64 or 128 and n_q_heads /
+ * n_kv_heads one of 1, 2, 4, 8 (NT_ESHAPE).  workspace: device, 16-byte
+ * aligned, at least nt_attn_workspace_bytes(desc) bytes (NT_ENOMEM).  q and
+ * out 16-byte aligned.  A pos outside [0, ctx_cap) makes out NaN and writes
+ * nothing to the cache. */
 typedef struct {
     int32_t n_q_heads, n_kv_heads, head_dim, ctx_cap;
     float scale;
+    float rope_theta;
 } nt_attn_desc;
 size_t    nt_attn_workspace_bytes(const nt_attn_desc *desc);
 nt_status nt_attn_decode(const nt_attn_desc *desc, const float *q, const float *k_new, const float *v_new,

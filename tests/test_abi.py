@@ -175,4 +175,8 @@ def test_attention_argument_errors():
     assert L.nt_attn_decode(C.byref(good), v(A), v(A), v(0), v(A), v(A), v(A), v(A), v(A), ws, None) == nt.NT_EINVAL
     assert L.nt_attn_decode(*args(good)) == nt.NT_ENODEV
     assert L.nt_attn_decode(*args(good, ws, 0)) == nt.NT_ENODEV      # both NULL is allowed
+    assert L.nt_attn_decode(*args(nt.attn_desc(32, 8, 128, 1152, rope_theta=-1.0))) == nt.NT_EINVAL
+    assert L.nt_attn_decode(*args(nt.attn_desc(32, 8, 128, 1152, rope_theta=5e5))) == nt.NT_ENODEV
+    assert L.nt_attn_decode(C.byref(good), v(A + 4), v(A), v(A), v(A), v(A), v(A), v(A), v(A), ws,
+                            None) == nt.NT_EALIGN                     # q must be 16-byte aligned
     assert nt.nt_attn_workspace_bytes(nt.attn_desc(32, 8, 96, 64)) == 0

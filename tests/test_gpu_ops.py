@@ -131,6 +131,34 @@ def test_attention_decode(hq, hkv, d, ctx, pos):
     assert np.array_equal(host(dk), kc) and np.array_equal(host(dv), vc)
 
 
+ROPE_CASES = [(32, 8, 128, 1152, 1024), (64, 8, 128, 4160, 4100), (4, 2, 64, 96, 70), (8, 8, 64, 64, 5),
+              (16, 8, 128, 300, 299)]
+
+
+@pytest.mark.parametrize("hq,hkv,d,ctx,pos", ROPE_CASES)
+def test_attention_with_rope(hq, hkv, d, ctx, pos):
+    """rope_theta > 0: q and the new k are rotated inside the kernel, exactly
+    what nt_rope followed by nt_attn_decode computes; q is left untouched."""
+    theta = 500000.0
+    q, kn, vn, kc, vc = _attn_inputs(hq, hkv, d, ctx, pos, seed=pos + 2 * ctx)
+    desc = nt.attn_desc(hq, hkv, d, ctx, rope_theta=theta)
+    ws = torch.empty(nt.nt_attn_workspace_bytes(desc), dtype=torch.uint8, device=device())
+    dq, dk, dv = to_dev(q), to_dev(kc), to_dev(vc)
+    out = torch.empty(hq * d, dtype=torch.float32, device=device())
+    nt.nt_attn_decode(desc, dq, to_dev(kn), to_dev(vn), dk, dv, _i32(pos), out, ws)
+    qr = O.rope(q, hq, d, pos, theta)
+    knr = O.rope(kn, hkv, d, pos, theta)
+    ref = O.attention(qr, knr, vn, kc, vc, hq, hkv, d, ctx, pos)    # updates kc, vc too
+    assert_close(host(out), ref, what="attention with rope")
+    assert np.array_equal(host(dq), q), "q was modified"
+    # the stored k may differ from the oracle's by one fp16 step where the
+    # fp32 rotation lands next to a rounding boundary
+    got_k = host(dk).view(np.float16).astype(np.float64)
+    ref_k = kc.view(np.float16).astype(np.float64)
+    assert np.all(np.abs(got_k - ref_k) <= np.abs(ref_k) * 2.0 ** -10 + 2.0 ** -24)
+    assert np.array_equal(host(dv), vc)
+
+
 def test_attention_with_entry_already_cached_and_bad_pos():
     hq, hkv, d, ctx, pos = 32, 8, 128, 1152, 700
     q, kn, vn, kc, vc = _attn_inputs(hq, hkv, d, ctx, pos, seed=3)
