@@ -607,23 +607,38 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >>
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void gbl_void;
 
-// One global_load_lds of V bytes per lane: lane i's bytes land at lds + V*i.
+// One global_load_lds of V bytes per lane: lane i reads base + off (off is
+// per lane, base wave-uniform) and its bytes land at LDS address lds + V*i
+// (lds wave-uniform, through M0).  Written as inline assembly on purpose: the
+// compiler then does not track these LDS writes, so it adds no conservative
+// "wait for every outstanding load" before unrelated LDS reads; every read
+// of a ring stage is preceded by an explicit s_waitcnt on the loads that fill
+// it.  The "memory" clobber keeps the copies ordered against other memory
+// operations in program order.
 template <int V>
-__device__ __forceinline__ void dma(const uint8_t *g, uint8_t *lds) {
+__device__ __forceinline__ void dma(const uint8_t *base, uint32_t off, uint32_t lds) {
     if constexpr (V == 16)
-        __builtin_amdgcn_global_load_lds((gbl_void *)g, (lds_void *)lds, 16, 0, 0);
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                     :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
     else
-        __builtin_amdgcn_global_load_lds((gbl_void *)g, (lds_void *)lds, 4, 0, 0);
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                     :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 
-// Copy one row slice (this wave's part of one row) into an LDS ring stage.
+// LDS address (32-bit, as M0 takes it) of a wave-uniform LDS location.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t((lds_void *)p)));
+}
+
+// Copy one row slice (this wave's part of one row) into the LDS ring stage at
+// LDS address dst.
 template <class Tr, int VEC>
-__device__ __forceinline__ void copy_slice(const uint8_t *W, uint32_t base, uint32_t lim, uint8_t *dst, int lane) {
+__device__ __forceinline__ void copy_slice(const uint8_t *W, uint32_t base, uint32_t lim, uint32_t dst, int lane) {
     using P = Plan<Tr, VEC>;
 #pragma unroll
-    for (int k = 0; k < P::kFull; ++k) dma<VEC>(W + min(base + uint32_t(k * P::kPer), lim), dst + k * P::kPer);
+    for (int k = 0; k < P::kFull; ++k) dma<VEC>(W, min(base + uint32_t(k * P::kPer), lim), dst + k * P::kPer);
     if constexpr (P::kRem > 0) {
-        if (lane < P::kRem / VEC) dma<VEC>(W + min(base + uint32_t(P::kFull * P::kPer), lim), dst + P::kFull * P::kPer);
+        if (lane < P::kRem / VEC) dma<VEC>(W, min(base + uint32_t(P::kFull * P::kPer), lim), dst + P::kFull * P::kPer);
     }
 }
 
@@ -639,13 +654,14 @@ constexpr int kLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
 // chunk Tr::x_chunk(l, j) of the slice.  Past the end of the vector the copy
 // re-reads its last 16 bytes (those values belong to lanes with no columns).
 template <class Tr>
-__device__ __forceinline__ void stage_vec(const float *src, int cols, int wave, int lane, uint8_t *lds, float *v) {
+__device__ __forceinline__ void stage_vec(const float *src, int cols, int wave, int lane, const uint8_t *lds,
+                                          uint32_t lds_a, float *v) {
     const uint8_t *g = reinterpret_cast<const uint8_t *>(src);
     const uint32_t lim = uint32_t(cols) * 4u - 16u, base = uint32_t(wave) * 16384u;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const int p = 64 * k + lane, l = p >> 4, j = ((p & 15) - l) & 15;
-        dma<16>(g + min(base + 16u * Tr::x_chunk(l, j), lim), lds + 1024 * k);
+        dma<16>(g, min(base + 16u * Tr::x_chunk(l, j), lim), lds_a + 1024 * k);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_sched_barrier(0);
@@ -663,11 +679,12 @@ template <class Tr, int VEC, bool NORM>
 __global__ void __launch_bounds__(512) gemv_lds(const GemvArgs a) {
     using P = Plan<Tr, VEC>;
     constexpr int S = P::kStages, SL = Tr::kSlice, NI = P::kInstr;
-    static_assert(S >= 3, "the ring holds a row being read, one being decoded and one in flight");
+    static_assert(S >= 2, "the ring holds the row being read and at least one in flight");
     static_assert(S * SL >= 16384, "the ring must hold a 4096-value activation slice");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     uint8_t *ring = smem + wave * (S * SL);
+    const uint32_t ring_a = lds_addr(ring);                          // the same, as an LDS address
     float *part = reinterpret_cast<float *>(smem + nw * (S * SL));   // [nw][kMaxRowsPerWG]
     float *red = part + nw * kMaxRowsPerWG;                          // [nw]
 
@@ -700,15 +717,15 @@ __global__ void __launch_bounds__(512) gemv_lds(const GemvArgs a) {
         NT_LOCATE(j);                                                                            \
         const uint8_t *W_ = seg_ == 0 ? W0 : (seg_ == 1 ? W1 : W2);                              \
         const uint32_t lim_ = seg_ == 0 ? lim0 : (seg_ == 1 ? lim1 : lim2);                      \
-        copy_slice<Tr, VEC>(W_, uint32_t(local_) * rb + lane_off, lim_, ring + (st) * SL, lane); \
+        copy_slice<Tr, VEC>(W_, uint32_t(local_) * rb + lane_off, lim_, ring_a + (st) * SL, lane); \
     } while (0)
 
     // activations (and gains) through this wave's ring area, before any row
     typename Tr::X xs;
-    stage_vec<Tr>(a.x, a.cols, wave, lane, ring, xs.v);
+    stage_vec<Tr>(a.x, a.cols, wave, lane, ring, ring_a, xs.v);
     if constexpr (NORM) {
         float gv[64];
-        stage_vec<Tr>(a.gain, a.cols, wave, lane, ring, gv);
+        stage_vec<Tr>(a.gain, a.cols, wave, lane, ring, ring_a, gv);
         // RMSNorm of the activation vector: the waves of a workgroup cover
         // every column, so each workgroup forms 1/rms itself
         float ss = 0.f;
@@ -724,19 +741,20 @@ __global__ void __launch_bounds__(512) gemv_lds(const GemvArgs a) {
 #pragma unroll
         for (int i = 0; i < 64; ++i) xs.v[i] = gv[i] * (xs.v[i] * inv);
     }
-    // S - 1 ring slots (placeholders past the last row, so the count is fixed)
+    // S ring slots (placeholders past the last row, so the count is fixed)
 #pragma unroll
-    for (int j = 0; j < S - 1; ++j) {
+    for (int j = 0; j < S; ++j) {
         if (j < n) NT_ISSUE(j, j);
-        else copy_slice<Tr, VEC>(W0, uint32_t(lane * VEC), 0u, ring + j * SL, lane);   // placeholder: 16 bytes
+        else copy_slice<Tr, VEC>(W0, uint32_t(lane * VEC), 0u, ring_a + j * SL, lane);   // placeholder: 16 bytes
     }
     Tr::sums(xs);
     const uint32_t magic = opaque(kMagicQ4);
 
     // Row j is decoded from registers while row j+1 is read from LDS and rows
-    // up to j+S-1 are in flight.  Row j sits in ring stage j mod S.
+    // up to j+S are in flight: row j's stage (j mod S) was read into registers
+    // during the previous step, so it is refilled at once.
     typename Tr::Raw ra, rb2;
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * NI));    // row 0 has landed
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 1) * NI));    // row 0 has landed
     __builtin_amdgcn_sched_barrier(0);
     Tr::load(ring, L, ra);
     int cs = 0;
@@ -744,9 +762,10 @@ __global__ void __launch_bounds__(512) gemv_lds(const GemvArgs a) {
     {                                                                                        \
         __builtin_amdgcn_sched_barrier(0);                                                   \
         const int sn = cs + 1 == S ? 0 : cs + 1;                /* stage of row j+1 */       \
-        if ((j) + S - 1 < n) {                                                               \
-            NT_ISSUE((j) + S - 1, cs == 0 ? S - 1 : cs - 1);    /* stage of row j-1 */       \
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * NI)); /* row j+1 has landed */    \
+        __builtin_amdgcn_s_waitcnt(kLgkm0);           /* row j is in registers, its stage free */ \
+        if ((j) + S < n) {                                                                   \
+            NT_ISSUE((j) + S, cs);                                                           \
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 1) * NI)); /* row j+1 has landed */    \
         } else {                                                                             \
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));                                        \
         }                                                                                    \

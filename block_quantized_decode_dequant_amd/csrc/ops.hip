@@ -110,7 +110,24 @@ __global__ void __launch_bounds__(kBlock) argmax_kernel(const float *__restrict_
     __shared__ int ri[16];
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    int64_t i0 = 0;
+    if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+        // 16-byte loads, several in flight per thread
+        const float4 *x4 = reinterpret_cast<const float4 *>(x);
+        const int64_t n4 = n / 4;
+#pragma unroll 8
+        for (int64_t i = threadIdx.x; i < n4; i += blockDim.x) {
+            const float4 v = x4[i];
+            const int b = int(4 * i);
+            if (better(v.x, b, bv, bi)) { bv = v.x; bi = b; }
+            if (better(v.y, b + 1, bv, bi)) { bv = v.y; bi = b + 1; }
+            if (better(v.z, b + 2, bv, bi)) { bv = v.z; bi = b + 2; }
+            if (better(v.w, b + 3, bv, bi)) { bv = v.w; bi = b + 3; }
+        }
+        i0 = 4 * n4;
+    }
+#pragma unroll 8
+    for (int64_t i = i0 + threadIdx.x; i < n; i += blockDim.x) {
         const float v = x[i];
         if (better(v, int(i), bv, bi)) { bv = v; bi = int(i); }
     }
