@@ -19,6 +19,8 @@
 // (rounded to fp16) by the workgroup that owns that slot, which attends to the
 // rounded values, so the cache and the attention agree.  A position outside
 // [0, ctx_cap) writes NaN outputs and touches no memory out of bounds.
+#include <cmath>
+
 #include "device_util.h"
 #include "nt_internal.h"
 
@@ -28,6 +30,12 @@ namespace {
 constexpr int kAttnThreads = 256;
 constexpr int kMaxChunk = 128;
 constexpr int kMergeThreads = 512;
+
+// RoPE frequencies theta^(-2i/D), i < D/2, formed in fp64 on the host and
+// passed by value (the angle pos * w_i is formed in fp64 on the device).
+struct RopeFreq {
+    double w[64];
+};
 
 __device__ __forceinline__ uint16_t f2h_bits(float v) { return __half_as_ushort(__float2half_rn(v)); }
 
@@ -46,7 +54,7 @@ template <int D, int G>
 __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
     const float *__restrict__ q, const float *__restrict__ k_new, const float *__restrict__ v_new,
     uint16_t *__restrict__ kc, uint16_t *__restrict__ vc, const int32_t *__restrict__ d_pos, int ctx_cap,
-    int chunk, float scale, float theta, float *__restrict__ part) {
+    int chunk, float scale, bool rope, const RopeFreq freq, float *__restrict__ part) {
     constexpr int LPP = D / 8;                   // score phase: lanes per position (8 dims each)
     constexpr int NPS = kAttnThreads / LPP;      // position subsets
     constexpr int NIK = kMaxChunk / NPS;         // positions per thread, at most
@@ -87,14 +95,15 @@ __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
             vr[i] = *reinterpret_cast<const uint32_t *>(vc + head_base + int64_t(t0 + tt) * D + 2 * dp);
     }
 
-    // ---- RoPE angles (fp64), then the new k / v of this step ----
-    const bool rope = theta > 0.f;
+    // ---- RoPE angles: pos * w_i in fp64, reduced to [-pi, pi] in fp64, then
+    // an fp32 sincos (the reduced angle is exact to ~1e-7 rad) ----
     if (rope && tid < D / 2) {
-        const double w = pow(double(theta), -2.0 * double(tid) / double(D));
-        double sn, cn;
-        sincos(double(pos) * w, &sn, &cn);
-        rc[tid] = float(cn);
-        rs[tid] = float(sn);
+        const double ph = double(pos) * freq.w[tid];
+        const double r = fma(-6.283185307179586, rint(ph * 0.15915494309189535), ph);
+        float sn, cn;
+        sincosf(float(r), &sn, &cn);
+        rc[tid] = cn;
+        rs[tid] = sn;
     }
     __syncthreads();
     if (owns_new && tid < D / 2) {
@@ -285,8 +294,12 @@ hipError_t launch_dg(const nt_attn_desc &a, int chunk, int nchunks, const float 
                      const float *v_new, uint16_t *kc, uint16_t *vc, const int32_t *d_pos, float *out,
                      float *part, hipStream_t st) {
     const float scale = a.scale > 0.f ? a.scale : 1.0f / sqrtf(float(D));
+    RopeFreq f{};
+    const bool rope = a.rope_theta > 0.f;
+    if (rope)
+        for (int i = 0; i < D / 2; ++i) f.w[i] = std::pow(double(a.rope_theta), -2.0 * double(i) / double(D));
     attn_split_kernel<D, G><<<dim3(nchunks, a.n_kv_heads), kAttnThreads, 0, st>>>(
-        q, k_new, v_new, kc, vc, d_pos, a.ctx_cap, chunk, scale, a.rope_theta, part);
+        q, k_new, v_new, kc, vc, d_pos, a.ctx_cap, chunk, scale, rope, f, part);
     const size_t lds = (size_t(nchunks) + size_t(kMergeThreads) + 2) * sizeof(float);
     attn_merge_kernel<D><<<a.n_q_heads, kMergeThreads, lds, st>>>(part, d_pos, a.ctx_cap, chunk, nchunks, out);
     return hipGetLastError();

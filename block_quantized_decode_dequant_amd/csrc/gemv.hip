@@ -653,26 +653,34 @@ constexpr int kLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
 // read step j spreads the 64 lanes over all banks; v[4j .. 4j+3] receives
 // chunk Tr::x_chunk(l, j) of the slice.  Past the end of the vector the copy
 // re-reads its last 16 bytes (those values belong to lanes with no columns).
-template <class Tr>
+// With an 8 KB area (HALVES = 2) lanes 0-31 are served first, then 32-63.
+template <class Tr, int HALVES>
 __device__ __forceinline__ void stage_vec(const float *src, int cols, int wave, int lane, const uint8_t *lds,
                                           uint32_t lds_a, float *v) {
+    constexpr int K = 16 / HALVES;                 // 1 KB copies per pass
     const uint8_t *g = reinterpret_cast<const uint8_t *>(src);
     const uint32_t lim = uint32_t(cols) * 4u - 16u, base = uint32_t(wave) * 16384u;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int p = 64 * k + lane, l = p >> 4, j = ((p & 15) - l) & 15;
-        dma<16>(g, min(base + 16u * Tr::x_chunk(l, j), lim), lds_a + 1024 * k);
-    }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __builtin_amdgcn_sched_barrier(0);
+    for (int hv = 0; hv < HALVES; ++hv) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const float4 q = *reinterpret_cast<const float4 *>(lds + 16 * (16 * lane + ((j + lane) & 15)));
-        v[4 * j] = q.x; v[4 * j + 1] = q.y; v[4 * j + 2] = q.z; v[4 * j + 3] = q.w;
+        for (int k = 0; k < K; ++k) {
+            const int p = 64 * (hv * K + k) + lane, l = p >> 4, j = ((p & 15) - l) & 15;
+            dma<16>(g, min(base + 16u * Tr::x_chunk(l, j), lim), lds_a + 1024 * k);
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_sched_barrier(0);
+        if (HALVES == 1 || (lane >> 5) == hv) {
+            const int lh = HALVES == 1 ? lane : lane - 32 * hv;     // lane within this pass's area
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float4 q = *reinterpret_cast<const float4 *>(lds + 16 * (16 * lh + ((j + lane) & 15)));
+                v[4 * j] = q.x; v[4 * j + 1] = q.y; v[4 * j + 2] = q.z; v[4 * j + 3] = q.w;
+            }
+        }
+        // the area is reused as soon as this pass ends: all reads must be done
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        __builtin_amdgcn_sched_barrier(0);
     }
-    // the area is reused as soon as this returns: all reads must be done
-    __builtin_amdgcn_s_waitcnt(kLgkm0);
-    __builtin_amdgcn_sched_barrier(0);
 }
 
 template <class Tr, int VEC, bool NORM>
@@ -680,7 +688,8 @@ __global__ void __launch_bounds__(512) gemv_lds(const GemvArgs a) {
     using P = Plan<Tr, VEC>;
     constexpr int S = P::kStages, SL = Tr::kSlice, NI = P::kInstr;
     static_assert(S >= 2, "the ring holds the row being read and at least one in flight");
-    static_assert(S * SL >= 16384, "the ring must hold a 4096-value activation slice");
+    constexpr int XH = S * SL >= 16384 ? 1 : 2;  // activation staging in one or two passes
+    static_assert(S * SL >= 8192, "the ring must hold half of a 4096-value activation slice");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     uint8_t *ring = smem + wave * (S * SL);
@@ -722,10 +731,10 @@ __global__ void __launch_bounds__(512) gemv_lds(const GemvArgs a) {
 
     // activations (and gains) through this wave's ring area, before any row
     typename Tr::X xs;
-    stage_vec<Tr>(a.x, a.cols, wave, lane, ring, ring_a, xs.v);
+    stage_vec<Tr, XH>(a.x, a.cols, wave, lane, ring, ring_a, xs.v);
     if constexpr (NORM) {
         float gv[64];
-        stage_vec<Tr>(a.gain, a.cols, wave, lane, ring, ring_a, gv);
+        stage_vec<Tr, XH>(a.gain, a.cols, wave, lane, ring, ring_a, gv);
         // RMSNorm of the activation vector: the waves of a workgroup cover
         // every column, so each workgroup forms 1/rms itself
         float ss = 0.f;
@@ -877,7 +886,7 @@ LdsShape lds_shape(int64_t items, int64_t cols, bool pairs) {
     const int64_t units = cols / 64;
     s.nw = int((units + 63) / 64);
     s.lds = size_t(s.nw) * (Tr::kStages * Tr::kSlice + kMaxRowsPerWG * 4) + size_t(s.nw) * 4;
-    const int waves_cu = waves_cu_env > 0 ? waves_cu_env : 8;
+    const int waves_cu = waves_cu_env > 0 ? waves_cu_env : 16;
     int64_t per_cu = int64_t(di.lds_per_cu) / int64_t(s.lds);
     const int64_t by_waves = waves_cu / s.nw > 0 ? waves_cu / s.nw : 1;
     if (per_cu > by_waves) per_cu = by_waves;
