@@ -20,6 +20,7 @@
 // rounded values, so the cache and the attention agree.  A position outside
 // [0, ctx_cap) writes NaN outputs and touches no memory out of bounds.
 #include <cmath>
+#include <cstdlib>
 
 #include "device_util.h"
 #include "nt_internal.h"
@@ -66,9 +67,18 @@ __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
     __shared__ float stat[G][2];
     __shared__ float red[NVS][G][D];
 
+    const int c = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+    // this thread's q octet for the G heads (needs no position: load first)
+    const int oc = tid % LPP, ps = tid / LPP;
+    float4 qa[G], qb[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float4 *qp = reinterpret_cast<const float4 *>(q + (g * G + h) * D + 8 * oc);
+        qa[h] = qp[0];
+        qb[h] = qp[1];
+    }
     const int pos = *d_pos;
     if (pos < 0 || pos >= ctx_cap) return;          // the merge kernel writes NaNs
-    const int c = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
     const int t0 = c * chunk;
     if (t0 > pos) return;                           // chunk not reached yet
     const int tn = min(chunk, pos + 1 - t0);        // positions in this chunk
@@ -77,7 +87,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
 
     // ---- every K and V load of the chunk, issued before anything else ----
     // K: thread (oc, ps) holds dims 8oc..8oc+7 of positions ps*nik + i
-    const int oc = tid % LPP, ps = tid / LPP, nik = chunk / NPS;
+    const int nik = chunk / NPS;
     uint4 kr[NIK];
 #pragma unroll
     for (int i = 0; i < NIK; ++i) {
@@ -124,12 +134,11 @@ __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
         vn[2 * tid + 1] = h2f(vb1);
     }
 
-    // ---- this thread's q octet for the G heads, rotated and scaled ----
+    // ---- the q octets, rotated and scaled ----
     float qr[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        const float4 *qp = reinterpret_cast<const float4 *>(q + (g * G + h) * D + 8 * oc);
-        const float4 a = qp[0], b = qp[1];
+        const float4 a = qa[h], b = qb[h];
         float v8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -321,11 +330,20 @@ hipError_t launch_d(const nt_attn_desc &a, int chunk, int nchunks, const float *
 }  // namespace
 
 int attn_chunk(const nt_attn_desc &a) {
-    // the largest power-of-two chunk that still gives at least 256 (kv head,
-    // chunk) workgroups at full context; at least one position per score
-    // subset of the split kernel (16 for head_dim 128, 32 for 64), at most 128
-    const int64_t want = int64_t(a.ctx_cap) * a.n_kv_heads / 256;
-    int c = a.head_dim == 64 ? 32 : 16;
+    // the largest power-of-two chunk that still gives at least kWantWGs (kv
+    // head, chunk) workgroups at full context: the split kernel is
+    // latency-bound, so parallelism wins over fewer partial records; at least
+    // one position per score subset (16 for head_dim 128, 32 for 64), at most
+    // 128.  NT_ATTN_CHUNK overrides (a power of two in that range).
+    static const int env = [] {
+        const char *v = std::getenv("NT_ATTN_CHUNK");
+        return v ? std::atoi(v) : 0;
+    }();
+    const int lo = a.head_dim == 64 ? 32 : 16;
+    if (env >= lo && env <= kMaxChunk && (env & (env - 1)) == 0) return env;
+    constexpr int kWantWGs = 256;
+    const int64_t want = int64_t(a.ctx_cap) * a.n_kv_heads / kWantWGs;
+    int c = lo;
     while (2 * c <= want && c < kMaxChunk) c *= 2;
     return c;
 }
