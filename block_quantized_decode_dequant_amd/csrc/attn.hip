@@ -77,33 +77,35 @@ __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
         qa[h] = qp[0];
         qb[h] = qp[1];
     }
-    const int pos = *d_pos;
-    if (pos < 0 || pos >= ctx_cap) return;          // the merge kernel writes NaNs
+    // ---- every K and V load of the chunk, issued before the position is
+    // known (rows past the cache end re-read its last row), so the cache
+    // reads overlap the read of *d_pos; rows past pos are loaded and ignored
     const int t0 = c * chunk;
-    if (t0 > pos) return;                           // chunk not reached yet
-    const int tn = min(chunk, pos + 1 - t0);        // positions in this chunk
     const int64_t head_base = int64_t(g) * ctx_cap * D;
-    const bool owns_new = k_new && pos < t0 + chunk;
-
-    // ---- every K and V load of the chunk, issued before anything else ----
     // K: thread (oc, ps) holds dims 8oc..8oc+7 of positions ps*nik + i
     const int nik = chunk / NPS;
     uint4 kr[NIK];
 #pragma unroll
     for (int i = 0; i < NIK; ++i) {
-        const int tt = ps * nik + i;
-        if (i < nik && tt < tn)
-            kr[i] = *reinterpret_cast<const uint4 *>(kc + head_base + int64_t(t0 + tt) * D + 8 * oc);
+        const int t = min(t0 + ps * nik + i, ctx_cap - 1);
+        if (i < nik) kr[i] = *reinterpret_cast<const uint4 *>(kc + head_base + int64_t(t) * D + 8 * oc);
     }
     // V: thread (dp, vs) holds dims 2dp, 2dp+1 of positions vs*niv + i
     const int dp = tid % NDP, vs = tid / NDP, niv = chunk / NVS;
     uint32_t vr[NIV];
 #pragma unroll
     for (int i = 0; i < NIV; ++i) {
-        const int tt = vs * niv + i;
-        if (i < niv && tt < tn)
-            vr[i] = *reinterpret_cast<const uint32_t *>(vc + head_base + int64_t(t0 + tt) * D + 2 * dp);
+        const int t = min(t0 + vs * niv + i, ctx_cap - 1);
+        if (i < niv) vr[i] = *reinterpret_cast<const uint32_t *>(vc + head_base + int64_t(t) * D + 2 * dp);
     }
+
+    const int pos = *d_pos;
+    if (pos < 0 || pos >= ctx_cap || t0 > pos) {    // invalid (the merge writes NaNs) or chunk not reached
+        __builtin_amdgcn_s_waitcnt(0);              // leave with no load outstanding
+        return;
+    }
+    const int tn = min(chunk, pos + 1 - t0);        // positions in this chunk
+    const bool owns_new = k_new && pos < t0 + chunk;
 
     // ---- RoPE angles: pos * w_i in fp64, reduced to [-pi, pi] in fp64, then
     // an fp32 sincos (the reduced angle is exact to ~1e-7 rad) ----
