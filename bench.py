@@ -21,7 +21,7 @@ and the rest streamed from pinned host RAM, each as tok/s against the
 weight-bytes / 8 TB/s bound (or the measured pinned H2D rate).
 
 Flags: --gpus N (only 1 is supported: this path runs on one GPU),
---steps K, --warmup W, --no-cpu-baseline, --decode none|8b|all.
+--steps K, --warmup W, --no-cpu-baseline, --decode none|8b|70b|all.
 """
 from __future__ import annotations
 
@@ -48,8 +48,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--decode", choices=["none", "8b", "all"], default="all",
-                    help="decode measurements: none, the 8B-shaped model, or all (8B, 70B, 70B streamed)")
+    ap.add_argument("--decode", choices=["none", "8b", "70b", "all"], default="all",
+                    help="decode measurements: none, the 8B-shaped model, the resident 70B-shaped model, "
+                         "or all (8B, 70B, 70B streamed)")
     ap.add_argument("--stream-tokens", type=int, default=3)
     return ap.parse_args()
 
@@ -383,9 +384,12 @@ def main():
         "detail": g["detail"],
     }
     if args.decode != "none":
-        dec = {"llama3_8b_q8_0": decode_resident(workloads.LLAMA_8B_Q8_0)}
-        if args.decode == "all":
+        dec = {}
+        if args.decode in ("8b", "all"):
+            dec["llama3_8b_q8_0"] = decode_resident(workloads.LLAMA_8B_Q8_0)
+        if args.decode in ("70b", "all"):
             dec["llama70b_q4_k_q6_k"] = decode_resident(workloads.LLAMA_70B_MIX)
+        if args.decode == "all":
             dec["llama70b_q6_k_streamed_24gib"] = decode_streamed(workloads.LLAMA_70B_Q6K,
                                                                   n_tokens=args.stream_tokens)
         line["decode"] = dec

@@ -59,13 +59,13 @@ __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
     constexpr int LPP = D / 8;                   // score phase: lanes per position (8 dims each)
     constexpr int NPS = kAttnThreads / LPP;      // position subsets
     constexpr int NIK = kMaxChunk / NPS;         // positions per thread, at most
-    constexpr int NDP = D / 2;                   // value phase: dim pairs
-    constexpr int NVS = kAttnThreads / NDP;      // position subsets
+    constexpr int NDQ = D / 4;                   // value phase: dim quads (8 bytes of V)
+    constexpr int NVS = kAttnThreads / NDQ;      // position subsets
     constexpr int NIV = kMaxChunk / NVS;
-    __shared__ float p[G][kMaxChunk];
+    __shared__ __attribute__((aligned(16))) float p[G][kMaxChunk];
     __shared__ float kn[D], vn[D], rc[D / 2], rs[D / 2];
     __shared__ float stat[G][2];
-    __shared__ float red[NVS][G][D];
+    __shared__ __attribute__((aligned(16))) float red[NVS][G][D];
 
     const int c = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
     // this thread's q octet for the G heads (needs no position: load first)
@@ -90,13 +90,13 @@ __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
         const int t = min(t0 + ps * nik + i, ctx_cap - 1);
         if (i < nik) kr[i] = *reinterpret_cast<const uint4 *>(kc + head_base + int64_t(t) * D + 8 * oc);
     }
-    // V: thread (dp, vs) holds dims 2dp, 2dp+1 of positions vs*niv + i
-    const int dp = tid % NDP, vs = tid / NDP, niv = chunk / NVS;
-    uint32_t vr[NIV];
+    // V: thread (dq, vs) holds dims 4dq..4dq+3 of positions vs*niv + i
+    const int dq = tid % NDQ, vs = tid / NDQ, niv = chunk / NVS;
+    uint2 vr[NIV];
 #pragma unroll
     for (int i = 0; i < NIV; ++i) {
         const int t = min(t0 + vs * niv + i, ctx_cap - 1);
-        if (i < niv) vr[i] = *reinterpret_cast<const uint32_t *>(vc + head_base + int64_t(t) * D + 2 * dp);
+        if (i < niv) vr[i] = *reinterpret_cast<const uint2 *>(vc + head_base + int64_t(t) * D + 4 * dq);
     }
 
     const int pos = *d_pos;
@@ -191,15 +191,15 @@ __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
     for (int h = wave; h < G; h += kAttnThreads / 64) {
         float m = -INFINITY;
         for (int tt = lane; tt < tn; tt += 64) m = fmaxf(m, p[h][tt]);
-        m = wave_max(m);
+        m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_max_to_lane63(m)), 63));
         float l = 0.f;
         for (int tt = lane; tt < tn; tt += 64) {
             const float e = expf(p[h][tt] - m);
             p[h][tt] = e;
             l += e;
         }
-        l = wave_sum(l);
-        if (lane == 0) {
+        l = wave_sum_to_lane63(l);
+        if (lane == 63) {
             stat[h][0] = m;
             stat[h][1] = l;
         }
@@ -207,34 +207,36 @@ __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
     __syncthreads();
 
     // ---- unnormalized o = sum_t p_t v_t over this thread's positions ----
-    float o0[G], o1[G];
+    float o[G][4];
 #pragma unroll
-    for (int h = 0; h < G; ++h) { o0[h] = 0.f; o1[h] = 0.f; }
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[h][e] = 0.f;
 #pragma unroll
     for (int i = 0; i < NIV; ++i) {
         const int tt = vs * niv + i;
         if (i < niv && tt < tn) {
-            float v0, v1;
+            float v[4];
             if (owns_new && t0 + tt == pos) {
-                v0 = vn[2 * dp];
-                v1 = vn[2 * dp + 1];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = vn[4 * dq + e];
             } else {
-                v0 = h_lo(vr[i]);
-                v1 = h_hi(vr[i]);
+                v[0] = h_lo(vr[i].x);
+                v[1] = h_hi(vr[i].x);
+                v[2] = h_lo(vr[i].y);
+                v[3] = h_hi(vr[i].y);
             }
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 const float pt = p[h][tt];
-                o0[h] = fmaf(pt, v0, o0[h]);
-                o1[h] = fmaf(pt, v1, o1[h]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[h][e] = fmaf(pt, v[e], o[h][e]);
             }
         }
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        red[vs][h][2 * dp] = o0[h];
-        red[vs][h][2 * dp + 1] = o1[h];
-    }
+    for (int h = 0; h < G; ++h)
+        *reinterpret_cast<float4 *>(&red[vs][h][4 * dq]) = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
     __syncthreads();
 
     // partial record per (g, h, c): [max, sum, o[0..D)], subsets added in order
@@ -336,7 +338,8 @@ int attn_chunk(const nt_attn_desc &a) {
     // head, chunk) workgroups at full context: the split kernel is
     // latency-bound, so parallelism wins over fewer partial records; at least
     // one position per score subset (16 for head_dim 128, 32 for 64), at most
-    // 128.  NT_ATTN_CHUNK overrides (a power of two in that range).
+    // 64 (measured best; up to 128 is supported).  NT_ATTN_CHUNK overrides (a
+    // power of two in [min, 128]).
     static const int env = [] {
         const char *v = std::getenv("NT_ATTN_CHUNK");
         return v ? std::atoi(v) : 0;
@@ -346,7 +349,7 @@ int attn_chunk(const nt_attn_desc &a) {
     constexpr int kWantWGs = 256;
     const int64_t want = int64_t(a.ctx_cap) * a.n_kv_heads / kWantWGs;
     int c = lo;
-    while (2 * c <= want && c < kMaxChunk) c *= 2;
+    while (2 * c <= want && c < 64) c *= 2;
     return c;
 }
 

@@ -83,6 +83,22 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
 __device__ __forceinline__ float h_lo(uint32_t w) { return __half2float(__ushort_as_half(static_cast<unsigned short>(w))); }
 __device__ __forceinline__ float h_hi(uint32_t w) { return __half2float(__ushort_as_half(static_cast<unsigned short>(w >> 16))); }
 
+// DPP-based max over the 64 lanes: the result lands in lane 63.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_keep(float v) {
+    // lanes the row mask leaves out keep their own value (bound_ctrl off, old = v)
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_max_to_lane63(float v) {
+    v = fmaxf(v, dpp_keep<0xb1>(v));
+    v = fmaxf(v, dpp_keep<0x4e>(v));
+    v = fmaxf(v, dpp_keep<0x141>(v));
+    v = fmaxf(v, dpp_keep<0x140>(v));
+    v = fmaxf(v, dpp_keep<0x142, 0xa>(v));
+    v = fmaxf(v, dpp_keep<0x143, 0xc>(v));
+    return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
