@@ -90,6 +90,16 @@ def test_tiny_model_greedy_parity(wtype):
     greedy_parity(cfg, w, n_pos=8, first_token=5, n_steps=6)
 
 
+@pytest.mark.parametrize("graph", [True, False], ids=["graph", "eager"])
+def test_wide_mix_model_uses_fused_paths_throughout(graph):
+    """hidden 2048: q and k (Q4_K) share one fused launch, v (Q6_K) takes its
+    own; every other matrix takes a fused path too (Q6_K down with 4-byte
+    copies)."""
+    cfg = tiny_config(n_layers=2, hidden=2048, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=512)
+    w = build_oracle_model(cfg, seed=15, wtype="mix")
+    greedy_parity(cfg, w, n_pos=5, first_token=3, n_steps=4, graph=graph)
+
+
 def test_tiny_model_eager_path():
     cfg = tiny_config(n_layers=3, n_q_heads=8, n_kv_heads=2)
     w = build_oracle_model(cfg, seed=12, wtype="mix")
