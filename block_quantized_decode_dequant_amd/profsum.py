@@ -2,6 +2,7 @@
 
     python -m block_quantized_decode_dequant_amd.profsum stats KERNEL_STATS.csv [--top N]
     python -m block_quantized_decode_dequant_amd.profsum trace KERNEL_TRACE.csv --match SUBSTR
+    python -m block_quantized_decode_dequant_amd.profsum pertoken KERNEL_TRACE.csv [--skip N]
     python -m block_quantized_decode_dequant_amd.profsum traffic --fetch F.csv --write W.csv \
         --cal-fetch CF.csv --cal-write CW.csv --cal-bytes N --out JSON
 
@@ -65,6 +66,36 @@ def cmd_trace(a):
             print(f"{k:40s} n={len(d):5d} avg_us={sum(d) / len(d):9.3f} min_us={min(d):9.3f} max_us={max(d):9.3f}")
 
 
+def cmd_pertoken(a):
+    """Per-token time of a decode run: the trace between embedding launches
+    (one per token), after --skip warm-up tokens, by kernel and launch shape."""
+    rows = list(csv.DictReader(open(a.csv)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    idx = [i for i, r in enumerate(rows) if "embed_kernel" in r["Kernel_Name"]]
+    skip = min(a.skip, len(idx) - 2)
+    seg = rows[idx[skip]:idx[-1]]
+    ntok = len(idx) - 1 - skip
+    wall = (int(seg[-1]["Start_Timestamp"]) - int(seg[0]["Start_Timestamp"])) / 1e3
+    per, cnt = collections.defaultdict(float), collections.Counter()
+    busy, gaps, prev_end = 0.0, 0.0, None
+    for r in seg:
+        s, e = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        key = (short(r["Kernel_Name"], 44), int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])),
+               int(r["Workgroup_Size_X"]))
+        per[key] += (e - s) / 1e3
+        cnt[key] += 1
+        busy += (e - s) / 1e3
+        if prev_end is not None:
+            gaps += max(0, s - prev_end) / 1e3
+        prev_end = e
+    print(f"tokens {ntok}: wall {wall / ntok:.1f} us/token, kernel time {busy / ntok:.1f} us/token, "
+          f"idle gaps {gaps / ntok:.1f} us/token, {len(seg) / ntok:.1f} launches/token")
+    print(f"{'kernel':44s} {'wg.x':>6s} {'thr':>5s} {'n/tok':>6s} {'avg_us':>8s} {'us/token':>9s} {'%':>6s}")
+    for k, v in sorted(per.items(), key=lambda kv: -kv[1]):
+        print(f"{k[0]:44s} {k[1]:6d} {k[2]:5d} {cnt[k] / ntok:6.1f} {v / cnt[k]:8.2f} {v / ntok:9.1f} "
+              f"{100 * v / busy:6.2f}")
+
+
 def counter_by_kernel(path: str, counter: str):
     """Average counter value (summed over instances) per dispatch, by kernel name."""
     per = collections.defaultdict(lambda: collections.defaultdict(float))
@@ -115,12 +146,15 @@ def main():
     t = sub.add_parser("trace")
     t.add_argument("csv")
     t.add_argument("--match", default="gemv")
+    pt = sub.add_parser("pertoken")
+    pt.add_argument("csv")
+    pt.add_argument("--skip", type=int, default=1)
     r = sub.add_parser("traffic")
     for k in ("fetch", "write", "cal_fetch", "cal_write", "out"):
         r.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
     r.add_argument("--cal-bytes", type=int, default=1 << 28)
     a = ap.parse_args()
-    {"stats": cmd_stats, "trace": cmd_trace, "traffic": cmd_traffic}[a.cmd](a)
+    {"stats": cmd_stats, "trace": cmd_trace, "pertoken": cmd_pertoken, "traffic": cmd_traffic}[a.cmd](a)
 
 
 if __name__ == "__main__":
