@@ -354,26 +354,20 @@ __global__ void __launch_bounds__(1024) gemv_generic(const uint8_t *__restrict__
 // registers the compiler could track.
 // =============================================================================
 
-constexpr uint32_t kMagicQ4 = 0x3c003c00u;   // two fp16 1.0
-constexpr uint32_t kNibQ4 = 0x00f000f0u;     // a nibble at fp16 fraction bits 4..7
 constexpr int kMaxRowsPerWG = 256;           // rows one workgroup reduces (LDS row sums)
 
-// Two fp16 values 1 + q/64 from nibbles already at bits 4..7 and 20..23
-// (v_and_or_b32 with the magic held in a VGPR).  The value keeps q exact; the
-// fp32 sums below carry the leading 1 (removed afterwards), which costs at
-// most 6 bits of the products' precision.
-__device__ __forceinline__ uint32_t nib_pair(uint32_t shifted, uint32_t magic) {
-    return (shifted & kNibQ4) | magic;
-}
-
-// Sum over the 8 nibbles of w of (1 + q/64) * x: low nibbles pair with xl[0..3],
-// high nibbles with xh[0..3] (byte k of w <-> index k).
-__device__ __forceinline__ void nib_fma(uint32_t w, const float *xl, const float *xh, uint32_t magic,
-                                        float &al, float &ah) {
-    const uint32_t c0 = nib_pair(w << 4, magic);   // low nibbles of bytes 0, 2
-    const uint32_t c1 = nib_pair(w >> 4, magic);   // low nibbles of bytes 1, 3
-    const uint32_t c2 = nib_pair(w, magic);        // high nibbles of bytes 0, 2
-    const uint32_t c3 = nib_pair(w >> 8, magic);   // high nibbles of bytes 1, 3
+// Nibble products without a bias term: a 4-bit code in bits 0..3 of an fp16
+// half is the subnormal q * 2^-24, in bits 4..7 the subnormal q * 2^-20, both
+// exact, and v_fma_mix_f32 widens them to fp32 exactly (fp16 denormals are
+// kept).  al collects 2^-24 * sum q x over the low nibbles of w, ah 2^-20 *
+// sum q x over the high nibbles (byte k of w <-> xl[k], xh[k]).  One shift
+// and four masks per 8 codes.
+__device__ __forceinline__ void nib_fma(uint32_t w, const float *xl, const float *xh, float &al, float &ah) {
+    const uint32_t t = w >> 8;
+    const uint32_t c0 = w & 0x000f000fu;   // low nibbles of bytes 0, 2
+    const uint32_t c1 = t & 0x000f000fu;   // low nibbles of bytes 1, 3
+    const uint32_t c2 = w & 0x00f000f0u;   // high nibbles of bytes 0, 2
+    const uint32_t c3 = t & 0x00f000f0u;   // high nibbles of bytes 1, 3
     al = fmaf(h_lo(c0), xl[0], al);
     al = fmaf(h_lo(c1), xl[1], al);
     al = fmaf(h_hi(c0), xl[2], al);
@@ -383,6 +377,9 @@ __device__ __forceinline__ void nib_fma(uint32_t w, const float *xl, const float
     ah = fmaf(h_hi(c2), xh[2], ah);
     ah = fmaf(h_hi(c3), xh[3], ah);
 }
+
+// 2^20 * (16 al + ah): the two nibble sums of nib_fma on one scale
+constexpr float kNib20 = 1048576.0f;
 
 // Sum of N values: pairwise within groups of four, groups added in order.
 template <int N>
@@ -406,7 +403,7 @@ struct F80 {
         const uint8_t *p = base + l.off;
         r.a = ld4(p); r.b = ld4(p + 16); r.c = ld4(p + 32); r.d = ld4(p + 48); r.e = ld1(p + 64);
     }
-    __device__ static float dot(const Raw &r, const X &xs, const L &, uint32_t) {
+    __device__ static float dot(const Raw &r, const X &xs, const L &) {
         const uint32_t w[17] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w,
                                 r.c.x, r.c.y, r.c.z, r.c.w, r.d.x, r.d.y, r.d.z, r.d.w, r.e};
         float s0 = 0.f, s1 = 0.f;
@@ -446,28 +443,28 @@ struct F40 {
         const uint8_t *p = base + l.off;
         r.a = ld4(p); r.b = ld4(p + 16); r.c = ld1(p + 32);
     }
-    // sum over one block of (1 + q/64) x: byte i holds value i (low) and i+16 (high)
-    __device__ static float block_acc(const uint32_t *q, const float *v, uint32_t magic) {
+    // sum over one block of q x: byte i holds value i (low) and i+16 (high)
+    __device__ static float block_acc(const uint32_t *q, const float *v) {
         float al = 0.f, ah = 0.f;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const float xl[4] = {v[4 * m + 0], v[4 * m + 1], v[4 * m + 2], v[4 * m + 3]};
             const float xh[4] = {v[16 + 4 * m + 0], v[16 + 4 * m + 1], v[16 + 4 * m + 2], v[16 + 4 * m + 3]};
-            nib_fma(q[m], xl, xh, magic, al, ah);
+            nib_fma(q[m], xl, xh, al, ah);
         }
-        return al + ah;
+        return kNib20 * fmaf(16.f, al, ah);
     }
-    __device__ static float dot(const Raw &r, const X &xs, const L &, uint32_t magic) {
+    __device__ static float dot(const Raw &r, const X &xs, const L &) {
         const uint32_t w[9] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w, r.c};
         const uint32_t q0[4] = {__builtin_amdgcn_perm(w[1], w[0], 0x05040302u),
                                 __builtin_amdgcn_perm(w[2], w[1], 0x05040302u),
                                 __builtin_amdgcn_perm(w[3], w[2], 0x05040302u),
                                 __builtin_amdgcn_perm(w[4], w[3], 0x05040302u)};
         const uint32_t q1[4] = {w[5], w[6], w[7], w[8]};
-        const float a0 = block_acc(q0, xs.v, magic), a1 = block_acc(q1, xs.v + 32, magic);
-        // sum (q-8) x = 64*(acc - X) - 8X = 64 acc - 72 X
+        const float a0 = block_acc(q0, xs.v), a1 = block_acc(q1, xs.v + 32);
+        // sum (q-8) x = sum q x - 8 X
         const float d0 = h2f(w[0]), d1 = h2f(w[4] >> 16);
-        return fmaf(d0, fmaf(64.f, a0, -72.f * xs.s0), d1 * fmaf(64.f, a1, -72.f * xs.s1));
+        return fmaf(d0, fmaf(-8.f, xs.s0, a0), d1 * fmaf(-8.f, xs.s1, a1));
     }
 };
 
@@ -491,11 +488,11 @@ struct F4K {
         r.q0 = ld4(base + l.off_q);
         r.q1 = ld4(base + l.off_q + 16);
     }
-    __device__ static float dot(const Raw &r, const X &xs, const L &l, uint32_t magic) {
+    __device__ static float dot(const Raw &r, const X &xs, const L &l) {
         const uint32_t q[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
         float al = 0.f, ah = 0.f;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) nib_fma(q[m], xs.v + 4 * m, xs.v + 32 + 4 * m, magic, al, ah);
+        for (int m = 0; m < 8; ++m) nib_fma(q[m], xs.v + 4 * m, xs.v + 32 + 4 * m, al, ah);
         const uint32_t p = l.p, sft = 16 * (p & 1);
         const uint32_t y = r.h.y >> sft, z = r.h.z >> sft, w = r.h.w >> sft;
         // both encodings computed, one kept by a lane mask: no branch
@@ -505,10 +502,10 @@ struct F4K {
         const uint32_t S1 = (((y >> 8) & 63) & lm) | ((((w >> 8) & 15) | (((y >> 14) & 3) << 4)) & hm);
         const uint32_t M1 = (((z >> 8) & 63) & lm) | ((((w >> 12) & 15) | (((z >> 14) & 3) << 4)) & hm);
         const float d = h2f(r.h.x), dmin = h2f(r.h.x >> 16);
-        // sum q x over a sub-block = 64 * (acc - X)
-        const float pos = fmaf(float(S0), al - xs.slo, float(S1) * (ah - xs.shi));
+        // sum q x over sub-block 2p = 2^24 al, over 2p+1 = 2^20 ah
+        const float pos = fmaf(float(16 * S0), al, float(S1) * ah);
         const float neg = fmaf(float(M0), xs.slo, float(M1) * xs.shi);
-        return fmaf(64.f * d, pos, -dmin * neg);
+        return fmaf(kNib20 * d, pos, -dmin * neg);
     }
 };
 
@@ -546,7 +543,7 @@ struct F6K {
         r.sc = ld3(p + 192 + 8 * l.h);
         r.d = ld1(p + 208);
     }
-    __device__ static float dot(const Raw &r, const X &xs, const L &l, uint32_t) {
+    __device__ static float dot(const Raw &r, const X &xs, const L &l) {
         const uint32_t sel = l.sel;
         const uint32_t A[5] = {r.a.x, r.a.y, r.a.z, r.a.w, r.a4};
         const uint32_t B[5] = {r.b.x, r.b.y, r.b.z, r.b.w, r.b4};
@@ -683,43 +680,93 @@ __device__ __forceinline__ void stage_vec(const float *src, int cols, int wave, 
     }
 }
 
-template <class Tr, int VEC, bool NORM>
+// The shared-area variant of the activation copy: pieces k = first,
+// first + step, ... < 16 of column slice `slice` are copied to the 16 KB area
+// at LDS address area (same placement as stage_vec), so the waves that share a
+// slice split the copy between them.
+template <class Tr>
+__device__ __forceinline__ void copy_vec_pieces(const float *src, int cols, int slice, int lane, uint32_t area,
+                                                int first, int step) {
+    const uint8_t *g = reinterpret_cast<const uint8_t *>(src);
+    const uint32_t lim = uint32_t(cols) * 4u - 16u, base = uint32_t(slice) * 16384u;
+    for (int k = first; k < 16; k += step) {
+        const int p = 64 * k + lane, l = p >> 4, j = ((p & 15) - l) & 15;
+        dma<16>(g, min(base + 16u * Tr::x_chunk(l, j), lim), area + 1024 * k);
+    }
+}
+
+// This lane's 64 values of a slice staged by copy_vec_pieces.
+__device__ __forceinline__ void read_vec(const uint8_t *area, int lane, float *v) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const float4 q = *reinterpret_cast<const float4 *>(area + 16 * (16 * lane + ((j + lane) & 15)));
+        v[4 * j] = q.x; v[4 * j + 1] = q.y; v[4 * j + 2] = q.z; v[4 * j + 3] = q.w;
+    }
+}
+
+// One workgroup = `groups` row groups of nw waves; wave w of a group owns
+// column slice w of the rows the group takes.  SHARED: the activations (and
+// gains) are copied once per workgroup into their own LDS area, issued
+// together with the first ring loads so the two latencies overlap; otherwise
+// each wave stages its slice through its own ring before the first row.
+template <class Tr, int VEC, bool NORM, bool SHARED>
 __global__ void __launch_bounds__(512) gemv_lds(const GemvArgs a) {
     using P = Plan<Tr, VEC>;
     constexpr int S = P::kStages, SL = Tr::kSlice, NI = P::kInstr;
     static_assert(S >= 2, "the ring holds the row being read and at least one in flight");
-    constexpr int XH = S * SL >= 16384 ? 1 : 2;  // activation staging in one or two passes
+    constexpr int XH = S * SL >= 16384 ? 1 : 2;  // ring staging in one or two passes
     static_assert(S * SL >= 8192, "the ring must hold half of a 4096-value activation slice");
+    static_assert(!SHARED || S * NI <= 63, "vmcnt range of the first wait");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    uint8_t *ring = smem + wave * (S * SL);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // nw waves per row (one per 4096 columns); row groups only with the
+    // shared area; wave = grp * nw + cw
+    const int nwv = blockDim.x >> 6;
+    const int nw = SHARED ? (a.units + 63) >> 6 : nwv;
+    int cw = wave, grp = 0, R = 1;                  // column slice, row group, groups
+    if constexpr (SHARED) {
+        while (cw >= nw) { cw -= nw; ++grp; }       // at most 7 steps, scalar
+        for (int w = 2 * nw; w <= nwv; w += nw) ++R;
+    }
+    // LDS: [SHARED: activations nw x 16 KB, gains nw x 16 KB] rings, row sums, norm partials
+    uint8_t *const xa = smem;
+    uint8_t *const ga = smem + nw * 16384;
+    uint8_t *const rings = smem + (SHARED ? nw * 16384 * (NORM ? 2 : 1) : 0);
+    uint8_t *ring = rings + wave * (S * SL);
     const uint32_t ring_a = lds_addr(ring);                          // the same, as an LDS address
-    float *part = reinterpret_cast<float *>(smem + nw * (S * SL));   // [nw][kMaxRowsPerWG]
-    float *red = part + nw * kMaxRowsPerWG;                          // [nw]
+    float *part = reinterpret_cast<float *>(rings + nwv * (S * SL));   // [nwv][kMaxRowsPerWG]
+    float *red = part + nwv * kMaxRowsPerWG;                          // [nwv]
 
     // Workgroup b takes items b, b + G, b + 2G, ... (an item is a row, or in
     // SwiGLU mode a gate row and its up row), so at any moment the workgroups
-    // stream one band of neighbouring rows.
+    // stream one band of neighbouring rows; row group g takes the workgroup's
+    // items g, g + R, g + 2R, ...
     const bool pairs = a.swiglu != 0;
     const int G = gridDim.x, b = blockIdx.x;
     const int items = pairs ? a.rows / 2 : a.rows;
-    const int nitems = (items - b + G - 1) / G;
-    const int n = pairs ? 2 * nitems : nitems;       // rows, in ring order
+    const int nitems = (items - b + G - 1) / G;      // items of this workgroup
+    const int mine = SHARED ? (nitems > grp ? (nitems - grp + R - 1) / R : 0) : nitems;
+    const int n = pairs ? 2 * mine : mine;           // rows of this wave, in ring order
 
-    const int u = wave * 64 + lane;
+    const int u = cw * 64 + lane;
     const bool ok = u < a.units;
     const typename Tr::L L = Tr::lane(lane);
-    const uint32_t lane_off = uint32_t(wave) * SL + uint32_t(lane * VEC);
+    const uint32_t lane_off = uint32_t(cw) * SL + uint32_t(lane * VEC);
     const int end0 = a.seg_end[0], end1 = a.seg_end[1];
     const uint32_t rb = a.row_bytes;
     const uint8_t *const W0 = a.W[0], *const W1 = a.W[1], *const W2 = a.W[2];
     const uint32_t lim0 = a.seg_lim[0], lim1 = a.seg_lim[1], lim2 = a.seg_lim[2];
 
-    // row j of this workgroup -> matrix seg_, row local_ within it
-#define NT_LOCATE(j)                                                                        \
-    const int r_ = pairs ? 2 * (b + ((j) >> 1) * G) + ((j) & 1) : b + (j) * G;              \
-    const int seg_ = pairs ? (r_ & 1) : (r_ < end0 ? 0 : (r_ < end1 ? 1 : 2));             \
-    const int local_ = pairs ? (r_ >> 1) : r_ - (seg_ == 0 ? 0 : (seg_ == 1 ? end0 : end1))
+    // global row r -> matrix seg_, row local_ within it
+#define NT_SEG(r)                                                                          \
+    const int seg_ = pairs ? ((r) & 1) : ((r) < end0 ? 0 : ((r) < end1 ? 1 : 2));         \
+    const int local_ = pairs ? ((r) >> 1) : (r) - (seg_ == 0 ? 0 : (seg_ == 1 ? end0 : end1))
+    // ring row j of this wave -> global row
+#define NT_LOCATE(j)                                                                       \
+    const int t_ = grp + (pairs ? ((j) >> 1) : (j)) * R;                                   \
+    const int r_ = pairs ? 2 * (b + t_ * G) + ((j) & 1) : b + t_ * G;                      \
+    NT_SEG(r_)
     // copy row j's slice into ring stage st
 #define NT_ISSUE(j, st)                                                                          \
     do {                                                                                         \
@@ -729,26 +776,19 @@ __global__ void __launch_bounds__(512) gemv_lds(const GemvArgs a) {
         copy_slice<Tr, VEC>(W_, uint32_t(local_) * rb + lane_off, lim_, ring_a + (st) * SL, lane); \
     } while (0)
 
-    // activations (and gains) through this wave's ring area, before any row
     typename Tr::X xs;
-    stage_vec<Tr, XH>(a.x, a.cols, wave, lane, ring, ring_a, xs.v);
-    if constexpr (NORM) {
-        float gv[64];
-        stage_vec<Tr, XH>(a.gain, a.cols, wave, lane, ring, ring_a, gv);
-        // RMSNorm of the activation vector: the waves of a workgroup cover
-        // every column, so each workgroup forms 1/rms itself
-        float ss = 0.f;
-#pragma unroll
-        for (int i = 0; i < 64; ++i) ss = fmaf(xs.v[i], xs.v[i], ss);
-        ss = ok ? ss : 0.f;
-        ss = wave_sum_to_lane63(ss);
-        if (lane == 63) red[wave] = ss;
-        __syncthreads();
-        float tot = 0.f;
-        for (int w = 0; w < nw; ++w) tot += red[w];
-        const float inv = 1.0f / sqrtf(tot / float(a.cols) + a.eps);
-#pragma unroll
-        for (int i = 0; i < 64; ++i) xs.v[i] = gv[i] * (xs.v[i] * inv);
+    float gv[NORM ? 64 : 1];
+    float ss = 0.f;
+    if constexpr (SHARED) {
+        // this wave's share of the activation (and gain) copies; they land
+        // while the first rows are in flight
+        const uint32_t xa_a = lds_addr(xa) + uint32_t(cw) * 16384u;
+        copy_vec_pieces<Tr>(a.x, a.cols, cw, lane, xa_a, grp, R);
+        if constexpr (NORM) copy_vec_pieces<Tr>(a.gain, a.cols, cw, lane, xa_a + uint32_t(nw) * 16384u, grp, R);
+    } else {
+        // activations (and gains) through this wave's ring area, before any row
+        stage_vec<Tr, XH>(a.x, a.cols, cw, lane, ring, ring_a, xs.v);
+        if constexpr (NORM) stage_vec<Tr, XH>(a.gain, a.cols, cw, lane, ring, ring_a, gv);
     }
     // S ring slots (placeholders past the last row, so the count is fixed)
 #pragma unroll
@@ -756,8 +796,35 @@ __global__ void __launch_bounds__(512) gemv_lds(const GemvArgs a) {
         if (j < n) NT_ISSUE(j, j);
         else copy_slice<Tr, VEC>(W0, uint32_t(lane * VEC), 0u, ring_a + j * SL, lane);   // placeholder: 16 bytes
     }
+    if constexpr (SHARED) {
+        // own copies done (the ring loads issued after them may still be in
+        // flight), then every wave's
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(S * NI));
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        read_vec(xa + cw * 16384, lane, xs.v);
+        if constexpr (NORM) read_vec(ga + cw * 16384, lane, gv);
+    }
+    if constexpr (NORM) {
+        // RMSNorm of the activation vector: the nw waves of a row group
+        // cover every column, so each group forms 1/rms itself
+#pragma unroll
+        for (int i = 0; i < 64; ++i) ss = fmaf(xs.v[i], xs.v[i], ss);
+        ss = ok ? ss : 0.f;
+        ss = wave_sum_to_lane63(ss);
+        if (lane == 63) red[wave] = ss;
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        float tot = 0.f;
+        for (int w = 0; w < nw; ++w) tot += red[grp * nw + w];
+        const float inv = 1.0f / sqrtf(tot / float(a.cols) + a.eps);
+#pragma unroll
+        for (int i = 0; i < 64; ++i) xs.v[i] = gv[i] * (xs.v[i] * inv);
+    }
     Tr::sums(xs);
-    const uint32_t magic = opaque(kMagicQ4);
 
     // Row j is decoded from registers while row j+1 is read from LDS and rows
     // up to j+S are in flight: row j's stage (j mod S) was read into registers
@@ -780,7 +847,7 @@ __global__ void __launch_bounds__(512) gemv_lds(const GemvArgs a) {
         }                                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                   \
         if ((j) + 1 < n) Tr::load(ring + sn * SL, L, nxt);                                   \
-        float v_ = Tr::dot(cur, xs, L, magic);                                               \
+        float v_ = Tr::dot(cur, xs, L);                                                      \
         v_ = ok ? v_ : 0.f;                                                                  \
         v_ = wave_sum_to_lane63(v_);                                                         \
         if (lane == 63) part[wave * kMaxRowsPerWG + (j)] = v_;                               \
@@ -791,31 +858,39 @@ __global__ void __launch_bounds__(512) gemv_lds(const GemvArgs a) {
         if (j + 1 >= n) break;
         NT_STEP(j + 1, rb2, ra);
     }
+    // a wave with no rows still has its placeholder copies outstanding
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
 
     // combine the column slices in a fixed order
     if (pairs) {
         float *h = a.y[0];
         for (int t = threadIdx.x; t < nitems; t += blockDim.x) {
-            float g = 0.f, up = 0.f;
+            const int g = t % R, jj = t / R;
+            const float *pp = part + g * nw * kMaxRowsPerWG + 2 * jj;
+            float gs = 0.f, up = 0.f;
             for (int w = 0; w < nw; ++w) {
-                g += part[w * kMaxRowsPerWG + 2 * t];
-                up += part[w * kMaxRowsPerWG + 2 * t + 1];
+                gs += pp[w * kMaxRowsPerWG];
+                up += pp[w * kMaxRowsPerWG + 1];
             }
-            h[b + t * G] = g / (1.0f + expf(-g)) * up;
+            h[b + t * G] = gs / (1.0f + expf(-gs)) * up;
         }
     } else {
-        for (int t = threadIdx.x; t < n; t += blockDim.x) {
-            float s = 0.f;
-            for (int w = 0; w < nw; ++w) s += part[w * kMaxRowsPerWG + t];
-            NT_LOCATE(t);
+        for (int t = threadIdx.x; t < nitems; t += blockDim.x) {
+            const int g = t % R, jj = t / R;
+            const float *pp = part + g * nw * kMaxRowsPerWG + jj;
+            float sum = 0.f;
+            for (int w = 0; w < nw; ++w) sum += pp[w * kMaxRowsPerWG];
+            const int r = b + t * G;
+            NT_SEG(r);
             float *y = (seg_ == 0 ? a.y[0] : (seg_ == 1 ? a.y[1] : a.y[2])) + local_;
-            *y = a.accumulate ? *y + s : s;
+            *y = a.accumulate ? *y + sum : sum;
         }
     }
 #undef NT_STEP
 #undef NT_ISSUE
 #undef NT_LOCATE
+#undef NT_SEG
 }
 
 int env_int(const char *name, int dflt) {
@@ -869,31 +944,57 @@ DevInfo dev_info() {
 }
 
 struct LdsShape {
-    int nw;
+    int nw;              // waves per row group (column slices)
+    int groups;          // row groups per workgroup
+    bool shared;         // activations in their own LDS area
     int64_t grid;
     size_t lds;
     int rows_per_wg;
 };
 
-// Workgroups of nw waves (one per 64-unit column slice), as many as fit on
-// the chip at once (LDS ring size and a target of 8 resident waves per CU),
-// each taking an even share of the rows.
+// Workgroups of `groups` row groups of nw waves (one per 64-unit column
+// slice).  The shared-area layout (one activation copy per workgroup, issued
+// with the first ring loads) suits narrow rows (up to 8192 columns) and, for
+// two-slice rows, the smaller RMSNorm launches, whose gain copy it hides: one
+// large workgroup per CU whose rings take what the activation (and gain)
+// areas leave.  Otherwise each wave stages its own
+// activations and as many single-group workgroups run as fit on a CU (LDS
+// ring size and a target of 16 resident waves per CU), each taking an even
+// share of the rows.
 template <class Tr>
-LdsShape lds_shape(int64_t items, int64_t cols, bool pairs) {
+LdsShape lds_shape(int64_t items, int64_t cols, bool pairs, bool norm, bool vec16) {
     static const int waves_cu_env = env_int("NT_GEMV_WAVES_CU", 0);
+    static const int shared_env = env_int("NT_GEMV_SHARED", -1);
+    static const int groups_env = env_int("NT_GEMV_GROUPS", 0);
     const DevInfo di = dev_info();
     LdsShape s;
     const int64_t units = cols / 64;
     s.nw = int((units + 63) / 64);
-    s.lds = size_t(s.nw) * (Tr::kStages * Tr::kSlice + kMaxRowsPerWG * 4) + size_t(s.nw) * 4;
+    const size_t per_wave = size_t(Tr::kStages) * Tr::kSlice + kMaxRowsPerWG * 4 + 4;
+    const size_t area = size_t(s.nw) * 16384 * (norm ? 2 : 1);
+    const int64_t bytes = items * (pairs ? 2 : 1) * units * (Tr::kSlice / 64);
+    // one column slice: every launch; two: RMSNorm launches up to 48 MB of rows
+    bool shared = vec16 && cols <= 8192 && (s.nw == 1 || (norm && bytes <= (int64_t(48) << 20)));
+    if (shared_env >= 0) shared = vec16 && cols <= 8192 && shared_env > 0;
+    s.groups = 1;
+    if (shared) {
+        int g = 8 / s.nw;
+        while (g > 0 && area + size_t(g) * s.nw * per_wave > size_t(di.lds_per_cu)) --g;
+        if (groups_env > 0 && groups_env < g) g = groups_env;
+        if (g < 1) shared = false;
+        else s.groups = g;
+    }
+    s.shared = shared;
+    const int nwv = s.nw * s.groups;
+    s.lds = (shared ? area : 0) + size_t(nwv) * per_wave;
     const int waves_cu = waves_cu_env > 0 ? waves_cu_env : 16;
     int64_t per_cu = int64_t(di.lds_per_cu) / int64_t(s.lds);
-    const int64_t by_waves = waves_cu / s.nw > 0 ? waves_cu / s.nw : 1;
+    const int64_t by_waves = waves_cu / nwv > 0 ? waves_cu / nwv : 1;
     if (per_cu > by_waves) per_cu = by_waves;
     if (per_cu < 1) per_cu = 1;
     int64_t grid = int64_t(di.cus) * per_cu;
     if (grid > items) grid = items;
-    const int64_t cap = pairs ? kMaxRowsPerWG / 2 : kMaxRowsPerWG;
+    const int64_t cap = int64_t(s.groups) * (pairs ? kMaxRowsPerWG / 2 : kMaxRowsPerWG);
     if (grid < (items + cap - 1) / cap) grid = (items + cap - 1) / cap;
     if (grid < 1) grid = 1;
     s.grid = grid;
@@ -902,28 +1003,31 @@ LdsShape lds_shape(int64_t items, int64_t cols, bool pairs) {
     return s;
 }
 
-template <class Tr, int VEC, bool NORM>
-hipError_t launch_lds_inst(const GemvArgs &a, bool pairs, hipStream_t st) {
-    const LdsShape s = lds_shape<Tr>(pairs ? a.rows / 2 : a.rows, a.cols, pairs);
-    // allow the large dynamic LDS ring (a launch that still exceeds the
+template <class Tr, int VEC, bool NORM, bool SHARED>
+hipError_t launch_lds_inst(const GemvArgs &a, const LdsShape &s, hipStream_t st) {
+    // allow the large dynamic LDS areas (a launch that still exceeds the
     // limit fails and is reported by the launch check below)
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_lds<Tr, VEC, NORM>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                       dev_info().lds_per_cu);
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_lds<Tr, VEC, NORM, SHARED>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, dev_info().lds_per_cu);
     (void)attr;
-    gemv_lds<Tr, VEC, NORM><<<dim3(unsigned(s.grid)), dim3(unsigned(64 * s.nw)), s.lds, st>>>(a);
+    gemv_lds<Tr, VEC, NORM, SHARED><<<dim3(unsigned(s.grid)), dim3(unsigned(64 * s.nw * s.groups)), s.lds, st>>>(a);
     return hipGetLastError();
 }
 
-// VEC = 16 when rows are 16-byte aligned (every Q4_K row is), else 4
+// VEC = 16 when rows are 16-byte aligned (every Q4_K row is), else 4; the
+// shared-area layout only with VEC = 16
 template <class Tr, bool WORD_ROWS>
 hipError_t launch_lds(const GemvArgs &a, bool pairs, bool vec16, hipStream_t st) {
     const bool norm = a.gain != nullptr;
+    const LdsShape s = lds_shape<Tr>(pairs ? a.rows / 2 : a.rows, a.cols, pairs, norm, vec16);
     if constexpr (WORD_ROWS) {
         if (!vec16)
-            return norm ? launch_lds_inst<Tr, 4, true>(a, pairs, st) : launch_lds_inst<Tr, 4, false>(a, pairs, st);
+            return norm ? launch_lds_inst<Tr, 4, true, false>(a, s, st) : launch_lds_inst<Tr, 4, false, false>(a, s, st);
     }
-    return norm ? launch_lds_inst<Tr, 16, true>(a, pairs, st) : launch_lds_inst<Tr, 16, false>(a, pairs, st);
+    if (s.shared)
+        return norm ? launch_lds_inst<Tr, 16, true, true>(a, s, st) : launch_lds_inst<Tr, 16, false, true>(a, s, st);
+    return norm ? launch_lds_inst<Tr, 16, true, false>(a, s, st) : launch_lds_inst<Tr, 16, false, false>(a, s, st);
 }
 
 }  // namespace
@@ -941,17 +1045,18 @@ bool gemv_fast_ok(nt_qtype t, int64_t rows, int64_t cols) {
 
 void gemv_launch_info(nt_qtype t, int64_t rows, int64_t cols, int32_t info[4]) {
     if (gemv_fast_ok(t, rows, cols)) {
+        const bool vec16 = gemv_row_bytes(t, cols) % 16 == 0;
         LdsShape s{};
         switch (t) {
-        case NT_Q8_0: s = lds_shape<F80>(rows, cols, false); break;
-        case NT_Q4_0: s = lds_shape<F40>(rows, cols, false); break;
-        case NT_Q4_K: s = lds_shape<F4K>(rows, cols, false); break;
-        default: s = lds_shape<F6K>(rows, cols, false); break;
+        case NT_Q8_0: s = lds_shape<F80>(rows, cols, false, false, vec16); break;
+        case NT_Q4_0: s = lds_shape<F40>(rows, cols, false, false, vec16); break;
+        case NT_Q4_K: s = lds_shape<F4K>(rows, cols, false, false, vec16); break;
+        default: s = lds_shape<F6K>(rows, cols, false, false, vec16); break;
         }
-        info[0] = 1 + (gemv_row_bytes(t, cols) % 16 == 0 ? 1 : 0);   // 2: 16-byte copies, 1: 4-byte
+        info[0] = 1 + (vec16 ? 1 : 0);   // 2: 16-byte copies, 1: 4-byte
         info[1] = s.rows_per_wg;
         info[2] = int32_t(s.grid);
-        info[3] = 64 * s.nw;
+        info[3] = 64 * s.nw * s.groups;
     } else {
         const int units = int(cols / 32), upl = units <= 1024 ? 1 : 2;
         const int nw = (units + 64 * upl - 1) / (64 * upl);

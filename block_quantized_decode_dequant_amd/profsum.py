@@ -29,9 +29,10 @@ FMT = {"F80": "q8_0", "F40": "q4_0", "F4K": "q4_k", "F6K": "q6_k"}
 
 def kernel_key(name: str):
     """The benchmark's name for a GEMV kernel instantiation, or None."""
-    m = re.search(r"gemv_lds<nt::\(anonymous namespace\)::(F\w+), (\d+), (true|false)>", name)
+    m = re.search(r"gemv_lds<nt::\(anonymous namespace\)::(F\w+), (\d+), (true|false)(?:, (true|false))?>", name)
     if m:
-        return f"gemv {FMT[m.group(1)]} lds vec{m.group(2)}" + (" +norm" if m.group(3) == "true" else "")
+        return (f"gemv {FMT[m.group(1)]} lds vec{m.group(2)}" + (" +norm" if m.group(3) == "true" else "")
+                + (" shared" if m.group(4) == "true" else ""))
     if "gemv_generic" in name:
         return "gemv generic"
     return None

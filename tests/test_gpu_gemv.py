@@ -174,7 +174,10 @@ def test_gemv_word_aligned_rows_and_deep_ring(t, rows, cols):
 
 
 # ---- fused variants: several matrices, RMSNorm prologue, SwiGLU epilogue ---------------
-FUSED_COLS = {O.Q8_0: [2048, 2112], O.Q4_0: [2048, 2112], O.Q4_K: [2048, 4096], O.Q6_K: [2048, 1536]}
+# 2048 / 4096 columns: one column slice (shared activation area, row groups);
+# 8192: two slices (shared area with RMSNorm, per-wave staging without);
+# 2112 / 1536: rows only word-aligned (4-byte copies, per-wave staging)
+FUSED_COLS = {O.Q8_0: [2048, 2112], O.Q4_0: [2048, 2112], O.Q4_K: [2048, 4096, 8192], O.Q6_K: [2048, 1536, 8192]}
 
 
 def _norm_inputs(cols, seed):
@@ -216,6 +219,24 @@ def test_gemv_swiglu_parity(t):
         assert np.all(got[rows:] == 5.0)
         ref = O.swiglu(O.gemv(t, Wg, rows, cols, n), O.gemv(t, Wu, rows, cols, n))
         assert_close(got[:rows], ref, what=f"swiglu {TID[TYPES.index(t)]} cols {cols}")
+
+
+# Shared-area layout at sizes where the row groups refill their rings (more rows per
+# wave than ring stages) and where most row groups have no row at all.
+SHARED_CASES = [(O.Q8_0, 7500, 4096, False), (O.Q8_0, 3, 4096, True), (O.Q4_0, 9000, 2048, True),
+                (O.Q4_K, 5000, 8192, True), (O.Q6_K, 7, 8192, True), (O.Q6_K, 10500, 4096, False)]
+
+
+@pytest.mark.parametrize("t,rows,cols,norm", SHARED_CASES,
+                         ids=[f"{TID[TYPES.index(t)]}-{r}x{c}-{'norm' if n else 'plain'}" for t, r, c, n in SHARED_CASES])
+def test_gemv_shared_activation_layout(t, rows, cols, norm):
+    eps = 1e-5
+    W = _blocks(t, rows * cols, 70 + rows)
+    x, g = _norm_inputs(cols, rows + cols)
+    n = O.rmsnorm(x, g, eps) if norm else x.astype(np.float64)
+    y = torch.full((rows,), 3.0, device=device())
+    nt.nt_gemv_multi(t, [to_dev(W)], [rows], [y], cols, to_dev(x), to_dev(g) if norm else None, eps)
+    assert_close(host(y), O.gemv(t, W, rows, cols, n), what=f"shared {TID[TYPES.index(t)]} {rows}x{cols}")
 
 
 def test_fused_gemv_rejects_shapes_outside_the_fast_path():
