@@ -348,10 +348,11 @@ __global__ void __launch_bounds__(1024) gemv_generic(const uint8_t *__restrict__
 // is copied from HBM into a per-wave LDS ring by global_load_lds (each
 // instruction moves 64 x VEC contiguous bytes, fully coalesced, straight into
 // LDS without passing through VGPRs); a lane then reads its own unit back
-// from LDS.  The ring keeps kStages - 1 rows in flight per wave, so about
-// 8 waves per CU keep ~100 KB of weight reads outstanding per CU.  Waits are
-// explicit (s_waitcnt vmcnt) because the ring's loads return to LDS, not to
-// registers the compiler could track.
+// from LDS.  The ring keeps kStages - 1 rows in flight per wave (one), so 8
+// waves per CU keep 20-35 KB of weight reads outstanding per CU, about what
+// HBM latency times bandwidth needs.  Waits are explicit (s_waitcnt vmcnt)
+// because the ring's loads return to LDS, not to registers the compiler could
+// track.
 // =============================================================================
 
 constexpr int kMaxRowsPerWG = 256;           // rows one workgroup reduces (LDS row sums)
@@ -392,7 +393,7 @@ __device__ __forceinline__ float sum_vals(const float *v) {
 
 // ---- Q8_0 fast: one lane = blocks 2u, 2u+1 (68 bytes at 68u, word-aligned) --
 struct F80 {
-    static constexpr int kSlice = 64 * 68, kStages = 4;
+    static constexpr int kSlice = 64 * 68, kStages = 2;
     struct L { uint32_t off; };
     struct X { float v[64]; float s0, s1; };
     struct Raw { u32x4 a, b, c, d; uint32_t e; };
@@ -432,7 +433,7 @@ struct F80 {
 
 // ---- Q4_0 fast: one lane = blocks 2u, 2u+1 (36 bytes at 36u, word-aligned) --
 struct F40 {
-    static constexpr int kSlice = 64 * 36, kStages = 8;
+    static constexpr int kSlice = 64 * 36, kStages = 2;
     struct L { uint32_t off; };
     struct X { float v[64]; float s0, s1; };
     struct Raw { u32x4 a, b; uint32_t c; };
@@ -472,7 +473,7 @@ struct F40 {
 // byte 32p + i: low nibble = value 64p + i (sub-block 2p), high nibble = value
 // 64p + 32 + i (sub-block 2p+1).
 struct F4K {
-    static constexpr int kSlice = 16 * 144, kStages = 8;
+    static constexpr int kSlice = 16 * 144, kStages = 2;
     struct L { uint32_t off_h, off_q, p; };
     struct X { float v[64]; float slo, shi; };   // v[i]: value 64p+i (lo: i<32, hi: i>=32)
     struct Raw { u32x4 h, q0, q1; };
@@ -516,7 +517,7 @@ struct F4K {
 // qh[32h + 16j + i] (bits 2k..2k+1), scales[8h + 2k + j] and d.  Odd blocks
 // start 2 bytes into a word: loads are word-aligned and v_perm realigns.
 struct F6K {
-    static constexpr int kSlice = 16 * 210, kStages = 5;
+    static constexpr int kSlice = 16 * 210, kStages = 2;
     struct L { uint32_t base, sel, h, j; };
     struct X { float v[64]; float s[4]; };       // v[16k + i]
     struct Raw { u32x4 a; uint32_t a4; u32x4 b; uint32_t b4; u32x4 c; uint32_t c4; u32x3 sc; uint32_t d; };
@@ -644,40 +645,32 @@ constexpr int kLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
 
 // A wave's 64 lanes need 64 activations each: 4096 consecutive values, 16 KB
 // (the wave's column slice).  Loading them lane by lane would touch 64 cache
-// lines per instruction; instead the slice is copied into LDS by 16
-// coalesced 1 KB copies and each lane reads its 16 chunks of 16 bytes back.
+// lines per instruction; instead the slice is copied into a 16 KB LDS area by
+// 16 coalesced 1 KB copies and each lane reads its 16 chunks of 16 bytes back.
 // The copy places chunk j of lane l at LDS chunk 16 l + (j + l) mod 16, so a
 // read step j spreads the 64 lanes over all banks; v[4j .. 4j+3] receives
 // chunk Tr::x_chunk(l, j) of the slice.  Past the end of the vector the copy
 // re-reads its last 16 bytes (those values belong to lanes with no columns).
-// With an 8 KB area (HALVES = 2) lanes 0-31 are served first, then 32-63.
-template <class Tr, int HALVES>
+template <class Tr>
 __device__ __forceinline__ void stage_vec(const float *src, int cols, int wave, int lane, const uint8_t *lds,
                                           uint32_t lds_a, float *v) {
-    constexpr int K = 16 / HALVES;                 // 1 KB copies per pass
     const uint8_t *g = reinterpret_cast<const uint8_t *>(src);
     const uint32_t lim = uint32_t(cols) * 4u - 16u, base = uint32_t(wave) * 16384u;
 #pragma unroll
-    for (int hv = 0; hv < HALVES; ++hv) {
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int p = 64 * (hv * K + k) + lane, l = p >> 4, j = ((p & 15) - l) & 15;
-            dma<16>(g, min(base + 16u * Tr::x_chunk(l, j), lim), lds_a + 1024 * k);
-        }
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        __builtin_amdgcn_sched_barrier(0);
-        if (HALVES == 1 || (lane >> 5) == hv) {
-            const int lh = HALVES == 1 ? lane : lane - 32 * hv;     // lane within this pass's area
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float4 q = *reinterpret_cast<const float4 *>(lds + 16 * (16 * lh + ((j + lane) & 15)));
-                v[4 * j] = q.x; v[4 * j + 1] = q.y; v[4 * j + 2] = q.z; v[4 * j + 3] = q.w;
-            }
-        }
-        // the area is reused as soon as this pass ends: all reads must be done
-        __builtin_amdgcn_s_waitcnt(kLgkm0);
-        __builtin_amdgcn_sched_barrier(0);
+    for (int k = 0; k < 16; ++k) {
+        const int p = 64 * k + lane, l = p >> 4, j = ((p & 15) - l) & 15;
+        dma<16>(g, min(base + 16u * Tr::x_chunk(l, j), lim), lds_a + 1024 * k);
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const float4 q = *reinterpret_cast<const float4 *>(lds + 16 * (16 * lane + ((j + lane) & 15)));
+        v[4 * j] = q.x; v[4 * j + 1] = q.y; v[4 * j + 2] = q.z; v[4 * j + 3] = q.w;
+    }
+    // the area is reused as soon as the reads are done
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // The shared-area variant of the activation copy: pieces k = first,
@@ -714,8 +707,9 @@ __global__ void __launch_bounds__(512) gemv_lds(const GemvArgs a) {
     using P = Plan<Tr, VEC>;
     constexpr int S = P::kStages, SL = Tr::kSlice, NI = P::kInstr;
     static_assert(S >= 2, "the ring holds the row being read and at least one in flight");
-    constexpr int XH = S * SL >= 16384 ? 1 : 2;  // ring staging in one or two passes
-    static_assert(S * SL >= 8192, "the ring must hold half of a 4096-value activation slice");
+    // per-wave LDS: the ring, at least 16 KB so that one activation slice
+    // can be staged through it before the first row
+    constexpr int RS = SHARED ? S * SL : (S * SL > 16384 ? S * SL : 16384);
     static_assert(!SHARED || S * NI <= 63, "vmcnt range of the first wait");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63;
@@ -733,9 +727,9 @@ __global__ void __launch_bounds__(512) gemv_lds(const GemvArgs a) {
     uint8_t *const xa = smem;
     uint8_t *const ga = smem + nw * 16384;
     uint8_t *const rings = smem + (SHARED ? nw * 16384 * (NORM ? 2 : 1) : 0);
-    uint8_t *ring = rings + wave * (S * SL);
+    uint8_t *ring = rings + wave * RS;
     const uint32_t ring_a = lds_addr(ring);                          // the same, as an LDS address
-    float *part = reinterpret_cast<float *>(rings + nwv * (S * SL));   // [nwv][kMaxRowsPerWG]
+    float *part = reinterpret_cast<float *>(rings + nwv * RS);        // [nwv][kMaxRowsPerWG]
     float *red = part + nwv * kMaxRowsPerWG;                          // [nwv]
 
     // Workgroup b takes items b, b + G, b + 2G, ... (an item is a row, or in
@@ -787,8 +781,8 @@ __global__ void __launch_bounds__(512) gemv_lds(const GemvArgs a) {
         if constexpr (NORM) copy_vec_pieces<Tr>(a.gain, a.cols, cw, lane, xa_a + uint32_t(nw) * 16384u, grp, R);
     } else {
         // activations (and gains) through this wave's ring area, before any row
-        stage_vec<Tr, XH>(a.x, a.cols, cw, lane, ring, ring_a, xs.v);
-        if constexpr (NORM) stage_vec<Tr, XH>(a.gain, a.cols, cw, lane, ring, ring_a, gv);
+        stage_vec<Tr>(a.x, a.cols, cw, lane, ring, ring_a, xs.v);
+        if constexpr (NORM) stage_vec<Tr>(a.gain, a.cols, cw, lane, ring, ring_a, gv);
     }
     // S ring slots (placeholders past the last row, so the count is fixed)
 #pragma unroll
@@ -953,14 +947,15 @@ struct LdsShape {
 };
 
 // Workgroups of `groups` row groups of nw waves (one per 64-unit column
-// slice).  The shared-area layout (one activation copy per workgroup, issued
-// with the first ring loads) suits narrow rows (up to 8192 columns) and, for
-// two-slice rows, the smaller RMSNorm launches, whose gain copy it hides: one
-// large workgroup per CU whose rings take what the activation (and gain)
-// areas leave.  Otherwise each wave stages its own
-// activations and as many single-group workgroups run as fit on a CU (LDS
-// ring size and a target of 16 resident waves per CU), each taking an even
-// share of the rows.
+// slice), 8 waves per CU.  Each wave keeps one row in flight while it decodes
+// the previous one (a two-stage ring): measured on this part, a streaming read
+// through LDS reaches its best rate with about 32 KB in flight per CU (8
+// waves, 4 KB each), and deeper rings or more waves lose bandwidth.  Rows of up
+// to two column slices (8192 columns) use the shared layout: one workgroup of
+// up to 8 waves per CU, activations (and gains) copied once per workgroup into
+// an area of their own while the first rows are in flight.  Wider rows: each
+// wave stages its slice through a 16 KB area that then holds its ring.  The
+// workgroups take even shares of the rows.
 template <class Tr>
 LdsShape lds_shape(int64_t items, int64_t cols, bool pairs, bool norm, bool vec16) {
     static const int waves_cu_env = env_int("NT_GEMV_WAVES_CU", 0);
@@ -970,24 +965,23 @@ LdsShape lds_shape(int64_t items, int64_t cols, bool pairs, bool norm, bool vec1
     LdsShape s;
     const int64_t units = cols / 64;
     s.nw = int((units + 63) / 64);
-    const size_t per_wave = size_t(Tr::kStages) * Tr::kSlice + kMaxRowsPerWG * 4 + 4;
+    const size_t ring = size_t(Tr::kStages) * Tr::kSlice;
     const size_t area = size_t(s.nw) * 16384 * (norm ? 2 : 1);
-    const int64_t bytes = items * (pairs ? 2 : 1) * units * (Tr::kSlice / 64);
-    // one column slice: every launch; two: RMSNorm launches up to 48 MB of rows
-    bool shared = vec16 && cols <= 8192 && (s.nw == 1 || (norm && bytes <= (int64_t(48) << 20)));
-    if (shared_env >= 0) shared = vec16 && cols <= 8192 && shared_env > 0;
+    // rows of up to two column slices (8192 columns) use the shared layout
+    bool shared = vec16 && cols <= 8192;
+    if (shared_env >= 0) shared = shared && shared_env > 0;
+    const size_t per_wave = (shared ? ring : (ring > 16384 ? ring : 16384)) + kMaxRowsPerWG * 4 + 4;
     s.groups = 1;
     if (shared) {
         int g = 8 / s.nw;
         while (g > 0 && area + size_t(g) * s.nw * per_wave > size_t(di.lds_per_cu)) --g;
         if (groups_env > 0 && groups_env < g) g = groups_env;
-        if (g < 1) shared = false;
-        else s.groups = g;
+        s.groups = g > 0 ? g : 1;      // two slices and their areas always fit one group
     }
     s.shared = shared;
     const int nwv = s.nw * s.groups;
     s.lds = (shared ? area : 0) + size_t(nwv) * per_wave;
-    const int waves_cu = waves_cu_env > 0 ? waves_cu_env : 16;
+    const int waves_cu = waves_cu_env > 0 ? waves_cu_env : 8;
     int64_t per_cu = int64_t(di.lds_per_cu) / int64_t(s.lds);
     const int64_t by_waves = waves_cu / nwv > 0 ? waves_cu / nwv : 1;
     if (per_cu > by_waves) per_cu = by_waves;
