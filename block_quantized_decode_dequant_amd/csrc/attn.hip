@@ -63,20 +63,18 @@ __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
     constexpr int NVS = kAttnThreads / NDQ;      // position subsets
     constexpr int NIV = kMaxChunk / NVS;
     __shared__ __attribute__((aligned(16))) float p[G][kMaxChunk];
-    __shared__ float kn[D], vn[D], rc[D / 2], rs[D / 2];
+    __shared__ __attribute__((aligned(16))) float qs[G * D];   // the G heads' q, rotated and scaled
+    __shared__ float kn[D], vn[D];
     __shared__ float stat[G][2];
     __shared__ __attribute__((aligned(16))) float red[NVS][G][D];
 
     const int c = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
-    // this thread's q octet for the G heads (needs no position: load first)
+    // the G heads' q, 4 values per thread (needs no position: load first)
+    constexpr int NQ = G * D / 4;                // threads holding q values
+    static_assert(NQ <= kAttnThreads, "one float4 of q per thread");
+    float4 q4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (tid < NQ) q4 = reinterpret_cast<const float4 *>(q + g * G * D)[tid];
     const int oc = tid % LPP, ps = tid / LPP;
-    float4 qa[G], qb[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const float4 *qp = reinterpret_cast<const float4 *>(q + (g * G + h) * D + 8 * oc);
-        qa[h] = qp[0];
-        qb[h] = qp[1];
-    }
     // ---- every K and V load of the chunk, issued before the position is
     // known (rows past the cache end re-read its last row), so the cache
     // reads overlap the read of *d_pos; rows past pos are loaded and ignored
@@ -107,23 +105,38 @@ __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
     const int tn = min(chunk, pos + 1 - t0);        // positions in this chunk
     const bool owns_new = k_new && pos < t0 + chunk;
 
-    // ---- RoPE angles: pos * w_i in fp64, reduced to [-pi, pi] in fp64, then
-    // an fp32 sincos (the reduced angle is exact to ~1e-7 rad) ----
-    if (rope && tid < D / 2) {
-        const double ph = double(pos) * freq.w[tid];
+    // ---- RoPE angle of pair i: pos * w_i in fp64, reduced to [-pi, pi] in
+    // fp64, then an fp32 sincos (the reduced angle is exact to ~1e-7 rad) ----
+    const auto angle = [&](int i, float &cn, float &sn) {
+        const double ph = double(pos) * freq.w[i];
         const double r = fma(-6.283185307179586, rint(ph * 0.15915494309189535), ph);
-        float sn, cn;
         sincosf(float(r), &sn, &cn);
-        rc[tid] = cn;
-        rs[tid] = sn;
+    };
+    // the q values, rotated and scaled, into LDS (values 4 tid .. 4 tid + 3:
+    // two pairs of one head)
+    if (tid < NQ) {
+        float x[4] = {q4.x, q4.y, q4.z, q4.w};
+        if (rope) {
+            const int i0 = (4 * tid % D) / 2;
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                float cs, sn;
+                angle(i0 + m, cs, sn);
+                const float x0 = x[2 * m], x1 = x[2 * m + 1];
+                x[2 * m] = x0 * cs - x1 * sn;
+                x[2 * m + 1] = x0 * sn + x1 * cs;
+            }
+        }
+        *reinterpret_cast<float4 *>(&qs[4 * tid]) = make_float4(x[0] * scale, x[1] * scale, x[2] * scale, x[3] * scale);
     }
-    __syncthreads();
     if (owns_new && tid < D / 2) {
         float k0 = k_new[g * D + 2 * tid], k1 = k_new[g * D + 2 * tid + 1];
         if (rope) {
+            float cs, sn;
+            angle(tid, cs, sn);
             const float a = k0, b = k1;
-            k0 = a * rc[tid] - b * rs[tid];
-            k1 = a * rs[tid] + b * rc[tid];
+            k0 = a * cs - b * sn;
+            k1 = a * sn + b * cs;
         }
         const uint16_t kb0 = f2h_bits(k0), kb1 = f2h_bits(k1);
         const uint16_t vb0 = f2h_bits(v_new[g * D + 2 * tid]), vb1 = f2h_bits(v_new[g * D + 2 * tid + 1]);
@@ -136,26 +149,16 @@ __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
         vn[2 * tid + 1] = h2f(vb1);
     }
 
-    // ---- the q octets, rotated and scaled ----
+    __syncthreads();                               // qs, kn, vn visible
+    // ---- this thread's q octet of each head ----
     float qr[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        const float4 a = qa[h], b = qb[h];
-        float v8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            float x0 = v8[2 * m], x1 = v8[2 * m + 1];
-            if (rope) {
-                const float cs = rc[4 * oc + m], sn = rs[4 * oc + m];
-                const float r0 = x0 * cs - x1 * sn, r1 = x0 * sn + x1 * cs;
-                x0 = r0;
-                x1 = r1;
-            }
-            qr[h][2 * m] = x0 * scale;
-            qr[h][2 * m + 1] = x1 * scale;
-        }
+        const float4 a = *reinterpret_cast<const float4 *>(&qs[h * D + 8 * oc]);
+        const float4 b = *reinterpret_cast<const float4 *>(&qs[h * D + 8 * oc + 4]);
+        qr[h][0] = a.x; qr[h][1] = a.y; qr[h][2] = a.z; qr[h][3] = a.w;
+        qr[h][4] = b.x; qr[h][5] = b.y; qr[h][6] = b.z; qr[h][7] = b.w;
     }
-    __syncthreads();                               // kn, vn visible
 
     // ---- scores ----
 #pragma unroll
