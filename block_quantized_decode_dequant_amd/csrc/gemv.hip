@@ -22,7 +22,9 @@
 //    reduces each row over its 64 lanes, and the waves of a workgroup (one
 //    per 2048-column slice) combine their partial sums through LDS in a fixed
 //    order.  No atomics: results are deterministic.
+#include <algorithm>
 #include <cstdlib>
+#include <type_traits>
 
 #include "device_util.h"
 #include "nt_internal.h"
@@ -47,6 +49,9 @@ struct GemvArgs {
     int accumulate;
     int swiglu;
 };
+
+GemvArgs gemv_args(nt_qtype t, int nseg, const void *const *W, const int64_t *rows, float *const *y, int64_t cols,
+                   const float *x, const float *gain, float eps, int accumulate);
 
 namespace {
 
@@ -702,8 +707,10 @@ __device__ __forceinline__ void read_vec(const uint8_t *area, int lane, float *v
 // gains) are copied once per workgroup into their own LDS area, issued
 // together with the first ring loads so the two latencies overlap; otherwise
 // each wave stages its slice through its own ring before the first row.
+// The body of one launch's workgroup b of G (a plain launch runs it with
+// blockIdx.x and gridDim.x; a paired launch splits its grid between two).
 template <class Tr, int VEC, bool NORM, bool SHARED>
-__global__ void __launch_bounds__(512) gemv_lds(const GemvArgs a) {
+__device__ __forceinline__ void gemv_body(const GemvArgs &a, const int b, const int G) {
     using P = Plan<Tr, VEC>;
     constexpr int S = P::kStages, SL = Tr::kSlice, NI = P::kInstr;
     static_assert(S >= 2, "the ring holds the row being read and at least one in flight");
@@ -737,7 +744,6 @@ __global__ void __launch_bounds__(512) gemv_lds(const GemvArgs a) {
     // stream one band of neighbouring rows; row group g takes the workgroup's
     // items g, g + R, g + 2R, ...
     const bool pairs = a.swiglu != 0;
-    const int G = gridDim.x, b = blockIdx.x;
     const int items = pairs ? a.rows / 2 : a.rows;
     const int nitems = (items - b + G - 1) / G;      // items of this workgroup
     const int mine = SHARED ? (nitems > grp ? (nitems - grp + R - 1) / R : 0) : nitems;
@@ -887,6 +893,23 @@ __global__ void __launch_bounds__(512) gemv_lds(const GemvArgs a) {
 #undef NT_SEG
 }
 
+template <class Tr, int VEC, bool NORM, bool SHARED>
+__global__ void __launch_bounds__(512) gemv_lds(const GemvArgs a) {
+    gemv_body<Tr, VEC, NORM, SHARED>(a, blockIdx.x, gridDim.x);
+}
+
+// Two GEMVs of different formats over the same activations in one launch
+// (shared layout, same row width): workgroups [0, ga) run the first, the rest
+// the second.  The decode step uses it for the q/k (Q4_K) and v (Q6_K)
+// projections of the mixed-format models.
+template <class TrA, class TrB, bool NORM>
+__global__ void __launch_bounds__(512) gemv_pair(const GemvArgs a, const GemvArgs c, const int ga) {
+    if (int(blockIdx.x) < ga)
+        gemv_body<TrA, 16, NORM, true>(a, blockIdx.x, ga);
+    else
+        gemv_body<TrB, 16, NORM, true>(c, blockIdx.x - ga, gridDim.x - ga);
+}
+
 int env_int(const char *name, int dflt) {
     const char *v = std::getenv(name);
     return v ? std::atoi(v) : dflt;
@@ -1024,7 +1047,78 @@ hipError_t launch_lds(const GemvArgs &a, bool pairs, bool vec16, hipStream_t st)
     return norm ? launch_lds_inst<Tr, 16, true, false>(a, s, st) : launch_lds_inst<Tr, 16, false, false>(a, s, st);
 }
 
+// Shared-layout shape of one half of a paired launch with `groups` row groups.
+template <class Tr>
+size_t pair_lds(int nw, int groups, bool norm) {
+    return size_t(nw) * 16384 * (norm ? 2 : 1) +
+           size_t(nw) * groups * (size_t(Tr::kStages) * Tr::kSlice + kMaxRowsPerWG * 4 + 4);
+}
+
+template <class TrA, class TrB>
+hipError_t launch_pair_inst(const GemvArgs &a, const GemvArgs &c, hipStream_t st) {
+    // two different formats, RMSNorm prologue: the q/k/v case
+    if constexpr (std::is_same_v<TrA, TrB>) {
+        return hipErrorInvalidValue;
+    } else {
+    const DevInfo di = dev_info();
+    if (a.gain == nullptr) return hipErrorInvalidValue;
+    constexpr bool norm = true;
+    const int nw = (a.units + 63) / 64;
+    const int ga_max = std::max(8 / nw, 1);
+    int groups = ga_max;
+    while (groups > 1 && std::max(pair_lds<TrA>(nw, groups, norm), pair_lds<TrB>(nw, groups, norm)) >
+                             size_t(di.lds_per_cu))
+        --groups;
+    const size_t lds = std::max(pair_lds<TrA>(nw, groups, norm), pair_lds<TrB>(nw, groups, norm));
+    // one workgroup per CU, split in proportion to the weight bytes, each side
+    // within its row-sum capacity and at most one workgroup per row
+    const int64_t bytes_a = int64_t(a.rows) * a.row_bytes, bytes_c = int64_t(c.rows) * c.row_bytes;
+    const int64_t cap = int64_t(groups) * kMaxRowsPerWG;
+    const int64_t min_a = (a.rows + cap - 1) / cap, min_c = (c.rows + cap - 1) / cap;
+    int64_t ga = (int64_t(di.cus) * bytes_a + (bytes_a + bytes_c) / 2) / (bytes_a + bytes_c);
+    ga = std::min<int64_t>(std::max<int64_t>(ga, min_a), a.rows);
+    int64_t gc = std::min<int64_t>(std::max<int64_t>(int64_t(di.cus) - ga, min_c), c.rows);
+    if (ga < 1) ga = 1;
+    if (gc < 1) gc = 1;
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_pair<TrA, TrB, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, dev_info().lds_per_cu);
+    (void)attr;
+    gemv_pair<TrA, TrB, true><<<dim3(unsigned(ga + gc)), dim3(unsigned(64 * nw * groups)), lds, st>>>(a, c, int(ga));
+    return hipGetLastError();
+    }
+}
+
+template <class TrA>
+hipError_t launch_pair_b(nt_qtype tb, const GemvArgs &a, const GemvArgs &c, hipStream_t st) {
+    switch (tb) {
+    case NT_Q8_0: return launch_pair_inst<TrA, F80>(a, c, st);
+    case NT_Q4_0: return launch_pair_inst<TrA, F40>(a, c, st);
+    case NT_Q4_K: return launch_pair_inst<TrA, F4K>(a, c, st);
+    case NT_Q6_K: return launch_pair_inst<TrA, F6K>(a, c, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
+
+bool gemv_pair_ok(nt_qtype t, int64_t rows, int64_t cols) {
+    return gemv_fast_ok(t, rows, cols) && cols <= 8192 && gemv_row_bytes(t, cols) % 16 == 0;
+}
+
+hipError_t launch_gemv_pair(nt_qtype ta, int na, const void *const *Wa, const int64_t *rows_a, float *const *ya,
+                            nt_qtype tb, int nb, const void *const *Wb, const int64_t *rows_b, float *const *yb,
+                            int64_t cols, const float *x, const float *gain, float eps, hipStream_t st) {
+    const GemvArgs a = gemv_args(ta, na, Wa, rows_a, ya, cols, x, gain, eps, 0);
+    const GemvArgs c = gemv_args(tb, nb, Wb, rows_b, yb, cols, x, gain, eps, 0);
+    switch (ta) {
+    case NT_Q8_0: return launch_pair_b<F80>(tb, a, c, st);
+    case NT_Q4_0: return launch_pair_b<F40>(tb, a, c, st);
+    case NT_Q4_K: return launch_pair_b<F4K>(tb, a, c, st);
+    case NT_Q6_K: return launch_pair_b<F6K>(tb, a, c, st);
+    default: return hipErrorInvalidValue;
+    }
+}
 
 int64_t gemv_row_bytes(nt_qtype t, int64_t cols) { return cols / block_elems(t) * block_bytes(t); }
 

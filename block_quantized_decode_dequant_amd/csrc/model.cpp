@@ -182,6 +182,20 @@ namespace {
 // made once.
 hipError_t norm_gemvs(int cnt, const nt_tensor_ref *mats, const int64_t *rows, float *const *ys, int64_t cols,
                       const float *x, const float *gain, float eps, float *nbuf, hipStream_t st) {
+    // exactly two runs of one format each (q/k in one format, v in another):
+    // one paired launch when both take the shared layout
+    int split = 1;
+    while (split < cnt && mats[split].type == mats[0].type) ++split;
+    bool two_runs = split < cnt && split <= 3 && cnt - split <= 3;
+    for (int s = split; two_runs && s < cnt; ++s) two_runs = mats[s].type == mats[split].type;
+    for (int s = 0; two_runs && s < cnt; ++s) two_runs = gemv_pair_ok(nt_qtype(mats[s].type), rows[s], cols);
+    if (two_runs) {
+        const void *Wa[3] = {nullptr, nullptr, nullptr}, *Wb[3] = {nullptr, nullptr, nullptr};
+        for (int s = 0; s < split; ++s) Wa[s] = mats[s].data;
+        for (int s = split; s < cnt; ++s) Wb[s - split] = mats[s].data;
+        return launch_gemv_pair(nt_qtype(mats[0].type), split, Wa, rows, ys, nt_qtype(mats[split].type), cnt - split,
+                                Wb, rows + split, ys + split, cols, x, gain, eps, st);
+    }
     bool have_n = false;
     for (int i = 0; i < cnt;) {
         const nt_qtype t = nt_qtype(mats[i].type);

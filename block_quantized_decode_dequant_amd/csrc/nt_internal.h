@@ -38,6 +38,13 @@ hipError_t launch_gemv_multi(nt_qtype t, int nseg, const void *const *W, const i
                              hipStream_t st);
 hipError_t launch_gemv_swiglu(nt_qtype t, const void *Wg, const void *Wu, int64_t rows, int64_t cols,
                               const float *x, const float *gain, float eps, float *h, hipStream_t st);
+// Two groups of matrices of different formats (each group one format, up to
+// three matrices) over the same RMSNorm-ed activations in one launch; both
+// groups must satisfy gemv_pair_ok (16-byte rows, at most 8192 columns).
+bool gemv_pair_ok(nt_qtype t, int64_t rows, int64_t cols);
+hipError_t launch_gemv_pair(nt_qtype ta, int na, const void *const *Wa, const int64_t *rows_a, float *const *ya,
+                            nt_qtype tb, int nb, const void *const *Wb, const int64_t *rows_b, float *const *yb,
+                            int64_t cols, const float *x, const float *gain, float eps, hipStream_t st);
 hipError_t launch_quantize(nt_qtype t, const float *x, void *blocks, int64_t n, hipStream_t st);
 hipError_t launch_delay(double us, hipStream_t st);
 hipError_t launch_rmsnorm(const float *x, const float *g, float *y, int64_t n, float eps, hipStream_t st);

@@ -92,8 +92,8 @@ def test_tiny_model_greedy_parity(wtype):
 
 @pytest.mark.parametrize("graph", [True, False], ids=["graph", "eager"])
 def test_wide_mix_model_uses_fused_paths_throughout(graph):
-    """hidden 2048: q and k (Q4_K) share one fused launch, v (Q6_K) takes its
-    own; every other matrix takes a fused path too (Q6_K down with 4-byte
+    """hidden 2048: q and k (Q4_K) and v (Q6_K) share one paired two-format
+    launch; every other matrix takes a fused path too (Q6_K down with 4-byte
     copies)."""
     cfg = tiny_config(n_layers=2, hidden=2048, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=512)
     w = build_oracle_model(cfg, seed=15, wtype="mix")
