@@ -148,17 +148,28 @@ def run_gpu(args):
     value = step_bytes / (wall / args.steps) / 1e9
 
     # Per-kernel durations, measured live: each case launched back to back
-    # `steps` times (rotating weight copies) between one pair of events, all
-    # queued behind a short delay kernel so the GPU never waits for the host.
+    # `steps` times (rotating weight copies) from a captured graph, one pair of
+    # events around its replay on the launch stream (no host work between the
+    # kernels).
+    case_graphs = []
+    with torch.cuda.stream(side):
+        for c in cases:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for s_ in range(args.steps):
+                    nt.nt_gemv(c["qt"], c["W"][s_ % copies], c["x"], c["y"], c["rows"], c["cols"])
+            case_graphs.append(g)
+    torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in cases]
+    with torch.cuda.stream(side):
+        for g in case_graphs:
+            g.replay()
+        for j, g in enumerate(case_graphs):
+            ev[j][0].record(side)
+            g.replay()
+            ev[j][1].record(side)
     torch.cuda.synchronize()
-    nt.nt_delay(min(1e6, 2000.0 + 300.0 * args.steps))
-    for j, c in enumerate(cases):
-        ev[j][0].record()
-        for s_ in range(args.steps):
-            nt.nt_gemv(c["qt"], c["W"][s_ % copies], c["x"], c["y"], c["rows"], c["cols"])
-        ev[j][1].record()
-    torch.cuda.synchronize()
+    del case_graphs
     per_case_ms = [ev[j][0].elapsed_time(ev[j][1]) / args.steps for j in range(len(cases))]
     span_ms = ev[0][0].elapsed_time(ev[-1][1]) / args.steps
 

@@ -353,7 +353,7 @@ __global__ void __launch_bounds__(1024) gemv_generic(const uint8_t *__restrict__
 // is copied from HBM into a per-wave LDS ring by global_load_lds (each
 // instruction moves 64 x VEC contiguous bytes, fully coalesced, straight into
 // LDS without passing through VGPRs); a lane then reads its own unit back
-// from LDS.  The ring keeps kStages - 1 rows in flight per wave (one), so 8
+// from LDS.  The ring keeps one row (two for wide Q4 rows) in flight per wave, so 8
 // waves per CU keep 20-35 KB of weight reads outstanding per CU, about what
 // HBM latency times bandwidth needs.  Waits are explicit (s_waitcnt vmcnt)
 // because the ring's loads return to LDS, not to registers the compiler could
@@ -398,7 +398,7 @@ __device__ __forceinline__ float sum_vals(const float *v) {
 
 // ---- Q8_0 fast: one lane = blocks 2u, 2u+1 (68 bytes at 68u, word-aligned) --
 struct F80 {
-    static constexpr int kSlice = 64 * 68, kStages = 2;
+    static constexpr int kSlice = 64 * 68, kStagesShared = 2, kStagesWide = 2;
     struct L { uint32_t off; };
     struct X { float v[64]; float s0, s1; };
     struct Raw { u32x4 a, b, c, d; uint32_t e; };
@@ -438,7 +438,7 @@ struct F80 {
 
 // ---- Q4_0 fast: one lane = blocks 2u, 2u+1 (36 bytes at 36u, word-aligned) --
 struct F40 {
-    static constexpr int kSlice = 64 * 36, kStages = 2;
+    static constexpr int kSlice = 64 * 36, kStagesShared = 2, kStagesWide = 3;
     struct L { uint32_t off; };
     struct X { float v[64]; float s0, s1; };
     struct Raw { u32x4 a, b; uint32_t c; };
@@ -478,7 +478,7 @@ struct F40 {
 // byte 32p + i: low nibble = value 64p + i (sub-block 2p), high nibble = value
 // 64p + 32 + i (sub-block 2p+1).
 struct F4K {
-    static constexpr int kSlice = 16 * 144, kStages = 2;
+    static constexpr int kSlice = 16 * 144, kStagesShared = 2, kStagesWide = 3;
     struct L { uint32_t off_h, off_q, p; };
     struct X { float v[64]; float slo, shi; };   // v[i]: value 64p+i (lo: i<32, hi: i>=32)
     struct Raw { u32x4 h, q0, q1; };
@@ -522,7 +522,7 @@ struct F4K {
 // qh[32h + 16j + i] (bits 2k..2k+1), scales[8h + 2k + j] and d.  Odd blocks
 // start 2 bytes into a word: loads are word-aligned and v_perm realigns.
 struct F6K {
-    static constexpr int kSlice = 16 * 210, kStages = 2;
+    static constexpr int kSlice = 16 * 210, kStagesShared = 2, kStagesWide = 2;
     struct L { uint32_t base, sel, h, j; };
     struct X { float v[64]; float s[4]; };       // v[16k + i]
     struct Raw { u32x4 a; uint32_t a4; u32x4 b; uint32_t b4; u32x4 c; uint32_t c4; u32x3 sc; uint32_t d; };
@@ -591,13 +591,15 @@ struct F6K {
 // How one row slice is copied: NFULL instructions of 64 x VEC bytes, then, if
 // the slice is not a whole number of those, one instruction on the first
 // REM / VEC lanes.  VEC = 16 needs 16-byte-aligned rows, VEC = 4 word-aligned.
-template <class Tr, int VEC>
+// Ring stages: two (one row in flight per wave) except for the 2304-byte
+// slices of wide rows, where seven waves per CU need a second row in flight.
+template <class Tr, int VEC, bool SHARED = true>
 struct Plan {
     static constexpr int kPer = 64 * VEC;
     static constexpr int kFull = Tr::kSlice / kPer;
     static constexpr int kRem = Tr::kSlice % kPer;
     static constexpr int kInstr = kFull + (kRem ? 1 : 0);
-    static constexpr int kStages = Tr::kStages;
+    static constexpr int kStages = SHARED ? Tr::kStagesShared : Tr::kStagesWide;
     static_assert(kRem % VEC == 0, "slice tail");
     static_assert((kStages - 1) * kInstr <= 63, "vmcnt holds at most 63 outstanding loads");
 };
@@ -711,7 +713,7 @@ __device__ __forceinline__ void read_vec(const uint8_t *area, int lane, float *v
 // blockIdx.x and gridDim.x; a paired launch splits its grid between two).
 template <class Tr, int VEC, bool NORM, bool SHARED>
 __device__ __forceinline__ void gemv_body(const GemvArgs &a, const int b, const int G) {
-    using P = Plan<Tr, VEC>;
+    using P = Plan<Tr, VEC, SHARED>;
     constexpr int S = P::kStages, SL = Tr::kSlice, NI = P::kInstr;
     static_assert(S >= 2, "the ring holds the row being read and at least one in flight");
     // per-wave LDS: the ring, at least 16 KB so that one activation slice
@@ -988,11 +990,11 @@ LdsShape lds_shape(int64_t items, int64_t cols, bool pairs, bool norm, bool vec1
     LdsShape s;
     const int64_t units = cols / 64;
     s.nw = int((units + 63) / 64);
-    const size_t ring = size_t(Tr::kStages) * Tr::kSlice;
     const size_t area = size_t(s.nw) * 16384 * (norm ? 2 : 1);
     // rows of up to two column slices (8192 columns) use the shared layout
     bool shared = vec16 && cols <= 8192;
     if (shared_env >= 0) shared = shared && shared_env > 0;
+    const size_t ring = size_t(shared ? Tr::kStagesShared : Tr::kStagesWide) * Tr::kSlice;
     const size_t per_wave = (shared ? ring : (ring > 16384 ? ring : 16384)) + kMaxRowsPerWG * 4 + 4;
     s.groups = 1;
     if (shared) {
@@ -1051,7 +1053,7 @@ hipError_t launch_lds(const GemvArgs &a, bool pairs, bool vec16, hipStream_t st)
 template <class Tr>
 size_t pair_lds(int nw, int groups, bool norm) {
     return size_t(nw) * 16384 * (norm ? 2 : 1) +
-           size_t(nw) * groups * (size_t(Tr::kStages) * Tr::kSlice + kMaxRowsPerWG * 4 + 4);
+           size_t(nw) * groups * (size_t(Tr::kStagesShared) * Tr::kSlice + kMaxRowsPerWG * 4 + 4);
 }
 
 template <class TrA, class TrB>
