@@ -31,8 +31,8 @@ def kernel_key(name: str):
     """The benchmark's name for a GEMV kernel instantiation, or None."""
     m = re.search(r"gemv_lds<nt::\(anonymous namespace\)::(F\w+), (\d+), (true|false)(?:, (true|false))?>", name)
     if m:
-        return (f"gemv {FMT[m.group(1)]} lds vec{m.group(2)}" + (" +norm" if m.group(3) == "true" else "")
-                + (" shared" if m.group(4) == "true" else ""))
+        # both activation layouts under one name, as the benchmark groups them
+        return f"gemv {FMT[m.group(1)]} lds vec{m.group(2)}" + (" +norm" if m.group(3) == "true" else "")
     if "gemv_generic" in name:
         return "gemv generic"
     return None
@@ -118,14 +118,21 @@ def cmd_traffic(a):
     scale_w = a.cal_bytes / (kib_w * 1024.0)
     f = counter_by_kernel(a.fetch, "FETCH_SIZE")
     w = counter_by_kernel(a.write, "WRITE_SIZE")
-    per_launch, detail = {}, {}
+    # instantiations the benchmark groups under one name (both activation
+    # layouts) are pooled: per-launch bytes = their total over their dispatches
+    tot = collections.defaultdict(lambda: [0.0, 0.0, 0])
     for name, (kib, n) in f.items():
         key = kernel_key(name)
         if not key or key == "gemv generic":
             continue
         wkib = w.get(name, (0.0, 0))[0]
-        b = kib * 1024 * scale_f + wkib * 1024 * scale_w
-        per_launch[key] = round(b)
+        tot[key][0] += kib * n
+        tot[key][1] += wkib * n
+        tot[key][2] += n
+    per_launch, detail = {}, {}
+    for key, (kib_sum, wkib_sum, n) in tot.items():
+        kib, wkib = kib_sum / n, wkib_sum / n
+        per_launch[key] = round(kib * 1024 * scale_f + wkib * 1024 * scale_w)
         detail[key] = {"dispatches": n, "fetch_kib_raw": round(kib, 1), "write_kib_raw": round(wkib, 1),
                        "fetch_bytes": round(kib * 1024 * scale_f), "write_bytes": round(wkib * 1024 * scale_w)}
     rec = {"gemv_source_sha256_16": hashlib.sha256(open(GEMV_SRC, "rb").read()).hexdigest()[:16],
