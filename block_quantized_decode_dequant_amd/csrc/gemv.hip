@@ -855,11 +855,17 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, const int b, const 
         if (lane == 63) part[wave * kMaxRowsPerWG + (j)] = v_;                               \
         cs = sn;                                                                             \
     }
+    // the first wave on each SIMD outranks the second by age; alternate an
+    // explicit priority per row so both advance at the same pace
+    const bool first_slot = wave < 4;
     for (int j = 0; j < n; j += 2) {
+        if (first_slot) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
         NT_STEP(j, ra, rb2);
         if (j + 1 >= n) break;
+        if (first_slot) __builtin_amdgcn_s_setprio(0); else __builtin_amdgcn_s_setprio(1);
         NT_STEP(j + 1, rb2, ra);
     }
+    __builtin_amdgcn_s_setprio(0);
     // a wave with no rows still has its placeholder copies outstanding
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
