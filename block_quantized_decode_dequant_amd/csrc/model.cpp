@@ -27,7 +27,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t x, n, q, k, v, o, g, u, attn, total;
+    size_t x, n, q, k, v, o, g, u, attn, pick, total;
 };
 
 nt_attn_desc attn_of(const nt_model_config &c) {
@@ -56,6 +56,7 @@ Layout layout_of(const nt_model_config &c) {
     L.g = take(4 * F);
     L.u = take(4 * F);
     L.attn = take(attn_workspace_bytes(attn_of(c)));
+    L.pick = take(16);                 // the greedy pick's atomic key and ticket
     L.total = off;
     return L;
 }
@@ -259,7 +260,7 @@ hipError_t head(nt_model *m, int32_t *d_pos, float *logits, int32_t *d_next, hip
     const int64_t rows[1] = {c.vocab};
     float *const out[1] = {logits};
     NT_TRY(norm_gemvs(1, &m->w.output, rows, out, c.hidden, x, m->w.output_norm, c.rms_eps, n, st));
-    NT_TRY(launch_argmax(logits, c.vocab, d_next, d_pos, st));
+    NT_TRY(launch_argmax_multi(logits, c.vocab, m->ws + m->lay.pick, d_next, d_pos, st));
     return hipSuccess;
 }
 
@@ -403,6 +404,11 @@ nt_status nt_model_create(const nt_model_config *cfg, const nt_model_weights *w,
     m->attn = attn_of(*cfg);
     m->lay = lay;
     m->ws = static_cast<uint8_t *>(w->workspace);
+    // the greedy pick's key and ticket start at zero (each pick leaves them so)
+    if (hipMemset(m->ws + lay.pick, 0, 16) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        delete m;
+        return fail(NT_EHIP, "nt_model_create: clearing the workspace failed");
+    }
     *out = m;
     return NT_OK;
 }

@@ -53,6 +53,10 @@ hipError_t launch_rope(float *q, float *k, int n_q_heads, int n_kv_heads, int he
 hipError_t launch_softmax(float *x, int64_t n, hipStream_t st);
 hipError_t launch_swiglu(const float *g, const float *u, float *out, int64_t n, hipStream_t st);
 hipError_t launch_argmax(const float *x, int64_t n, int32_t *out, int32_t *pos_inc, hipStream_t st);
+// The same over many workgroups; scratch: 16 device bytes, zero before the
+// first call, left zero by every call (x 16-byte aligned).
+hipError_t launch_argmax_multi(const float *x, int64_t n, void *scratch, int32_t *out, int32_t *pos_inc,
+                               hipStream_t st);
 hipError_t launch_embed(nt_qtype t, const void *table, int64_t vocab, int64_t hidden, const int32_t *d_token,
                         float *out, hipStream_t st);
 int attn_chunk(const nt_attn_desc &a);

@@ -150,6 +150,76 @@ __global__ void __launch_bounds__(kBlock) argmax_kernel(const float *__restrict_
     }
 }
 
+// The same pick spread over many workgroups (the decode step's head: 128K
+// logits are too many for one workgroup's memory bandwidth).  Each
+// workgroup reduces its contiguous range, then folds its best (value, index)
+// into one 64-bit key with a device-scope atomic max; the key orders values
+// like better() (NaN lowest, -0 as +0, lower index first on ties).  A ticket
+// counter tells the last workgroup that every other fold is done (each
+// workgroup waits for its max to return before taking a ticket); that one
+// writes the index, bumps the position and clears key and ticket for the
+// next call.  Key and ticket start at zero (the model clears them once).
+__device__ __forceinline__ unsigned long long pick_key(float v, int i) {
+    if (v != v || i == 0x7fffffff) return 0ull;
+    uint32_t b = __float_as_uint(v == 0.f ? 0.f : v);
+    b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return (static_cast<unsigned long long>(b) << 32) | (0xffffffffu - uint32_t(i));
+}
+
+constexpr int kPickBlock = 256;
+
+__global__ void __launch_bounds__(kPickBlock) argmax_multi_kernel(const float *__restrict__ x, int64_t n,
+                                                                  unsigned long long *key, unsigned int *ticket,
+                                                                  int32_t *__restrict__ out, int32_t *__restrict__ pos) {
+    __shared__ float rv[kPickBlock / 64];
+    __shared__ int ri[kPickBlock / 64];
+    // contiguous ranges, multiples of 4 values (x is 16-byte aligned)
+    const int64_t per = ((n + gridDim.x - 1) / gridDim.x + 3) / 4 * 4;
+    const int64_t lo = int64_t(blockIdx.x) * per, hi = lo + per < n ? lo + per : n;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    const int64_t hi4 = lo + (hi > lo ? (hi - lo) / 4 * 4 : 0);
+    for (int64_t i = lo + 4 * threadIdx.x; i < hi4; i += 4 * kPickBlock) {
+        const float4 v = *reinterpret_cast<const float4 *>(x + i);
+        const int b = int(i);
+        if (better(v.x, b, bv, bi)) { bv = v.x; bi = b; }
+        if (better(v.y, b + 1, bv, bi)) { bv = v.y; bi = b + 1; }
+        if (better(v.z, b + 2, bv, bi)) { bv = v.z; bi = b + 2; }
+        if (better(v.w, b + 3, bv, bi)) { bv = v.w; bi = b + 3; }
+    }
+    for (int64_t i = hi4 + threadIdx.x; i < hi; i += kPickBlock) {
+        const float v = x[i];
+        if (better(v, int(i), bv, bi)) { bv = v; bi = int(i); }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const float ov = __shfl_xor(bv, m, 64);
+        const int oi = __shfl_xor(bi, m, 64);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) { rv[wave] = bv; ri[wave] = bi; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float v = rv[0];
+        int id = ri[0];
+        for (int w = 1; w < kPickBlock / 64; ++w)
+            if (better(rv[w], ri[w], v, id)) { v = rv[w]; id = ri[w]; }
+        const unsigned long long prev =
+            __hip_atomic_fetch_max(key, pick_key(v, id), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the ticket is taken only once the max has returned: the increment
+        // depends on its result (a key is never all ones, so it is always 1)
+        const unsigned int t = __hip_atomic_fetch_add(ticket, prev == ~0ull ? 2u : 1u, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+        if (t == gridDim.x - 1) {
+            const unsigned long long k = __hip_atomic_exchange(key, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *out = k == 0ull ? 0 : int(0xffffffffu - uint32_t(k));
+            if (pos) *pos += 1;
+        }
+    }
+}
+
 // Decodes row *d_token of a packed [vocab x hidden] table into out[hidden]; a
 // token outside [0, vocab) yields NaNs instead of an out-of-bounds read.
 template <int T>
@@ -233,6 +303,17 @@ hipError_t launch_swiglu(const float *g, const float *u, float *out, int64_t n, 
 
 hipError_t launch_argmax(const float *x, int64_t n, int32_t *out, int32_t *pos_inc, hipStream_t st) {
     argmax_kernel<<<1, kBlock, 0, st>>>(x, n, out, pos_inc);
+    return hipGetLastError();
+}
+
+hipError_t launch_argmax_multi(const float *x, int64_t n, void *scratch, int32_t *out, int32_t *pos_inc,
+                               hipStream_t st) {
+    // about 4 KB of logits per workgroup, at most 512 workgroups
+    int64_t want = (n + 1023) / 1024;
+    const int grid = int(want < 1 ? 1 : (want > 512 ? 512 : want));
+    unsigned long long *key = static_cast<unsigned long long *>(scratch);
+    unsigned int *ticket = reinterpret_cast<unsigned int *>(key + 1);
+    argmax_multi_kernel<<<grid, kPickBlock, 0, st>>>(x, n, key, ticket, out, pos_inc);
     return hipGetLastError();
 }
 
