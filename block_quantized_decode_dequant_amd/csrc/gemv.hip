@@ -740,6 +740,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, const int b, const 
     const uint32_t ring_a = lds_addr(ring);                          // the same, as an LDS address
     float *part = reinterpret_cast<float *>(rings + nwv * RS);        // [nwv][kMaxRowsPerWG]
     float *red = part + nwv * kMaxRowsPerWG;                          // [nwv]
+    float *ypre = red + nwv;                                          // [nwv][64]
 
     // Workgroup b takes items b, b + G, b + 2G, ... (an item is a row, or in
     // SwiGLU mode a gate row and its up row), so at any moment the workgroups
@@ -778,6 +779,15 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, const int b, const 
         copy_slice<Tr, VEC>(W_, uint32_t(local_) * rb + lane_off, lim_, ring_a + (st) * SL, lane); \
     } while (0)
 
+    // accumulating into one matrix's outputs: the old values of items
+    // 64w .. 64w+63 are copied into LDS now (one 4-byte copy per lane, landing
+    // with the activations), so the epilogue does not wait on memory for them
+    const bool y_early = a.accumulate && !pairs && a.seg_end[0] == a.rows && nitems <= 64 * nwv;
+    if (y_early) {
+        const int t = 64 * wave + lane;
+        const uint32_t off = uint32_t(b + (t < nitems ? t : 0) * G) * 4u;
+        dma<4>(reinterpret_cast<const uint8_t *>(a.y[0]), off, lds_addr(ypre) + 256u * uint32_t(wave));
+    }
     typename Tr::X xs;
     float gv[NORM ? 64 : 1];
     float ss = 0.f;
@@ -892,7 +902,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, const int b, const 
             const int r = b + t * G;
             NT_SEG(r);
             float *y = (seg_ == 0 ? a.y[0] : (seg_ == 1 ? a.y[1] : a.y[2])) + local_;
-            *y = a.accumulate ? *y + sum : sum;
+            *y = a.accumulate ? (y_early ? ypre[t] : *y) + sum : sum;
         }
     }
 #undef NT_STEP
@@ -1001,7 +1011,7 @@ LdsShape lds_shape(int64_t items, int64_t cols, bool pairs, bool norm, bool vec1
     bool shared = vec16 && cols <= 8192;
     if (shared_env >= 0) shared = shared && shared_env > 0;
     const size_t ring = size_t(shared ? Tr::kStagesShared : Tr::kStagesWide) * Tr::kSlice;
-    const size_t per_wave = (shared ? ring : (ring > 16384 ? ring : 16384)) + kMaxRowsPerWG * 4 + 4;
+    const size_t per_wave = (shared ? ring : (ring > 16384 ? ring : 16384)) + kMaxRowsPerWG * 4 + 4 + 256;
     s.groups = 1;
     if (shared) {
         int g = 8 / s.nw;
@@ -1059,7 +1069,7 @@ hipError_t launch_lds(const GemvArgs &a, bool pairs, bool vec16, hipStream_t st)
 template <class Tr>
 size_t pair_lds(int nw, int groups, bool norm) {
     return size_t(nw) * 16384 * (norm ? 2 : 1) +
-           size_t(nw) * groups * (size_t(Tr::kStagesShared) * Tr::kSlice + kMaxRowsPerWG * 4 + 4);
+           size_t(nw) * groups * (size_t(Tr::kStagesShared) * Tr::kSlice + kMaxRowsPerWG * 4 + 4 + 256);
 }
 
 template <class TrA, class TrB>
