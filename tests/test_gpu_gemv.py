@@ -222,9 +222,12 @@ def test_gemv_swiglu_parity(t):
 
 
 # Shared-area layout at sizes where the row groups refill their rings (more rows per
-# wave than ring stages) and where most row groups have no row at all.
+# wave than ring stages), where most row groups have no row at all, and for rows
+# wider than two column slices.
 SHARED_CASES = [(O.Q8_0, 7500, 4096, False), (O.Q8_0, 3, 4096, True), (O.Q4_0, 9000, 2048, True),
-                (O.Q4_K, 5000, 8192, True), (O.Q6_K, 7, 8192, True), (O.Q6_K, 10500, 4096, False)]
+                (O.Q4_K, 5000, 8192, True), (O.Q6_K, 7, 8192, True), (O.Q6_K, 10500, 4096, False),
+                # wider rows whose activation area still fits beside one row group
+                (O.Q8_0, 600, 14336, False), (O.Q4_K, 300, 16384, True), (O.Q6_K, 200, 12288, False)]
 
 
 @pytest.mark.parametrize("t,rows,cols,norm", SHARED_CASES,
