@@ -353,7 +353,7 @@ __global__ void __launch_bounds__(1024) gemv_generic(const uint8_t *__restrict__
 // is copied from HBM into a per-wave LDS ring by global_load_lds (each
 // instruction moves 64 x VEC contiguous bytes, fully coalesced, straight into
 // LDS without passing through VGPRs); a lane then reads its own unit back
-// from LDS.  The ring keeps one row (two for wide Q4 rows) in flight per wave, so 8
+// from LDS.  The ring keeps one row (two for Q4_K rows) in flight per wave, so 8
 // waves per CU keep 20-35 KB of weight reads outstanding per CU, about what
 // HBM latency times bandwidth needs.  Waits are explicit (s_waitcnt vmcnt)
 // because the ring's loads return to LDS, not to registers the compiler could
@@ -478,7 +478,7 @@ struct F40 {
 // byte 32p + i: low nibble = value 64p + i (sub-block 2p), high nibble = value
 // 64p + 32 + i (sub-block 2p+1).
 struct F4K {
-    static constexpr int kSlice = 16 * 144, kStagesShared = 2, kStagesWide = 3;
+    static constexpr int kSlice = 16 * 144, kStagesShared = 3, kStagesWide = 3;
     struct L { uint32_t off_h, off_q, p; };
     struct X { float v[64]; float slo, shi; };   // v[i]: value 64p+i (lo: i<32, hi: i>=32)
     struct Raw { u32x4 h, q0, q1; };
@@ -591,8 +591,9 @@ struct F6K {
 // How one row slice is copied: NFULL instructions of 64 x VEC bytes, then, if
 // the slice is not a whole number of those, one instruction on the first
 // REM / VEC lanes.  VEC = 16 needs 16-byte-aligned rows, VEC = 4 word-aligned.
-// Ring stages: two (one row in flight per wave) except for the 2304-byte
-// slices of wide rows, where seven waves per CU need a second row in flight.
+// Ring stages: two (one row in flight per wave) except for Q4_K's 2304-byte
+// slices (and wide Q4_0 rows), which need a second row in flight to keep
+// enough bytes outstanding per CU (measured per format in the decode step).
 template <class Tr, int VEC, bool SHARED = true>
 struct Plan {
     static constexpr int kPer = 64 * VEC;
