@@ -19,6 +19,7 @@
 // (rounded to fp16) by the workgroup that owns that slot, which attends to the
 // rounded values, so the cache and the attention agree.  A position outside
 // [0, ctx_cap) writes NaN outputs and touches no memory out of bounds.
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 
@@ -80,8 +81,9 @@ __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
     // reads overlap the read of *d_pos; rows past pos are loaded and ignored
     const int t0 = c * chunk;
     const int64_t head_base = int64_t(g) * ctx_cap * D;
-    // K: thread (oc, ps) holds dims 8oc..8oc+7 of positions ps*nik + i
-    const int nik = chunk / NPS;
+    // K: thread (oc, ps) holds dims 8oc..8oc+7 of positions ps*nik + i (a
+    // chunk that is not a multiple of NPS leaves the last subsets short)
+    const int nik = (chunk + NPS - 1) / NPS;
     uint4 kr[NIK];
 #pragma unroll
     for (int i = 0; i < NIK; ++i) {
@@ -89,7 +91,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
         if (i < nik) kr[i] = *reinterpret_cast<const uint4 *>(kc + head_base + int64_t(t) * D + 8 * oc);
     }
     // V: thread (dq, vs) holds dims 4dq..4dq+3 of positions vs*niv + i
-    const int dq = tid % NDQ, vs = tid / NDQ, niv = chunk / NVS;
+    const int dq = tid % NDQ, vs = tid / NDQ, niv = (chunk + NVS - 1) / NVS;
     uint2 vr[NIV];
 #pragma unroll
     for (int i = 0; i < NIV; ++i) {
@@ -337,23 +339,29 @@ hipError_t launch_d(const nt_attn_desc &a, int chunk, int nchunks, const float *
 }  // namespace
 
 int attn_chunk(const nt_attn_desc &a) {
-    // the largest power-of-two chunk that still gives at least kWantWGs (kv
-    // head, chunk) workgroups at full context: the split kernel is
-    // latency-bound, so parallelism wins over fewer partial records; at least
-    // one position per score subset (16 for head_dim 128, 32 for 64), at most
-    // 64 (measured best; up to 128 is supported).  NT_ATTN_CHUNK overrides (a
-    // power of two in [min, 128]).
+    // Positions per workgroup: the split kernel is bound by its arithmetic
+    // and latency, not by bandwidth, so the chunk is chosen for the busiest
+    // CU: at full context the (kv head, chunk) workgroups come to a whole
+    // number per CU of a 256-CU part: two, e.g. 65 positions for 8 kv heads
+    // at 4160 (512 workgroups instead of 520 at 64, where 8 CUs ran a third
+    // one), or one where two would leave a workgroup fewer than 128
+    // (position, q head) pairs, e.g. 36 positions of 4 heads at 1152, where
+    // the fixed cost per workgroup dominates (measured: 8 kv heads of 8 q
+    // heads at 4160, 65 vs 64: -1.0 % decode time; of 4 q heads at 1152, 36
+    // vs 18 and 32: -0.8 %).  NT_ATTN_CHUNK overrides (any value in [8, 128]).
     static const int env = [] {
         const char *v = std::getenv("NT_ATTN_CHUNK");
         return v ? std::atoi(v) : 0;
     }();
-    const int lo = a.head_dim == 64 ? 32 : 16;
-    if (env >= lo && env <= kMaxChunk && (env & (env - 1)) == 0) return env;
-    constexpr int kWantWGs = 256;
-    const int64_t want = int64_t(a.ctx_cap) * a.n_kv_heads / kWantWGs;
-    int c = lo;
-    while (2 * c <= want && c < 64) c *= 2;
-    return c;
+    if (env >= 8 && env <= kMaxChunk) return env;
+    const int kv = std::max(1, a.n_kv_heads), G = std::max(1, a.n_q_heads / kv);
+    int per_head = std::max(1, 512 / kv);
+    int c = (a.ctx_cap + per_head - 1) / per_head;
+    if (c * G < 128) {
+        per_head = std::max(1, 256 / kv);
+        c = (a.ctx_cap + per_head - 1) / per_head;
+    }
+    return std::min(kMaxChunk, std::max(8, c));
 }
 
 size_t attn_workspace_bytes(const nt_attn_desc &a) {

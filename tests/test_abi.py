@@ -165,7 +165,7 @@ def test_attention_argument_errors():
     v = C.c_void_p
     good = nt.attn_desc(32, 8, 128, 1152)
     ws = nt.nt_attn_workspace_bytes(good)
-    assert ws == 32 * 36 * 130 * 4      # chunk 32 -> 36 chunks of (max, sum, o[128]) per q head
+    assert ws == 32 * 32 * 130 * 4      # chunk 36 -> 32 chunks of (max, sum, o[128]) per q head
     args = lambda d, wsb=ws, kn=A: (C.byref(d), v(A), v(kn), v(kn), v(A), v(A), v(A), v(A), v(A), wsb, None)
     assert L.nt_attn_decode(*args(nt.attn_desc(12, 8, 128, 64))) == nt.NT_ESHAPE     # 12 % 8 != 0
     assert L.nt_attn_decode(*args(nt.attn_desc(32, 8, 96, 64))) == nt.NT_ESHAPE      # head_dim 96
