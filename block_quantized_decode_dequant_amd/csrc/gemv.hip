@@ -623,12 +623,14 @@ typedef const __attribute__((address_space(1))) void gbl_void;
 // operations in program order.
 template <int V>
 __device__ __forceinline__ void dma(const uint8_t *base, uint32_t off, uint32_t lds) {
+    int m0_out;   // M0 is declared written (an output), so no value of the compiler's lives in it across the copy
     if constexpr (V == 16)
-        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                     :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
+        asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     : "={m0}"(m0_out) : "v"(off), "s"(base), "s"(lds) : "memory");
     else
-        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-                     :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
+        asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                     : "={m0}"(m0_out) : "v"(off), "s"(base), "s"(lds) : "memory");
+    (void)m0_out;
 }
 
 // LDS address (32-bit, as M0 takes it) of a wave-uniform LDS location.

@@ -192,3 +192,16 @@ def test_llama8b_shaped_two_layers_full_vocab():
     cfg = O.Config(2, 4096, 32, 8, 128, 14336, 128256, 1152, 1e-5, 500000.0)
     w = build_oracle_model(cfg, seed=21, wtype=O.Q8_0, gains="one")
     greedy_parity(cfg, w, n_pos=1024, first_token=1, n_steps=3)
+
+
+def test_llama70b_layer_shape_mixed_kquants():
+    """One layer at the Llama-70B shape (hidden 8192, 64/8 heads of 128, FFN
+    28672, RoPE theta 5e5) in the mixed recipe (Q4_K; Q6_K for attn_v,
+    ffn_down and the head), KV prefix of 4096 positions in a 4160-slot cache:
+    the paired Q4_K/Q6_K q/k/v launch at 8192 columns, the 28672-row SwiGLU
+    launch, the 28672-column down projection and attention over 4097-4099
+    positions, each in the launch configuration of the 70B benchmark model.
+    (Vocabulary 2048 keeps the oracle's build within seconds.)"""
+    cfg = O.Config(1, 8192, 64, 8, 128, 28672, 2048, 4160, 1e-5, 500000.0)
+    w = build_oracle_model(cfg, seed=31, wtype="mix", gains="one")
+    greedy_parity(cfg, w, n_pos=4096, first_token=1, n_steps=3)
