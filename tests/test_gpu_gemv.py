@@ -88,7 +88,10 @@ def _gemv_case(t, rows, cols, seed, accumulate=False):
     assert_close(got[:rows], ref, what=f"gemv {TID[TYPES.index(t)]} {rows}x{cols}")
 
 
-SHAPES = [(1, 256), (3, 512), (37, 1024), (101, 4352), (64, 40960), (5, 2048 + 256)]
+# ... plus one row on the fast path, two rows of the 28672-column (per-wave
+# staging) layout, and the largest column count the calls accept
+SHAPES = [(1, 256), (3, 512), (37, 1024), (101, 4352), (64, 40960), (5, 2048 + 256),
+          (1, 8192), (2, 28672), (3, 65536)]
 
 
 @pytest.mark.parametrize("t", TYPES, ids=TID)

@@ -106,6 +106,8 @@ ATTN_CASES = [
     (32, 8, 128, 1152, 1024), (32, 8, 128, 1152, 0), (32, 8, 128, 1152, 1151), (32, 8, 128, 1152, 31),
     (32, 8, 128, 1152, 32), (64, 8, 128, 4160, 4096), (64, 8, 128, 4160, 4159), (4, 2, 64, 32, 17),
     (8, 8, 64, 64, 63), (16, 8, 128, 300, 150),
+    # long context: the chunk reaches its 128-position cap, 128 chunks per kv head
+    (32, 8, 128, 16384, 16000),
 ]
 
 
