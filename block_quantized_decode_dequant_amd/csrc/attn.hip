@@ -75,6 +75,15 @@ __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
     static_assert(NQ <= kAttnThreads, "one float4 of q per thread");
     float4 q4 = make_float4(0.f, 0.f, 0.f, 0.f);
     if (tid < NQ) q4 = reinterpret_cast<const float4 *>(q + g * G * D)[tid];
+    // the new token's k and v pair of this thread, loaded by every workgroup
+    // with q (1 KB): only the one that owns slot pos uses them, but it then
+    // needs no second memory round trip after reading the position
+    // (k_new and v_new are only 4-byte aligned: two float loads each)
+    float2 kn2 = make_float2(0.f, 0.f), vn2 = make_float2(0.f, 0.f);
+    if (k_new && tid < D / 2) {
+        kn2 = make_float2(k_new[g * D + 2 * tid], k_new[g * D + 2 * tid + 1]);
+        vn2 = make_float2(v_new[g * D + 2 * tid], v_new[g * D + 2 * tid + 1]);
+    }
     const int oc = tid % LPP, ps = tid / LPP;
     // ---- every K and V load of the chunk, issued before the position is
     // known (rows past the cache end re-read its last row), so the cache
@@ -132,7 +141,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
         *reinterpret_cast<float4 *>(&qs[4 * tid]) = make_float4(x[0] * scale, x[1] * scale, x[2] * scale, x[3] * scale);
     }
     if (owns_new && tid < D / 2) {
-        float k0 = k_new[g * D + 2 * tid], k1 = k_new[g * D + 2 * tid + 1];
+        float k0 = kn2.x, k1 = kn2.y;
         if (rope) {
             float cs, sn;
             angle(tid, cs, sn);
@@ -141,7 +150,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
             k1 = a * sn + b * cs;
         }
         const uint16_t kb0 = f2h_bits(k0), kb1 = f2h_bits(k1);
-        const uint16_t vb0 = f2h_bits(v_new[g * D + 2 * tid]), vb1 = f2h_bits(v_new[g * D + 2 * tid + 1]);
+        const uint16_t vb0 = f2h_bits(vn2.x), vb1 = f2h_bits(vn2.y);
         const int64_t at = head_base + int64_t(pos) * D + 2 * tid;
         *reinterpret_cast<uint32_t *>(kc + at) = uint32_t(kb0) | (uint32_t(kb1) << 16);
         *reinterpret_cast<uint32_t *>(vc + at) = uint32_t(vb0) | (uint32_t(vb1) << 16);
