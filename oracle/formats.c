@@ -1,5 +1,5 @@
 /*
- * formats.c -- the four block-quantized weight formats: sizes, decoders and
+ * formats.c -- the block-quantized weight formats: sizes, decoders and
  * the oracle's own encoders.  Test infrastructure only.
  *
  * Source: the ntransformer write-up (GeekNews topic 26894), "Overview", names
@@ -16,6 +16,10 @@
  *         sub-block j = e/32 has 6-bit scale S_j and 6-bit min M_j;
  *         q = nibble of qs[32*(j/2) + e%32] (low for even j, high for odd j)
  *         x_e = (d*S_j)*q - dmin*M_j
+ *   Q5_K 176 B / 256 values: d, dmin (fp16) | scales u8[12] | qh u8[32] | qs u8[128]
+ *         scales, mins and low 4 bits as in Q4_K; the fifth bit of value
+ *         e = 32j + l is bit j of qh[l]; q in [0,31]
+ *         x_e = (d*S_j)*q - dmin*M_j
  *   Q6_K 210 B / 256 values: ql u8[128] | qh u8[64] | scales int8[16] | d (fp16)
  *         half h = e/128, r = e%128, k = r/32, l = r%32;
  *         low 4 bits: nibble of ql[64h + 32(k&1) + l] (low if k<2, else high);
@@ -29,6 +33,9 @@
  *
  * Decoders form each value exactly in fp64 (every product here has at most
  * 23 significant bits) and round once to fp32.
+ *
+ * Q5_K is the next format the write-up lists ("Overview"); it has the same
+ * 6-bit scale/min packing as Q4_K plus one bit plane, 5.5 bits per weight.
  */
 #include "oracle.h"
 
@@ -40,7 +47,7 @@ int64_t or_block_elems(int type)
     switch (type) {
     case OR_F32: case OR_F16: return 1;
     case OR_Q8_0: case OR_Q4_0: return 32;
-    case OR_Q4_K: case OR_Q6_K: return 256;
+    case OR_Q4_K: case OR_Q5_K: case OR_Q6_K: return 256;
     default: return -1;
     }
 }
@@ -53,6 +60,7 @@ int64_t or_block_bytes(int type)
     case OR_Q8_0: return 34;
     case OR_Q4_0: return 18;
     case OR_Q4_K: return 144;
+    case OR_Q5_K: return 176;
     case OR_Q6_K: return 210;
     default: return -1;
     }
@@ -115,6 +123,22 @@ static void dq_q4_k(const uint8_t *blk, float *out)
     }
 }
 
+static void dq_q5_k(const uint8_t *blk, float *out)
+{
+    double d = or_f16_to_f64(rd16(blk));
+    double dmin = or_f16_to_f64(rd16(blk + 2));
+    const uint8_t *sc = blk + 4, *qh = blk + 16, *qs = blk + 48;
+    for (int e = 0; e < 256; ++e) {
+        int j = e / 32, l = e % 32, S, M;
+        q4k_scale_min(sc, j, &S, &M);
+        uint8_t byte = qs[32 * (j / 2) + l];
+        int lo = (j % 2 == 0) ? (byte & 15) : (byte >> 4);
+        int q = lo | (((qh[l] >> j) & 1) << 4);
+        /* d*S*q (at most 22 bits) and dmin*M are exact; one rounding. */
+        out[e] = (float)(d * S * q - dmin * M);
+    }
+}
+
 static void dq_q6_k(const uint8_t *blk, float *out)
 {
     const uint8_t *ql = blk, *qh = blk + 128;
@@ -144,6 +168,7 @@ int or_dequant(int type, const uint8_t *blocks, int64_t n, float *out)
         case OR_Q8_0: dq_q8_0(blk, o); break;
         case OR_Q4_0: dq_q4_0(blk, o); break;
         case OR_Q4_K: dq_q4_k(blk, o); break;
+        case OR_Q5_K: dq_q5_k(blk, o); break;
         case OR_Q6_K: dq_q6_k(blk, o); break;
         }
     }
@@ -192,9 +217,12 @@ static int q_q4_0(const float *x, uint8_t *blk)
     return 0;
 }
 
-static int q_q4_k(const float *x, uint8_t *blk)
+/* Q4_K and Q5_K: the same steps, with codes of `levels` + 1 values (15 or
+ * 31).  Returns the per-sub-block offsets o, steps d*S and the packed header
+ * (d, dmin, scales) in blk[0..16). */
+static void kq_header(const float *x, int levels, uint8_t *blk, double o[8], double step[8])
 {
-    double m[8], o[8], s[8], mmax = 0, smax = 0;
+    double m[8], s[8], mmax = 0, smax = 0;
     int S[8], M[8];
     /* 1. Per sub-block offset: the negated minimum, clipped at 0; one shared
      *    fp16 dmin with 6-bit multipliers rounded up, so o_j >= m_j.        */
@@ -211,40 +239,66 @@ static int q_q4_k(const float *x, uint8_t *blk)
         M[j] = (dmin == 0.0) ? 0 : (int)ceil(m[j] / dmin);
         o[j] = dmin * M[j];
     }
-    /* 2. Per sub-block step covering [-o_j, max x] in 15 steps; one shared
-     *    fp16 d with 6-bit multipliers rounded up, so step_j >= s_j.        */
+    /* 2. Per sub-block step covering [-o_j, max x] in `levels` steps; one
+     *    shared fp16 d with 6-bit multipliers rounded up, so step_j >= s_j. */
     for (int j = 0; j < 8; ++j) {
         double mx = -o[j];
         for (int i = 0; i < 32; ++i)
             mx = fmax(mx, (double)x[32 * j + i]);
-        s[j] = (mx + o[j]) / 15.0;
+        s[j] = (mx + o[j]) / (double)levels;
         smax = fmax(smax, s[j]);
     }
     uint16_t dh = or_f64_to_f16_up(smax / 63.0);
     double d = or_f16_to_f64(dh);
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < 8; ++j) {
         S[j] = (d == 0.0) ? 0 : (int)ceil(s[j] / d);
-
+        step[j] = d * S[j];
+    }
     wr16(blk, dh);
     wr16(blk + 2, dminh);
-    uint8_t *b = blk + 4, *qs = blk + 16;
+    uint8_t *b = blk + 4;
     memset(b, 0, 12);
-    memset(qs, 0, 128);
     for (int j = 0; j < 4; ++j) {
         b[j] = (uint8_t)((S[j] & 63) | ((S[j + 4] >> 4) << 6));
         b[j + 4] = (uint8_t)((M[j] & 63) | ((M[j + 4] >> 4) << 6));
         b[j + 8] = (uint8_t)((S[j + 4] & 15) | ((M[j + 4] & 15) << 4));
     }
-    /* 3. Codes. */
-    for (int j = 0; j < 8; ++j) {
-        double step = d * S[j];
+}
+
+/* 3. Code of value x in sub-block j: round((x + o_j) / step_j) in [0, levels]. */
+static int kq_code(double x, double o, double step, int levels)
+{
+    double q = (step == 0.0) ? 0.0 : round((x + o) / step);
+    return (int)fmin((double)levels, fmax(0.0, q));
+}
+
+static int q_q4_k(const float *x, uint8_t *blk)
+{
+    double o[8], step[8];
+    kq_header(x, 15, blk, o, step);
+    uint8_t *qs = blk + 16;
+    memset(qs, 0, 128);
+    for (int j = 0; j < 8; ++j)
         for (int i = 0; i < 32; ++i) {
-            double q = (step == 0.0) ? 0.0 : round(((double)x[32 * j + i] + o[j]) / step);
-            int qi = (int)fmin(15.0, fmax(0.0, q));
-            uint8_t *byte = &qs[32 * (j / 2) + i];
-            *byte |= (uint8_t)((j % 2 == 0) ? qi : (qi << 4));
+            int qi = kq_code((double)x[32 * j + i], o[j], step[j], 15);
+            qs[32 * (j / 2) + i] |= (uint8_t)((j % 2 == 0) ? qi : (qi << 4));
         }
-    }
+    return 0;
+}
+
+static int q_q5_k(const float *x, uint8_t *blk)
+{
+    double o[8], step[8];
+    kq_header(x, 31, blk, o, step);
+    uint8_t *qh = blk + 16, *qs = blk + 48;
+    memset(qh, 0, 32);
+    memset(qs, 0, 128);
+    for (int j = 0; j < 8; ++j)
+        for (int i = 0; i < 32; ++i) {
+            int qi = kq_code((double)x[32 * j + i], o[j], step[j], 31);
+            qs[32 * (j / 2) + i] |= (uint8_t)((j % 2 == 0) ? (qi & 15) : ((qi & 15) << 4));
+            qh[i] |= (uint8_t)((qi >> 4) << j);
+        }
     return 0;
 }
 
@@ -298,6 +352,7 @@ int or_quantize(int type, const float *x, int64_t n, uint8_t *blocks)
         case OR_Q8_0: q_q8_0(xb, blk); break;
         case OR_Q4_0: q_q4_0(xb, blk); break;
         case OR_Q4_K: q_q4_k(xb, blk); break;
+        case OR_Q5_K: q_q5_k(xb, blk); break;
         case OR_Q6_K: q_q6_k(xb, blk); break;
         }
     }

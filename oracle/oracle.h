@@ -37,7 +37,7 @@ extern "C" {
 #endif
 
 /* Block type ids (the GGUF type-field numbering). */
-enum { OR_F32 = 0, OR_F16 = 1, OR_Q4_0 = 2, OR_Q8_0 = 8, OR_Q4_K = 12, OR_Q6_K = 14 };
+enum { OR_F32 = 0, OR_F16 = 1, OR_Q4_0 = 2, OR_Q8_0 = 8, OR_Q4_K = 12, OR_Q5_K = 13, OR_Q6_K = 14 };
 
 /* ---- IEEE binary16 by bit manipulation ---------------------------------- */
 double   or_f16_to_f64(uint16_t h);

@@ -19,7 +19,7 @@ import oracle as O
 from block_quantized_decode_dequant_amd import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-TYPES = {"q8_0": O.Q8_0, "q4_0": O.Q4_0, "q4_k": O.Q4_K, "q6_k": O.Q6_K}
+TYPES = {"q8_0": O.Q8_0, "q4_0": O.Q4_0, "q4_k": O.Q4_K, "q5_k": O.Q5_K, "q6_k": O.Q6_K}
 
 
 def load_golden(path):
@@ -46,7 +46,7 @@ GOLDEN_FILES = sorted(glob.glob(os.path.join(GOLDEN, "*.txt")))
 
 def test_golden_files_present():
     names = {os.path.basename(p) for p in GOLDEN_FILES}
-    for need in ["q8_0_e1.txt", "q8_0_e2.txt", "q4_0_e3.txt", "q4_k_e4.txt", "q6_k_e5.txt"]:
+    for need in ["q8_0_e1.txt", "q8_0_e2.txt", "q4_0_e3.txt", "q4_k_e4.txt", "q5_k_e6.txt", "q6_k_e5.txt"]:
         assert need in names
 
 
@@ -60,8 +60,9 @@ def test_hand_worked_blocks(path):
 
 
 def test_block_sizes():
-    assert [O.block_elems(t) for t in (O.Q8_0, O.Q4_0, O.Q4_K, O.Q6_K)] == [32, 32, 256, 256]
-    assert [O.block_bytes(t) for t in (O.Q8_0, O.Q4_0, O.Q4_K, O.Q6_K)] == [34, 18, 144, 210]
+    assert [O.block_elems(t) for t in (O.Q8_0, O.Q4_0, O.Q4_K, O.Q5_K, O.Q6_K)] == [32, 32, 256, 256, 256]
+    assert [O.block_bytes(t) for t in (O.Q8_0, O.Q4_0, O.Q4_K, O.Q5_K, O.Q6_K)] == [34, 18, 144, 176, 210]
+    assert O.row_bytes(O.Q5_K, 8192) * 8 / 8192 == 5.5     # bits per weight
     assert O.row_bytes(O.Q4_K, 8192) == 32 * 144
     assert O.row_bytes(O.Q4_K, 100) == -1
     assert O.block_elems(99) == -1
@@ -156,6 +157,16 @@ def _bound_q4_k(x):
     return np.repeat(step_hi / 2, 32, axis=1).reshape(x.shape)
 
 
+def _bound_q5_k(x):
+    xs = x.reshape(-1, 8, 32)
+    m = np.maximum(0, -xs.min(axis=2))
+    dmin_hi = m.max(axis=1, keepdims=True) / 63 * (1 + U10) + Q16
+    s_hi = (np.maximum(xs.max(axis=2), 0) + m + dmin_hi) / 31
+    d_hi = s_hi.max(axis=1, keepdims=True) / 63 * (1 + U10) + Q16
+    step_hi = s_hi + d_hi
+    return np.repeat(step_hi / 2, 32, axis=1).reshape(x.shape)
+
+
 def _bound_q6_k(x):
     xs = x.reshape(-1, 16, 16)
     s = np.abs(xs).max(axis=2) / 31
@@ -163,7 +174,8 @@ def _bound_q6_k(x):
     return np.repeat((s + d_hi) / 2, 16, axis=1).reshape(x.shape)
 
 
-BOUNDS = {O.Q8_0: _bound_q8_0, O.Q4_0: _bound_q4_0, O.Q4_K: _bound_q4_k, O.Q6_K: _bound_q6_k}
+BOUNDS = {O.Q8_0: _bound_q8_0, O.Q4_0: _bound_q4_0, O.Q4_K: _bound_q4_k, O.Q5_K: _bound_q5_k,
+          O.Q6_K: _bound_q6_k}
 
 
 def _edge_blocks(be):
@@ -177,7 +189,7 @@ def _edge_blocks(be):
     return np.concatenate([z, spike, neg, pos, const, -const, ramp])
 
 
-@pytest.mark.parametrize("t", [O.Q8_0, O.Q4_0, O.Q4_K, O.Q6_K], ids=["q8_0", "q4_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("t", [O.Q8_0, O.Q4_0, O.Q4_K, O.Q5_K, O.Q6_K], ids=["q8_0", "q4_0", "q4_k", "q5_k", "q6_k"])
 @pytest.mark.parametrize("std", [0.02, 1.0])
 def test_quantize_round_trip_bound(t, std):
     be = O.block_elems(t)
@@ -189,7 +201,7 @@ def test_quantize_round_trip_bound(t, std):
     assert np.all(err <= bound), (err - bound).max()
 
 
-@pytest.mark.parametrize("t", [O.Q8_0, O.Q4_0, O.Q4_K, O.Q6_K], ids=["q8_0", "q4_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("t", [O.Q8_0, O.Q4_0, O.Q4_K, O.Q5_K, O.Q6_K], ids=["q8_0", "q4_0", "q4_k", "q5_k", "q6_k"])
 def test_quantize_zero_block(t):
     be = O.block_elems(t)
     z = np.zeros(3 * be, np.float32)
@@ -202,6 +214,8 @@ def _grid_input(t, nblocks):
     Q8_0: k * 2^-10, k in [-127, 127], one |k| = 127 per block -> d = 2^-10.
     Q4_0: k * 2^-3, k in [-7, 7], one |k| = 7 per block -> d = 2^-3.
     Q4_K: k * 63 * 2^-12, k in [0, 15], a 0 and a 15 per sub-block -> dmin = 0,
+          d = 2^-12, every sub-scale 63.
+    Q5_K: k * 63 * 2^-12, k in [0, 31], a 0 and a 31 per sub-block -> dmin = 0,
           d = 2^-12, every sub-scale 63.
     Q6_K: k * 127 * 2^-12, k in [-31, 31], one |k| = 31 per sub-block ->
           d = 2^-12, every sub-scale 127.
@@ -216,11 +230,14 @@ def _grid_input(t, nblocks):
     if t == O.Q4_K:
         k = g.integers(0, 16, size=(nblocks * 8, 32)); k[:, 0] = 0; k[:, 31] = 15
         return (k * 63 * 2.0**-12).astype(np.float32).reshape(-1)
+    if t == O.Q5_K:
+        k = g.integers(0, 32, size=(nblocks * 8, 32)); k[:, 0] = 0; k[:, 31] = 31
+        return (k * 63 * 2.0**-12).astype(np.float32).reshape(-1)
     k = g.integers(-31, 32, size=(nblocks * 16, 16)); k[:, 7] = 31
     return (k * 127 * 2.0**-12).astype(np.float32).reshape(-1)
 
 
-@pytest.mark.parametrize("t", [O.Q8_0, O.Q4_0, O.Q4_K, O.Q6_K], ids=["q8_0", "q4_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("t", [O.Q8_0, O.Q4_0, O.Q4_K, O.Q5_K, O.Q6_K], ids=["q8_0", "q4_0", "q4_k", "q5_k", "q6_k"])
 def test_quantize_exact_on_grid_values(t):
     x = _grid_input(t, 16)
     assert np.array_equal(O.dequant(t, O.quantize(t, x), x.size), x)
@@ -243,3 +260,34 @@ def test_q8_0_packing_matches_generator_layout():
     vals = O.dequant(O.Q8_0, a, qs.size).astype(np.float64)
     d = d_bits.view(np.float16).astype(np.float64)
     assert np.array_equal(vals, np.repeat(d, 32) * qs.astype(np.float64))
+
+
+def test_q5_k_without_fifth_bits_decodes_as_q4_k():
+    """Q5_K is Q4_K plus a bit plane: with every qh byte 0, a Q5_K block
+    (header, 32 zero bytes, the same nibbles) decodes exactly like the Q4_K
+    block; setting bit j of qh[l] adds d*S_j*16 to value 32j + l and nothing
+    else.  Checked on encoded random blocks, so every scale/min packing case
+    occurs."""
+    x = synth.normal_f32(5, 930, 16 * 256, std=0.05)
+    b4 = O.quantize(O.Q4_K, x).reshape(-1, 144)
+    b5 = np.zeros((b4.shape[0], 176), np.uint8)
+    b5[:, :16] = b4[:, :16]
+    b5[:, 48:] = b4[:, 16:]
+    assert np.array_equal(O.dequant(O.Q5_K, b5.reshape(-1), x.size), O.dequant(O.Q4_K, b4.reshape(-1), x.size))
+    g = synth.rng(5, 931)
+    for blk in range(4):
+        j, l = int(g.integers(0, 8)), int(g.integers(0, 32))
+        b5b = b5.copy()
+        b5b[blk, 16 + l] |= np.uint8(1 << j)
+        before = O.dequant(O.Q5_K, b5.reshape(-1), x.size).astype(np.float64)
+        after = O.dequant(O.Q5_K, b5b.reshape(-1), x.size).astype(np.float64)
+        e = 256 * blk + 32 * j + l
+        d = O.f16_to_f64(int(b5[blk, 0]) | (int(b5[blk, 1]) << 8))
+        sc = b5[blk, 4:16]
+        S = (sc[j] & 63) if j < 4 else ((sc[j + 4] & 15) | ((sc[j - 4] >> 6) << 4))
+        changed = np.nonzero(after != before)[0]
+        assert set(changed.tolist()) <= {e}
+        # each decoded value is one rounding of an exact value: the difference
+        # is d*S*16 up to one fp32 ulp of each
+        ulp = 2.0**-23 * max(abs(after[e]), abs(before[e]), 2.0**-126)
+        assert abs((after[e] - before[e]) - d * int(S) * 16) <= 2 * ulp
