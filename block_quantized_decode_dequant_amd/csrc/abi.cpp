@@ -30,7 +30,7 @@ int64_t block_elems(nt_qtype t) {
     switch (t) {
     case NT_F32: case NT_F16: return 1;
     case NT_Q8_0: case NT_Q4_0: return 32;
-    case NT_Q4_K: case NT_Q6_K: return 256;
+    case NT_Q4_K: case NT_Q5_K: case NT_Q6_K: return 256;
     }
     return -1;
 }
@@ -42,12 +42,15 @@ int64_t block_bytes(nt_qtype t) {
     case NT_Q8_0: return 34;
     case NT_Q4_0: return 18;
     case NT_Q4_K: return 144;
+    case NT_Q5_K: return 176;
     case NT_Q6_K: return 210;
     }
     return -1;
 }
 
-bool is_quant(nt_qtype t) { return t == NT_Q8_0 || t == NT_Q4_0 || t == NT_Q4_K || t == NT_Q6_K; }
+bool is_quant(nt_qtype t) {
+    return t == NT_Q8_0 || t == NT_Q4_0 || t == NT_Q4_K || t == NT_Q5_K || t == NT_Q6_K;
+}
 
 // Device presence, checked after argument validation.
 static nt_status need_device() {
@@ -73,6 +76,7 @@ static const char *qname(nt_qtype t) {
     case NT_Q8_0: return "q8_0";
     case NT_Q4_0: return "q4_0";
     case NT_Q4_K: return "q4_k";
+    case NT_Q5_K: return "q5_k";
     case NT_Q6_K: return "q6_k";
     case NT_F32: return "f32";
     case NT_F16: return "f16";
@@ -131,6 +135,7 @@ nt_status nt_dequant(nt_qtype t, const void *blocks, float *out, int64_t n, nt_s
 nt_status nt_dequant_q8_0(const void *b, float *o, int64_t n, nt_stream s) { return nt_dequant(NT_Q8_0, b, o, n, s); }
 nt_status nt_dequant_q4_0(const void *b, float *o, int64_t n, nt_stream s) { return nt_dequant(NT_Q4_0, b, o, n, s); }
 nt_status nt_dequant_q4_k(const void *b, float *o, int64_t n, nt_stream s) { return nt_dequant(NT_Q4_K, b, o, n, s); }
+nt_status nt_dequant_q5_k(const void *b, float *o, int64_t n, nt_stream s) { return nt_dequant(NT_Q5_K, b, o, n, s); }
 nt_status nt_dequant_q6_k(const void *b, float *o, int64_t n, nt_stream s) { return nt_dequant(NT_Q6_K, b, o, n, s); }
 
 // ---- GEMV ------------------------------------------------------------------------
@@ -224,6 +229,7 @@ nt_status nt_gemv_swiglu(nt_qtype t, const void *W_gate, const void *W_up, int64
 NT_GEMV_FN(nt_gemv_q8_0, NT_Q8_0)
 NT_GEMV_FN(nt_gemv_q4_0, NT_Q4_0)
 NT_GEMV_FN(nt_gemv_q4_k, NT_Q4_K)
+NT_GEMV_FN(nt_gemv_q5_k, NT_Q5_K)
 NT_GEMV_FN(nt_gemv_q6_k, NT_Q6_K)
 #undef NT_GEMV_FN
 

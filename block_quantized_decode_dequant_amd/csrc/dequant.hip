@@ -43,6 +43,27 @@ __device__ __forceinline__ float dq_q4_k(const uint8_t *blk, int e) {
     return ds * static_cast<float>(q) - dm;         // one rounding
 }
 
+// Q5_K: Q4_K's header and nibbles (qs after 32 bytes of qh) plus bit j of
+// qh[l] as the fifth bit of value 32j + l; (d*S)*q has at most 22 bits.
+__device__ __forceinline__ float dq_q5_k(const uint8_t *blk, int e) {
+    const float d = h2f(rd16(blk)), dmin = h2f(rd16(blk + 2));
+    const uint8_t *b = blk + 4;
+    const int j = e >> 5, l = e & 31;
+    int S, M;
+    if (j < 4) {
+        S = b[j] & 63;
+        M = b[j + 4] & 63;
+    } else {
+        S = (b[j + 4] & 15) | ((b[j - 4] >> 6) << 4);
+        M = (b[j + 4] >> 4) | ((b[j] >> 6) << 4);
+    }
+    uint32_t byte = blk[48 + 32 * (j >> 1) + l];
+    int q = int((j & 1) ? (byte >> 4) : (byte & 15)) | (((blk[16 + l] >> j) & 1) << 4);
+    const float ds = d * static_cast<float>(S);     // exact
+    const float dm = dmin * static_cast<float>(M);  // exact
+    return ds * static_cast<float>(q) - dm;         // one rounding
+}
+
 __device__ __forceinline__ float dq_q6_k(const uint8_t *blk, int e) {
     const int h = e >> 7, r = e & 127, k = r >> 5, l = r & 31;
     uint32_t lob = blk[64 * h + 32 * (k & 1) + l];
@@ -58,7 +79,7 @@ template <nt_qtype T>
 __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t *__restrict__ blocks,
                                                        float *__restrict__ out, int64_t n) {
     constexpr int BE = (T == NT_Q8_0 || T == NT_Q4_0) ? 32 : 256;
-    constexpr int BB = T == NT_Q8_0 ? 34 : T == NT_Q4_0 ? 18 : T == NT_Q4_K ? 144 : 210;
+    constexpr int BB = T == NT_Q8_0 ? 34 : T == NT_Q4_0 ? 18 : T == NT_Q4_K ? 144 : T == NT_Q5_K ? 176 : 210;
     const int64_t stride = int64_t(gridDim.x) * blockDim.x;
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
         const uint8_t *blk = blocks + (i / BE) * BB;
@@ -67,6 +88,7 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t *__restrict_
         if constexpr (T == NT_Q8_0) v = dq_q8_0(blk, e);
         else if constexpr (T == NT_Q4_0) v = dq_q4_0(blk, e);
         else if constexpr (T == NT_Q4_K) v = dq_q4_k(blk, e);
+        else if constexpr (T == NT_Q5_K) v = dq_q5_k(blk, e);
         else v = dq_q6_k(blk, e);
         out[i] = v;
     }
@@ -83,6 +105,7 @@ hipError_t launch_dequant(nt_qtype t, const void *blocks, float *out, int64_t n,
     case NT_Q8_0: dequant_kernel<NT_Q8_0><<<grid, threads, 0, st>>>(b, out, n); break;
     case NT_Q4_0: dequant_kernel<NT_Q4_0><<<grid, threads, 0, st>>>(b, out, n); break;
     case NT_Q4_K: dequant_kernel<NT_Q4_K><<<grid, threads, 0, st>>>(b, out, n); break;
+    case NT_Q5_K: dequant_kernel<NT_Q5_K><<<grid, threads, 0, st>>>(b, out, n); break;
     case NT_Q6_K: dequant_kernel<NT_Q6_K><<<grid, threads, 0, st>>>(b, out, n); break;
     default: return hipErrorInvalidValue;
     }

@@ -204,6 +204,61 @@ struct Q4K {
     }
 };
 
+// ---- Q5_K: one unit = one 16-byte code chunk of a 176-byte super-block ------
+// The Q4_K chunk (bytes 48 + 16t .. of qs: pair p = t/2, half hh = t%2, low
+// nibbles sub-block 2p, high nibbles 2p+1, element l = 16hh + i of each) plus
+// the 16 bytes qh[16hh ..] whose bits 2p and 2p+1 are the two sub-blocks'
+// fifth bits.  Codes q in [0, 31] are assembled one per byte and converted
+// with byte-to-float conversions; scale and min as in Q4_K.
+struct Q5K {
+    static constexpr int kBlockElems = 256;
+    struct Raw { u32x4 hdr, qh, q; };
+    using X = Q4K::X;
+
+    __device__ static void load_x(const float *x, int64_t unit, X &xs) { Q4K::load_x(x, unit, xs); }
+    __device__ static void load(const uint8_t *W, int64_t g, uint32_t t, Raw &r) {
+        const uint8_t *p = W + g * 176;
+        r.hdr = ld4(p);
+        r.qh = ld4(p + 16 + 16 * (t & 1));
+        r.q = ld4(p + 48 + 16 * t);
+    }
+    __device__ static float dot(const Raw &r, const X &xs) {
+        const uint32_t qw[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+        const uint32_t hw[4] = {r.qh.x, r.qh.y, r.qh.z, r.qh.w};
+        const uint32_t p = xs.t >> 1;
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = opaque((qw[i] & kLo4) | (((hw[i] >> (2 * p)) & 0x01010101u) << 4));
+            const uint32_t hi = opaque(((qw[i] >> 4) & kLo4) | (((hw[i] >> (2 * p + 1)) & 0x01010101u) << 4));
+            s0 = fmaf(ubyte<0>(lo), xs.lo[4 * i + 0], s0);
+            s0 = fmaf(ubyte<1>(lo), xs.lo[4 * i + 1], s0);
+            s0 = fmaf(ubyte<2>(lo), xs.lo[4 * i + 2], s0);
+            s0 = fmaf(ubyte<3>(lo), xs.lo[4 * i + 3], s0);
+            s1 = fmaf(ubyte<0>(hi), xs.hi[4 * i + 0], s1);
+            s1 = fmaf(ubyte<1>(hi), xs.hi[4 * i + 1], s1);
+            s1 = fmaf(ubyte<2>(hi), xs.hi[4 * i + 2], s1);
+            s1 = fmaf(ubyte<3>(hi), xs.hi[4 * i + 3], s1);
+        }
+        const uint32_t sft = 16 * (p & 1);
+        const uint32_t y = r.hdr.y >> sft, z = r.hdr.z >> sft, w = r.hdr.w >> sft;
+        uint32_t S0, M0, S1, M1;
+        if (p < 2) {
+            S0 = y & 63; M0 = z & 63;
+            S1 = (y >> 8) & 63; M1 = (z >> 8) & 63;
+        } else {
+            S0 = (w & 15) | (((y >> 6) & 3) << 4);
+            M0 = ((w >> 4) & 15) | (((z >> 6) & 3) << 4);
+            S1 = ((w >> 8) & 15) | (((y >> 14) & 3) << 4);
+            M1 = ((w >> 12) & 15) | (((z >> 14) & 3) << 4);
+        }
+        const float d = h2f(r.hdr.x), dmin = h2f(r.hdr.x >> 16);
+        const float pos = fmaf(float(S0), s0, float(S1) * s1);
+        const float neg = fmaf(float(M0), xs.slo, float(M1) * xs.shi);
+        return fmaf(d, pos, -dmin * neg);
+    }
+};
+
 // ---- Q6_K: one unit = 32 values of a 210-byte super-block -------------------
 // Unit t (0..7): half h = t/4, lane slot m = t%4; values 128h + 32k + 8m + i
 // for k = 0..3, i = 0..7.  Bytes used: ql[64h + 8m + i] (k = 0 low, k = 2
@@ -512,6 +567,62 @@ struct F4K {
         const float pos = fmaf(float(16 * S0), al, float(S1) * ah);
         const float neg = fmaf(float(M0), xs.slo, float(M1) * xs.shi);
         return fmaf(kNib20 * d, pos, -dmin * neg);
+    }
+};
+
+// ---- Q5_K fast: one lane = code pair p (32 bytes) of super-block b ---------
+// As F4K (byte 32p + i of qs: low nibble = value 64p + i, high nibble = value
+// 64p + 32 + i), plus all 32 bytes of qh, whose bits 2p and 2p+1 are the
+// fifth bits of those values.  Codes are assembled one per byte (nibble |
+// bit << 4) and converted with byte-to-float conversions.
+struct F5K {
+    static constexpr int kSlice = 16 * 176, kStagesShared = 3, kStagesWide = 3;
+    struct L { uint32_t off_h, off_q, p; };
+    using X = F4K::X;
+    struct Raw { u32x4 h, qh0, qh1, q0, q1; };
+    __device__ static L lane(int l) {
+        const uint32_t b = uint32_t(l >> 2), p = uint32_t(l & 3);
+        return {176 * b, 176 * b + 48 + 32 * p, p};
+    }
+    __device__ static uint32_t x_chunk(int l, int j) { return F4K::x_chunk(l, j); }
+    __device__ static void sums(X &xs) { F4K::sums(xs); }
+    __device__ static void load(const uint8_t *base, const L &l, Raw &r) {
+        r.h = ld4(base + l.off_h);
+        r.qh0 = ld4(base + l.off_h + 16);
+        r.qh1 = ld4(base + l.off_h + 32);
+        r.q0 = ld4(base + l.off_q);
+        r.q1 = ld4(base + l.off_q + 16);
+    }
+    __device__ static float dot(const Raw &r, const X &xs, const L &l) {
+        const uint32_t q[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
+        const uint32_t hb[8] = {r.qh0.x, r.qh0.y, r.qh0.z, r.qh0.w, r.qh1.x, r.qh1.y, r.qh1.z, r.qh1.w};
+        const uint32_t p = l.p, sl = 2 * p, sh = 2 * p + 1;
+        float al = 0.f, ah = 0.f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const uint32_t lo = opaque((q[m] & kLo4) | (((hb[m] >> sl) & 0x01010101u) << 4));
+            const uint32_t hi = opaque(((q[m] >> 4) & kLo4) | (((hb[m] >> sh) & 0x01010101u) << 4));
+            al = fmaf(ubyte<0>(lo), xs.v[4 * m + 0], al);
+            al = fmaf(ubyte<1>(lo), xs.v[4 * m + 1], al);
+            al = fmaf(ubyte<2>(lo), xs.v[4 * m + 2], al);
+            al = fmaf(ubyte<3>(lo), xs.v[4 * m + 3], al);
+            ah = fmaf(ubyte<0>(hi), xs.v[32 + 4 * m + 0], ah);
+            ah = fmaf(ubyte<1>(hi), xs.v[32 + 4 * m + 1], ah);
+            ah = fmaf(ubyte<2>(hi), xs.v[32 + 4 * m + 2], ah);
+            ah = fmaf(ubyte<3>(hi), xs.v[32 + 4 * m + 3], ah);
+        }
+        const uint32_t sft = 16 * (p & 1);
+        const uint32_t y = r.h.y >> sft, z = r.h.z >> sft, w = r.h.w >> sft;
+        // both encodings computed, one kept by a lane mask: no branch
+        const uint32_t lm = opaque(p < 2 ? 0xffffffffu : 0u), hm = ~lm;
+        const uint32_t S0 = ((y & 63) & lm) | (((w & 15) | (((y >> 6) & 3) << 4)) & hm);
+        const uint32_t M0 = ((z & 63) & lm) | ((((w >> 4) & 15) | (((z >> 6) & 3) << 4)) & hm);
+        const uint32_t S1 = (((y >> 8) & 63) & lm) | ((((w >> 8) & 15) | (((y >> 14) & 3) << 4)) & hm);
+        const uint32_t M1 = (((z >> 8) & 63) & lm) | ((((w >> 12) & 15) | (((z >> 14) & 3) << 4)) & hm);
+        const float d = h2f(r.h.x), dmin = h2f(r.h.x >> 16);
+        const float pos = fmaf(float(S0), al, float(S1) * ah);
+        const float neg = fmaf(float(M0), xs.slo, float(M1) * xs.shi);
+        return fmaf(d, pos, -dmin * neg);
     }
 };
 
@@ -1120,6 +1231,7 @@ hipError_t launch_pair_b(nt_qtype tb, const GemvArgs &a, const GemvArgs &c, hipS
     case NT_Q8_0: return launch_pair_inst<TrA, F80>(a, c, st);
     case NT_Q4_0: return launch_pair_inst<TrA, F40>(a, c, st);
     case NT_Q4_K: return launch_pair_inst<TrA, F4K>(a, c, st);
+    case NT_Q5_K: return launch_pair_inst<TrA, F5K>(a, c, st);
     case NT_Q6_K: return launch_pair_inst<TrA, F6K>(a, c, st);
     default: return hipErrorInvalidValue;
     }
@@ -1140,6 +1252,7 @@ hipError_t launch_gemv_pair(nt_qtype ta, int na, const void *const *Wa, const in
     case NT_Q8_0: return launch_pair_b<F80>(tb, a, c, st);
     case NT_Q4_0: return launch_pair_b<F40>(tb, a, c, st);
     case NT_Q4_K: return launch_pair_b<F4K>(tb, a, c, st);
+    case NT_Q5_K: return launch_pair_b<F5K>(tb, a, c, st);
     case NT_Q6_K: return launch_pair_b<F6K>(tb, a, c, st);
     default: return hipErrorInvalidValue;
     }
@@ -1164,6 +1277,7 @@ void gemv_launch_info(nt_qtype t, int64_t rows, int64_t cols, int32_t info[4]) {
         case NT_Q8_0: s = lds_shape<F80>(rows, cols, false, false, vec16); break;
         case NT_Q4_0: s = lds_shape<F40>(rows, cols, false, false, vec16); break;
         case NT_Q4_K: s = lds_shape<F4K>(rows, cols, false, false, vec16); break;
+        case NT_Q5_K: s = lds_shape<F5K>(rows, cols, false, false, vec16); break;
         default: s = lds_shape<F6K>(rows, cols, false, false, vec16); break;
         }
         info[0] = 1 + (vec16 ? 1 : 0);   // 2: 16-byte copies, 1: 4-byte
@@ -1188,6 +1302,7 @@ hipError_t launch_gemv_fused(nt_qtype t, const GemvArgs &a, bool pairs, hipStrea
     case NT_Q8_0: return launch_lds<F80, true>(a, pairs, vec16, st);
     case NT_Q4_0: return launch_lds<F40, true>(a, pairs, vec16, st);
     case NT_Q4_K: return launch_lds<F4K, false>(a, pairs, true, st);
+    case NT_Q5_K: return launch_lds<F5K, false>(a, pairs, true, st);
     case NT_Q6_K: return launch_lds<F6K, true>(a, pairs, vec16, st);
     default: return hipErrorInvalidValue;
     }
@@ -1229,6 +1344,7 @@ hipError_t launch_gemv(nt_qtype t, const void *W, const float *x, float *y, int6
     case NT_Q8_0: return launch_generic<Q80>(W, x, y, rows, cols, accumulate, st);
     case NT_Q4_0: return launch_generic<Q40>(W, x, y, rows, cols, accumulate, st);
     case NT_Q4_K: return launch_generic<Q4K>(W, x, y, rows, cols, accumulate, st);
+    case NT_Q5_K: return launch_generic<Q5K>(W, x, y, rows, cols, accumulate, st);
     case NT_Q6_K: return launch_generic<Q6K>(W, x, y, rows, cols, accumulate, st);
     default: return hipErrorInvalidValue;
     }

@@ -249,6 +249,16 @@ __device__ float decode_one(const uint8_t *row, int64_t e) {
         const uint32_t byte = blk[16 + 32 * (j >> 1) + (i & 31)];
         const int q = (j & 1) ? (byte >> 4) : (byte & 15);
         return (h2f(rd16(blk)) * float(S)) * float(q) - h2f(rd16(blk + 2)) * float(M);
+    } else if constexpr (T == NT_Q5_K) {
+        const uint8_t *blk = row + (e / 256) * 176;
+        const int i = int(e % 256), j = i >> 5, l = i & 31;
+        const uint8_t *b = blk + 4;
+        int S, M;
+        if (j < 4) { S = b[j] & 63; M = b[j + 4] & 63; }
+        else { S = (b[j + 4] & 15) | ((b[j - 4] >> 6) << 4); M = (b[j + 4] >> 4) | ((b[j] >> 6) << 4); }
+        const uint32_t byte = blk[48 + 32 * (j >> 1) + l];
+        const int q = int((j & 1) ? (byte >> 4) : (byte & 15)) | (((blk[16 + l] >> j) & 1) << 4);
+        return (h2f(rd16(blk)) * float(S)) * float(q) - h2f(rd16(blk + 2)) * float(M);
     } else {
         const uint8_t *blk = row + (e / 256) * 210;
         const int i = int(e % 256), h = i >> 7, r = i & 127, k = r >> 5, l = r & 31;
@@ -270,7 +280,7 @@ __global__ void __launch_bounds__(256) embed_kernel(const uint8_t *__restrict__ 
         return;
     }
     constexpr int BE = (T == NT_Q8_0 || T == NT_Q4_0) ? 32 : 256;
-    constexpr int BB = T == NT_Q8_0 ? 34 : T == NT_Q4_0 ? 18 : T == NT_Q4_K ? 144 : 210;
+    constexpr int BB = T == NT_Q8_0 ? 34 : T == NT_Q4_0 ? 18 : T == NT_Q4_K ? 144 : T == NT_Q5_K ? 176 : 210;
     const uint8_t *row = table + int64_t(tok) * (hidden / BE) * BB;
     out[e] = decode_one<T>(row, e);
 }
@@ -325,6 +335,7 @@ hipError_t launch_embed(nt_qtype t, const void *table, int64_t vocab, int64_t hi
     case NT_Q8_0: embed_kernel<NT_Q8_0><<<grid, 256, 0, st>>>(tb, vocab, hidden, d_token, out); break;
     case NT_Q4_0: embed_kernel<NT_Q4_0><<<grid, 256, 0, st>>>(tb, vocab, hidden, d_token, out); break;
     case NT_Q4_K: embed_kernel<NT_Q4_K><<<grid, 256, 0, st>>>(tb, vocab, hidden, d_token, out); break;
+    case NT_Q5_K: embed_kernel<NT_Q5_K><<<grid, 256, 0, st>>>(tb, vocab, hidden, d_token, out); break;
     case NT_Q6_K: embed_kernel<NT_Q6_K><<<grid, 256, 0, st>>>(tb, vocab, hidden, d_token, out); break;
     default: return hipErrorInvalidValue;
     }

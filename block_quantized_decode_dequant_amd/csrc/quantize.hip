@@ -11,6 +11,8 @@
 //         dmin = fp16_up(max m_j / 63); M_j = ceil(m_j/dmin); o_j = dmin*M_j;
 //         s_j = (max(max x, -o_j) + o_j)/15; d = fp16_up(max s_j / 63);
 //         S_j = ceil(s_j/d); q = clamp(round((x + o_j)/(d*S_j)), 0, 15)
+//   Q5_K  as Q4_K with 31 in place of 15 (q in [0, 31]: low 4 bits in qs, the
+//         fifth in qh)
 //   Q6_K  per 16-value sub-block j: s_j = max|x|/31; d = fp16_up(max s_j/127);
 //         S_j = ceil(s_j/d); q = clamp(round(x/(d*S_j)), -32, 31) + 32
 // fp16_rne rounds to nearest (ties to even); fp16_up gives the smallest fp16
@@ -78,8 +80,11 @@ __device__ void enc_q4_0(const float *x, uint8_t *blk) {
     }
 }
 
-__device__ void enc_q4_k(const float *x, uint8_t *blk) {
-    double m[8], o[8], s[8], mmax = 0.0, smax = 0.0;
+// Q4_K and Q5_K header: offsets o_j, steps d*S_j and the packed d, dmin and
+// scale bytes in blk[0..16); codes take LEVELS + 1 values (15 or 31).
+template <int LEVELS>
+__device__ void enc_kq_header(const float *x, uint8_t *blk, double o[8], double step[8]) {
+    double m[8], s[8], mmax = 0.0, smax = 0.0;
     int S[8], M[8];
     for (int j = 0; j < 8; ++j) {
         double mn = 0.0;
@@ -96,13 +101,15 @@ __device__ void enc_q4_k(const float *x, uint8_t *blk) {
     for (int j = 0; j < 8; ++j) {
         double mx = -o[j];
         for (int i = 0; i < 32; ++i) mx = fmax(mx, double(x[32 * j + i]));
-        s[j] = (mx + o[j]) / 15.0;
+        s[j] = (mx + o[j]) / double(LEVELS);
         smax = fmax(smax, s[j]);
     }
     const uint32_t dh = f16_encode_pos<true>(smax / 63.0);
     const double d = f16_value(dh);
-    for (int j = 0; j < 8; ++j) S[j] = d == 0.0 ? 0 : int(ceil(s[j] / d));
-
+    for (int j = 0; j < 8; ++j) {
+        S[j] = d == 0.0 ? 0 : int(ceil(s[j] / d));
+        step[j] = d * double(S[j]);
+    }
     put16(blk, dh);
     put16(blk + 2, dminh);
     for (int j = 0; j < 4; ++j) {
@@ -110,16 +117,37 @@ __device__ void enc_q4_k(const float *x, uint8_t *blk) {
         blk[8 + j] = uint8_t((M[j] & 63) | ((M[j + 4] >> 4) << 6));
         blk[12 + j] = uint8_t((S[j + 4] & 15) | ((M[j + 4] & 15) << 4));
     }
-    for (int p = 0; p < 4; ++p) {          // byte 32p + i: sub-block 2p low, 2p+1 high
-        const double st0 = d * double(S[2 * p]), st1 = d * double(S[2 * p + 1]);
+}
+
+// code of value v in a sub-block with offset o and step st: round((v + o)/st) in [0, LEVELS]
+template <int LEVELS>
+__device__ __forceinline__ int enc_kq_code(float v, double o, double st) {
+    const double q = st == 0.0 ? 0.0 : round((double(v) + o) / st);
+    return int(fmin(double(LEVELS), fmax(0.0, q)));
+}
+
+__device__ void enc_q4_k(const float *x, uint8_t *blk) {
+    double o[8], step[8];
+    enc_kq_header<15>(x, blk, o, step);
+    for (int p = 0; p < 4; ++p)            // byte 32p + i: sub-block 2p low, 2p+1 high
         for (int i = 0; i < 32; ++i) {
-            double q0 = st0 == 0.0 ? 0.0 : round((double(x[64 * p + i]) + o[2 * p]) / st0);
-            double q1 = st1 == 0.0 ? 0.0 : round((double(x[64 * p + 32 + i]) + o[2 * p + 1]) / st1);
-            const int lo = int(fmin(15.0, fmax(0.0, q0)));
-            const int hi = int(fmin(15.0, fmax(0.0, q1)));
+            const int lo = enc_kq_code<15>(x[64 * p + i], o[2 * p], step[2 * p]);
+            const int hi = enc_kq_code<15>(x[64 * p + 32 + i], o[2 * p + 1], step[2 * p + 1]);
             blk[16 + 32 * p + i] = uint8_t(lo | (hi << 4));
         }
-    }
+}
+
+__device__ void enc_q5_k(const float *x, uint8_t *blk) {
+    double o[8], step[8];
+    enc_kq_header<31>(x, blk, o, step);
+    for (int i = 0; i < 32; ++i) blk[16 + i] = 0;   // qh: bit j of qh[i] = fifth bit of value 32j + i
+    for (int p = 0; p < 4; ++p)
+        for (int i = 0; i < 32; ++i) {
+            const int lo = enc_kq_code<31>(x[64 * p + i], o[2 * p], step[2 * p]);
+            const int hi = enc_kq_code<31>(x[64 * p + 32 + i], o[2 * p + 1], step[2 * p + 1]);
+            blk[48 + 32 * p + i] = uint8_t((lo & 15) | ((hi & 15) << 4));
+            blk[16 + i] |= uint8_t(((lo >> 4) << (2 * p)) | ((hi >> 4) << (2 * p + 1)));
+        }
 }
 
 __device__ void enc_q6_k(const float *x, uint8_t *blk) {
@@ -159,7 +187,7 @@ template <int T>
 __global__ void __launch_bounds__(128) quantize_kernel(const float *__restrict__ x, uint8_t *__restrict__ out,
                                                       int64_t nblocks) {
     constexpr int BE = (T == NT_Q8_0 || T == NT_Q4_0) ? 32 : 256;
-    constexpr int BB = T == NT_Q8_0 ? 34 : T == NT_Q4_0 ? 18 : T == NT_Q4_K ? 144 : 210;
+    constexpr int BB = T == NT_Q8_0 ? 34 : T == NT_Q4_0 ? 18 : T == NT_Q4_K ? 144 : T == NT_Q5_K ? 176 : 210;
     const int64_t stride = int64_t(gridDim.x) * blockDim.x;
     for (int64_t b = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; b < nblocks; b += stride) {
         const float *xb = x + b * BE;
@@ -167,6 +195,7 @@ __global__ void __launch_bounds__(128) quantize_kernel(const float *__restrict__
         if constexpr (T == NT_Q8_0) enc_q8_0(xb, ob);
         else if constexpr (T == NT_Q4_0) enc_q4_0(xb, ob);
         else if constexpr (T == NT_Q4_K) enc_q4_k(xb, ob);
+        else if constexpr (T == NT_Q5_K) enc_q5_k(xb, ob);
         else enc_q6_k(xb, ob);
     }
 }
@@ -183,6 +212,7 @@ hipError_t launch_quantize(nt_qtype t, const float *x, void *blocks, int64_t n, 
     case NT_Q8_0: quantize_kernel<NT_Q8_0><<<grid, threads, 0, st>>>(x, o, nb); break;
     case NT_Q4_0: quantize_kernel<NT_Q4_0><<<grid, threads, 0, st>>>(x, o, nb); break;
     case NT_Q4_K: quantize_kernel<NT_Q4_K><<<grid, threads, 0, st>>>(x, o, nb); break;
+    case NT_Q5_K: quantize_kernel<NT_Q5_K><<<grid, threads, 0, st>>>(x, o, nb); break;
     case NT_Q6_K: quantize_kernel<NT_Q6_K><<<grid, threads, 0, st>>>(x, o, nb); break;
     default: return hipErrorInvalidValue;
     }

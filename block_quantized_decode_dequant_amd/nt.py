@@ -14,10 +14,10 @@ import os
 from . import build as _build
 
 NT_OK, NT_EINVAL, NT_ESHAPE, NT_EALIGN, NT_ENOMEM, NT_EHIP, NT_ESTATE, NT_ENODEV = range(8)
-F32, F16, Q4_0, Q8_0, Q4_K, Q6_K = 0, 1, 2, 8, 12, 14
-QTYPES = {"f32": F32, "f16": F16, "q4_0": Q4_0, "q8_0": Q8_0, "q4_k": Q4_K, "q6_k": Q6_K}
-BLOCK_ELEMS = {Q8_0: 32, Q4_0: 32, Q4_K: 256, Q6_K: 256}
-BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_K: 144, Q6_K: 210}
+F32, F16, Q4_0, Q8_0, Q4_K, Q5_K, Q6_K = 0, 1, 2, 8, 12, 13, 14
+QTYPES = {"f32": F32, "f16": F16, "q4_0": Q4_0, "q8_0": Q8_0, "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K}
+BLOCK_ELEMS = {Q8_0: 32, Q4_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_K: 144, Q5_K: 176, Q6_K: 210}
 
 
 class AttnDesc(C.Structure):
@@ -80,7 +80,7 @@ def _declare(L):
         "nt_attn_workspace_bytes": (C.c_size_t, [C.POINTER(AttnDesc)]),
         "nt_attn_decode": (st, [C.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]),
     }
-    for t in ("q8_0", "q4_0", "q4_k", "q6_k"):
+    for t in ("q8_0", "q4_0", "q4_k", "q5_k", "q6_k"):
         sig[f"nt_dequant_{t}"] = (st, [vp, vp, i64, vp])
         sig[f"nt_gemv_{t}"] = (st, [vp, vp, vp, i64, i64, i32, vp])
     for name, (res, args) in sig.items():
@@ -147,6 +147,7 @@ def nt_dequant(qtype: int, blocks, out, n: int, stream=None):
 def nt_dequant_q8_0(blocks, out, n, stream=None): nt_dequant(Q8_0, blocks, out, n, stream)
 def nt_dequant_q4_0(blocks, out, n, stream=None): nt_dequant(Q4_0, blocks, out, n, stream)
 def nt_dequant_q4_k(blocks, out, n, stream=None): nt_dequant(Q4_K, blocks, out, n, stream)
+def nt_dequant_q5_k(blocks, out, n, stream=None): nt_dequant(Q5_K, blocks, out, n, stream)
 def nt_dequant_q6_k(blocks, out, n, stream=None): nt_dequant(Q6_K, blocks, out, n, stream)
 
 
@@ -161,6 +162,7 @@ def nt_gemv(qtype: int, W, x, y, rows: int, cols: int, accumulate: bool = False,
 def nt_gemv_q8_0(W, x, y, rows, cols, accumulate=False, stream=None): nt_gemv(Q8_0, W, x, y, rows, cols, accumulate, stream)
 def nt_gemv_q4_0(W, x, y, rows, cols, accumulate=False, stream=None): nt_gemv(Q4_0, W, x, y, rows, cols, accumulate, stream)
 def nt_gemv_q4_k(W, x, y, rows, cols, accumulate=False, stream=None): nt_gemv(Q4_K, W, x, y, rows, cols, accumulate, stream)
+def nt_gemv_q5_k(W, x, y, rows, cols, accumulate=False, stream=None): nt_gemv(Q5_K, W, x, y, rows, cols, accumulate, stream)
 def nt_gemv_q6_k(W, x, y, rows, cols, accumulate=False, stream=None): nt_gemv(Q6_K, W, x, y, rows, cols, accumulate, stream)
 
 

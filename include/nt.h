@@ -64,12 +64,16 @@ typedef enum {
  *   NT_Q4_K : 144-byte super-blocks of 256 values: fp16 d, fp16 dmin, 12 bytes
  *             of packed 6-bit sub-block scales S_j and mins M_j (j = 0..7),
  *             128 bytes of 4-bit codes; x = (d*S_j)*q - dmin*M_j
+ *   NT_Q5_K : 176-byte super-blocks of 256 values: fp16 d, fp16 dmin, the
+ *             same 12 scale/min bytes as Q4_K, 32 bytes qh, 128 bytes of
+ *             low 4 bits laid out as in Q4_K; bit j of qh[l] is the fifth bit
+ *             of value 32j + l, q in [0, 31]; x = (d*S_j)*q - dmin*M_j
  *   NT_Q6_K : 210-byte super-blocks of 256 values: 128 bytes of low 4 bits,
  *             64 bytes of high 2 bits, 16 int8 sub-block scales, fp16 d;
  *             x = d*scale[e/16]*(q-32)
  * (Layouts: the public GGUF block definitions; the write-up's "Overview"
  * names the formats.) */
-typedef enum { NT_F32 = 0, NT_F16 = 1, NT_Q4_0 = 2, NT_Q8_0 = 8, NT_Q4_K = 12, NT_Q6_K = 14 } nt_qtype;
+typedef enum { NT_F32 = 0, NT_F16 = 1, NT_Q4_0 = 2, NT_Q8_0 = 8, NT_Q4_K = 12, NT_Q5_K = 13, NT_Q6_K = 14 } nt_qtype;
 
 typedef void *nt_stream; /* hipStream_t */
 
@@ -92,6 +96,7 @@ int64_t nt_qtype_row_bytes(nt_qtype t, int64_t cols);
 nt_status nt_dequant_q8_0(const void *blocks, float *out, int64_t n, nt_stream stream);
 nt_status nt_dequant_q4_0(const void *blocks, float *out, int64_t n, nt_stream stream);
 nt_status nt_dequant_q4_k(const void *blocks, float *out, int64_t n, nt_stream stream);
+nt_status nt_dequant_q5_k(const void *blocks, float *out, int64_t n, nt_stream stream);
 nt_status nt_dequant_q6_k(const void *blocks, float *out, int64_t n, nt_stream stream);
 nt_status nt_dequant(nt_qtype t, const void *blocks, float *out, int64_t n, nt_stream stream);
 
@@ -108,6 +113,8 @@ nt_status nt_gemv_q8_0(const void *W, const float *x, float *y, int64_t rows, in
 nt_status nt_gemv_q4_0(const void *W, const float *x, float *y, int64_t rows, int64_t cols,
                        int accumulate, nt_stream stream);
 nt_status nt_gemv_q4_k(const void *W, const float *x, float *y, int64_t rows, int64_t cols,
+                       int accumulate, nt_stream stream);
+nt_status nt_gemv_q5_k(const void *W, const float *x, float *y, int64_t rows, int64_t cols,
                        int accumulate, nt_stream stream);
 nt_status nt_gemv_q6_k(const void *W, const float *x, float *y, int64_t rows, int64_t cols,
                        int accumulate, nt_stream stream);
@@ -301,6 +308,7 @@ nt_status nt_stream_stats_get(nt_model *m, nt_stream_stats *out);
  *   Q4_K: per 32-value sub-block, m = -min(0, min x), dmin = fp16_up(max m/63),
  *         M = ceil(m/dmin), o = dmin*M, s = (max(max x, -o) + o)/15,
  *         d = fp16_up(max s/63), S = ceil(s/d), q = clamp(round((x+o)/(d*S)), 0, 15)
+ *   Q5_K: as Q4_K with 31 in place of 15 (q in [0, 31])
  *   Q6_K: per 16-value sub-block, s = max|x|/31, d = fp16_up(max s/127),
  *         S = ceil(s/d), q = clamp(round(x/(d*S)), -32, 31) + 32
  * (fp16_up(v) = the smallest fp16 >= v.)  The pages read GGUF files encoded

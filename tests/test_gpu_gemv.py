@@ -22,8 +22,8 @@ from .test_oracle_formats import load_golden
 
 pytestmark = pytest.mark.gpu
 
-TYPES = [O.Q8_0, O.Q4_0, O.Q4_K, O.Q6_K]
-TID = ["q8_0", "q4_0", "q4_k", "q6_k"]
+TYPES = [O.Q8_0, O.Q4_0, O.Q4_K, O.Q5_K, O.Q6_K]
+TID = ["q8_0", "q4_0", "q4_k", "q5_k", "q6_k"]
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
@@ -180,7 +180,8 @@ def test_gemv_word_aligned_rows_and_deep_ring(t, rows, cols):
 # 2048 / 4096 columns: one column slice (shared activation area, row groups);
 # 8192: two slices (shared area with RMSNorm, per-wave staging without);
 # 2112 / 1536: rows only word-aligned (4-byte copies, per-wave staging)
-FUSED_COLS = {O.Q8_0: [2048, 2112], O.Q4_0: [2048, 2112], O.Q4_K: [2048, 4096, 8192], O.Q6_K: [2048, 1536, 8192]}
+FUSED_COLS = {O.Q8_0: [2048, 2112], O.Q4_0: [2048, 2112], O.Q4_K: [2048, 4096, 8192], O.Q5_K: [2048, 8192],
+              O.Q6_K: [2048, 1536, 8192]}
 
 
 def _norm_inputs(cols, seed):
@@ -230,7 +231,8 @@ def test_gemv_swiglu_parity(t):
 SHARED_CASES = [(O.Q8_0, 7500, 4096, False), (O.Q8_0, 3, 4096, True), (O.Q4_0, 9000, 2048, True),
                 (O.Q4_K, 5000, 8192, True), (O.Q6_K, 7, 8192, True), (O.Q6_K, 10500, 4096, False),
                 # wider rows whose activation area still fits beside one row group
-                (O.Q8_0, 600, 14336, False), (O.Q4_K, 300, 16384, True), (O.Q6_K, 200, 12288, False)]
+                (O.Q8_0, 600, 14336, False), (O.Q4_K, 300, 16384, True), (O.Q6_K, 200, 12288, False),
+                (O.Q5_K, 5000, 8192, True), (O.Q5_K, 9, 4096, False), (O.Q5_K, 250, 12288, True)]
 
 
 @pytest.mark.parametrize("t,rows,cols,norm", SHARED_CASES,

@@ -82,8 +82,8 @@ def greedy_parity(cfg, w, n_pos, first_token, n_steps, graph=True):
     return near_ties
 
 
-@pytest.mark.parametrize("wtype", [O.Q8_0, O.Q4_0, O.Q4_K, O.Q6_K, "mix"],
-                         ids=["q8_0", "q4_0", "q4_k", "q6_k", "mix"])
+@pytest.mark.parametrize("wtype", [O.Q8_0, O.Q4_0, O.Q4_K, O.Q5_K, O.Q6_K, "mix"],
+                         ids=["q8_0", "q4_0", "q4_k", "q5_k", "q6_k", "mix"])
 def test_tiny_model_greedy_parity(wtype):
     cfg = tiny_config()
     w = build_oracle_model(cfg, seed=11, wtype=wtype)

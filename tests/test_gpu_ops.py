@@ -85,7 +85,7 @@ def test_argmax_ties_and_edges():
     assert int(host(out)[0]) == 0
 
 
-@pytest.mark.parametrize("t", [O.Q8_0, O.Q4_0, O.Q4_K, O.Q6_K], ids=["q8_0", "q4_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("t", [O.Q8_0, O.Q4_0, O.Q4_K, O.Q5_K, O.Q6_K], ids=["q8_0", "q4_0", "q4_k", "q5_k", "q6_k"])
 def test_embed_row_bit_exact(t):
     vocab, hidden = 300, 1024
     table = O.quantize(t, synth.normal_f32(10, 550 + t, vocab * hidden, std=0.02))
