@@ -576,7 +576,7 @@ struct F4K {
 // fifth bits of those values.  Codes are assembled one per byte (nibble |
 // bit << 4) and converted with byte-to-float conversions.
 struct F5K {
-    static constexpr int kSlice = 16 * 176, kStagesShared = 3, kStagesWide = 3;
+    static constexpr int kSlice = 16 * 176, kStagesShared = 2, kStagesWide = 3;
     struct L { uint32_t off_h, off_q, p; };
     using X = F4K::X;
     struct Raw { u32x4 h, qh0, qh1, q0, q1; };
