@@ -13,7 +13,8 @@ kernel with the most time in the timed region gives the `roofline` object.
 The CPU baseline times the oracle (plain fp64 C, test-side code) on a bounded
 sample of the same workload: the first rows of each matrix.
 
-Decode measurements ride along in the same JSON line ("decode"): the
+Q5_K GEMV at the two Llama-70B FFN shapes rides along ("q5_k_gemv"), timed like
+the sweep's per-kernel times.  Decode measurements ride along in the same JSON line ("decode"): the
 Llama-3-8B-shaped Q8_0 model (128 greedy tokens from position 1024), the
 Llama-70B-shaped Q4_K/Q6_K model (64 tokens from 4096), each replayed from a
 captured HIP graph, and the 70B all-Q6_K model with 24 GiB of layers resident
@@ -232,6 +233,54 @@ def run_gpu(args):
                 copies=copies, step_bytes=step_bytes, queued_step_ms=span_ms)
 
 
+def q5_k_gemv(steps):
+    """Q5_K GEMV at the two Llama-70B FFN projection shapes (28672x8192 and
+    8192x28672), measured like the sweep's per-kernel times: weights encoded
+    on the device from the sweep's N(0, 0.02) values, rotated copies (>= 1 GiB
+    apart), one HIP graph of `steps` back-to-back launches, events around its
+    replay.  Reported beside the sweep, not part of `value`."""
+    import torch
+
+    from block_quantized_decode_dequant_amd import nt, synth, workloads
+
+    dev = torch.device("cuda:0")
+    out = []
+    for si in (2, 3):
+        rows, cols = workloads.KQ_SHAPES[si]
+        w32 = torch.from_numpy(synth.normal_f32(workloads.SEED, workloads.kq_w_stream(si), rows * cols,
+                                                std=0.02)).to(dev)
+        x = torch.from_numpy(synth.activation(workloads.SEED, workloads.kq_x_stream(si), cols)).to(dev)
+        nbytes = rows * nt.row_bytes(nt.Q5_K, cols)
+        base = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        nt.nt_quantize(nt.Q5_K, w32, base, rows * cols)
+        del w32
+        copies = max(2, -(-(1 << 30) // nbytes) + 1)
+        Ws = [base] + [base.clone() for _ in range(copies - 1)]
+        y = torch.empty(rows, dtype=torch.float32, device=dev)
+        side = torch.cuda.Stream()
+        with torch.cuda.stream(side):
+            nt.nt_gemv(nt.Q5_K, Ws[0], x, y, rows, cols)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for k in range(steps):
+                    nt.nt_gemv(nt.Q5_K, Ws[k % copies], x, y, rows, cols)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(side):
+            g.replay()
+            a.record(side)
+            g.replay()
+            b.record(side)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / steps
+        alg = nbytes + 4 * cols + 4 * rows
+        out.append({"rows": rows, "cols": cols, "bytes": alg, "us": round(us, 3),
+                    "gbs": round(alg / (us * 1e-6) / 1e9, 1), "frac": round(alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)})
+        del g, Ws, base
+        torch.cuda.empty_cache()
+    return out
+
+
 def time_decode(model, shape, n_tokens, warmup=8):
     import torch
     dev = torch.device("cuda:0")
@@ -427,6 +476,7 @@ def main():
         "queued_launch_ms_per_step": round(g["queued_step_ms"], 4),
         "roofline": g["roofline"],
         "detail": g["detail"],
+        "q5_k_gemv": q5_k_gemv(args.steps),
     }
     if args.decode != "none":
         dec = {}
