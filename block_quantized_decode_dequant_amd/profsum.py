@@ -24,7 +24,7 @@ import re
 HERE = os.path.dirname(os.path.abspath(__file__))
 GEMV_SRC = os.path.join(HERE, "csrc", "gemv.hip")
 
-FMT = {"F80": "q8_0", "F40": "q4_0", "F4K": "q4_k", "F6K": "q6_k"}
+FMT = {"F80": "q8_0", "F40": "q4_0", "F4K": "q4_k", "F5K": "q5_k", "F6K": "q6_k"}
 
 
 def kernel_key(name: str):
