@@ -1122,9 +1122,12 @@ LdsShape lds_shape(int64_t items, int64_t cols, bool pairs, bool norm, bool vec1
     s.nw = int((units + 63) / 64);
     const size_t area = size_t(s.nw) * 16384 * (norm ? 2 : 1);
     // rows of up to two column slices (8192 columns) use the shared layout,
-    // and so do wider rows whose activation area fits beside one row group
+    // and so do wider rows whose activation area fits beside two row groups
+    // (which then share one copy of it; with a single group the per-wave
+    // layout and its deeper ring measured faster: Q5_K 8192x28672 35.4 vs
+    // 36.3 us)
     const size_t ring_sh = size_t(Tr::kStagesShared) * Tr::kSlice;
-    const bool fits_one = area + size_t(s.nw) * (ring_sh + kMaxRowsPerWG * 4 + 4 + 256) <= size_t(di.lds_per_cu);
+    const bool fits_one = area + 2 * size_t(s.nw) * (ring_sh + kMaxRowsPerWG * 4 + 4 + 256) <= size_t(di.lds_per_cu);
     static const int wide_env = env_int("NT_GEMV_SHARED_WIDE", 1);
     bool shared = vec16 && (cols <= 8192 || (wide_env > 0 && fits_one));
     if (shared_env >= 0) shared = shared && shared_env > 0;
