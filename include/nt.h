@@ -264,7 +264,16 @@ void      nt_model_destroy(nt_model *m);
  * arguments change).  Steps on the NULL stream always run eagerly. */
 nt_status nt_model_set_graph(nt_model *m, int enable);
 /* Enqueues one decode step on `stream`.  d_token, d_pos: device int32
- * (d_next may equal d_token); logits: device fp32[vocab]. */
+ * (d_next may equal d_token); logits: device fp32[vocab].  With token =
+ * *d_token and pos = *d_pos read on the device: embed row `token`, run every
+ * layer (k and v of this token stored at slot pos of each layer's cache,
+ * attention over slots [0, pos]), the output RMSNorm and head into logits,
+ * then *d_next = argmax(logits) (lowest index on ties, a NaN never wins, 0
+ * when every logit is NaN) and *d_pos = pos + 1.  Out-of-range values live on
+ * the device, so no status reports them: a token outside [0, vocab) gives
+ * NaN logits and token 0 (slot pos then holds NaN k and v); a pos outside
+ * [0, ctx_cap) gives NaN logits and token 0 and writes nothing to the cache.
+ * In both cases the position still advances. */
 nt_status nt_decode_step(nt_model *m, const int32_t *d_token, int32_t *d_pos, float *logits,
                          int32_t *d_next, nt_stream stream);
 

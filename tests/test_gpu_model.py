@@ -205,3 +205,52 @@ def test_llama70b_layer_shape_mixed_kquants():
     cfg = O.Config(1, 8192, 64, 8, 128, 28672, 2048, 4160, 1e-5, 500000.0)
     w = build_oracle_model(cfg, seed=31, wtype="mix", gains="one")
     greedy_parity(cfg, w, n_pos=4096, first_token=1, n_steps=3)
+
+
+def test_step_past_the_cache_and_with_a_bad_token():
+    """Out-of-range device values: a step at pos == ctx_cap gives NaN logits
+    and token 0, advances the position and leaves both caches (and a guard
+    region after them) untouched; a token outside [0, vocab) gives NaN logits
+    and token 0 and writes nothing past the caches."""
+    cfg = tiny_config(n_layers=2, ctx_cap=16)
+    w = build_oracle_model(cfg, seed=41, wtype=O.Q4_K)
+    kk, vv = kv_prefix(cfg, 7, cfg.ctx_cap)
+    dev = device()
+    n, guard = kk.size, 4096
+    # the caches, each followed by a guard region that must keep its pattern
+    kcg = torch.full((n + guard,), 0x1234, dtype=torch.int16, device=dev)
+    vcg = torch.full((n + guard,), 0x4321, dtype=torch.int16, device=dev)
+    kcg[:n] = torch.from_numpy(kk.reshape(-1).view(np.int16).copy()).to(dev)
+    vcg[:n] = torch.from_numpy(vv.reshape(-1).view(np.int16).copy()).to(dev)
+    ncfg = nt.model_config(cfg.n_layers, cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn,
+                           cfg.vocab, cfg.ctx_cap, cfg.rms_eps, cfg.rope_theta)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    weights = {
+        "tok_embd": _dev_qt(w.tok_embd), "output": _dev_qt(w.output), "output_norm": f32(w.output_norm),
+        "layers": [{"attn_norm": f32(L.attn_norm), "ffn_norm": f32(L.ffn_norm),
+                    **{k: _dev_qt(getattr(L, k)) for k in nt.Model.MATS}} for L in w.layers],
+    }
+    ws = torch.empty(nt.nt_model_workspace_bytes(ncfg), dtype=torch.uint8, device=dev)
+    model = nt.Model(ncfg, weights, kcg[:n], vcg[:n], ws)
+    before_k, before_v = kcg.clone(), vcg.clone()
+    logits = torch.zeros(cfg.vocab, dtype=torch.float32, device=dev)
+    d_tok = torch.tensor([3], dtype=torch.int32, device=dev)
+    d_pos = torch.tensor([cfg.ctx_cap], dtype=torch.int32, device=dev)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        model.step(d_tok, d_pos, logits, d_tok)
+    torch.cuda.synchronize()
+    assert np.all(np.isnan(host(logits)))
+    assert int(host(d_tok)[0]) == 0 and int(host(d_pos)[0]) == cfg.ctx_cap + 1
+    assert torch.equal(kcg, before_k) and torch.equal(vcg, before_v)
+    # a token outside [0, vocab) at a valid position
+    d_tok.fill_(cfg.vocab)
+    d_pos.fill_(5)
+    with torch.cuda.stream(side):
+        model.step(d_tok, d_pos, logits, d_tok)
+    torch.cuda.synchronize()
+    assert np.all(np.isnan(host(logits)))
+    assert int(host(d_tok)[0]) == 0 and int(host(d_pos)[0]) == 6
+    assert torch.equal(kcg[n:], before_k[n:]) and torch.equal(vcg[n:], before_v[n:])
+    model.close()
