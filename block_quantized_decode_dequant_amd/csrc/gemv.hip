@@ -23,7 +23,9 @@
 //    per 2048-column slice) combine their partial sums through LDS in a fixed
 //    order.  No atomics: results are deterministic.
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include "device_util.h"
@@ -1075,10 +1077,19 @@ struct DevInfo {
     int lds_per_cu = 0;
 };
 
-DevInfo dev_info() {
-    static DevInfo cache[64];
+int current_device() {
     int d = 0;
     if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) d = 0;
+    return d;
+}
+
+// Filled once per device, under a lock (launches may come from several
+// threads).
+DevInfo dev_info() {
+    static std::mutex mu;
+    static DevInfo cache[64];
+    const int d = current_device();
+    std::lock_guard<std::mutex> lock(mu);
     DevInfo &di = cache[d];
     if (di.cus == 0) {
         int cus = 0, lds = 0;
@@ -1090,6 +1101,17 @@ DevInfo dev_info() {
         di.cus = cus;
     }
     return di;
+}
+
+// Lets kernel `fn` use all of a CU's LDS as dynamic LDS: set once per device
+// (a second, concurrent setting is harmless).  A launch that still exceeds
+// the limit fails and is reported by the launch check.
+void allow_full_lds(const void *fn, std::atomic<uint64_t> &done) {
+    const int d = current_device();
+    if ((done.load(std::memory_order_acquire) >> d) & 1) return;
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, dev_info().lds_per_cu) != hipSuccess)
+        (void)hipGetLastError();                // not left for the launch check to report
+    done.fetch_or(uint64_t(1) << d, std::memory_order_release);
 }
 
 struct LdsShape {
@@ -1163,10 +1185,8 @@ template <class Tr, int VEC, bool NORM, bool SHARED>
 hipError_t launch_lds_inst(const GemvArgs &a, const LdsShape &s, hipStream_t st) {
     // allow the large dynamic LDS areas (a launch that still exceeds the
     // limit fails and is reported by the launch check below)
-    static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_lds<Tr, VEC, NORM, SHARED>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, dev_info().lds_per_cu);
-    (void)attr;
+    static std::atomic<uint64_t> done{0};          // devices this kernel is set up on
+    allow_full_lds(reinterpret_cast<const void *>(&gemv_lds<Tr, VEC, NORM, SHARED>), done);
     gemv_lds<Tr, VEC, NORM, SHARED><<<dim3(unsigned(s.grid)), dim3(unsigned(64 * s.nw * s.groups)), s.lds, st>>>(a);
     return hipGetLastError();
 }
@@ -1219,10 +1239,8 @@ hipError_t launch_pair_inst(const GemvArgs &a, const GemvArgs &c, hipStream_t st
     int64_t gc = std::min<int64_t>(std::max<int64_t>(int64_t(di.cus) - ga, min_c), c.rows);
     if (ga < 1) ga = 1;
     if (gc < 1) gc = 1;
-    static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_pair<TrA, TrB, true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, dev_info().lds_per_cu);
-    (void)attr;
+    static std::atomic<uint64_t> done{0};
+    allow_full_lds(reinterpret_cast<const void *>(&gemv_pair<TrA, TrB, true>), done);
     gemv_pair<TrA, TrB, true><<<dim3(unsigned(ga + gc)), dim3(unsigned(64 * nw * groups)), lds, st>>>(a, c, int(ga));
     return hipGetLastError();
     }

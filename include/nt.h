@@ -30,8 +30,9 @@
  *    readable up to the next multiple of 4 bytes past its last block (kernels
  *    read whole aligned 32-bit words; every allocator that rounds sizes to 4
  *    bytes or more, including hipMalloc and torch, satisfies this).
- *  - Calls are re-entrant; no global state is written except the
- *    thread-local error message.
+ *  - Calls are re-entrant and thread-safe.  Beyond the thread-local error
+ *    message, the only global state is per-device launch information
+ *    (device attributes, kernel LDS limits), set once under a lock.
  */
 #ifndef NT_H
 #define NT_H

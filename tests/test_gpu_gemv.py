@@ -255,3 +255,43 @@ def test_fused_gemv_rejects_shapes_outside_the_fast_path():
     with pytest.raises(nt.NTError) as e:
         nt.nt_gemv_multi(O.Q6_K, [W], [4], [y], 256, x)       # 210-byte rows: not word-aligned
     assert e.value.status == nt.NT_ESHAPE
+
+
+def test_gemv_from_several_threads():
+    """Calls are thread-safe: four host threads, each on its own stream, launch
+    GEMVs of different formats and shapes (first launches included, so the
+    per-device launch settings are filled concurrently); every result equals
+    the same launch made alone."""
+    import threading
+    dev = device()
+    cases = [(O.Q4_K, 300, 8192), (O.Q6_K, 200, 28672), (O.Q5_K, 257, 4096), (O.Q8_0, 129, 14336)]
+    inputs = []
+    for i, (t, rows, cols) in enumerate(cases):
+        W = to_dev(_blocks(t, rows * cols, 80 + i))
+        x = to_dev(synth.normal_f32(80 + i, 450, cols))
+        inputs.append((t, rows, cols, W, x))
+    outs = [torch.empty(rows, dtype=torch.float32, device=dev) for _, rows, *_ in inputs]
+    torch.cuda.synchronize()            # inputs in place before other streams read them
+    errors = []
+
+    def work(k):
+        try:
+            t, rows, cols, W, x = inputs[k]
+            s = torch.cuda.Stream()
+            for _ in range(20):
+                nt.nt_gemv(t, W, x, outs[k], rows, cols, stream=s)
+            s.synchronize()
+        except Exception as e:          # noqa: BLE001 - reported below
+            errors.append(e)
+
+    ths = [threading.Thread(target=work, args=(k,)) for k in range(len(inputs))]
+    for th in ths:
+        th.start()
+    for th in ths:
+        th.join()
+    assert not errors, errors
+    for k, (t, rows, cols, W, x) in enumerate(inputs):
+        ref = torch.empty(rows, dtype=torch.float32, device=dev)
+        nt.nt_gemv(t, W, x, ref, rows, cols)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[k], ref), f"case {k}"
