@@ -416,3 +416,79 @@ class Model:
         s = StreamStats()
         _check(lib().nt_stream_stats_get(self.handle, C.byref(s)), "nt_stream_stats_get")
         return {k: getattr(s, k) for k, _ in StreamStats._fields_}
+
+
+# ---- GGUF model files (host-side reader in libnt) -------------------------------------
+def _declare_gguf(L):
+    vp, st, i64 = C.c_void_p, C.c_int, C.c_int64
+    sig = {
+        "nt_gguf_open": (st, [C.c_char_p, C.POINTER(vp)]),
+        "nt_gguf_close": (None, [vp]),
+        "nt_gguf_tensor_count": (i64, [vp]),
+        "nt_gguf_find_tensor": (i64, [vp, C.c_char_p]),
+        "nt_gguf_tensor_info": (st, [vp, i64, C.POINTER(C.c_char_p), C.POINTER(C.c_int32), C.POINTER(i64),
+                                     C.POINTER(i64), C.POINTER(vp), C.POINTER(C.c_size_t)]),
+        "nt_gguf_llama_config": (st, [vp, C.c_int32, C.POINTER(ModelConfig)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+
+
+class GGUF:
+    """An open GGUF file (libnt maps it read-only).  tensor(name) returns
+    (type, rows, cols, read-only numpy uint8 view of the mapped bytes); the
+    views are valid until close()."""
+
+    def __init__(self, path: str):
+        L = lib()
+        _declare_gguf(L)
+        h = C.c_void_p()
+        _check(L.nt_gguf_open(os.fsencode(path), C.byref(h)), "nt_gguf_open")
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None) and self.handle.value:
+            lib().nt_gguf_close(self.handle)
+            self.handle = C.c_void_p()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __len__(self):
+        return int(lib().nt_gguf_tensor_count(self.handle))
+
+    def info(self, i: int):
+        import numpy as np
+        name, t, rows, cols = C.c_char_p(), C.c_int32(), C.c_int64(), C.c_int64()
+        data, nbytes = C.c_void_p(), C.c_size_t()
+        _check(lib().nt_gguf_tensor_info(self.handle, i, C.byref(name), C.byref(t), C.byref(rows), C.byref(cols),
+                                         C.byref(data), C.byref(nbytes)), "nt_gguf_tensor_info")
+        view = np.ctypeslib.as_array((C.c_uint8 * nbytes.value).from_address(data.value))
+        view.flags.writeable = False
+        return name.value.decode(), t.value, rows.value, cols.value, view
+
+    def names(self):
+        return [self.info(i)[0] for i in range(len(self))]
+
+    def tensor(self, name: str):
+        i = lib().nt_gguf_find_tensor(self.handle, name.encode())
+        if i < 0:
+            raise KeyError(name)
+        _, t, rows, cols, view = self.info(i)
+        return t, rows, cols, view
+
+    def llama_config(self, ctx_cap: int = 0) -> ModelConfig:
+        cfg = ModelConfig()
+        _check(lib().nt_gguf_llama_config(self.handle, ctx_cap, C.byref(cfg)), "nt_gguf_llama_config")
+        return cfg

@@ -339,6 +339,36 @@ nt_status nt_read_bytes(const void *src, int64_t bytes, float *sink, nt_stream s
 nt_status nt_copy_bytes(void *dst, const void *src, int64_t bytes, nt_stream stream);
 nt_status nt_delay(double microseconds, nt_stream stream);
 
+/* ---- GGUF model files ("Overview": the engine loads GGUF models) -----------
+ * Host-side reader of the GGUF v2/v3 container: the file is mapped read-only
+ * and parsed with every read bounds-checked (a truncated or malformed file
+ * returns NT_EINVAL with a message, never reads past the mapping).  Tensor
+ * data stays in the mapping: `data` pointers are host addresses valid until
+ * nt_gguf_close; copy them to the device to build an nt_model (the Llama
+ * tensor names are token_embd.weight, output_norm.weight, output.weight and
+ * blk.<i>.{attn_norm, attn_q, attn_k, attn_v, attn_output, ffn_norm,
+ * ffn_gate, ffn_up, ffn_down}.weight).  No GGUF file from another tool is
+ * available to this library's tests, so compatibility with such files is
+ * checked against the published format only. */
+typedef struct nt_gguf nt_gguf;
+nt_status nt_gguf_open(const char *path, nt_gguf **out);
+void      nt_gguf_close(nt_gguf *g);
+int64_t   nt_gguf_tensor_count(const nt_gguf *g);            /* -1 for NULL */
+int64_t   nt_gguf_find_tensor(const nt_gguf *g, const char *name);   /* index or -1 */
+/* Tensor i: name (valid until close), type (the GGUF/ggml type id; the
+ * nt_qtype values are the same ids), rows x cols (cols = the fastest
+ * dimension, rows = the product of the others), host data and its size.
+ * NT_ESHAPE (data NULL) for a type whose size this library does not know. */
+nt_status nt_gguf_tensor_info(const nt_gguf *g, int64_t i, const char **name, int32_t *type, int64_t *rows,
+                              int64_t *cols, const void **data, size_t *bytes);
+/* The decode configuration of a Llama model file from its llama.* keys and
+ * token_embd.weight (vocab = its rows); ctx_cap > 0 sets the KV capacity,
+ * 0 takes llama.context_length.  head_dim = llama.attention.key_length, or
+ * hidden / head_count when that key is absent (llama.attention.value_length,
+ * when stored, must equal it: NT_ESHAPE otherwise); rope_theta defaults to
+ * 10000 and head_count_kv to head_count. */
+nt_status nt_gguf_llama_config(const nt_gguf *g, int32_t ctx_cap, nt_model_config *cfg);
+
 #ifdef __cplusplus
 }
 #endif

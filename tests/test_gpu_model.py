@@ -254,3 +254,34 @@ def test_step_past_the_cache_and_with_a_bad_token():
     assert int(host(d_tok)[0]) == 0 and int(host(d_pos)[0]) == 6
     assert torch.equal(kcg[n:], before_k[n:]) and torch.equal(vcg[n:], before_v[n:])
     model.close()
+
+
+def test_decode_from_a_gguf_file(tmp_path):
+    """A model read from a GGUF file (written by the tests' writer from the
+    oracle's blocks, loaded by libnt's reader and gguf_model.load_llama)
+    decodes bit for bit like the same weights uploaded directly, whose logits
+    the parity tests above check against the oracle."""
+    from block_quantized_decode_dequant_amd import gguf_model
+
+    from .gguf_writer import llama_gguf
+
+    cfg = tiny_config(n_layers=2, n_q_heads=8, n_kv_heads=2)
+    w = build_oracle_model(cfg, seed=53, wtype="mix")
+    path = tmp_path / "tiny.gguf"
+    path.write_bytes(llama_gguf(cfg, w))
+    gcfg, gweights = gguf_model.load_llama(str(path), ctx_cap=cfg.ctx_cap)
+    assert (gcfg.n_layers, gcfg.hidden, gcfg.vocab, gcfg.ctx_cap) == (cfg.n_layers, cfg.hidden, cfg.vocab, cfg.ctx_cap)
+    kk, vv = kv_prefix(cfg, 7, 8)
+    direct, _, _ = upload(cfg, w, kk, vv)
+    dev = device()
+    ws = torch.empty(nt.nt_model_workspace_bytes(gcfg), dtype=torch.uint8, device=dev)
+    kc = torch.from_numpy(kk.copy()).to(dev)
+    vc = torch.from_numpy(vv.copy()).to(dev)
+    from_file = nt.Model(gcfg, gweights, kc, vc, ws)
+    a, ta = _run_steps(direct, cfg, 8, 5, 4)
+    b, tb = _run_steps(from_file, cfg, 8, 5, 4)
+    assert ta == tb
+    for s, (x, y) in enumerate(zip(a, b)):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), f"step {s}"
+    direct.close()
+    from_file.close()
