@@ -68,6 +68,8 @@ def _declare(L):
         "nt_gemv_multi": (st, [i32, i32, C.POINTER(vp), C.POINTER(i64), C.POINTER(vp), i64, vp, vp, C.c_float,
                                i32, vp]),
         "nt_gemv_swiglu": (st, [i32, vp, vp, i64, i64, vp, vp, C.c_float, vp, vp]),
+        "nt_gemm_batch_workspace_bytes": (C.c_size_t, [i32, i64]),
+        "nt_gemm_batch": (st, [i32, vp, vp, vp, i64, i64, i32, i32, vp, C.c_size_t, vp]),
         "nt_read_bytes": (st, [vp, i64, vp, vp]),
         "nt_copy_bytes": (st, [vp, vp, i64, vp]),
         "nt_delay": (st, [C.c_double, vp]),
@@ -195,6 +197,22 @@ def nt_gemv_swiglu(qtype: int, W_gate, W_up, rows: int, cols: int, x, h, gain=No
     _check(lib().nt_gemv_swiglu(qtype, _ptr(W_gate, rows * rb, "W_gate"), _ptr(W_up, rows * rb, "W_up"), rows, cols,
                                 _ptr(x, 4 * cols, "x"), _ptr(gain, 4 * cols, "gain"), float(eps),
                                 _ptr(h, 4 * rows, "h"), _stream(stream)), "nt_gemv_swiglu")
+
+
+# ---- batched verify pass -------------------------------------------------------------------
+def nt_gemm_batch_workspace_bytes(qtype: int, cols: int) -> int:
+    return lib().nt_gemm_batch_workspace_bytes(qtype, cols)
+
+
+def nt_gemm_batch(qtype: int, W, X, Y, rows: int, cols: int, k: int, workspace, accumulate: bool = False,
+                  stream=None):
+    """Y[n] (+)= W . X[n] for n < k (X: k x cols, Y: k x rows, fp32, back to back)."""
+    rb = row_bytes(qtype, cols)
+    need_w = rows * rb if rb > 0 else 0
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().nt_gemm_batch(qtype, _ptr(W, need_w, "W"), _ptr(X, 4 * k * cols, "X"), _ptr(Y, 4 * k * rows, "Y"),
+                               rows, cols, k, int(bool(accumulate)), _ptr(workspace, 0, "workspace"), ws_bytes,
+                               _stream(stream)), "nt_gemm_batch")
 
 
 # ---- encode -----------------------------------------------------------------------------

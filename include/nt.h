@@ -152,6 +152,23 @@ nt_status nt_gemv_multi(nt_qtype t, int32_t nseg, const void *const *W, const in
 nt_status nt_gemv_swiglu(nt_qtype t, const void *W_gate, const void *W_up, int64_t rows, int64_t cols,
                          const float *x, const float *gain, float eps, float *h, nt_stream stream);
 
+/* ---- batched verify pass ("Overview": self-speculative decoding, where the
+ * resident layers draft tokens and the whole model checks them in one pass) --
+ * Y_n[r] = (Y_n[r] +) sum_c W[r, c] * X_n[c] for n in [0, k), r in [0, rows),
+ * 1 <= k <= 8: every weight is read once for the k vectors.  X is k vectors of
+ * cols fp32 back to back (X_n at X + n * cols), Y is k vectors of rows fp32
+ * (Y_n at Y + n * rows); W is as for nt_gemv.  Types: NT_Q8_0, NT_Q4_K and
+ * NT_Q6_K (others: NT_EINVAL); cols a whole number of blocks, at most 65536;
+ * rows below 2^31.  The products run on the matrix cores with each x split
+ * into two fp16 parts (about 2^-22 relative error per element; |x| must stay
+ * below 65504); weights are not rounded.  workspace: device memory of at
+ * least nt_gemm_batch_workspace_bytes(t, cols), 16-byte aligned, used only
+ * during the call (stream order).  W, X and the workspace 16-byte aligned, Y
+ * 4-byte aligned; Y must not overlap X, W or the workspace. */
+size_t nt_gemm_batch_workspace_bytes(nt_qtype t, int64_t cols);
+nt_status nt_gemm_batch(nt_qtype t, const void *W, const float *X, float *Y, int64_t rows, int64_t cols,
+                        int32_t k, int32_t accumulate, void *workspace, size_t workspace_bytes, nt_stream stream);
+
 /* ---- per-token ops ("Architecture": RMSNorm, RoPE, SwiGLU, softmax kernels;
  * "Main features": the Llama block) --------------------------------------
  * All buffers are device fp32 unless stated, 4-byte aligned, and may not

@@ -144,6 +144,15 @@ def gemv(t: int, W: np.ndarray, rows: int, cols: int, x, nthreads: int | None = 
     return y
 
 
+def gemm_batch(t: int, W: np.ndarray, rows: int, cols: int, X, nthreads: int | None = None) -> np.ndarray:
+    """The verify pass of self-speculative decoding (ntransformer write-up,
+    "Overview"): k activation vectors against one matrix, Y[n] = W . X[n],
+    by its definition, one oracle GEMV per vector.  X: k x cols; returns
+    k x rows (fp64)."""
+    X = np.atleast_2d(np.asarray(X))
+    return np.stack([gemv(t, W, rows, cols, X[n], nthreads) for n in range(X.shape[0])])
+
+
 def gemv_rows(t: int, W: np.ndarray, rows: int, cols: int, x, row_ids,
               nthreads: int | None = None) -> np.ndarray:
     W = np.ascontiguousarray(W, dtype=np.uint8)

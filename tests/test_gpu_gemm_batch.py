@@ -1,0 +1,121 @@
+"""GPU parity for the batched verify pass (nt_gemm_batch: k <= 8 activation
+vectors against one block-quantized matrix on the matrix cores) against the
+fp64 oracle, one oracle GEMV per vector.
+
+Bar: elementwise within 1e-4 + 2e-3 |y|, as for the GEMV (the activations'
+fp16 hi/lo split leaves about 2^-22 relative error per element, far inside
+it).  Shapes span one tile, ragged row tiles, a partial 256-column step
+(Q8_0), every k from 1 to 8, the widest rows the call takes, and the full
+8192 x 8192 70B projection shape.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from block_quantized_decode_dequant_amd import nt, synth, workloads
+
+from .gpu_util import assert_close, device, host, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TYPES = [O.Q8_0, O.Q4_K, O.Q6_K]
+TID = ["q8_0", "q4_k", "q6_k"]
+GUARD = 12345.0
+
+
+def _run(t, W, X, rows, cols, k, y0=None, dev_w=None):
+    dev = device()
+    ws = torch.empty(nt.nt_gemm_batch_workspace_bytes(t, cols), dtype=torch.uint8, device=dev)
+    Y = torch.full((k * rows + 64,), GUARD, dtype=torch.float32, device=dev)
+    if y0 is not None:
+        Y[:k * rows] = to_dev(y0.reshape(-1))
+    nt.nt_gemm_batch(t, dev_w if dev_w is not None else to_dev(W), to_dev(X.reshape(-1)), Y, rows, cols, k, ws,
+                     accumulate=y0 is not None)
+    got = host(Y)
+    assert np.all(got[k * rows:] == GUARD), "written past the k output vectors"
+    return got[:k * rows].reshape(k, rows)
+
+
+def _case(t, rows, cols, k, seed, accumulate=False):
+    W = O.quantize(t, synth.normal_f32(seed, 500 + t, rows * cols, std=0.02))
+    X = np.stack([synth.normal_f32(seed, 510 + 8 * t + n, cols) for n in range(k)])
+    y0 = np.stack([synth.normal_f32(seed, 600 + n, rows) for n in range(k)]) if accumulate else None
+    got = _run(t, W, X, rows, cols, k, y0)
+    ref = O.gemm_batch(t, W, rows, cols, X) + (y0.astype(np.float64) if accumulate else 0.0)
+    for n in range(k):
+        assert_close(got[n], ref[n], what=f"gemm_batch {TID[TYPES.index(t)]} {rows}x{cols} k={k} vector {n}")
+
+
+SHAPES = [(1, 256, 1), (16, 256, 8), (37, 1024, 3), (101, 4352, 8), (300, 8192, 5), (5, 2304, 2),
+          (2, 28672, 8), (3, 65536, 4)]
+
+
+@pytest.mark.parametrize("t", TYPES, ids=TID)
+@pytest.mark.parametrize("rows,cols,k", SHAPES)
+def test_gemm_batch_parity(t, rows, cols, k):
+    _case(t, rows, cols, k, seed=rows + cols + k)
+
+
+@pytest.mark.parametrize("t", TYPES, ids=TID)
+@pytest.mark.parametrize("k", range(1, 9))
+def test_gemm_batch_every_k(t, k):
+    _case(t, 45, 1536, k, seed=70 + k)
+
+
+@pytest.mark.parametrize("t", TYPES, ids=TID)
+def test_gemm_batch_accumulate(t):
+    _case(t, 77, 3072, 6, seed=9, accumulate=True)
+
+
+def test_gemm_batch_q8_0_partial_step_and_odd_blocks():
+    # 33 and 13 blocks per row: the last 256-column step is partial and rows
+    # start at 2-byte offsets
+    _case(O.Q8_0, 19, 33 * 32, 8, seed=3)
+    _case(O.Q8_0, 50, 13 * 32, 3, seed=4)
+    _case(O.Q8_0, 7, 32, 2, seed=5)
+
+
+def test_gemm_batch_rows_are_independent_of_k():
+    """Each vector's result equals the batch-of-one call for that vector, to
+    the GEMV's bar (the k = 1 call is the same kernel, so this checks that
+    the vectors do not mix)."""
+    t, rows, cols = O.Q4_K, 64, 2048
+    W = O.quantize(t, synth.normal_f32(12, 530, rows * cols, std=0.02))
+    X = np.stack([synth.normal_f32(12, 540 + n, cols) for n in range(8)])
+    all8 = _run(t, W, X, rows, cols, 8)
+    for n in (0, 3, 7):
+        one = _run(t, W, X[n:n + 1], rows, cols, 1)
+        assert np.array_equal(one[0], all8[n])
+
+
+@pytest.mark.parametrize("t", [O.Q4_K, O.Q6_K], ids=["q4_k", "q6_k"])
+def test_gemm_batch_70b_projection_shape(t):
+    """8192 x 8192 with k = 8, every output against the oracle."""
+    rows, cols = workloads.KQ_SHAPES[0]
+    w = synth.normal_f32(workloads.SEED, workloads.kq_w_stream(0), rows * cols, std=0.02)
+    W = O.quantize(t, w)
+    X = np.stack([synth.activation(workloads.SEED, workloads.kq_x_stream(0) + 100 * n, cols) for n in range(8)])
+    got = _run(t, W, X, rows, cols, 8)
+    ref = O.gemm_batch(t, W, rows, cols, X)
+    for n in range(8):
+        assert_close(got[n], ref[n], what=f"gemm_batch {t} {rows}x{cols} vector {n}")
+
+
+def test_gemm_batch_rejects_bad_arguments():
+    dev = device()
+    W = torch.zeros(144 * 4, dtype=torch.uint8, device=dev)
+    X = torch.zeros(9 * 256, dtype=torch.float32, device=dev)
+    Y = torch.zeros(9 * 4, dtype=torch.float32, device=dev)
+    ws = torch.empty(nt.nt_gemm_batch_workspace_bytes(O.Q4_K, 256), dtype=torch.uint8, device=dev)
+    for k in (0, 9):
+        with pytest.raises(nt.NTError):
+            nt.nt_gemm_batch(O.Q4_K, W, X, Y, 4, 256, k, ws)
+    with pytest.raises(nt.NTError):
+        nt.nt_gemm_batch(O.Q4_0, W, X, Y, 4, 256, 2, ws)
+    with pytest.raises(nt.NTError) as e:
+        nt.nt_gemm_batch(O.Q4_K, W, X, Y, 4, 256, 2, ws[:-16])
+    assert e.value.status == nt.NT_ENOMEM
+    Y.fill_(3.0)
+    nt.nt_gemm_batch(O.Q4_K, W, X, Y, 0, 256, 2, ws)
+    assert torch.all(Y == 3.0)

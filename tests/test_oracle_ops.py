@@ -242,3 +242,20 @@ def test_attention_rejects_bad_shapes():
         O.attention(np.zeros(24), np.zeros(16), np.zeros(16), kc, kc.copy(), 3, 2, 8, 4, 0)
     with pytest.raises(ValueError):
         O.attention(np.zeros(32), np.zeros(16), np.zeros(16), kc, kc.copy(), 4, 2, 8, 4, 4)
+
+
+@pytest.mark.parametrize("t", [O.Q8_0, O.Q4_K, O.Q6_K])
+def test_gemm_batch_is_the_dequantized_matrix_product(t):
+    # k vectors against one matrix: the decoded matrix times X (numpy, fp64),
+    # and each row of the result is that vector's own product (no mixing)
+    rows, cols, k = 9, 512, 3
+    W = O.quantize(t, synth.normal_f32(21, t, rows * cols, std=0.05))
+    X = np.stack([synth.normal_f32(22, 10 * t + n, cols) for n in range(k)])
+    Y = O.gemm_batch(t, W, rows, cols, X)
+    Wd = O.dequant(t, W, rows * cols).astype(np.float64).reshape(rows, cols)
+    assert Y.shape == (k, rows)
+    np.testing.assert_allclose(Y, X.astype(np.float64) @ Wd.T, rtol=1e-12, atol=1e-12)
+    X2 = X.copy()
+    X2[1] = 0.0
+    Y2 = O.gemm_batch(t, W, rows, cols, X2)
+    assert np.all(Y2[1] == 0.0) and np.array_equal(Y2[[0, 2]], Y[[0, 2]])
