@@ -31,6 +31,7 @@
 // A workgroup of kWaves waves owns 16 rows; its waves take interleaved
 // 256-column steps and add their partial sums through LDS in a fixed order.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_util.h"
 #include "nt_internal.h"
@@ -43,7 +44,14 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t w2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 8;
+#ifndef NT_BG_WAVES
+#define NT_BG_WAVES 4
+#endif
+#ifndef NT_BG_TILES
+#define NT_BG_TILES 2
+#endif
+constexpr int kWaves = NT_BG_WAVES;   // waves of a workgroup (they split the columns)
+constexpr int kTiles = NT_BG_TILES;   // 16-row tiles of a wave (they share the activations)
 
 // Order of a dword's four bytes in the K slots of one lane: the halves of
 // (w & 0x00ff00ff) then of (w >> 8 & 0x00ff00ff), i.e. bytes 0, 2, 1, 3.
@@ -58,21 +66,34 @@ __device__ __forceinline__ uint32_t hmul(uint32_t w, _Float16 c) {
 }
 __device__ __forceinline__ f4 mfma(h4 a, h4 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0); }
 
-// The 32-bit word at a 2-byte-aligned address: two aligned words and a byte
-// funnel.  With sh == 0 the second load re-reads the first word, so no word
-// wholly past the bytes asked for is touched.
-__device__ __forceinline__ uint32_t ldu(const uint8_t *p) {
-    const uint32_t sh = uint32_t(reinterpret_cast<uintptr_t>(p) & 3);
-    const uint8_t *a = p - sh;
-    const uint32_t lo = ld1(a), hi = ld1(a + (sh ? 4 : 0));
-    return funnel(hi, lo, shift_sel(sh));
-}
+// Per format: load() issues every global load of one 256-column step into
+// a Raw of registers (no use of the data), compute() turns a loaded Raw into
+// MFMAs, so the main loop can keep the next step's loads in flight.
 
 // ---- Q8_0: a step is 8 blocks; MFMA m covers block m/2, elements
-// 8g + 4(m&1) + perm4(i) for lane group g.
+// 8g + 4(m&1) + perm4(i) for lane group g.  The 8 code bytes of a lane sit at
+// a 2-byte-aligned offset: two aligned loads (8 + 4 bytes; with a word-aligned
+// start the second re-reads the last word, so nothing wholly past the block
+// is touched) and a byte funnel.  Blocks past the end of a row (a partial
+// last step) load block 0 of the row and get scale 0.
 struct BQ80 {
     static constexpr bool kMin = false;
+    struct Raw { u32x2 a[8]; uint32_t c[8], d[8]; };
     __host__ __device__ static int elem(int m, int g, int i) { return 32 * (m >> 1) + 8 * g + 4 * (m & 1) + perm4(i); }
+    __device__ static void load(const uint8_t *row, int s, int g, int nblk, Raw &r) {
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb) {
+            const int blk = 8 * s + bb;
+            const bool live = blk < nblk;
+            const uint8_t *b = row + int64_t(live ? blk : 0) * 34;
+            const uint32_t bs = uint32_t(reinterpret_cast<uintptr_t>(b) & 3);   // 0 or 2
+            const uint8_t *p = b + 2 + 8 * g;
+            const uint32_t sh = bs ^ 2;                                        // (b + 2) & 3
+            r.a[bb] = *reinterpret_cast<const u32x2 *>(p - sh);
+            r.c[bb] = ld1(p - sh + (sh ? 8 : 4));
+            r.d[bb] = ld1(b - bs);
+        }
+    }
     // int8 codes of a word -> two fp16 pairs q (bytes 0,2 and 1,3): 0x64uu is
     // 1024 + uu, the sign bit flipped makes uu = q + 128.
     __device__ static h4 codes(uint32_t w) {
@@ -80,15 +101,18 @@ struct BQ80 {
         const uint32_t b = hadd(((w >> 8) & 0x00ff00ffu) ^ 0x64806480u, _Float16(-1152.f));
         return pack(a, b);
     }
-    __device__ static void step(const uint8_t *row, int s, int g, int nblk, const h4 *xa, h4, f4 &acc) {
+    __device__ static void compute(const Raw &r, const uint8_t *row, int s, int nblk, const h4 *xa, h4, f4 &acc) {
 #pragma unroll
         for (int bb = 0; bb < 8; ++bb) {
             const int blk = 8 * s + bb;
-            if (blk >= nblk) break;                       // uniform over the wave
-            const uint8_t *b = row + int64_t(blk) * 34;
-            const uint32_t w0 = ldu(b + 2 + 8 * g), w1 = ldu(b + 6 + 8 * g);
-            const uint32_t dsh = uint32_t(reinterpret_cast<uintptr_t>(b) & 2);
-            const float d = h2f(ld1(b - dsh) >> (8 * dsh));
+            const bool live = blk < nblk;
+            const uint8_t *b = row + int64_t(live ? blk : 0) * 34;
+            const uint32_t bs = uint32_t(reinterpret_cast<uintptr_t>(b) & 3);
+            const uint32_t sh = bs ^ 2;
+            const uint32_t sel = shift_sel(sh);
+            const uint32_t w0 = funnel(r.a[bb].y, r.a[bb].x, sel);
+            const uint32_t w1 = funnel(sh ? r.c[bb] : r.a[bb].y, r.a[bb].y, sel);
+            const float d = live ? h2f(r.d[bb] >> (8 * bs)) : 0.f;
             f4 c = mfma(xa[2 * bb], codes(w0), f4{0.f, 0.f, 0.f, 0.f});
             c = mfma(xa[2 * bb + 1], codes(w1), c);
             acc += d * c;
@@ -105,9 +129,16 @@ struct BQ80 {
 // B = M_j.
 struct BQ4K {
     static constexpr bool kMin = true;
+    struct Raw { u32x4 h; u32x2 q[4]; };
     __host__ __device__ static int elem(int m, int g, int i) {
         const int p = m >> 2, nib = (m >> 1) & 1, j = m & 1;
         return 32 * (2 * p + nib) + 8 * g + 4 * j + perm4(i);
+    }
+    __device__ static void load(const uint8_t *row, int s, int g, int, Raw &r) {
+        const uint8_t *b = row + int64_t(s) * 144;
+        r.h = ld4(b);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) r.q[p] = *reinterpret_cast<const u32x2 *>(b + 16 + 32 * p + 8 * g);
     }
     __device__ static void scale_min(const u32x4 &h, int j, uint32_t &S, uint32_t &M) {
         const uint32_t sc[3] = {h.y, h.z, h.w};
@@ -120,23 +151,18 @@ struct BQ4K {
             M = (byte(j + 4) >> 4) | ((byte(j) >> 6) << 4);
         }
     }
-    __device__ static void step(const uint8_t *row, int s, int g, int, const h4 *xa, h4 xm, f4 &acc) {
-        const uint8_t *b = row + int64_t(s) * 144;
-        const u32x4 h = ld4(b);
-        w2 q[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) q[p] = *reinterpret_cast<const w2 *>(b + 16 + 32 * p + 8 * g);
+    __device__ static void compute(const Raw &r, int g, const h4 *xa, h4 xm, f4 &acc) {
         f4 c = {0.f, 0.f, 0.f, 0.f};
         uint32_t Mw[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             uint32_t S0, M0, S1, M1;
-            scale_min(h, 2 * p, S0, M0);
-            scale_min(h, 2 * p + 1, S1, M1);
+            scale_min(r.h, 2 * p, S0, M0);
+            scale_min(r.h, 2 * p + 1, S1, M1);
             const _Float16 f0 = _Float16(float(S0 * 1024u)), f1 = _Float16(float(S1 * 64u));
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const uint32_t w = q[p][j], t = w >> 8;
+                const uint32_t w = r.q[p][j], t = w >> 8;
                 c = mfma(xa[4 * p + j], pack(hmul(w & 0x000f000fu, f0), hmul(t & 0x000f000fu, f0)), c);
                 c = mfma(xa[4 * p + 2 + j], pack(hmul(w & 0x00f000f0u, f1), hmul(t & 0x00f000f0u, f1)), c);
             }
@@ -147,7 +173,7 @@ struct BQ4K {
         const h4 mb = {_Float16(float(ma & 0xffffu)), _Float16(float(ma >> 16)), _Float16(float(mc & 0xffffu)),
                        _Float16(float(mc >> 16))};
         const f4 cm = mfma(xm, mb, f4{0.f, 0.f, 0.f, 0.f});
-        const float d = h2f(h.x) * 16384.f, dmin = h2f(h.x >> 16);
+        const float d = h2f(r.h.x) * 16384.f, dmin = h2f(r.h.x >> 16);
         acc += d * c - dmin * cm;
     }
 };
@@ -157,11 +183,30 @@ struct BQ4K {
 // 128h + 32k + 16lh + 4g + perm4(i); the low four bits come from
 // ql[64h + 32(k&1) + 16lh + 4g + i] (nibble k>>1), the top two from
 // qh[32h + 16lh + 4g + i] (bits 2k, 2k+1).  Codes become q - 32 exactly.
+// Each needed word is one aligned 8-byte load (it stays inside the
+// super-block for every offset used) and a byte funnel.
 struct BQ6K {
     static constexpr bool kMin = false;
+    struct Raw { u32x2 ql[2][2][2], qh[2][2]; u32x4 sw; uint32_t tail; };
     __host__ __device__ static int elem(int m, int g, int i) {
         const int h = m >> 3, k = (m >> 1) & 3, lh = m & 1;
         return 128 * h + 32 * k + 16 * lh + 4 * g + perm4(i);
+    }
+    __device__ static void load(const uint8_t *row, int s, int g, int, Raw &r) {
+        const uint8_t *b = row + int64_t(s) * 210;
+        const uint32_t sh = uint32_t(reinterpret_cast<uintptr_t>(b) & 2);
+        const uint8_t *a = b - sh;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int lh = 0; lh < 2; ++lh) {
+                r.ql[h][0][lh] = *reinterpret_cast<const u32x2 *>(a + 64 * h + 16 * lh + 4 * g);
+                r.ql[h][1][lh] = *reinterpret_cast<const u32x2 *>(a + 64 * h + 32 + 16 * lh + 4 * g);
+                r.qh[h][lh] = *reinterpret_cast<const u32x2 *>(a + 128 + 32 * h + 16 * lh + 4 * g);
+            }
+        // 16 int8 scales and d: words at 192 - sh .. 208 - sh
+        r.sw = ld4(a + 192);
+        r.tail = ld1(a + 208);
     }
     __device__ static h4 codes(uint32_t lo4, uint32_t qh, int k) {
         const uint32_t q = lo4 | (((qh >> (2 * k)) & 0x03030303u) << 4);
@@ -169,32 +214,20 @@ struct BQ6K {
         const uint32_t b = hadd(((q >> 8) & 0x00ff00ffu) | 0x64006400u, _Float16(-1056.f));
         return pack(a, b);
     }
-    __device__ static void step(const uint8_t *row, int s, int g, int, const h4 *xa, h4, f4 &acc) {
-        const uint8_t *b = row + int64_t(s) * 210;
-        uint32_t ql[2][2][2], qh[2][2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int lh = 0; lh < 2; ++lh) {
-                ql[h][0][lh] = ldu(b + 64 * h + 16 * lh + 4 * g);
-                ql[h][1][lh] = ldu(b + 64 * h + 32 + 16 * lh + 4 * g);
-                qh[h][lh] = ldu(b + 128 + 32 * h + 16 * lh + 4 * g);
-            }
-        // 16 int8 scales and d: words at 192 - sh .. 208 - sh, funnelled
-        const uint32_t sh = uint32_t(reinterpret_cast<uintptr_t>(b) & 2);
-        const u32x4 sw = ld4(b + 192 - sh);
-        const uint32_t tail = ld1(b + 208 - sh);
+    __device__ static void compute(const Raw &r, const uint8_t *row, int s, const h4 *xa, f4 &acc) {
+        const uint32_t sh = uint32_t(reinterpret_cast<uintptr_t>(row + int64_t(s) * 210) & 2);
         const uint32_t sel = shift_sel(sh);
-        const uint32_t sc[4] = {funnel(sw.y, sw.x, sel), funnel(sw.z, sw.y, sel), funnel(sw.w, sw.z, sel),
-                                funnel(tail, sw.w, sel)};
-        const float d = h2f(sh ? tail >> 16 : tail);
+        auto fw = [&](const u32x2 &v) { return funnel(v.y, v.x, sel); };
+        const uint32_t sc[4] = {funnel(r.sw.y, r.sw.x, sel), funnel(r.sw.z, r.sw.y, sel),
+                                funnel(r.sw.w, r.sw.z, sel), funnel(r.tail, r.sw.w, sel)};
+        const float d = h2f(sh ? r.tail >> 16 : r.tail);
         f4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             const int h = m >> 3, k = (m >> 1) & 3, lh = m & 1;
-            const uint32_t l = ql[h][k & 1][lh];
+            const uint32_t l = fw(r.ql[h][k & 1][lh]);
             const uint32_t lo4 = (k < 2 ? l : l >> 4) & 0x0f0f0f0fu;
-            const f4 c = mfma(xa[m], codes(lo4, qh[h][lh], k), f4{0.f, 0.f, 0.f, 0.f});
+            const f4 c = mfma(xa[m], codes(lo4, fw(r.qh[h][lh]), k), f4{0.f, 0.f, 0.f, 0.f});
             const float scm = float(int8_t((sc[m >> 2] >> (8 * (m & 3))) & 0xffu));
             t += scm * c;
         }
@@ -206,8 +239,8 @@ struct BQ6K {
 // (fp16) = hi or lo part of x_n[256 s + elem(m, g, i)], n = lane % 8,
 // lo for lane % 16 >= 8, zero for n >= k or past cols.  For K-quant mins,
 // xm[(s * 64 + lane) * 4 + i]: K slot 4g + i of lane (b, g) is the hi (slots
-// 0-7) or lo (8-15) part of the sum of x_b over sub-block (4g + i) & 7;
-// zero for b >= 8.
+// 0-7) or lo (8-15) part of the fp32 sum of x_b over sub-block (4g + i) & 7
+// (four-way partial sums of 8 float4s, in a fixed order); zero for b >= 8.
 __device__ __forceinline__ uint16_t hbits(float v) { return __half_as_ushort(__float2half_rn(v)); }
 __device__ __forceinline__ uint16_t split_part(float v, bool lo) {
     const __half hi = __float2half_rn(v);
@@ -216,39 +249,73 @@ __device__ __forceinline__ uint16_t split_part(float v, bool lo) {
 
 template <class F>
 __global__ void __launch_bounds__(256) bgemm_prep(const float *__restrict__ X, int64_t cols, int k, int nsteps,
-                                                  uint32_t *__restrict__ xp, uint32_t *__restrict__ xm) {
+                                                  uint32_t *__restrict__ xp, uint16_t *__restrict__ xm) {
     const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (t >= int64_t(nsteps) * 1024) return;
-    const int m = int(t & 15), lane = int((t >> 4) & 63);
-    const int64_t s = t >> 10;
-    const int b = lane & 15, g = lane >> 4, n = b & 7;
-    const bool lo = b >= 8;
-    uint32_t hv[4];
+    const int64_t nx = int64_t(nsteps) * 1024;
+    if (t < nx) {
+        // one thread per (step, lane, MFMA): four fp16 parts
+        const int m = int(t & 15), lane = int((t >> 4) & 63);
+        const int64_t s = t >> 10;
+        const int b = lane & 15, g = lane >> 4, n = b & 7;
+        const bool lo = b >= 8;
+        uint32_t hv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t e = s * 256 + F::elem(m, g, i);
-        const float v = (n < k && e < cols) ? X[n * cols + e] : 0.f;
-        hv[i] = split_part(v, lo);
-    }
-    xp[2 * t] = hv[0] | (hv[1] << 16);
-    xp[2 * t + 1] = hv[2] | (hv[3] << 16);
-    if constexpr (F::kMin) {
-        if (m == 0) {
-            uint32_t mv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int kk = 4 * g + i, j = kk & 7;
-                float sx = 0.f;
-                if (b < 8 && n < k) {
-                    const float *p = X + n * cols + s * 256 + 32 * j;
-                    for (int u = 0; u < 32; ++u) sx += p[u];
-                }
-                mv[i] = split_part(sx, kk >= 8);
-            }
-            const int64_t o = (s * 64 + lane) * 2;
-            xm[o] = mv[0] | (mv[1] << 16);
-            xm[o + 1] = mv[2] | (mv[3] << 16);
+        for (int i = 0; i < 4; ++i) {
+            const int64_t e = s * 256 + F::elem(m, g, i);
+            const float v = (n < k && e < cols) ? X[n * cols + e] : 0.f;
+            hv[i] = split_part(v, lo);
         }
+        xp[2 * t] = hv[0] | (hv[1] << 16);
+        xp[2 * t + 1] = hv[2] | (hv[3] << 16);
+        return;
+    }
+    if constexpr (F::kMin) {
+        // one thread per (step, lane, K slot) of the min MFMA's A operand
+        const int64_t u = t - nx;
+        if (u >= int64_t(nsteps) * 256) return;
+        const int i = int(u & 3), lane = int((u >> 2) & 63);
+        const int64_t s = u >> 8;
+        const int b = lane & 15, g = lane >> 4, kk = 4 * g + i, j = kk & 7;
+        float sx = 0.f;
+        if (b < 8 && b < k) {
+            const float4 *p = reinterpret_cast<const float4 *>(X + b * cols + s * 256 + 32 * j);
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const float4 q = p[v];
+                sx += (q.x + q.y) + (q.z + q.w);
+            }
+        }
+        xm[u] = split_part(sx, kk >= 8);
+    }
+}
+
+template <class F>
+__device__ __forceinline__ void load_step(const uint8_t *const (&row)[kTiles], int s, int lane, int g, int nblk,
+                                          const uint32_t *__restrict__ xp, const uint32_t *__restrict__ xm,
+                                          typename F::Raw (&r)[kTiles], u32x4 (&xr)[8], u32x2 &xmr) {
+    const u32x4 *px = reinterpret_cast<const u32x4 *>(xp) + (int64_t(s) * 64 + lane) * 8;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xr[q] = px[q];
+    if constexpr (F::kMin) xmr = *reinterpret_cast<const u32x2 *>(xm + (int64_t(s) * 64 + lane) * 2);
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) F::load(row[t], s, g, nblk, r[t]);
+}
+
+template <class F>
+__device__ __forceinline__ void compute_step(const typename F::Raw (&r)[kTiles], const u32x4 (&xr)[8],
+                                             const u32x2 &xmr, const uint8_t *const (&row)[kTiles], int s, int g,
+                                             int nblk, f4 (&acc)[kTiles]) {
+    h4 xa[16];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        xa[2 * q] = pack(xr[q].x, xr[q].y);
+        xa[2 * q + 1] = pack(xr[q].z, xr[q].w);
+    }
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+        if constexpr (std::is_same<F, BQ80>::value) F::compute(r[t], row[t], s, nblk, xa, h4{}, acc[t]);
+        else if constexpr (std::is_same<F, BQ4K>::value) F::compute(r[t], g, xa, pack(xmr.x, xmr.y), acc[t]);
+        else F::compute(r[t], row[t], s, xa, acc[t]);
     }
 }
 
@@ -257,38 +324,50 @@ __global__ void __launch_bounds__(64 * kWaves) bgemm(const uint8_t *__restrict__
                                                       int nsteps, int nblk, const uint32_t *__restrict__ xp,
                                                       const uint32_t *__restrict__ xm, float *__restrict__ Y,
                                                       int k, int accumulate) {
-    __shared__ float part[kWaves][16][8];
+    __shared__ float part[kWaves][16 * kTiles][8];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, r = lane & 15, g = lane >> 4;
-    const int64_t R = int64_t(blockIdx.x) * 16 + r;
+    const int64_t R0 = int64_t(blockIdx.x) * 16 * kTiles + r;
     // rows past the end read row 0 (in bounds); their results are not written
-    const uint8_t *row = W + (R < rows ? R : 0) * row_bytes;
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = wv; s < nsteps; s += kWaves) {
-        const u32x4 *px = reinterpret_cast<const u32x4 *>(xp) + (int64_t(s) * 64 + lane) * 8;
-        h4 xa[16];
+    const uint8_t *row[kTiles];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const u32x4 v = px[q];
-            xa[2 * q] = pack(v.x, v.y);
-            xa[2 * q + 1] = pack(v.z, v.w);
+    for (int t = 0; t < kTiles; ++t) row[t] = W + (R0 + 16 * t < rows ? R0 + 16 * t : 0) * row_bytes;
+    f4 acc[kTiles];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+    if (wv < nsteps) {
+        // one step ahead, in two register sets used in turn: the loads of the
+        // next step are in flight while this one is computed (a step past
+        // the end re-loads the current one, from cache)
+        typename F::Raw ra[kTiles], rb[kTiles];
+        u32x4 xa_[8], xb_[8];
+        u32x2 ma = {0u, 0u}, mb = {0u, 0u};
+        load_step<F>(row, wv, lane, g, nblk, xp, xm, ra, xa_, ma);
+        for (int s = wv; s < nsteps; s += 2 * kWaves) {
+            const int s1 = s + kWaves < nsteps ? s + kWaves : s;
+            load_step<F>(row, s1, lane, g, nblk, xp, xm, rb, xb_, mb);
+            // keeps the loads above ahead of the arithmetic (the scheduler
+            // would otherwise sink them to their first use)
+            asm volatile("" ::: "memory");
+            compute_step<F>(ra, xa_, ma, row, s, g, nblk, acc);
+            if (s + kWaves >= nsteps) break;
+            const int s2 = s + 2 * kWaves < nsteps ? s + 2 * kWaves : s1;
+            load_step<F>(row, s2, lane, g, nblk, xp, xm, ra, xa_, ma);
+            asm volatile("" ::: "memory");
+            compute_step<F>(rb, xb_, mb, row, s1, g, nblk, acc);
         }
-        h4 xmin = {};
-        if constexpr (F::kMin) {
-            const w2 v = *reinterpret_cast<const w2 *>(xm + (int64_t(s) * 64 + lane) * 2);
-            xmin = pack(v.x, v.y);
-        }
-        F::step(row, s, g, nblk, xa, xmin, acc);
     }
     // lanes g and g + 2 hold the hi and lo parts of outputs n = 4g + i
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float o = acc[i] + __shfl_down(acc[i], 32, 64);
-        if (g < 2) part[wv][r][4 * g + i] = o;
-    }
+    for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float o = acc[t][i] + __shfl_down(acc[t][i], 32, 64);
+            if (g < 2) part[wv][16 * t + r][4 * g + i] = o;
+        }
     __syncthreads();
-    if (threadIdx.x < 128) {
-        const int rr = threadIdx.x & 15, n = threadIdx.x >> 4;
-        const int64_t R2 = int64_t(blockIdx.x) * 16 + rr;
+    for (int j = threadIdx.x; j < 128 * kTiles; j += 64 * kWaves) {
+        const int rr = j % (16 * kTiles), n = j / (16 * kTiles);
+        const int64_t R2 = int64_t(blockIdx.x) * 16 * kTiles + rr;
         if (n < k && R2 < rows) {
             float v = 0.f;
 #pragma unroll
@@ -316,11 +395,12 @@ hipError_t run_bgemm(const void *W, int64_t row_bytes, int64_t rows, int64_t col
     const int ns = int(bgemm_steps(cols));
     uint32_t *xp = static_cast<uint32_t *>(ws);
     uint32_t *xm = F::kMin ? xp + int64_t(ns) * 2048 : nullptr;
-    const int64_t nt = int64_t(ns) * 1024;
-    hipLaunchKernelGGL(bgemm_prep<F>, dim3(unsigned((nt + 255) / 256)), dim3(256), 0, st, X, cols, k, ns, xp, xm);
+    const int64_t nt = int64_t(ns) * (F::kMin ? 1024 + 256 : 1024);
+    hipLaunchKernelGGL(bgemm_prep<F>, dim3(unsigned((nt + 255) / 256)), dim3(256), 0, st, X, cols, k, ns, xp,
+                       reinterpret_cast<uint16_t *>(xm));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || rows == 0) return e;
-    hipLaunchKernelGGL(bgemm<F>, dim3(unsigned((rows + 15) / 16)), dim3(64 * kWaves), 0, st,
+    hipLaunchKernelGGL(bgemm<F>, dim3(unsigned((rows + 16 * kTiles - 1) / (16 * kTiles))), dim3(64 * kWaves), 0, st,
                        static_cast<const uint8_t *>(W), row_bytes, int(rows), ns, int(nblk), xp, xm, Y, k, accumulate);
     return hipGetLastError();
 }
