@@ -14,7 +14,8 @@ The CPU baseline times the oracle (plain fp64 C, test-side code) on a bounded
 sample of the same workload: the first rows of each matrix.
 
 Q5_K GEMV at the two Llama-70B FFN shapes rides along ("q5_k_gemv"), timed like
-the sweep's per-kernel times.  Decode measurements ride along in the same JSON line ("decode"): the
+the sweep's per-kernel times, and so does the batched verify pass of
+self-speculative decoding ("verify_gemm": k = 8 vectors per weight read).  Decode measurements ride along in the same JSON line ("decode"): the
 Llama-3-8B-shaped Q8_0 model (128 greedy tokens from position 1024), the
 Llama-70B-shaped Q4_K/Q6_K model (64 tokens from 4096), each replayed from a
 captured HIP graph, and the 70B all-Q6_K model with 24 GiB of layers resident
@@ -281,6 +282,71 @@ def q5_k_gemv(steps):
     return out
 
 
+VERIFY_K = 8
+VERIFY_CASES = [("q8_0", 4096, 4096), ("q4_k", 8192, 8192), ("q4_k", 28672, 8192), ("q6_k", 8192, 8192),
+                ("q6_k", 8192, 28672)]
+
+
+def verify_gemm(steps):
+    """The batched verify pass (nt_gemm_batch, k = 8 draft tokens against one
+    matrix) at the 8B Q8_0 and 70B K-quant projection shapes, timed like the
+    sweep (device-encoded weights from N(0, 0.02) values, rotated copies
+    >= 1 GiB apart, one HIP graph of `steps` launches) beside one GEMV of the
+    same matrix.  "gbs": algorithmic bytes (weights once, k activation and
+    output vectors) per second; "x_vs_k_gemv": k GEMV times over the batched
+    time.  Reported beside the sweep, not part of `value`."""
+    import numpy as np
+    import torch
+
+    from block_quantized_decode_dequant_amd import nt, synth, workloads
+
+    dev = torch.device("cuda:0")
+    k = VERIFY_K
+    out = []
+    for name, rows, cols in VERIFY_CASES:
+        t = {"q8_0": nt.Q8_0, "q4_k": nt.Q4_K, "q6_k": nt.Q6_K}[name]
+        w32 = torch.from_numpy(synth.normal_f32(workloads.SEED, 700 + rows // 1024 + cols // 1024, rows * cols,
+                                                std=0.02)).to(dev)
+        X = torch.from_numpy(np.concatenate([synth.activation(workloads.SEED, 710 + n, cols)
+                                             for n in range(k)])).to(dev)
+        nbytes = rows * nt.row_bytes(t, cols)
+        base = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        nt.nt_quantize(t, w32, base, rows * cols)
+        del w32
+        copies = max(2, -(-(1 << 30) // nbytes) + 1)
+        Ws = [base] + [base.clone() for _ in range(copies - 1)]
+        Y = torch.empty(k * rows, dtype=torch.float32, device=dev)
+        ws = torch.empty(nt.nt_gemm_batch_workspace_bytes(t, cols), dtype=torch.uint8, device=dev)
+        side = torch.cuda.Stream()
+
+        def timed(call):
+            with torch.cuda.stream(side):
+                call(0)
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    for i in range(steps):
+                        call(i)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(side):
+                g.replay()
+                a.record(side)
+                g.replay()
+                b.record(side)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / steps
+
+        us = timed(lambda i: nt.nt_gemm_batch(t, Ws[i % copies], X, Y, rows, cols, k, ws))
+        us1 = timed(lambda i: nt.nt_gemv(t, Ws[i % copies], X[:cols], Y[:rows], rows, cols))
+        alg = nbytes + 4 * k * (cols + rows)
+        out.append({"type": name, "rows": rows, "cols": cols, "k": k, "bytes": alg, "us": round(us, 3),
+                    "gbs": round(alg / (us * 1e-6) / 1e9, 1), "frac": round(alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                    "gemv_us": round(us1, 3), "x_vs_k_gemv": round(k * us1 / us, 2)})
+        del Ws, base
+        torch.cuda.empty_cache()
+    return out
+
+
 def time_decode(model, shape, n_tokens, warmup=8):
     import torch
     dev = torch.device("cuda:0")
@@ -477,6 +543,7 @@ def main():
         "roofline": g["roofline"],
         "detail": g["detail"],
         "q5_k_gemv": q5_k_gemv(args.steps),
+        "verify_gemm": verify_gemm(args.steps),
     }
     if args.decode != "none":
         dec = {}
