@@ -28,8 +28,9 @@
 //    K slots is free as long as A and B agree, so each lane takes the codes of
 //    its row that lie together in memory.
 //
-// A workgroup of kWaves waves owns 16 rows; its waves take interleaved
-// 256-column steps and add their partial sums through LDS in a fixed order.
+// A workgroup of kWaves waves owns 16 * kTiles rows; each wave takes all its
+// tiles and interleaved 256-column steps, and the waves add their partial
+// sums through LDS in a fixed order.
 #include <algorithm>
 #include <type_traits>
 
@@ -47,11 +48,11 @@ typedef uint32_t w2 __attribute__((ext_vector_type(2)));
 #ifndef NT_BG_WAVES
 #define NT_BG_WAVES 4
 #endif
-#ifndef NT_BG_TILES
-#define NT_BG_TILES 2
-#endif
 constexpr int kWaves = NT_BG_WAVES;   // waves of a workgroup (they split the columns)
-constexpr int kTiles = NT_BG_TILES;   // 16-row tiles of a wave (they share the activations)
+// 16-row tiles of a wave (they share the activation loads): 2, or 4 for
+// Q4_K matrices of at least kTallRows rows (enough workgroups to fill the
+// chip; fewer activation bytes per weight byte)
+constexpr int kTallRows = 16384;
 
 // Order of a dword's four bytes in the K slots of one lane: the halves of
 // (w & 0x00ff00ff) then of (w >> 8 & 0x00ff00ff), i.e. bytes 0, 2, 1, 3.
@@ -289,7 +290,7 @@ __global__ void __launch_bounds__(256) bgemm_prep(const float *__restrict__ X, i
     }
 }
 
-template <class F>
+template <class F, int kTiles>
 __device__ __forceinline__ void load_step(const uint8_t *const (&row)[kTiles], int s, int lane, int g, int nblk,
                                           const uint32_t *__restrict__ xp, const uint32_t *__restrict__ xm,
                                           typename F::Raw (&r)[kTiles], u32x4 (&xr)[8], u32x2 &xmr) {
@@ -301,7 +302,7 @@ __device__ __forceinline__ void load_step(const uint8_t *const (&row)[kTiles], i
     for (int t = 0; t < kTiles; ++t) F::load(row[t], s, g, nblk, r[t]);
 }
 
-template <class F>
+template <class F, int kTiles>
 __device__ __forceinline__ void compute_step(const typename F::Raw (&r)[kTiles], const u32x4 (&xr)[8],
                                              const u32x2 &xmr, const uint8_t *const (&row)[kTiles], int s, int g,
                                              int nblk, f4 (&acc)[kTiles]) {
@@ -319,7 +320,7 @@ __device__ __forceinline__ void compute_step(const typename F::Raw (&r)[kTiles],
     }
 }
 
-template <class F>
+template <class F, int kTiles>
 __global__ void __launch_bounds__(64 * kWaves) bgemm(const uint8_t *__restrict__ W, int64_t row_bytes, int rows,
                                                       int nsteps, int nblk, const uint32_t *__restrict__ xp,
                                                       const uint32_t *__restrict__ xm, float *__restrict__ Y,
@@ -341,19 +342,19 @@ __global__ void __launch_bounds__(64 * kWaves) bgemm(const uint8_t *__restrict__
         typename F::Raw ra[kTiles], rb[kTiles];
         u32x4 xa_[8], xb_[8];
         u32x2 ma = {0u, 0u}, mb = {0u, 0u};
-        load_step<F>(row, wv, lane, g, nblk, xp, xm, ra, xa_, ma);
+        load_step<F, kTiles>(row, wv, lane, g, nblk, xp, xm, ra, xa_, ma);
         for (int s = wv; s < nsteps; s += 2 * kWaves) {
             const int s1 = s + kWaves < nsteps ? s + kWaves : s;
-            load_step<F>(row, s1, lane, g, nblk, xp, xm, rb, xb_, mb);
+            load_step<F, kTiles>(row, s1, lane, g, nblk, xp, xm, rb, xb_, mb);
             // keeps the loads above ahead of the arithmetic (the scheduler
             // would otherwise sink them to their first use)
             asm volatile("" ::: "memory");
-            compute_step<F>(ra, xa_, ma, row, s, g, nblk, acc);
+            compute_step<F, kTiles>(ra, xa_, ma, row, s, g, nblk, acc);
             if (s + kWaves >= nsteps) break;
             const int s2 = s + 2 * kWaves < nsteps ? s + 2 * kWaves : s1;
-            load_step<F>(row, s2, lane, g, nblk, xp, xm, ra, xa_, ma);
+            load_step<F, kTiles>(row, s2, lane, g, nblk, xp, xm, ra, xa_, ma);
             asm volatile("" ::: "memory");
-            compute_step<F>(rb, xb_, mb, row, s1, g, nblk, acc);
+            compute_step<F, kTiles>(rb, xb_, mb, row, s1, g, nblk, acc);
         }
     }
     // lanes g and g + 2 hold the hi and lo parts of outputs n = 4g + i
@@ -400,7 +401,15 @@ hipError_t run_bgemm(const void *W, int64_t row_bytes, int64_t rows, int64_t col
                        reinterpret_cast<uint16_t *>(xm));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || rows == 0) return e;
-    hipLaunchKernelGGL(bgemm<F>, dim3(unsigned((rows + 16 * kTiles - 1) / (16 * kTiles))), dim3(64 * kWaves), 0, st,
+    if constexpr (std::is_same<F, BQ4K>::value) {
+        if (rows >= kTallRows) {
+            hipLaunchKernelGGL((bgemm<F, 4>), dim3(unsigned((rows + 63) / 64)), dim3(64 * kWaves), 0, st,
+                               static_cast<const uint8_t *>(W), row_bytes, int(rows), ns, int(nblk), xp, xm, Y, k,
+                               accumulate);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((bgemm<F, 2>), dim3(unsigned((rows + 31) / 32)), dim3(64 * kWaves), 0, st,
                        static_cast<const uint8_t *>(W), row_bytes, int(rows), ns, int(nblk), xp, xm, Y, k, accumulate);
     return hipGetLastError();
 }

@@ -89,6 +89,13 @@ def test_gemm_batch_rows_are_independent_of_k():
         assert np.array_equal(one[0], all8[n])
 
 
+def test_gemm_batch_q4_k_tall_matrix_layout():
+    # 16384 rows and more take four row tiles per wave: ragged last group,
+    # and the row count at the switch
+    _case(O.Q4_K, 16384 + 48, 512, 8, seed=31)
+    _case(O.Q4_K, 16384, 256, 3, seed=32)
+
+
 @pytest.mark.parametrize("t", [O.Q4_K, O.Q6_K], ids=["q4_k", "q6_k"])
 def test_gemm_batch_70b_projection_shape(t):
     """8192 x 8192 with k = 8, every output against the oracle."""
