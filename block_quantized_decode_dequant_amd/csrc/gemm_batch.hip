@@ -324,8 +324,12 @@ template <class F, int kTiles>
 __global__ void __launch_bounds__(64 * kWaves) bgemm(const uint8_t *__restrict__ W, int64_t row_bytes, int rows,
                                                       int nsteps, int nblk, const uint32_t *__restrict__ xp,
                                                       const uint32_t *__restrict__ xm, float *__restrict__ Y,
-                                                      int k, int accumulate) {
+                                                      int k, int accumulate, float *__restrict__ partial) {
     __shared__ float part[kWaves][16 * kTiles][8];
+    // column split: workgroup row blockIdx.y takes steps [s_lo, s_hi) and,
+    // when there are several, writes its sums to partial[blockIdx.y][n][row]
+    const int nsplit = gridDim.y;
+    const int s_lo = int(int64_t(nsteps) * blockIdx.y / nsplit), s_hi = int(int64_t(nsteps) * (blockIdx.y + 1) / nsplit);
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, r = lane & 15, g = lane >> 4;
     const int64_t R0 = int64_t(blockIdx.x) * 16 * kTiles + r;
     // rows past the end read row 0 (in bounds); their results are not written
@@ -335,23 +339,23 @@ __global__ void __launch_bounds__(64 * kWaves) bgemm(const uint8_t *__restrict__
     f4 acc[kTiles];
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
-    if (wv < nsteps) {
+    if (s_lo + wv < s_hi) {
         // one step ahead, in two register sets used in turn: the loads of the
         // next step are in flight while this one is computed (a step past
         // the end re-loads the current one, from cache)
         typename F::Raw ra[kTiles], rb[kTiles];
         u32x4 xa_[8], xb_[8];
         u32x2 ma = {0u, 0u}, mb = {0u, 0u};
-        load_step<F, kTiles>(row, wv, lane, g, nblk, xp, xm, ra, xa_, ma);
-        for (int s = wv; s < nsteps; s += 2 * kWaves) {
-            const int s1 = s + kWaves < nsteps ? s + kWaves : s;
+        load_step<F, kTiles>(row, s_lo + wv, lane, g, nblk, xp, xm, ra, xa_, ma);
+        for (int s = s_lo + wv; s < s_hi; s += 2 * kWaves) {
+            const int s1 = s + kWaves < s_hi ? s + kWaves : s;
             load_step<F, kTiles>(row, s1, lane, g, nblk, xp, xm, rb, xb_, mb);
             // keeps the loads above ahead of the arithmetic (the scheduler
             // would otherwise sink them to their first use)
             asm volatile("" ::: "memory");
             compute_step<F, kTiles>(ra, xa_, ma, row, s, g, nblk, acc);
-            if (s + kWaves >= nsteps) break;
-            const int s2 = s + 2 * kWaves < nsteps ? s + 2 * kWaves : s1;
+            if (s + kWaves >= s_hi) break;
+            const int s2 = s + 2 * kWaves < s_hi ? s + 2 * kWaves : s1;
             load_step<F, kTiles>(row, s2, lane, g, nblk, xp, xm, ra, xa_, ma);
             asm volatile("" ::: "memory");
             compute_step<F, kTiles>(rb, xb_, mb, row, s1, g, nblk, acc);
@@ -373,10 +377,24 @@ __global__ void __launch_bounds__(64 * kWaves) bgemm(const uint8_t *__restrict__
             float v = 0.f;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) v += part[w][rr][n];
-            float *py = Y + n * int64_t(rows) + R2;
-            *py = accumulate ? *py + v : v;
+            if (nsplit > 1) {
+                partial[(int64_t(blockIdx.y) * k + n) * rows + R2] = v;
+            } else {
+                float *py = Y + n * int64_t(rows) + R2;
+                *py = accumulate ? *py + v : v;
+            }
         }
     }
+}
+
+// Y[n][r] (+)= sum over splits, in split order, of partial[split][n][r].
+__global__ void __launch_bounds__(256) bgemm_reduce(const float *__restrict__ partial, int nsplit, int k, int rows,
+                                                    float *__restrict__ Y, int accumulate) {
+    const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= int64_t(k) * rows) return;
+    float v = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) v += partial[int64_t(sp) * k * rows + t];
+    Y[t] = accumulate ? Y[t] + v : v;
 }
 
 }  // namespace
@@ -385,9 +403,24 @@ int64_t bgemm_steps(int64_t cols) { return (cols + 255) / 256; }
 
 bool gemm_batch_type_ok(nt_qtype t) { return t == NT_Q8_0 || t == NT_Q4_K || t == NT_Q6_K; }
 
+// fp32 partial sums of a column-split launch: at most 8 vectors x 65536
+// (split, row) pairs
+constexpr int64_t kPartialFloats = 8 * 65536;
+
 size_t gemm_batch_workspace_bytes(nt_qtype t, int64_t cols) {
     const int64_t ns = bgemm_steps(cols);
-    return size_t(ns) * 8192 + (t == NT_Q4_K ? size_t(ns) * 512 : 0);
+    return size_t(ns) * 8192 + (t == NT_Q4_K ? size_t(ns) * 512 : 0) + size_t(kPartialFloats) * 4;
+}
+
+// Column splits for a matrix whose row groups alone give fewer than 256
+// workgroups: about 512 workgroups in all, at least one step per wave, and
+// within the partial-sum area.
+int bgemm_splits(int64_t groups, int ns, int64_t rows) {
+    if (groups >= 256) return 1;
+    int64_t sp = (512 + groups - 1) / groups;
+    sp = std::min<int64_t>(sp, std::max(1, ns / kWaves));
+    sp = std::min<int64_t>(sp, 65536 / std::max<int64_t>(rows, 1));
+    return int(std::max<int64_t>(sp, 1));
 }
 
 template <class F>
@@ -396,6 +429,8 @@ hipError_t run_bgemm(const void *W, int64_t row_bytes, int64_t rows, int64_t col
     const int ns = int(bgemm_steps(cols));
     uint32_t *xp = static_cast<uint32_t *>(ws);
     uint32_t *xm = F::kMin ? xp + int64_t(ns) * 2048 : nullptr;
+    float *partial = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + int64_t(ns) * 8192 +
+                                               (F::kMin ? int64_t(ns) * 512 : 0));
     const int64_t nt = int64_t(ns) * (F::kMin ? 1024 + 256 : 1024);
     hipLaunchKernelGGL(bgemm_prep<F>, dim3(unsigned((nt + 255) / 256)), dim3(256), 0, st, X, cols, k, ns, xp,
                        reinterpret_cast<uint16_t *>(xm));
@@ -405,12 +440,20 @@ hipError_t run_bgemm(const void *W, int64_t row_bytes, int64_t rows, int64_t col
         if (rows >= kTallRows) {
             hipLaunchKernelGGL((bgemm<F, 4>), dim3(unsigned((rows + 63) / 64)), dim3(64 * kWaves), 0, st,
                                static_cast<const uint8_t *>(W), row_bytes, int(rows), ns, int(nblk), xp, xm, Y, k,
-                               accumulate);
+                               accumulate, partial);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((bgemm<F, 2>), dim3(unsigned((rows + 31) / 32)), dim3(64 * kWaves), 0, st,
-                       static_cast<const uint8_t *>(W), row_bytes, int(rows), ns, int(nblk), xp, xm, Y, k, accumulate);
+    const int64_t groups = (rows + 31) / 32;
+    const int sp = bgemm_splits(groups, ns, rows);
+    hipLaunchKernelGGL((bgemm<F, 2>), dim3(unsigned(groups), unsigned(sp)), dim3(64 * kWaves), 0, st,
+                       static_cast<const uint8_t *>(W), row_bytes, int(rows), ns, int(nblk), xp, xm, Y, k, accumulate,
+                       partial);
+    if (sp == 1) return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t nt2 = int64_t(k) * rows;
+    hipLaunchKernelGGL(bgemm_reduce, dim3(unsigned((nt2 + 255) / 256)), dim3(256), 0, st, partial, sp, k, int(rows),
+                       Y, accumulate);
     return hipGetLastError();
 }
 

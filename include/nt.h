@@ -161,9 +161,12 @@ nt_status nt_gemv_swiglu(nt_qtype t, const void *W_gate, const void *W_up, int64
  * NT_Q6_K (others: NT_EINVAL); cols a whole number of blocks, at most 65536;
  * rows below 2^31.  The products run on the matrix cores with each x split
  * into two fp16 parts (about 2^-22 relative error per element; |x| must stay
- * below 65504); weights are not rounded.  workspace: device memory of at
- * least nt_gemm_batch_workspace_bytes(t, cols), 16-byte aligned, used only
- * during the call (stream order).  W, X and the workspace 16-byte aligned, Y
+ * below 65504); weights are not rounded.  Matrices with few rows are split
+ * over columns as well, with the partial sums added in a fixed order by a
+ * second kernel (results are deterministic).  workspace: device memory of at
+ * least nt_gemm_batch_workspace_bytes(t, cols) (the split activations plus
+ * 2 MiB of partial sums), 16-byte aligned, used only during the call (stream
+ * order); calls that share a workspace must not overlap.  W, X and the workspace 16-byte aligned, Y
  * 4-byte aligned; Y must not overlap X, W or the workspace. */
 size_t nt_gemm_batch_workspace_bytes(nt_qtype t, int64_t cols);
 nt_status nt_gemm_batch(nt_qtype t, const void *W, const float *X, float *Y, int64_t rows, int64_t cols,

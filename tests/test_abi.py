@@ -75,7 +75,7 @@ def test_gemv_argument_errors():
     assert _gemv(nt.Q6_K, A, A, A, 4, 256) == nt.NT_ENODEV   # valid, but no GPU here
 
 
-def _batch(t, W, X, Y, rows, cols, k, ws=A, ws_bytes=1 << 20):
+def _batch(t, W, X, Y, rows, cols, k, ws=A, ws_bytes=4 << 20):
     return nt.lib().nt_gemm_batch(t, C.c_void_p(W), C.c_void_p(X), C.c_void_p(Y), rows, cols, k, 0,
                                   C.c_void_p(ws), ws_bytes, None)
 
@@ -83,8 +83,9 @@ def _batch(t, W, X, Y, rows, cols, k, ws=A, ws_bytes=1 << 20):
 @no_gpu_only
 def test_gemm_batch_argument_errors():
     wsb = nt.nt_gemm_batch_workspace_bytes
-    assert wsb(nt.Q4_K, 8192) == 32 * (8192 + 512) and wsb(nt.Q6_K, 8192) == 32 * 8192
-    assert wsb(nt.Q8_0, 33 * 32) == 5 * 8192            # a partial last 256-column step
+    part = 8 * 65536 * 4                                # column-split partial sums
+    assert wsb(nt.Q4_K, 8192) == 32 * (8192 + 512) + part and wsb(nt.Q6_K, 8192) == 32 * 8192 + part
+    assert wsb(nt.Q8_0, 33 * 32) == 5 * 8192 + part     # a partial last 256-column step
     assert wsb(nt.Q4_0, 256) == 0 and wsb(nt.Q4_K, 100) == 0 and wsb(nt.Q4_K, 65536 + 256) == 0
     assert _batch(nt.Q4_K, A, A, A, 4, 256, 0) == nt.NT_EINVAL
     assert _batch(nt.Q4_K, A, A, A, 4, 256, 9) == nt.NT_EINVAL
@@ -99,7 +100,7 @@ def test_gemm_batch_argument_errors():
     assert _batch(nt.Q4_K, A, A + 4, A, 4, 256, 2) == nt.NT_EALIGN
     assert _batch(nt.Q4_K, A, A, A + 2, 4, 256, 2) == nt.NT_EALIGN
     assert _batch(nt.Q4_K, A, A, A, 4, 256, 2, ws=A + 8) == nt.NT_EALIGN
-    assert _batch(nt.Q4_K, A, A, A, 4, 256, 2, ws_bytes=8192) == nt.NT_ENOMEM
+    assert _batch(nt.Q4_K, A, A, A, 4, 256, 2, ws_bytes=wsb(nt.Q4_K, 256) - 4) == nt.NT_ENOMEM
     assert _batch(nt.Q4_K, 0, 0, 0, 0, 256, 2, ws=0) == nt.NT_OK          # nothing to do
     assert _batch(nt.Q6_K, A, A, A + 4, 4, 256, 8) == nt.NT_ENODEV        # valid, but no GPU here
 
