@@ -45,10 +45,7 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t w2 __attribute__((ext_vector_type(2)));
 
-#ifndef NT_BG_WAVES
-#define NT_BG_WAVES 4
-#endif
-constexpr int kWaves = NT_BG_WAVES;   // waves of a workgroup (they split the columns)
+constexpr int kWaves = 4;   // waves of a workgroup (they split the columns)
 // 16-row tiles of a wave (they share the activation loads): 2, or 4 for
 // Q4_K matrices of at least kTallRows rows (enough workgroups to fill the
 // chip; fewer activation bytes per weight byte)
@@ -415,6 +412,8 @@ size_t gemm_batch_workspace_bytes(nt_qtype t, int64_t cols) {
 // Column splits for a matrix whose row groups alone give fewer than 256
 // workgroups: about 512 workgroups in all, at least one step per wave, and
 // within the partial-sum area.
+// (Splitting 8192-row matrices as well, to 1024 workgroups, made them slower:
+// Q4_K 8192x8192 at k = 8 25 -> 34 us.)
 int bgemm_splits(int64_t groups, int ns, int64_t rows) {
     if (groups >= 256) return 1;
     int64_t sp = (512 + groups - 1) / groups;
