@@ -241,7 +241,7 @@ size_t nt_gemm_batch_workspace_bytes(nt_qtype t, int64_t cols) {
 nt_status nt_gemm_batch(nt_qtype t, const void *W, const float *X, float *Y, int64_t rows, int64_t cols,
                         int32_t k, int32_t accumulate, void *workspace, size_t workspace_bytes, nt_stream stream) {
     set_error("");
-    if (!gemm_batch_type_ok(t)) return fail(NT_EINVAL, "nt_gemm_batch: type not taken (Q8_0, Q4_K, Q6_K)");
+    if (!gemm_batch_type_ok(t)) return fail(NT_EINVAL, "nt_gemm_batch: not a block-quantized type");
     if (k < 1 || k > 8) return fail(NT_EINVAL, "nt_gemm_batch: k must be 1..8");
     if (rows < 0 || cols <= 0) return fail(NT_EINVAL, "nt_gemm_batch: rows < 0 or cols <= 0");
     if (cols % block_elems(t) != 0) return fail(NT_ESHAPE, "nt_gemm_batch: cols not a whole number of blocks");

@@ -176,6 +176,92 @@ struct BQ4K {
     }
 };
 
+// ---- Q4_0: a step is 8 blocks of 18 bytes; lane group g takes code bytes
+// 4g..4g+3 of a block (one word at a 2-byte-aligned offset, loaded as two
+// aligned words as for Q8_0): MFMA 2bb holds its low nibbles (values
+// 4g + perm4(i)), MFMA 2bb + 1 its high nibbles (16 + 4g + perm4(i)).  Codes
+// become q - 8 exactly.
+struct BQ40 {
+    static constexpr bool kMin = false;
+    struct Raw { uint32_t lo[8], hi[8], d[8]; };
+    __host__ __device__ static int elem(int m, int g, int i) { return 32 * (m >> 1) + 16 * (m & 1) + 4 * g + perm4(i); }
+    __device__ static void load(const uint8_t *row, int s, int g, int nblk, Raw &r) {
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb) {
+            const int blk = 8 * s + bb;
+            const uint8_t *b = row + int64_t(blk < nblk ? blk : 0) * 18;
+            const uint32_t bs = uint32_t(reinterpret_cast<uintptr_t>(b) & 3);   // 0 or 2
+            const uint32_t sh = bs ^ 2;                                        // (b + 2) & 3
+            const uint8_t *a = b + 2 + 4 * g - sh;
+            r.lo[bb] = ld1(a);
+            r.hi[bb] = ld1(a + (sh ? 4 : 0));
+            r.d[bb] = ld1(b - bs);
+        }
+    }
+    __device__ static h4 nib(uint32_t w) {   // bits 0-3 of each byte: q - 8 as fp16, bytes 0,2 then 1,3
+        const uint32_t a = hadd((w & 0x000f000fu) | 0x64006400u, _Float16(-1032.f));
+        const uint32_t b = hadd(((w >> 8) & 0x000f000fu) | 0x64006400u, _Float16(-1032.f));
+        return pack(a, b);
+    }
+    __device__ static void compute(const Raw &r, const uint8_t *row, int s, int nblk, const h4 *xa, h4, f4 &acc) {
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb) {
+            const int blk = 8 * s + bb;
+            const bool live = blk < nblk;
+            const uint8_t *b = row + int64_t(live ? blk : 0) * 18;
+            const uint32_t bs = uint32_t(reinterpret_cast<uintptr_t>(b) & 3);
+            const uint32_t w = funnel(r.hi[bb], r.lo[bb], shift_sel(bs ^ 2));
+            const float d = live ? h2f(r.d[bb] >> (8 * bs)) : 0.f;
+            f4 c = mfma(xa[2 * bb], nib(w), f4{0.f, 0.f, 0.f, 0.f});
+            c = mfma(xa[2 * bb + 1], nib(w >> 4), c);
+            acc += d * c;
+        }
+    }
+};
+
+// ---- Q5_K: as Q4_K (same lanes, same MFMA order, scales folded into the
+// codes, one more MFMA for the mins) with the fifth bit of value 32j + l in
+// bit j of qh[l]: a lane's qh bytes are 8g..8g+7, like its code bytes.
+// S q <= 63 * 31 = 1953 keeps S q 2^-14 exact in fp16.
+struct BQ5K {
+    static constexpr bool kMin = true;
+    struct Raw { u32x4 h; u32x2 qh; u32x2 q[4]; };
+    __host__ __device__ static int elem(int m, int g, int i) { return BQ4K::elem(m, g, i); }
+    __device__ static void load(const uint8_t *row, int s, int g, int, Raw &r) {
+        const uint8_t *b = row + int64_t(s) * 176;
+        r.h = ld4(b);
+        r.qh = *reinterpret_cast<const u32x2 *>(b + 16 + 8 * g);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) r.q[p] = *reinterpret_cast<const u32x2 *>(b + 48 + 32 * p + 8 * g);
+    }
+    __device__ static void compute(const Raw &r, int g, const h4 *xa, h4 xm, f4 &acc) {
+        f4 c = {0.f, 0.f, 0.f, 0.f};
+        uint32_t Mw[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            uint32_t S0, M0, S1, M1;
+            BQ4K::scale_min(r.h, 2 * p, S0, M0);
+            BQ4K::scale_min(r.h, 2 * p + 1, S1, M1);
+            const _Float16 f0 = _Float16(float(S0 * 1024u)), f1 = _Float16(float(S1 * 1024u));
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const uint32_t w = r.q[p][j], hb = r.qh[j];
+                const uint32_t q0 = (w & 0x0f0f0f0fu) | (((hb >> (2 * p)) & 0x01010101u) << 4);
+                const uint32_t q1 = ((w >> 4) & 0x0f0f0f0fu) | (((hb >> (2 * p + 1)) & 0x01010101u) << 4);
+                c = mfma(xa[4 * p + j], pack(hmul(q0 & 0x001f001fu, f0), hmul((q0 >> 8) & 0x001f001fu, f0)), c);
+                c = mfma(xa[4 * p + 2 + j], pack(hmul(q1 & 0x001f001fu, f1), hmul((q1 >> 8) & 0x001f001fu, f1)), c);
+            }
+            Mw[p] = M0 | (M1 << 16);
+        }
+        const uint32_t ma = (g & 1) ? Mw[2] : Mw[0], mc = (g & 1) ? Mw[3] : Mw[1];
+        const h4 mb = {_Float16(float(ma & 0xffffu)), _Float16(float(ma >> 16)), _Float16(float(mc & 0xffffu)),
+                       _Float16(float(mc >> 16))};
+        const f4 cm = mfma(xm, mb, f4{0.f, 0.f, 0.f, 0.f});
+        const float d = h2f(r.h.x) * 16384.f, dmin = h2f(r.h.x >> 16);
+        acc += d * c - dmin * cm;
+    }
+};
+
 // ---- Q6_K: a step is one super-block (210 bytes, so only 2-byte aligned).
 // MFMA m = 8h + 2k + lh is the 16-value scale group scales[m]: values
 // 128h + 32k + 16lh + 4g + perm4(i); the low four bits come from
@@ -311,8 +397,9 @@ __device__ __forceinline__ void compute_step(const typename F::Raw (&r)[kTiles],
     }
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
-        if constexpr (std::is_same<F, BQ80>::value) F::compute(r[t], row[t], s, nblk, xa, h4{}, acc[t]);
-        else if constexpr (std::is_same<F, BQ4K>::value) F::compute(r[t], g, xa, pack(xmr.x, xmr.y), acc[t]);
+        if constexpr (std::is_same<F, BQ80>::value || std::is_same<F, BQ40>::value)
+            F::compute(r[t], row[t], s, nblk, xa, h4{}, acc[t]);
+        else if constexpr (F::kMin) F::compute(r[t], g, xa, pack(xmr.x, xmr.y), acc[t]);
         else F::compute(r[t], row[t], s, xa, acc[t]);
     }
 }
@@ -398,7 +485,9 @@ __global__ void __launch_bounds__(256) bgemm_reduce(const float *__restrict__ pa
 
 int64_t bgemm_steps(int64_t cols) { return (cols + 255) / 256; }
 
-bool gemm_batch_type_ok(nt_qtype t) { return t == NT_Q8_0 || t == NT_Q4_K || t == NT_Q6_K; }
+bool gemm_batch_type_ok(nt_qtype t) {
+    return t == NT_Q8_0 || t == NT_Q4_0 || t == NT_Q4_K || t == NT_Q5_K || t == NT_Q6_K;
+}
 
 // fp32 partial sums of a column-split launch: at most 8 vectors x 65536
 // (split, row) pairs
@@ -406,7 +495,8 @@ constexpr int64_t kPartialFloats = 8 * 65536;
 
 size_t gemm_batch_workspace_bytes(nt_qtype t, int64_t cols) {
     const int64_t ns = bgemm_steps(cols);
-    return size_t(ns) * 8192 + (t == NT_Q4_K ? size_t(ns) * 512 : 0) + size_t(kPartialFloats) * 4;
+    const bool mins = t == NT_Q4_K || t == NT_Q5_K;
+    return size_t(ns) * 8192 + (mins ? size_t(ns) * 512 : 0) + size_t(kPartialFloats) * 4;
 }
 
 // Column splits for a matrix whose row groups alone give fewer than 256
@@ -461,6 +551,8 @@ hipError_t launch_gemm_batch(nt_qtype t, const void *W, int64_t rows, int64_t co
     const int64_t nblk = cols / block_elems(t), row_bytes = nblk * block_bytes(t);
     switch (t) {
     case NT_Q8_0: return run_bgemm<BQ80>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);
+    case NT_Q4_0: return run_bgemm<BQ40>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);
+    case NT_Q5_K: return run_bgemm<BQ5K>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);
     case NT_Q4_K: return run_bgemm<BQ4K>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);
     case NT_Q6_K: return run_bgemm<BQ6K>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);
     default: return hipErrorInvalidValue;

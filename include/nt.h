@@ -157,8 +157,8 @@ nt_status nt_gemv_swiglu(nt_qtype t, const void *W_gate, const void *W_up, int64
  * Y_n[r] = (Y_n[r] +) sum_c W[r, c] * X_n[c] for n in [0, k), r in [0, rows),
  * 1 <= k <= 8: every weight is read once for the k vectors.  X is k vectors of
  * cols fp32 back to back (X_n at X + n * cols), Y is k vectors of rows fp32
- * (Y_n at Y + n * rows); W is as for nt_gemv.  Types: NT_Q8_0, NT_Q4_K and
- * NT_Q6_K (others: NT_EINVAL); cols a whole number of blocks, at most 65536;
+ * (Y_n at Y + n * rows); W is as for nt_gemv.  Types: the five block
+ * formats (others: NT_EINVAL); cols a whole number of blocks, at most 65536;
  * rows below 2^31.  The products run on the matrix cores with each x split
  * into two fp16 parts (about 2^-22 relative error per element; |x| must stay
  * below 65504); weights are not rounded.  Matrices with few rows are split

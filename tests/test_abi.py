@@ -86,11 +86,13 @@ def test_gemm_batch_argument_errors():
     part = 8 * 65536 * 4                                # column-split partial sums
     assert wsb(nt.Q4_K, 8192) == 32 * (8192 + 512) + part and wsb(nt.Q6_K, 8192) == 32 * 8192 + part
     assert wsb(nt.Q8_0, 33 * 32) == 5 * 8192 + part     # a partial last 256-column step
-    assert wsb(nt.Q4_0, 256) == 0 and wsb(nt.Q4_K, 100) == 0 and wsb(nt.Q4_K, 65536 + 256) == 0
+    assert wsb(nt.Q5_K, 256) == 8192 + 512 + part and wsb(nt.Q4_0, 320) == 2 * 8192 + part
+    assert wsb(nt.F32, 256) == 0 and wsb(nt.Q4_K, 100) == 0 and wsb(nt.Q4_K, 65536 + 256) == 0
     assert _batch(nt.Q4_K, A, A, A, 4, 256, 0) == nt.NT_EINVAL
     assert _batch(nt.Q4_K, A, A, A, 4, 256, 9) == nt.NT_EINVAL
-    assert _batch(nt.Q4_0, A, A, A, 4, 256, 2) == nt.NT_EINVAL
-    assert _batch(nt.Q5_K, A, A, A, 4, 256, 2) == nt.NT_EINVAL
+    assert _batch(nt.F32, A, A, A, 4, 256, 2) == nt.NT_EINVAL
+    assert _batch(nt.F16, A, A, A, 4, 256, 2) == nt.NT_EINVAL
+    assert _batch(nt.Q4_0, A, A, A, 4, 96, 2) == nt.NT_ENODEV           # valid (3 blocks), but no GPU here
     assert _batch(nt.Q4_K, A, A, A, 4, 100, 2) == nt.NT_ESHAPE
     assert _batch(nt.Q8_0, A, A, A, 4, 65536 + 32, 2) == nt.NT_ESHAPE
     assert _batch(nt.Q4_K, A, A, A, -1, 256, 2) == nt.NT_EINVAL

@@ -5,7 +5,7 @@ fp64 oracle, one oracle GEMV per vector.
 Bar: elementwise within 1e-4 + 2e-3 |y|, as for the GEMV (the activations'
 fp16 hi/lo split leaves about 2^-22 relative error per element, far inside
 it).  Shapes span one tile, ragged row tiles, a partial 256-column step
-(Q8_0), every k from 1 to 8, the widest rows the call takes, and the full
+(Q8_0, Q4_0), column-split launches (few rows), every k from 1 to 8, the widest rows the call takes, and the full
 8192 x 8192 70B projection shape.
 """
 import numpy as np
@@ -19,8 +19,8 @@ from .gpu_util import assert_close, device, host, to_dev
 
 pytestmark = pytest.mark.gpu
 
-TYPES = [O.Q8_0, O.Q4_K, O.Q6_K]
-TID = ["q8_0", "q4_k", "q6_k"]
+TYPES = [O.Q8_0, O.Q4_0, O.Q4_K, O.Q5_K, O.Q6_K]
+TID = ["q8_0", "q4_0", "q4_k", "q5_k", "q6_k"]
 GUARD = 12345.0
 
 
@@ -68,12 +68,13 @@ def test_gemm_batch_accumulate(t):
     _case(t, 77, 3072, 6, seed=9, accumulate=True)
 
 
-def test_gemm_batch_q8_0_partial_step_and_odd_blocks():
+@pytest.mark.parametrize("t", [O.Q8_0, O.Q4_0], ids=["q8_0", "q4_0"])
+def test_gemm_batch_partial_step_and_odd_blocks(t):
     # 33 and 13 blocks per row: the last 256-column step is partial and rows
     # start at 2-byte offsets
-    _case(O.Q8_0, 19, 33 * 32, 8, seed=3)
-    _case(O.Q8_0, 50, 13 * 32, 3, seed=4)
-    _case(O.Q8_0, 7, 32, 2, seed=5)
+    _case(t, 19, 33 * 32, 8, seed=3)
+    _case(t, 50, 13 * 32, 3, seed=4)
+    _case(t, 7, 32, 2, seed=5)
 
 
 def test_gemm_batch_rows_are_independent_of_k():
@@ -111,7 +112,7 @@ def test_gemm_batch_70b_projection_shape(t):
 
 def test_gemm_batch_rejects_bad_arguments():
     dev = device()
-    W = torch.zeros(144 * 4, dtype=torch.uint8, device=dev)
+    W = torch.zeros(4 * 1024, dtype=torch.uint8, device=dev)    # room for 4 F32 rows of 256
     X = torch.zeros(9 * 256, dtype=torch.float32, device=dev)
     Y = torch.zeros(9 * 4, dtype=torch.float32, device=dev)
     ws = torch.empty(nt.nt_gemm_batch_workspace_bytes(O.Q4_K, 256), dtype=torch.uint8, device=dev)
@@ -119,7 +120,7 @@ def test_gemm_batch_rejects_bad_arguments():
         with pytest.raises(nt.NTError):
             nt.nt_gemm_batch(O.Q4_K, W, X, Y, 4, 256, k, ws)
     with pytest.raises(nt.NTError):
-        nt.nt_gemm_batch(O.Q4_0, W, X, Y, 4, 256, 2, ws)
+        nt.nt_gemm_batch(nt.F32, W, X, Y, 4, 256, 2, ws)
     with pytest.raises(nt.NTError) as e:
         nt.nt_gemm_batch(O.Q4_K, W, X, Y, 4, 256, 2, ws[:-16])
     assert e.value.status == nt.NT_ENOMEM
