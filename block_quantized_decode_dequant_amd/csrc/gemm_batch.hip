@@ -12,9 +12,10 @@
 //    tile, K 16 codes of one scale group (or of one super-block whose scales
 //    are folded into the codes).  With N = weight row, every lane applies the
 //    scales of its own row to its own accumulators.
-//  * weight codes become fp16 exactly: small integers, or (Q4_K) the integer
-//    S_j * q scaled by 2^-14, built from the nibble as an fp16 subnormal times
-//    an exact fp16 scale.  Nothing about the weights is rounded.
+//  * weight codes become fp16 exactly: small integers, or (Q4_K, Q5_K) the
+//    integer S_j * q scaled by 2^-14, built from the code as an fp16
+//    subnormal times an exact fp16 scale.  Nothing about the weights is
+//    rounded.
 //  * each activation is split into fp16 hi + lo (hi = fp16(x), lo =
 //    fp16(x - hi)), which leaves about 2^-22 relative error; the hi parts fill
 //    M rows 0-7 and the lo parts rows 8-15, which the padding of k <= 8 to 16
