@@ -21,8 +21,8 @@
 //    M rows 0-7 and the lo parts rows 8-15, which the padding of k <= 8 to 16
 //    would otherwise waste.  Products are exact in fp32; the MFMA sums in fp32.
 //  * a prologue kernel writes the split activations once per call in the
-//    order the lanes consume them, so each wave reads 128 contiguous bytes
-//    per lane per 256 columns.
+//    order the lanes consume them: each of a wave's eight 16-byte loads per
+//    256 columns reads one contiguous kilobyte.
 //  * MFMA lane layout (16x16x16 f16): src0 lane l holds A[l % 16][4(l/16) + i],
 //    src1 lane l holds B[4(l/16) + i][l % 16], the result lane l holds
 //    D[4(l/16) + i][l % 16], i = 0..3.  Inside one MFMA the order of the 16
@@ -320,7 +320,7 @@ struct BQ6K {
     }
 };
 
-// Split activations in lane order: xp[((s * 64 + lane) * 16 + m) * 4 + i]
+// Split activations in lane order: xp[(((s * 8 + m / 2) * 64 + lane) * 2 + m % 2) * 4 + i]
 // (fp16) = hi or lo part of x_n[256 s + elem(m, g, i)], n = lane % 8,
 // lo for lane % 16 >= 8, zero for n >= k or past cols.  For K-quant mins,
 // xm[(s * 64 + lane) * 4 + i]: K slot 4g + i of lane (b, g) is the hi (slots
@@ -350,8 +350,10 @@ __global__ void __launch_bounds__(256) bgemm_prep(const float *__restrict__ X, i
             const float v = (n < k && e < cols) ? X[n * cols + e] : 0.f;
             hv[i] = split_part(v, lo);
         }
-        xp[2 * t] = hv[0] | (hv[1] << 16);
-        xp[2 * t + 1] = hv[2] | (hv[3] << 16);
+        // MFMA pair m / 2 of every lane of a step is one contiguous 1 KB run
+        const int64_t o = ((s * 8 + (m >> 1)) * 64 + lane) * 4 + (m & 1) * 2;
+        xp[o] = hv[0] | (hv[1] << 16);
+        xp[o + 1] = hv[2] | (hv[3] << 16);
         return;
     }
     if constexpr (F::kMin) {
@@ -378,9 +380,9 @@ template <class F, int kTiles>
 __device__ __forceinline__ void load_step(const uint8_t *const (&row)[kTiles], int s, int lane, int g, int nblk,
                                           const uint32_t *__restrict__ xp, const uint32_t *__restrict__ xm,
                                           typename F::Raw (&r)[kTiles], u32x4 (&xr)[8], u32x2 &xmr) {
-    const u32x4 *px = reinterpret_cast<const u32x4 *>(xp) + (int64_t(s) * 64 + lane) * 8;
+    const u32x4 *px = reinterpret_cast<const u32x4 *>(xp) + int64_t(s) * 512 + lane;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) xr[q] = px[q];
+    for (int q = 0; q < 8; ++q) xr[q] = px[64 * q];
     if constexpr (F::kMin) xmr = *reinterpret_cast<const u32x2 *>(xm + (int64_t(s) * 64 + lane) * 2);
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) F::load(row[t], s, g, nblk, r[t]);
