@@ -119,25 +119,29 @@ struct BQ80 {
     }
 };
 
-// ---- Q4_K: a step is one super-block; lane group g takes bytes 8g..8g+7 of
-// each 32-byte pair chunk p (low nibbles: sub-block 2p, high: 2p+1).  MFMA
-// m = 4p + 2*nib + j uses dword j of chunk p.  The codes carry their 6-bit
-// scale: (q * 2^-24 or q * 2^-20 as an fp16 subnormal) * fp16(S * 2^10 or
-// S * 2^6) = S q 2^-14 exactly (S q <= 945).  The mins go through one more
-// MFMA: A = per-sub-block activation sums (hi in K slots 0-7, lo in 8-15),
-// B = M_j.
+// ---- Q4_K: a step is one super-block.  The 6-bit scales are folded into
+// the codes: (q * 2^-24 or q * 2^-20 as an fp16 subnormal) * fp16(S * 2^10
+// or S * 2^6) = S q 2^-14 exactly (S q <= 945), so one MFMA chain covers the
+// whole super-block and any value may sit in any K slot.  Lane group g takes
+// code bytes [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16), so each load
+// instruction reads 64 contiguous bytes of a row.  MFMA m uses word m / 2 of
+// those eight (low nibbles for even m, high for odd); code byte c holds
+// values 32 (2 (c / 32)) + c % 32 (low) and 32 (2 (c / 32) + 1) + c % 32
+// (high).  The mins go through one more MFMA: A = per-sub-block activation
+// sums (hi in K slots 0-7, lo in 8-15), B = M_j.
 struct BQ4K {
     static constexpr bool kMin = true;
-    struct Raw { u32x4 h; u32x2 q[4]; };
+    struct Raw { u32x4 h, q0, q1; };
+    __host__ __device__ static int code_byte(int w, int g) { return w < 4 ? 16 * g + 4 * w : 64 + 16 * g + 4 * (w - 4); }
     __host__ __device__ static int elem(int m, int g, int i) {
-        const int p = m >> 2, nib = (m >> 1) & 1, j = m & 1;
-        return 32 * (2 * p + nib) + 8 * g + 4 * j + perm4(i);
+        const int c = code_byte(m >> 1, g) + perm4(i);
+        return 32 * (2 * (c >> 5) + (m & 1)) + (c & 31);
     }
     __device__ static void load(const uint8_t *row, int s, int g, int, Raw &r) {
         const uint8_t *b = row + int64_t(s) * 144;
         r.h = ld4(b);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) r.q[p] = *reinterpret_cast<const u32x2 *>(b + 16 + 32 * p + 8 * g);
+        r.q0 = ld4(b + 16 + 16 * g);
+        r.q1 = ld4(b + 80 + 16 * g);
     }
     __device__ static void scale_min(const u32x4 &h, int j, uint32_t &S, uint32_t &M) {
         const uint32_t sc[3] = {h.y, h.z, h.w};
@@ -151,26 +155,28 @@ struct BQ4K {
         }
     }
     __device__ static void compute(const Raw &r, int g, const h4 *xa, h4 xm, f4 &acc) {
+        uint32_t S[8], M[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) scale_min(r.h, j, S[j], M[j]);
+        // the two code pairs of this lane: chunks g / 2 (bytes 16g..) and 2 + g / 2 (bytes 64 + 16g..)
+        const int hp = g >> 1;
+        const uint32_t Sa0 = hp ? S[2] : S[0], Sa1 = hp ? S[3] : S[1];
+        const uint32_t Sb0 = hp ? S[6] : S[4], Sb1 = hp ? S[7] : S[5];
+        const _Float16 fa0 = _Float16(float(Sa0 * 1024u)), fa1 = _Float16(float(Sa1 * 64u));
+        const _Float16 fb0 = _Float16(float(Sb0 * 1024u)), fb1 = _Float16(float(Sb1 * 64u));
+        const uint32_t words[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
         f4 c = {0.f, 0.f, 0.f, 0.f};
-        uint32_t Mw[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            uint32_t S0, M0, S1, M1;
-            scale_min(r.h, 2 * p, S0, M0);
-            scale_min(r.h, 2 * p + 1, S1, M1);
-            const _Float16 f0 = _Float16(float(S0 * 1024u)), f1 = _Float16(float(S1 * 64u));
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const uint32_t w = r.q[p][j], t = w >> 8;
-                c = mfma(xa[4 * p + j], pack(hmul(w & 0x000f000fu, f0), hmul(t & 0x000f000fu, f0)), c);
-                c = mfma(xa[4 * p + 2 + j], pack(hmul(w & 0x00f000f0u, f1), hmul(t & 0x00f000f0u, f1)), c);
-            }
-            Mw[p] = M0 | (M1 << 16);
+        for (int w = 0; w < 8; ++w) {
+            const uint32_t v = words[w], t = v >> 8;
+            const _Float16 f0 = w < 4 ? fa0 : fb0, f1 = w < 4 ? fa1 : fb1;
+            c = mfma(xa[2 * w], pack(hmul(v & 0x000f000fu, f0), hmul(t & 0x000f000fu, f0)), c);
+            c = mfma(xa[2 * w + 1], pack(hmul(v & 0x00f000f0u, f1), hmul(t & 0x00f000f0u, f1)), c);
         }
         // B of the min MFMA: K slot 4g + i takes M_{(4g + i) & 7}
-        const uint32_t ma = (g & 1) ? Mw[2] : Mw[0], mc = (g & 1) ? Mw[3] : Mw[1];
-        const h4 mb = {_Float16(float(ma & 0xffffu)), _Float16(float(ma >> 16)), _Float16(float(mc & 0xffffu)),
-                       _Float16(float(mc >> 16))};
+        const int jb = 4 * (g & 1);
+        const uint32_t m0 = jb ? M[4] : M[0], m1 = jb ? M[5] : M[1], m2 = jb ? M[6] : M[2], m3 = jb ? M[7] : M[3];
+        const h4 mb = {_Float16(float(m0)), _Float16(float(m1)), _Float16(float(m2)), _Float16(float(m3))};
         const f4 cm = mfma(xm, mb, f4{0.f, 0.f, 0.f, 0.f});
         const float d = h2f(r.h.x) * 16384.f, dmin = h2f(r.h.x >> 16);
         acc += d * c - dmin * cm;
@@ -220,14 +226,19 @@ struct BQ40 {
     }
 };
 
-// ---- Q5_K: as Q4_K (same lanes, same MFMA order, scales folded into the
-// codes, one more MFMA for the mins) with the fifth bit of value 32j + l in
-// bit j of qh[l]: a lane's qh bytes are 8g..8g+7, like its code bytes.
+// ---- Q5_K: as Q4_K (scales folded into the codes, one more MFMA for the
+// mins) with the fifth bit of value 32j + l in bit j of qh[l].  Lane group g
+// takes bytes 8g..8g+7 of each 32-byte code chunk and the same qh bytes.
 // S q <= 63 * 31 = 1953 keeps S q 2^-14 exact in fp16.
 struct BQ5K {
     static constexpr bool kMin = true;
     struct Raw { u32x4 h; u32x2 qh; u32x2 q[4]; };
-    __host__ __device__ static int elem(int m, int g, int i) { return BQ4K::elem(m, g, i); }
+    // value of MFMA m = 4p + 2 nib + j, slot i of lane group g: bytes 8g..8g+7
+    // of code chunk p (and of qh), dword j, low (nib 0) or high nibbles
+    __host__ __device__ static int elem(int m, int g, int i) {
+        const int p = m >> 2, nib = (m >> 1) & 1, j = m & 1;
+        return 32 * (2 * p + nib) + 8 * g + 4 * j + perm4(i);
+    }
     __device__ static void load(const uint8_t *row, int s, int g, int, Raw &r) {
         const uint8_t *b = row + int64_t(s) * 176;
         r.h = ld4(b);
