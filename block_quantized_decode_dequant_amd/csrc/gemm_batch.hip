@@ -226,48 +226,45 @@ struct BQ40 {
     }
 };
 
-// ---- Q5_K: as Q4_K (scales folded into the codes, one more MFMA for the
-// mins) with the fifth bit of value 32j + l in bit j of qh[l].  Lane group g
-// takes bytes 8g..8g+7 of each 32-byte code chunk and the same qh bytes.
+// ---- Q5_K: as Q4_K (same lanes and K slots, scales folded into the
+// codes, one more MFMA for the mins) with the fifth bit of value 32j + l in
+// bit j of qh[l].  A lane's code bytes c all have c % 32 in
+// [16 (g % 2), 16 (g % 2) + 16), so one 16-byte piece of qh serves them.
 // S q <= 63 * 31 = 1953 keeps S q 2^-14 exact in fp16.
 struct BQ5K {
     static constexpr bool kMin = true;
-    struct Raw { u32x4 h; u32x2 qh; u32x2 q[4]; };
-    // value of MFMA m = 4p + 2 nib + j, slot i of lane group g: bytes 8g..8g+7
-    // of code chunk p (and of qh), dword j, low (nib 0) or high nibbles
-    __host__ __device__ static int elem(int m, int g, int i) {
-        const int p = m >> 2, nib = (m >> 1) & 1, j = m & 1;
-        return 32 * (2 * p + nib) + 8 * g + 4 * j + perm4(i);
-    }
+    struct Raw { u32x4 h, qh, q0, q1; };
+    __host__ __device__ static int elem(int m, int g, int i) { return BQ4K::elem(m, g, i); }
     __device__ static void load(const uint8_t *row, int s, int g, int, Raw &r) {
         const uint8_t *b = row + int64_t(s) * 176;
         r.h = ld4(b);
-        r.qh = *reinterpret_cast<const u32x2 *>(b + 16 + 8 * g);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) r.q[p] = *reinterpret_cast<const u32x2 *>(b + 48 + 32 * p + 8 * g);
+        r.qh = ld4(b + 16 + 16 * (g & 1));
+        r.q0 = ld4(b + 48 + 16 * g);
+        r.q1 = ld4(b + 112 + 16 * g);
     }
     __device__ static void compute(const Raw &r, int g, const h4 *xa, h4 xm, f4 &acc) {
+        uint32_t S[8], M[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) BQ4K::scale_min(r.h, j, S[j], M[j]);
+        const int hp = g >> 1;
+        const uint32_t words[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
+        const uint32_t hw[4] = {r.qh.x, r.qh.y, r.qh.z, r.qh.w};
         f4 c = {0.f, 0.f, 0.f, 0.f};
-        uint32_t Mw[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            uint32_t S0, M0, S1, M1;
-            BQ4K::scale_min(r.h, 2 * p, S0, M0);
-            BQ4K::scale_min(r.h, 2 * p + 1, S1, M1);
+        for (int w = 0; w < 8; ++w) {
+            const int p = w < 4 ? hp : 2 + hp;                 // code chunk: sub-blocks 2p, 2p + 1
+            const uint32_t S0 = (w < 4 ? (hp ? S[2] : S[0]) : (hp ? S[6] : S[4]));
+            const uint32_t S1 = (w < 4 ? (hp ? S[3] : S[1]) : (hp ? S[7] : S[5]));
             const _Float16 f0 = _Float16(float(S0 * 1024u)), f1 = _Float16(float(S1 * 1024u));
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const uint32_t w = r.q[p][j], hb = r.qh[j];
-                const uint32_t q0 = (w & 0x0f0f0f0fu) | (((hb >> (2 * p)) & 0x01010101u) << 4);
-                const uint32_t q1 = ((w >> 4) & 0x0f0f0f0fu) | (((hb >> (2 * p + 1)) & 0x01010101u) << 4);
-                c = mfma(xa[4 * p + j], pack(hmul(q0 & 0x001f001fu, f0), hmul((q0 >> 8) & 0x001f001fu, f0)), c);
-                c = mfma(xa[4 * p + 2 + j], pack(hmul(q1 & 0x001f001fu, f1), hmul((q1 >> 8) & 0x001f001fu, f1)), c);
-            }
-            Mw[p] = M0 | (M1 << 16);
+            const uint32_t v = words[w], hb = hw[w & 3];
+            const uint32_t q0 = (v & 0x0f0f0f0fu) | (((hb >> (2 * p)) & 0x01010101u) << 4);
+            const uint32_t q1 = ((v >> 4) & 0x0f0f0f0fu) | (((hb >> (2 * p + 1)) & 0x01010101u) << 4);
+            c = mfma(xa[2 * w], pack(hmul(q0 & 0x001f001fu, f0), hmul((q0 >> 8) & 0x001f001fu, f0)), c);
+            c = mfma(xa[2 * w + 1], pack(hmul(q1 & 0x001f001fu, f1), hmul((q1 >> 8) & 0x001f001fu, f1)), c);
         }
-        const uint32_t ma = (g & 1) ? Mw[2] : Mw[0], mc = (g & 1) ? Mw[3] : Mw[1];
-        const h4 mb = {_Float16(float(ma & 0xffffu)), _Float16(float(ma >> 16)), _Float16(float(mc & 0xffffu)),
-                       _Float16(float(mc >> 16))};
+        const int jb = 4 * (g & 1);
+        const uint32_t m0 = jb ? M[4] : M[0], m1 = jb ? M[5] : M[1], m2 = jb ? M[6] : M[2], m3 = jb ? M[7] : M[3];
+        const h4 mb = {_Float16(float(m0)), _Float16(float(m1)), _Float16(float(m2)), _Float16(float(m3))};
         const f4 cm = mfma(xm, mb, f4{0.f, 0.f, 0.f, 0.f});
         const float d = h2f(r.h.x) * 16384.f, dmin = h2f(r.h.x >> 16);
         acc += d * c - dmin * cm;
@@ -275,59 +272,66 @@ struct BQ5K {
 };
 
 // ---- Q6_K: a step is one super-block (210 bytes, so only 2-byte aligned).
-// MFMA m = 8h + 2k + lh is the 16-value scale group scales[m]: values
-// 128h + 32k + 16lh + 4g + perm4(i); the low four bits come from
-// ql[64h + 32(k&1) + 16lh + 4g + i] (nibble k>>1), the top two from
-// qh[32h + 16lh + 4g + i] (bits 2k, 2k+1).  Codes become q - 32 exactly.
-// Each needed word is one aligned 8-byte load (it stays inside the
-// super-block for every offset used) and a byte funnel.
+// Value (h, k, l) = 128h + 32k + l has code q = ql4 + 16 qh2 (ql4: nibble
+// k / 2 of ql[64h + 32 (k % 2) + l], qh2: bits 2k, 2k + 1 of qh[32h + l]) and
+// scale sc = scales[8h + 2k + l / 16]; q - 32 = ql4 + 16 (qh2 - 2), and both
+// sc * ql4 (<= 1920) and 16 sc (qh2 - 2) (16 times an integer <= 256) are
+// exact in fp16, so the scales fold into the codes: two MFMAs per operand
+// (one per part) cover any mix of scale groups and d is applied once.  Lane
+// group g takes ql bytes [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16) (each
+// load reads 64 contiguous bytes of a row), the qh bytes of the same values
+// ([16 (g % 2), + 16) of each 32-byte half) and scale bytes g, g + 4,
+// g + 8, g + 12.  Every 16-byte piece is two aligned loads and a funnel.
 struct BQ6K {
     static constexpr bool kMin = false;
-    struct Raw { u32x2 ql[2][2][2], qh[2][2]; u32x4 sw; uint32_t tail; };
+    struct Raw { u32x4 v[5]; uint32_t e[5], dw; };   // ql pieces 0, 1, qh pieces 0, 1, scales; next words; d
     __host__ __device__ static int elem(int m, int g, int i) {
-        const int h = m >> 3, k = (m >> 1) & 3, lh = m & 1;
-        return 128 * h + 32 * k + 16 * lh + 4 * g + perm4(i);
+        const int c = BQ4K::code_byte(m >> 1, g) + perm4(i);
+        return 128 * (c >> 6) + 32 * (((c >> 5) & 1) + 2 * (m & 1)) + (c & 31);
     }
     __device__ static void load(const uint8_t *row, int s, int g, int, Raw &r) {
         const uint8_t *b = row + int64_t(s) * 210;
         const uint32_t sh = uint32_t(reinterpret_cast<uintptr_t>(b) & 2);
         const uint8_t *a = b - sh;
+        const int off[5] = {16 * g, 64 + 16 * g, 128 + 16 * (g & 1), 160 + 16 * (g & 1), 192};
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int lh = 0; lh < 2; ++lh) {
-                r.ql[h][0][lh] = *reinterpret_cast<const u32x2 *>(a + 64 * h + 16 * lh + 4 * g);
-                r.ql[h][1][lh] = *reinterpret_cast<const u32x2 *>(a + 64 * h + 32 + 16 * lh + 4 * g);
-                r.qh[h][lh] = *reinterpret_cast<const u32x2 *>(a + 128 + 32 * h + 16 * lh + 4 * g);
-            }
-        // 16 int8 scales and d: words at 192 - sh .. 208 - sh
-        r.sw = ld4(a + 192);
-        r.tail = ld1(a + 208);
+        for (int t = 0; t < 5; ++t) {
+            r.v[t] = ld4(a + off[t]);
+            r.e[t] = ld1(a + off[t] + (sh ? 16 : 12));     // with sh == 0 the last word again
+        }
+        r.dw = ld1(a + 208);                                 // d: bytes 208, 209
     }
-    __device__ static h4 codes(uint32_t lo4, uint32_t qh, int k) {
-        const uint32_t q = lo4 | (((qh >> (2 * k)) & 0x03030303u) << 4);
-        const uint32_t a = hadd((q & 0x00ff00ffu) | 0x64006400u, _Float16(-1056.f));
-        const uint32_t b = hadd(((q >> 8) & 0x00ff00ffu) | 0x64006400u, _Float16(-1056.f));
-        return pack(a, b);
-    }
-    __device__ static void compute(const Raw &r, const uint8_t *row, int s, const h4 *xa, f4 &acc) {
+    __device__ static void compute(const Raw &r, const uint8_t *row, int s, int g, const h4 *xa, f4 &acc) {
         const uint32_t sh = uint32_t(reinterpret_cast<uintptr_t>(row + int64_t(s) * 210) & 2);
         const uint32_t sel = shift_sel(sh);
-        auto fw = [&](const u32x2 &v) { return funnel(v.y, v.x, sel); };
-        const uint32_t sc[4] = {funnel(r.sw.y, r.sw.x, sel), funnel(r.sw.z, r.sw.y, sel),
-                                funnel(r.sw.w, r.sw.z, sel), funnel(r.tail, r.sw.w, sel)};
-        const float d = h2f(sh ? r.tail >> 16 : r.tail);
-        f4 t = {0.f, 0.f, 0.f, 0.f};
+        uint32_t w[5][4];
+#pragma unroll
+        for (int t = 0; t < 5; ++t) {
+            w[t][0] = funnel(r.v[t].y, r.v[t].x, sel);
+            w[t][1] = funnel(r.v[t].z, r.v[t].y, sel);
+            w[t][2] = funnel(r.v[t].w, r.v[t].z, sel);
+            w[t][3] = funnel(r.e[t], r.v[t].w, sel);
+        }
+        const float d = h2f(sh ? r.dw >> 16 : r.dw);
+        const uint32_t kk2 = 2 * uint32_t(g >> 1);          // qh bit of k = g / 2 (+4 for the high nibbles)
+        f4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
-            const int h = m >> 3, k = (m >> 1) & 3, lh = m & 1;
-            const uint32_t l = fw(r.ql[h][k & 1][lh]);
-            const uint32_t lo4 = (k < 2 ? l : l >> 4) & 0x0f0f0f0fu;
-            const f4 c = mfma(xa[m], codes(lo4, fw(r.qh[h][lh]), k), f4{0.f, 0.f, 0.f, 0.f});
-            const float scm = float(int8_t((sc[m >> 2] >> (8 * (m & 3))) & 0xffu));
-            t += scm * c;
+            const int wi = m >> 1, nib = m & 1, half = wi >> 2;
+            const uint32_t v = w[half][wi & 3], hb = w[2 + half][wi & 3];
+            const int scw = nib + 2 * half;                 // scale groups g + 4 nib + 8 half: byte g of word scw
+            const float sc = float(int8_t((w[4][scw] >> (8 * g)) & 0xffu));
+            const _Float16 f = _Float16(sc), f16x = _Float16(16.f * sc);
+            const uint32_t ql4 = (nib ? v >> 4 : v) & 0x0f0f0f0fu;
+            const uint32_t qh2 = (hb >> (kk2 + 4 * nib)) & 0x03030303u;
+            const h4 b1 = pack(hmul(hadd((ql4 & 0x00ff00ffu) | 0x64006400u, _Float16(-1024.f)), f),
+                               hmul(hadd(((ql4 >> 8) & 0x00ff00ffu) | 0x64006400u, _Float16(-1024.f)), f));
+            const h4 b2 = pack(hmul(hadd((qh2 & 0x00ff00ffu) | 0x64006400u, _Float16(-1026.f)), f16x),
+                               hmul(hadd(((qh2 >> 8) & 0x00ff00ffu) | 0x64006400u, _Float16(-1026.f)), f16x));
+            c = mfma(xa[m], b1, c);
+            c = mfma(xa[m], b2, c);
         }
-        acc += d * t;
+        acc += d * c;
     }
 };
 
@@ -414,7 +418,7 @@ __device__ __forceinline__ void compute_step(const typename F::Raw (&r)[kTiles],
         if constexpr (std::is_same<F, BQ80>::value || std::is_same<F, BQ40>::value)
             F::compute(r[t], row[t], s, nblk, xa, h4{}, acc[t]);
         else if constexpr (F::kMin) F::compute(r[t], g, xa, pack(xmr.x, xmr.y), acc[t]);
-        else F::compute(r[t], row[t], s, xa, acc[t]);
+        else F::compute(r[t], row[t], s, g, xa, acc[t]);
     }
 }
 
