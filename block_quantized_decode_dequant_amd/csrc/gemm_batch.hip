@@ -9,13 +9,13 @@
 // products run on the matrix cores (v_mfma_f32_16x16x16_f16):
 //
 //  * the MFMA's M dimension holds the activations, N the 16 weight rows of a
-//    tile, K 16 codes of one scale group (or of one super-block whose scales
-//    are folded into the codes).  With N = weight row, every lane applies the
+//    tile, K 16 codes of one scale group (Q8_0, Q4_0) or any 16 codes of a
+//    super-block whose scales are folded into the codes (K-quants).  With N = weight row, every lane applies the
 //    scales of its own row to its own accumulators.
-//  * weight codes become fp16 exactly: small integers, or (Q4_K, Q5_K) the
-//    integer S_j * q scaled by 2^-14, built from the code as an fp16
-//    subnormal times an exact fp16 scale.  Nothing about the weights is
-//    rounded.
+//  * weight codes become fp16 exactly: small integers, or with the scales
+//    folded in (Q4_K, Q5_K: S_j * q * 2^-14; Q6_K: sc * ql4 and
+//    16 sc (qh2 - 2), the two parts of its code, in two MFMAs).  Nothing
+//    about the weights is rounded.
 //  * each activation is split into fp16 hi + lo (hi = fp16(x), lo =
 //    fp16(x - hi)), which leaves about 2^-22 relative error; the hi parts fill
 //    M rows 0-7 and the lo parts rows 8-15, which the padding of k <= 8 to 16
