@@ -358,13 +358,15 @@ __global__ void __launch_bounds__(256) bgemm_prep(const float *__restrict__ X, i
         const int64_t s = t >> 10;
         const int b = lane & 15, g = lane >> 4, n = b & 7;
         const bool lo = b >= 8;
+        // the four values are x[e0 + perm4(i)] for a 4-aligned e0 in every
+        // format: one 16-byte load (cols is a multiple of 32)
+        const int64_t e0 = s * 256 + F::elem(m, g, 0);
+        const float4 v = (n < k && e0 < cols) ? *reinterpret_cast<const float4 *>(X + n * cols + e0)
+                                              : float4{0.f, 0.f, 0.f, 0.f};
+        const float vv[4] = {v.x, v.y, v.z, v.w};
         uint32_t hv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t e = s * 256 + F::elem(m, g, i);
-            const float v = (n < k && e < cols) ? X[n * cols + e] : 0.f;
-            hv[i] = split_part(v, lo);
-        }
+        for (int i = 0; i < 4; ++i) hv[i] = split_part(vv[perm4(i)], lo);
         // MFMA pair m / 2 of every lane of a step is one contiguous 1 KB run
         const int64_t o = ((s * 8 + (m >> 1)) * 64 + lane) * 4 + (m & 1) * 2;
         xp[o] = hv[0] | (hv[1] << 16);
