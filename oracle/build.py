@@ -1,6 +1,6 @@
 """Builds the oracle's C sources into oracle/liboracle.so with gcc.
 
-Test infrastructure: the checker is compiled so tests and the CPU baseline can
+Test infrastructure: the oracle is compiled so tests and the CPU baseline can
 call it; the product library never links it.
 """
 from __future__ import annotations
