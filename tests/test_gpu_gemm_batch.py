@@ -5,8 +5,9 @@ fp64 oracle, one oracle GEMV per vector.
 Bar: elementwise within 1e-4 + 2e-3 |y|, as for the GEMV (the activations'
 fp16 hi/lo split leaves about 2^-22 relative error per element, far inside
 it).  Shapes span one tile, ragged row tiles, a partial 256-column step
-(Q8_0, Q4_0), column-split launches (few rows), every k from 1 to 8, the widest rows the call takes, and the full
-8192 x 8192 70B projection shape.
+(Q8_0, Q4_0), column-split launches (few rows), every k from 1 to 8, the
+widest rows the call takes, the full 8192 x 8192 70B projection shape, and
+sampled rows of the two FFN shapes.
 """
 import numpy as np
 import pytest
@@ -108,6 +109,24 @@ def test_gemm_batch_70b_projection_shape(t):
     ref = O.gemm_batch(t, W, rows, cols, X)
     for n in range(8):
         assert_close(got[n], ref[n], what=f"gemm_batch {t} {rows}x{cols} vector {n}")
+
+
+@pytest.mark.parametrize("t,si", [(O.Q4_K, 2), (O.Q6_K, 3)], ids=["q4_k-28672x8192", "q6_k-8192x28672"])
+def test_gemm_batch_70b_ffn_shapes_sampled(t, si):
+    """The FFN projection shapes the benchmark times (the four-tile launch
+    for Q4_K 28672 x 8192, 112 column steps for Q6_K 8192 x 28672) at k = 8:
+    the first and last 64 rows and 448 random rows against the oracle."""
+    rows, cols = workloads.KQ_SHAPES[si]
+    w = synth.normal_f32(workloads.SEED, workloads.kq_w_stream(si), rows * cols, std=0.02)
+    W = O.quantize(t, w)
+    del w
+    X = np.stack([synth.activation(workloads.SEED, workloads.kq_x_stream(si) + 100 * n, cols) for n in range(8)])
+    got = _run(t, W, X, rows, cols, 8)
+    rng = np.random.default_rng(si)
+    ids = np.unique(np.concatenate([np.arange(64), rng.choice(rows, 448, replace=False), np.arange(rows - 64, rows)]))
+    for n in range(8):
+        ref = O.gemv_rows(t, W, rows, cols, X[n], ids)
+        assert_close(got[n][ids], ref, what=f"gemm_batch {t} {rows}x{cols} vector {n} (sampled rows)")
 
 
 def test_gemm_batch_rejects_bad_arguments():
