@@ -69,28 +69,26 @@ __device__ __forceinline__ f4 mfma(h4 a, h4 b, f4 c) { return __builtin_amdgcn_m
 // a Raw of registers (no use of the data), compute() turns a loaded Raw into
 // MFMAs, so the main loop can keep the next step's loads in flight.
 
-// ---- Q8_0: a step is 8 blocks; MFMA m covers block m/2, elements
-// 8g + 4(m&1) + perm4(i) for lane group g.  The 8 code bytes of a lane sit at
-// a 2-byte-aligned offset: two aligned loads (8 + 4 bytes; with a word-aligned
-// start the second re-reads the last word, so nothing wholly past the block
-// is touched) and a byte funnel.  Blocks past the end of a row (a partial
-// last step) load block 0 of the row and get scale 0.
+// ---- Q8_0: a step is 8 blocks; MFMA m covers block m/2, values
+// 8g + 4(m&1) + perm4(i) for lane group g.  A block starts 2-byte aligned
+// (bs = its address mod 4, 0 or 2); each lane loads the 12 bytes at the
+// word-aligned address b - bs + 8g, which hold its 8 code bytes (from byte
+// 2 + bs of the load) and, in lane group 0, the block's d (bytes bs, bs + 1),
+// handed to the row's other lanes by a lane permute.  The load ends at most
+// at byte 36 - bs of the block, inside the word that holds its last bytes.
+// Blocks past the end of a row (a partial last step) load block 0 of the row
+// and get scale 0.
 struct BQ80 {
     static constexpr bool kMin = false;
-    struct Raw { u32x2 a[8]; uint32_t c[8], d[8]; };
+    struct Raw { u32x3 v[8]; };
     __host__ __device__ static int elem(int m, int g, int i) { return 32 * (m >> 1) + 8 * g + 4 * (m & 1) + perm4(i); }
     __device__ static void load(const uint8_t *row, int s, int g, int nblk, Raw &r) {
 #pragma unroll
         for (int bb = 0; bb < 8; ++bb) {
             const int blk = 8 * s + bb;
-            const bool live = blk < nblk;
-            const uint8_t *b = row + int64_t(live ? blk : 0) * 34;
+            const uint8_t *b = row + int64_t(blk < nblk ? blk : 0) * 34;
             const uint32_t bs = uint32_t(reinterpret_cast<uintptr_t>(b) & 3);   // 0 or 2
-            const uint8_t *p = b + 2 + 8 * g;
-            const uint32_t sh = bs ^ 2;                                        // (b + 2) & 3
-            r.a[bb] = *reinterpret_cast<const u32x2 *>(p - sh);
-            r.c[bb] = ld1(p - sh + (sh ? 8 : 4));
-            r.d[bb] = ld1(b - bs);
+            r.v[bb] = ld3(b - bs + 8 * g);
         }
     }
     // int8 codes of a word -> two fp16 pairs q (bytes 0,2 and 1,3): 0x64uu is
@@ -101,17 +99,19 @@ struct BQ80 {
         return pack(a, b);
     }
     __device__ static void compute(const Raw &r, const uint8_t *row, int s, int nblk, const h4 *xa, h4, f4 &acc) {
+        const int src = int(__lane_id() & 15);          // lane group 0 of this row
+        const uint32_t sel2 = shift_sel(2);
 #pragma unroll
         for (int bb = 0; bb < 8; ++bb) {
             const int blk = 8 * s + bb;
             const bool live = blk < nblk;
             const uint8_t *b = row + int64_t(live ? blk : 0) * 34;
             const uint32_t bs = uint32_t(reinterpret_cast<uintptr_t>(b) & 3);
-            const uint32_t sh = bs ^ 2;
-            const uint32_t sel = shift_sel(sh);
-            const uint32_t w0 = funnel(r.a[bb].y, r.a[bb].x, sel);
-            const uint32_t w1 = funnel(sh ? r.c[bb] : r.a[bb].y, r.a[bb].y, sel);
-            const float d = live ? h2f(r.d[bb] >> (8 * bs)) : 0.f;
+            const u32x3 v = r.v[bb];
+            const uint32_t w0 = bs ? v.y : funnel(v.y, v.x, sel2);
+            const uint32_t w1 = bs ? v.z : funnel(v.z, v.y, sel2);
+            const uint32_t dw = uint32_t(__shfl(int(v.x), src, 64));
+            const float d = live ? h2f(bs ? dw >> 16 : dw) : 0.f;
             f4 c = mfma(xa[2 * bb], codes(w0), f4{0.f, 0.f, 0.f, 0.f});
             c = mfma(xa[2 * bb + 1], codes(w1), c);
             acc += d * c;

@@ -166,8 +166,9 @@ nt_status nt_gemv_swiglu(nt_qtype t, const void *W_gate, const void *W_up, int64
  * second kernel (results are deterministic).  workspace: device memory of at
  * least nt_gemm_batch_workspace_bytes(t, cols) (the split activations plus
  * 2 MiB of partial sums), 16-byte aligned, used only during the call (stream
- * order); calls that share a workspace must not overlap.  W, X and the workspace 16-byte aligned, Y
- * 4-byte aligned; Y must not overlap X, W or the workspace. */
+ * order); calls that share a workspace must not overlap.  W, X and the
+ * workspace 16-byte aligned, Y 4-byte aligned; Y must not overlap X, W or
+ * the workspace. */
 size_t nt_gemm_batch_workspace_bytes(nt_qtype t, int64_t cols);
 nt_status nt_gemm_batch(nt_qtype t, const void *W, const float *X, float *Y, int64_t rows, int64_t cols,
                         int32_t k, int32_t accumulate, void *workspace, size_t workspace_bytes, nt_stream stream);
