@@ -184,13 +184,15 @@ struct BQ4K {
 };
 
 // ---- Q4_0: a step is 8 blocks of 18 bytes; lane group g takes code bytes
-// 4g..4g+3 of a block (one word at a 2-byte-aligned offset, loaded as two
-// aligned words as for Q8_0): MFMA 2bb holds its low nibbles (values
-// 4g + perm4(i)), MFMA 2bb + 1 its high nibbles (16 + 4g + perm4(i)).  Codes
-// become q - 8 exactly.
+// 4g..4g+3 of a block: MFMA 2bb holds their low nibbles (values
+// 4g + perm4(i)), MFMA 2bb + 1 their high nibbles (16 + 4g + perm4(i)).
+// Codes become q - 8 exactly.  As for Q8_0, each lane loads 8 bytes from the
+// word-aligned address b - bs + 4g (its code bytes from byte 2 + bs; d in
+// lane group 0, permuted to the others); the load ends at most at byte
+// 20 - bs of the block, inside the word that holds its last bytes.
 struct BQ40 {
     static constexpr bool kMin = false;
-    struct Raw { uint32_t lo[8], hi[8], d[8]; };
+    struct Raw { u32x2 v[8]; };
     __host__ __device__ static int elem(int m, int g, int i) { return 32 * (m >> 1) + 16 * (m & 1) + 4 * g + perm4(i); }
     __device__ static void load(const uint8_t *row, int s, int g, int nblk, Raw &r) {
 #pragma unroll
@@ -198,11 +200,7 @@ struct BQ40 {
             const int blk = 8 * s + bb;
             const uint8_t *b = row + int64_t(blk < nblk ? blk : 0) * 18;
             const uint32_t bs = uint32_t(reinterpret_cast<uintptr_t>(b) & 3);   // 0 or 2
-            const uint32_t sh = bs ^ 2;                                        // (b + 2) & 3
-            const uint8_t *a = b + 2 + 4 * g - sh;
-            r.lo[bb] = ld1(a);
-            r.hi[bb] = ld1(a + (sh ? 4 : 0));
-            r.d[bb] = ld1(b - bs);
+            r.v[bb] = *reinterpret_cast<const u32x2 *>(b - bs + 4 * g);
         }
     }
     __device__ static h4 nib(uint32_t w) {   // bits 0-3 of each byte: q - 8 as fp16, bytes 0,2 then 1,3
@@ -211,14 +209,18 @@ struct BQ40 {
         return pack(a, b);
     }
     __device__ static void compute(const Raw &r, const uint8_t *row, int s, int nblk, const h4 *xa, h4, f4 &acc) {
+        const int src = int(__lane_id() & 15);          // lane group 0 of this row
+        const uint32_t sel2 = shift_sel(2);
 #pragma unroll
         for (int bb = 0; bb < 8; ++bb) {
             const int blk = 8 * s + bb;
             const bool live = blk < nblk;
             const uint8_t *b = row + int64_t(live ? blk : 0) * 18;
             const uint32_t bs = uint32_t(reinterpret_cast<uintptr_t>(b) & 3);
-            const uint32_t w = funnel(r.hi[bb], r.lo[bb], shift_sel(bs ^ 2));
-            const float d = live ? h2f(r.d[bb] >> (8 * bs)) : 0.f;
+            const u32x2 v = r.v[bb];
+            const uint32_t w = bs ? v.y : funnel(v.y, v.x, sel2);
+            const uint32_t dw = uint32_t(__shfl(int(v.x), src, 64));
+            const float d = live ? h2f(bs ? dw >> 16 : dw) : 0.f;
             f4 c = mfma(xa[2 * bb], nib(w), f4{0.f, 0.f, 0.f, 0.f});
             c = mfma(xa[2 * bb + 1], nib(w >> 4), c);
             acc += d * c;
