@@ -18,8 +18,12 @@ def tiny_config(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64, 
 
 
 def _types(wtype):
-    """Per-tensor types: one type everywhere, or the mixed K-quant recipe
-    (Q6_K for attn_v, ffn_down and the output head, Q4_K elsewhere)."""
+    """Per-tensor types: one type everywhere, the mixed K-quant recipe
+    (Q6_K for attn_v, ffn_down and the output head, Q4_K elsewhere), or a
+    dict naming each tensor's type (keys tok, wq, wk, wv, wo, gate, up, down,
+    out)."""
+    if isinstance(wtype, dict):
+        return dict(wtype)
     if wtype == "mix":
         base = O.Q4_K
         return dict(tok=base, wq=base, wk=base, wv=O.Q6_K, wo=base, gate=base, up=base,

@@ -132,3 +132,83 @@ def test_step_rejects_out_of_range():
         dec.step(cfg.vocab, 0)
     with pytest.raises(ValueError):
         dec.step(0, cfg.ctx_cap)
+
+
+# A decode step read a second time, in numpy fp64 (tests/spec_np.py), on a
+# model whose every matrix, gain and cached value is non-zero: this pins the
+# parts the special cases above zero out -- the rotation of q, the stacking
+# of the attention and feed-forward blocks over several layers, and the
+# cache written by one step and read by the next.
+SPEC_TYPES = dict(tok=O.Q8_0, wq=O.Q8_0, wk=O.Q4_0, wv=O.Q6_K, wo=O.Q4_0, gate=O.Q8_0, up=O.Q6_K,
+                  down=O.Q4_0, out=O.Q6_K)
+
+
+def _spec_model(cfg, w, kk, vv):
+    from . import spec_np
+    qt = lambda q: (q.type, q.data)
+    weights = dict(tok_embd=qt(w.tok_embd), output=qt(w.output), output_norm=w.output_norm,
+                   layers=[dict(attn_norm=L.attn_norm, ffn_norm=L.ffn_norm,
+                                **{k: qt(getattr(L, k)) for k in ("wq", "wk", "wv", "wo", "w_gate", "w_up",
+                                                                   "w_down")}) for L in w.layers])
+    c = dict(n_layers=cfg.n_layers, hidden=cfg.hidden, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
+             head_dim=cfg.head_dim, ffn=cfg.ffn, vocab=cfg.vocab, ctx_cap=cfg.ctx_cap, rms_eps=cfg.rms_eps,
+             rope_theta=cfg.rope_theta)
+    return spec_np.SpecModel(c, weights, kk.view(np.float16), vv.view(np.float16))
+
+
+@pytest.mark.parametrize("n_q_heads,n_kv_heads", [(4, 2), (8, 2)])
+def test_decode_step_matches_an_independent_numpy_reading(n_q_heads, n_kv_heads):
+    cfg = tiny_config(n_layers=3, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, rope_theta=10000.0)
+    w = build_oracle_model(cfg, seed=8, wtype=SPEC_TYPES)
+    n_pos = 6
+    kk = np.stack([synth.kv_prefix_bits(8, l, 0, cfg.n_kv_heads, cfg.ctx_cap, cfg.head_dim, n_pos)
+                   for l in range(cfg.n_layers)])
+    vv = np.stack([synth.kv_prefix_bits(8, l, 1, cfg.n_kv_heads, cfg.ctx_cap, cfg.head_dim, n_pos)
+                   for l in range(cfg.n_layers)])
+    spec = _spec_model(cfg, w, kk, vv)
+    dec = O.Decoder(cfg, w, kk.copy(), vv.copy())
+    # every weight matrix has non-zero entries, every gain differs from 1
+    for L in w.layers:
+        assert np.any(L.attn_norm != 1) and np.any(L.ffn_norm != 1)
+        for k in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"):
+            assert np.count_nonzero(getattr(L, k).data) > 0
+    tok_o = tok_s = 5
+    for s in range(4):
+        ref, nxt_s = spec.step(tok_s, n_pos + s)
+        got, nxt_o = dec.step(tok_o, n_pos + s)
+        scale = np.abs(ref).max()
+        assert np.abs(got - ref).max() <= 1e-12 * scale, f"step {s}: {np.abs(got - ref).max() / scale:.2e}"
+        assert nxt_o == nxt_s, f"step {s}"
+        # the cache both wrote at slot pos holds the same fp16 values
+        assert np.array_equal(dec.kv_k[:, :, n_pos + s, :], spec.k[:, :, n_pos + s, :].view(np.uint16))
+        assert np.array_equal(dec.kv_v[:, :, n_pos + s, :], spec.v[:, :, n_pos + s, :].view(np.uint16))
+        tok_o, tok_s = nxt_o, nxt_s
+
+
+def test_spec_reading_sees_a_dropped_query_rotation():
+    """The numpy reading is sharp enough to catch the mistake the special
+    cases cannot: the same step without RoPE on q differs well beyond the
+    tolerance above."""
+    from . import spec_np
+    cfg = tiny_config(n_layers=2, rope_theta=10000.0)
+    w = build_oracle_model(cfg, seed=9, wtype=SPEC_TYPES)
+    n_pos = 6
+    kk = np.stack([synth.kv_prefix_bits(9, l, 0, cfg.n_kv_heads, cfg.ctx_cap, cfg.head_dim, n_pos)
+                   for l in range(cfg.n_layers)])
+    vv = np.stack([synth.kv_prefix_bits(9, l, 1, cfg.n_kv_heads, cfg.ctx_cap, cfg.head_dim, n_pos)
+                   for l in range(cfg.n_layers)])
+    dec = O.Decoder(cfg, w, kk.copy(), vv.copy())
+    got, _ = dec.step(5, n_pos)
+    spec = _spec_model(cfg, w, kk, vv)
+    rope = spec_np.rope
+    assert cfg.n_q_heads != cfg.n_kv_heads
+
+    def rope_k_only(v, n_heads, d, pos, theta):     # the q heads pass unrotated
+        return v if n_heads == cfg.n_q_heads else rope(v, n_heads, d, pos, theta)
+
+    spec_np.rope = rope_k_only
+    try:
+        bad, _ = spec.step(5, n_pos)
+    finally:
+        spec_np.rope = rope
+    assert np.abs(got - bad).max() > 1e-6 * np.abs(got).max()
