@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--decode", choices=["none", "8b", "70b", "all"], default="all",
                     help="decode measurements: none, the 8B-shaped model, the resident 70B-shaped model, "
                          "or all (8B, 70B, 70B streamed)")
@@ -76,6 +76,43 @@ def load_traffic(kernel: str):
     if rec.get("gemv_source_sha256_16") != kernel_source_hash():
         return None
     return rec.get("per_launch_bytes", {}).get(kernel)
+
+
+ONE_GIB = 1 << 30
+
+
+def copies_for(nbytes: int) -> int:
+    """Copies of a matrix so that consecutive reads of one copy are at least
+    1 GiB of reads apart (4x the 256 MB last-level cache)."""
+    return max(2, -(-ONE_GIB // nbytes) + 1)
+
+
+def time_rotated(torch, call, n_copies: int, steps: int, side) -> float:
+    """Mean microseconds per launch of call(copy): two HIP graphs of `steps`
+    launches each (a warm-up and a timed one) walk one continuous cyclic
+    sequence of copy indices, so two reads of one copy are always n_copies
+    launches apart, across the two replays too.  Events bracket the timed
+    replay on the stream the kernels run on."""
+    graphs = []
+    with torch.cuda.stream(side):
+        call(0)                                   # first use outside capture
+        for start in (0, steps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for i in range(start, start + steps):
+                    call(i % n_copies)
+            graphs.append(g)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(side):
+        graphs[0].replay()
+        a.record(side)
+        graphs[1].replay()
+        b.record(side)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / steps
+    del graphs
+    return us
 
 
 def build_sweep(nt, torch, dev, synth, workloads):
@@ -158,7 +195,7 @@ def run_gpu(args):
                     step(i)
         with torch.cuda.graph(g_timed, stream=side):
             for s_ in range(args.steps):
-                step(s_)
+                step(args.warmup + s_)            # continues the warm-up's copy rotation
     torch.cuda.synchronize()
     with torch.cuda.stream(side):
         if args.warmup > 0:
@@ -176,30 +213,22 @@ def run_gpu(args):
     value = step_bytes / (wall / args.steps) / 1e9
 
     # Per-kernel durations, measured live: each case launched back to back
-    # `steps` times (rotating weight copies) from a captured graph, one pair of
-    # events around its replay on the launch stream (no host work between the
-    # kernels).
-    case_graphs = []
-    with torch.cuda.stream(side):
-        for c in cases:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=side):
-                for s_ in range(args.steps):
-                    nt.nt_gemv(c["qt"], c["W"][s_ % copies], c["x"], c["y"], c["rows"], c["cols"])
-            case_graphs.append(g)
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in cases]
-    with torch.cuda.stream(side):
-        for g in case_graphs:
-            g.replay()
-        for j, g in enumerate(case_graphs):
-            ev[j][0].record(side)
-            g.replay()
-            ev[j][1].record(side)
-    torch.cuda.synchronize()
-    del case_graphs
-    per_case_ms = [ev[j][0].elapsed_time(ev[j][1]) / args.steps for j in range(len(cases))]
-    span_ms = ev[0][0].elapsed_time(ev[-1][1]) / args.steps
+    # `steps` times from a captured graph, one pair of events around the
+    # replay on the launch stream (no host work between the kernels).  Each
+    # case rotates copies of its own matrix sized so that two reads of one
+    # copy are at least 1 GiB of reads apart, so the last-level cache cannot
+    # serve them (the sweep's own copies are sized for the whole step).
+    per_case_ms = []
+    for c in cases:
+        n = copies_for(c["bytes"])
+        Ws = list(c["W"]) + [c["W"][0].clone() for _ in range(max(0, n - len(c["W"])))]
+        us = time_rotated(torch, lambda i: nt.nt_gemv(c["qt"], Ws[i], c["x"], c["y"], c["rows"], c["cols"]),
+                          n, args.steps, side)
+        per_case_ms.append(us * 1e-3)
+        c["case_copies"] = n
+        del Ws
+        torch.cuda.empty_cache()
+    case_sum_ms = sum(per_case_ms)
 
     # per-kernel totals; a kernel is one instantiation (block type, path, tile
     # rows), as the library reports it, which is what rocprofv3 lists by name
@@ -222,7 +251,7 @@ def run_gpu(args):
                 "avg_launch_us": round(d["ms"] / d["launches"] * 1e3, 3),
                 "read_ceiling": ceiling, "frac_of_read_ceiling": round(achieved / ceiling, 4)}
     detail = [dict(type=c["type"], rows=c["rows"], cols=c["cols"], bytes=c["bytes"],
-                   launch=nt.nt_gemv_launch_info(c["qt"], c["rows"], c["cols"]),
+                   launch=nt.nt_gemv_launch_info(c["qt"], c["rows"], c["cols"]), copies=c["case_copies"],
                    us=round(ms * 1e3, 3), gbs=round(c["bytes"] / (ms * 1e-3) / 1e9, 1),
                    frac=round(c["bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
               for c, ms in zip(cases, per_case_ms)]
@@ -231,7 +260,38 @@ def run_gpu(args):
         del c["W"]
     torch.cuda.empty_cache()
     return dict(value=value, ms_per_step=ms_per_step, roofline=roofline, detail=detail,
-                copies=copies, step_bytes=step_bytes, queued_step_ms=span_ms)
+                copies=copies, step_bytes=step_bytes, case_sum_ms=case_sum_ms)
+
+
+def q8_0_gemv(steps):
+    """The single Q8_0 GEMV workload, y = W x with W 4096 x 4096: int8 codes
+    uniform on [-127, 127], one fp16 scale |N(0,1)| * 0.01 per 32-value block,
+    x ~ N(0, 1), seed 0 (synth.q8_0_random_matrix, drawn on the host), timed
+    like the sweep's per-kernel times with copies >= 1 GiB apart.  Reported
+    beside the sweep, not part of `value`."""
+    import torch
+
+    from block_quantized_decode_dequant_amd import nt, synth, workloads
+
+    dev = torch.device("cuda:0")
+    wl = workloads.Q8_0_GEMV
+    rows, cols = wl["rows"], wl["cols"]
+    base = torch.from_numpy(synth.q8_0_random_matrix(workloads.SEED, rows, cols)).to(dev)
+    x = torch.from_numpy(synth.activation(workloads.SEED, synth.Q8_CFG_X, cols)).to(dev)
+    y = torch.empty(rows, dtype=torch.float32, device=dev)
+    nbytes = base.numel()
+    copies = copies_for(nbytes)
+    Ws = [base] + [base.clone() for _ in range(copies - 1)]
+    side = torch.cuda.Stream()
+    us = time_rotated(torch, lambda i: nt.nt_gemv(nt.Q8_0, Ws[i], x, y, rows, cols), copies, steps, side)
+    alg = gemv_bytes(nt.Q8_0, rows, cols, nt)
+    li = nt.nt_gemv_launch_info(nt.Q8_0, rows, cols)
+    out = {"workload": wl["name"], "rows": rows, "cols": cols, "bytes": alg, "copies": copies, "launch": li,
+           "us": round(us, 3), "gbs": round(alg / (us * 1e-6) / 1e9, 1),
+           "frac": round(alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    del Ws, base
+    torch.cuda.empty_cache()
+    return out
 
 
 def q5_k_gemv(steps):
@@ -255,29 +315,15 @@ def q5_k_gemv(steps):
         base = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         nt.nt_quantize(nt.Q5_K, w32, base, rows * cols)
         del w32
-        copies = max(2, -(-(1 << 30) // nbytes) + 1)
+        copies = copies_for(nbytes)
         Ws = [base] + [base.clone() for _ in range(copies - 1)]
         y = torch.empty(rows, dtype=torch.float32, device=dev)
         side = torch.cuda.Stream()
-        with torch.cuda.stream(side):
-            nt.nt_gemv(nt.Q5_K, Ws[0], x, y, rows, cols)
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=side):
-                for k in range(steps):
-                    nt.nt_gemv(nt.Q5_K, Ws[k % copies], x, y, rows, cols)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(side):
-            g.replay()
-            a.record(side)
-            g.replay()
-            b.record(side)
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / steps
+        us = time_rotated(torch, lambda i: nt.nt_gemv(nt.Q5_K, Ws[i], x, y, rows, cols), copies, steps, side)
         alg = nbytes + 4 * cols + 4 * rows
         out.append({"rows": rows, "cols": cols, "bytes": alg, "us": round(us, 3),
                     "gbs": round(alg / (us * 1e-6) / 1e9, 1), "frac": round(alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)})
-        del g, Ws, base
+        del Ws, base
         torch.cuda.empty_cache()
     return out
 
@@ -313,31 +359,14 @@ def verify_gemm(steps):
         base = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         nt.nt_quantize(t, w32, base, rows * cols)
         del w32
-        copies = max(2, -(-(1 << 30) // nbytes) + 1)
+        copies = copies_for(nbytes)
         Ws = [base] + [base.clone() for _ in range(copies - 1)]
         Y = torch.empty(k * rows, dtype=torch.float32, device=dev)
         ws = torch.empty(nt.nt_gemm_batch_workspace_bytes(t, cols), dtype=torch.uint8, device=dev)
         side = torch.cuda.Stream()
-
-        def timed(call):
-            with torch.cuda.stream(side):
-                call(0)
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=side):
-                    for i in range(steps):
-                        call(i)
-            torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            with torch.cuda.stream(side):
-                g.replay()
-                a.record(side)
-                g.replay()
-                b.record(side)
-            torch.cuda.synchronize()
-            return a.elapsed_time(b) * 1e3 / steps
-
-        us = timed(lambda i: nt.nt_gemm_batch(t, Ws[i % copies], X, Y, rows, cols, k, ws))
-        us1 = timed(lambda i: nt.nt_gemv(t, Ws[i % copies], X[:cols], Y[:rows], rows, cols))
+        us = time_rotated(torch, lambda i: nt.nt_gemm_batch(t, Ws[i], X, Y, rows, cols, k, ws), copies, steps, side)
+        us1 = time_rotated(torch, lambda i: nt.nt_gemv(t, Ws[i], X[:cols], Y[:rows], rows, cols), copies, steps,
+                           side)
         alg = nbytes + 4 * k * (cols + rows)
         out.append({"type": name, "rows": rows, "cols": cols, "k": k, "bytes": alg, "us": round(us, 3),
                     "gbs": round(alg / (us * 1e-6) / 1e9, 1), "frac": round(alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
@@ -474,14 +503,65 @@ def decode_streamed(shape, cap_bytes=24 << 30, n_tokens=3):
     return out
 
 
-def cpu_baseline(seconds: float):
-    """The oracle's fp64 GEMV on the first rows of every sweep matrix."""
+def host_cpu():
+    """CPU model name, logical CPUs the OS reports and CPUs this process may run on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return model, os.cpu_count() or 1, usable
+
+
+CPU_SHARE = 16      # host threads one single-GPU job may keep busy on the GPU machines
+
+
+def oracle_decode_token(threads: int):
+    """Seconds the oracle takes for one decode token of the Llama-3-8B-shaped
+    Q8_0 model (32 layers, full 128256-row head, attention over 1024 cached
+    positions).  The weights are all-zero Q8_0 blocks: the oracle decodes and
+    multiplies every block whatever its values, so its time per token does not
+    depend on them; the KV prefix is seeded N(0, 1) fp16."""
     import numpy as np
 
     import oracle as O
     from block_quantized_decode_dequant_amd import synth, workloads
 
-    cores = O.default_threads()
+    s = workloads.LLAMA_8B_Q8_0
+    H, D, F, V = s.hidden, s.head_dim, s.ffn, s.vocab
+    QD, KD = s.n_q_heads * D, s.n_kv_heads * D
+    z = lambda r, c: O.QTensor(O.Q8_0, np.zeros(r * O.row_bytes(O.Q8_0, c), np.uint8))
+    ones = np.ones(H, np.float32)
+    layers = [O.LayerWeights(attn_norm=ones, wq=z(QD, H), wk=z(KD, H), wv=z(KD, H), wo=z(H, QD), ffn_norm=ones,
+                             w_gate=z(F, H), w_up=z(F, H), w_down=z(H, F)) for _ in range(s.n_layers)]
+    w = O.ModelWeights(tok_embd=z(V, H), output_norm=ones, output=z(V, H), layers=layers)
+    cfg = O.Config(s.n_layers, H, s.n_q_heads, s.n_kv_heads, D, F, V, s.ctx_cap, s.rms_eps, s.rope_theta)
+    kk = np.stack([synth.kv_prefix_bits(0, l, 0, s.n_kv_heads, s.ctx_cap, D, s.ctx) for l in range(s.n_layers)])
+    vv = np.stack([synth.kv_prefix_bits(0, l, 1, s.n_kv_heads, s.ctx_cap, D, s.ctx) for l in range(s.n_layers)])
+    dec = O.Decoder(cfg, w, kk, vv)
+    t0 = time.perf_counter()
+    dec.step(1, s.ctx, nthreads=threads)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(seconds: float):
+    """The oracle's fp64 GEMV on the first rows of every sweep matrix, on
+    CPU_SHARE threads and on one core; and one oracle decode token of the
+    8B-shaped model on one core."""
+    import numpy as np
+
+    import oracle as O
+    from block_quantized_decode_dequant_amd import synth, workloads
+
+    model, n_logical, n_usable = host_cpu()
+    cores = min(CPU_SHARE, n_usable)
     sample_rows = 256
     work = []
     for si, (rows, cols) in enumerate(workloads.KQ_SHAPES):
@@ -492,6 +572,7 @@ def cpu_baseline(seconds: float):
             t = O.QTYPES[tname]
             blocks = O.quantize(t, w)
             work.append((t, blocks, r, cols, x, r * O.row_bytes(t, cols) + 4 * cols + 4 * r))
+
     def timed(nthreads, budget):
         done_bytes, t0, passes = 0, time.perf_counter(), 0
         while True:
@@ -505,11 +586,18 @@ def cpu_baseline(seconds: float):
 
     gbs, passes, el = timed(cores, seconds)
     gbs1, passes1, el1 = timed(1, max(1.0, seconds / 4))
+    tok1 = oracle_decode_token(1)
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"first {sample_rows} rows of each of the 8 sweep matrices, "
                       f"{passes} passes, {el:.1f} s, fp64 oracle GEMV with {cores} threads; "
                       f"one core: {passes1} passes, {el1:.1f} s",
-            "value_one_core": round(gbs1, 3)}
+            "value_one_core": round(gbs1, 3),
+            "cpu_model": model, "logical_cpus": n_logical, "usable_cpus": n_usable,
+            "threads_note": f"{cores} threads: the host share of one single-GPU job",
+            "decode_8b_token_s_one_core": round(tok1, 2),
+            "decode_8b_token_sample": "one token of the Llama-3-8B-shaped Q8_0 model at position 1024 "
+                                      "(32 layers, 128256-row head), oracle on one core; all-zero weight "
+                                      "blocks (the oracle's work does not depend on the values)"}
 
 
 def main():
@@ -539,9 +627,10 @@ def main():
                    "weights": "fp32 N(0,0.02) encoded in HBM, x N(0,1), seed 0",
                    "rotated_copies": g["copies"], "step_bytes": g["step_bytes"]},
         "frac_of_peak": round(g["value"] / PEAK_HBM_GBS, 4),
-        "queued_launch_ms_per_step": round(g["queued_step_ms"], 4),
+        "per_case_sum_ms": round(g["case_sum_ms"], 4),
         "roofline": g["roofline"],
         "detail": g["detail"],
+        "q8_0_gemv": q8_0_gemv(args.steps),
         "q5_k_gemv": q5_k_gemv(args.steps),
         "verify_gemm": verify_gemm(args.steps),
     }

@@ -382,12 +382,6 @@ nt_status nt_read_bytes(const void *src, int64_t bytes, float *sink, nt_stream s
     return finish(launch_read_bytes(src, bytes, sink, as_stream(stream)), "nt_read_bytes");
 }
 
-nt_status nt_delay(double microseconds, nt_stream stream) {
-    set_error("");
-    if (!(microseconds >= 0.0) || microseconds > 1e6) return fail(NT_EINVAL, "nt_delay: need 0 <= us <= 1e6");
-    if (nt_status s = need_device()) return s;
-    return finish(launch_delay(microseconds, as_stream(stream)), "nt_delay");
-}
 
 nt_status nt_copy_bytes(void *dst, const void *src, int64_t bytes, nt_stream stream) {
     set_error("");

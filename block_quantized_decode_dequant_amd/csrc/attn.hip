@@ -21,7 +21,6 @@
 // [0, ctx_cap) writes NaN outputs and touches no memory out of bounds.
 #include <algorithm>
 #include <cmath>
-#include <cstdlib>
 
 #include "device_util.h"
 #include "nt_internal.h"
@@ -357,12 +356,7 @@ int attn_chunk(const nt_attn_desc &a) {
     // (position, q head) pairs, e.g. 36 positions of 4 heads at 1152, where
     // the fixed cost per workgroup dominates (measured: 8 kv heads of 8 q
     // heads at 4160, 65 vs 64: -1.0 % decode time; of 4 q heads at 1152, 36
-    // vs 18 and 32: -0.8 %).  NT_ATTN_CHUNK overrides (any value in [8, 128]).
-    static const int env = [] {
-        const char *v = std::getenv("NT_ATTN_CHUNK");
-        return v ? std::atoi(v) : 0;
-    }();
-    if (env >= 8 && env <= kMaxChunk) return env;
+    // vs 18 and 32: -0.8 %).
     const int kv = std::max(1, a.n_kv_heads), G = std::max(1, a.n_q_heads / kv);
     int per_head = std::max(1, 512 / kv);
     int c = (a.ctx_cap + per_head - 1) / per_head;

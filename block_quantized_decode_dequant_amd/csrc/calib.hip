@@ -37,30 +37,12 @@ __global__ void __launch_bounds__(256) copy_kernel(u32x4 *__restrict__ dst, cons
         dst[i] = __builtin_nontemporal_load(src + i);
 }
 
-// Spins one wave until `ticks` of the constant-rate wall clock have passed
-// (always terminates: the bound is fixed at launch).
-__global__ void delay_kernel(uint64_t ticks) {
-    const uint64_t t0 = wall_clock64();
-    while (wall_clock64() - t0 < ticks) __builtin_amdgcn_s_sleep(32);
-}
-
 int calib_grid(int64_t n16) {
     int64_t want = (n16 + 255) / 256;
     return int(want < 8192 ? want : 8192);
 }
 
 }  // namespace
-
-hipError_t launch_delay(double us, hipStream_t st) {
-    int dev = 0, khz = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
-    if (e != hipSuccess) return e;
-    const uint64_t ticks = uint64_t(us * double(khz) / 1000.0);
-    delay_kernel<<<1, 64, 0, st>>>(ticks);
-    return hipGetLastError();
-}
 
 hipError_t launch_read_bytes(const void *src, int64_t bytes, float *sink, hipStream_t st) {
     const int64_t n16 = bytes / 16;

@@ -24,7 +24,6 @@
 //    order.  No atomics: results are deterministic.
 #include <algorithm>
 #include <atomic>
-#include <cstdlib>
 #include <mutex>
 #include <type_traits>
 
@@ -1044,11 +1043,6 @@ __global__ void __launch_bounds__(512) gemv_pair(const GemvArgs a, const GemvArg
         gemv_body<TrB, 16, NORM, true>(c, blockIdx.x - ga, gridDim.x - ga);
 }
 
-int env_int(const char *name, int dflt) {
-    const char *v = std::getenv(name);
-    return v ? std::atoi(v) : dflt;
-}
-
 template <class Tr>
 hipError_t launch_generic(const void *W, const float *x, float *y, int64_t rows, int64_t cols, int acc,
                           hipStream_t st) {
@@ -1135,9 +1129,6 @@ struct LdsShape {
 // workgroups take even shares of the rows.
 template <class Tr>
 LdsShape lds_shape(int64_t items, int64_t cols, bool pairs, bool norm, bool vec16) {
-    static const int waves_cu_env = env_int("NT_GEMV_WAVES_CU", 0);
-    static const int shared_env = env_int("NT_GEMV_SHARED", -1);
-    static const int groups_env = env_int("NT_GEMV_GROUPS", 0);
     const DevInfo di = dev_info();
     LdsShape s;
     const int64_t units = cols / 64;
@@ -1150,22 +1141,19 @@ LdsShape lds_shape(int64_t items, int64_t cols, bool pairs, bool norm, bool vec1
     // 36.3 us)
     const size_t ring_sh = size_t(Tr::kStagesShared) * Tr::kSlice;
     const bool fits_one = area + 2 * size_t(s.nw) * (ring_sh + kMaxRowsPerWG * 4 + 4 + 256) <= size_t(di.lds_per_cu);
-    static const int wide_env = env_int("NT_GEMV_SHARED_WIDE", 1);
-    bool shared = vec16 && (cols <= 8192 || (wide_env > 0 && fits_one));
-    if (shared_env >= 0) shared = shared && shared_env > 0;
+    const bool shared = vec16 && (cols <= 8192 || fits_one);
     const size_t ring = size_t(shared ? Tr::kStagesShared : Tr::kStagesWide) * Tr::kSlice;
     const size_t per_wave = (shared ? ring : (ring > 16384 ? ring : 16384)) + kMaxRowsPerWG * 4 + 4 + 256;
     s.groups = 1;
     if (shared) {
         int g = 8 / s.nw;
         while (g > 0 && area + size_t(g) * s.nw * per_wave > size_t(di.lds_per_cu)) --g;
-        if (groups_env > 0 && groups_env < g) g = groups_env;
         s.groups = g > 0 ? g : 1;      // two slices and their areas always fit one group
     }
     s.shared = shared;
     const int nwv = s.nw * s.groups;
     s.lds = (shared ? area : 0) + size_t(nwv) * per_wave;
-    const int waves_cu = waves_cu_env > 0 ? waves_cu_env : 8;
+    constexpr int waves_cu = 8;
     int64_t per_cu = int64_t(di.lds_per_cu) / int64_t(s.lds);
     const int64_t by_waves = waves_cu / nwv > 0 ? waves_cu / nwv : 1;
     if (per_cu > by_waves) per_cu = by_waves;
@@ -1282,11 +1270,10 @@ hipError_t launch_gemv_pair(nt_qtype ta, int na, const void *const *Wa, const in
 int64_t gemv_row_bytes(nt_qtype t, int64_t cols) { return cols / block_elems(t) * block_bytes(t); }
 
 bool gemv_fast_ok(nt_qtype t, int64_t rows, int64_t cols) {
-    static const bool force_generic = env_int("NT_GEMV_GENERIC", 0) != 0;
     const int64_t rb = gemv_row_bytes(t, cols);
     // word-aligned rows, whole 64-value units, at most 8 column slices, and
     // byte offsets that fit in 32 bits
-    return !force_generic && rb % 4 == 0 && cols % 64 == 0 && cols > 0 && cols <= 32768 &&
+    return rb % 4 == 0 && cols % 64 == 0 && cols > 0 && cols <= 32768 &&
            rows * rb < (int64_t(1) << 32);
 }
 

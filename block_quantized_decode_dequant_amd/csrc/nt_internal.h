@@ -46,7 +46,6 @@ hipError_t launch_gemv_pair(nt_qtype ta, int na, const void *const *Wa, const in
                             nt_qtype tb, int nb, const void *const *Wb, const int64_t *rows_b, float *const *yb,
                             int64_t cols, const float *x, const float *gain, float eps, hipStream_t st);
 hipError_t launch_quantize(nt_qtype t, const float *x, void *blocks, int64_t n, hipStream_t st);
-hipError_t launch_delay(double us, hipStream_t st);
 hipError_t launch_rmsnorm(const float *x, const float *g, float *y, int64_t n, float eps, hipStream_t st);
 hipError_t launch_rope(float *q, float *k, int n_q_heads, int n_kv_heads, int head_dim, const int32_t *d_pos,
                        float theta, hipStream_t st);

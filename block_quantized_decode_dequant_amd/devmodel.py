@@ -33,19 +33,42 @@ def matrix_shape(s: ModelShape, name: str):
             "wo": (H, QD), "w_gate": (F, H), "w_up": (F, H), "w_down": (H, F)}[name]
 
 
-def encode_into(out: torch.Tensor, qtype: int, rows: int, cols: int, seed: int, stream_id: int,
-                std: float = 0.02, chunk_elems: int = 1 << 26):
-    """Fill `out` (uint8, rows x row_bytes) with encoded N(0, std) values."""
-    rb = nt.row_bytes(qtype, cols)
-    g = torch.Generator(device=out.device)
+def value_chunks(rows: int, cols: int, seed: int, stream_id: int, device, std: float = 0.02,
+                 chunk_elems: int = 1 << 26):
+    """Yields (first_row, n_rows, values): the seeded N(0, std) fp32 values of
+    a rows x cols matrix, drawn on the device by torch's generator in row
+    chunks (the same values on every call)."""
+    g = torch.Generator(device=device)
     g.manual_seed(seed * 1_000_003 + stream_id)
     rc = max(1, chunk_elems // cols)
     for r0 in range(0, rows, rc):
         n = min(rc, rows - r0)
-        w = torch.randn(n * cols, generator=g, device=out.device, dtype=torch.float32)
+        w = torch.randn(n * cols, generator=g, device=device, dtype=torch.float32)
         w.mul_(std)
+        yield r0, n, w
+
+
+def encode_into(out: torch.Tensor, qtype: int, rows: int, cols: int, seed: int, stream_id: int,
+                std: float = 0.02, chunk_elems: int = 1 << 26):
+    """Fill `out` (uint8, rows x row_bytes) with encoded N(0, std) values."""
+    rb = nt.row_bytes(qtype, cols)
+    for r0, n, w in value_chunks(rows, cols, seed, stream_id, out.device, std, chunk_elems):
         nt.nt_quantize(qtype, w, out[r0 * rb:(r0 + n) * rb], n * cols)
         del w
+
+
+def matrix_specs(s: ModelShape, streamed_from: int | None = None):
+    """Every quantized matrix of the model as (layer or None, name, rows, cols,
+    type, generator stream id); layers >= streamed_from are left out."""
+    types = tensor_types(s.weights)
+    out = [(None, "tok_embd", *matrix_shape(s, "tok_embd"), types["tok_embd"], 1),
+           (None, "output", *matrix_shape(s, "output"), types["output"], 2)]
+    for l in range(s.n_layers):
+        if streamed_from is not None and l >= streamed_from:
+            continue
+        for i, name in enumerate(MATS):
+            out.append((l, name, *matrix_shape(s, name), types[name], 16 + 16 * l + i))
+    return out
 
 
 def build(s: ModelShape, seed: int = 0, device=None, streamed_from: int | None = None):
@@ -53,25 +76,20 @@ def build(s: ModelShape, seed: int = 0, device=None, streamed_from: int | None =
     weights (they are served by nt_stream_layers from host blobs)."""
     dev = device or torch.device("cuda:0")
     types = tensor_types(s.weights)
-
-    def qmat(name, sid):
-        rows, cols = matrix_shape(s, name)
-        t = types[name]
+    mats = {}
+    for l, name, rows, cols, t, sid in matrix_specs(s, streamed_from):
         out = torch.empty(rows * nt.row_bytes(t, cols), dtype=torch.uint8, device=dev)
         encode_into(out, t, rows, cols, seed, sid)
-        return (t, out)
+        mats[(l, name)] = (t, out)
 
     ones = torch.ones(s.hidden, dtype=torch.float32, device=dev)
     layers = []
     for l in range(s.n_layers):
         lw = {"attn_norm": ones, "ffn_norm": ones}
-        for i, name in enumerate(MATS):
-            if streamed_from is not None and l >= streamed_from:
-                lw[name] = (types[name], None)
-            else:
-                lw[name] = qmat(name, 16 + 16 * l + i)
+        for name in MATS:
+            lw[name] = mats.get((l, name), (types[name], None))
         layers.append(lw)
-    weights = {"tok_embd": qmat("tok_embd", 1), "output": qmat("output", 2), "output_norm": ones,
+    weights = {"tok_embd": mats[(None, "tok_embd")], "output": mats[(None, "output")], "output_norm": ones,
                "layers": layers}
     cfg = nt.model_config(s.n_layers, s.hidden, s.n_q_heads, s.n_kv_heads, s.head_dim, s.ffn, s.vocab,
                           s.ctx_cap, s.rms_eps, s.rope_theta)
@@ -86,7 +104,7 @@ def build(s: ModelShape, seed: int = 0, device=None, streamed_from: int | None =
         caches.append(c)
     ws = torch.empty(nt.nt_model_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
     model = nt.Model(cfg, weights, caches[0], caches[1], ws)
-    return model, dict(weights=weights, types=types)
+    return model, dict(weights=weights, types=types, k_cache=caches[0], v_cache=caches[1])
 
 
 def weight_bytes_per_token(s: ModelShape) -> int:

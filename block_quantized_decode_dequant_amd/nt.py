@@ -72,7 +72,6 @@ def _declare(L):
         "nt_gemm_batch": (st, [i32, vp, vp, vp, i64, i64, i32, i32, vp, C.c_size_t, vp]),
         "nt_read_bytes": (st, [vp, i64, vp, vp]),
         "nt_copy_bytes": (st, [vp, vp, i64, vp]),
-        "nt_delay": (st, [C.c_double, vp]),
         "nt_rmsnorm": (st, [vp, vp, vp, i64, C.c_float, vp]),
         "nt_rope": (st, [vp, vp, C.c_int32, C.c_int32, C.c_int32, vp, C.c_float, vp]),
         "nt_softmax": (st, [vp, i64, vp]),
@@ -231,10 +230,6 @@ def nt_read_bytes(src, nbytes: int, sink, stream=None):
 def nt_copy_bytes(dst, src, nbytes: int, stream=None):
     _check(lib().nt_copy_bytes(_ptr(dst, nbytes, "dst"), _ptr(src, nbytes, "src"), nbytes,
                                _stream(stream)), "nt_copy_bytes")
-
-
-def nt_delay(microseconds: float, stream=None):
-    _check(lib().nt_delay(float(microseconds), _stream(stream)), "nt_delay")
 
 
 # ---- per-token ops --------------------------------------------------------------------

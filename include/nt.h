@@ -353,12 +353,9 @@ nt_status nt_quantize(nt_qtype t, const float *x, void *blocks, int64_t n, nt_st
  * a value whose (practically never taken) store into `sink` (device, >= 4096
  * floats) keeps the reads from being elided.
  * nt_copy_bytes: plain device-to-device copy of `bytes` bytes (both 16-byte
- * aligned, bytes a multiple of 16).
- * nt_delay: occupies `stream` for `microseconds` (0..1e6) with one spinning
- * wave, so a host can queue work behind it and time kernels back to back. */
+ * aligned, bytes a multiple of 16). */
 nt_status nt_read_bytes(const void *src, int64_t bytes, float *sink, nt_stream stream);
 nt_status nt_copy_bytes(void *dst, const void *src, int64_t bytes, nt_stream stream);
-nt_status nt_delay(double microseconds, nt_stream stream);
 
 /* ---- GGUF model files ("Overview": the engine loads GGUF models) -----------
  * Host-side reader of the GGUF v2/v3 container: the file is mapped read-only
