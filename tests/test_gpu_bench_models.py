@@ -65,6 +65,8 @@ def oracle_decoder(shape, extra):
     dev = extra["k_cache"].device
     host = {}
     for l, name, rows, cols, t, sid in devmodel.matrix_specs(shape):
+        if l is not None and name == "wq" and l % 10 == 0:
+            print(f"  oracle encoding: layer {l} of {shape.n_layers}", flush=True)
         ob = oracle_bytes(rows, cols, t, sid, dev)
         d = (w[name] if l is None else w["layers"][l][name])[1]
         assert torch.equal(d, torch.from_numpy(ob).to(dev)), f"layer {l} {name}: device bytes differ from the oracle's"
