@@ -231,6 +231,23 @@ nt_status nt_attn_decode(const nt_attn_desc *desc, const float *q, const float *
                          uint16_t *k_cache, uint16_t *v_cache, const int32_t *d_pos, float *out,
                          void *workspace, size_t workspace_bytes, nt_stream stream);
 
+/* The same attention without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Arguments, results and errors as for
+ * nt_attn_decode.  The partial results live in a fixed array of
+ * NT_ATTN_NOALLOC_SCRATCH_BYTES bytes that the library keeps in each device's
+ * memory until the process ends; its address is looked up (not allocated) on
+ * the first call on a device, and no call allocates memory.  A shape whose
+ * nt_attn_workspace_bytes exceeds the array returns NT_ENOMEM (use
+ * nt_attn_decode).  Every call on one device shares that device's array:
+ * calls ordered on one stream are safe, calls that overlap in time on one
+ * device (other streams, other threads) race and give undefined results.
+ * Nothing in the array needs to start at zero. */
+#define NT_ATTN_NOALLOC_SCRATCH_BYTES (8u << 20)
+nt_status nt_attn_decode_noalloc(const nt_attn_desc *desc, const float *q, const float *k_new,
+                                 const float *v_new, uint16_t *k_cache, uint16_t *v_cache, const int32_t *d_pos,
+                                 float *out, nt_stream stream);
+
 /* ---- one batch-1 Llama decode step ("Main features": RoPE, GQA, SwiGLU,
  * RMSNorm, KV cache; "Architecture": engine, sampler) ------------------------
  * Per token, with pos = *d_pos and x the residual stream:
