@@ -54,6 +54,9 @@ def parse():
                     help="decode measurements: none, the 8B-shaped model, the resident 70B-shaped model, "
                          "or all (8B, 70B, 70B streamed)")
     ap.add_argument("--stream-tokens", type=int, default=3)
+    ap.add_argument("--file-layers", type=int, default=8,
+                    help="layers of the 70B Q6_K model read from a file each step in the three-tier leg (0: skip)")
+    ap.add_argument("--file-dir", default=None, help="directory for the layer file (default: the temp directory)")
     return ap.parse_args()
 
 
@@ -551,6 +554,100 @@ def oracle_decode_token(threads: int):
     return time.perf_counter() - t0
 
 
+def decode_file_tier(shape, n_file, where=None, vram_cap=24 << 30, n_tokens=2):
+    """The three-tier mode on the 70B all-Q6_K model: the first 24 GiB of
+    layers resident, the last n_file layers read from a file every step
+    (O_DIRECT when the file system allows it) through two pinned staging
+    buffers, the layers between them from pinned host RAM; reads, copies and
+    compute are pipelined by the host (a copy is enqueued once its read has
+    finished).  The file holds only the file tier's layers; it is written
+    first, then read back, then deleted."""
+    import shutil
+    import tempfile
+
+    import torch
+
+    from block_quantized_decode_dequant_amd import devmodel, nt
+
+    types = devmodel.tensor_types(shape.weights)
+    tl = [types[n] for n in devmodel.MATS]
+    cfg = nt.model_config(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                          shape.ffn, shape.vocab, shape.ctx_cap, shape.rms_eps, shape.rope_theta)
+    _, blob = nt.nt_layer_blob_layout(cfg, tl)
+    stride = -(-blob // 4096) * 4096
+    where = where or tempfile.gettempdir()
+    free = shutil.disk_usage(where).free
+    n_file = int(min(n_file, max(0, (free - (4 << 30)) // stride)))   # leave 4 GiB free on the disk
+    if n_file <= 0:
+        return {"skipped": f"no room for one {stride}-byte layer in {where} ({free} bytes free)"}
+    first_streamed = int(min(shape.n_layers, vram_cap // blob))
+    first_file = shape.n_layers - n_file
+    planned = nt.nt_tier_plan(cfg, tl, vram_cap, (first_file - first_streamed) * blob)
+    assert planned == (first_streamed, first_file), planned
+    t0 = time.perf_counter()
+    model, extra = devmodel.build(shape, streamed_from=first_streamed)
+    blobs, nbytes = devmodel.fill_streamed_blobs(shape, first_streamed, last=first_file)
+    fd, path = tempfile.mkstemp(prefix="nt_layers_", suffix=".bin", dir=where)
+    os.close(fd)
+    try:
+        tw = time.perf_counter()
+        stride_w, _ = devmodel.write_streamed_file(shape, first_file, path)
+        os.sync()
+        write_s = time.perf_counter() - tw
+        build_s = time.perf_counter() - t0
+        dev = torch.device("cuda:0")
+        dbuf = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(2)]
+        raw = torch.empty(2 * stride + 4096, dtype=torch.uint8, pin_memory=True)
+        lead = (-raw.data_ptr()) % 4096
+        st0, st1 = raw[lead:lead + stride], raw[lead + stride:lead + 2 * stride]
+        copy_stream = torch.cuda.Stream()
+        model.stream_layers_tiered(first_streamed, blobs, dbuf[0], dbuf[1], copy_stream, path, first_file, 0,
+                                   stride_w, st0, st1, direct=True)
+        d_tok = torch.tensor([1], dtype=torch.int32, device=dev)
+        d_pos = torch.tensor([shape.ctx], dtype=torch.int32, device=dev)
+        logits = torch.empty(shape.vocab, dtype=torch.float32, device=dev)
+        side = torch.cuda.Stream()
+        with torch.cuda.stream(side):
+            model.step(d_tok, d_pos, logits, d_tok)           # warm-up token
+        torch.cuda.synchronize()
+        recs = []
+        t1 = time.perf_counter()
+        for _ in range(n_tokens):
+            with torch.cuda.stream(side):
+                model.step(d_tok, d_pos, logits, d_tok)
+            recs.append((model.stream_stats(), model.file_stats()))
+        torch.cuda.synchronize()
+        total = time.perf_counter() - t1
+        avg = lambda f: sum(f(r) for r in recs) / len(recs)
+        read_ms = avg(lambda r: r[1]["read_ms"])
+        span_ms = avg(lambda r: r[1]["read_span_ms"])
+        copy_ms = avg(lambda r: r[0]["copy_ms"])
+        comp_ms = avg(lambda r: r[0]["compute_ms"])
+        wall_ms = avg(lambda r: r[0]["wall_ms"])
+        fbytes = n_file * nbytes
+        ns = shape.n_layers - first_streamed
+        out = {"resident_layers": first_streamed, "pinned_layers": first_file - first_streamed,
+               "file_layers": n_file, "blob_bytes": int(nbytes), "file_stride": int(stride_w),
+               "o_direct": bool(recs[-1][1]["direct"]), "file_dir": where,
+               "file_bytes_per_token": int(fbytes), "h2d_bytes_per_token": int(ns * nbytes),
+               "tok_s": round(n_tokens / total, 3), "ms_per_token": round(total / n_tokens * 1e3, 1),
+               "file_read_gbs": round(fbytes / (read_ms * 1e-3) / 1e9, 2),
+               "file_read_gbs_span": round(fbytes / (span_ms * 1e-3) / 1e9, 2),
+               "h2d_gbs": round(ns * nbytes / (copy_ms * 1e-3) / 1e9, 2),
+               "read_ms": round(read_ms, 1), "read_span_ms": round(span_ms, 1), "copy_ms": round(copy_ms, 1),
+               "streamed_compute_ms": round(comp_ms, 2), "wall_ms": round(wall_ms, 1),
+               "copy_and_compute_hidden_frac": round(max(0.0, min(1.0, (span_ms + copy_ms + comp_ms - wall_ms)
+                                                                 / (copy_ms + comp_ms))), 4),
+               "tokens": n_tokens, "write_s": round(write_s, 1), "build_s": round(build_s, 1)}
+        model.stream_layers(None, None, None, None, None)
+        model.close()
+        del model, extra, blobs, dbuf, raw
+        torch.cuda.empty_cache()
+        return out
+    finally:
+        os.unlink(path)
+
+
 def cpu_baseline(seconds: float):
     """The oracle's fp64 GEMV on the first rows of every sweep matrix, on
     CPU_SHARE threads and on one core; and one oracle decode token of the
@@ -643,6 +740,9 @@ def main():
         if args.decode == "all":
             dec["llama70b_q6_k_streamed_24gib"] = decode_streamed(workloads.LLAMA_70B_Q6K,
                                                                   n_tokens=args.stream_tokens)
+            if args.file_layers > 0:
+                dec["llama70b_q6_k_three_tier_file"] = decode_file_tier(workloads.LLAMA_70B_Q6K, args.file_layers,
+                                                                        args.file_dir)
         line["decode"] = dec
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -102,6 +102,7 @@ const char *nt_status_str(nt_status s) {
     case NT_EHIP: return "NT_EHIP: HIP runtime error";
     case NT_ESTATE: return "NT_ESTATE: call not valid in the current state";
     case NT_ENODEV: return "NT_ENODEV: no GPU device";
+    case NT_EIO: return "NT_EIO: file read failed";
     }
     return "unknown nt_status";
 }

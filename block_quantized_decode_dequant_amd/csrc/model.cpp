@@ -11,10 +11,33 @@
 // Every step is enqueued on the caller's stream.  Token and position live in
 // device memory, so one captured HIP graph replays unchanged for every
 // token; the argmax kernel writes the next token and advances the position.
+//
+// The third tier ("Performance": 3-tier cache with an NVMe/mmap fallback;
+// "NVMe direct streaming": disk -> pinned staging -> host-to-device copy ->
+// GPU buffer -> compute) serves the last layers from a file.  A reader
+// thread reads blob j into one of two pinned staging buffers; only after that
+// read has finished does the host enqueue the copy of blob j and the compute
+// of its layer, so no GPU work ever waits on host progress: a failed read
+// ends the step with NT_EIO and leaves nothing queued that could wait
+// forever.
+#include <fcntl.h>
+#include <linux/aio_abi.h>
+#include <sys/stat.h>
+#include <sys/syscall.h>
+#include <unistd.h>
+
 #include <hip/hip_runtime.h>
 
+#include <cerrno>
+#include <chrono>
+#include <cstdlib>
+#include <condition_variable>
 #include <cstring>
+#include <deque>
+#include <memory>
+#include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "nt_internal.h"
@@ -116,7 +139,243 @@ size_t matrix_bytes(const nt_model_config &c, int which, nt_qtype t) {
     return size_t(rows) * size_t(cols / block_elems(t) * block_bytes(t));
 }
 
+constexpr uint64_t kFileAlign = 4096;     // O_DIRECT buffer, offset and length granule
+
+double host_seconds() {
+    return std::chrono::duration<double>(std::chrono::steady_clock::now().time_since_epoch()).count();
+}
+
+// O_DIRECT reads go through two library-owned bounce chunks: the kernel
+// cannot hand HIP-pinned host memory to a direct block read (the read fails
+// with EFAULT), so each chunk lands in ordinary aligned memory and is copied
+// into the pinned staging buffer while the next chunk is read (Linux native
+// asynchronous I/O; a plain blocking read when it is not available).
+constexpr size_t kChunk = size_t(32) << 20;
+
+long sys_io_setup(unsigned n, aio_context_t *ctx) { return syscall(SYS_io_setup, n, ctx); }
+long sys_io_destroy(aio_context_t ctx) { return syscall(SYS_io_destroy, ctx); }
+long sys_io_submit(aio_context_t ctx, long n, struct iocb **v) { return syscall(SYS_io_submit, ctx, n, v); }
+long sys_io_getevents(aio_context_t ctx, long lo, long hi, struct io_event *ev, struct timespec *to) {
+    return syscall(SYS_io_getevents, ctx, lo, hi, ev, to);
+}
+
 }  // namespace
+
+// The file tier: blob j of the file layers sits at offset + j * stride.  One
+// reader thread serves read requests (blob j into staging slot j % 2) in
+// order; before it overwrites a slot it waits for the host-to-device copy
+// out of that slot that was enqueued last.
+struct FileTier {
+    int fd = -1;
+    bool direct = false;
+    int device = 0;
+    int32_t first = 0, count = 0;         // file layers [first, first + count)
+    uint64_t offset = 0, stride = 0;
+    size_t blob = 0, read_len = 0;        // blob bytes, bytes read per blob (blob rounded up to kFileAlign)
+    void *staging[2] = {nullptr, nullptr};
+    hipEvent_t staged_free[2] = {nullptr, nullptr};   // recorded after each copy out of a slot
+    void *bounce[2] = {nullptr, nullptr};             // O_DIRECT only: kChunk bytes each, 4096-aligned
+    aio_context_t aio = 0;                            // O_DIRECT only, when native AIO is available
+
+    std::thread th;
+    std::mutex mu;
+    std::condition_variable cv;
+    struct Job { int f; int slot; bool wait_copy; };
+    std::deque<Job> queue;
+    int outstanding = 0;                  // posted, not yet finished
+    bool quit = false;
+    // per step, per file layer: 0 not done, 1 read, 2 failed
+    std::vector<int> state;
+    std::vector<std::string> err;
+    std::vector<double> t0, t1;
+    uint64_t reads = 0, read_bytes = 0;
+
+    void run() {
+        (void)hipSetDevice(device);
+        for (;;) {
+            Job j{};
+            {
+                std::unique_lock<std::mutex> lk(mu);
+                cv.wait(lk, [&] { return quit || !queue.empty(); });
+                if (queue.empty()) return;      // quit with nothing left
+                j = queue.front();
+                queue.pop_front();
+            }
+            std::string e;
+            const double a = host_seconds();
+            if (j.wait_copy) {
+                const hipError_t he = hipEventSynchronize(staged_free[j.slot]);
+                if (he != hipSuccess) {
+                    e = std::string("waiting for the staging buffer: ") + hipGetErrorString(he);
+                    (void)hipGetLastError();
+                }
+            }
+            size_t got = 0;
+            if (e.empty()) {
+                uint8_t *dst = static_cast<uint8_t *>(staging[j.slot]);
+                const uint64_t off = offset + uint64_t(j.f) * stride;
+                got = direct ? (aio ? read_aio(dst, off, e) : read_bounced(dst, off, e)) : read_plain(dst, off, e);
+                if (e.empty() && got < blob)
+                    e = "the file ends inside blob " + std::to_string(j.f) + " (" + std::to_string(got) + " of " +
+                        std::to_string(blob) + " bytes)";
+            }
+            const double z = host_seconds();
+            {
+                std::lock_guard<std::mutex> lk(mu);
+                state[j.f] = e.empty() ? 1 : 2;
+                err[j.f] = e;
+                t0[j.f] = a;
+                t1[j.f] = z;
+                if (e.empty()) {
+                    ++reads;
+                    read_bytes += blob;
+                }
+                --outstanding;
+            }
+            cv.notify_all();
+        }
+    }
+    // blocking reads straight into the destination (through the page cache)
+    size_t read_plain(uint8_t *dst, uint64_t off, std::string &e) {
+        size_t got = 0;
+        while (got < read_len) {
+            const ssize_t r = pread(fd, dst + got, read_len - got, off_t(off + got));
+            if (r < 0) {
+                if (errno == EINTR) continue;
+                e = std::string("read failed: ") + std::strerror(errno);
+                break;
+            }
+            if (r == 0) break;              // end of file
+            got += size_t(r);
+        }
+        return got;
+    }
+    // O_DIRECT, blocking, one chunk at a time through bounce[0]
+    size_t read_bounced(uint8_t *dst, uint64_t off, std::string &e) {
+        size_t got = 0;
+        while (got < read_len) {
+            const size_t want = std::min(kChunk, read_len - got);
+            ssize_t r;
+            do {
+                r = pread(fd, bounce[0], want, off_t(off + got));
+            } while (r < 0 && errno == EINTR);
+            if (r < 0) {
+                e = std::string("read failed: ") + std::strerror(errno);
+                break;
+            }
+            std::memcpy(dst + got, bounce[0], size_t(r));
+            got += size_t(r);
+            if (size_t(r) < want) break;    // end of file
+        }
+        return got;
+    }
+    // O_DIRECT with native AIO: chunk c + 1 is read into one bounce chunk
+    // while chunk c is copied out of the other
+    size_t read_aio(uint8_t *dst, uint64_t off, std::string &e) {
+        const size_t nch = (read_len + kChunk - 1) / kChunk;
+        struct iocb cb[2];
+        auto submit = [&](size_t c) -> bool {
+            struct iocb &x = cb[c & 1];
+            std::memset(&x, 0, sizeof(x));
+            x.aio_lio_opcode = IOCB_CMD_PREAD;
+            x.aio_fildes = uint32_t(fd);
+            x.aio_buf = uint64_t(uintptr_t(bounce[c & 1]));
+            x.aio_nbytes = std::min(kChunk, read_len - c * kChunk);
+            x.aio_offset = int64_t(off + c * kChunk);
+            x.aio_data = c;
+            struct iocb *v[1] = {&x};
+            long r;
+            do {
+                r = sys_io_submit(aio, 1, v);
+            } while (r < 0 && errno == EINTR);
+            if (r != 1) e = std::string("read submission failed: ") + std::strerror(errno);
+            return r == 1;
+        };
+        // waits for the one read in flight; its byte count, or -1 on error
+        auto complete = [&]() -> long {
+            struct io_event ev;
+            struct timespec to = {60, 0};
+            long r;
+            do {
+                r = sys_io_getevents(aio, 1, 1, &ev, &to);
+            } while (r < 0 && errno == EINTR);
+            if (r != 1) {
+                e = r == 0 ? "read timed out after 60 s" : std::string("read wait failed: ") + std::strerror(errno);
+                return -1;
+            }
+            if (ev.res < 0) {
+                e = std::string("read failed: ") + std::strerror(int(-ev.res));
+                return -1;
+            }
+            return long(ev.res);
+        };
+        size_t got = 0;
+        if (!submit(0)) return 0;
+        for (size_t c = 0; c < nch; ++c) {
+            const long r = complete();
+            if (r < 0) return got;          // nothing else is in flight
+            const size_t want = std::min(kChunk, read_len - c * kChunk);
+            const bool more = size_t(r) == want && c + 1 < nch;
+            if (more && !submit(c + 1)) return got;
+            std::memcpy(dst + c * kChunk, bounce[c & 1], size_t(r));
+            got += size_t(r);
+            if (!more) {
+                if (size_t(r) < want) break;    // end of file: nothing was submitted after it
+            }
+        }
+        return got;
+    }
+    void post(int f, int slot, bool wait_copy) {
+        {
+            std::lock_guard<std::mutex> lk(mu);
+            queue.push_back({f, slot, wait_copy});
+            ++outstanding;
+        }
+        cv.notify_all();
+    }
+    // blocks until blob f is read; false (with the reason) if the read failed
+    bool wait(int f, std::string &why) {
+        std::unique_lock<std::mutex> lk(mu);
+        cv.wait(lk, [&] { return state[f] != 0; });
+        if (state[f] == 2) {
+            why = err[f];
+            return false;
+        }
+        return true;
+    }
+    // drops queued requests and waits for the one in progress
+    void drain() {
+        std::unique_lock<std::mutex> lk(mu);
+        outstanding -= int(queue.size());
+        queue.clear();
+        cv.wait(lk, [&] { return outstanding == 0; });
+    }
+    void begin_step() {
+        std::lock_guard<std::mutex> lk(mu);
+        state.assign(size_t(count), 0);
+        err.assign(size_t(count), std::string());
+        t0.assign(size_t(count), 0.0);
+        t1.assign(size_t(count), 0.0);
+    }
+    ~FileTier() {
+        if (th.joinable()) {
+            drain();
+            {
+                std::lock_guard<std::mutex> lk(mu);
+                quit = true;
+            }
+            cv.notify_all();
+            th.join();
+        }
+        for (int b = 0; b < 2; ++b) {
+            if (staged_free[b]) (void)hipEventDestroy(staged_free[b]);
+            std::free(bounce[b]);
+        }
+        if (aio) (void)sys_io_destroy(aio);
+        if (fd >= 0) close(fd);
+    }
+};
+
 }  // namespace nt
 
 using namespace nt;
@@ -148,6 +407,9 @@ struct nt_model {
     hipEvent_t step_t0 = nullptr, step_t1 = nullptr;
     bool have_step = false;
     uint64_t steps = 0, layers_streamed = 0, h2d_bytes = 0;
+    // the file tier (layers [file->first, n_layers)), when enabled
+    std::unique_ptr<FileTier> file;
+    bool staged_used[2] = {false, false};
 
     float *f(size_t off) const { return reinterpret_cast<float *>(ws + off); }
     void drop_graph() {
@@ -165,6 +427,8 @@ struct nt_model {
         }
         kill(step_t0);
         kill(step_t1);
+        file.reset();
+        staged_used[0] = staged_used[1] = false;
     }
 };
 
@@ -287,15 +551,29 @@ hipError_t prefetch(nt_model *m, int s) {
     return hipSuccess;
 }
 
+// A streamed step: layers [first_streamed, first_file) come from pinned host
+// blobs copied ahead on the copy stream; layers from first_file on come from
+// the file, each copied only once its read has finished.  d_buf[s % 2] holds
+// streamed layer s.  On a failed read the step stops enqueuing (nothing
+// queued waits on work that is not queued) and returns the read's message
+// in `why`.
 hipError_t enqueue_streamed(nt_model *m, const int32_t *d_token, int32_t *d_pos, float *logits, int32_t *d_next,
-                            hipStream_t st) {
+                            hipStream_t st, std::string &why) {
     const nt_model_config &c = m->cfg;
     const int ns = c.n_layers - m->first_streamed;
+    FileTier *ft = m->file.get();
+    const int nf = ft ? ft->count : 0, np = ns - nf;
     NT_TRY(hipEventRecord(m->step_t0, st));
+    // file reads start at once: they depend on nothing the step computes
+    if (nf > 0) {
+        ft->drain();                     // nothing is left over from a step that stopped early
+        ft->begin_step();
+        for (int f = 0; f < 2 && f < nf; ++f) ft->post(f, f, m->staged_used[f]);
+    }
     // the copy side stream must not run ahead of work already queued on the
     // compute stream that still reads the staging buffers
-    if (ns > 0) NT_TRY(prefetch(m, 0));
-    if (ns > 1) NT_TRY(prefetch(m, 1));
+    if (np > 0) NT_TRY(prefetch(m, 0));
+    if (np > 1) NT_TRY(prefetch(m, 1));
     NT_TRY(launch_embed(nt_qtype(m->w.tok_embd.type), m->w.tok_embd.data, c.vocab, c.hidden, d_token,
                         m->f(m->lay.x), st));
     nt_tensor_ref mats[kBlobOrder];
@@ -305,6 +583,23 @@ hipError_t enqueue_streamed(nt_model *m, const int32_t *d_token, int32_t *d_pos,
     }
     for (int s = 0; s < ns; ++s) {
         const int l = m->first_streamed + s, b = s & 1;
+        if (s >= np) {
+            // file layer f: wait (on the host) for its read, then copy it
+            const int f = s - np, slot = f & 1;
+            if (!ft->wait(f, why)) {
+                ft->drain();
+                return hipErrorFileNotFound;      // reported as NT_EIO with `why`
+            }
+            NT_TRY(hipStreamWaitEvent(m->copy_stream, m->freed[b], 0));
+            NT_TRY(hipEventRecord(m->copy_t0[s], m->copy_stream));
+            NT_TRY(hipMemcpyAsync(m->d_buf[b], ft->staging[slot], m->blob_bytes, hipMemcpyHostToDevice,
+                                  m->copy_stream));
+            NT_TRY(hipEventRecord(m->copy_t1[s], m->copy_stream));
+            NT_TRY(hipEventRecord(m->ready[b], m->copy_stream));
+            NT_TRY(hipEventRecord(ft->staged_free[slot], m->copy_stream));
+            m->staged_used[slot] = true;
+            if (f + 2 < nf) ft->post(f + 2, slot, true);
+        }
         NT_TRY(hipStreamWaitEvent(st, m->ready[b], 0));
         NT_TRY(hipEventRecord(m->comp_t0[s], st));
         for (int i = 0; i < kBlobOrder; ++i) {
@@ -314,7 +609,7 @@ hipError_t enqueue_streamed(nt_model *m, const int32_t *d_token, int32_t *d_pos,
         NT_TRY(run_layer(m, l, mats, m->layers[l].attn_norm, m->layers[l].ffn_norm, d_pos, st));
         NT_TRY(hipEventRecord(m->comp_t1[s], st));
         NT_TRY(hipEventRecord(m->freed[b], st));
-        if (s + 2 < ns) NT_TRY(prefetch(m, s + 2));
+        if (s + 2 < np) NT_TRY(prefetch(m, s + 2));
     }
     NT_TRY(head(m, d_pos, logits, d_next, st));
     NT_TRY(hipEventRecord(m->step_t1, st));
@@ -436,7 +731,9 @@ nt_status nt_decode_step(nt_model *m, const int32_t *d_token, int32_t *d_pos, fl
         return fail(NT_EALIGN, "nt_decode_step: misaligned pointer");
     hipStream_t st = as_stream(stream);
     if (m->streaming) {
-        hipError_t e = enqueue_streamed(m, d_token, d_pos, logits, d_next, st);
+        std::string why;
+        hipError_t e = enqueue_streamed(m, d_token, d_pos, logits, d_next, st, why);
+        if (!why.empty()) return fail(NT_EIO, "nt_decode_step: file tier: " + why);
         return e == hipSuccess ? NT_OK : hip_fail(e, "nt_decode_step (streamed)");
     }
     for (int l = 0; l < m->cfg.n_layers; ++l) {
@@ -474,10 +771,11 @@ nt_status nt_decode_step(nt_model *m, const int32_t *d_token, int32_t *d_pos, fl
     return e == hipSuccess ? NT_OK : hip_fail(e, "nt_decode_step: graph launch");
 }
 
-nt_status nt_stream_layers(nt_model *m, const nt_stream_desc *d) {
+nt_status nt_stream_layers_tiered(nt_model *m, const nt_stream_desc *d, const nt_file_tier *file) {
     set_error("");
     if (!m) return fail(NT_EINVAL, "nt_stream_layers: null model");
     if (!d) {
+        if (file) return fail(NT_EINVAL, "nt_stream_layers: a file tier needs a stream descriptor");
         if (m->streaming) (void)hipStreamSynchronize(m->copy_stream);
         m->streaming = false;
         m->drop_events();
@@ -487,8 +785,13 @@ nt_status nt_stream_layers(nt_model *m, const nt_stream_desc *d) {
     if (d->first_streamed_layer < 0 || d->first_streamed_layer > c.n_layers)
         return fail(NT_EINVAL, "nt_stream_layers: first_streamed_layer out of range");
     const int ns = c.n_layers - d->first_streamed_layer;
-    if (ns > 0 && (!d->h_layer_blobs || !d->d_buf[0] || !d->d_buf[1] || !d->copy_stream))
+    const int first_file = file ? file->first_file_layer : c.n_layers;
+    if (first_file < d->first_streamed_layer || first_file > c.n_layers)
+        return fail(NT_EINVAL, "nt_stream_layers: first_file_layer must lie in [first_streamed_layer, n_layers]");
+    const int nf = c.n_layers - first_file, np = ns - nf;
+    if (ns > 0 && (!d->d_buf[0] || !d->d_buf[1] || !d->copy_stream))
         return fail(NT_EINVAL, "nt_stream_layers: null pointer");
+    if (np > 0 && !d->h_layer_blobs) return fail(NT_EINVAL, "nt_stream_layers: null blob array");
     for (int l = 0; l < d->first_streamed_layer; ++l) {
         const nt_layer_weights &L = m->layers[l];
         if (!L.wq.data || !L.wk.data || !L.wv.data || !L.wo.data || !L.w_gate.data || !L.w_up.data || !L.w_down.data)
@@ -511,7 +814,7 @@ nt_status nt_stream_layers(nt_model *m, const nt_stream_desc *d) {
         if (d->buf_bytes < bytes) return fail(NT_ENOMEM, "nt_stream_layers: staging buffers smaller than a blob");
         if (!aligned(d->d_buf[0], kAlign) || !aligned(d->d_buf[1], kAlign))
             return fail(NT_EALIGN, "nt_stream_layers: staging buffers must be 256-byte aligned");
-        for (int s = 0; s < ns; ++s) {
+        for (int s = 0; s < np; ++s) {
             const void *h = d->h_layer_blobs[s];
             if (!h) return fail(NT_EINVAL, "nt_stream_layers: null blob");
             hipPointerAttribute_t attr;
@@ -520,6 +823,60 @@ nt_status nt_stream_layers(nt_model *m, const nt_stream_desc *d) {
                 return fail(NT_ESTATE, "nt_stream_layers: blob " + std::to_string(s) + " is not pinned host memory");
             }
         }
+    }
+    // the file tier: checked and opened before any state changes
+    std::unique_ptr<FileTier> ft;
+    if (nf > 0) {
+        const uint64_t read_len = (uint64_t(bytes) + kFileAlign - 1) / kFileAlign * kFileAlign;
+        if (!file->path) return fail(NT_EINVAL, "nt_stream_layers: null file path");
+        if (file->offset % kFileAlign || file->stride % kFileAlign)
+            return fail(NT_EALIGN, "nt_stream_layers: file offset and stride must be multiples of 4096");
+        if (file->stride < bytes) return fail(NT_EINVAL, "nt_stream_layers: file stride smaller than a blob");
+        if (file->staging_bytes < read_len)
+            return fail(NT_ENOMEM, "nt_stream_layers: file staging buffers smaller than a blob rounded up to 4096");
+        for (int b = 0; b < 2; ++b) {
+            const void *h = file->h_staging[b];
+            if (!h) return fail(NT_EINVAL, "nt_stream_layers: null file staging buffer");
+            if (!aligned(h, kFileAlign)) return fail(NT_EALIGN, "nt_stream_layers: file staging buffers must be 4096-byte aligned");
+            hipPointerAttribute_t attr;
+            if (hipPointerGetAttributes(&attr, h) != hipSuccess || attr.type != hipMemoryTypeHost) {
+                (void)hipGetLastError();
+                return fail(NT_ESTATE, "nt_stream_layers: file staging buffer " + std::to_string(b) +
+                                           " is not pinned host memory");
+            }
+        }
+        ft.reset(new FileTier());
+        int fd = -1;
+        if (file->direct) {
+            fd = open(file->path, O_RDONLY | O_DIRECT | O_CLOEXEC);
+            ft->direct = fd >= 0;
+        }
+        if (fd < 0) fd = open(file->path, O_RDONLY | O_CLOEXEC);   // the file system refused O_DIRECT, or not asked
+        if (fd < 0) return fail(NT_EIO, std::string("nt_stream_layers: cannot open the layer file: ") + std::strerror(errno));
+        ft->fd = fd;
+        struct stat sb;
+        if (fstat(fd, &sb) != 0) return fail(NT_EIO, "nt_stream_layers: cannot stat the layer file");
+        const uint64_t need = file->offset + uint64_t(nf - 1) * file->stride + bytes;
+        if (uint64_t(sb.st_size) < need)
+            return fail(NT_EINVAL, "nt_stream_layers: the layer file is shorter than its " + std::to_string(nf) +
+                                       " blobs (" + std::to_string(sb.st_size) + " < " + std::to_string(need) + ")");
+        if (ft->direct) {
+            for (int b = 0; b < 2; ++b)
+                if (posix_memalign(&ft->bounce[b], kFileAlign, kChunk) != 0) {
+                    ft->bounce[b] = nullptr;
+                    return fail(NT_ENOMEM, "nt_stream_layers: cannot allocate the host bounce buffers for O_DIRECT reads");
+                }
+            aio_context_t ctx = 0;
+            if (sys_io_setup(4, &ctx) == 0) ft->aio = ctx;   // else blocking O_DIRECT reads
+        }
+        ft->first = first_file;
+        ft->count = nf;
+        ft->offset = file->offset;
+        ft->stride = file->stride;
+        ft->blob = bytes;
+        ft->read_len = size_t(read_len);
+        ft->staging[0] = file->h_staging[0];
+        ft->staging[1] = file->h_staging[1];
     }
     if (nt_status s = device_present()) return s;
     if (m->streaming) (void)hipStreamSynchronize(m->copy_stream);
@@ -530,6 +887,7 @@ nt_status nt_stream_layers(nt_model *m, const nt_stream_desc *d) {
     for (int b = 0; b < 2 && e == hipSuccess; ++b) {
         e = mk(&m->ready[b]);
         if (e == hipSuccess) e = mk(&m->freed[b]);
+        if (e == hipSuccess && ft) e = hipEventCreateWithFlags(&ft->staged_free[b], hipEventDisableTiming);
     }
     m->copy_t0.assign(size_t(ns), nullptr);
     m->copy_t1.assign(size_t(ns), nullptr);
@@ -543,12 +901,25 @@ nt_status nt_stream_layers(nt_model *m, const nt_stream_desc *d) {
     }
     if (e == hipSuccess) e = mk(&m->step_t0);
     if (e == hipSuccess) e = mk(&m->step_t1);
+    if (e == hipSuccess && ft) e = hipGetDevice(&ft->device);
     if (e != hipSuccess) {
         m->drop_events();
         return hip_fail(e, "nt_stream_layers: event creation");
     }
+    if (ft) {
+        ft->begin_step();
+        FileTier *raw = ft.get();
+        try {
+            ft->th = std::thread([raw] { raw->run(); });
+        } catch (...) {
+            m->drop_events();
+            return fail(NT_ESTATE, "nt_stream_layers: cannot start the file reader thread");
+        }
+        m->file = std::move(ft);
+    }
     m->first_streamed = d->first_streamed_layer;
-    m->blobs.assign(d->h_layer_blobs, d->h_layer_blobs + ns);
+    m->blobs.assign(d->h_layer_blobs ? d->h_layer_blobs : nullptr,
+                    d->h_layer_blobs ? d->h_layer_blobs + np : nullptr);
     m->d_buf[0] = d->d_buf[0];
     m->d_buf[1] = d->d_buf[1];
     m->blob_bytes = bytes;
@@ -558,6 +929,22 @@ nt_status nt_stream_layers(nt_model *m, const nt_stream_desc *d) {
     m->streaming = true;
     m->have_step = false;
     m->steps = m->layers_streamed = m->h2d_bytes = 0;
+    return NT_OK;
+}
+
+nt_status nt_stream_layers(nt_model *m, const nt_stream_desc *d) { return nt_stream_layers_tiered(m, d, nullptr); }
+
+nt_status nt_tier_plan(const nt_model_config *cfg, const int32_t types[7], uint64_t vram_bytes,
+                       uint64_t pinned_bytes, int32_t *first_streamed, int32_t *first_file) {
+    set_error("");
+    if (!cfg || !types || !first_streamed || !first_file) return fail(NT_EINVAL, "nt_tier_plan: null pointer");
+    size_t offs[kBlobOrder], bytes = 0;
+    if (nt_status s = nt_layer_blob_layout(cfg, types, offs, &bytes)) return s;
+    const uint64_t L = uint64_t(cfg->n_layers);
+    const uint64_t in_vram = std::min<uint64_t>(L, vram_bytes / bytes);
+    const uint64_t in_ram = std::min<uint64_t>(L - in_vram, pinned_bytes / bytes);
+    *first_streamed = int32_t(in_vram);
+    *first_file = int32_t(in_vram + in_ram);
     return NT_OK;
 }
 
@@ -583,6 +970,31 @@ nt_status nt_stream_stats_get(nt_model *m, nt_stream_stats *out) {
     out->compute_ms = comp;
     if (hipEventElapsedTime(&ms, m->step_t0, m->step_t1) == hipSuccess) out->wall_ms = ms;
     (void)hipGetLastError();
+    return NT_OK;
+}
+
+nt_status nt_file_stats_get(nt_model *m, nt_file_stats *out) {
+    set_error("");
+    if (!m || !out) return fail(NT_EINVAL, "nt_file_stats_get: null pointer");
+    std::memset(out, 0, sizeof(*out));
+    FileTier *ft = m->file.get();
+    if (!m->streaming || !ft) return fail(NT_ESTATE, "nt_file_stats_get: no file tier");
+    std::lock_guard<std::mutex> lk(ft->mu);
+    out->reads = ft->reads;
+    out->read_bytes = ft->read_bytes;
+    out->direct = ft->direct ? 1 : 0;
+    out->file_layers = ft->count;
+    double busy = 0.0, lo = 0.0, hi = 0.0;
+    bool any = false;
+    for (int f = 0; f < ft->count; ++f) {
+        if (ft->state[f] != 1) continue;
+        busy += ft->t1[f] - ft->t0[f];
+        if (!any || ft->t0[f] < lo) lo = ft->t0[f];
+        if (!any || ft->t1[f] > hi) hi = ft->t1[f];
+        any = true;
+    }
+    out->read_ms = busy * 1e3;
+    out->read_span_ms = any ? (hi - lo) * 1e3 : 0.0;
     return NT_OK;
 }
 

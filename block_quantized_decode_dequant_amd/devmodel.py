@@ -9,6 +9,7 @@ host-side generators and the oracle's encoder instead.)
 """
 from __future__ import annotations
 
+import numpy as np
 import torch
 
 from . import nt
@@ -125,8 +126,9 @@ def kv_bytes_per_token(s: ModelShape, pos: int) -> int:
     return s.n_layers * 2 * s.n_kv_heads * (pos + 1) * s.head_dim * 2
 
 
-def fill_streamed_blobs(s: ModelShape, first: int, seed: int = 0, device=None):
-    """Pinned host blobs for layers [first, n_layers) in nt_layer_blob_layout order."""
+def fill_streamed_blobs(s: ModelShape, first: int, seed: int = 0, device=None, last: int | None = None):
+    """Pinned host blobs for layers [first, last) (last defaults to n_layers)
+    in nt_layer_blob_layout order."""
     dev = device or torch.device("cuda:0")
     types = tensor_types(s.weights)
     tlist = [types[n] for n in MATS]
@@ -136,10 +138,11 @@ def fill_streamed_blobs(s: ModelShape, first: int, seed: int = 0, device=None):
     stage = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
     # one pinned region sliced per layer (a pinned allocator may round each
     # separate allocation up to a power of two)
-    ns = s.n_layers - first
+    last = s.n_layers if last is None else last
+    ns = last - first
     pinned = torch.empty(max(ns, 1) * nbytes, dtype=torch.uint8, pin_memory=True)
     blobs = []
-    for l in range(first, s.n_layers):
+    for l in range(first, last):
         for i, name in enumerate(MATS):
             rows, cols = matrix_shape(s, name)
             size = rows * nt.row_bytes(types[name], cols)
@@ -149,3 +152,43 @@ def fill_streamed_blobs(s: ModelShape, first: int, seed: int = 0, device=None):
         blobs.append(h)
     torch.cuda.synchronize()
     return blobs, nbytes
+
+
+FILE_ALIGN = 4096
+
+
+def write_layer_file(path, blobs, nbytes: int) -> int:
+    """Writes layer blobs (host numpy uint8 arrays or CPU tensors of nbytes
+    each) back to back at a stride of nbytes rounded up to 4096, so blob j
+    starts at j * stride; returns the stride."""
+    stride = (nbytes + FILE_ALIGN - 1) // FILE_ALIGN * FILE_ALIGN
+    pad = bytes(stride - nbytes)
+    with open(path, "wb") as fh:
+        for b in blobs:
+            a = b if isinstance(b, np.ndarray) else b.numpy()
+            fh.write(memoryview(np.ascontiguousarray(a)))
+            fh.write(pad)
+    return stride
+
+
+def write_streamed_file(s: ModelShape, first: int, path, seed: int = 0, device=None):
+    """Layers [first, n_layers) of the device-built model as a layer file
+    (nt_layer_blob_layout order, 4096-byte stride); returns (stride, blob bytes)."""
+    dev = device or torch.device("cuda:0")
+    types = tensor_types(s.weights)
+    tlist = [types[n] for n in MATS]
+    cfg = nt.model_config(s.n_layers, s.hidden, s.n_q_heads, s.n_kv_heads, s.head_dim, s.ffn, s.vocab,
+                          s.ctx_cap, s.rms_eps, s.rope_theta)
+    offs, nbytes = nt.nt_layer_blob_layout(cfg, tlist)
+    stage = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+
+    def blobs():
+        for l in range(first, s.n_layers):
+            for i, name in enumerate(MATS):
+                rows, cols = matrix_shape(s, name)
+                size = rows * nt.row_bytes(types[name], cols)
+                encode_into(stage[offs[i]:offs[i] + size], types[name], rows, cols, seed, 16 + 16 * l + i)
+            yield stage.cpu()
+
+    stride = write_layer_file(path, blobs(), nbytes)
+    return stride, nbytes

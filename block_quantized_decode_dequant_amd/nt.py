@@ -13,7 +13,7 @@ import os
 
 from . import build as _build
 
-NT_OK, NT_EINVAL, NT_ESHAPE, NT_EALIGN, NT_ENOMEM, NT_EHIP, NT_ESTATE, NT_ENODEV = range(8)
+NT_OK, NT_EINVAL, NT_ESHAPE, NT_EALIGN, NT_ENOMEM, NT_EHIP, NT_ESTATE, NT_ENODEV, NT_EIO = range(9)
 F32, F16, Q4_0, Q8_0, Q4_K, Q5_K, Q6_K = 0, 1, 2, 8, 12, 13, 14
 QTYPES = {"f32": F32, "f16": F16, "q4_0": Q4_0, "q8_0": Q8_0, "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K}
 BLOCK_ELEMS = {Q8_0: 32, Q4_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
@@ -318,6 +318,17 @@ class StreamStats(C.Structure):
                 ("copy_ms", C.c_double), ("compute_ms", C.c_double), ("wall_ms", C.c_double)]
 
 
+class FileTier(C.Structure):
+    _fields_ = [("path", C.c_char_p), ("first_file_layer", C.c_int32), ("offset", C.c_uint64),
+                ("stride", C.c_uint64), ("h_staging", C.c_void_p * 2), ("staging_bytes", C.c_size_t),
+                ("direct", C.c_int32)]
+
+
+class FileStats(C.Structure):
+    _fields_ = [("reads", C.c_uint64), ("read_bytes", C.c_uint64), ("read_ms", C.c_double),
+                ("read_span_ms", C.c_double), ("direct", C.c_int32), ("file_layers", C.c_int32)]
+
+
 def _declare_model(L):
     vp, st = C.c_void_p, C.c_int
     sig = {
@@ -330,6 +341,10 @@ def _declare_model(L):
                                       C.POINTER(C.c_size_t)]),
         "nt_stream_layers": (st, [vp, C.POINTER(StreamDesc)]),
         "nt_stream_stats_get": (st, [vp, C.POINTER(StreamStats)]),
+        "nt_stream_layers_tiered": (st, [vp, C.POINTER(StreamDesc), C.POINTER(FileTier)]),
+        "nt_file_stats_get": (st, [vp, C.POINTER(FileStats)]),
+        "nt_tier_plan": (st, [C.POINTER(ModelConfig), C.POINTER(C.c_int32), C.c_uint64, C.c_uint64,
+                              C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -346,6 +361,16 @@ def model_config(n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, 
 def nt_model_workspace_bytes(cfg: ModelConfig) -> int:
     _declare_model(lib())
     return lib().nt_model_workspace_bytes(C.byref(cfg))
+
+
+def nt_tier_plan(cfg: ModelConfig, types, vram_bytes: int, pinned_bytes: int):
+    """(first_streamed_layer, first_file_layer) for the given tier capacities."""
+    _declare_model(lib())
+    t = (C.c_int32 * 7)(*types)
+    a, b = C.c_int32(0), C.c_int32(0)
+    _check(lib().nt_tier_plan(C.byref(cfg), t, int(vram_bytes), int(pinned_bytes), C.byref(a), C.byref(b)),
+           "nt_tier_plan")
+    return int(a.value), int(b.value)
 
 
 def nt_layer_blob_layout(cfg: ModelConfig, types):
@@ -424,6 +449,28 @@ class Model:
         desc = StreamDesc(first_streamed, C.cast(arr, C.POINTER(C.c_void_p)), bufs, nbytes,
                           _stream(copy_stream))
         _check(lib().nt_stream_layers(self.handle, C.byref(desc)), "nt_stream_layers")
+
+    def stream_layers_tiered(self, first_streamed: int, host_blobs, d_buf0, d_buf1, copy_stream, path: str,
+                             first_file: int, offset: int, stride: int, staging0, staging1, direct: bool = True):
+        """As stream_layers, with layers [first_file, n_layers) read from `path`
+        (blob j at offset + j * stride) through the pinned host staging
+        tensors staging0 / staging1; host_blobs covers [first_streamed, first_file)."""
+        n = len(host_blobs)
+        arr = (C.c_void_p * max(n, 1))(*[b.data_ptr() for b in host_blobs])
+        bufs = (C.c_void_p * 2)(d_buf0.data_ptr(), d_buf1.data_ptr())
+        nbytes = min(d_buf0.numel(), d_buf1.numel()) * d_buf0.element_size()
+        desc = StreamDesc(first_streamed, C.cast(arr, C.POINTER(C.c_void_p)), bufs, nbytes, _stream(copy_stream))
+        sbytes = min(staging0.numel(), staging1.numel()) * staging0.element_size()
+        pbytes = path.encode()
+        ft = FileTier(pbytes, first_file, offset, stride, (C.c_void_p * 2)(staging0.data_ptr(), staging1.data_ptr()),
+                      sbytes, int(bool(direct)))
+        self._stream_keep = [host_blobs, d_buf0, d_buf1, arr, copy_stream, staging0, staging1, pbytes]
+        _check(lib().nt_stream_layers_tiered(self.handle, C.byref(desc), C.byref(ft)), "nt_stream_layers_tiered")
+
+    def file_stats(self) -> dict:
+        s = FileStats()
+        _check(lib().nt_file_stats_get(self.handle, C.byref(s)), "nt_file_stats_get")
+        return {k: getattr(s, k) for k, _ in FileStats._fields_}
 
     def stream_stats(self) -> dict:
         s = StreamStats()

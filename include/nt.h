@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define NT_ABI_VERSION 1
+#define NT_ABI_VERSION 2
 
 typedef enum {
     NT_OK = 0,
@@ -54,7 +54,8 @@ typedef enum {
     NT_ENOMEM = 4,
     NT_EHIP = 5,
     NT_ESTATE = 6,
-    NT_ENODEV = 7
+    NT_ENODEV = 7,
+    NT_EIO = 8
 } nt_status;
 
 /* Weight formats.  Ids are the GGUF type-field numbers.
@@ -344,6 +345,63 @@ typedef struct {
 } nt_stream_stats;
 /* Waits for the last step, then reports. */
 nt_status nt_stream_stats_get(nt_model *m, nt_stream_stats *out);
+
+/* ---- the third tier: layers read from a file ("Performance": a 3-tier
+ * cache of VRAM-resident layers, pinned-RAM layers copied host-to-device, and
+ * an NVMe/mmap fallback; "Main features": the data path is chosen VRAM, then
+ * pinned host RAM, then the fallback; "NVMe direct streaming": the data
+ * flows disk -> pinned staging -> host-to-device copy -> GPU buffer ->
+ * compute) ---------------------------------------------------------------
+ * As nt_stream_layers, with the streamed layers split in two: layers
+ * [first_streamed_layer, first_file_layer) come from desc->h_layer_blobs
+ * (first_file_layer - first_streamed_layer pinned blobs), layers
+ * [first_file_layer, n_layers) from the file: the blob of layer
+ * first_file_layer + j (nt_layer_blob_layout order) starts at byte
+ * offset + j * stride of `path`.  Every step reads each file blob into
+ * h_staging[j % 2] on a reader thread of the library and only once that
+ * read has finished enqueues its host-to-device copy into d_buf and its
+ * layer's compute: the GPU never waits on the host, so a failed read cannot
+ * stall the device.  With `direct` set and a file system that allows it the
+ * file is opened with O_DIRECT (reads bypass the page cache); since a direct
+ * read cannot target HIP-pinned memory, each 32 MiB chunk lands in one of two
+ * library-owned bounce buffers (64 MiB of ordinary host memory, allocated
+ * here and freed with the tier) and is copied into the staging buffer while
+ * the next chunk is read.  Otherwise reads go through the page cache
+ * straight into the staging buffer.  nt_decode_step then
+ * returns after the last file read of the step has finished (it blocks on
+ * the reads), and a failed or short read makes it return NT_EIO: the step's
+ * later layers, the head and the position update are not enqueued, so
+ * logits, *d_next and *d_pos are not valid for that step.
+ * Requirements: offset and stride multiples of 4096, stride >= the blob
+ * size; the file at least offset + (count - 1) * stride + blob bytes long
+ * (NT_EINVAL otherwise; a file that cannot be opened is NT_EIO); h_staging
+ * two pinned host buffers (hipHostMalloc), 4096-byte aligned, each at least
+ * staging_bytes >= the blob size rounded up to 4096 (each read is that long;
+ * the bytes past the blob are ignored).  file == NULL is nt_stream_layers. */
+typedef struct {
+    const char *path;
+    int32_t first_file_layer;
+    uint64_t offset, stride;
+    void *h_staging[2];
+    size_t staging_bytes;
+    int32_t direct;
+} nt_file_tier;
+nt_status nt_stream_layers_tiered(nt_model *m, const nt_stream_desc *desc, const nt_file_tier *file);
+typedef struct {
+    uint64_t reads, read_bytes;   /* totals since the file tier was enabled */
+    double read_ms;               /* last step: summed duration of its file reads */
+    double read_span_ms;          /* last step: first read's start to last read's end */
+    int32_t direct;               /* 1: the file was opened with O_DIRECT (reads bypass the page cache) */
+    int32_t file_layers;
+} nt_file_stats;
+/* Reports the file reads of the last step (complete once nt_decode_step returned). */
+nt_status nt_file_stats_get(nt_model *m, nt_file_stats *out);
+/* The data-path choice as plain arithmetic: with every layer's blob the size
+ * nt_layer_blob_layout gives for `types`, the first floor(vram_bytes / blob)
+ * layers stay resident, the next floor(pinned_bytes / blob) are pinned, the
+ * rest come from the file (each count capped by the layers left). */
+nt_status nt_tier_plan(const nt_model_config *cfg, const int32_t types[7], uint64_t vram_bytes,
+                       uint64_t pinned_bytes, int32_t *first_streamed, int32_t *first_file);
 
 /* ---- encode (quantize) -------------------------------------------------------
  * blocks <- encoding of x[0, n) (device fp32, 4-byte aligned) into packed

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_call():
 
 def test_version_status_and_geometry():
     L = nt.lib()
-    assert L.nt_abi_version() == 1
+    assert L.nt_abi_version() == 2
     for s in range(8):
         assert nt.status_str(s).startswith("NT_")
     assert [L.nt_qtype_block_elems(t) for t in (nt.Q8_0, nt.Q4_0, nt.Q4_K, nt.Q6_K)] == [32, 32, 256, 256]
@@ -212,3 +212,17 @@ def test_attention_argument_errors():
     assert L.nt_attn_decode(C.byref(good), v(A + 4), v(A), v(A), v(A), v(A), v(A), v(A), v(A), ws,
                             None) == nt.NT_EALIGN                     # q must be 16-byte aligned
     assert nt.nt_attn_workspace_bytes(nt.attn_desc(32, 8, 96, 64)) == 0
+
+
+def test_tier_plan_fills_vram_then_pinned_then_file():
+    """The data-path choice (VRAM, then pinned host RAM, then the file) as
+    plain arithmetic over whole layer blobs."""
+    cfg = nt.model_config(80, 8192, 64, 8, 128, 28672, 128256, 4160)
+    types = [nt.Q6_K] * 7
+    _, blob = nt.nt_layer_blob_layout(cfg, types)
+    assert blob == 701890560                       # the write-up's ~670 MB (MiB) per 70B layer
+    assert nt.nt_tier_plan(cfg, types, 24 << 30, 0) == (36, 36)            # 24 GiB resident, the rest from the file
+    assert nt.nt_tier_plan(cfg, types, 24 << 30, 10 * blob + 5) == (36, 46)
+    assert nt.nt_tier_plan(cfg, types, 0, 1 << 50) == (0, 80)
+    assert nt.nt_tier_plan(cfg, types, 1 << 50, 1 << 50) == (80, 80)
+    assert nt.nt_tier_plan(cfg, types, blob - 1, blob) == (0, 1)

@@ -261,3 +261,101 @@ def test_decode_from_a_gguf_file(tmp_path):
         assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), f"step {s}"
     direct.close()
     from_file.close()
+
+
+def _host_blob(L, offs, nbytes):
+    b = np.zeros(nbytes, np.uint8)
+    for off, k in zip(offs, nt.Model.MATS):
+        data = getattr(L, k).data
+        b[off:off + data.size] = data
+    return b
+
+
+def _pinned_staging(nbytes):
+    """Two pinned host buffers, 4096-byte aligned, of at least nbytes each."""
+    s = (nbytes + 4095) // 4096 * 4096
+    raw = torch.empty(2 * s + 4096, dtype=torch.uint8, pin_memory=True)
+    lead = (-raw.data_ptr()) % 4096
+    return raw, raw[lead:lead + s], raw[lead + s:lead + 2 * s]
+
+
+def _three_tier(cfg, w, kk, vv, path, first_streamed, first_file, direct=True):
+    """A model with layers [0, first_streamed) resident, [first_streamed,
+    first_file) pinned, [first_file, n_layers) read from `path`."""
+    from block_quantized_decode_dequant_amd import devmodel
+
+    model, _, _ = upload(cfg, w, kk, vv)
+    types = [getattr(w.layers[first_streamed], k).type for k in nt.Model.MATS]
+    offs, nbytes = nt.nt_layer_blob_layout(model.cfg, types)
+    blobs = []
+    for L in w.layers[first_streamed:first_file]:
+        b = torch.zeros(nbytes, dtype=torch.uint8, pin_memory=True)
+        b.copy_(torch.from_numpy(_host_blob(L, offs, nbytes)))
+        blobs.append(b)
+    stride = devmodel.write_layer_file(path, (_host_blob(L, offs, nbytes) for L in w.layers[first_file:]), nbytes)
+    dbuf = [torch.empty(nbytes, dtype=torch.uint8, device=device()) for _ in range(2)]
+    keep, s0, s1 = _pinned_staging(nbytes)
+    copy_stream = torch.cuda.Stream()
+    model.stream_layers_tiered(first_streamed, blobs, dbuf[0], dbuf[1], copy_stream, str(path), first_file, 0,
+                               stride, s0, s1, direct=direct)
+    model._test_keep = [keep, blobs, dbuf]
+    return model, nbytes, stride
+
+
+@pytest.mark.parametrize("direct", [True, False], ids=["o_direct", "page_cache"])
+def test_three_tiers_match_resident_and_the_oracle(tmp_path, direct):
+    """Layers 0-1 resident, 2-3 from pinned host blobs, 4-6 read from a file
+    each step (host-ordered: read, then copy, then compute): bit for bit the
+    resident run, and the oracle's greedy decode."""
+    cfg = tiny_config(n_layers=7)
+    w = build_oracle_model(cfg, seed=16, wtype="mix")
+    kk, vv = kv_prefix(cfg, 5, 6)
+    res, _, _ = upload(cfg, w, kk, vv)
+    res.set_graph(False)
+    ref, _ = _run_steps(res, cfg, 6, 3, 5)
+    res.close()
+    model, nbytes, stride = _three_tier(cfg, w, kk, vv, tmp_path / "layers.bin", 2, 4, direct=direct)
+    dec = O.Decoder(cfg, w, kk.copy(), vv.copy())
+    got = []
+    greedy_parity_run(model, dec, cfg.vocab, 6, 3, 5, what="three tiers", graph=False,
+                      each_step=lambda s_, lg: got.append(lg.copy()))
+    for s, (a, b) in enumerate(zip(ref, got)):
+        assert np.array_equal(a, b), f"three-tier step {s} differs from resident"
+    fs = model.file_stats()
+    print(f"file tier: direct={fs['direct']} reads={fs['reads']} read_ms={fs['read_ms']:.3f}", flush=True)
+    assert fs["file_layers"] == 3 and fs["reads"] == 5 * 3 and fs["read_bytes"] == 5 * 3 * nbytes
+    st = model.stream_stats()
+    assert st["layers_streamed"] == 5 * 5 and st["h2d_bytes"] == 5 * 5 * nbytes
+    model.stream_layers(None, None, None, None, None)
+    model.close()
+
+
+def test_file_tier_read_failure_returns_eio_and_recovers(tmp_path):
+    """A layer file cut short after the tier was enabled: the step's read of
+    the missing blob fails, nt_decode_step returns NT_EIO having enqueued
+    nothing that waits on it (the device still drains), the position does
+    not advance; with the file restored the next step matches the oracle."""
+    cfg = tiny_config(n_layers=4)
+    w = build_oracle_model(cfg, seed=17, wtype=O.Q4_K)
+    kk, vv = kv_prefix(cfg, 5, 6)
+    path = tmp_path / "layers.bin"
+    model, nbytes, stride = _three_tier(cfg, w, kk, vv, path, 1, 2, direct=False)
+    full = path.read_bytes()
+    with open(path, "r+b") as fh:
+        fh.truncate(stride + nbytes // 2)       # the second file blob is cut in half
+    dev = device()
+    d_tok = torch.tensor([3], dtype=torch.int32, device=dev)
+    d_pos = torch.tensor([6], dtype=torch.int32, device=dev)
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device=dev)
+    side = torch.cuda.Stream()
+    with pytest.raises(nt.NTError) as ei:
+        with torch.cuda.stream(side):
+            model.step(d_tok, d_pos, logits, d_tok)
+    assert ei.value.status == nt.NT_EIO and "ends inside blob 1" in str(ei.value)
+    torch.cuda.synchronize()                    # nothing queued waits on the failed read
+    assert int(host(d_pos)[0]) == 6
+    path.write_bytes(full)
+    dec = O.Decoder(cfg, w, kk.copy(), vv.copy())
+    greedy_parity_run(model, dec, cfg.vocab, 6, 3, 3, what="after recovery", graph=False)
+    model.stream_layers(None, None, None, None, None)
+    model.close()
