@@ -105,4 +105,41 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// ---- explicit memory waits and asynchronous copies into LDS ----------------
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt
+// fields at their maxima, i.e. no wait on them).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
+
+// One global_load_lds of V bytes per lane: lane i reads base + off (off is
+// per lane, base wave-uniform) and its bytes land at LDS address lds + V*i
+// (lds wave-uniform, through M0).  Written as inline assembly on purpose: the
+// compiler then does not track these LDS writes, so it adds no conservative
+// "wait for every outstanding load" before unrelated LDS reads; every read
+// of a ring stage is preceded by an explicit s_waitcnt on the loads that fill
+// it.  The "memory" clobber keeps the copies ordered against other memory
+// operations in program order.
+template <int V>
+__device__ __forceinline__ void dma(const uint8_t *base, uint32_t off, uint32_t lds) {
+    int m0_out;   // M0 is declared written (an output), so no value of the compiler's lives in it across the copy
+    if constexpr (V == 16)
+        asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     : "={m0}"(m0_out) : "v"(off), "s"(base), "s"(lds) : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                     : "={m0}"(m0_out) : "v"(off), "s"(base), "s"(lds) : "memory");
+    (void)m0_out;
+}
+
+// LDS address (32-bit, as M0 takes it) of a wave-uniform LDS location.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t((lds_void *)p)));
+}
+
+// s_waitcnt immediate that waits for all LDS operations (lgkmcnt 0) only.
+constexpr int kLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
 }  // namespace nt
