@@ -234,9 +234,11 @@ NT_GEMV_FN(nt_gemv_q5_k, NT_Q5_K)
 NT_GEMV_FN(nt_gemv_q6_k, NT_Q6_K)
 
 // ---- batched verify pass ------------------------------------------------------------
-size_t nt_gemm_batch_workspace_bytes(nt_qtype t, int64_t cols) {
-    if (!gemm_batch_type_ok(t) || cols <= 0 || cols > kMaxGemvCols || cols % block_elems(t) != 0) return 0;
-    return gemm_batch_workspace_bytes(t, cols);
+size_t nt_gemm_batch_workspace_bytes(nt_qtype t, int64_t rows, int64_t cols) {
+    if (!gemm_batch_type_ok(t) || rows < 0 || rows > (int64_t(1) << 31) - 1 || cols <= 0 || cols > kMaxGemvCols ||
+        cols % block_elems(t) != 0)
+        return 0;
+    return gemm_batch_workspace_bytes(t, rows, cols);
 }
 
 nt_status nt_gemm_batch(nt_qtype t, const void *W, const float *X, float *Y, int64_t rows, int64_t cols,
@@ -249,10 +251,11 @@ nt_status nt_gemm_batch(nt_qtype t, const void *W, const float *X, float *Y, int
     if (cols > kMaxGemvCols) return fail(NT_ESHAPE, "nt_gemm_batch: cols above 65536");
     if (rows > (int64_t(1) << 31) - 1) return fail(NT_ESHAPE, "nt_gemm_batch: rows above 2^31 - 1");
     if (rows == 0) return NT_OK;
-    if (!W || !X || !Y || !workspace) return fail(NT_EINVAL, "nt_gemm_batch: null pointer");
+    const size_t need = gemm_batch_workspace_bytes(t, rows, cols);
+    if (!W || !X || !Y || (need > 0 && !workspace)) return fail(NT_EINVAL, "nt_gemm_batch: null pointer");
     if (!aligned(W, 16) || !aligned(X, 16) || !aligned(workspace, 16) || !aligned(Y, 4))
         return fail(NT_EALIGN, "nt_gemm_batch: W, X and workspace 16-byte aligned, Y 4-byte aligned");
-    if (workspace_bytes < gemm_batch_workspace_bytes(t, cols))
+    if (workspace_bytes < need)
         return fail(NT_ENOMEM, "nt_gemm_batch: workspace smaller than nt_gemm_batch_workspace_bytes");
     if (nt_status s = need_device()) return s;
     return finish(launch_gemm_batch(t, W, rows, cols, X, k, Y, accumulate, workspace, as_stream(stream)),

@@ -9,30 +9,34 @@
 // products run on the matrix cores (v_mfma_f32_16x16x16_f16):
 //
 //  * the MFMA's M dimension holds the activations, N the 16 weight rows of a
-//    tile, K 16 codes of one scale group (Q8_0, Q4_0) or any 16 codes of a
-//    super-block whose scales are folded into the codes (K-quants).  With N = weight row, every lane applies the
-//    scales of its own row to its own accumulators.
-//  * weight codes become fp16 exactly: small integers, or with the scales
-//    folded in (Q4_K, Q5_K: S_j * q * 2^-14; Q6_K: sc * ql4 and
-//    16 sc (qh2 - 2), the two parts of its code, in two MFMAs).  Nothing
-//    about the weights is rounded.
+//    tile, K 16 codes of one scale group (Q8_0, Q4_0, Q6_K, whose group
+//    scale is applied to the MFMA's fp32 sums) or any 16 codes of a Q4_K /
+//    Q5_K super-block, whose 6-bit scales are folded into the codes.  With
+//    N = weight row, every lane applies the scales of its own row to its own
+//    accumulators.
+//  * weight codes become fp16 exactly: small integers (q, q - 8, q - 32) or
+//    S_j * q * 2^-14 (Q4_K, Q5_K).  Nothing about the weights is rounded.
 //  * each activation is split into fp16 hi + lo (hi = fp16(x), lo =
 //    fp16(x - hi)), which leaves about 2^-22 relative error; the hi parts fill
 //    M rows 0-7 and the lo parts rows 8-15, which the padding of k <= 8 to 16
 //    would otherwise waste.  Products are exact in fp32; the MFMA sums in fp32.
-//  * a prologue kernel writes the split activations once per call in the
-//    order the lanes consume them: each of a wave's eight 16-byte loads per
-//    256 columns reads one contiguous kilobyte.
+//    Activations large enough for a part or a 32-value sum to overflow fp16
+//    are split scaled by a power of two per 256 columns, undone in fp32.
+//  * a first kernel writes each 256-column step's split activations once
+//    (an "activation record") in the order the lanes consume them, so every
+//    row tile reads them with eight 1 KB contiguous loads.
+//  * the weights move through LDS: each wave copies its tiles' row runs with
+//    global_load_lds (whole contiguous runs of a row per instruction; loads
+//    that put 16 rows' bytes into one instruction's lanes, as the MFMA layout
+//    would, reach far less of HBM's bandwidth) and reads its MFMA operands
+//    from LDS.
 //  * MFMA lane layout (16x16x16 f16): src0 lane l holds A[l % 16][4(l/16) + i],
 //    src1 lane l holds B[4(l/16) + i][l % 16], the result lane l holds
 //    D[4(l/16) + i][l % 16], i = 0..3.  Inside one MFMA the order of the 16
 //    K slots is free as long as A and B agree, so each lane takes the codes of
 //    its row that lie together in memory.
-//
-// A workgroup of kWaves waves owns 16 * kTiles rows; each wave takes all its
-// tiles and interleaved 256-column steps, and the waves add their partial
-// sums through LDS in a fixed order.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "device_util.h"
@@ -46,11 +50,7 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t w2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;   // waves of a workgroup (they split the columns)
-// 16-row tiles of a wave (they share the activation loads): 2, or 4 for
-// Q4_K matrices of at least kTallRows rows (enough workgroups to fill the
-// chip; fewer activation bytes per weight byte)
-constexpr int kTallRows = 16384;
+constexpr int kNumCUs = 256;   // compute units of an MI355X
 
 // Order of a dword's four bytes in the K slots of one lane: the halves of
 // (w & 0x00ff00ff) then of (w >> 8 & 0x00ff00ff), i.e. bytes 0, 2, 1, 3.
@@ -80,13 +80,13 @@ __device__ __forceinline__ f4 mfma(h4 a, h4 b, f4 c) { return __builtin_amdgcn_m
 // and get scale 0.
 struct BQ80 {
     static constexpr bool kMin = false;
+    static constexpr int kStepBytes = 272, kTiles = 1;
     struct Raw { u32x3 v[8]; };
     __host__ __device__ static int elem(int m, int g, int i) { return 32 * (m >> 1) + 8 * g + 4 * (m & 1) + perm4(i); }
-    __device__ static void load(const uint8_t *row, int s, int g, int nblk, Raw &r) {
+    __device__ static void load(const uint8_t *p, int s, int g, int nblk, Raw &r) {
 #pragma unroll
         for (int bb = 0; bb < 8; ++bb) {
-            const int blk = 8 * s + bb;
-            const uint8_t *b = row + int64_t(blk < nblk ? blk : 0) * 34;
+            const uint8_t *b = p + (8 * s + bb < nblk ? bb : 0) * 34;
             const uint32_t bs = uint32_t(reinterpret_cast<uintptr_t>(b) & 3);   // 0 or 2
             r.v[bb] = ld3(b - bs + 8 * g);
         }
@@ -98,14 +98,13 @@ struct BQ80 {
         const uint32_t b = hadd(((w >> 8) & 0x00ff00ffu) ^ 0x64806480u, _Float16(-1152.f));
         return pack(a, b);
     }
-    __device__ static void compute(const Raw &r, const uint8_t *row, int s, int nblk, const h4 *xa, h4, f4 &acc) {
+    __device__ static void compute(const Raw &r, const uint8_t *p, int s, int, int nblk, const h4 *xa, h4, f4 &acc) {
         const int src = int(__lane_id() & 15);          // lane group 0 of this row
         const uint32_t sel2 = shift_sel(2);
 #pragma unroll
         for (int bb = 0; bb < 8; ++bb) {
-            const int blk = 8 * s + bb;
-            const bool live = blk < nblk;
-            const uint8_t *b = row + int64_t(live ? blk : 0) * 34;
+            const bool live = 8 * s + bb < nblk;
+            const uint8_t *b = p + (live ? bb : 0) * 34;
             const uint32_t bs = uint32_t(reinterpret_cast<uintptr_t>(b) & 3);
             const u32x3 v = r.v[bb];
             const uint32_t w0 = bs ? v.y : funnel(v.y, v.x, sel2);
@@ -131,18 +130,21 @@ struct BQ80 {
 // sums (hi in K slots 0-7, lo in 8-15), B = M_j.
 struct BQ4K {
     static constexpr bool kMin = true;
+    static constexpr int kStepBytes = 144, kTiles = 2;
     struct Raw { u32x4 h, q0, q1; };
     __host__ __device__ static int code_byte(int w, int g) { return w < 4 ? 16 * g + 4 * w : 64 + 16 * g + 4 * (w - 4); }
     __host__ __device__ static int elem(int m, int g, int i) {
         const int c = code_byte(m >> 1, g) + perm4(i);
         return 32 * (2 * (c >> 5) + (m & 1)) + (c & 31);
     }
-    __device__ static void load(const uint8_t *row, int s, int g, int, Raw &r) {
-        const uint8_t *b = row + int64_t(s) * 144;
+    __device__ static void load(const uint8_t *b, int, int g, int, Raw &r) {
         r.h = ld4(b);
         r.q0 = ld4(b + 16 + 16 * g);
         r.q1 = ld4(b + 80 + 16 * g);
     }
+    // 6-bit scale S_j and min M_j of sub-block j from the 12 scale bytes
+    // (words h.y, h.z, h.w): j < 4: low 6 bits of bytes j and j + 4; j >= 4:
+    // low / high nibble of byte j + 4 with the top two bits of byte j - 4 / j.
     __device__ static void scale_min(const u32x4 &h, int j, uint32_t &S, uint32_t &M) {
         const uint32_t sc[3] = {h.y, h.z, h.w};
         auto byte = [&](int k) { return (sc[k >> 2] >> (8 * (k & 3))) & 0xffu; };
@@ -154,14 +156,15 @@ struct BQ4K {
             M = (byte(j + 4) >> 4) | ((byte(j) >> 6) << 4);
         }
     }
-    __device__ static void compute(const Raw &r, int g, const h4 *xa, h4 xm, f4 &acc) {
-        uint32_t S[8], M[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) scale_min(r.h, j, S[j], M[j]);
-        // the two code pairs of this lane: chunks g / 2 (bytes 16g..) and 2 + g / 2 (bytes 64 + 16g..)
-        const int hp = g >> 1;
-        const uint32_t Sa0 = hp ? S[2] : S[0], Sa1 = hp ? S[3] : S[1];
-        const uint32_t Sb0 = hp ? S[6] : S[4], Sb1 = hp ? S[7] : S[5];
+    __device__ static void compute(const Raw &r, const uint8_t *, int, int g, int, const h4 *xa, h4 xm, f4 &acc) {
+        // the two code pairs of this lane: chunks g / 2 (bytes 16g..) and
+        // 2 + g / 2 (bytes 64 + 16g..), sub-blocks 2hp, 2hp + 1 and 4 + 2hp,
+        // 5 + 2hp; only those four scales are decoded (bit fields at a
+        // lane-dependent offset)
+        const uint32_t o = 16u * uint32_t(g >> 1);
+        const uint32_t Sa0 = __builtin_amdgcn_ubfe(r.h.y, o, 6), Sa1 = __builtin_amdgcn_ubfe(r.h.y, o + 8, 6);
+        const uint32_t Sb0 = __builtin_amdgcn_ubfe(r.h.w, o, 4) | (__builtin_amdgcn_ubfe(r.h.y, o + 6, 2) << 4);
+        const uint32_t Sb1 = __builtin_amdgcn_ubfe(r.h.w, o + 8, 4) | (__builtin_amdgcn_ubfe(r.h.y, o + 14, 2) << 4);
         const _Float16 fa0 = _Float16(float(Sa0 * 1024u)), fa1 = _Float16(float(Sa1 * 64u));
         const _Float16 fb0 = _Float16(float(Sb0 * 1024u)), fb1 = _Float16(float(Sb1 * 64u));
         const uint32_t words[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
@@ -173,11 +176,19 @@ struct BQ4K {
             c = mfma(xa[2 * w], pack(hmul(v & 0x000f000fu, f0), hmul(t & 0x000f000fu, f0)), c);
             c = mfma(xa[2 * w + 1], pack(hmul(v & 0x00f000f0u, f1), hmul(t & 0x00f000f0u, f1)), c);
         }
-        // B of the min MFMA: K slot 4g + i takes M_{(4g + i) & 7}
-        const int jb = 4 * (g & 1);
-        const uint32_t m0 = jb ? M[4] : M[0], m1 = jb ? M[5] : M[1], m2 = jb ? M[6] : M[2], m3 = jb ? M[7] : M[3];
-        const h4 mb = {_Float16(float(m0)), _Float16(float(m1)), _Float16(float(m2)), _Float16(float(m3))};
-        const f4 cm = mfma(xm, mb, f4{0.f, 0.f, 0.f, 0.f});
+        // B of the min MFMA: K slot 4g + i takes M_{(4g + i) & 7}: M_i (low 6
+        // bits of byte 4 + i) for even g, M_{4+i} (high nibble of byte 8 + i,
+        // top bits of byte 4 + i) for odd g
+        const bool odd = g & 1;
+        const uint32_t src = odd ? r.h.w : r.h.z, off = odd ? 4u : 0u, wlo = odd ? 4u : 6u, whi = odd ? 2u : 0u;
+        _Float16 mv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t M = __builtin_amdgcn_ubfe(src, 8u * i + off, wlo) |
+                               (__builtin_amdgcn_ubfe(r.h.z, 8u * i + 6u, whi) << 4);
+            mv[i] = _Float16(float(M));
+        }
+        const f4 cm = mfma(xm, h4{mv[0], mv[1], mv[2], mv[3]}, f4{0.f, 0.f, 0.f, 0.f});
         const float d = h2f(r.h.x) * 16384.f, dmin = h2f(r.h.x >> 16);
         acc += d * c - dmin * cm;
     }
@@ -192,13 +203,13 @@ struct BQ4K {
 // 20 - bs of the block, inside the word that holds its last bytes.
 struct BQ40 {
     static constexpr bool kMin = false;
+    static constexpr int kStepBytes = 144, kTiles = 2;
     struct Raw { u32x2 v[8]; };
     __host__ __device__ static int elem(int m, int g, int i) { return 32 * (m >> 1) + 16 * (m & 1) + 4 * g + perm4(i); }
-    __device__ static void load(const uint8_t *row, int s, int g, int nblk, Raw &r) {
+    __device__ static void load(const uint8_t *p, int s, int g, int nblk, Raw &r) {
 #pragma unroll
         for (int bb = 0; bb < 8; ++bb) {
-            const int blk = 8 * s + bb;
-            const uint8_t *b = row + int64_t(blk < nblk ? blk : 0) * 18;
+            const uint8_t *b = p + (8 * s + bb < nblk ? bb : 0) * 18;
             const uint32_t bs = uint32_t(reinterpret_cast<uintptr_t>(b) & 3);   // 0 or 2
             r.v[bb] = *reinterpret_cast<const u32x2 *>(b - bs + 4 * g);
         }
@@ -208,14 +219,13 @@ struct BQ40 {
         const uint32_t b = hadd(((w >> 8) & 0x000f000fu) | 0x64006400u, _Float16(-1032.f));
         return pack(a, b);
     }
-    __device__ static void compute(const Raw &r, const uint8_t *row, int s, int nblk, const h4 *xa, h4, f4 &acc) {
+    __device__ static void compute(const Raw &r, const uint8_t *p, int s, int, int nblk, const h4 *xa, h4, f4 &acc) {
         const int src = int(__lane_id() & 15);          // lane group 0 of this row
         const uint32_t sel2 = shift_sel(2);
 #pragma unroll
         for (int bb = 0; bb < 8; ++bb) {
-            const int blk = 8 * s + bb;
-            const bool live = blk < nblk;
-            const uint8_t *b = row + int64_t(live ? blk : 0) * 18;
+            const bool live = 8 * s + bb < nblk;
+            const uint8_t *b = p + (live ? bb : 0) * 18;
             const uint32_t bs = uint32_t(reinterpret_cast<uintptr_t>(b) & 3);
             const u32x2 v = r.v[bb];
             const uint32_t w = bs ? v.y : funnel(v.y, v.x, sel2);
@@ -235,16 +245,16 @@ struct BQ40 {
 // S q <= 63 * 31 = 1953 keeps S q 2^-14 exact in fp16.
 struct BQ5K {
     static constexpr bool kMin = true;
+    static constexpr int kStepBytes = 176, kTiles = 1;
     struct Raw { u32x4 h, qh, q0, q1; };
     __host__ __device__ static int elem(int m, int g, int i) { return BQ4K::elem(m, g, i); }
-    __device__ static void load(const uint8_t *row, int s, int g, int, Raw &r) {
-        const uint8_t *b = row + int64_t(s) * 176;
+    __device__ static void load(const uint8_t *b, int, int g, int, Raw &r) {
         r.h = ld4(b);
         r.qh = ld4(b + 16 + 16 * (g & 1));
         r.q0 = ld4(b + 48 + 16 * g);
         r.q1 = ld4(b + 112 + 16 * g);
     }
-    __device__ static void compute(const Raw &r, int g, const h4 *xa, h4 xm, f4 &acc) {
+    __device__ static void compute(const Raw &r, const uint8_t *, int, int g, int, const h4 *xa, h4 xm, f4 &acc) {
         uint32_t S[8], M[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) BQ4K::scale_min(r.h, j, S[j], M[j]);
@@ -276,218 +286,323 @@ struct BQ5K {
 // ---- Q6_K: a step is one super-block (210 bytes, so only 2-byte aligned).
 // Value (h, k, l) = 128h + 32k + l has code q = ql4 + 16 qh2 (ql4: nibble
 // k / 2 of ql[64h + 32 (k % 2) + l], qh2: bits 2k, 2k + 1 of qh[32h + l]) and
-// scale sc = scales[8h + 2k + l / 16]; q - 32 = ql4 + 16 (qh2 - 2), and both
-// sc * ql4 (<= 1920) and 16 sc (qh2 - 2) (16 times an integer <= 256) are
-// exact in fp16, so the scales fold into the codes: two MFMAs per operand
-// (one per part) cover any mix of scale groups and d is applied once.  Lane
-// group g takes ql bytes [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16) (each
-// load reads 64 contiguous bytes of a row), the qh bytes of the same values
-// ([16 (g % 2), + 16) of each 32-byte half) and scale bytes g, g + 4,
-// g + 8, g + 12.  Every 16-byte piece is two aligned loads and a funnel.
+// scale scales[8h + 2k + l / 16].  MFMA m covers scale group m = 8h + 2k +
+// l / 16 (its 16 values share a scale): lane group g takes l = 16 (m % 2) +
+// 4g + perm4(i), i.e. four consecutive ql bytes and four consecutive qh
+// bytes, one word of each.  The six-bit codes become q - 32 exactly in fp16
+// (a byte permute sets the exponent byte 0x64, one packed subtraction), the
+// MFMA sums one group, and the group's d * scale is applied in fp32.  Every
+// word is two aligned reads and a funnel.
 struct BQ6K {
     static constexpr bool kMin = false;
-    struct Raw { u32x4 v[5]; uint32_t e[5], dw; };   // ql pieces 0, 1, qh pieces 0, 1, scales; next words; d
+    static constexpr int kStepBytes = 210, kTiles = 1;
+    // word pairs at byte offsets 4g + 16j (ql, j < 8), 128 + 4g + 16j (qh,
+    // j < 4) from the word-aligned block start; scale words 192..208 (the
+    // last also holds d)
+    struct Raw { uint32_t ql[8][2], qh[4][2], sc[5]; };
     __host__ __device__ static int elem(int m, int g, int i) {
-        const int c = BQ4K::code_byte(m >> 1, g) + perm4(i);
-        return 128 * (c >> 6) + 32 * (((c >> 5) & 1) + 2 * (m & 1)) + (c & 31);
+        return 128 * (m >> 3) + 32 * ((m >> 1) & 3) + 16 * (m & 1) + 4 * g + perm4(i);
     }
-    __device__ static void load(const uint8_t *row, int s, int g, int, Raw &r) {
-        const uint8_t *b = row + int64_t(s) * 210;
+    __device__ static void load(const uint8_t *b, int, int g, int, Raw &r) {
+        const uint8_t *a = b - (reinterpret_cast<uintptr_t>(b) & 2);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            r.ql[j][0] = ld1(a + 4 * g + 16 * j);
+            r.ql[j][1] = ld1(a + 4 * g + 16 * j + 4);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            r.qh[j][0] = ld1(a + 128 + 4 * g + 16 * j);
+            r.qh[j][1] = ld1(a + 128 + 4 * g + 16 * j + 4);
+        }
+#pragma unroll
+        for (int j = 0; j < 5; ++j) r.sc[j] = ld1(a + 192 + 4 * j);
+    }
+    __device__ static void compute(const Raw &r, const uint8_t *b, int, int, int, const h4 *xa, h4, f4 &acc) {
         const uint32_t sh = uint32_t(reinterpret_cast<uintptr_t>(b) & 2);
-        const uint8_t *a = b - sh;
-        const int off[5] = {16 * g, 64 + 16 * g, 128 + 16 * (g & 1), 160 + 16 * (g & 1), 192};
-#pragma unroll
-        for (int t = 0; t < 5; ++t) {
-            r.v[t] = ld4(a + off[t]);
-            r.e[t] = ld1(a + off[t] + (sh ? 16 : 12));     // with sh == 0 the last word again
-        }
-        r.dw = ld1(a + 208);                                 // d: bytes 208, 209
-    }
-    __device__ static void compute(const Raw &r, const uint8_t *row, int s, int g, const h4 *xa, f4 &acc) {
-        const uint32_t sh = uint32_t(reinterpret_cast<uintptr_t>(row + int64_t(s) * 210) & 2);
         const uint32_t sel = shift_sel(sh);
-        uint32_t w[5][4];
+        uint32_t ql[8], qh[4], sc[4];
 #pragma unroll
-        for (int t = 0; t < 5; ++t) {
-            w[t][0] = funnel(r.v[t].y, r.v[t].x, sel);
-            w[t][1] = funnel(r.v[t].z, r.v[t].y, sel);
-            w[t][2] = funnel(r.v[t].w, r.v[t].z, sel);
-            w[t][3] = funnel(r.e[t], r.v[t].w, sel);
-        }
-        const float d = h2f(sh ? r.dw >> 16 : r.dw);
-        const uint32_t kk2 = 2 * uint32_t(g >> 1);          // qh bit of k = g / 2 (+4 for the high nibbles)
-        f4 c = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 8; ++j) ql[j] = funnel(r.ql[j][1], r.ql[j][0], sel);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qh[j] = funnel(r.qh[j][1], r.qh[j][0], sel);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sc[j] = funnel(r.sc[j + 1], r.sc[j], sel);
+        const float d = h2f(sh ? r.sc[4] >> 16 : r.sc[4]);
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
-            const int wi = m >> 1, nib = m & 1, half = wi >> 2;
-            const uint32_t v = w[half][wi & 3], hb = w[2 + half][wi & 3];
-            const int scw = nib + 2 * half;                 // scale groups g + 4 nib + 8 half: byte g of word scw
-            const float sc = float(int8_t((w[4][scw] >> (8 * g)) & 0xffu));
-            const _Float16 f = _Float16(sc), f16x = _Float16(16.f * sc);
-            const uint32_t ql4 = (nib ? v >> 4 : v) & 0x0f0f0f0fu;
-            const uint32_t qh2 = (hb >> (kk2 + 4 * nib)) & 0x03030303u;
-            const h4 b1 = pack(hmul(hadd((ql4 & 0x00ff00ffu) | 0x64006400u, _Float16(-1024.f)), f),
-                               hmul(hadd(((ql4 >> 8) & 0x00ff00ffu) | 0x64006400u, _Float16(-1024.f)), f));
-            const h4 b2 = pack(hmul(hadd((qh2 & 0x00ff00ffu) | 0x64006400u, _Float16(-1026.f)), f16x),
-                               hmul(hadd(((qh2 >> 8) & 0x00ff00ffu) | 0x64006400u, _Float16(-1026.f)), f16x));
-            c = mfma(xa[m], b1, c);
-            c = mfma(xa[m], b2, c);
+            const int h = m >> 3, k = (m >> 1) & 3, lg = m & 1;
+            const uint32_t w = ql[4 * h + 2 * (k & 1) + lg];
+            const uint32_t ql4 = ((k >> 1) ? w >> 4 : w) & 0x0f0f0f0fu;
+            const uint32_t q6 = ql4 | (((qh[2 * h + lg] >> (2 * k)) & 0x03030303u) << 4);
+            // fp16 1024 + q for bytes 0, 2 and 1, 3; minus 1056 gives q - 32
+            const uint32_t p0 = hadd(__builtin_amdgcn_perm(0x64646464u, q6, 0x04020400u), _Float16(-1056.f));
+            const uint32_t p1 = hadd(__builtin_amdgcn_perm(0x64646464u, q6, 0x04030401u), _Float16(-1056.f));
+            const f4 c = mfma(xa[m], pack(p0, p1), f4{0.f, 0.f, 0.f, 0.f});
+            const float ds = d * float(int8_t((sc[m >> 2] >> (8 * (m & 3))) & 0xffu));
+            acc += ds * c;
         }
-        acc += d * c;
     }
 };
 
-// Split activations in lane order: xp[(((s * 8 + m / 2) * 64 + lane) * 2 + m % 2) * 4 + i]
-// (fp16) = hi or lo part of x_n[256 s + elem(m, g, i)], n = lane % 8,
-// lo for lane % 16 >= 8, zero for n >= k or past cols.  For K-quant mins,
-// xm[(s * 64 + lane) * 4 + i]: K slot 4g + i of lane (b, g) is the hi (slots
-// 0-7) or lo (8-15) part of the fp32 sum of x_b over sub-block (4g + i) & 7
-// (four-way partial sums of 8 float4s, in a fixed order); zero for b >= 8.
 __device__ __forceinline__ uint16_t hbits(float v) { return __half_as_ushort(__float2half_rn(v)); }
 __device__ __forceinline__ uint16_t split_part(float v, bool lo) {
     const __half hi = __float2half_rn(v);
     return lo ? hbits(v - __half2float(hi)) : __half_as_ushort(hi);
 }
 
+typedef uint32_t u32x4a __attribute__((ext_vector_type(4)));   // 16-byte aligned
+
+// Geometry of one format's pipeline.  Each wave streams T 16-row tiles
+// through its own ring of S LDS stages, one 256-column step per stage.  A
+// tile row is the Lc bytes from the 16-byte granule that holds the row's
+// step start: they cover the L bytes of the step whatever its offset in the
+// granule, and each copy instruction moves 64 whole granules (1 KB).  Rows
+// sit Lp bytes apart in LDS, an odd number of granules, so the 16 lanes that
+// read one offset of 16 rows hit distinct banks; a tile takes NI whole copy
+// instructions (the lanes past the 16 rows fill padding).
 template <class F>
-__global__ void __launch_bounds__(256) bgemm_prep(const float *__restrict__ X, int64_t cols, int k, int nsteps,
-                                                  uint32_t *__restrict__ xp, uint16_t *__restrict__ xm) {
-    const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t nx = int64_t(nsteps) * 1024;
-    if (t < nx) {
-        // one thread per (step, lane, MFMA): four fp16 parts
-        const int m = int(t & 15), lane = int((t >> 4) & 63);
-        const int64_t s = t >> 10;
-        const int b = lane & 15, g = lane >> 4, n = b & 7;
-        const bool lo = b >= 8;
-        // the four values are x[e0 + perm4(i)] for a 4-aligned e0 in every
-        // format: one 16-byte load (cols is a multiple of 32)
-        const int64_t e0 = s * 256 + F::elem(m, g, 0);
-        const float4 v = (n < k && e0 < cols) ? *reinterpret_cast<const float4 *>(X + n * cols + e0)
-                                              : float4{0.f, 0.f, 0.f, 0.f};
-        const float vv[4] = {v.x, v.y, v.z, v.w};
+struct Geo {
+    static constexpr int T = F::kTiles;
+    static constexpr int S = 3;                                  // ring stages: two steps copied ahead
+    static constexpr int NW = 4;                                 // waves per workgroup
+    static constexpr int L = F::kStepBytes;
+    static constexpr int Lc = (L + 15 + 15) / 16 * 16;
+    static constexpr int Lp = ((Lc / 16) & 1) ? Lc : Lc + 16;
+    static constexpr int NI = (16 * Lp + 1023) / 1024;           // copy instructions per tile
+    static constexpr int TB = NI * 1024;                         // LDS bytes of one tile
+    static constexpr int WAVE = S * T * TB;                      // LDS bytes of one wave's ring
+    static constexpr int LDS = NW * WAVE;
+    static constexpr int REC = 8192 + (F::kMin ? 512 : 0) + 32;  // activation record of one step
+    static constexpr int WPC = 2;                                // workgroups per CU (two waves per SIMD)
+    static_assert(WPC * LDS <= 160 * 1024, "LDS of two workgroups per CU");
+};
+
+// Activation records, one workgroup per 256-column step s.  Record layout
+// (bytes): [0, 8192) the split activations in the order the lanes consume
+// them: u32x2 at ((m / 2) * 64 + lane) * 16 + (m % 2) * 8 holds, as two
+// fp16 pairs, the hi (lane % 16 < 8) or lo part of s_n x_n[256 s +
+// elem(m, g, perm4(i))], n = lane % 8, g = lane / 16 (zero for n >= k or
+// past cols); K-quants then [8192, 8704): uint16 at (lane * 4 + i) * 2, K
+// slot 4g + i of the min MFMA: hi (slots 0-7) or lo part of the fp32 sum of
+// s_b x_b over sub-block (4g + i) % 8, b = lane % 16 (zero for b >= 8); the
+// last 32 bytes: 1 / s_n for n = 0..7.  s_n = 2^-e_n is the largest power
+// of two scale (at most 1) that keeps 32 max |x_n| over the step below
+// 2^14, so no fp16 part and no sub-block sum overflows: an exact scaling
+// that the main kernel undoes on the step's fp32 sums.
+template <class F>
+__global__ void __launch_bounds__(256) bgemm_prep(const float *__restrict__ X, int64_t cols, int k,
+                                                  uint8_t *__restrict__ rec) {
+    using G = Geo<F>;
+    __shared__ __attribute__((aligned(16))) float xs[8][260];
+    const int s = blockIdx.x, t = threadIdx.x;
+    uint8_t *const out = rec + int64_t(s) * G::REC;
+    {
+        const int n = t >> 5, c = 8 * (t & 31);
+        const int64_t col = int64_t(s) * 256 + c;   // cols is a multiple of 32: all 8 columns or none
+        float4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+        if (n < k && col < cols) {
+            const float4 *px = reinterpret_cast<const float4 *>(X + n * cols + col);
+            a = px[0];
+            b = px[1];
+        }
+        float mx = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                         fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 32));
+        int e2 = 0;
+        (void)frexpf(fminf(mx, 1.0e36f) * 32.f, &e2);   // 32 max = f 2^e2, f in [0.5, 1)
+        const int e = min(max(e2 - 14, 0), 120);
+        const float sd = ldexpf(1.f, -e);
+        float *row = &xs[n][c];
+        row[0] = a.x * sd; row[1] = a.y * sd; row[2] = a.z * sd; row[3] = a.w * sd;
+        row[4] = b.x * sd; row[5] = b.y * sd; row[6] = b.z * sd; row[7] = b.w * sd;
+        if ((t & 31) == 0) reinterpret_cast<float *>(out + G::REC - 32)[n] = ldexpf(1.f, e);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int it = t + 256 * u;                  // output u32x2 index: consecutive threads, consecutive bytes
+        const int mo = it & 1, lane = (it >> 1) & 63, m = 2 * (it >> 7) + mo;
+        const int b = lane & 15, g = lane >> 4;
+        const float4 q = *reinterpret_cast<const float4 *>(&xs[b & 7][F::elem(m, g, 0)]);
+        const float vv[4] = {q.x, q.y, q.z, q.w};
         uint32_t hv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hv[i] = split_part(vv[perm4(i)], lo);
-        // MFMA pair m / 2 of every lane of a step is one contiguous 1 KB run
-        const int64_t o = ((s * 8 + (m >> 1)) * 64 + lane) * 4 + (m & 1) * 2;
-        xp[o] = hv[0] | (hv[1] << 16);
-        xp[o + 1] = hv[2] | (hv[3] << 16);
-        return;
+        for (int i = 0; i < 4; ++i) hv[i] = split_part(vv[perm4(i)], b >= 8);
+        reinterpret_cast<u32x2 *>(out)[it] = u32x2{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
     }
     if constexpr (F::kMin) {
-        // one thread per (step, lane, K slot) of the min MFMA's A operand
-        const int64_t u = t - nx;
-        if (u >= int64_t(nsteps) * 256) return;
-        const int i = int(u & 3), lane = int((u >> 2) & 63);
-        const int64_t s = u >> 8;
-        const int b = lane & 15, g = lane >> 4, kk = 4 * g + i, j = kk & 7;
+        const int i = t & 3, lane = t >> 2, b = lane & 15, kk = 4 * (lane >> 4) + i, j = kk & 7;
         float sx = 0.f;
-        if (b < 8 && b < k) {
-            const float4 *p = reinterpret_cast<const float4 *>(X + b * cols + s * 256 + 32 * j);
+        if (b < 8) {
 #pragma unroll
             for (int v = 0; v < 8; ++v) {
-                const float4 q = p[v];
+                const float4 q = *reinterpret_cast<const float4 *>(&xs[b][32 * j + 4 * v]);
                 sx += (q.x + q.y) + (q.z + q.w);
             }
         }
-        xm[u] = split_part(sx, kk >= 8);
+        reinterpret_cast<uint16_t *>(out + 8192)[t] = split_part(sx, kk >= 8);
     }
 }
 
-template <class F, int kTiles>
-__device__ __forceinline__ void load_step(const uint8_t *const (&row)[kTiles], int s, int lane, int g, int nblk,
-                                          const uint32_t *__restrict__ xp, const uint32_t *__restrict__ xm,
-                                          typename F::Raw (&r)[kTiles], u32x4 (&xr)[8], u32x2 &xmr) {
-    const u32x4 *px = reinterpret_cast<const u32x4 *>(xp) + int64_t(s) * 512 + lane;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) xr[q] = px[64 * q];
-    if constexpr (F::kMin) xmr = *reinterpret_cast<const u32x2 *>(xm + (int64_t(s) * 64 + lane) * 2);
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t) F::load(row[t], s, g, nblk, r[t]);
+__device__ __forceinline__ void wait_vm(int n) {
+    switch (n) {
+    case 13: __builtin_amdgcn_s_waitcnt(vmcnt_imm(13)); break;
+    case 14: __builtin_amdgcn_s_waitcnt(vmcnt_imm(14)); break;
+    case 15: __builtin_amdgcn_s_waitcnt(vmcnt_imm(15)); break;
+    case 16: __builtin_amdgcn_s_waitcnt(vmcnt_imm(16)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;   // n = 0 (other counts do not occur)
+    }
+    __builtin_amdgcn_sched_barrier(0);
 }
 
-template <class F, int kTiles>
-__device__ __forceinline__ void compute_step(const typename F::Raw (&r)[kTiles], const u32x4 (&xr)[8],
-                                             const u32x2 &xmr, const uint8_t *const (&row)[kTiles], int s, int g,
-                                             int nblk, f4 (&acc)[kTiles]) {
-    h4 xa[16];
+// One step's activations in registers: the 16 MFMA A operands (from the
+// record's split activations), the min MFMA's A operand, and 1 / s_n for
+// the four outputs of this lane.
+struct XRegs {
+    u32x4a x[8];
+    u32x2 m;
+    f4 up;
+};
+
+template <class F>
+__device__ __forceinline__ void load_x(const uint8_t *__restrict__ rec, int s, int lane, int g, XRegs &xr) {
+    const uint8_t *const rc = rec + int64_t(s) * Geo<F>::REC;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        xa[2 * q] = pack(xr[q].x, xr[q].y);
-        xa[2 * q + 1] = pack(xr[q].z, xr[q].w);
-    }
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
-        if constexpr (std::is_same<F, BQ80>::value || std::is_same<F, BQ40>::value)
-            F::compute(r[t], row[t], s, nblk, xa, h4{}, acc[t]);
-        else if constexpr (F::kMin) F::compute(r[t], g, xa, pack(xmr.x, xmr.y), acc[t]);
-        else F::compute(r[t], row[t], s, g, xa, acc[t]);
-    }
+    for (int q = 0; q < 8; ++q) xr.x[q] = *reinterpret_cast<const u32x4a *>(rc + (q * 64 + lane) * 16);
+    if constexpr (F::kMin) xr.m = *reinterpret_cast<const u32x2 *>(rc + 8192 + lane * 8);
+    xr.up = *reinterpret_cast<const f4 *>(rc + Geo<F>::REC - 32 + 16 * (g & 1));
 }
 
-template <class F, int kTiles>
-__global__ void __launch_bounds__(64 * kWaves) bgemm(const uint8_t *__restrict__ W, int64_t row_bytes, int rows,
-                                                      int nsteps, int nblk, const uint32_t *__restrict__ xp,
-                                                      const uint32_t *__restrict__ xm, float *__restrict__ Y,
-                                                      int k, int accumulate, float *__restrict__ partial) {
-    __shared__ float part[kWaves][16 * kTiles][8];
-    // column split: workgroup row blockIdx.y takes steps [s_lo, s_hi) and,
-    // when there are several, writes its sums to partial[blockIdx.y][n][row]
-    const int nsplit = gridDim.y;
-    const int s_lo = int(int64_t(nsteps) * blockIdx.y / nsplit), s_hi = int(int64_t(nsteps) * (blockIdx.y + 1) / nsplit);
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, r = lane & 15, g = lane >> 4;
-    const int64_t R0 = int64_t(blockIdx.x) * 16 * kTiles + r;
-    // rows past the end read row 0 (in bounds); their results are not written
-    const uint8_t *row[kTiles];
+// Main pass.  Workgroup (x, y) owns rows [64 T x, 64 T (x + 1)) and steps
+// [y sps, (y + 1) sps); its waves work independently (no barrier): wave w
+// owns the T 16-row tiles from row 16 T (4 x + w).  Each step's weights flow
+// through the wave's ring of S LDS stages (global_load_lds of whole row
+// runs, so every copy instruction reads long contiguous pieces of a few
+// rows), copied two steps ahead; the step's activations come from the
+// records (L2-resident, 1 KB contiguous per load instruction) into
+// registers one step ahead.  The loads of one wave complete in issue
+// order, and each step issues its activations before the weights two steps
+// on, so one wait covers both.  A wave reads its weight operands from LDS,
+// computes each tile's sums for the step, undoes the record's scale, and at
+// the end writes its outputs to Y (one split) or to partial[split][n][row],
+// which bgemm_reduce adds in split order.
+template <class F>
+__global__ void __launch_bounds__(64 * Geo<F>::NW, Geo<F>::WPC) bgemm(const uint8_t *__restrict__ W, int64_t row_bytes, int rows,
+                                                          int nsteps, int nblk, const uint8_t *__restrict__ rec,
+                                                          int sps, float *__restrict__ Y, int k, int accumulate,
+                                                          float *__restrict__ partial) {
+    using G = Geo<F>;
+    constexpr int T = G::T;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, kept in a scalar register
+    const int split = blockIdx.y, nsplit = gridDim.y;
+    const int s_lo = split * sps, n = min(sps, nsteps - s_lo);
+    const int64_t T0 = (int64_t(blockIdx.x) * G::NW + wv) * 16 * T;    // first row of this wave's tiles
+    if (T0 >= rows) return;
+    const int64_t last = rows - 1;
+    // copies read whole 16-byte granules; none starts past the one that
+    // holds the matrix's last byte (W is 16-byte aligned)
+    const int64_t last_granule = (int64_t(rows) * row_bytes - 1) & ~int64_t(15);
+    const int64_t base_rel = (T0 * row_bytes) & ~int64_t(15);
+    const uint8_t *const wbase = W + base_rel;                         // this wave's copy base (uniform)
+    uint8_t *const ring = lds + wv * G::WAVE;
+    // this lane's part of a tile copy: instruction i fills LDS bytes
+    // [1024 i, 1024 i + 1024) of the tile, lane l the granule at 1024 i + 16 l:
+    // byte w of row q's run (lanes past row 15 or the run copy a granule of
+    // the matrix into the padding)
+    int64_t cstart[T][G::NI];
+    int cw[G::NI];
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) row[t] = W + (R0 + 16 * t < rows ? R0 + 16 * t : 0) * row_bytes;
-    f4 acc[kTiles];
+    for (int i = 0; i < G::NI; ++i) {
+        const int P = 1024 * i + 16 * lane, q = min(P / G::Lp, 15);
+        cw[i] = P - q * G::Lp;
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
-    if (s_lo + wv < s_hi) {
-        // one step ahead, in two register sets used in turn: the loads of the
-        // next step are in flight while this one is computed (a step past
-        // the end re-loads the current one, from cache)
-        typename F::Raw ra[kTiles], rb[kTiles];
-        u32x4 xa_[8], xb_[8];
-        u32x2 ma = {0u, 0u}, mb = {0u, 0u};
-        load_step<F, kTiles>(row, s_lo + wv, lane, g, nblk, xp, xm, ra, xa_, ma);
-        for (int s = s_lo + wv; s < s_hi; s += 2 * kWaves) {
-            const int s1 = s + kWaves < s_hi ? s + kWaves : s;
-            load_step<F, kTiles>(row, s1, lane, g, nblk, xp, xm, rb, xb_, mb);
-            // keeps the loads above ahead of the arithmetic (the scheduler
-            // would otherwise sink them to their first use)
-            asm volatile("" ::: "memory");
-            compute_step<F, kTiles>(ra, xa_, ma, row, s, g, nblk, acc);
-            if (s + kWaves >= s_hi) break;
-            const int s2 = s + 2 * kWaves < s_hi ? s + 2 * kWaves : s1;
-            load_step<F, kTiles>(row, s2, lane, g, nblk, xp, xm, ra, xa_, ma);
-            asm volatile("" ::: "memory");
-            compute_step<F, kTiles>(rb, xb_, mb, row, s1, g, nblk, acc);
+        for (int u = 0; u < T; ++u) cstart[u][i] = min(T0 + 16 * u + q, last) * row_bytes;
+    }
+    const auto issue_w = [&](int b, int s) {
+#pragma unroll
+        for (int u = 0; u < T; ++u) {
+            const uint32_t dst = lds_addr(ring + (b * T + u) * G::TB);
+#pragma unroll
+            for (int i = 0; i < G::NI; ++i) {
+                const int64_t a0 = (cstart[u][i] + int64_t(s) * G::L) & ~int64_t(15);
+                dma<16>(wbase, uint32_t(min(a0 + cw[i], last_granule) - base_rel), dst + 1024 * i);
+            }
         }
-    }
-    // lanes g and g + 2 hold the hi and lo parts of outputs n = 4g + i
+    };
+    int64_t rstart[T];                                                 // this lane's rows
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t)
+    for (int u = 0; u < T; ++u) rstart[u] = min(T0 + 16 * u + r, last) * row_bytes;
+    f4 acc[T];
+#pragma unroll
+    for (int u = 0; u < T; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
+
+    const auto compute = [&](int t, const XRegs &xr) {
+        const int s = s_lo + t;
+        h4 xa[16];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            xa[2 * q] = pack(xr.x[q].x, xr.x[q].y);
+            xa[2 * q + 1] = pack(xr.x[q].z, xr.x[q].w);
+        }
+        const h4 xm = F::kMin ? pack(xr.m.x, xr.m.y) : h4{};
+        const uint8_t *const st = ring + (t % G::S) * T * G::TB;
+#pragma unroll
+        for (int u = 0; u < T; ++u) {
+            const int mis = int((rstart[u] + int64_t(s) * G::L) & 15);
+            const uint8_t *const p = st + u * G::TB + r * G::Lp + mis;   // this lane's row, step s
+            typename F::Raw raw;
+            F::load(p, s, g, nblk, raw);
+            f4 c = {0.f, 0.f, 0.f, 0.f};
+            F::compute(raw, p, s, g, nblk, xa, xm, c);
+            acc[u] += xr.up * c;
+        }
+    };
+
+    // per step: activations (8 + kMin + 1 loads), then T NI weight copies;
+    // both are issued two steps ahead, so step t's are in once at most those
+    // of step t + 1 are outstanding
+    constexpr int kX = 9 + (F::kMin ? 1 : 0), kW = T * G::NI;
+    XRegs x0, x1, x2;
+    const auto step = [&](int t, const XRegs &cur, XRegs &ahead) {
+        wait_vm(t + 1 < n ? kX + kW : 0);
+        if (t + 2 < n) {
+            load_x<F>(rec, s_lo + t + 2, lane, g, ahead);
+            issue_w((t + 2) % G::S, s_lo + t + 2);
+        }
+        compute(t, cur);
+    };
+    issue_w(0, s_lo);
+    load_x<F>(rec, s_lo, lane, g, x0);
+    if (n > 1) {
+        issue_w(1, s_lo + 1);
+        load_x<F>(rec, s_lo + 1, lane, g, x1);
+    }
+    for (int t = 0; t < n; t += 3) {
+        step(t, x0, x2);
+        if (t + 1 >= n) break;
+        step(t + 1, x1, x0);
+        if (t + 2 >= n) break;
+        step(t + 2, x2, x1);
+    }
+    // lanes g and g + 2 hold the hi and lo parts of outputs n = 4g + i of row r
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+        const int64_t R = T0 + 16 * u + r;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float o = acc[t][i] + __shfl_down(acc[t][i], 32, 64);
-            if (g < 2) part[wv][16 * t + r][4 * g + i] = o;
-        }
-    __syncthreads();
-    for (int j = threadIdx.x; j < 128 * kTiles; j += 64 * kWaves) {
-        const int rr = j % (16 * kTiles), n = j / (16 * kTiles);
-        const int64_t R2 = int64_t(blockIdx.x) * 16 * kTiles + rr;
-        if (n < k && R2 < rows) {
-            float v = 0.f;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) v += part[w][rr][n];
-            if (nsplit > 1) {
-                partial[(int64_t(blockIdx.y) * k + n) * rows + R2] = v;
-            } else {
-                float *py = Y + n * int64_t(rows) + R2;
-                *py = accumulate ? *py + v : v;
+            const int nn = 4 * g + i;
+            const float o = acc[u][i] + __shfl_down(acc[u][i], 32, 64);
+            if (g < 2 && nn < k && R < rows) {
+                if (nsplit > 1) {
+                    partial[(int64_t(split) * k + nn) * rows + R] = o;
+                } else {
+                    float *py = Y + nn * int64_t(rows) + R;
+                    *py = accumulate ? *py + o : o;
+                }
             }
         }
     }
@@ -503,73 +618,93 @@ __global__ void __launch_bounds__(256) bgemm_reduce(const float *__restrict__ pa
     Y[t] = accumulate ? Y[t] + v : v;
 }
 
-}  // namespace
+struct BgemmShape {
+    int groups, nsplit, sps;
+};
 
-int64_t bgemm_steps(int64_t cols) { return (cols + 255) / 256; }
-
-bool gemm_batch_type_ok(nt_qtype t) {
-    return t == NT_Q8_0 || t == NT_Q4_0 || t == NT_Q4_K || t == NT_Q5_K || t == NT_Q6_K;
+// Column splits: the fewest that minimise (rounds of workgroups over the
+// chip, WPC per CU) x (steps per workgroup + the ring's fill), so that
+// short or narrow matrices still fill the CUs.
+template <class F>
+BgemmShape bgemm_shape(int64_t rows, int64_t cols) {
+    using G = Geo<F>;
+    BgemmShape b{};
+    const int ns = int((cols + 255) / 256);
+    b.groups = int((rows + 16 * G::T * G::NW - 1) / (16 * G::T * G::NW));
+    const int64_t slots = int64_t(kNumCUs) * G::WPC;
+    int64_t best = -1;
+    for (int sp = 1; sp <= std::min(ns, 64); ++sp) {
+        const int sps = (ns + sp - 1) / sp;
+        if ((ns + sps - 1) / sps != sp) continue;          // same steps per split as a smaller count
+        const int64_t rounds = (int64_t(b.groups) * sp + slots - 1) / slots;
+        const int64_t cost = rounds * (sps + G::S - 1);
+        if (best < 0 || cost < best) {
+            best = cost;
+            b.nsplit = sp;
+            b.sps = sps;
+        }
+    }
+    return b;
 }
 
-// fp32 partial sums of a column-split launch: at most 8 vectors x 65536
-// (split, row) pairs
-constexpr int64_t kPartialFloats = 8 * 65536;
-
-size_t gemm_batch_workspace_bytes(nt_qtype t, int64_t cols) {
-    const int64_t ns = bgemm_steps(cols);
-    const bool mins = t == NT_Q4_K || t == NT_Q5_K;
-    return size_t(ns) * 8192 + (mins ? size_t(ns) * 512 : 0) + size_t(kPartialFloats) * 4;
-}
-
-// Column splits for a matrix whose row groups alone give fewer than 256
-// workgroups: about 512 workgroups in all, at least one step per wave, and
-// within the partial-sum area.
-// (Splitting 8192-row matrices as well, to 1024 workgroups, made them slower:
-// Q4_K 8192x8192 at k = 8 25 -> 34 us.)
-int bgemm_splits(int64_t groups, int ns, int64_t rows) {
-    if (groups >= 256) return 1;
-    int64_t sp = (512 + groups - 1) / groups;
-    sp = std::min<int64_t>(sp, std::max(1, ns / kWaves));
-    sp = std::min<int64_t>(sp, 65536 / std::max<int64_t>(rows, 1));
-    return int(std::max<int64_t>(sp, 1));
+template <class F>
+size_t workspace_for(int64_t rows, int64_t cols) {
+    const BgemmShape b = bgemm_shape<F>(rows, cols);
+    const int64_t ns = (cols + 255) / 256;
+    return size_t(ns) * Geo<F>::REC + (b.nsplit > 1 ? size_t(b.nsplit) * 8 * size_t(rows) * 4 : 0);
 }
 
 template <class F>
 hipError_t run_bgemm(const void *W, int64_t row_bytes, int64_t rows, int64_t cols, int64_t nblk, const float *X,
                      int k, float *Y, int accumulate, void *ws, hipStream_t st) {
-    const int ns = int(bgemm_steps(cols));
-    uint32_t *xp = static_cast<uint32_t *>(ws);
-    uint32_t *xm = F::kMin ? xp + int64_t(ns) * 2048 : nullptr;
-    float *partial = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + int64_t(ns) * 8192 +
-                                               (F::kMin ? int64_t(ns) * 512 : 0));
-    const int64_t nt = int64_t(ns) * (F::kMin ? 1024 + 256 : 1024);
-    hipLaunchKernelGGL(bgemm_prep<F>, dim3(unsigned((nt + 255) / 256)), dim3(256), 0, st, X, cols, k, ns, xp,
-                       reinterpret_cast<uint16_t *>(xm));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || rows == 0) return e;
-    if constexpr (std::is_same<F, BQ4K>::value) {
-        if (rows >= kTallRows) {
-            hipLaunchKernelGGL((bgemm<F, 4>), dim3(unsigned((rows + 63) / 64)), dim3(64 * kWaves), 0, st,
-                               static_cast<const uint8_t *>(W), row_bytes, int(rows), ns, int(nblk), xp, xm, Y, k,
-                               accumulate, partial);
-            return hipGetLastError();
-        }
+    using G = Geo<F>;
+    const int ns = int((cols + 255) / 256);
+    const BgemmShape b = bgemm_shape<F>(rows, cols);
+    uint8_t *const rec = static_cast<uint8_t *>(ws);
+    float *const partial = reinterpret_cast<float *>(rec + int64_t(ns) * G::REC);
+    // more than 64 KB of dynamic LDS: allowed once per device
+    static std::atomic<uint64_t> done{0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (!((done.load(std::memory_order_acquire) >> dev) & 1)) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&bgemm<F>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
+        if (e != hipSuccess) return e;
+        done.fetch_or(uint64_t(1) << dev, std::memory_order_release);
     }
-    const int64_t groups = (rows + 31) / 32;
-    const int sp = bgemm_splits(groups, ns, rows);
-    hipLaunchKernelGGL((bgemm<F, 2>), dim3(unsigned(groups), unsigned(sp)), dim3(64 * kWaves), 0, st,
-                       static_cast<const uint8_t *>(W), row_bytes, int(rows), ns, int(nblk), xp, xm, Y, k, accumulate,
-                       partial);
-    if (sp == 1) return hipGetLastError();
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bgemm_prep<F>, dim3(unsigned(ns)), dim3(256), 0, st, X, cols, k, rec);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bgemm<F>, dim3(unsigned(b.groups), unsigned(b.nsplit)), dim3(64 * G::NW), G::LDS, st,
+                       static_cast<const uint8_t *>(W), row_bytes, int(rows), ns, int(nblk), rec, b.sps, Y, k,
+                       accumulate, partial);
+    if ((e = hipGetLastError()) != hipSuccess || b.nsplit == 1) return e;
     const int64_t nt2 = int64_t(k) * rows;
-    hipLaunchKernelGGL(bgemm_reduce, dim3(unsigned((nt2 + 255) / 256)), dim3(256), 0, st, partial, sp, k, int(rows),
-                       Y, accumulate);
+    hipLaunchKernelGGL(bgemm_reduce, dim3(unsigned((nt2 + 255) / 256)), dim3(256), 0, st, partial, b.nsplit, k,
+                       int(rows), Y, accumulate);
     return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm_batch_type_ok(nt_qtype t) {
+    return t == NT_Q8_0 || t == NT_Q4_0 || t == NT_Q4_K || t == NT_Q5_K || t == NT_Q6_K;
+}
+
+size_t gemm_batch_workspace_bytes(nt_qtype t, int64_t rows, int64_t cols) {
+    switch (t) {
+    case NT_Q8_0: return workspace_for<BQ80>(rows, cols);
+    case NT_Q4_0: return workspace_for<BQ40>(rows, cols);
+    case NT_Q5_K: return workspace_for<BQ5K>(rows, cols);
+    case NT_Q4_K: return workspace_for<BQ4K>(rows, cols);
+    case NT_Q6_K: return workspace_for<BQ6K>(rows, cols);
+    default: return 0;
+    }
 }
 
 hipError_t launch_gemm_batch(nt_qtype t, const void *W, int64_t rows, int64_t cols, const float *X, int k, float *Y,
                              int accumulate, void *ws, hipStream_t st) {
+    if (rows == 0) return hipSuccess;
     const int64_t nblk = cols / block_elems(t), row_bytes = nblk * block_bytes(t);
     switch (t) {
     case NT_Q8_0: return run_bgemm<BQ80>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);

@@ -67,9 +67,9 @@ hipError_t launch_read_bytes(const void *src, int64_t bytes, float *sink, hipStr
 hipError_t launch_copy_bytes(void *dst, const void *src, int64_t bytes, hipStream_t st);
 
 // k <= 8 activation vectors against one matrix on the matrix cores
-// (Q8_0, Q4_K, Q6_K); ws: gemm_batch_workspace_bytes, 16-byte aligned.
+// (all five block formats); ws: gemm_batch_workspace_bytes, 16-byte aligned.
 bool gemm_batch_type_ok(nt_qtype t);
-size_t gemm_batch_workspace_bytes(nt_qtype t, int64_t cols);
+size_t gemm_batch_workspace_bytes(nt_qtype t, int64_t rows, int64_t cols);
 hipError_t launch_gemm_batch(nt_qtype t, const void *W, int64_t rows, int64_t cols, const float *X, int k, float *Y,
                              int accumulate, void *ws, hipStream_t st);
 

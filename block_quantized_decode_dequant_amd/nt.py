@@ -68,7 +68,7 @@ def _declare(L):
         "nt_gemv_multi": (st, [i32, i32, C.POINTER(vp), C.POINTER(i64), C.POINTER(vp), i64, vp, vp, C.c_float,
                                i32, vp]),
         "nt_gemv_swiglu": (st, [i32, vp, vp, i64, i64, vp, vp, C.c_float, vp, vp]),
-        "nt_gemm_batch_workspace_bytes": (C.c_size_t, [i32, i64]),
+        "nt_gemm_batch_workspace_bytes": (C.c_size_t, [i32, i64, i64]),
         "nt_gemm_batch": (st, [i32, vp, vp, vp, i64, i64, i32, i32, vp, C.c_size_t, vp]),
         "nt_read_bytes": (st, [vp, i64, vp, vp]),
         "nt_copy_bytes": (st, [vp, vp, i64, vp]),
@@ -199,8 +199,8 @@ def nt_gemv_swiglu(qtype: int, W_gate, W_up, rows: int, cols: int, x, h, gain=No
 
 
 # ---- batched verify pass -------------------------------------------------------------------
-def nt_gemm_batch_workspace_bytes(qtype: int, cols: int) -> int:
-    return lib().nt_gemm_batch_workspace_bytes(qtype, cols)
+def nt_gemm_batch_workspace_bytes(qtype: int, rows: int, cols: int) -> int:
+    return lib().nt_gemm_batch_workspace_bytes(qtype, rows, cols)
 
 
 def nt_gemm_batch(qtype: int, W, X, Y, rows: int, cols: int, k: int, workspace, accumulate: bool = False,

@@ -161,16 +161,22 @@ nt_status nt_gemv_swiglu(nt_qtype t, const void *W_gate, const void *W_up, int64
  * (Y_n at Y + n * rows); W is as for nt_gemv.  Types: the five block
  * formats (others: NT_EINVAL); cols a whole number of blocks, at most 65536;
  * rows below 2^31.  The products run on the matrix cores with each x split
- * into two fp16 parts (about 2^-22 relative error per element; |x| must stay
- * below 65504); weights are not rounded.  Matrices with few rows are split
- * over columns as well, with the partial sums added in a fixed order by a
- * second kernel (results are deterministic).  workspace: device memory of at
- * least nt_gemm_batch_workspace_bytes(t, cols) (the split activations plus
- * 2 MiB of partial sums), 16-byte aligned, used only during the call (stream
- * order); calls that share a workspace must not overlap.  W, X and the
- * workspace 16-byte aligned, Y 4-byte aligned; Y must not overlap X, W or
- * the workspace. */
-size_t nt_gemm_batch_workspace_bytes(nt_qtype t, int64_t cols);
+ * into two fp16 parts (about 2^-22 relative error per element); weights are
+ * not rounded.  Where a part would overflow fp16 (|x| near 65504 or above,
+ * or, for the K-quant mins, a sum of 32 activations that large) the vectors
+ * of that 256-column step are split scaled by an exact power of two and
+ * their sums scaled back, so any finite X is valid.  The call runs two or
+ * three kernels: one writes each step's split activations to the workspace
+ * (8224 bytes per 256 columns, 8736 for Q4_K and Q5_K), the main one reads
+ * them and the weights; when the columns are split between workgroups (few
+ * rows), the partial sums also go to the workspace and a third kernel adds
+ * them in a fixed order (results are deterministic).  workspace: device
+ * memory of at least nt_gemm_batch_workspace_bytes(t, rows, cols) bytes
+ * (never 0 for valid arguments; 0 means the arguments are invalid),
+ * 16-byte aligned, used only during the call (stream order); calls that
+ * share a workspace must not overlap.  W, X and the workspace 16-byte
+ * aligned, Y 4-byte aligned; Y must not overlap X, W or the workspace. */
+size_t nt_gemm_batch_workspace_bytes(nt_qtype t, int64_t rows, int64_t cols);
 nt_status nt_gemm_batch(nt_qtype t, const void *W, const float *X, float *Y, int64_t rows, int64_t cols,
                         int32_t k, int32_t accumulate, void *workspace, size_t workspace_bytes, nt_stream stream);
 

@@ -83,11 +83,21 @@ def _batch(t, W, X, Y, rows, cols, k, ws=A, ws_bytes=4 << 20):
 @no_gpu_only
 def test_gemm_batch_argument_errors():
     wsb = nt.nt_gemm_batch_workspace_bytes
-    part = 8 * 65536 * 4                                # column-split partial sums
-    assert wsb(nt.Q4_K, 8192) == 32 * (8192 + 512) + part and wsb(nt.Q6_K, 8192) == 32 * 8192 + part
-    assert wsb(nt.Q8_0, 33 * 32) == 5 * 8192 + part     # a partial last 256-column step
-    assert wsb(nt.Q5_K, 256) == 8192 + 512 + part and wsb(nt.Q4_0, 320) == 2 * 8192 + part
-    assert wsb(nt.F32, 256) == 0 and wsb(nt.Q4_K, 100) == 0 and wsb(nt.Q4_K, 65536 + 256) == 0
+    # one activation record per 256 columns (8192 bytes of split activations,
+    # 512 of sub-block sums for K-quants with mins, 32 of scales), then fp32
+    # partial sums of 8 vectors per column range when there is more than one
+    rec = {nt.Q4_K: 8736, nt.Q5_K: 8736, nt.Q6_K: 8224, nt.Q8_0: 8224, nt.Q4_0: 8224}
+    assert wsb(nt.Q4_K, 4, 256) == 8736 and wsb(nt.Q8_0, 1, 32) == 8224   # one range
+    for t, rows, cols in [(nt.Q4_K, 8192, 8192), (nt.Q6_K, 8192, 28672), (nt.Q8_0, 4096, 4096),
+                          (nt.Q4_K, 3, 65536), (nt.Q5_K, 40040, 2048), (nt.Q4_0, 600, 8960)]:
+        ns = -(-cols // 256)
+        extra = wsb(t, rows, cols) - ns * rec[t]
+        assert extra >= 0 and extra % (8 * rows * 4) == 0, (t, rows, cols)
+        assert extra // (8 * rows * 4) <= min(ns, 64)
+    assert wsb(nt.Q4_K, 8192, 8192) > 32 * 8736          # too few rows to fill the chip: split
+    assert wsb(nt.Q4_K, 3, 65536) > 256 * 8736
+    assert wsb(nt.F32, 4, 256) == 0 and wsb(nt.Q4_K, 4, 100) == 0 and wsb(nt.Q4_K, 4, 65536 + 256) == 0
+    assert wsb(nt.Q4_K, -1, 256) == 0
     assert _batch(nt.Q4_K, A, A, A, 4, 256, 0) == nt.NT_EINVAL
     assert _batch(nt.Q4_K, A, A, A, 4, 256, 9) == nt.NT_EINVAL
     assert _batch(nt.F32, A, A, A, 4, 256, 2) == nt.NT_EINVAL
@@ -97,12 +107,13 @@ def test_gemm_batch_argument_errors():
     assert _batch(nt.Q8_0, A, A, A, 4, 65536 + 32, 2) == nt.NT_ESHAPE
     assert _batch(nt.Q4_K, A, A, A, -1, 256, 2) == nt.NT_EINVAL
     assert _batch(nt.Q4_K, 0, A, A, 4, 256, 2) == nt.NT_EINVAL
+    assert _batch(nt.Q4_K, A, A, A, 4, 2048, 2, ws=0) == nt.NT_EINVAL        # needs a workspace
     assert _batch(nt.Q4_K, A, A, A, 4, 256, 2, ws=0) == nt.NT_EINVAL
     assert _batch(nt.Q4_K, A + 4, A, A, 4, 256, 2) == nt.NT_EALIGN
     assert _batch(nt.Q4_K, A, A + 4, A, 4, 256, 2) == nt.NT_EALIGN
     assert _batch(nt.Q4_K, A, A, A + 2, 4, 256, 2) == nt.NT_EALIGN
     assert _batch(nt.Q4_K, A, A, A, 4, 256, 2, ws=A + 8) == nt.NT_EALIGN
-    assert _batch(nt.Q4_K, A, A, A, 4, 256, 2, ws_bytes=wsb(nt.Q4_K, 256) - 4) == nt.NT_ENOMEM
+    assert _batch(nt.Q4_K, A, A, A, 4, 2048, 2, ws_bytes=wsb(nt.Q4_K, 4, 2048) - 4) == nt.NT_ENOMEM
     assert _batch(nt.Q4_K, 0, 0, 0, 0, 256, 2, ws=0) == nt.NT_OK          # nothing to do
     assert _batch(nt.Q6_K, A, A, A + 4, 4, 256, 8) == nt.NT_ENODEV        # valid, but no GPU here
 

@@ -27,7 +27,8 @@ GUARD = 12345.0
 
 def _run(t, W, X, rows, cols, k, y0=None, dev_w=None):
     dev = device()
-    ws = torch.empty(nt.nt_gemm_batch_workspace_bytes(t, cols), dtype=torch.uint8, device=dev)
+    nws = nt.nt_gemm_batch_workspace_bytes(t, rows, cols)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     Y = torch.full((k * rows + 64,), GUARD, dtype=torch.float32, device=dev)
     if y0 is not None:
         Y[:k * rows] = to_dev(y0.reshape(-1))
@@ -91,11 +92,31 @@ def test_gemm_batch_rows_are_independent_of_k():
         assert np.array_equal(one[0], all8[n])
 
 
-def test_gemm_batch_q4_k_tall_matrix_layout():
-    # 16384 rows and more take four row tiles per wave: ragged last group,
-    # and the row count at the switch
-    _case(O.Q4_K, 16384 + 48, 512, 8, seed=31)
-    _case(O.Q4_K, 16384, 256, 3, seed=32)
+def test_gemm_batch_tall_and_wide_matrices():
+    # 40040 rows of 2048 columns (ragged last workgroup, with a partial
+    # 16-row tile), and 600 rows of 8960 columns (35 steps: column ranges of
+    # unequal length, partial sums added by the second kernel)
+    _case(O.Q4_K, 40040, 2048, 8, seed=31)
+    _case(O.Q6_K, 40040, 2048, 3, seed=33)
+    _case(O.Q8_0, 600, 8960, 5, seed=32)
+
+
+@pytest.mark.parametrize("t", [O.Q8_0, O.Q4_K, O.Q6_K], ids=["q8_0", "q4_k", "q6_k"])
+def test_gemm_batch_large_activations_are_scaled_not_lost(t):
+    """Activations whose fp16 hi part (or, for the K-quant mins, a 32-value
+    sum) would overflow: each 256-column step splits them scaled by a power
+    of two and the sums are scaled back, so the results match the oracle."""
+    rows, cols, k = 96, 4096, 4
+    W = O.quantize(t, synth.normal_f32(41, 550, rows * cols, std=0.02))
+    X = np.stack([synth.normal_f32(41, 560 + n, cols) for n in range(k)])
+    X[1] *= 3.0e5            # every |x| far above fp16's range
+    X[2, 100] = 1.0e8        # one huge value in one column range
+    X[3] *= 2500.0           # values fit fp16, sums of 32 do not
+    got = _run(t, W, X, rows, cols, k)
+    ref = O.gemm_batch(t, W, rows, cols, X)
+    for n in range(k):
+        assert_close(got[n], ref[n], atol=1e-4 * max(1.0, np.abs(ref[n]).max()),
+                     what=f"gemm_batch {t} large activations, vector {n}")
 
 
 @pytest.mark.parametrize("t", [O.Q4_K, O.Q6_K], ids=["q4_k", "q6_k"])
@@ -113,8 +134,8 @@ def test_gemm_batch_70b_projection_shape(t):
 
 @pytest.mark.parametrize("t,si", [(O.Q4_K, 2), (O.Q6_K, 3)], ids=["q4_k-28672x8192", "q6_k-8192x28672"])
 def test_gemm_batch_70b_ffn_shapes_sampled(t, si):
-    """The FFN projection shapes the benchmark times (the four-tile launch
-    for Q4_K 28672 x 8192, 112 column steps for Q6_K 8192 x 28672) at k = 8:
+    """The FFN projection shapes the benchmark times (Q4_K 28672 x 8192 in
+    256-row workgroups over four column ranges, Q6_K 8192 x 28672 over 14) at k = 8:
     the first and last 64 rows and 448 random rows against the oracle."""
     rows, cols = workloads.KQ_SHAPES[si]
     w = synth.normal_f32(workloads.SEED, workloads.kq_w_stream(si), rows * cols, std=0.02)
@@ -131,18 +152,20 @@ def test_gemm_batch_70b_ffn_shapes_sampled(t, si):
 
 def test_gemm_batch_rejects_bad_arguments():
     dev = device()
-    W = torch.zeros(4 * 1024, dtype=torch.uint8, device=dev)    # room for 4 F32 rows of 256
-    X = torch.zeros(9 * 256, dtype=torch.float32, device=dev)
+    W = torch.zeros(4 * 8 * 144, dtype=torch.uint8, device=dev)    # 4 Q4_K rows of 2048 (also 4 F32 rows of 256)
+    X = torch.zeros(9 * 2048, dtype=torch.float32, device=dev)
     Y = torch.zeros(9 * 4, dtype=torch.float32, device=dev)
-    ws = torch.empty(nt.nt_gemm_batch_workspace_bytes(O.Q4_K, 256), dtype=torch.uint8, device=dev)
+    nws = nt.nt_gemm_batch_workspace_bytes(O.Q4_K, 4, 2048)
+    assert nws > 0                                                  # four rows: split over columns
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     for k in (0, 9):
         with pytest.raises(nt.NTError):
-            nt.nt_gemm_batch(O.Q4_K, W, X, Y, 4, 256, k, ws)
+            nt.nt_gemm_batch(O.Q4_K, W, X, Y, 4, 2048, k, ws)
     with pytest.raises(nt.NTError):
         nt.nt_gemm_batch(nt.F32, W, X, Y, 4, 256, 2, ws)
     with pytest.raises(nt.NTError) as e:
-        nt.nt_gemm_batch(O.Q4_K, W, X, Y, 4, 256, 2, ws[:-16])
+        nt.nt_gemm_batch(O.Q4_K, W, X, Y, 4, 2048, 2, ws[:-16])
     assert e.value.status == nt.NT_ENOMEM
     Y.fill_(3.0)
-    nt.nt_gemm_batch(O.Q4_K, W, X, Y, 0, 256, 2, ws)
+    nt.nt_gemm_batch(O.Q4_K, W, X, Y, 0, 2048, 2, ws)
     assert torch.all(Y == 3.0)
