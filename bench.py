@@ -13,17 +13,21 @@ kernel with the most time in the timed region gives the `roofline` object.
 The CPU baseline times the oracle (plain fp64 C, test-side code) on a bounded
 sample of the same workload: the first rows of each matrix.
 
-Q5_K GEMV at the two Llama-70B FFN shapes rides along ("q5_k_gemv"), timed like
-the sweep's per-kernel times, and so does the batched verify pass of
-self-speculative decoding ("verify_gemm": k = 8 vectors per weight read).  Decode measurements ride along in the same JSON line ("decode"): the
-Llama-3-8B-shaped Q8_0 model (128 greedy tokens from position 1024), the
-Llama-70B-shaped Q4_K/Q6_K model (64 tokens from 4096), each replayed from a
-captured HIP graph, and the 70B all-Q6_K model with 24 GiB of layers resident
-and the rest streamed from pinned host RAM, each as tok/s against the
-weight-bytes / 8 TB/s bound (or the measured pinned H2D rate).
+Alongside, in the same JSON line: the Q8_0 GEMV at 4096x4096 ("q8_0_gemv",
+the small configuration), Q5_K GEMV at the two Llama-70B FFN shapes
+("q5_k_gemv"), and the batched verify pass of self-speculative decoding
+("verify_gemm": k = 8 vectors per weight read), each timed like the sweep's
+per-kernel times.  Decode measurements ("decode"): the Llama-3-8B-shaped Q8_0
+model (128 greedy tokens from position 1024), the Llama-70B-shaped Q4_K/Q6_K
+model (64 tokens from 4096), each replayed from a captured HIP graph, the 70B
+all-Q6_K model with 24 GiB of layers resident and the rest streamed from
+pinned host RAM, and the same with the last --file-layers layers read from a
+file each step (the third tier), each as tok/s against the weight-bytes /
+8 TB/s bound (or the measured pinned H2D and file read rates).
 
 Flags: --gpus N (only 1 is supported: this path runs on one GPU),
---steps K, --warmup W, --no-cpu-baseline, --decode none|8b|70b|all.
+--steps K, --warmup W, --no-cpu-baseline, --cpu-seconds S, --decode
+none|8b|70b|all, --stream-tokens T, --file-layers F, --file-dir D.
 """
 from __future__ import annotations
 
@@ -698,13 +702,20 @@ def cpu_baseline(seconds: float):
                                       "blocks (the oracle's work does not depend on the values)"}
 
 
+def done(what: str, t0: float):
+    """One line on stderr as each leg ends (the JSON line stays the only stdout)."""
+    print(f"bench.py: {what} done ({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
+    t0 = time.perf_counter()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               "(no sharding or collectives are built)", file=sys.stderr)
         raise SystemExit(2)
     g = run_gpu(args)
+    done("sweep", t0)
     from block_quantized_decode_dequant_amd import workloads
 
     line = {
@@ -728,25 +739,31 @@ def main():
         "per_case_sum_ms": round(g["case_sum_ms"], 4),
         "roofline": g["roofline"],
         "detail": g["detail"],
-        "q8_0_gemv": q8_0_gemv(args.steps),
-        "q5_k_gemv": q5_k_gemv(args.steps),
-        "verify_gemm": verify_gemm(args.steps),
     }
+    line["q8_0_gemv"] = q8_0_gemv(args.steps)
+    line["q5_k_gemv"] = q5_k_gemv(args.steps)
+    line["verify_gemm"] = verify_gemm(args.steps)
+    done("q8_0, q5_k and verify legs", t0)
     if args.decode != "none":
         dec = {}
         if args.decode in ("8b", "all"):
             dec["llama3_8b_q8_0"] = decode_resident(workloads.LLAMA_8B_Q8_0)
+            done("8B decode", t0)
         if args.decode in ("70b", "all"):
             dec["llama70b_q4_k_q6_k"] = decode_resident(workloads.LLAMA_70B_MIX)
+            done("70B decode", t0)
         if args.decode == "all":
             dec["llama70b_q6_k_streamed_24gib"] = decode_streamed(workloads.LLAMA_70B_Q6K,
                                                                   n_tokens=args.stream_tokens)
+            done("70B streamed decode", t0)
             if args.file_layers > 0:
                 dec["llama70b_q6_k_three_tier_file"] = decode_file_tier(workloads.LLAMA_70B_Q6K, args.file_layers,
                                                                         args.file_dir)
+                done("70B three-tier decode", t0)
         line["decode"] = dec
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        done("cpu baseline", t0)
     print(json.dumps(line), flush=True)
 
 

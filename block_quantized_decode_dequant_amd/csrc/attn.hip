@@ -10,10 +10,10 @@
 // rotation kernel.
 //
 // The context is split into chunks of C positions so that n_kv_heads x chunks
-// workgroups fill the chip.  A workgroup first issues every load of its
-// chunk's K and V (each thread holds its share in registers), then computes
-// the G heads' scores, their chunk-local softmax statistics and the
-// unnormalized weighted sum of V, and leaves (max, sum, o[D]) per head.  A
+// workgroups fill the chip.  A workgroup first issues asynchronous copies of
+// its chunk's K and V rows into LDS, then computes the G heads' scores, their
+// chunk-local softmax statistics and the unnormalized weighted sum of V (both
+// products on the matrix cores), and leaves (max, sum, o[D]) per head.  A
 // merge kernel combines the chunks with the log-sum-exp rule in a fixed order
 // (deterministic).  The current token's k and v are stored at slot pos
 // (rounded to fp16) by the workgroup that owns that slot, which attends to the
@@ -132,7 +132,8 @@ __host__ __device__ constexpr size_t attn_lds_bytes(int D, int G, int cpw) {
 // q heads, N = 16 positions, K = 16 dims; q split into fp16 hi + lo parts,
 // two MFMAs per step, so the scores carry ~2^-22 relative error; K is fp16
 // already); chunk softmax statistics by 16-lane DPP reductions; P V on the
-// vector units; the partial record per head.
+// matrix cores too (M = q heads, N = 16 dims, K = 16 positions, p split into
+// fp16 hi + lo parts); the partial record per head.
 template <int D, int G>
 __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
     const float *__restrict__ q, const float *__restrict__ k_new, const float *__restrict__ v_new,

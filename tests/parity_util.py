@@ -32,11 +32,12 @@ def allowed_near_ties(n_steps: int) -> int:
 
 
 def greedy_parity_run(model, dec, vocab: int, n_pos: int, first_token: int, n_steps: int, what: str = "",
-                      graph: bool = True, oracle_threads: int | None = None, each_step=None):
+                      graph: bool = True, oracle_threads: int | None = None, each_step=None, say=None):
     """Decode n_steps tokens on the GPU (`model`, an nt.Model) and in the
     oracle (`dec`, an oracle.Decoder on the same weights and cache), compare
     as the module docstring states, and return a summary dict.  each_step(s,
-    logits) sees the GPU logits of every step (for extra checks)."""
+    logits) sees the GPU logits of every step (for extra checks); say(msg),
+    if given, reports each step as it ends."""
     import torch
 
     from .gpu_util import device, host
@@ -60,6 +61,8 @@ def greedy_parity_run(model, dec, vocab: int, n_pos: int, first_token: int, n_st
         worst = max(worst, dmax / np.abs(ref).max())
         if each_step is not None:
             each_step(s, got)
+        if say is not None:
+            say(f"{what}: step {s + 1} of {n_steps} compared, max|d| {dmax:.3e}")
         if gpu_next != ref_next:
             top2 = np.sort(ref)[-2:]
             gap = top2[1] - top2[0]

@@ -58,7 +58,7 @@ def oracle_bytes(rows, cols, t, sid, dev):
     return out
 
 
-def oracle_decoder(shape, extra):
+def oracle_decoder(shape, extra, say=print):
     """An oracle.Decoder over the oracle's own encoding of the model's values;
     every matrix of the device model must equal it byte for byte."""
     w = extra["weights"]
@@ -66,7 +66,7 @@ def oracle_decoder(shape, extra):
     host = {}
     for l, name, rows, cols, t, sid in devmodel.matrix_specs(shape):
         if l is not None and name == "wq" and l % 10 == 0:
-            print(f"  oracle encoding: layer {l} of {shape.n_layers}", flush=True)
+            say(f"  oracle encoding: layer {l} of {shape.n_layers}")
         ob = oracle_bytes(rows, cols, t, sid, dev)
         d = (w[name] if l is None else w["layers"][l][name])[1]
         assert torch.equal(d, torch.from_numpy(ob).to(dev)), f"layer {l} {name}: device bytes differ from the oracle's"
@@ -84,15 +84,22 @@ def oracle_decoder(shape, extra):
     return O.Decoder(cfg, mw, kk, vv)
 
 
-def _bench_model_parity(shape, n_steps, what):
-    print(f"{what}: building {shape.name} on the device", flush=True)
+def _bench_model_parity(shape, n_steps, what, capfd):
+    """Runs for minutes (the oracle encodes and decodes the whole model on the
+    host), so its progress goes straight to the terminal, past pytest's
+    output capture."""
+    def say(msg):
+        with capfd.disabled():
+            print(msg, flush=True)
+
+    say(f"{what}: building {shape.name} on the device")
     model, extra = devmodel.build(shape)
     torch.cuda.synchronize()
-    dec = oracle_decoder(shape, extra)
-    print(f"{what}: oracle encoding done, equal to the device bytes; decoding", flush=True)
+    dec = oracle_decoder(shape, extra, say)
+    say(f"{what}: oracle encoding done, equal to the device bytes; decoding")
     try:
         r = greedy_parity_run(model, dec, shape.vocab, shape.ctx, 1, n_steps, what=what, graph=True,
-                              oracle_threads=16)
+                              oracle_threads=16, say=say)
     finally:
         model.close()
         del model, extra, dec
@@ -101,10 +108,10 @@ def _bench_model_parity(shape, n_steps, what):
 
 
 @pytest.mark.timeout(900)
-def test_llama8b_q8_0_benchmark_model_full_depth():
-    _bench_model_parity(workloads.LLAMA_8B_Q8_0, 16, "8B Q8_0 (32 layers)")
+def test_llama8b_q8_0_benchmark_model_full_depth(capfd):
+    _bench_model_parity(workloads.LLAMA_8B_Q8_0, 16, "8B Q8_0 (32 layers)", capfd)
 
 
 @pytest.mark.timeout(900)
-def test_llama70b_mix_benchmark_model_full_depth():
-    _bench_model_parity(workloads.LLAMA_70B_MIX, 4, "70B Q4_K/Q6_K (80 layers)")
+def test_llama70b_mix_benchmark_model_full_depth(capfd):
+    _bench_model_parity(workloads.LLAMA_70B_MIX, 4, "70B Q4_K/Q6_K (80 layers)", capfd)
