@@ -513,29 +513,30 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, Geo<F>::WPC) bgemm(const uint
     // [1024 i, 1024 i + 1024) of the tile, lane l the granule at 1024 i + 16 l:
     // byte w of row q's run (lanes past row 15 or the run copy a granule of
     // the matrix into the padding)
-    int64_t cstart[T][G::NI];
-    int cw[G::NI];
+    // Offsets are kept relative to the copy base in 32 bits (a wave's tiles
+    // span at most 32 rows): the copy of step s starts at
+    // (crel + s L) & ~15 (base_rel and w are multiples of 16).
+    uint32_t crel[T][G::NI];
 #pragma unroll
     for (int i = 0; i < G::NI; ++i) {
         const int P = 1024 * i + 16 * lane, q = min(P / G::Lp, 15);
-        cw[i] = P - q * G::Lp;
+        const int w = P - q * G::Lp;
 #pragma unroll
-        for (int u = 0; u < T; ++u) cstart[u][i] = min(T0 + 16 * u + q, last) * row_bytes;
+        for (int u = 0; u < T; ++u) crel[u][i] = uint32_t(min(T0 + 16 * u + q, last) * row_bytes - base_rel) + uint32_t(w);
     }
+    const uint32_t lim = uint32_t(min<int64_t>(last_granule - base_rel, 0xfffffff0));
     const auto issue_w = [&](int b, int s) {
+        const uint32_t sL = uint32_t(s) * uint32_t(G::L);
 #pragma unroll
         for (int u = 0; u < T; ++u) {
             const uint32_t dst = lds_addr(ring + (b * T + u) * G::TB);
 #pragma unroll
-            for (int i = 0; i < G::NI; ++i) {
-                const int64_t a0 = (cstart[u][i] + int64_t(s) * G::L) & ~int64_t(15);
-                dma<16>(wbase, uint32_t(min(a0 + cw[i], last_granule) - base_rel), dst + 1024 * i);
-            }
+            for (int i = 0; i < G::NI; ++i) dma<16>(wbase, min((crel[u][i] + sL) & ~15u, lim), dst + 1024 * i);
         }
     };
-    int64_t rstart[T];                                                 // this lane's rows
+    uint32_t rlo[T];                                                   // low bits of this lane's row starts
 #pragma unroll
-    for (int u = 0; u < T; ++u) rstart[u] = min(T0 + 16 * u + r, last) * row_bytes;
+    for (int u = 0; u < T; ++u) rlo[u] = uint32_t(min(T0 + 16 * u + r, last) * row_bytes);
     f4 acc[T];
 #pragma unroll
     for (int u = 0; u < T; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
@@ -552,7 +553,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, Geo<F>::WPC) bgemm(const uint
         const uint8_t *const st = ring + (t % G::S) * T * G::TB;
 #pragma unroll
         for (int u = 0; u < T; ++u) {
-            const int mis = int((rstart[u] + int64_t(s) * G::L) & 15);
+            const int mis = int((rlo[u] + uint32_t(s) * uint32_t(G::L)) & 15u);
             const uint8_t *const p = st + u * G::TB + r * G::Lp + mis;   // this lane's row, step s
             typename F::Raw raw;
             F::load(p, s, g, nblk, raw);
