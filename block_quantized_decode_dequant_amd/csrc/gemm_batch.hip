@@ -6,16 +6,19 @@
 // in one pass, so the matrices are read once for k tokens instead of k times.
 // At k = 8 the arithmetic is 16 flops per weight; Q4_K at HBM speed would
 // need about 230 TFLOP/s of fp32 FMA, above the vector units' peak, so the
-// products run on the matrix cores (v_mfma_f32_16x16x16_f16):
+// products run on the matrix cores (v_mfma_f32_16x16x16_f16, and
+// v_mfma_f32_16x16x32_f16 for Q4_K):
 //
 //  * the MFMA's M dimension holds the activations, N the 16 weight rows of a
-//    tile, K 16 codes of one scale group (Q8_0, Q4_0, Q6_K, whose group
-//    scale is applied to the MFMA's fp32 sums) or any 16 codes of a Q4_K /
-//    Q5_K super-block, whose 6-bit scales are folded into the codes.  With
-//    N = weight row, every lane applies the scales of its own row to its own
-//    accumulators.
-//  * weight codes become fp16 exactly: small integers (q, q - 8, q - 32) or
-//    S_j * q * 2^-14 (Q4_K, Q5_K).  Nothing about the weights is rounded.
+//    tile, K 16 codes of one scale group (Q8_0, Q4_0, Q6_K) or the 32 codes
+//    of one Q4_K sub-block, whose scale is applied to the MFMA's fp32 sums,
+//    or any 16 codes of a Q5_K super-block, whose 6-bit scales are folded
+//    into the codes.  With N = weight row, every lane applies the scales of
+//    its own row to its own accumulators.
+//  * weight codes become fp16 exactly: small integers (q, q - 8, q - 32),
+//    Q4_K nibbles masked in place (the subnormals q 2^-24 and 16 q 2^-24,
+//    which the matrix cores multiply exactly), or S_j q 2^-14 (Q5_K).
+//    Nothing about the weights is rounded.
 //  * each activation is split into fp16 hi + lo (hi = fp16(x), lo =
 //    fp16(x - hi)), which leaves about 2^-22 relative error; the hi parts fill
 //    M rows 0-7 and the lo parts rows 8-15, which the padding of k <= 8 to 16
@@ -32,9 +35,13 @@
 //    from LDS.
 //  * MFMA lane layout (16x16x16 f16): src0 lane l holds A[l % 16][4(l/16) + i],
 //    src1 lane l holds B[4(l/16) + i][l % 16], the result lane l holds
-//    D[4(l/16) + i][l % 16], i = 0..3.  Inside one MFMA the order of the 16
-//    K slots is free as long as A and B agree, so each lane takes the codes of
-//    its row that lie together in memory.
+//    D[4(l/16) + i][l % 16], i = 0..3 (16x16x32: eight K slots per lane, the
+//    same result layout).  Inside one MFMA the order of the K slots is free
+//    as long as A and B agree, so each lane takes the codes of its row that
+//    lie together in memory.
+//  * one workgroup of eight waves per CU; the waves of a workgroup split the
+//    rows and, where that leaves too few workgroups, the columns, whose sums
+//    meet in LDS at the end.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
@@ -64,6 +71,18 @@ __device__ __forceinline__ uint32_t hmul(uint32_t w, _Float16 c) {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, w) * h2{c, c});
 }
 __device__ __forceinline__ f4 mfma(h4 a, h4 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0); }
+
+// 16x16x32 f16: src lane l holds 8 K slots of row / column l % 16 (the same
+// slots for A and B), the result the same layout as 16x16x16.
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4n __attribute__((ext_vector_type(4)));   // natural (16-byte) alignment
+typedef uint32_t u32x2n __attribute__((ext_vector_type(2)));   // 8-byte alignment
+__device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+__device__ __forceinline__ h8 cat(h4 a, h4 b) { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); }
+__device__ __forceinline__ h8 h8bits(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    return __builtin_bit_cast(h8, u32x4n{a, b, c, d});
+}
+__device__ __forceinline__ float ubyte(uint32_t w, int k) { return float((w >> (8 * k)) & 0xffu); }
 
 // Per format: load() issues every global load of one 256-column step into
 // a Raw of registers (no use of the data), compute() turns a loaded Raw into
@@ -118,79 +137,58 @@ struct BQ80 {
     }
 };
 
-// ---- Q4_K: a step is one super-block.  The 6-bit scales are folded into
-// the codes: (q * 2^-24 or q * 2^-20 as an fp16 subnormal) * fp16(S * 2^10
-// or S * 2^6) = S q 2^-14 exactly (S q <= 945), so one MFMA chain covers the
-// whole super-block and any value may sit in any K slot.  Lane group g takes
-// code bytes [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16), so each load
-// instruction reads 64 contiguous bytes of a row.  MFMA m uses word m / 2 of
-// those eight (low nibbles for even m, high for odd); code byte c holds
-// values 32 (2 (c / 32)) + c % 32 (low) and 32 (2 (c / 32) + 1) + c % 32
-// (high).  The mins go through one more MFMA: A = per-sub-block activation
-// sums (hi in K slots 0-7, lo in 8-15), B = M_j.
+// ---- Q4_K: a step is one super-block.  One 16x16x32 MFMA per sub-block j
+// (32 values sharing a 6-bit scale S_j and min M_j): lane group g takes code
+// bytes [8g, 8g + 8) of chunk j / 2 (low nibbles for even j, high for odd),
+// value 32 j + 8 g + 4 (m % 2) + perm4(i) for record slot m = 2j + m % 2.  A
+// nibble masked in place is an fp16 subnormal, q 2^-24 (low) or 16 q 2^-24
+// (high), which the matrix cores take exactly; S_j then scales the MFMA's
+// fp32 sums, so the codes need no arithmetic beyond their masks.  The mins
+// go through one more MFMA: A = per-sub-block activation sums (hi in K slots
+// 0-7, lo in 8-15), B = M_j, also as subnormals.  Rows of 144-byte blocks
+// keep every step start 16-byte aligned.
 struct BQ4K {
     static constexpr bool kMin = true;
     static constexpr int kStepBytes = 144, kTiles = 2;
-    struct Raw { u32x4 h, q0, q1; };
-    __host__ __device__ static int code_byte(int w, int g) { return w < 4 ? 16 * g + 4 * w : 64 + 16 * g + 4 * (w - 4); }
-    __host__ __device__ static int elem(int m, int g, int i) {
-        const int c = code_byte(m >> 1, g) + perm4(i);
-        return 32 * (2 * (c >> 5) + (m & 1)) + (c & 31);
-    }
+    struct Raw { u32x4n h; u32x2n q[4]; };
+    __host__ __device__ static int elem(int m, int g, int i) { return 32 * (m >> 1) + 8 * g + 4 * (m & 1) + perm4(i); }
     __device__ static void load(const uint8_t *b, int, int g, int, Raw &r) {
-        r.h = ld4(b);
-        r.q0 = ld4(b + 16 + 16 * g);
-        r.q1 = ld4(b + 80 + 16 * g);
+        const uint8_t *const a = static_cast<const uint8_t *>(__builtin_assume_aligned(b, 16));
+        r.h = *reinterpret_cast<const u32x4n *>(a);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) r.q[c] = *reinterpret_cast<const u32x2n *>(a + 16 + 32 * c + 8 * g);
     }
     // 6-bit scale S_j and min M_j of sub-block j from the 12 scale bytes
     // (words h.y, h.z, h.w): j < 4: low 6 bits of bytes j and j + 4; j >= 4:
     // low / high nibble of byte j + 4 with the top two bits of byte j - 4 / j.
-    __device__ static void scale_min(const u32x4 &h, int j, uint32_t &S, uint32_t &M) {
-        const uint32_t sc[3] = {h.y, h.z, h.w};
-        auto byte = [&](int k) { return (sc[k >> 2] >> (8 * (k & 3))) & 0xffu; };
-        if (j < 4) {
-            S = byte(j) & 63;
-            M = byte(j + 4) & 63;
-        } else {
-            S = (byte(j + 4) & 15) | ((byte(j - 4) >> 6) << 4);
-            M = (byte(j + 4) >> 4) | ((byte(j) >> 6) << 4);
-        }
-    }
+    // As bytes: S_0..3 = h.y & 0x3f.., S_4..7 = (h.w & 0x0f..) | (h.y >> 2 &
+    // 0x30..), M_0..3 = h.z & 0x3f.., M_4..7 = (h.w >> 4 & 0x0f..) | (h.z >> 2
+    // & 0x30..).
     __device__ static void compute(const Raw &r, const uint8_t *, int, int g, int, const h4 *xa, h4 xm, f4 &acc) {
-        // the two code pairs of this lane: chunks g / 2 (bytes 16g..) and
-        // 2 + g / 2 (bytes 64 + 16g..), sub-blocks 2hp, 2hp + 1 and 4 + 2hp,
-        // 5 + 2hp; only those four scales are decoded (bit fields at a
-        // lane-dependent offset)
-        const uint32_t o = 16u * uint32_t(g >> 1);
-        const uint32_t Sa0 = __builtin_amdgcn_ubfe(r.h.y, o, 6), Sa1 = __builtin_amdgcn_ubfe(r.h.y, o + 8, 6);
-        const uint32_t Sb0 = __builtin_amdgcn_ubfe(r.h.w, o, 4) | (__builtin_amdgcn_ubfe(r.h.y, o + 6, 2) << 4);
-        const uint32_t Sb1 = __builtin_amdgcn_ubfe(r.h.w, o + 8, 4) | (__builtin_amdgcn_ubfe(r.h.y, o + 14, 2) << 4);
-        const _Float16 fa0 = _Float16(float(Sa0 * 1024u)), fa1 = _Float16(float(Sa1 * 64u));
-        const _Float16 fb0 = _Float16(float(Sb0 * 1024u)), fb1 = _Float16(float(Sb1 * 64u));
-        const uint32_t words[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
-        f4 c = {0.f, 0.f, 0.f, 0.f};
+        const uint32_t s03 = r.h.y & 0x3f3f3f3fu;
+        const uint32_t s47 = (r.h.w & 0x0f0f0f0fu) | ((r.h.y >> 2) & 0x30303030u);
+        f4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-            const uint32_t v = words[w], t = v >> 8;
-            const _Float16 f0 = w < 4 ? fa0 : fb0, f1 = w < 4 ? fa1 : fb1;
-            c = mfma(xa[2 * w], pack(hmul(v & 0x000f000fu, f0), hmul(t & 0x000f000fu, f0)), c);
-            c = mfma(xa[2 * w + 1], pack(hmul(v & 0x00f000f0u, f1), hmul(t & 0x00f000f0u, f1)), c);
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t w0 = r.q[c].x, w1 = r.q[c].y, t0 = w0 >> 8, t1 = w1 >> 8;
+            const uint32_t sw = c < 2 ? s03 : s47;
+            const f4 cl = mfma32(cat(xa[4 * c], xa[4 * c + 1]),
+                                 h8bits(w0 & 0x000f000fu, t0 & 0x000f000fu, w1 & 0x000f000fu, t1 & 0x000f000fu),
+                                 f4{0.f, 0.f, 0.f, 0.f});
+            const f4 ch = mfma32(cat(xa[4 * c + 2], xa[4 * c + 3]),
+                                 h8bits(w0 & 0x00f000f0u, t0 & 0x00f000f0u, w1 & 0x00f000f0u, t1 & 0x00f000f0u),
+                                 f4{0.f, 0.f, 0.f, 0.f});
+            lo += ubyte(sw, 2 * (c & 1)) * cl;
+            hi += ubyte(sw, 2 * (c & 1) + 1) * ch;
         }
-        // B of the min MFMA: K slot 4g + i takes M_{(4g + i) & 7}: M_i (low 6
-        // bits of byte 4 + i) for even g, M_{4+i} (high nibble of byte 8 + i,
-        // top bits of byte 4 + i) for odd g
-        const bool odd = g & 1;
-        const uint32_t src = odd ? r.h.w : r.h.z, off = odd ? 4u : 0u, wlo = odd ? 4u : 6u, whi = odd ? 2u : 0u;
-        _Float16 mv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t M = __builtin_amdgcn_ubfe(src, 8u * i + off, wlo) |
-                               (__builtin_amdgcn_ubfe(r.h.z, 8u * i + 6u, whi) << 4);
-            mv[i] = _Float16(float(M));
-        }
-        const f4 cm = mfma(xm, h4{mv[0], mv[1], mv[2], mv[3]}, f4{0.f, 0.f, 0.f, 0.f});
-        const float d = h2f(r.h.x) * 16384.f, dmin = h2f(r.h.x >> 16);
-        acc += d * c - dmin * cm;
+        // B of the min MFMA: K slot 4g + i takes M_{(4g + i) & 7}, i.e. M_i for
+        // even g and M_{4+i} for odd g, each byte widened to a subnormal half
+        const uint32_t mw = (g & 1) ? ((r.h.w >> 4) & 0x0f0f0f0fu) | ((r.h.z >> 2) & 0x30303030u)
+                                    : r.h.z & 0x3f3f3f3fu;
+        const f4 cm = mfma(xm, pack(__builtin_amdgcn_perm(0u, mw, 0x0c010c00u), __builtin_amdgcn_perm(0u, mw, 0x0c030c02u)),
+                           f4{0.f, 0.f, 0.f, 0.f});
+        const float d = h2f(r.h.x) * 16777216.f, dmin = h2f(r.h.x >> 16) * 16777216.f;
+        acc += d * (lo + 0.0625f * hi) - dmin * cm;
     }
 };
 
@@ -238,16 +236,40 @@ struct BQ40 {
     }
 };
 
-// ---- Q5_K: as Q4_K (same lanes and K slots, scales folded into the
-// codes, one more MFMA for the mins) with the fifth bit of value 32j + l in
-// bit j of qh[l].  A lane's code bytes c all have c % 32 in
+// ---- Q5_K: scales folded into the codes: (q * 2^-24 as an fp16
+// subnormal) * fp16(S * 2^10) = S q 2^-14 exactly, so one MFMA chain
+// covers the whole super-block and any value may sit in any K slot; one more
+// MFMA for the mins (as Q4_K).  The fifth bit of value 32j + l is bit j of
+// qh[l].  A lane's code bytes c all have c % 32 in
 // [16 (g % 2), 16 (g % 2) + 16), so one 16-byte piece of qh serves them.
 // S q <= 63 * 31 = 1953 keeps S q 2^-14 exact in fp16.
 struct BQ5K {
     static constexpr bool kMin = true;
     static constexpr int kStepBytes = 176, kTiles = 1;
     struct Raw { u32x4 h, qh, q0, q1; };
-    __host__ __device__ static int elem(int m, int g, int i) { return BQ4K::elem(m, g, i); }
+    // lane group g takes code bytes [16g, 16g + 16) and [64 + 16g, 64 + 16g +
+    // 16); MFMA m uses word m / 2 of those eight (low nibbles for even m, high
+    // for odd); code byte c holds values 64 (c / 32) + c % 32 (low) and 32
+    // more (high)
+    __host__ __device__ static int code_byte(int w, int g) { return w < 4 ? 16 * g + 4 * w : 64 + 16 * g + 4 * (w - 4); }
+    __host__ __device__ static int elem(int m, int g, int i) {
+        const int c = code_byte(m >> 1, g) + perm4(i);
+        return 32 * (2 * (c >> 5) + (m & 1)) + (c & 31);
+    }
+    // 6-bit scale S_j and min M_j of sub-block j from the 12 scale bytes
+    // (words h.y, h.z, h.w): j < 4: low 6 bits of bytes j and j + 4; j >= 4:
+    // low / high nibble of byte j + 4 with the top two bits of byte j - 4 / j.
+    __device__ static void scale_min(const u32x4 &h, int j, uint32_t &S, uint32_t &M) {
+        const uint32_t sc[3] = {h.y, h.z, h.w};
+        auto byte = [&](int k) { return (sc[k >> 2] >> (8 * (k & 3))) & 0xffu; };
+        if (j < 4) {
+            S = byte(j) & 63;
+            M = byte(j + 4) & 63;
+        } else {
+            S = (byte(j + 4) & 15) | ((byte(j - 4) >> 6) << 4);
+            M = (byte(j + 4) >> 4) | ((byte(j) >> 6) << 4);
+        }
+    }
     __device__ static void load(const uint8_t *b, int, int g, int, Raw &r) {
         r.h = ld4(b);
         r.qh = ld4(b + 16 + 16 * (g & 1));
@@ -257,7 +279,7 @@ struct BQ5K {
     __device__ static void compute(const Raw &r, const uint8_t *, int, int g, int, const h4 *xa, h4 xm, f4 &acc) {
         uint32_t S[8], M[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) BQ4K::scale_min(r.h, j, S[j], M[j]);
+        for (int j = 0; j < 8; ++j) scale_min(r.h, j, S[j], M[j]);
         const int hp = g >> 1;
         const uint32_t words[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
         const uint32_t hw[4] = {r.qh.x, r.qh.y, r.qh.z, r.qh.w};
@@ -365,7 +387,7 @@ template <class F>
 struct Geo {
     static constexpr int T = F::kTiles;
     static constexpr int S = 3;                                  // ring stages: two steps copied ahead
-    static constexpr int NW = 4;                                 // waves per workgroup
+    static constexpr int NW = 8;                                 // waves per workgroup (two per SIMD)
     static constexpr int L = F::kStepBytes;
     static constexpr int Lc = (L + 15 + 15) / 16 * 16;
     static constexpr int Lp = ((Lc / 16) & 1) ? Lc : Lc + 16;
@@ -374,8 +396,7 @@ struct Geo {
     static constexpr int WAVE = S * T * TB;                      // LDS bytes of one wave's ring
     static constexpr int LDS = NW * WAVE;
     static constexpr int REC = 8192 + (F::kMin ? 512 : 0) + 32;  // activation record of one step
-    static constexpr int WPC = 2;                                // workgroups per CU (two waves per SIMD)
-    static_assert(WPC * LDS <= 160 * 1024, "LDS of two workgroups per CU");
+    static_assert(LDS <= 160 * 1024, "LDS of one workgroup per CU");
 };
 
 // Activation records, one workgroup per 256-column step s.  Record layout
@@ -475,120 +496,140 @@ __device__ __forceinline__ void load_x(const uint8_t *__restrict__ rec, int s, i
     xr.up = *reinterpret_cast<const f4 *>(rc + Geo<F>::REC - 32 + 16 * (g & 1));
 }
 
-// Main pass.  Workgroup (x, y) owns rows [64 T x, 64 T (x + 1)) and steps
-// [y sps, (y + 1) sps); its waves work independently (no barrier): wave w
-// owns the T 16-row tiles from row 16 T (4 x + w).  Each step's weights flow
-// through the wave's ring of S LDS stages (global_load_lds of whole row
-// runs, so every copy instruction reads long contiguous pieces of a few
-// rows), copied two steps ahead; the step's activations come from the
-// records (L2-resident, 1 KB contiguous per load instruction) into
-// registers one step ahead.  The loads of one wave complete in issue
-// order, and each step issues its activations before the weights two steps
-// on, so one wait covers both.  A wave reads its weight operands from LDS,
-// computes each tile's sums for the step, undoes the record's scale, and at
-// the end writes its outputs to Y (one split) or to partial[split][n][row],
-// which bgemm_reduce adds in split order.
+// Main pass.  A workgroup's NW waves form nr = NW / nc row groups of nc
+// column splits: wave w takes the T 16-row tiles from row 16 T (nr x + w /
+// nc) and the steps [c sps, (c + 1) sps) of column split c = nc y + w % nc
+// (y > 0 only when the columns are also split between workgroups).  The
+// waves work independently until the end (no barrier in the loop).  Each
+// step's weights flow through the wave's ring of S LDS stages
+// (global_load_lds of whole row runs, so every copy instruction reads long
+// contiguous pieces of a few rows), copied two steps ahead; the step's
+// activations come from the records (L2-resident, 1 KB contiguous per load
+// instruction) into registers two steps ahead.  The loads of one wave
+// complete in issue order, and each step issues its activations before the
+// weights two steps on, so one wait covers both.  A wave reads its weight
+// operands from LDS, computes each tile's sums for the step and undoes the
+// record's scale.  At the end the nc splits of a row group add their sums
+// through LDS in split order, and the first wave of the group writes them to
+// Y (one split between workgroups) or to partial[y][n][row], which
+// bgemm_reduce adds in workgroup order.
 template <class F>
-__global__ void __launch_bounds__(64 * Geo<F>::NW, Geo<F>::WPC) bgemm(const uint8_t *__restrict__ W, int64_t row_bytes, int rows,
+__global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__restrict__ W, int64_t row_bytes, int rows,
                                                           int nsteps, int nblk, const uint8_t *__restrict__ rec,
-                                                          int sps, float *__restrict__ Y, int k, int accumulate,
+                                                          int nc, int sps, float *__restrict__ Y, int k, int accumulate,
                                                           float *__restrict__ partial) {
     using G = Geo<F>;
     constexpr int T = G::T;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, kept in a scalar register
-    const int split = blockIdx.y, nsplit = gridDim.y;
-    const int s_lo = split * sps, n = min(sps, nsteps - s_lo);
-    const int64_t T0 = (int64_t(blockIdx.x) * G::NW + wv) * 16 * T;    // first row of this wave's tiles
-    if (T0 >= rows) return;
-    const int64_t last = rows - 1;
-    // copies read whole 16-byte granules; none starts past the one that
-    // holds the matrix's last byte (W is 16-byte aligned)
-    const int64_t last_granule = (int64_t(rows) * row_bytes - 1) & ~int64_t(15);
-    const int64_t base_rel = (T0 * row_bytes) & ~int64_t(15);
-    const uint8_t *const wbase = W + base_rel;                         // this wave's copy base (uniform)
-    uint8_t *const ring = lds + wv * G::WAVE;
-    // this lane's part of a tile copy: instruction i fills LDS bytes
-    // [1024 i, 1024 i + 1024) of the tile, lane l the granule at 1024 i + 16 l:
-    // byte w of row q's run (lanes past row 15 or the run copy a granule of
-    // the matrix into the padding)
-    // Offsets are kept relative to the copy base in 32 bits (a wave's tiles
-    // span at most 32 rows): the copy of step s starts at
-    // (crel + s L) & ~15 (base_rel and w are multiples of 16).
-    uint32_t crel[T][G::NI];
-#pragma unroll
-    for (int i = 0; i < G::NI; ++i) {
-        const int P = 1024 * i + 16 * lane, q = min(P / G::Lp, 15);
-        const int w = P - q * G::Lp;
-#pragma unroll
-        for (int u = 0; u < T; ++u) crel[u][i] = uint32_t(min(T0 + 16 * u + q, last) * row_bytes - base_rel) + uint32_t(w);
-    }
-    const uint32_t lim = uint32_t(min<int64_t>(last_granule - base_rel, 0xfffffff0));
-    const auto issue_w = [&](int b, int s) {
-        const uint32_t sL = uint32_t(s) * uint32_t(G::L);
-#pragma unroll
-        for (int u = 0; u < T; ++u) {
-            const uint32_t dst = lds_addr(ring + (b * T + u) * G::TB);
-#pragma unroll
-            for (int i = 0; i < G::NI; ++i) dma<16>(wbase, min((crel[u][i] + sL) & ~15u, lim), dst + 1024 * i);
-        }
-    };
-    uint32_t rlo[T];                                                   // low bits of this lane's row starts
-#pragma unroll
-    for (int u = 0; u < T; ++u) rlo[u] = uint32_t(min(T0 + 16 * u + r, last) * row_bytes);
+    const int wc = wv % nc, nr = G::NW / nc;
+    const int s_lo = (blockIdx.y * nc + wc) * sps, n = max(0, min(sps, nsteps - s_lo));
+    const int64_t T0 = (int64_t(blockIdx.x) * nr + wv / nc) * 16 * T;  // first row of this wave's tiles
     f4 acc[T];
 #pragma unroll
     for (int u = 0; u < T; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
-
-    const auto compute = [&](int t, const XRegs &xr) {
-        const int s = s_lo + t;
-        h4 xa[16];
+    if (T0 < rows && n > 0) {
+        const int64_t last = rows - 1;
+        // copies read whole 16-byte granules; none starts past the one that
+        // holds the matrix's last byte (W is 16-byte aligned)
+        const int64_t last_granule = (int64_t(rows) * row_bytes - 1) & ~int64_t(15);
+        const int64_t base_rel = (T0 * row_bytes) & ~int64_t(15);
+        const uint8_t *const wbase = W + base_rel;                         // this wave's copy base (uniform)
+        uint8_t *const ring = lds + wv * G::WAVE;
+        // this lane's part of a tile copy: instruction i fills LDS bytes
+        // [1024 i, 1024 i + 1024) of the tile, lane l the granule at 1024 i + 16 l:
+        // byte w of row q's run (lanes past row 15 or the run copy a granule of
+        // the matrix into the padding)
+        // Offsets are kept relative to the copy base in 32 bits (a wave's tiles
+        // span at most 32 rows): the copy of step s starts at
+        // (crel + s L) & ~15 (base_rel and w are multiples of 16).
+        uint32_t crel[T][G::NI];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            xa[2 * q] = pack(xr.x[q].x, xr.x[q].y);
-            xa[2 * q + 1] = pack(xr.x[q].z, xr.x[q].w);
-        }
-        const h4 xm = F::kMin ? pack(xr.m.x, xr.m.y) : h4{};
-        const uint8_t *const st = ring + (t % G::S) * T * G::TB;
+        for (int i = 0; i < G::NI; ++i) {
+            const int P = 1024 * i + 16 * lane, q = min(P / G::Lp, 15);
+            const int w = P - q * G::Lp;
 #pragma unroll
-        for (int u = 0; u < T; ++u) {
-            const int mis = int((rlo[u] + uint32_t(s) * uint32_t(G::L)) & 15u);
-            const uint8_t *const p = st + u * G::TB + r * G::Lp + mis;   // this lane's row, step s
-            typename F::Raw raw;
-            F::load(p, s, g, nblk, raw);
-            f4 c = {0.f, 0.f, 0.f, 0.f};
-            F::compute(raw, p, s, g, nblk, xa, xm, c);
-            acc[u] += xr.up * c;
+            for (int u = 0; u < T; ++u) crel[u][i] = uint32_t(min(T0 + 16 * u + q, last) * row_bytes - base_rel) + uint32_t(w);
         }
-    };
+        const uint32_t lim = uint32_t(min<int64_t>(last_granule - base_rel, 0xfffffff0));
+        const auto issue_w = [&](int b, int s) {
+            const uint32_t sL = uint32_t(s) * uint32_t(G::L);
+#pragma unroll
+            for (int u = 0; u < T; ++u) {
+                const uint32_t dst = lds_addr(ring + (b * T + u) * G::TB);
+#pragma unroll
+                for (int i = 0; i < G::NI; ++i) dma<16>(wbase, min((crel[u][i] + sL) & ~15u, lim), dst + 1024 * i);
+            }
+        };
+        uint32_t rlo[T];                                                   // low bits of this lane's row starts
+#pragma unroll
+        for (int u = 0; u < T; ++u) rlo[u] = uint32_t(min(T0 + 16 * u + r, last) * row_bytes);
 
-    // per step: activations (8 + kMin + 1 loads), then T NI weight copies;
-    // both are issued two steps ahead, so step t's are in once at most those
-    // of step t + 1 are outstanding
-    constexpr int kX = 9 + (F::kMin ? 1 : 0), kW = T * G::NI;
-    XRegs x0, x1, x2;
-    const auto step = [&](int t, const XRegs &cur, XRegs &ahead) {
-        wait_vm(t + 1 < n ? kX + kW : 0);
-        if (t + 2 < n) {
-            load_x<F>(rec, s_lo + t + 2, lane, g, ahead);
-            issue_w((t + 2) % G::S, s_lo + t + 2);
+        const auto compute = [&](int t, const XRegs &xr) {
+            const int s = s_lo + t;
+            h4 xa[16];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                xa[2 * q] = pack(xr.x[q].x, xr.x[q].y);
+                xa[2 * q + 1] = pack(xr.x[q].z, xr.x[q].w);
+            }
+            const h4 xm = F::kMin ? pack(xr.m.x, xr.m.y) : h4{};
+            const uint8_t *const st = ring + (t % G::S) * T * G::TB;
+#pragma unroll
+            for (int u = 0; u < T; ++u) {
+                const int mis = int((rlo[u] + uint32_t(s) * uint32_t(G::L)) & 15u);
+                const uint8_t *const p = st + u * G::TB + r * G::Lp + mis;   // this lane's row, step s
+                typename F::Raw raw;
+                F::load(p, s, g, nblk, raw);
+                f4 c = {0.f, 0.f, 0.f, 0.f};
+                F::compute(raw, p, s, g, nblk, xa, xm, c);
+                acc[u] += xr.up * c;
+            }
+        };
+
+        // per step: activations (8 + kMin + 1 loads), then T NI weight copies;
+        // both are issued two steps ahead, so step t's are in once at most those
+        // of step t + 1 are outstanding
+        constexpr int kX = 9 + (F::kMin ? 1 : 0), kW = T * G::NI;
+        XRegs x0, x1, x2;
+        const auto step = [&](int t, const XRegs &cur, XRegs &ahead) {
+            wait_vm(t + 1 < n ? kX + kW : 0);
+            if (t + 2 < n) {
+                load_x<F>(rec, s_lo + t + 2, lane, g, ahead);
+                issue_w((t + 2) % G::S, s_lo + t + 2);
+            }
+            compute(t, cur);
+        };
+        issue_w(0, s_lo);
+        load_x<F>(rec, s_lo, lane, g, x0);
+        if (n > 1) {
+            issue_w(1, s_lo + 1);
+            load_x<F>(rec, s_lo + 1, lane, g, x1);
         }
-        compute(t, cur);
-    };
-    issue_w(0, s_lo);
-    load_x<F>(rec, s_lo, lane, g, x0);
-    if (n > 1) {
-        issue_w(1, s_lo + 1);
-        load_x<F>(rec, s_lo + 1, lane, g, x1);
+        for (int t = 0; t < n; t += 3) {
+            step(t, x0, x2);
+            if (t + 1 >= n) break;
+            step(t + 1, x1, x0);
+            if (t + 2 >= n) break;
+            step(t + 2, x2, x1);
+        }
     }
-    for (int t = 0; t < n; t += 3) {
-        step(t, x0, x2);
-        if (t + 1 >= n) break;
-        step(t + 1, x1, x0);
-        if (t + 2 >= n) break;
-        step(t + 2, x2, x1);
+    if (nc > 1) {
+        // every wave's copies have landed and its ring reads are done (the
+        // last step waits for all loads); the rings become the exchange area
+        __syncthreads();
+        f4 *const xch = reinterpret_cast<f4 *>(lds);                     // [wave][tile][lane]
+#pragma unroll
+        for (int u = 0; u < T; ++u) xch[(wv * T + u) * 64 + lane] = acc[u];
+        __syncthreads();
+        if (wc == 0) {
+#pragma unroll
+            for (int u = 0; u < T; ++u)
+                for (int c = 1; c < nc; ++c) acc[u] += xch[((wv + c) * T + u) * 64 + lane];
+        }
     }
+    if (wc != 0 || T0 >= rows) return;
     // lanes g and g + 2 hold the hi and lo parts of outputs n = 4g + i of row r
 #pragma unroll
     for (int u = 0; u < T; ++u) {
@@ -598,8 +639,8 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, Geo<F>::WPC) bgemm(const uint
             const int nn = 4 * g + i;
             const float o = acc[u][i] + __shfl_down(acc[u][i], 32, 64);
             if (g < 2 && nn < k && R < rows) {
-                if (nsplit > 1) {
-                    partial[(int64_t(split) * k + nn) * rows + R] = o;
+                if (gridDim.y > 1) {
+                    partial[(int64_t(blockIdx.y) * k + nn) * rows + R] = o;
                 } else {
                     float *py = Y + nn * int64_t(rows) + R;
                     *py = accumulate ? *py + o : o;
@@ -620,29 +661,41 @@ __global__ void __launch_bounds__(256) bgemm_reduce(const float *__restrict__ pa
 }
 
 struct BgemmShape {
-    int groups, nsplit, sps;
+    int groups, nc, nsplit, sps;
 };
 
-// Column splits: the fewest that minimise (rounds of workgroups over the
-// chip, WPC per CU) x (steps per workgroup + the ring's fill), so that
-// short or narrow matrices still fill the CUs.
+// Launch shape: one workgroup of NW waves per CU.  The columns are split
+// nc ways between the waves of a workgroup (their sums meet in LDS) and/or
+// nsplit ways between workgroups (partial sums through the workspace and a
+// third kernel).  The choice minimises (rounds of workgroups over the CUs) x
+// (steps per wave + the ring's fill), plus a few steps for the third kernel,
+// plus a term for the activation records: waves of one column split read the
+// same record at the same step (served once by the CU's cache), so a CU
+// reads nc records per step instead of one.  Costs in twentieths of a
+// step; ties go to fewer splits.
 template <class F>
 BgemmShape bgemm_shape(int64_t rows, int64_t cols) {
     using G = Geo<F>;
+    constexpr int kReduceCost = 60;   // the third kernel: three steps of one wave
     BgemmShape b{};
     const int ns = int((cols + 255) / 256);
-    b.groups = int((rows + 16 * G::T * G::NW - 1) / (16 * G::T * G::NW));
-    const int64_t slots = int64_t(kNumCUs) * G::WPC;
+    const int64_t tiles = (rows + 16 * G::T - 1) / (16 * G::T);
     int64_t best = -1;
     for (int sp = 1; sp <= std::min(ns, 64); ++sp) {
-        const int sps = (ns + sp - 1) / sp;
-        if ((ns + sps - 1) / sps != sp) continue;          // same steps per split as a smaller count
-        const int64_t rounds = (int64_t(b.groups) * sp + slots - 1) / slots;
-        const int64_t cost = rounds * (sps + G::S - 1);
-        if (best < 0 || cost < best) {
-            best = cost;
-            b.nsplit = sp;
-            b.sps = sps;
+        for (int nc = 1; nc <= G::NW; nc *= 2) {
+            const int total = nc * sp, sps = (ns + total - 1) / total;
+            if ((ns + sps - 1) / sps != total) continue;   // some split would have no step
+            const int64_t groups = (tiles + G::NW / nc - 1) / (G::NW / nc);
+            const int64_t rounds = (groups * sp + kNumCUs - 1) / kNumCUs;
+            const int64_t cost = 20 * rounds * (sps + G::S - 1) + (sp > 1 ? kReduceCost : 0) +
+                                 rounds * sps * (nc - 1);
+            if (best < 0 || cost < best) {
+                best = cost;
+                b.groups = int(groups);
+                b.nc = nc;
+                b.nsplit = sp;
+                b.sps = sps;
+            }
         }
     }
     return b;
@@ -677,7 +730,7 @@ hipError_t run_bgemm(const void *W, int64_t row_bytes, int64_t rows, int64_t col
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bgemm<F>, dim3(unsigned(b.groups), unsigned(b.nsplit)), dim3(64 * G::NW), G::LDS, st,
-                       static_cast<const uint8_t *>(W), row_bytes, int(rows), ns, int(nblk), rec, b.sps, Y, k,
+                       static_cast<const uint8_t *>(W), row_bytes, int(rows), ns, int(nblk), rec, b.nc, b.sps, Y, k,
                        accumulate, partial);
     if ((e = hipGetLastError()) != hipSuccess || b.nsplit == 1) return e;
     const int64_t nt2 = int64_t(k) * rows;

@@ -94,8 +94,9 @@ def test_gemm_batch_argument_errors():
         extra = wsb(t, rows, cols) - ns * rec[t]
         assert extra >= 0 and extra % (8 * rows * 4) == 0, (t, rows, cols)
         assert extra // (8 * rows * 4) <= min(ns, 64)
-    assert wsb(nt.Q4_K, 8192, 8192) > 32 * 8736          # too few rows to fill the chip: split
-    assert wsb(nt.Q4_K, 3, 65536) > 256 * 8736
+    # enough rows: the waves of a workgroup split the columns, no partial sums
+    assert wsb(nt.Q4_K, 8192, 8192) == 32 * 8736 and wsb(nt.Q8_0, 4096, 4096) == 16 * 8224
+    assert wsb(nt.Q4_K, 3, 65536) > 256 * 8736          # a few rows: split between workgroups too
     assert wsb(nt.F32, 4, 256) == 0 and wsb(nt.Q4_K, 4, 100) == 0 and wsb(nt.Q4_K, 4, 65536 + 256) == 0
     assert wsb(nt.Q4_K, -1, 256) == 0
     assert _batch(nt.Q4_K, A, A, A, 4, 256, 0) == nt.NT_EINVAL

@@ -6,8 +6,8 @@ Bar: elementwise within 1e-4 + 2e-3 |y|, as for the GEMV (the activations'
 fp16 hi/lo split leaves about 2^-22 relative error per element, far inside
 it).  Shapes span one tile, ragged row tiles, a partial 256-column step
 (Q8_0, Q4_0), column-split launches (few rows), every k from 1 to 8, the
-widest rows the call takes, the full 8192 x 8192 70B projection shape, and
-sampled rows of the two FFN shapes.
+widest rows the call takes, the full 8192 x 8192 70B and 4096 x 4096 8B
+projection shapes, and sampled rows of the two FFN shapes.
 """
 import numpy as np
 import pytest
@@ -92,10 +92,22 @@ def test_gemm_batch_rows_are_independent_of_k():
         assert np.array_equal(one[0], all8[n])
 
 
+@pytest.mark.parametrize("t", TYPES, ids=TID)
+@pytest.mark.parametrize("rows,cols,k", [(1500, 5888, 8), (16, 16640, 5), (16, 24576, 3)])
+def test_gemm_batch_launch_shapes(t, rows, cols, k):
+    """Column splits between the waves of a workgroup (sums added in LDS in
+    split order: 1500 x 5888 splits 23 steps 8 ways for one-tile formats,
+    the last split shorter), between workgroups only (16 x 16640: partial
+    sums added by the third kernel, the last split shorter) and both (16 x
+    24576)."""
+    _case(t, rows, cols, k, seed=rows + cols)
+
+
 def test_gemm_batch_tall_and_wide_matrices():
     # 40040 rows of 2048 columns (ragged last workgroup, with a partial
-    # 16-row tile), and 600 rows of 8960 columns (35 steps: column ranges of
-    # unequal length, partial sums added by the second kernel)
+    # 16-row tile; more workgroups than CUs), and 600 rows of 8960 columns
+    # (35 steps split between workgroups: partial sums added by the third
+    # kernel)
     _case(O.Q4_K, 40040, 2048, 8, seed=31)
     _case(O.Q6_K, 40040, 2048, 3, seed=33)
     _case(O.Q8_0, 600, 8960, 5, seed=32)
@@ -119,11 +131,13 @@ def test_gemm_batch_large_activations_are_scaled_not_lost(t):
                      what=f"gemm_batch {t} large activations, vector {n}")
 
 
-@pytest.mark.parametrize("t", [O.Q4_K, O.Q6_K], ids=["q4_k", "q6_k"])
-def test_gemm_batch_70b_projection_shape(t):
-    """8192 x 8192 with k = 8, every output against the oracle."""
-    rows, cols = workloads.KQ_SHAPES[0]
-    w = synth.normal_f32(workloads.SEED, workloads.kq_w_stream(0), rows * cols, std=0.02)
+@pytest.mark.parametrize("t,rows,cols", [(O.Q4_K, 8192, 8192), (O.Q6_K, 8192, 8192), (O.Q8_0, 4096, 4096)],
+                         ids=["q4_k-8192x8192", "q6_k-8192x8192", "q8_0-4096x4096"])
+def test_gemm_batch_projection_shapes(t, rows, cols):
+    """The 70B (K-quants) and 8B (Q8_0) attention projection shapes with
+    k = 8, every output against the oracle.  These launches split the
+    columns between the waves of each workgroup (4 or 8 ways)."""
+    w = synth.normal_f32(workloads.SEED, workloads.kq_w_stream(0) + (rows != 8192), rows * cols, std=0.02)
     W = O.quantize(t, w)
     X = np.stack([synth.activation(workloads.SEED, workloads.kq_x_stream(0) + 100 * n, cols) for n in range(8)])
     got = _run(t, W, X, rows, cols, 8)
