@@ -16,8 +16,9 @@ sample of the same workload: the first rows of each matrix.
 Alongside, in the same JSON line: the Q8_0 GEMV at 4096x4096 ("q8_0_gemv",
 the small configuration), Q5_K GEMV at the two Llama-70B FFN shapes
 ("q5_k_gemv"), and the batched verify pass of self-speculative decoding
-("verify_gemm": k = 8 vectors per weight read), each timed like the sweep's
-per-kernel times.  Decode measurements ("decode"): the Llama-3-8B-shaped Q8_0
+("verify_gemm": k = 8 vectors per weight read), and whole-matrix
+dequantization to fp32 ("dequant"), each timed like the sweep's per-kernel
+times.  Decode measurements ("decode"): the Llama-3-8B-shaped Q8_0
 model (128 greedy tokens from position 1024), the Llama-70B-shaped Q4_K/Q6_K
 model (64 tokens from 4096), each replayed from a captured HIP graph, the 70B
 all-Q6_K model with 24 GiB of layers resident and the rest streamed from
@@ -331,6 +332,48 @@ def q5_k_gemv(steps):
         out.append({"rows": rows, "cols": cols, "bytes": alg, "us": round(us, 3),
                     "gbs": round(alg / (us * 1e-6) / 1e9, 1), "frac": round(alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)})
         del Ws, base
+        torch.cuda.empty_cache()
+    return out
+
+
+DEQUANT_CASES = [("q8_0", 4096, 4096), ("q4_k", 8192, 8192), ("q6_k", 8192, 8192)]
+
+
+def dequant_leg(steps):
+    """nt_dequant of whole matrices to fp32 (the Q8_0 4096x4096 and 70B
+    8192x8192 K-quant projection shapes), timed like the sweep: blocks encoded
+    on the device from N(0, 0.02) values, block copies and output buffers each
+    rotated over at least 1 GiB, one HIP graph of `steps` launches.  "bytes":
+    blocks read + fp32 output written; "fill_gbs": the same outputs written by
+    a plain fill (torch's fill_), the write-side ceiling.  Reported beside the
+    sweep, not part of `value`."""
+    import math
+
+    import torch
+
+    from block_quantized_decode_dequant_amd import nt, synth, workloads
+
+    dev = torch.device("cuda:0")
+    out = []
+    for name, rows, cols in DEQUANT_CASES:
+        t = {"q8_0": nt.Q8_0, "q4_k": nt.Q4_K, "q6_k": nt.Q6_K}[name]
+        n = rows * cols
+        w32 = torch.from_numpy(synth.normal_f32(workloads.SEED, 800 + rows // 1024, n, std=0.02)).to(dev)
+        nbytes = rows * nt.row_bytes(t, cols)
+        base = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        nt.nt_quantize(t, w32, base, n)
+        del w32
+        Ws = [base] + [base.clone() for _ in range(copies_for(nbytes) - 1)]
+        Ys = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(copies_for(4 * n))]
+        cyc = len(Ws) * len(Ys) // math.gcd(len(Ws), len(Ys))
+        side = torch.cuda.Stream()
+        us = time_rotated(torch, lambda i: nt.nt_dequant(t, Ws[i % len(Ws)], Ys[i % len(Ys)], n), cyc, steps, side)
+        fill_us = time_rotated(torch, lambda i: Ys[i % len(Ys)].fill_(1.0), len(Ys), steps, side)
+        alg = nbytes + 4 * n
+        out.append({"type": name, "rows": rows, "cols": cols, "bytes": alg, "us": round(us, 3),
+                    "gbs": round(alg / (us * 1e-6) / 1e9, 1), "frac": round(alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                    "fill_gbs": round(4 * n / (fill_us * 1e-6) / 1e9, 1)})
+        del Ws, Ys, base
         torch.cuda.empty_cache()
     return out
 
@@ -743,7 +786,8 @@ def main():
     line["q8_0_gemv"] = q8_0_gemv(args.steps)
     line["q5_k_gemv"] = q5_k_gemv(args.steps)
     line["verify_gemm"] = verify_gemm(args.steps)
-    done("q8_0, q5_k and verify legs", t0)
+    line["dequant"] = dequant_leg(args.steps)
+    done("q8_0, q5_k, verify and dequant legs", t0)
     if args.decode != "none":
         dec = {}
         if args.decode in ("8b", "all"):

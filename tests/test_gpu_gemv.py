@@ -34,6 +34,9 @@ def _blocks(t, nvals, seed, std=0.02):
 # ---- dequant -------------------------------------------------------------------
 @pytest.mark.parametrize("t", TYPES, ids=TID)
 def test_dequant_bit_exact(t):
+    """Both kernels: a 16-byte-aligned output (256-value windows, one 16-byte
+    store per lane) and a 4-byte-aligned one (one value per thread); for the
+    32-value formats the last window is partial (3 blocks past a multiple of 8)."""
     device()
     parts = [_blocks(t, 64 * 256, 1), _blocks(t, 8 * 256, 2, std=3.0)]
     for path in sorted(glob.glob(os.path.join(GOLDEN, "*.txt"))):
@@ -41,11 +44,20 @@ def test_dequant_bit_exact(t):
         if gt == t:
             parts.append(blk)
     blocks = np.concatenate(parts)
+    nb = blocks.size // O.block_bytes(t)
+    if O.block_elems(t) == 32:
+        extra = (8 - nb % 8 + 3) % 8 or 8          # leaves 3 blocks in the last window
+        blocks = np.concatenate([blocks, _blocks(t, 32 * extra, 3)])
+        assert (blocks.size // O.block_bytes(t)) % 8 == 3
     n = blocks.size // O.block_bytes(t) * O.block_elems(t)
-    out = torch.empty(n, dtype=torch.float32, device=device())
-    nt.nt_dequant(t, to_dev(blocks), out, n)
     ref = O.dequant(t, blocks, n)
-    assert np.array_equal(host(out).view(np.uint32), ref.view(np.uint32))
+    dev_blocks = to_dev(blocks)
+    out = torch.full((n + 8,), float("nan"), dtype=torch.float32, device=device())
+    for off in (0, 1):
+        nt.nt_dequant(t, dev_blocks, out[off:off + n], n)
+        got = host(out)
+        assert np.array_equal(got[off:off + n].view(np.uint32), ref.view(np.uint32)), f"output offset {4 * off} bytes"
+        assert np.isnan(got[off + n:]).all(), "written past n"
 
 
 def test_dequant_q8_0_subnormal_scales():
