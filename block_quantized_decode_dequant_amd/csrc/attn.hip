@@ -186,7 +186,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
             const int slot = lane % NP;
             const int piece = slot ^ (rl & SWZ);
             const uint32_t off = uint32_t(min(t0 + rl, last)) * uint32_t(2 * D) + uint32_t(piece) * 16u;
-            dma<16>(kb, off, lds_addr(k_rows) + 1024 * cp);
+            dma<16, true>(kb, off, lds_addr(k_rows) + 1024 * cp);
         }
         for (int k = 0; k < cpw; ++k) {
             const int cp = wave * cpw + k;
@@ -194,7 +194,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_split_kernel(
             const int slot = lane % NP;
             const int piece = slot ^ (rl & SWZ);
             const uint32_t off = uint32_t(min(t0 + rl, last)) * uint32_t(2 * D) + uint32_t(piece) * 16u;
-            dma<16>(vb, off, lds_addr(v_rows) + 1024 * cp);
+            dma<16, true>(vb, off, lds_addr(v_rows) + 1024 * cp);
         }
     }
 

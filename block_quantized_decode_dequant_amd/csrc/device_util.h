@@ -122,10 +122,13 @@ typedef const __attribute__((address_space(1))) void gbl_void;
 // of a ring stage is preceded by an explicit s_waitcnt on the loads that fill
 // it.  The "memory" clobber keeps the copies ordered against other memory
 // operations in program order.
-template <int V>
+template <int V, bool NT = false>
 __device__ __forceinline__ void dma(const uint8_t *base, uint32_t off, uint32_t lds) {
     int m0_out;   // M0 is declared written (an output), so no value of the compiler's lives in it across the copy
-    if constexpr (V == 16)
+    if constexpr (V == 16 && NT)
+        asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                     : "={m0}"(m0_out) : "v"(off), "s"(base), "s"(lds) : "memory");
+    else if constexpr (V == 16)
         asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                      : "={m0}"(m0_out) : "v"(off), "s"(base), "s"(lds) : "memory");
     else

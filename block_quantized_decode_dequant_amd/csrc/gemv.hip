@@ -723,9 +723,9 @@ template <class Tr, int VEC>
 __device__ __forceinline__ void copy_slice(const uint8_t *W, uint32_t base, uint32_t lim, uint32_t dst, int lane) {
     using P = Plan<Tr, VEC>;
 #pragma unroll
-    for (int k = 0; k < P::kFull; ++k) dma<VEC>(W, min(base + uint32_t(k * P::kPer), lim), dst + k * P::kPer);
+    for (int k = 0; k < P::kFull; ++k) dma<VEC, true>(W, min(base + uint32_t(k * P::kPer), lim), dst + k * P::kPer);
     if constexpr (P::kRem > 0) {
-        if (lane < P::kRem / VEC) dma<VEC>(W, min(base + uint32_t(P::kFull * P::kPer), lim), dst + P::kFull * P::kPer);
+        if (lane < P::kRem / VEC) dma<VEC, true>(W, min(base + uint32_t(P::kFull * P::kPer), lim), dst + P::kFull * P::kPer);
     }
 }
 
