@@ -121,7 +121,10 @@ typedef const __attribute__((address_space(1))) void gbl_void;
 // "wait for every outstanding load" before unrelated LDS reads; every read
 // of a ring stage is preceded by an explicit s_waitcnt on the loads that fill
 // it.  The "memory" clobber keeps the copies ordered against other memory
-// operations in program order.
+// operations in program order.  NT (16-byte copies): the non-temporal cache
+// policy, for data read once per token (weights, K/V rows), so the lines it
+// brings in do not push out the activations and outputs that the next
+// kernels read again.
 template <int V, bool NT = false>
 __device__ __forceinline__ void dma(const uint8_t *base, uint32_t off, uint32_t lds) {
     int m0_out;   // M0 is declared written (an output), so no value of the compiler's lives in it across the copy
