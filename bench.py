@@ -33,7 +33,6 @@ none|8b|70b|all, --stream-tokens T, --file-layers F, --file-dir D.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -45,7 +44,6 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 METRIC = "achieved HBM GB/s of dequant-GEMV and batch-1 decode tok/s (% of roofline)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_traffic.json")
-GEMV_SRC = os.path.join(ROOT, "block_quantized_decode_dequant_amd", "csrc", "gemv.hip")
 
 
 def parse():
@@ -71,7 +69,10 @@ def gemv_bytes(qtype: int, rows: int, cols: int, nt) -> int:
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(GEMV_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the GEMV kernel sources (gemv.hip and the helpers it uses), the
+    key under which the committed traffic counters were taken."""
+    from block_quantized_decode_dequant_amd import profsum
+    return profsum.gemv_source_hash()
 
 
 def load_traffic(kernel: str):

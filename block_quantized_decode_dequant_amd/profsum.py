@@ -22,7 +22,17 @@ import os
 import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-GEMV_SRC = os.path.join(HERE, "csrc", "gemv.hip")
+# the GEMV kernels' sources: the kernel file and the copy and wait helpers it uses
+GEMV_SRCS = [os.path.join(HERE, "csrc", "gemv.hip"), os.path.join(HERE, "csrc", "device_util.h")]
+
+
+def gemv_source_hash() -> str:
+    """First 16 hex digits of the SHA-256 of the GEMV kernel sources, in order."""
+    h = hashlib.sha256()
+    for path in GEMV_SRCS:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 FMT = {"F80": "q8_0", "F40": "q4_0", "F4K": "q4_k", "F5K": "q5_k", "F6K": "q6_k"}
 
@@ -135,7 +145,7 @@ def cmd_traffic(a):
         per_launch[key] = round(kib * 1024 * scale_f + wkib * 1024 * scale_w)
         detail[key] = {"dispatches": n, "fetch_kib_raw": round(kib, 1), "write_kib_raw": round(wkib, 1),
                        "fetch_bytes": round(kib * 1024 * scale_f), "write_bytes": round(wkib * 1024 * scale_w)}
-    rec = {"gemv_source_sha256_16": hashlib.sha256(open(GEMV_SRC, "rb").read()).hexdigest()[:16],
+    rec = {"gemv_source_sha256_16": gemv_source_hash(),
            "calibration": {"kernel": "copy_kernel", "bytes_each_way": a.cal_bytes,
                            "fetch_kib_raw": round(kib_f, 1), "write_kib_raw": round(kib_w, 1),
                            "fetch_scale": round(scale_f, 4), "write_scale": round(scale_w, 4)},
