@@ -41,7 +41,9 @@
 //    lie together in memory.
 //  * one workgroup of eight waves per CU; the waves of a workgroup split the
 //    rows and, where that leaves too few workgroups, the columns, whose sums
-//    meet in LDS at the end.
+//    meet in LDS at the end.  Where all eight waves work on one column range
+//    (and LDS allows: the one-tile K-quants), they share each step's
+//    activation record through a ring in LDS instead of each loading it.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
@@ -397,6 +399,15 @@ struct Geo {
     static constexpr int LDS = NW * WAVE;
     static constexpr int REC = 8192 + (F::kMin ? 512 : 0) + 32;  // activation record of one step
     static_assert(LDS <= 160 * 1024, "LDS of one workgroup per CU");
+    // shared records (all waves of a workgroup on one column range): a ring of
+    // R records after the weight rings, then 2R step counters and one 16-byte
+    // slot per wave for the placeholder copies (fits for Q5_K and Q6_K)
+    static constexpr int R = 7;
+    static constexpr int RING_REC = LDS;                         // offset of the record ring
+    static constexpr int CNT = LDS + R * REC;                    // offset of the counters
+    static constexpr int SLOT = CNT + 64;                        // offset of the placeholder slots
+    static constexpr int LDS_SH = SLOT + 16 * NW;
+    static constexpr bool kShare = LDS_SH <= 160 * 1024;
 };
 
 // Activation records, one workgroup per 256-column step s.  Record layout
@@ -469,6 +480,10 @@ __global__ void __launch_bounds__(256) bgemm_prep(const float *__restrict__ X, i
 
 __device__ __forceinline__ void wait_vm(int n) {
     switch (n) {
+    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6)); break;
+    case 7: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7)); break;
     case 13: __builtin_amdgcn_s_waitcnt(vmcnt_imm(13)); break;
     case 14: __builtin_amdgcn_s_waitcnt(vmcnt_imm(14)); break;
     case 15: __builtin_amdgcn_s_waitcnt(vmcnt_imm(15)); break;
@@ -476,6 +491,23 @@ __device__ __forceinline__ void wait_vm(int n) {
     default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;   // n = 0 (other counts do not occur)
     }
     __builtin_amdgcn_sched_barrier(0);
+}
+
+// Step counters of the shared record ring, in LDS: plain workgroup-scope
+// atomics (no implied waits: the copies they report on were waited for
+// explicitly), one count per wave (lane 0 adds it).  A wait polls with a
+// sleep between reads and gives up after about 2^20 polls (far beyond any
+// real wait), so every wave always ends.
+__device__ __forceinline__ void lds_count(uint32_t *p) {
+    if (__lane_id() == 0) __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_wait_count(uint32_t *p, uint32_t target) {
+    for (int spin = 0; spin < (1 << 20); ++spin) {
+        if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
 }
 
 // One step's activations in registers: the 16 MFMA A operands (from the
@@ -512,8 +544,9 @@ __device__ __forceinline__ void load_x(const uint8_t *__restrict__ rec, int s, i
 // record's scale.  At the end the nc splits of a row group add their sums
 // through LDS in split order, and the first wave of the group writes them to
 // Y (one split between workgroups) or to partial[y][n][row], which
-// bgemm_reduce adds in workgroup order.
-template <class F>
+// bgemm_reduce adds in workgroup order.  SHARE (nc = 1 only): the records
+// come through a workgroup ring in LDS instead (below).
+template <class F, bool SHARE>
 __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__restrict__ W, int64_t row_bytes, int rows,
                                                           int nsteps, int nblk, const uint8_t *__restrict__ rec,
                                                           int nc, int sps, float *__restrict__ Y, int k, int accumulate,
@@ -529,12 +562,20 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
     f4 acc[T];
 #pragma unroll
     for (int u = 0; u < T; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
-    if (T0 < rows && n > 0) {
+    uint32_t *const cnt = reinterpret_cast<uint32_t *>(lds + G::CNT);   // SHARE: arrived[R], done[R]
+    if constexpr (SHARE) {
+        if (threadIdx.x < 2 * G::R) cnt[threadIdx.x] = 0u;
+        __syncthreads();
+    }
+    // SHARE: every wave takes part in the record ring, including waves past
+    // the last row, which copy and compute on the last rows (never stored)
+    if ((SHARE || T0 < rows) && n > 0) {
         const int64_t last = rows - 1;
+        const int64_t T0c = min<int64_t>(T0, last);                  // copy origin (T0 unless past the rows)
         // copies read whole 16-byte granules; none starts past the one that
         // holds the matrix's last byte (W is 16-byte aligned)
         const int64_t last_granule = (int64_t(rows) * row_bytes - 1) & ~int64_t(15);
-        const int64_t base_rel = (T0 * row_bytes) & ~int64_t(15);
+        const int64_t base_rel = (T0c * row_bytes) & ~int64_t(15);
         const uint8_t *const wbase = W + base_rel;                         // this wave's copy base (uniform)
         uint8_t *const ring = lds + wv * G::WAVE;
         // this lane's part of a tile copy: instruction i fills LDS bytes
@@ -550,7 +591,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
             const int P = 1024 * i + 16 * lane, q = min(P / G::Lp, 15);
             const int w = P - q * G::Lp;
 #pragma unroll
-            for (int u = 0; u < T; ++u) crel[u][i] = uint32_t(min(T0 + 16 * u + q, last) * row_bytes - base_rel) + uint32_t(w);
+            for (int u = 0; u < T; ++u) crel[u][i] = uint32_t(min(T0c + 16 * u + q, last) * row_bytes - base_rel) + uint32_t(w);
         }
         const uint32_t lim = uint32_t(min<int64_t>(last_granule - base_rel, 0xfffffff0));
         const auto issue_w = [&](int b, int s) {
@@ -564,7 +605,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
         };
         uint32_t rlo[T];                                                   // low bits of this lane's row starts
 #pragma unroll
-        for (int u = 0; u < T; ++u) rlo[u] = uint32_t(min(T0 + 16 * u + r, last) * row_bytes);
+        for (int u = 0; u < T; ++u) rlo[u] = uint32_t(min(T0c + 16 * u + r, last) * row_bytes);
 
         const auto compute = [&](int t, const XRegs &xr) {
             const int s = s_lo + t;
@@ -588,10 +629,71 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
             }
         };
 
+        constexpr int kW = T * G::NI;
+        if constexpr (SHARE) {
+            // The workgroup's waves share one record per step through a ring of R
+            // = 7 LDS records: wave w copies bytes [1024 w, 1024 w + 1024) of it,
+            // wave 0 also the sums and scales after 8192 (the others a 16-byte
+            // placeholder, so every wave issues two copies per record), four
+            // steps ahead.  Issue order: records 0, 1, 2, weights 0, record 3,
+            // weights 1, then per step t record t + 4 and weights t + 2, so at step
+            // t, with only weights t + 1 still allowed in flight, this wave's
+            // weights t and its pieces of record t + 3 have landed.  arrived[b]
+            // counts the waves whose pieces of the record in slot b have landed
+            // (each reports record t + 3 at step t), done[b] those that have read
+            // it: a wave reads record t once all eight have reported it, and copies
+            // record t + 4 into its slot once all have read record t - 3.  The
+            // slowest wave never waits (every other wave has reported and read
+            // those), so every wait ends, and the waves may drift three steps apart.
+            constexpr int kAhead = 4, kReport = 3;
+            static_assert(G::R == kAhead + kReport, "ring of records in flight and being read");
+            const auto issue_rec = [&](int j) {
+                const uint8_t *const rb = rec + int64_t(s_lo + j) * G::REC;
+                const uint32_t dst = lds_addr(lds + G::RING_REC + (j % G::R) * G::REC);
+                dma<16>(rb, uint32_t(1024 * wv + 16 * lane), dst + 1024 * wv);
+                if (wv == 0) {
+                    if (lane < (G::REC - 8192) / 16) dma<16>(rb, uint32_t(8192 + 16 * lane), dst + 8192);
+                } else if (lane == 0) {
+                    dma<16>(rb, 0u, lds_addr(lds + G::SLOT + 16 * wv));
+                }
+            };
+            for (int j = 0; j < kAhead - 1 && j < n; ++j) issue_rec(j);
+            issue_w(0, s_lo);
+            if (kAhead - 1 < n) issue_rec(kAhead - 1);
+            if (n > 1) issue_w(1, s_lo + 1);
+            // the two waves of a SIMD (w, w + 4) take turns at the higher issue
+            // priority, one step each, so they advance at the same pace and
+            // neither waits long for the other at the counters
+            const bool first_slot = wv < 4;
+            for (int t = 0; t < n; ++t) {
+                const int b = t % G::R;
+                if (first_slot == ((t & 1) == 0)) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
+                wait_vm(t + 1 < n ? kW : 0);                      // weights t, pieces of record t + 3 landed
+                for (int j = t == 0 ? 0 : t + kReport; j <= t + kReport && j < n; ++j) lds_count(&cnt[j % G::R]);
+                lds_wait_count(&cnt[b], 8u * uint32_t(t / G::R + 1));
+                const uint8_t *const rc = lds + G::RING_REC + b * G::REC;
+                XRegs xr;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) xr.x[q] = *reinterpret_cast<const u32x4a *>(rc + (q * 64 + lane) * 16);
+                if constexpr (F::kMin) xr.m = *reinterpret_cast<const u32x2 *>(rc + 8192 + lane * 8);
+                xr.up = *reinterpret_cast<const f4 *>(rc + G::REC - 32 + 16 * (g & 1));
+                __builtin_amdgcn_s_waitcnt(kLgkm0);
+                __builtin_amdgcn_sched_barrier(0);
+                lds_count(&cnt[G::R + b]);
+                if (t + kAhead < n) {
+                    const int j = t + kAhead;
+                    if (j >= G::R) lds_wait_count(&cnt[G::R + j % G::R], 8u * uint32_t(j / G::R));
+                    issue_rec(j);
+                }
+                if (t + 2 < n) issue_w((t + 2) % G::S, s_lo + t + 2);
+                compute(t, xr);
+            }
+            __builtin_amdgcn_s_setprio(0);
+        } else {
         // per step: activations (8 + kMin + 1 loads), then T NI weight copies;
         // both are issued two steps ahead, so step t's are in once at most those
         // of step t + 1 are outstanding
-        constexpr int kX = 9 + (F::kMin ? 1 : 0), kW = T * G::NI;
+        constexpr int kX = 9 + (F::kMin ? 1 : 0);
         XRegs x0, x1, x2;
         const auto step = [&](int t, const XRegs &cur, XRegs &ahead) {
             wait_vm(t + 1 < n ? kX + kW : 0);
@@ -613,6 +715,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
             step(t + 1, x1, x0);
             if (t + 2 >= n) break;
             step(t + 2, x2, x1);
+        }
         }
     }
     if (nc > 1) {
@@ -687,8 +790,11 @@ BgemmShape bgemm_shape(int64_t rows, int64_t cols) {
             if ((ns + sps - 1) / sps != total) continue;   // some split would have no step
             const int64_t groups = (tiles + G::NW / nc - 1) / (G::NW / nc);
             const int64_t rounds = (groups * sp + kNumCUs - 1) / kNumCUs;
-            const int64_t cost = 20 * rounds * (sps + G::S - 1) + (sp > 1 ? kReduceCost : 0) +
-                                 rounds * sps * (nc - 1);
+            // shared records (one column range per workgroup, where LDS allows):
+            // a fifth less per step than records loaded by every wave
+            const bool shared = G::kShare && nc == 1;
+            const int64_t cost = (shared ? 16 : 20) * rounds * (sps + G::S - 1) + (sp > 1 ? kReduceCost : 0) +
+                                 (shared ? 0 : rounds * sps * (nc - 1));
             if (best < 0 || cost < best) {
                 best = cost;
                 b.groups = int(groups);
@@ -716,22 +822,37 @@ hipError_t run_bgemm(const void *W, int64_t row_bytes, int64_t rows, int64_t col
     const BgemmShape b = bgemm_shape<F>(rows, cols);
     uint8_t *const rec = static_cast<uint8_t *>(ws);
     float *const partial = reinterpret_cast<float *>(rec + int64_t(ns) * G::REC);
-    // more than 64 KB of dynamic LDS: allowed once per device
+    // more than 64 KB of dynamic LDS: allowed once per device for each variant
     static std::atomic<uint64_t> done{0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
     if (!((done.load(std::memory_order_acquire) >> dev) & 1)) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&bgemm<F>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&bgemm<F, false>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
+        if constexpr (G::kShare) {
+            if (e == hipSuccess)
+                e = hipFuncSetAttribute(reinterpret_cast<const void *>(&bgemm<F, true>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_SH);
+        }
         if (e != hipSuccess) return e;
         done.fetch_or(uint64_t(1) << dev, std::memory_order_release);
     }
     hipLaunchKernelGGL(bgemm_prep<F>, dim3(unsigned(ns)), dim3(256), 0, st, X, cols, k, rec);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bgemm<F>, dim3(unsigned(b.groups), unsigned(b.nsplit)), dim3(64 * G::NW), G::LDS, st,
-                       static_cast<const uint8_t *>(W), row_bytes, int(rows), ns, int(nblk), rec, b.nc, b.sps, Y, k,
-                       accumulate, partial);
+    const dim3 grid(unsigned(b.groups), unsigned(b.nsplit));
+    const uint8_t *const w8 = static_cast<const uint8_t *>(W);
+    bool shared = false;
+    if constexpr (G::kShare) {
+        if (b.nc == 1) {
+            shared = true;
+            hipLaunchKernelGGL((bgemm<F, true>), grid, dim3(64 * G::NW), G::LDS_SH, st, w8, row_bytes, int(rows), ns,
+                               int(nblk), rec, b.nc, b.sps, Y, k, accumulate, partial);
+        }
+    }
+    if (!shared)
+        hipLaunchKernelGGL((bgemm<F, false>), grid, dim3(64 * G::NW), G::LDS, st, w8, row_bytes, int(rows), ns,
+                           int(nblk), rec, b.nc, b.sps, Y, k, accumulate, partial);
     if ((e = hipGetLastError()) != hipSuccess || b.nsplit == 1) return e;
     const int64_t nt2 = int64_t(k) * rows;
     hipLaunchKernelGGL(bgemm_reduce, dim3(unsigned((nt2 + 255) / 256)), dim3(256), 0, st, partial, b.nsplit, k,
