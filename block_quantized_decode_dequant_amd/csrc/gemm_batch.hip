@@ -194,6 +194,13 @@ struct BQ4K {
     }
 };
 
+// Q4_K with one 16-row tile per wave: the same operands, for launches whose
+// waves share the activation records (the one-tile weight rings leave LDS
+// room for the record ring).
+struct BQ4K1 : BQ4K {
+    static constexpr int kTiles = 1;
+};
+
 // ---- Q4_0: a step is 8 blocks of 18 bytes; lane group g takes code bytes
 // 4g..4g+3 of a block: MFMA 2bb holds their low nibbles (values
 // 4g + perm4(i)), MFMA 2bb + 1 their high nibbles (16 + 4g + perm4(i)).
@@ -765,6 +772,7 @@ __global__ void __launch_bounds__(256) bgemm_reduce(const float *__restrict__ pa
 
 struct BgemmShape {
     int groups, nc, nsplit, sps;
+    int64_t cost;
 };
 
 // Launch shape: one workgroup of NW waves per CU.  The columns are split
@@ -777,9 +785,10 @@ struct BgemmShape {
 // reads nc records per step instead of one.  Costs in twentieths of a
 // step; ties go to fewer splits.
 template <class F>
-BgemmShape bgemm_shape(int64_t rows, int64_t cols) {
+BgemmShape bgemm_shape(int64_t rows, int64_t cols, bool shared_only = false) {
     using G = Geo<F>;
-    constexpr int kReduceCost = 60;   // the third kernel: three steps of one wave
+    constexpr int kReduceCost = 60;   // the third kernel: about three one-tile steps of one wave
+    shared_only = shared_only || std::is_same<F, BQ4K1>::value;   // the one-tile Q4_K is for shared records only
     BgemmShape b{};
     const int ns = int((cols + 255) / 256);
     const int64_t tiles = (rows + 16 * G::T - 1) / (16 * G::T);
@@ -791,16 +800,19 @@ BgemmShape bgemm_shape(int64_t rows, int64_t cols) {
             const int64_t groups = (tiles + G::NW / nc - 1) / (G::NW / nc);
             const int64_t rounds = (groups * sp + kNumCUs - 1) / kNumCUs;
             // shared records (one column range per workgroup, where LDS allows):
-            // a fifth less per step than records loaded by every wave
+            // a fifth less per step than records loaded by every wave; a step
+            // costs in proportion to the tiles it covers
             const bool shared = G::kShare && nc == 1;
-            const int64_t cost = (shared ? 16 : 20) * rounds * (sps + G::S - 1) + (sp > 1 ? kReduceCost : 0) +
-                                 (shared ? 0 : rounds * sps * (nc - 1));
+            if (shared_only && !shared) continue;
+            const int64_t cost = (shared ? 16 : 20) * G::T * rounds * (sps + G::S - 1) +
+                                 (sp > 1 ? kReduceCost : 0) + (shared ? 0 : G::T * rounds * sps * (nc - 1));
             if (best < 0 || cost < best) {
                 best = cost;
                 b.groups = int(groups);
                 b.nc = nc;
                 b.nsplit = sp;
                 b.sps = sps;
+                b.cost = cost;
             }
         }
     }
@@ -866,12 +878,22 @@ bool gemm_batch_type_ok(nt_qtype t) {
     return t == NT_Q8_0 || t == NT_Q4_0 || t == NT_Q4_K || t == NT_Q5_K || t == NT_Q6_K;
 }
 
+// Q4_K: two tiles per wave with per-wave records, or one tile per wave with
+// records shared through LDS where that needs no split between workgroups and
+// its launch shape costs less (measured at k = 8: 28672 x 8192 49.6 -> 47.7
+// us one-tile; 8192 x 8192, where the one-tile shape needs a four-way split
+// and the third kernel, 20.3 -> 21.2 us, so two-tile).
+bool q4k_one_tile(int64_t rows, int64_t cols) {
+    const BgemmShape two = bgemm_shape<BQ4K>(rows, cols), one = bgemm_shape<BQ4K1>(rows, cols, true);
+    return one.groups > 0 && one.nsplit == 1 && one.cost < two.cost;
+}
+
 size_t gemm_batch_workspace_bytes(nt_qtype t, int64_t rows, int64_t cols) {
     switch (t) {
     case NT_Q8_0: return workspace_for<BQ80>(rows, cols);
     case NT_Q4_0: return workspace_for<BQ40>(rows, cols);
     case NT_Q5_K: return workspace_for<BQ5K>(rows, cols);
-    case NT_Q4_K: return workspace_for<BQ4K>(rows, cols);
+    case NT_Q4_K: return q4k_one_tile(rows, cols) ? workspace_for<BQ4K1>(rows, cols) : workspace_for<BQ4K>(rows, cols);
     case NT_Q6_K: return workspace_for<BQ6K>(rows, cols);
     default: return 0;
     }
@@ -885,7 +907,9 @@ hipError_t launch_gemm_batch(nt_qtype t, const void *W, int64_t rows, int64_t co
     case NT_Q8_0: return run_bgemm<BQ80>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);
     case NT_Q4_0: return run_bgemm<BQ40>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);
     case NT_Q5_K: return run_bgemm<BQ5K>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);
-    case NT_Q4_K: return run_bgemm<BQ4K>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);
+    case NT_Q4_K:
+        if (q4k_one_tile(rows, cols)) return run_bgemm<BQ4K1>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);
+        return run_bgemm<BQ4K>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);
     case NT_Q6_K: return run_bgemm<BQ6K>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);
     default: return hipErrorInvalidValue;
     }
