@@ -684,15 +684,16 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
                 for (int q = 0; q < 8; ++q) xr.x[q] = *reinterpret_cast<const u32x4a *>(rc + (q * 64 + lane) * 16);
                 if constexpr (F::kMin) xr.m = *reinterpret_cast<const u32x2 *>(rc + 8192 + lane * 8);
                 xr.up = *reinterpret_cast<const f4 *>(rc + G::REC - 32 + 16 * (g & 1));
-                __builtin_amdgcn_s_waitcnt(kLgkm0);
-                __builtin_amdgcn_sched_barrier(0);
-                lds_count(&cnt[G::R + b]);
+                // the next copies go out while those reads are in flight
                 if (t + kAhead < n) {
                     const int j = t + kAhead;
                     if (j >= G::R) lds_wait_count(&cnt[G::R + j % G::R], 8u * uint32_t(j / G::R));
                     issue_rec(j);
                 }
                 if (t + 2 < n) issue_w((t + 2) % G::S, s_lo + t + 2);
+                __builtin_amdgcn_s_waitcnt(kLgkm0);               // record t is in registers
+                __builtin_amdgcn_sched_barrier(0);
+                lds_count(&cnt[G::R + b]);
                 compute(t, xr);
             }
             __builtin_amdgcn_s_setprio(0);
