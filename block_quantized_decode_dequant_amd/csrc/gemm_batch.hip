@@ -508,10 +508,17 @@ __device__ __forceinline__ void wait_vm(int n) {
 __device__ __forceinline__ void lds_count(uint32_t *p) {
     if (__lane_id() == 0) __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void lds_wait_count(uint32_t *p, uint32_t target) {
-    for (int spin = 0; spin < (1 << 20); ++spin) {
-        if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
-        __builtin_amdgcn_s_sleep(1);
+__device__ __forceinline__ uint32_t lds_read_count(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// seen: a value of *p read earlier (counts only grow), so a wait whose
+// target was already reached then costs no further read
+__device__ __forceinline__ void lds_wait_count(uint32_t *p, uint32_t target, uint32_t seen = 0) {
+    if (seen < target) {
+        for (int spin = 0; spin < (1 << 20); ++spin) {
+            if (lds_read_count(p) >= target) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
@@ -673,11 +680,14 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
             // neither waits long for the other at the counters
             const bool first_slot = wv < 4;
             for (int t = 0; t < n; ++t) {
-                const int b = t % G::R;
+                const int b = t % G::R, jn = t + kAhead;
                 if (first_slot == ((t & 1) == 0)) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
+                // both counters this step waits on, read before the weight wait
+                const uint32_t arrived0 = lds_read_count(&cnt[b]);
+                const uint32_t done0 = lds_read_count(&cnt[G::R + jn % G::R]);
                 wait_vm(t + 1 < n ? kW : 0);                      // weights t, pieces of record t + 3 landed
                 for (int j = t == 0 ? 0 : t + kReport; j <= t + kReport && j < n; ++j) lds_count(&cnt[j % G::R]);
-                lds_wait_count(&cnt[b], 8u * uint32_t(t / G::R + 1));
+                lds_wait_count(&cnt[b], 8u * uint32_t(t / G::R + 1), arrived0);
                 const uint8_t *const rc = lds + G::RING_REC + b * G::REC;
                 XRegs xr;
 #pragma unroll
@@ -685,10 +695,9 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
                 if constexpr (F::kMin) xr.m = *reinterpret_cast<const u32x2 *>(rc + 8192 + lane * 8);
                 xr.up = *reinterpret_cast<const f4 *>(rc + G::REC - 32 + 16 * (g & 1));
                 // the next copies go out while those reads are in flight
-                if (t + kAhead < n) {
-                    const int j = t + kAhead;
-                    if (j >= G::R) lds_wait_count(&cnt[G::R + j % G::R], 8u * uint32_t(j / G::R));
-                    issue_rec(j);
+                if (jn < n) {
+                    if (jn >= G::R) lds_wait_count(&cnt[G::R + jn % G::R], 8u * uint32_t(jn / G::R), done0);
+                    issue_rec(jn);
                 }
                 if (t + 2 < n) issue_w((t + 2) % G::S, s_lo + t + 2);
                 __builtin_amdgcn_s_waitcnt(kLgkm0);               // record t is in registers
