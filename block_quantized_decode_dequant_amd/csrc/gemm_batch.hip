@@ -431,10 +431,14 @@ struct Geo {
 // that the main kernel undoes on the step's fp32 sums.
 template <class F>
 __global__ void __launch_bounds__(256) bgemm_prep(const float *__restrict__ X, int64_t cols, int k,
-                                                  uint8_t *__restrict__ rec) {
+                                                  uint8_t *__restrict__ rec, uint32_t *__restrict__ tickets,
+                                                  int ntickets) {
     using G = Geo<F>;
     __shared__ __attribute__((aligned(16))) float xs[8][260];
     const int s = blockIdx.x, t = threadIdx.x;
+    // the main kernel's per-row-group tickets start each call at zero
+    for (int i = s * 256 + t; i < ntickets; i += gridDim.x * 256)
+        __hip_atomic_store(tickets + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint8_t *const out = rec + int64_t(s) * G::REC;
     {
         const int n = t >> 5, c = 8 * (t & 31);
@@ -557,14 +561,15 @@ __device__ __forceinline__ void load_x(const uint8_t *__restrict__ rec, int s, i
 // operands from LDS, computes each tile's sums for the step and undoes the
 // record's scale.  At the end the nc splits of a row group add their sums
 // through LDS in split order, and the first wave of the group writes them to
-// Y (one split between workgroups) or to partial[y][n][row], which
-// bgemm_reduce adds in workgroup order.  SHARE (nc = 1 only): the records
-// come through a workgroup ring in LDS instead (below).
-template <class F, bool SHARE>
+// Y, or (SPLIT: the columns also split between workgroups) to
+// partial[y][n][row], where the last of the nsplit waves that cover the same
+// rows adds them in workgroup order (below).  SHARE (nc = 1 only): the
+// records come through a workgroup ring in LDS instead (below).
+template <class F, bool SHARE, bool SPLIT>
 __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__restrict__ W, int64_t row_bytes, int rows,
                                                           int nsteps, int nblk, const uint8_t *__restrict__ rec,
                                                           int nc, int sps, float *__restrict__ Y, int k, int accumulate,
-                                                          float *__restrict__ partial) {
+                                                          float *__restrict__ partial, uint32_t *__restrict__ tickets) {
     using G = Geo<F>;
     constexpr int T = G::T;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -759,8 +764,9 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
             const int nn = 4 * g + i;
             const float o = acc[u][i] + __shfl_down(acc[u][i], 32, 64);
             if (g < 2 && nn < k && R < rows) {
-                if (gridDim.y > 1) {
-                    partial[(int64_t(blockIdx.y) * k + nn) * rows + R] = o;
+                if constexpr (SPLIT) {
+                    __hip_atomic_store(partial + (int64_t(blockIdx.y) * k + nn) * rows + R, o, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
                 } else {
                     float *py = Y + nn * int64_t(rows) + R;
                     *py = accumulate ? *py + o : o;
@@ -768,16 +774,52 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
             }
         }
     }
-}
-
-// Y[n][r] (+)= sum over splits, in split order, of partial[split][n][r].
-__global__ void __launch_bounds__(256) bgemm_reduce(const float *__restrict__ partial, int nsplit, int k, int rows,
-                                                    float *__restrict__ Y, int accumulate) {
-    const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (t >= int64_t(k) * rows) return;
-    float v = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) v += partial[int64_t(sp) * k * rows + t];
-    Y[t] = accumulate ? Y[t] + v : v;
+    if constexpr (SPLIT) {
+        // Columns split between workgroups: the partial sums above are
+        // agent-scope stores (written through to the level every XCD reads,
+        // not left dirty in this XCD's L2).  Once they have completed, the
+        // wave takes a ticket for its rows; the wave that draws the last of
+        // the nsplit adds the rows' partial sums in split order (agent-scope
+        // loads) and writes Y.  Nothing waits on another wave.
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        uint32_t tk = 0;
+        if (lane == 0)
+            tk = __hip_atomic_fetch_add(tickets + int64_t(blockIdx.x) * nr + wv / nc, 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+        if (__builtin_amdgcn_readfirstlane(tk) != gridDim.y - 1) return;
+        // 2T outputs per lane (output i = lane + 64 j is n = i / 16T, row T0
+        // + i mod 16T), four splits at a time: 8T loads in flight before the
+        // first add.  A split past the last reloads the last one and adds +0
+        // instead, which leaves every sum as it is (sums start at +0);
+        // outputs past k or the last row load a valid one and store nothing.
+        const int nrow = int(min<int64_t>(rows - T0, 16 * T)), ns = int(gridDim.y);
+        float v[2 * T];
+        int64_t o[2 * T];
+#pragma unroll
+        for (int j = 0; j < 2 * T; ++j) {
+            const int i = lane + 64 * j, nn = i / (16 * T), rr = i % (16 * T);
+            o[j] = int64_t(min(nn, k - 1)) * rows + T0 + min(rr, nrow - 1);
+            v[j] = 0.f;
+        }
+        for (int sp0 = 0; sp0 < ns; sp0 += 4) {
+            float p[4][2 * T];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int j = 0; j < 2 * T; ++j)
+                    p[q][j] = __hip_atomic_load(partial + int64_t(min(sp0 + q, ns - 1)) * k * rows + o[j],
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int j = 0; j < 2 * T; ++j) v[j] += sp0 + q < ns ? p[q][j] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 2 * T; ++j) {
+            const int i = lane + 64 * j, nn = i / (16 * T), rr = i % (16 * T);
+            if (nn < k && rr < nrow) Y[o[j]] = accumulate ? Y[o[j]] + v[j] : v[j];
+        }
+    }
 }
 
 struct BgemmShape {
@@ -787,17 +829,17 @@ struct BgemmShape {
 
 // Launch shape: one workgroup of NW waves per CU.  The columns are split
 // nc ways between the waves of a workgroup (their sums meet in LDS) and/or
-// nsplit ways between workgroups (partial sums through the workspace and a
-// third kernel).  The choice minimises (rounds of workgroups over the CUs) x
-// (steps per wave + the ring's fill), plus a few steps for the third kernel,
-// plus a term for the activation records: waves of one column split read the
-// same record at the same step (served once by the CU's cache), so a CU
-// reads nc records per step instead of one.  Costs in twentieths of a
-// step; ties go to fewer splits.
+// nsplit ways between workgroups (partial sums through the workspace, added
+// by the last wave to finish).  The choice minimises (rounds of workgroups
+// over the CUs) x (steps per wave + the ring's fill), plus a few steps for
+// the cross-workgroup sum, plus a term for the activation records: waves of
+// one column split read the same record at the same step (served once by
+// the CU's cache), so a CU reads nc records per step instead of one.  Costs
+// in twentieths of a step; ties go to fewer splits.
 template <class F>
 BgemmShape bgemm_shape(int64_t rows, int64_t cols, bool shared_only = false) {
     using G = Geo<F>;
-    constexpr int kReduceCost = 60;   // the third kernel: about three one-tile steps of one wave
+    constexpr int kReduceCost = 60;   // the cross-workgroup sum: about three one-tile steps of one wave
     shared_only = shared_only || std::is_same<F, BQ4K1>::value;   // the one-tile Q4_K is for shared records only
     BgemmShape b{};
     const int ns = int((cols + 255) / 256);
@@ -833,7 +875,19 @@ template <class F>
 size_t workspace_for(int64_t rows, int64_t cols) {
     const BgemmShape b = bgemm_shape<F>(rows, cols);
     const int64_t ns = (cols + 255) / 256;
-    return size_t(ns) * Geo<F>::REC + (b.nsplit > 1 ? size_t(b.nsplit) * 8 * size_t(rows) * 4 : 0);
+    return size_t(ns) * Geo<F>::REC + (b.nsplit > 1 ? size_t(b.nsplit) * 8 * size_t(rows) * 4 + size_t(b.groups) * Geo<F>::NW * 4 : 0);
+}
+
+// The main kernel in one of its four forms (shared records or not; columns
+// split between workgroups or not).
+template <class F, bool SHARE, bool SPLIT>
+hipError_t launch_main(dim3 grid, hipStream_t st, const uint8_t *W, int64_t row_bytes, int64_t rows, int ns,
+                       int64_t nblk, const uint8_t *rec, const BgemmShape &b, float *Y, int k, int accumulate,
+                       float *partial, uint32_t *tickets) {
+    using G = Geo<F>;
+    hipLaunchKernelGGL((bgemm<F, SHARE, SPLIT>), grid, dim3(64 * G::NW), SHARE ? G::LDS_SH : G::LDS, st, W, row_bytes,
+                       int(rows), ns, int(nblk), rec, b.nc, b.sps, Y, k, accumulate, partial, tickets);
+    return hipGetLastError();
 }
 
 template <class F>
@@ -842,44 +896,44 @@ hipError_t run_bgemm(const void *W, int64_t row_bytes, int64_t rows, int64_t col
     using G = Geo<F>;
     const int ns = int((cols + 255) / 256);
     const BgemmShape b = bgemm_shape<F>(rows, cols);
+    const bool split = b.nsplit > 1;
     uint8_t *const rec = static_cast<uint8_t *>(ws);
     float *const partial = reinterpret_cast<float *>(rec + int64_t(ns) * G::REC);
-    // more than 64 KB of dynamic LDS: allowed once per device for each variant
+    uint32_t *const tickets = reinterpret_cast<uint32_t *>(partial + (split ? int64_t(b.nsplit) * 8 * rows : 0));
+    const int ntickets = split ? b.groups * (G::NW / b.nc) : 0;   // one per wave's rows of a workgroup column
+    // more than 64 KB of dynamic LDS: allowed once per device for each form
     static std::atomic<uint64_t> done{0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
     if (!((done.load(std::memory_order_acquire) >> dev) & 1)) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&bgemm<F, false>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
+        const auto allow = [](const void *fn, int bytes) {
+            return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        };
+        hipError_t e = allow(reinterpret_cast<const void *>(&bgemm<F, false, false>), G::LDS);
+        if (e == hipSuccess) e = allow(reinterpret_cast<const void *>(&bgemm<F, false, true>), G::LDS);
         if constexpr (G::kShare) {
-            if (e == hipSuccess)
-                e = hipFuncSetAttribute(reinterpret_cast<const void *>(&bgemm<F, true>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_SH);
+            if (e == hipSuccess) e = allow(reinterpret_cast<const void *>(&bgemm<F, true, false>), G::LDS_SH);
+            if (e == hipSuccess) e = allow(reinterpret_cast<const void *>(&bgemm<F, true, true>), G::LDS_SH);
         }
         if (e != hipSuccess) return e;
         done.fetch_or(uint64_t(1) << dev, std::memory_order_release);
     }
-    hipLaunchKernelGGL(bgemm_prep<F>, dim3(unsigned(ns)), dim3(256), 0, st, X, cols, k, rec);
+    hipLaunchKernelGGL(bgemm_prep<F>, dim3(unsigned(ns)), dim3(256), 0, st, X, cols, k, rec, tickets, ntickets);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 grid(unsigned(b.groups), unsigned(b.nsplit));
     const uint8_t *const w8 = static_cast<const uint8_t *>(W);
-    bool shared = false;
     if constexpr (G::kShare) {
-        if (b.nc == 1) {
-            shared = true;
-            hipLaunchKernelGGL((bgemm<F, true>), grid, dim3(64 * G::NW), G::LDS_SH, st, w8, row_bytes, int(rows), ns,
-                               int(nblk), rec, b.nc, b.sps, Y, k, accumulate, partial);
-        }
+        if (b.nc == 1)
+            return split ? launch_main<F, true, true>(grid, st, w8, row_bytes, rows, ns, nblk, rec, b, Y, k, accumulate,
+                                                      partial, tickets)
+                         : launch_main<F, true, false>(grid, st, w8, row_bytes, rows, ns, nblk, rec, b, Y, k,
+                                                       accumulate, partial, tickets);
     }
-    if (!shared)
-        hipLaunchKernelGGL((bgemm<F, false>), grid, dim3(64 * G::NW), G::LDS, st, w8, row_bytes, int(rows), ns,
-                           int(nblk), rec, b.nc, b.sps, Y, k, accumulate, partial);
-    if ((e = hipGetLastError()) != hipSuccess || b.nsplit == 1) return e;
-    const int64_t nt2 = int64_t(k) * rows;
-    hipLaunchKernelGGL(bgemm_reduce, dim3(unsigned((nt2 + 255) / 256)), dim3(256), 0, st, partial, b.nsplit, k,
-                       int(rows), Y, accumulate);
-    return hipGetLastError();
+    return split ? launch_main<F, false, true>(grid, st, w8, row_bytes, rows, ns, nblk, rec, b, Y, k, accumulate,
+                                               partial, tickets)
+                 : launch_main<F, false, false>(grid, st, w8, row_bytes, rows, ns, nblk, rec, b, Y, k, accumulate,
+                                                partial, tickets);
 }
 
 }  // namespace
@@ -892,7 +946,7 @@ bool gemm_batch_type_ok(nt_qtype t) {
 // records shared through LDS where that needs no split between workgroups and
 // its launch shape costs less (measured at k = 8: 28672 x 8192 49.6 -> 47.7
 // us one-tile; 8192 x 8192, where the one-tile shape needs a four-way split
-// and the third kernel, 20.3 -> 21.2 us, so two-tile).
+// between workgroups, 20.3 -> 21.2 us, so two-tile).
 bool q4k_one_tile(int64_t rows, int64_t cols) {
     const BgemmShape two = bgemm_shape<BQ4K>(rows, cols), one = bgemm_shape<BQ4K1>(rows, cols, true);
     return one.groups > 0 && one.nsplit == 1 && one.cost < two.cost;

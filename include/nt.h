@@ -165,12 +165,14 @@ nt_status nt_gemv_swiglu(nt_qtype t, const void *W_gate, const void *W_up, int64
  * not rounded.  Where a part would overflow fp16 (|x| near 65504 or above,
  * or, for the K-quant mins, a sum of 32 activations that large) the vectors
  * of that 256-column step are split scaled by an exact power of two and
- * their sums scaled back, so any finite X is valid.  The call runs two or
- * three kernels: one writes each step's split activations to the workspace
- * (8224 bytes per 256 columns, 8736 for Q4_K and Q5_K), the main one reads
- * them and the weights; when the columns are split between workgroups (few
- * rows), the partial sums also go to the workspace and a third kernel adds
- * them in a fixed order (results are deterministic).  workspace: device
+ * their sums scaled back, so any finite X is valid.  The call runs two
+ * kernels: one writes each step's split activations to the workspace (8224
+ * bytes per 256 columns, 8736 for Q4_K and Q5_K), the main one reads them
+ * and the weights; when the columns are split between workgroups (few
+ * rows), the partial sums also go to the workspace, with one counter per
+ * row set, and the last workgroup to finish a row set adds them in a fixed
+ * order (results are deterministic; no workgroup waits for another).  The
+ * first kernel clears the counters.  workspace: device
  * memory of at least nt_gemm_batch_workspace_bytes(t, rows, cols) bytes
  * (never 0 for valid arguments; 0 means the arguments are invalid),
  * 16-byte aligned, used only during the call (stream order); calls that

@@ -84,16 +84,22 @@ def _batch(t, W, X, Y, rows, cols, k, ws=A, ws_bytes=4 << 20):
 def test_gemm_batch_argument_errors():
     wsb = nt.nt_gemm_batch_workspace_bytes
     # one activation record per 256 columns (8192 bytes of split activations,
-    # 512 of sub-block sums for K-quants with mins, 32 of scales), then fp32
-    # partial sums of 8 vectors per column range when there is more than one
+    # 512 of sub-block sums for K-quants with mins, 32 of scales), then, when
+    # the columns are split between workgroups, fp32 partial sums of 8
+    # vectors per column range and a 4-byte counter per wave of each
+    # workgroup column (8 waves, at most one workgroup column per 16 rows)
     rec = {nt.Q4_K: 8736, nt.Q5_K: 8736, nt.Q6_K: 8224, nt.Q8_0: 8224, nt.Q4_0: 8224}
     assert wsb(nt.Q4_K, 4, 256) == 8736 and wsb(nt.Q8_0, 1, 32) == 8224   # one range
     for t, rows, cols in [(nt.Q4_K, 8192, 8192), (nt.Q6_K, 8192, 28672), (nt.Q8_0, 4096, 4096),
                           (nt.Q4_K, 3, 65536), (nt.Q5_K, 40040, 2048), (nt.Q4_0, 600, 8960)]:
         ns = -(-cols // 256)
         extra = wsb(t, rows, cols) - ns * rec[t]
-        assert extra >= 0 and extra % (8 * rows * 4) == 0, (t, rows, cols)
-        assert extra // (8 * rows * 4) <= min(ns, 64)
+        split, counters = divmod(extra, 8 * rows * 4)
+        assert extra >= 0 and split != 1 and split <= min(ns, 64), (t, rows, cols)
+        if split == 0:
+            assert counters == 0, (t, rows, cols)
+        else:
+            assert counters > 0 and counters % 32 == 0 and counters <= 32 * -(-rows // 16), (t, rows, cols)
     # enough rows: the waves of a workgroup split the columns, no partial sums
     assert wsb(nt.Q4_K, 8192, 8192) == 32 * 8736 and wsb(nt.Q8_0, 4096, 4096) == 16 * 8224
     assert wsb(nt.Q4_K, 3, 65536) > 256 * 8736          # a few rows: split between workgroups too

@@ -98,8 +98,8 @@ def test_gemm_batch_launch_shapes(t, rows, cols, k):
     """Column splits between the waves of a workgroup (sums added in LDS in
     split order: 1500 x 5888 splits 23 steps 8 ways for one-tile formats,
     the last split shorter), between workgroups only (16 x 16640: partial
-    sums added by the third kernel, the last split shorter) and both (16 x
-    24576)."""
+    sums added by the last wave to finish, the last split shorter) and both
+    (16 x 24576)."""
     _case(t, rows, cols, k, seed=rows + cols)
 
 
