@@ -943,13 +943,13 @@ bool gemm_batch_type_ok(nt_qtype t) {
 }
 
 // Q4_K: two tiles per wave with per-wave records, or one tile per wave with
-// records shared through LDS where that needs no split between workgroups and
-// its launch shape costs less (measured at k = 8: 28672 x 8192 49.6 -> 47.7
-// us one-tile; 8192 x 8192, where the one-tile shape needs a four-way split
-// between workgroups, 20.3 -> 21.2 us, so two-tile).
+// records shared through LDS where its launch shape costs less (measured at
+// k = 8: 28672 x 8192 49.6 -> 47.7 us one-tile; 8192 x 8192, a four-way
+// split between workgroups, 20.0-20.1 -> 18.7-18.8 us since the last wave
+// adds the partial sums, 21.2 us while a third kernel did).
 bool q4k_one_tile(int64_t rows, int64_t cols) {
     const BgemmShape two = bgemm_shape<BQ4K>(rows, cols), one = bgemm_shape<BQ4K1>(rows, cols, true);
-    return one.groups > 0 && one.nsplit == 1 && one.cost < two.cost;
+    return one.groups > 0 && one.cost < two.cost;
 }
 
 size_t gemm_batch_workspace_bytes(nt_qtype t, int64_t rows, int64_t cols) {
