@@ -414,7 +414,7 @@ def verify_gemm(steps):
         Ws = [base] + [base.clone() for _ in range(copies - 1)]
         Y = torch.empty(k * rows, dtype=torch.float32, device=dev)
         nws = nt.nt_gemm_batch_workspace_bytes(t, rows, cols)
-        ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+        ws = torch.zeros(nws, dtype=torch.uint8, device=dev)
         side = torch.cuda.Stream()
         us = time_rotated(torch, lambda i: nt.nt_gemm_batch(t, Ws[i], X, Y, rows, cols, k, ws), copies, steps, side)
         us1 = time_rotated(torch, lambda i: nt.nt_gemv(t, Ws[i], X[:cols], Y[:rows], rows, cols), copies, steps,

@@ -58,8 +58,13 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t w2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 
 constexpr int kNumCUs = 256;   // compute units of an MI355X
+// The workspace starts with the counters of the column splits between
+// workgroups (one per wave's rows of a workgroup column), zero between calls.
+constexpr int kMaxTickets = 4096;
+constexpr size_t kTicketBytes = 4 * kMaxTickets;
 
 // Order of a dword's four bytes in the K slots of one lane: the halves of
 // (w & 0x00ff00ff) then of (w >> 8 & 0x00ff00ff), i.e. bytes 0, 2, 1, 3.
@@ -154,6 +159,14 @@ struct BQ4K {
     static constexpr int kStepBytes = 144, kTiles = 2;
     struct Raw { u32x4n h; u32x2n q[4]; };
     __host__ __device__ static int elem(int m, int g, int i) { return 32 * (m >> 1) + 8 * g + 4 * (m & 1) + perm4(i); }
+    // the eight (m, g) whose values lie in the step's 32-column block jb:
+    // entry e gives m, g and the offset o in the block (elem(m, g, i) = 32
+    // jb + o + perm4(i))
+    __host__ __device__ static void blk(int jb, int e, int &m, int &g, int &o) {
+        m = 2 * jb + (e & 1);
+        g = e >> 1;
+        o = 8 * g + 4 * (e & 1);
+    }
     __device__ static void load(const uint8_t *b, int, int g, int, Raw &r) {
         const uint8_t *const a = static_cast<const uint8_t *>(__builtin_assume_aligned(b, 16));
         r.h = *reinterpret_cast<const u32x4n *>(a);
@@ -265,6 +278,11 @@ struct BQ5K {
         const int c = code_byte(m >> 1, g) + perm4(i);
         return 32 * (2 * (c >> 5) + (m & 1)) + (c & 31);
     }
+    __host__ __device__ static void blk(int jb, int e, int &m, int &g, int &o) {   // as for BQ4K
+        m = 2 * (4 * (jb >> 2) + (e & 3)) + (jb & 1);
+        g = 2 * ((jb >> 1) & 1) + (e >> 2);
+        o = 16 * (e >> 2) + 4 * (e & 3);
+    }
     // 6-bit scale S_j and min M_j of sub-block j from the 12 scale bytes
     // (words h.y, h.z, h.w): j < 4: low 6 bits of bytes j and j + 4; j >= 4:
     // low / high nibble of byte j + 4 with the top two bits of byte j - 4 / j.
@@ -333,6 +351,11 @@ struct BQ6K {
     struct Raw { uint32_t ql[8][2], qh[4][2], sc[5]; };
     __host__ __device__ static int elem(int m, int g, int i) {
         return 128 * (m >> 3) + 32 * ((m >> 1) & 3) + 16 * (m & 1) + 4 * g + perm4(i);
+    }
+    __host__ __device__ static void blk(int jb, int e, int &m, int &g, int &o) {   // as for BQ4K
+        m = 8 * (jb >> 2) + 2 * (jb & 3) + (e & 1);
+        g = e >> 1;
+        o = 16 * (e & 1) + 4 * g;
     }
     __device__ static void load(const uint8_t *b, int, int g, int, Raw &r) {
         const uint8_t *a = b - (reinterpret_cast<uintptr_t>(b) & 2);
@@ -431,14 +454,10 @@ struct Geo {
 // that the main kernel undoes on the step's fp32 sums.
 template <class F>
 __global__ void __launch_bounds__(256) bgemm_prep(const float *__restrict__ X, int64_t cols, int k,
-                                                  uint8_t *__restrict__ rec, uint32_t *__restrict__ tickets,
-                                                  int ntickets) {
+                                                  uint8_t *__restrict__ rec) {
     using G = Geo<F>;
     __shared__ __attribute__((aligned(16))) float xs[8][260];
     const int s = blockIdx.x, t = threadIdx.x;
-    // the main kernel's per-row-group tickets start each call at zero
-    for (int i = s * 256 + t; i < ntickets; i += gridDim.x * 256)
-        __hip_atomic_store(tickets + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint8_t *const out = rec + int64_t(s) * G::REC;
     {
         const int n = t >> 5, c = 8 * (t & 31);
@@ -495,6 +514,7 @@ __device__ __forceinline__ void wait_vm(int n) {
     case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5)); break;
     case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6)); break;
     case 7: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); break;
     case 13: __builtin_amdgcn_s_waitcnt(vmcnt_imm(13)); break;
     case 14: __builtin_amdgcn_s_waitcnt(vmcnt_imm(14)); break;
     case 15: __builtin_amdgcn_s_waitcnt(vmcnt_imm(15)); break;
@@ -506,11 +526,11 @@ __device__ __forceinline__ void wait_vm(int n) {
 
 // Step counters of the shared record ring, in LDS: plain workgroup-scope
 // atomics (no implied waits: the copies they report on were waited for
-// explicitly), one count per wave (lane 0 adds it).  A wait polls with a
-// sleep between reads and gives up after about 2^20 polls (far beyond any
-// real wait), so every wave always ends.
-__device__ __forceinline__ void lds_count(uint32_t *p) {
-    if (__lane_id() == 0) __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+// explicitly), added by lane 0 of a wave.  A wait polls with a sleep
+// between reads and gives up after about 2^20 polls (far beyond any real
+// wait), so every wave always ends.
+__device__ __forceinline__ void lds_count(uint32_t *p, uint32_t v = 1u) {
+    if (__lane_id() == 0) __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 __device__ __forceinline__ uint32_t lds_read_count(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -546,6 +566,78 @@ __device__ __forceinline__ void load_x(const uint8_t *__restrict__ rec, int s, i
     xr.up = *reinterpret_cast<const f4 *>(rc + Geo<F>::REC - 32 + 16 * (g & 1));
 }
 
+// One wave forms the activation record of a step in LDS (the record
+// bgemm_prep writes, bit for bit but for the sign of zeros that stand for
+// vectors past k and columns past the end) from the step's fp32
+// activations, copied into the same slot (vector n's 1 KB at 1024 n, its
+// 16-byte chunk c at chunk position c ^ n, so the eight lanes of a read
+// group hit distinct banks).  Lane l takes vector n = l mod 8 and the 32
+// columns of block jb = l / 8 (columns col0 + 32 jb ...): the vector's
+// maximum over the step comes from the eight lanes that hold it, then the
+// lane scales its values, splits them into fp16 hi and lo parts and writes
+// the eight (m, g) entries of its block (and, with mins, its sub-block
+// sum).  All reads of the slot are issued before the first write (the
+// writes depend on the maximum).
+template <class F>
+__device__ __forceinline__ void form_record(uint8_t *slot, int lane, int64_t col0, int k, int64_t cols) {
+    const int n = lane & 7, jb = lane >> 3;
+    float v[32];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const f4 x = *reinterpret_cast<const f4 *>(slot + 1024 * n + 16 * ((8 * jb + q) ^ n));
+        v[4 * q] = x.x;
+        v[4 * q + 1] = x.y;
+        v[4 * q + 2] = x.z;
+        v[4 * q + 3] = x.w;
+    }
+    // a vector past k or a block past the last column (cols is a multiple
+    // of 32) holds zeros: it takes no part in the maximum and is scaled by 0
+    // (a -0 from a negative value adds nothing to any sum)
+    const bool live = n < k && col0 + 32 * jb < cols;
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(v[i]));
+    mx = live ? mx : 0.f;
+    mx = fmaxf(mx, __shfl_xor(mx, 8, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    int e2 = 0;
+    (void)frexpf(fminf(mx, 1.0e36f) * 32.f, &e2);   // as in bgemm_prep
+    const int e = min(max(e2 - 14, 0), 120);
+    const float sd = live ? ldexpf(1.f, -e) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] *= sd;
+    __builtin_amdgcn_sched_barrier(0);
+    u32x2 *const rw = reinterpret_cast<u32x2 *>(slot);
+#pragma unroll
+    for (int en = 0; en < 8; ++en) {
+        int m = 0, gg = 0, o = 0;
+        F::blk(jb, en, m, gg, o);
+        // words (o, o + 2) and (o + 1, o + 3): values perm4(0..3) in K-slot order
+        const h2 h0 = __builtin_convertvector(f2{v[o], v[o + 2]}, h2);
+        const h2 h1 = __builtin_convertvector(f2{v[o + 1], v[o + 3]}, h2);
+        const h2 l0 = __builtin_convertvector(f2{v[o] - float(h0.x), v[o + 2] - float(h0.y)}, h2);
+        const h2 l1 = __builtin_convertvector(f2{v[o + 1] - float(h1.x), v[o + 3] - float(h1.y)}, h2);
+        const int it = ((m >> 1) * 64 + n + 16 * gg) * 2 + (m & 1);   // hi part: lane n + 16 g
+        rw[it] = u32x2{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1)};
+        rw[it + 16] = u32x2{__builtin_bit_cast(uint32_t, l0), __builtin_bit_cast(uint32_t, l1)};   // lane + 8: lo
+    }
+    if constexpr (F::kMin) {
+        float sx = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) sx += (v[4 * q] + v[4 * q + 1]) + (v[4 * q + 2] + v[4 * q + 3]);
+        // K slot kk = 4 g' + i of lane b' + 16 g': hi (kk < 8) or lo part of
+        // sub-block kk mod 8's sum of vector b' (zero for b' >= 8)
+        uint16_t *const s16 = reinterpret_cast<uint16_t *>(slot + 8192);
+        const int i = jb & 3, lh = n + 16 * (jb >> 2), ll = lh + 32;
+        s16[lh * 4 + i] = split_part(sx, false);
+        s16[(lh + 8) * 4 + i] = 0;
+        s16[ll * 4 + i] = split_part(sx, true);
+        s16[(ll + 8) * 4 + i] = 0;
+    }
+    if (jb == 0) reinterpret_cast<float *>(slot + Geo<F>::REC - 32)[n] = ldexpf(1.f, e);
+}
+
 // Main pass.  A workgroup's NW waves form nr = NW / nc row groups of nc
 // column splits: wave w takes the T 16-row tiles from row 16 T (nr x + w /
 // nc) and the steps [c sps, (c + 1) sps) of column split c = nc y + w % nc
@@ -569,7 +661,8 @@ template <class F, bool SHARE, bool SPLIT>
 __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__restrict__ W, int64_t row_bytes, int rows,
                                                           int nsteps, int nblk, const uint8_t *__restrict__ rec,
                                                           int nc, int sps, float *__restrict__ Y, int k, int accumulate,
-                                                          float *__restrict__ partial, uint32_t *__restrict__ tickets) {
+                                                          float *__restrict__ partial, uint32_t *__restrict__ tickets,
+                                                          const float *__restrict__ X, int64_t cols) {
     using G = Geo<F>;
     constexpr int T = G::T;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -651,35 +744,50 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
         constexpr int kW = T * G::NI;
         if constexpr (SHARE) {
             // The workgroup's waves share one record per step through a ring of R
-            // = 7 LDS records: wave w copies bytes [1024 w, 1024 w + 1024) of it,
-            // wave 0 also the sums and scales after 8192 (the others a 16-byte
-            // placeholder, so every wave issues two copies per record), four
-            // steps ahead.  Issue order: records 0, 1, 2, weights 0, record 3,
-            // weights 1, then per step t record t + 4 and weights t + 2, so at step
-            // t, with only weights t + 1 still allowed in flight, this wave's
-            // weights t and its pieces of record t + 3 have landed.  arrived[b]
-            // counts the waves whose pieces of the record in slot b have landed
-            // (each reports record t + 3 at step t), done[b] those that have read
-            // it: a wave reads record t once all eight have reported it, and copies
-            // record t + 4 into its slot once all have read record t - 3.  The
-            // slowest wave never waits (every other wave has reported and read
+            // = 7 LDS slots.  Record j is made by wave j mod 8: four steps ahead it
+            // copies the step's activations (eight 1 KB copies) into slot j mod R,
+            // and once they have landed it forms the record in place (form_record)
+            // and adds 8 to arrived[slot].  Issue order: activations 0, 1, 2,
+            // weights 0, activations 3, weights 1, then per step t activations t
+            // + 4 and weights t + 2, so at step t, with only weights t + 1 still
+            // allowed in flight, weights t and activations t + 3 have landed:
+            // records 0-2 are formed before the loop and record t + 3 at step t.
+            // done[b] counts the waves that have read the record in slot b: a wave
+            // reads record t once it is formed (arrived), and the maker of record
+            // t + 4 copies into its slot once all have read record t - 3.  The
+            // slowest wave never waits (every other wave has formed and read
             // those), so every wait ends, and the waves may drift three steps apart.
             constexpr int kAhead = 4, kReport = 3;
             static_assert(G::R == kAhead + kReport, "ring of records in flight and being read");
-            const auto issue_rec = [&](int j) {
-                const uint8_t *const rb = rec + int64_t(s_lo + j) * G::REC;
-                const uint32_t dst = lds_addr(lds + G::RING_REC + (j % G::R) * G::REC);
-                dma<16>(rb, uint32_t(1024 * wv + 16 * lane), dst + 1024 * wv);
-                if (wv == 0) {
-                    if (lane < (G::REC - 8192) / 16) dma<16>(rb, uint32_t(8192 + 16 * lane), dst + 8192);
-                } else if (lane == 0) {
-                    dma<16>(rb, 0u, lds_addr(lds + G::SLOT + 16 * wv));
+            const auto slot = [&](int j) { return lds + G::RING_REC + (j % G::R) * G::REC; };
+            const auto issue_x = [&](int j) {
+                const int64_t c0 = int64_t(s_lo + j) * 256;   // first column of the step
+                const uint32_t dst = lds_addr(slot(j));
+#pragma unroll
+                for (int v = 0; v < 8; ++v) {
+                    // lane l copies chunk l ^ v of vector min(v, k - 1) (any
+                    // chunk past the last column: the row's first chunk)
+                    const int64_t col = c0 + 4 * (lane ^ v);
+                    const uint32_t off = uint32_t((int64_t(min(v, k - 1)) * cols + (col < cols ? col : 0)) * 4);
+                    dma<16>(reinterpret_cast<const uint8_t *>(X), off, dst + 1024 * v);
                 }
             };
-            for (int j = 0; j < kAhead - 1 && j < n; ++j) issue_rec(j);
+            const auto form = [&](int j) {
+                form_record<F>(slot(j), lane, int64_t(s_lo + j) * 256, k, cols);
+                __builtin_amdgcn_s_waitcnt(kLgkm0);   // the record is in LDS
+                __builtin_amdgcn_sched_barrier(0);
+                lds_count(&cnt[j % G::R], 8u);
+            };
+            const auto mine = [&](int j) { return j < n && j % G::NW == wv; };
+            for (int j = 0; j < kAhead - 1; ++j)
+                if (mine(j)) issue_x(j);
             issue_w(0, s_lo);
-            if (kAhead - 1 < n) issue_rec(kAhead - 1);
+            if (mine(kAhead - 1)) issue_x(kAhead - 1);
             if (n > 1) issue_w(1, s_lo + 1);
+            if (wv < kAhead - 1 && wv < n) {
+                wait_vm(n > 1 ? 2 * kW : kW);                   // this wave's activations for record wv
+                form(wv);
+            }
             // the two waves of a SIMD (w, w + 4) take turns at the higher issue
             // priority, one step each, so they advance at the same pace and
             // neither waits long for the other at the counters
@@ -690,19 +798,19 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
                 // both counters this step waits on, read before the weight wait
                 const uint32_t arrived0 = lds_read_count(&cnt[b]);
                 const uint32_t done0 = lds_read_count(&cnt[G::R + jn % G::R]);
-                wait_vm(t + 1 < n ? kW : 0);                      // weights t, pieces of record t + 3 landed
-                for (int j = t == 0 ? 0 : t + kReport; j <= t + kReport && j < n; ++j) lds_count(&cnt[j % G::R]);
+                wait_vm(t + 1 < n ? kW : 0);                      // weights t, activations t + 3 landed
+                if (mine(t + kReport)) form(t + kReport);
                 lds_wait_count(&cnt[b], 8u * uint32_t(t / G::R + 1), arrived0);
-                const uint8_t *const rc = lds + G::RING_REC + b * G::REC;
+                const uint8_t *const rc = slot(t);
                 XRegs xr;
 #pragma unroll
                 for (int q = 0; q < 8; ++q) xr.x[q] = *reinterpret_cast<const u32x4a *>(rc + (q * 64 + lane) * 16);
                 if constexpr (F::kMin) xr.m = *reinterpret_cast<const u32x2 *>(rc + 8192 + lane * 8);
                 xr.up = *reinterpret_cast<const f4 *>(rc + G::REC - 32 + 16 * (g & 1));
                 // the next copies go out while those reads are in flight
-                if (jn < n) {
+                if (mine(jn)) {
                     if (jn >= G::R) lds_wait_count(&cnt[G::R + jn % G::R], 8u * uint32_t(jn / G::R), done0);
-                    issue_rec(jn);
+                    issue_x(jn);
                 }
                 if (t + 2 < n) issue_w((t + 2) % G::S, s_lo + t + 2);
                 __builtin_amdgcn_s_waitcnt(kLgkm0);               // record t is in registers
@@ -778,15 +886,18 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
         // Columns split between workgroups: the partial sums above are
         // agent-scope stores (written through to the level every XCD reads,
         // not left dirty in this XCD's L2).  Once they have completed, the
-        // wave takes a ticket for its rows; the wave that draws the last of
-        // the nsplit adds the rows' partial sums in split order (agent-scope
-        // loads) and writes Y.  Nothing waits on another wave.
+        // wave takes a ticket for its rows (a counter at the start of the
+        // workspace, zero between calls); the wave that draws the last of
+        // the nsplit sets it back to zero, adds the rows' partial sums in
+        // split order (agent-scope loads) and writes Y.  Nothing waits on
+        // another wave.
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        uint32_t *const tp = tickets + int64_t(blockIdx.x) * nr + wv / nc;
         uint32_t tk = 0;
-        if (lane == 0)
-            tk = __hip_atomic_fetch_add(tickets + int64_t(blockIdx.x) * nr + wv / nc, 1u, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) tk = __hip_atomic_fetch_add(tp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (__builtin_amdgcn_readfirstlane(tk) != gridDim.y - 1) return;
+        // every split has drawn: the counter goes back to zero for the next call
+        if (lane == 0) __hip_atomic_store(tp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // 2T outputs per lane (output i = lane + 64 j is n = i / 16T, row T0
         // + i mod 16T), four splits at a time: 8T loads in flight before the
         // first add.  A split past the last reloads the last one and adds +0
@@ -850,6 +961,7 @@ BgemmShape bgemm_shape(int64_t rows, int64_t cols, bool shared_only = false) {
             const int total = nc * sp, sps = (ns + total - 1) / total;
             if ((ns + sps - 1) / sps != total) continue;   // some split would have no step
             const int64_t groups = (tiles + G::NW / nc - 1) / (G::NW / nc);
+            if (sp > 1 && groups * (G::NW / nc) > kMaxTickets) continue;   // counters of a split
             const int64_t rounds = (groups * sp + kNumCUs - 1) / kNumCUs;
             // shared records (one column range per workgroup, where LDS allows):
             // a fifth less per step than records loaded by every wave; a step
@@ -871,11 +983,19 @@ BgemmShape bgemm_shape(int64_t rows, int64_t cols, bool shared_only = false) {
     return b;
 }
 
+// Shared records (formed in LDS by the main kernel) or records written by
+// bgemm_prep to the workspace.
+template <class F>
+bool shared_records(const BgemmShape &b) {
+    return Geo<F>::kShare && b.nc == 1;
+}
+
 template <class F>
 size_t workspace_for(int64_t rows, int64_t cols) {
     const BgemmShape b = bgemm_shape<F>(rows, cols);
     const int64_t ns = (cols + 255) / 256;
-    return size_t(ns) * Geo<F>::REC + (b.nsplit > 1 ? size_t(b.nsplit) * 8 * size_t(rows) * 4 + size_t(b.groups) * Geo<F>::NW * 4 : 0);
+    return kTicketBytes + (shared_records<F>(b) ? 0 : size_t(ns) * Geo<F>::REC) +
+           (b.nsplit > 1 ? size_t(b.nsplit) * 8 * size_t(rows) * 4 : 0);
 }
 
 // The main kernel in one of its four forms (shared records or not; columns
@@ -883,10 +1003,10 @@ size_t workspace_for(int64_t rows, int64_t cols) {
 template <class F, bool SHARE, bool SPLIT>
 hipError_t launch_main(dim3 grid, hipStream_t st, const uint8_t *W, int64_t row_bytes, int64_t rows, int ns,
                        int64_t nblk, const uint8_t *rec, const BgemmShape &b, float *Y, int k, int accumulate,
-                       float *partial, uint32_t *tickets) {
+                       float *partial, uint32_t *tickets, const float *X, int64_t cols) {
     using G = Geo<F>;
     hipLaunchKernelGGL((bgemm<F, SHARE, SPLIT>), grid, dim3(64 * G::NW), SHARE ? G::LDS_SH : G::LDS, st, W, row_bytes,
-                       int(rows), ns, int(nblk), rec, b.nc, b.sps, Y, k, accumulate, partial, tickets);
+                       int(rows), ns, int(nblk), rec, b.nc, b.sps, Y, k, accumulate, partial, tickets, X, cols);
     return hipGetLastError();
 }
 
@@ -896,11 +1016,10 @@ hipError_t run_bgemm(const void *W, int64_t row_bytes, int64_t rows, int64_t col
     using G = Geo<F>;
     const int ns = int((cols + 255) / 256);
     const BgemmShape b = bgemm_shape<F>(rows, cols);
-    const bool split = b.nsplit > 1;
-    uint8_t *const rec = static_cast<uint8_t *>(ws);
-    float *const partial = reinterpret_cast<float *>(rec + int64_t(ns) * G::REC);
-    uint32_t *const tickets = reinterpret_cast<uint32_t *>(partial + (split ? int64_t(b.nsplit) * 8 * rows : 0));
-    const int ntickets = split ? b.groups * (G::NW / b.nc) : 0;   // one per wave's rows of a workgroup column
+    const bool split = b.nsplit > 1, share = shared_records<F>(b);
+    uint32_t *const tickets = static_cast<uint32_t *>(ws);
+    uint8_t *const rec = static_cast<uint8_t *>(ws) + kTicketBytes;
+    float *const partial = reinterpret_cast<float *>(rec + (share ? 0 : int64_t(ns) * G::REC));
     // more than 64 KB of dynamic LDS: allowed once per device for each form
     static std::atomic<uint64_t> done{0};
     int dev = 0;
@@ -918,22 +1037,21 @@ hipError_t run_bgemm(const void *W, int64_t row_bytes, int64_t rows, int64_t col
         if (e != hipSuccess) return e;
         done.fetch_or(uint64_t(1) << dev, std::memory_order_release);
     }
-    hipLaunchKernelGGL(bgemm_prep<F>, dim3(unsigned(ns)), dim3(256), 0, st, X, cols, k, rec, tickets, ntickets);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const dim3 grid(unsigned(b.groups), unsigned(b.nsplit));
     const uint8_t *const w8 = static_cast<const uint8_t *>(W);
     if constexpr (G::kShare) {
-        if (b.nc == 1)
+        if (share)
             return split ? launch_main<F, true, true>(grid, st, w8, row_bytes, rows, ns, nblk, rec, b, Y, k, accumulate,
-                                                      partial, tickets)
+                                                      partial, tickets, X, cols)
                          : launch_main<F, true, false>(grid, st, w8, row_bytes, rows, ns, nblk, rec, b, Y, k,
-                                                       accumulate, partial, tickets);
+                                                       accumulate, partial, tickets, X, cols);
     }
+    hipLaunchKernelGGL(bgemm_prep<F>, dim3(unsigned(ns)), dim3(256), 0, st, X, cols, k, rec);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     return split ? launch_main<F, false, true>(grid, st, w8, row_bytes, rows, ns, nblk, rec, b, Y, k, accumulate,
-                                               partial, tickets)
+                                               partial, tickets, X, cols)
                  : launch_main<F, false, false>(grid, st, w8, row_bytes, rows, ns, nblk, rec, b, Y, k, accumulate,
-                                                partial, tickets);
+                                                partial, tickets, X, cols);
 }
 
 }  // namespace

@@ -165,19 +165,24 @@ nt_status nt_gemv_swiglu(nt_qtype t, const void *W_gate, const void *W_up, int64
  * not rounded.  Where a part would overflow fp16 (|x| near 65504 or above,
  * or, for the K-quant mins, a sum of 32 activations that large) the vectors
  * of that 256-column step are split scaled by an exact power of two and
- * their sums scaled back, so any finite X is valid.  The call runs two
- * kernels: one writes each step's split activations to the workspace (8224
- * bytes per 256 columns, 8736 for Q4_K and Q5_K), the main one reads them
- * and the weights; when the columns are split between workgroups (few
- * rows), the partial sums also go to the workspace, with one counter per
- * row set, and the last workgroup to finish a row set adds them in a fixed
- * order (results are deterministic; no workgroup waits for another).  The
- * first kernel clears the counters.  workspace: device
- * memory of at least nt_gemm_batch_workspace_bytes(t, rows, cols) bytes
- * (never 0 for valid arguments; 0 means the arguments are invalid),
- * 16-byte aligned, used only during the call (stream order); calls that
- * share a workspace must not overlap.  W, X and the workspace 16-byte
- * aligned, Y 4-byte aligned; Y must not overlap X, W or the workspace. */
+ * their sums scaled back, so any finite X is valid.  The call runs one or
+ * two kernels: for Q4_K, Q5_K and Q6_K on most shapes the main kernel forms
+ * each step's split activations in on-chip memory itself; otherwise a first
+ * kernel writes them to the workspace (8224 bytes per 256 columns, 8736 for
+ * Q4_K and Q5_K) and the main one reads them.  When the columns are split
+ * between workgroups (few rows), the partial sums also go to the workspace
+ * and, per set of rows, the last wave to finish adds them in a fixed order
+ * (results are deterministic; no wave waits for another), counted by the
+ * counters in the workspace's first 16384 bytes.  workspace: device memory
+ * of at least nt_gemm_batch_workspace_bytes(t, rows, cols) bytes (never 0
+ * for valid arguments; 0 means the arguments are invalid), 16-byte
+ * aligned, whose first 16384 bytes are zero before the first call that
+ * uses it: every call leaves them zero again, the rest of the workspace
+ * is used only during the call (stream order), so one zero-filled
+ * workspace serves any sequence of calls (any shapes, graph replays) as
+ * long as nothing else writes its first 16384 bytes.  Calls that share a
+ * workspace must not overlap.  W, X and the workspace 16-byte aligned, Y
+ * 4-byte aligned; Y must not overlap X, W or the workspace. */
 size_t nt_gemm_batch_workspace_bytes(nt_qtype t, int64_t rows, int64_t cols);
 nt_status nt_gemm_batch(nt_qtype t, const void *W, const float *X, float *Y, int64_t rows, int64_t cols,
                         int32_t k, int32_t accumulate, void *workspace, size_t workspace_bytes, nt_stream stream);

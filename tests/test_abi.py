@@ -83,26 +83,29 @@ def _batch(t, W, X, Y, rows, cols, k, ws=A, ws_bytes=4 << 20):
 @no_gpu_only
 def test_gemm_batch_argument_errors():
     wsb = nt.nt_gemm_batch_workspace_bytes
-    # one activation record per 256 columns (8192 bytes of split activations,
-    # 512 of sub-block sums for K-quants with mins, 32 of scales), then, when
-    # the columns are split between workgroups, fp32 partial sums of 8
-    # vectors per column range and a 4-byte counter per wave of each
-    # workgroup column (8 waves, at most one workgroup column per 16 rows)
+    # 16384 bytes of split counters, then one activation record per 256
+    # columns where a first kernel writes them (8192 bytes of split
+    # activations, 512 of sub-block sums for K-quants with mins, 32 of
+    # scales; none where the main kernel forms them in LDS), then, when the
+    # columns are split between workgroups, fp32 partial sums of 8 vectors
+    # per column range
     rec = {nt.Q4_K: 8736, nt.Q5_K: 8736, nt.Q6_K: 8224, nt.Q8_0: 8224, nt.Q4_0: 8224}
-    assert wsb(nt.Q4_K, 4, 256) == 8736 and wsb(nt.Q8_0, 1, 32) == 8224   # one range
+    C = 16384
+    assert wsb(nt.Q8_0, 1, 32) == C + 8224          # one range, records from the first kernel
     for t, rows, cols in [(nt.Q4_K, 8192, 8192), (nt.Q6_K, 8192, 28672), (nt.Q8_0, 4096, 4096),
                           (nt.Q4_K, 3, 65536), (nt.Q5_K, 40040, 2048), (nt.Q4_0, 600, 8960)]:
         ns = -(-cols // 256)
-        extra = wsb(t, rows, cols) - ns * rec[t]
-        split, counters = divmod(extra, 8 * rows * 4)
-        assert extra >= 0 and split != 1 and split <= min(ns, 64), (t, rows, cols)
-        if split == 0:
-            assert counters == 0, (t, rows, cols)
+        extra = wsb(t, rows, cols) - C
+        for records in (0, ns * rec[t]):
+            split, r = divmod(extra - records, 8 * rows * 4)
+            if extra >= records and r == 0 and split != 1 and split <= min(ns, 64):
+                break
         else:
-            assert counters > 0 and counters % 32 == 0 and counters <= 32 * -(-rows // 16), (t, rows, cols)
+            raise AssertionError((t, rows, cols, extra))
     # enough rows: the waves of a workgroup split the columns, no partial sums
-    assert wsb(nt.Q4_K, 8192, 8192) == 32 * 8736 and wsb(nt.Q8_0, 4096, 4096) == 16 * 8224
-    assert wsb(nt.Q4_K, 3, 65536) > 256 * 8736          # a few rows: split between workgroups too
+    assert wsb(nt.Q8_0, 4096, 4096) == C + 16 * 8224
+    assert wsb(nt.Q4_K, 28672, 8192) == C                # records formed in LDS, no split
+    assert wsb(nt.Q4_K, 3, 65536) > C + 3 * 8 * 4 * 2   # a few rows: split between workgroups
     assert wsb(nt.F32, 4, 256) == 0 and wsb(nt.Q4_K, 4, 100) == 0 and wsb(nt.Q4_K, 4, 65536 + 256) == 0
     assert wsb(nt.Q4_K, -1, 256) == 0
     assert _batch(nt.Q4_K, A, A, A, 4, 256, 0) == nt.NT_EINVAL

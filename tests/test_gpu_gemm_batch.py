@@ -28,7 +28,7 @@ GUARD = 12345.0
 def _run(t, W, X, rows, cols, k, y0=None, dev_w=None):
     dev = device()
     nws = nt.nt_gemm_batch_workspace_bytes(t, rows, cols)
-    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(nws, dtype=torch.uint8, device=dev)
     Y = torch.full((k * rows + 64,), GUARD, dtype=torch.float32, device=dev)
     if y0 is not None:
         Y[:k * rows] = to_dev(y0.reshape(-1))
@@ -164,6 +164,33 @@ def test_gemm_batch_70b_ffn_shapes_sampled(t, si):
         assert_close(got[n][ids], ref, what=f"gemm_batch {t} {rows}x{cols} vector {n} (sampled rows)")
 
 
+def test_gemm_batch_one_workspace_many_calls():
+    """One workspace serves a sequence of calls of different formats and
+    launch forms (records formed in LDS by the main kernel or written by a
+    first kernel; columns split between workgroups or not), twice over.
+    Only its first 16384 bytes (the split counters) start at zero, the rest
+    holds garbage, and the counters are zero again after every call."""
+    dev = device()
+    cases = [(O.Q6_K, 300, 8192, 5), (O.Q8_0, 37, 1024, 3), (O.Q4_K, 300, 8192, 8), (O.Q5_K, 101, 4352, 2),
+             (O.Q6_K, 1500, 5888, 4), (O.Q4_K, 3, 65536, 4), (O.Q6_K, 16, 16640, 7)]
+    nws = max(nt.nt_gemm_batch_workspace_bytes(t, r, c) for t, r, c, _ in cases)
+    ws = torch.full((nws,), 0xA5, dtype=torch.uint8, device=dev)
+    ws[:16384] = 0
+    data = []
+    for i, (t, rows, cols, k) in enumerate(cases):
+        W = O.quantize(t, synth.normal_f32(i, 700 + t, rows * cols, std=0.02))
+        X = np.stack([synth.normal_f32(i, 710 + n, cols) for n in range(k)])
+        data.append((t, rows, cols, k, to_dev(W), to_dev(X.reshape(-1)), O.gemm_batch(t, W, rows, cols, X)))
+    for rep in range(2):
+        for t, rows, cols, k, dw, dx, ref in data:
+            Y = torch.full((k * rows,), GUARD, dtype=torch.float32, device=dev)
+            nt.nt_gemm_batch(t, dw, dx, Y, rows, cols, k, ws)
+            got = host(Y).reshape(k, rows)
+            for n in range(k):
+                assert_close(got[n], ref[n], what=f"gemm_batch {TID[TYPES.index(t)]} {rows}x{cols} call {rep} vector {n}")
+            assert torch.count_nonzero(ws[:16384]).item() == 0, "split counters not back at zero"
+
+
 def test_gemm_batch_rejects_bad_arguments():
     dev = device()
     W = torch.zeros(4 * 8 * 144, dtype=torch.uint8, device=dev)    # 4 Q4_K rows of 2048 (also 4 F32 rows of 256)
@@ -171,7 +198,7 @@ def test_gemm_batch_rejects_bad_arguments():
     Y = torch.zeros(9 * 4, dtype=torch.float32, device=dev)
     nws = nt.nt_gemm_batch_workspace_bytes(O.Q4_K, 4, 2048)
     assert nws > 0                                                  # four rows: split over columns
-    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(nws, dtype=torch.uint8, device=dev)
     for k in (0, 9):
         with pytest.raises(nt.NTError):
             nt.nt_gemm_batch(O.Q4_K, W, X, Y, 4, 2048, k, ws)
