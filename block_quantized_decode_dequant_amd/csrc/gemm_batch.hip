@@ -107,8 +107,18 @@ __device__ __forceinline__ float ubyte(uint32_t w, int k) { return float((w >> (
 struct BQ80 {
     static constexpr bool kMin = false;
     static constexpr int kStepBytes = 272, kTiles = 1;
+    // 120 KB of weight rings leave room for four record slots; a Q8_0 step
+    // reads its own records cheaply, so forming them costs slightly more
+    // (measured at k = 8: 14336 x 4096 25.8 -> 22.1 us shared, 4096 x 14336
+    // 25.5 -> 21.1, 128256 x 4096 164-168 -> 170, 4096 x 4096 12.5 either way)
+    static constexpr int kRingSlots = 4, kRingAhead = 3, kRingReport = 2, kShareCost = 21;
     struct Raw { u32x3 v[8]; };
     __host__ __device__ static int elem(int m, int g, int i) { return 32 * (m >> 1) + 8 * g + 4 * (m & 1) + perm4(i); }
+    __host__ __device__ static void blk(int jb, int e, int &m, int &g, int &o) {   // as for BQ4K
+        m = 2 * jb + (e & 1);
+        g = e >> 1;
+        o = 8 * g + 4 * (e & 1);
+    }
     __device__ static void load(const uint8_t *p, int s, int g, int nblk, Raw &r) {
 #pragma unroll
         for (int bb = 0; bb < 8; ++bb) {
@@ -156,7 +166,7 @@ struct BQ80 {
 // keep every step start 16-byte aligned.
 struct BQ4K {
     static constexpr bool kMin = true;
-    static constexpr int kStepBytes = 144, kTiles = 2;
+    static constexpr int kStepBytes = 144, kTiles = 1;   // one tile: LDS room for the record ring
     struct Raw { u32x4n h; u32x2n q[4]; };
     __host__ __device__ static int elem(int m, int g, int i) { return 32 * (m >> 1) + 8 * g + 4 * (m & 1) + perm4(i); }
     // the eight (m, g) whose values lie in the step's 32-column block jb:
@@ -205,13 +215,6 @@ struct BQ4K {
         const float d = h2f(r.h.x) * 16777216.f, dmin = h2f(r.h.x >> 16) * 16777216.f;
         acc += d * (lo + 0.0625f * hi) - dmin * cm;
     }
-};
-
-// Q4_K with one 16-row tile per wave: the same operands, for launches whose
-// waves share the activation records (the one-tile weight rings leave LDS
-// room for the record ring).
-struct BQ4K1 : BQ4K {
-    static constexpr int kTiles = 1;
 };
 
 // ---- Q4_0: a step is 8 blocks of 18 bytes; lane group g takes code bytes
@@ -415,6 +418,19 @@ typedef uint32_t u32x4a __attribute__((ext_vector_type(4)));   // 16-byte aligne
 // sit Lp bytes apart in LDS, an odd number of granules, so the 16 lanes that
 // read one offset of 16 rows hit distinct banks; a tile takes NI whole copy
 // instructions (the lanes past the 16 rows fill padding).
+// Record ring of the shared-record form: slots, how many steps ahead a
+// step's activations are copied and its record formed, and the launch-shape
+// cost of one of its steps in twentieths of a per-wave-record step (a format
+// may set its own with kRingSlots, kRingAhead, kRingReport, kShareCost).
+template <class F, class = void>
+struct RingOf {
+    static constexpr int slots = 7, ahead = 4, report = 3, cost = 16;
+};
+template <class F>
+struct RingOf<F, std::void_t<decltype(F::kRingSlots)>> {
+    static constexpr int slots = F::kRingSlots, ahead = F::kRingAhead, report = F::kRingReport, cost = F::kShareCost;
+};
+
 template <class F>
 struct Geo {
     static constexpr int T = F::kTiles;
@@ -430,13 +446,16 @@ struct Geo {
     static constexpr int REC = 8192 + (F::kMin ? 512 : 0) + 32;  // activation record of one step
     static_assert(LDS <= 160 * 1024, "LDS of one workgroup per CU");
     // shared records (all waves of a workgroup on one column range): a ring of
-    // R records after the weight rings, then 2R step counters and one 16-byte
-    // slot per wave for the placeholder copies (fits for Q5_K and Q6_K)
-    static constexpr int R = 7;
+    // R record slots after the weight rings, then 2R step counters.  Step j's
+    // activations are copied KA steps ahead and its record formed KR steps
+    // ahead (fits for Q8_0 with four slots, Q4_K one-tile, Q5_K and Q6_K with
+    // seven)
+    static constexpr int KA = RingOf<F>::ahead, KR = RingOf<F>::report;
+    static constexpr int R = RingOf<F>::slots;
+    static_assert(R > KA && KA > KR && KR >= 0 && 2 * R <= 16, "record ring");
     static constexpr int RING_REC = LDS;                         // offset of the record ring
     static constexpr int CNT = LDS + R * REC;                    // offset of the counters
-    static constexpr int SLOT = CNT + 64;                        // offset of the placeholder slots
-    static constexpr int LDS_SH = SLOT + 16 * NW;
+    static constexpr int LDS_SH = CNT + 64;
     static constexpr bool kShare = LDS_SH <= 160 * 1024;
 };
 
@@ -515,6 +534,7 @@ __device__ __forceinline__ void wait_vm(int n) {
     case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6)); break;
     case 7: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7)); break;
     case 8: __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); break;
+    case 10: __builtin_amdgcn_s_waitcnt(vmcnt_imm(10)); break;
     case 13: __builtin_amdgcn_s_waitcnt(vmcnt_imm(13)); break;
     case 14: __builtin_amdgcn_s_waitcnt(vmcnt_imm(14)); break;
     case 15: __builtin_amdgcn_s_waitcnt(vmcnt_imm(15)); break;
@@ -744,21 +764,23 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
         constexpr int kW = T * G::NI;
         if constexpr (SHARE) {
             // The workgroup's waves share one record per step through a ring of R
-            // = 7 LDS slots.  Record j is made by wave j mod 8: four steps ahead it
+            // LDS slots.  Record j is made by wave j mod 8: KA steps ahead it
             // copies the step's activations (eight 1 KB copies) into slot j mod R,
-            // and once they have landed it forms the record in place (form_record)
-            // and adds 8 to arrived[slot].  Issue order: activations 0, 1, 2,
-            // weights 0, activations 3, weights 1, then per step t activations t
-            // + 4 and weights t + 2, so at step t, with only weights t + 1 still
-            // allowed in flight, weights t and activations t + 3 have landed:
-            // records 0-2 are formed before the loop and record t + 3 at step t.
-            // done[b] counts the waves that have read the record in slot b: a wave
-            // reads record t once it is formed (arrived), and the maker of record
-            // t + 4 copies into its slot once all have read record t - 3.  The
-            // slowest wave never waits (every other wave has formed and read
-            // those), so every wait ends, and the waves may drift three steps apart.
-            constexpr int kAhead = 4, kReport = 3;
-            static_assert(G::R == kAhead + kReport, "ring of records in flight and being read");
+            // and KR < KA steps ahead, once they have landed, it forms the record
+            // in place (form_record) and adds 8 to arrived[slot].  Issue order:
+            // activations 0 .. KA - 2, weights 0, activations KA - 1, weights 1,
+            // then per step t activations t + KA and weights t + 2, so at step t,
+            // with only weights t + 1 still allowed in flight, weights t and
+            // activations t + KA - 1 have landed: records 0 .. KR - 1 are formed
+            // before the loop and record t + KR at step t.  done[b] counts the
+            // waves that have read the record in slot b: a wave reads record t once
+            // it is formed (arrived), and the maker of record t + KA copies into
+            // its slot once all have read record t + KA - R.  The slowest wave
+            // never waits (every other wave has formed and read those), so every
+            // wait ends; a wave may run KR steps ahead of the maker of a record it
+            // needs, a maker R - KA steps ahead of the slowest reader (R = 7, KA =
+            // 4, KR = 3: three and three).
+            constexpr int kAhead = G::KA, kReport = G::KR;
             const auto slot = [&](int j) { return lds + G::RING_REC + (j % G::R) * G::REC; };
             const auto issue_x = [&](int j) {
                 const int64_t c0 = int64_t(s_lo + j) * 256;   // first column of the step
@@ -784,7 +806,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
             issue_w(0, s_lo);
             if (mine(kAhead - 1)) issue_x(kAhead - 1);
             if (n > 1) issue_w(1, s_lo + 1);
-            if (wv < kAhead - 1 && wv < n) {
+            if (wv < kReport && wv < n) {
                 wait_vm(n > 1 ? 2 * kW : kW);                   // this wave's activations for record wv
                 form(wv);
             }
@@ -899,9 +921,9 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
         // every split has drawn: the counter goes back to zero for the next call
         if (lane == 0) __hip_atomic_store(tp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // 2T outputs per lane (output i = lane + 64 j is n = i / 16T, row T0
-        // + i mod 16T), four splits at a time: 8T loads in flight before the
-        // first add.  A split past the last reloads the last one and adds +0
-        // instead, which leaves every sum as it is (sums start at +0);
+        // + i mod 16T), eight splits at a time: 16T loads in flight before
+        // the first add.  A split past the last reloads the last one and adds
+        // +0 instead, which leaves every sum as it is (sums start at +0);
         // outputs past k or the last row load a valid one and store nothing.
         const int nrow = int(min<int64_t>(rows - T0, 16 * T)), ns = int(gridDim.y);
         float v[2 * T];
@@ -912,16 +934,16 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
             o[j] = int64_t(min(nn, k - 1)) * rows + T0 + min(rr, nrow - 1);
             v[j] = 0.f;
         }
-        for (int sp0 = 0; sp0 < ns; sp0 += 4) {
-            float p[4][2 * T];
+        for (int sp0 = 0; sp0 < ns; sp0 += 8) {
+            float p[8][2 * T];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < 8; ++q)
 #pragma unroll
                 for (int j = 0; j < 2 * T; ++j)
                     p[q][j] = __hip_atomic_load(partial + int64_t(min(sp0 + q, ns - 1)) * k * rows + o[j],
                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < 8; ++q)
 #pragma unroll
                 for (int j = 0; j < 2 * T; ++j) v[j] += sp0 + q < ns ? p[q][j] : 0.f;
         }
@@ -935,6 +957,7 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
 
 struct BgemmShape {
     int groups, nc, nsplit, sps;
+    bool shared;   // records formed in LDS (nc = 1 only) or by the record kernel
     int64_t cost;
 };
 
@@ -945,13 +968,14 @@ struct BgemmShape {
 // over the CUs) x (steps per wave + the ring's fill), plus a few steps for
 // the cross-workgroup sum, plus a term for the activation records: waves of
 // one column split read the same record at the same step (served once by
-// the CU's cache), so a CU reads nc records per step instead of one.  Costs
-// in twentieths of a step; ties go to fewer splits.
+// the CU's cache), so a CU reads nc records per step instead of one, and
+// the per-wave-record forms run the record kernel first.  Costs in
+// twentieths of a step; ties go to fewer splits.
 template <class F>
-BgemmShape bgemm_shape(int64_t rows, int64_t cols, bool shared_only = false) {
+BgemmShape bgemm_shape(int64_t rows, int64_t cols) {
     using G = Geo<F>;
-    constexpr int kReduceCost = 60;   // the cross-workgroup sum: about three one-tile steps of one wave
-    shared_only = shared_only || std::is_same<F, BQ4K1>::value;   // the one-tile Q4_K is for shared records only
+    constexpr int kReduceCost = 20;   // the cross-workgroup sum: about one one-tile step of one wave
+    constexpr int kRecordCost = 40;   // the record kernel of the per-wave-record forms: about two steps
     BgemmShape b{};
     const int ns = int((cols + 255) / 256);
     const int64_t tiles = (rows + 16 * G::T - 1) / (16 * G::T);
@@ -964,19 +988,23 @@ BgemmShape bgemm_shape(int64_t rows, int64_t cols, bool shared_only = false) {
             if (sp > 1 && groups * (G::NW / nc) > kMaxTickets) continue;   // counters of a split
             const int64_t rounds = (groups * sp + kNumCUs - 1) / kNumCUs;
             // shared records (one column range per workgroup, where LDS allows):
-            // a fifth less per step than records loaded by every wave; a step
-            // costs in proportion to the tiles it covers
-            const bool shared = G::kShare && nc == 1;
-            if (shared_only && !shared) continue;
-            const int64_t cost = (shared ? 16 : 20) * G::T * rounds * (sps + G::S - 1) +
-                                 (sp > 1 ? kReduceCost : 0) + (shared ? 0 : G::T * rounds * sps * (nc - 1));
-            if (best < 0 || cost < best) {
-                best = cost;
-                b.groups = int(groups);
-                b.nc = nc;
-                b.nsplit = sp;
-                b.sps = sps;
-                b.cost = cost;
+            // for the K-quants a fifth less per step than records loaded by
+            // every wave; a step costs in proportion to the tiles it covers
+            for (int form = 0; form < 2; ++form) {
+                const bool shared = form == 1;
+                if (shared && !(G::kShare && nc == 1)) continue;
+                const int64_t cost = (shared ? RingOf<F>::cost : 20) * G::T * rounds * (sps + G::S - 1) +
+                                     (sp > 1 ? kReduceCost : 0) +
+                                     (shared ? 0 : G::T * rounds * sps * (nc - 1) + kRecordCost);
+                if (best < 0 || cost < best) {
+                    best = cost;
+                    b.groups = int(groups);
+                    b.nc = nc;
+                    b.nsplit = sp;
+                    b.sps = sps;
+                    b.shared = shared;
+                    b.cost = cost;
+                }
             }
         }
     }
@@ -987,7 +1015,7 @@ BgemmShape bgemm_shape(int64_t rows, int64_t cols, bool shared_only = false) {
 // bgemm_prep to the workspace.
 template <class F>
 bool shared_records(const BgemmShape &b) {
-    return Geo<F>::kShare && b.nc == 1;
+    return Geo<F>::kShare && b.nc == 1 && b.shared;
 }
 
 template <class F>
@@ -1060,22 +1088,12 @@ bool gemm_batch_type_ok(nt_qtype t) {
     return t == NT_Q8_0 || t == NT_Q4_0 || t == NT_Q4_K || t == NT_Q5_K || t == NT_Q6_K;
 }
 
-// Q4_K: two tiles per wave with per-wave records, or one tile per wave with
-// records shared through LDS where its launch shape costs less (measured at
-// k = 8: 28672 x 8192 49.6 -> 47.7 us one-tile; 8192 x 8192, a four-way
-// split between workgroups, 20.0-20.1 -> 18.7-18.8 us since the last wave
-// adds the partial sums, 21.2 us while a third kernel did).
-bool q4k_one_tile(int64_t rows, int64_t cols) {
-    const BgemmShape two = bgemm_shape<BQ4K>(rows, cols), one = bgemm_shape<BQ4K1>(rows, cols, true);
-    return one.groups > 0 && one.cost < two.cost;
-}
-
 size_t gemm_batch_workspace_bytes(nt_qtype t, int64_t rows, int64_t cols) {
     switch (t) {
     case NT_Q8_0: return workspace_for<BQ80>(rows, cols);
     case NT_Q4_0: return workspace_for<BQ40>(rows, cols);
     case NT_Q5_K: return workspace_for<BQ5K>(rows, cols);
-    case NT_Q4_K: return q4k_one_tile(rows, cols) ? workspace_for<BQ4K1>(rows, cols) : workspace_for<BQ4K>(rows, cols);
+    case NT_Q4_K: return workspace_for<BQ4K>(rows, cols);
     case NT_Q6_K: return workspace_for<BQ6K>(rows, cols);
     default: return 0;
     }
@@ -1089,9 +1107,7 @@ hipError_t launch_gemm_batch(nt_qtype t, const void *W, int64_t rows, int64_t co
     case NT_Q8_0: return run_bgemm<BQ80>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);
     case NT_Q4_0: return run_bgemm<BQ40>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);
     case NT_Q5_K: return run_bgemm<BQ5K>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);
-    case NT_Q4_K:
-        if (q4k_one_tile(rows, cols)) return run_bgemm<BQ4K1>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);
-        return run_bgemm<BQ4K>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);
+    case NT_Q4_K: return run_bgemm<BQ4K>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);
     case NT_Q6_K: return run_bgemm<BQ6K>(W, row_bytes, rows, cols, nblk, X, k, Y, accumulate, ws, st);
     default: return hipErrorInvalidValue;
     }

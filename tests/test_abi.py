@@ -91,7 +91,8 @@ def test_gemm_batch_argument_errors():
     # per column range
     rec = {nt.Q4_K: 8736, nt.Q5_K: 8736, nt.Q6_K: 8224, nt.Q8_0: 8224, nt.Q4_0: 8224}
     C = 16384
-    assert wsb(nt.Q8_0, 1, 32) == C + 8224          # one range, records from the first kernel
+    assert wsb(nt.Q4_0, 1, 32) == C + 8224          # one range, records from the first kernel
+    assert wsb(nt.Q8_0, 1, 32) == C                 # one range, records formed in LDS
     for t, rows, cols in [(nt.Q4_K, 8192, 8192), (nt.Q6_K, 8192, 28672), (nt.Q8_0, 4096, 4096),
                           (nt.Q4_K, 3, 65536), (nt.Q5_K, 40040, 2048), (nt.Q4_0, 600, 8960)]:
         ns = -(-cols // 256)
@@ -102,9 +103,8 @@ def test_gemm_batch_argument_errors():
                 break
         else:
             raise AssertionError((t, rows, cols, extra))
-    # enough rows: the waves of a workgroup split the columns, no partial sums
-    assert wsb(nt.Q8_0, 4096, 4096) == C + 16 * 8224
-    assert wsb(nt.Q4_K, 28672, 8192) == C                # records formed in LDS, no split
+    assert wsb(nt.Q8_0, 4096, 4096) == C + 8 * 8 * 4096 * 4   # records in LDS, eight-way split
+    assert wsb(nt.Q4_K, 28672, 8192) == C                # records in LDS, no split
     assert wsb(nt.Q4_K, 3, 65536) > C + 3 * 8 * 4 * 2   # a few rows: split between workgroups
     assert wsb(nt.F32, 4, 256) == 0 and wsb(nt.Q4_K, 4, 100) == 0 and wsb(nt.Q4_K, 4, 65536 + 256) == 0
     assert wsb(nt.Q4_K, -1, 256) == 0
