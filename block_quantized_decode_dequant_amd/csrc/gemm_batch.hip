@@ -167,6 +167,9 @@ struct BQ80 {
 struct BQ4K {
     static constexpr bool kMin = true;
     static constexpr int kStepBytes = 144, kTiles = 1;   // one tile: LDS room for the record ring
+    // wide form: sixteen waves (four per SIMD), two ring stages, seven record slots
+    static constexpr int kWideWaves = 16, kWideStages = 2;
+    static constexpr int kWideRingSlots = 7, kWideRingAhead = 4, kWideRingReport = 3, kWideCost = 29;
     struct Raw { u32x4n h; u32x2n q[4]; };
     __host__ __device__ static int elem(int m, int g, int i) { return 32 * (m >> 1) + 8 * g + 4 * (m & 1) + perm4(i); }
     // the eight (m, g) whose values lie in the step's 32-column block jb:
@@ -271,6 +274,9 @@ struct BQ40 {
 struct BQ5K {
     static constexpr bool kMin = true;
     static constexpr int kStepBytes = 176, kTiles = 1;
+    // wide form as for Q6_K
+    static constexpr int kWideWaves = 16, kWideStages = 2;
+    static constexpr int kWideRingSlots = 3, kWideRingAhead = 2, kWideRingReport = 1, kWideCost = 29;
     struct Raw { u32x4 h, qh, q0, q1; };
     // lane group g takes code bytes [16g, 16g + 16) and [64 + 16g, 64 + 16g +
     // 16); MFMA m uses word m / 2 of those eight (low nibbles for even m, high
@@ -348,6 +354,9 @@ struct BQ5K {
 struct BQ6K {
     static constexpr bool kMin = false;
     static constexpr int kStepBytes = 210, kTiles = 1;
+    // wide form: sixteen waves, two ring stages, three record slots (128 KB of weight rings)
+    static constexpr int kWideWaves = 16, kWideStages = 2;
+    static constexpr int kWideRingSlots = 3, kWideRingAhead = 2, kWideRingReport = 1, kWideCost = 29;
     // word pairs at byte offsets 4g + 16j (ql, j < 8), 128 + 4g + 16j (qh,
     // j < 4) from the word-aligned block start; scale words 192..208 (the
     // last also holds d)
@@ -418,24 +427,50 @@ typedef uint32_t u32x4a __attribute__((ext_vector_type(4)));   // 16-byte aligne
 // sit Lp bytes apart in LDS, an odd number of granules, so the 16 lanes that
 // read one offset of 16 rows hit distinct banks; a tile takes NI whole copy
 // instructions (the lanes past the 16 rows fill padding).
-// Record ring of the shared-record form: slots, how many steps ahead a
-// step's activations are copied and its record formed, and the launch-shape
-// cost of one of its steps in twentieths of a per-wave-record step (a format
-// may set its own with kRingSlots, kRingAhead, kRingReport, kShareCost).
-template <class F, class = void>
+// Launch forms of the main kernel: 0 = per-wave records (from the record
+// kernel), 1 = shared records formed in LDS, eight waves (two per SIMD) and
+// three weight-ring stages, 2 = shared records with the wide pipeline a
+// format may set (kWideWaves waves, kWideStages stages, its own record ring:
+// more waves per SIMD hide more latency on long column ranges).
+constexpr int kOwn = 0, kShared = 1, kWide = 2;
+
+// Record ring of a shared-record form: slots, how many steps ahead a step's
+// activations are copied and its record formed, and the launch-shape cost of
+// one of its steps in twentieths of a per-wave-record step (a format may set
+// its own with kRingSlots, kRingAhead, kRingReport, kShareCost; the wide
+// form with kWideRingSlots, kWideRingAhead, kWideRingReport, kWideCost).
+template <class F, int FORM, class = void>
 struct RingOf {
     static constexpr int slots = 7, ahead = 4, report = 3, cost = 16;
 };
 template <class F>
-struct RingOf<F, std::void_t<decltype(F::kRingSlots)>> {
+struct RingOf<F, kShared, std::void_t<decltype(F::kRingSlots)>> {
     static constexpr int slots = F::kRingSlots, ahead = F::kRingAhead, report = F::kRingReport, cost = F::kShareCost;
 };
-
 template <class F>
+struct RingOf<F, kWide, std::void_t<decltype(F::kWideRingSlots)>> {
+    static constexpr int slots = F::kWideRingSlots, ahead = F::kWideRingAhead, report = F::kWideRingReport,
+                         cost = F::kWideCost;
+};
+
+// Waves per workgroup and weight-ring stages of a launch form.
+template <class F, int FORM, class = void>
+struct PipeOf {
+    static constexpr int waves = 8, stages = 3;
+    static constexpr bool exists = FORM != kWide;
+};
+template <class F>
+struct PipeOf<F, kWide, std::void_t<decltype(F::kWideWaves)>> {
+    static constexpr int waves = F::kWideWaves, stages = F::kWideStages;
+    static constexpr bool exists = true;
+};
+
+template <class F, int FORM = kOwn>
 struct Geo {
     static constexpr int T = F::kTiles;
-    static constexpr int S = 3;                                  // ring stages: two steps copied ahead
-    static constexpr int NW = 8;                                 // waves per workgroup (two per SIMD)
+    static constexpr int S = PipeOf<F, FORM>::stages;            // ring stages: S - 1 steps copied ahead
+    static constexpr int NW = PipeOf<F, FORM>::waves;            // waves per workgroup
+    static_assert(NW % 4 == 0 && NW <= 16 && (S == 2 || S == 3), "launch form");
     static constexpr int L = F::kStepBytes;
     static constexpr int Lc = (L + 15 + 15) / 16 * 16;
     static constexpr int Lp = ((Lc / 16) & 1) ? Lc : Lc + 16;
@@ -450,13 +485,14 @@ struct Geo {
     // activations are copied KA steps ahead and its record formed KR steps
     // ahead (fits for Q8_0 with four slots, Q4_K one-tile, Q5_K and Q6_K with
     // seven)
-    static constexpr int KA = RingOf<F>::ahead, KR = RingOf<F>::report;
-    static constexpr int R = RingOf<F>::slots;
+    static constexpr int KA = RingOf<F, FORM>::ahead, KR = RingOf<F, FORM>::report;
+    static constexpr int R = RingOf<F, FORM>::slots;
     static_assert(R > KA && KA > KR && KR >= 0 && 2 * R <= 16, "record ring");
     static constexpr int RING_REC = LDS;                         // offset of the record ring
     static constexpr int CNT = LDS + R * REC;                    // offset of the counters
     static constexpr int LDS_SH = CNT + 64;
-    static constexpr bool kShare = LDS_SH <= 160 * 1024;
+    // this shared-record form exists for the format (its rings fit in LDS)
+    static constexpr bool kShare = FORM != kOwn && PipeOf<F, FORM>::exists && LDS_SH <= 160 * 1024;
 };
 
 // Activation records, one workgroup per 256-column step s.  Record layout
@@ -677,13 +713,14 @@ __device__ __forceinline__ void form_record(uint8_t *slot, int lane, int64_t col
 // partial[y][n][row], where the last of the nsplit waves that cover the same
 // rows adds them in workgroup order (below).  SHARE (nc = 1 only): the
 // records come through a workgroup ring in LDS instead (below).
-template <class F, bool SHARE, bool SPLIT>
-__global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__restrict__ W, int64_t row_bytes, int rows,
+template <class F, int FORM, bool SPLIT>
+__global__ void __launch_bounds__((64 * Geo<F, FORM>::NW), 1) bgemm(const uint8_t *__restrict__ W, int64_t row_bytes, int rows,
                                                           int nsteps, int nblk, const uint8_t *__restrict__ rec,
                                                           int nc, int sps, float *__restrict__ Y, int k, int accumulate,
                                                           float *__restrict__ partial, uint32_t *__restrict__ tickets,
                                                           const float *__restrict__ X, int64_t cols) {
-    using G = Geo<F>;
+    using G = Geo<F, FORM>;
+    constexpr bool SHARE = FORM != kOwn;
     constexpr int T = G::T;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
@@ -798,31 +835,35 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
                 form_record<F>(slot(j), lane, int64_t(s_lo + j) * 256, k, cols);
                 __builtin_amdgcn_s_waitcnt(kLgkm0);   // the record is in LDS
                 __builtin_amdgcn_sched_barrier(0);
-                lds_count(&cnt[j % G::R], 8u);
+                lds_count(&cnt[j % G::R], uint32_t(G::NW));
             };
             const auto mine = [&](int j) { return j < n && j % G::NW == wv; };
+            constexpr int kWA = G::S - 1;                        // weights copied kWA steps ahead
+            constexpr uint32_t kAll = uint32_t(G::NW);
             for (int j = 0; j < kAhead - 1; ++j)
                 if (mine(j)) issue_x(j);
             issue_w(0, s_lo);
             if (mine(kAhead - 1)) issue_x(kAhead - 1);
-            if (n > 1) issue_w(1, s_lo + 1);
+            if (kWA > 1 && n > 1) issue_w(1, s_lo + 1);
             if (wv < kReport && wv < n) {
-                wait_vm(n > 1 ? 2 * kW : kW);                   // this wave's activations for record wv
+                wait_vm(kWA > 1 && n > 1 ? 2 * kW : kW);        // this wave's activations for record wv
                 form(wv);
             }
-            // the two waves of a SIMD (w, w + 4) take turns at the higher issue
+            // the waves of a SIMD (w, w + 4, ...) take turns at the higher issue
             // priority, one step each, so they advance at the same pace and
-            // neither waits long for the other at the counters
-            const bool first_slot = wv < 4;
+            // none waits long for another at the counters
             for (int t = 0; t < n; ++t) {
                 const int b = t % G::R, jn = t + kAhead;
-                if (first_slot == ((t & 1) == 0)) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
+                if ((G::NW == 8 ? (wv < 4) == ((t & 1) == 0) : ((wv >> 2) + t) % (G::NW / 4) == 0))
+                    __builtin_amdgcn_s_setprio(1);
+                else
+                    __builtin_amdgcn_s_setprio(0);
                 // both counters this step waits on, read before the weight wait
                 const uint32_t arrived0 = lds_read_count(&cnt[b]);
                 const uint32_t done0 = lds_read_count(&cnt[G::R + jn % G::R]);
-                wait_vm(t + 1 < n ? kW : 0);                      // weights t, activations t + 3 landed
+                wait_vm(t + 1 < n ? (kWA - 1) * kW : 0);          // weights t, activations t + KA - 1 landed
                 if (mine(t + kReport)) form(t + kReport);
-                lds_wait_count(&cnt[b], 8u * uint32_t(t / G::R + 1), arrived0);
+                lds_wait_count(&cnt[b], kAll * uint32_t(t / G::R + 1), arrived0);
                 const uint8_t *const rc = slot(t);
                 XRegs xr;
 #pragma unroll
@@ -831,10 +872,10 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
                 xr.up = *reinterpret_cast<const f4 *>(rc + G::REC - 32 + 16 * (g & 1));
                 // the next copies go out while those reads are in flight
                 if (mine(jn)) {
-                    if (jn >= G::R) lds_wait_count(&cnt[G::R + jn % G::R], 8u * uint32_t(jn / G::R), done0);
+                    if (jn >= G::R) lds_wait_count(&cnt[G::R + jn % G::R], kAll * uint32_t(jn / G::R), done0);
                     issue_x(jn);
                 }
-                if (t + 2 < n) issue_w((t + 2) % G::S, s_lo + t + 2);
+                if (t + kWA < n) issue_w((t + kWA) % G::S, s_lo + t + kWA);
                 __builtin_amdgcn_s_waitcnt(kLgkm0);               // record t is in registers
                 __builtin_amdgcn_sched_barrier(0);
                 lds_count(&cnt[G::R + b]);
@@ -957,44 +998,51 @@ __global__ void __launch_bounds__(64 * Geo<F>::NW, 1) bgemm(const uint8_t *__res
 
 struct BgemmShape {
     int groups, nc, nsplit, sps;
-    bool shared;   // records formed in LDS (nc = 1 only) or by the record kernel
+    int form;      // kOwn (records from the record kernel), kShared or kWide (formed in LDS; nc = 1)
     int64_t cost;
 };
 
-// Launch shape: one workgroup of NW waves per CU.  The columns are split
-// nc ways between the waves of a workgroup (their sums meet in LDS) and/or
-// nsplit ways between workgroups (partial sums through the workspace, added
-// by the last wave to finish).  The choice minimises (rounds of workgroups
-// over the CUs) x (steps per wave + the ring's fill), plus a few steps for
-// the cross-workgroup sum, plus a term for the activation records: waves of
-// one column split read the same record at the same step (served once by
-// the CU's cache), so a CU reads nc records per step instead of one, and
-// the per-wave-record forms run the record kernel first.  Costs in
-// twentieths of a step; ties go to fewer splits.
+// Launch shape: one workgroup of NW waves per CU, in one of the launch
+// forms.  The columns are split nc ways between the waves of a workgroup
+// (per-wave-record form only: their sums meet in LDS) and/or nsplit ways
+// between workgroups (partial sums through the workspace, added by the last
+// wave to finish).  The choice minimises (rounds of workgroups over the
+// CUs) x (steps per wave + the ring's fill) x the form's cost per step,
+// plus a few steps for the cross-workgroup sum, plus, for the
+// per-wave-record form, a term for the activation records (waves of one
+// column split read the same record at the same step, served once by the
+// CU's cache, so a CU reads nc records per step instead of one) and the
+// record kernel.  Costs in twentieths of a per-wave-record step of one
+// tile; ties go to the earlier form and fewer splits.  The shared and wide
+// forms' step costs are measured ratios (k = 8: the wide form took Q4_K
+// 28672 x 8192 39.2-39.3 -> 38.2 us and Q6_K 8192 x 28672 53.8-54.0 ->
+// 49.8 us, and lost at 8192 x 8192, where it needs eight splits).
 template <class F>
 BgemmShape bgemm_shape(int64_t rows, int64_t cols) {
-    using G = Geo<F>;
     constexpr int kReduceCost = 20;   // the cross-workgroup sum: about one one-tile step of one wave
     constexpr int kRecordCost = 40;   // the record kernel of the per-wave-record forms: about two steps
     BgemmShape b{};
-    const int ns = int((cols + 255) / 256);
-    const int64_t tiles = (rows + 16 * G::T - 1) / (16 * G::T);
     int64_t best = -1;
-    for (int sp = 1; sp <= std::min(ns, 64); ++sp) {
-        for (int nc = 1; nc <= G::NW; nc *= 2) {
-            const int total = nc * sp, sps = (ns + total - 1) / total;
-            if ((ns + sps - 1) / sps != total) continue;   // some split would have no step
-            const int64_t groups = (tiles + G::NW / nc - 1) / (G::NW / nc);
-            if (sp > 1 && groups * (G::NW / nc) > kMaxTickets) continue;   // counters of a split
-            const int64_t rounds = (groups * sp + kNumCUs - 1) / kNumCUs;
-            // shared records (one column range per workgroup, where LDS allows):
-            // for the K-quants a fifth less per step than records loaded by
-            // every wave; a step costs in proportion to the tiles it covers
-            for (int form = 0; form < 2; ++form) {
-                const bool shared = form == 1;
-                if (shared && !(G::kShare && nc == 1)) continue;
-                const int64_t cost = (shared ? RingOf<F>::cost : 20) * G::T * rounds * (sps + G::S - 1) +
-                                     (sp > 1 ? kReduceCost : 0) +
+    const int ns = int((cols + 255) / 256);
+    // one launch form: per-wave records (any nc) or shared records (nc = 1)
+    const auto consider = [&](auto geo, int form) {
+        using G = decltype(geo);
+        const bool shared = form != kOwn;
+        const int step_cost = form == kOwn ? 20 : form == kShared ? RingOf<F, kShared>::cost : RingOf<F, kWide>::cost;
+        const int64_t tiles = (rows + 16 * G::T - 1) / (16 * G::T);
+        for (int sp = 1; sp <= std::min(ns, 64); ++sp) {
+            for (int nc = 1; nc <= (shared ? 1 : G::NW); nc *= 2) {
+                const int total = nc * sp, sps = (ns + total - 1) / total;
+                if ((ns + sps - 1) / sps != total) continue;   // some split would have no step
+                const int64_t groups = (tiles + G::NW / nc - 1) / (G::NW / nc);
+                if (sp > 1 && groups * (G::NW / nc) > kMaxTickets) continue;   // counters of a split
+                const int64_t rounds = (groups * sp + kNumCUs - 1) / kNumCUs;
+                // a step of a wave costs in proportion to the tiles it covers; the
+                // shared forms have no record kernel and their own cost per step
+                // (the wide form's covers twice the rows per workgroup, and its
+                // start costs one step more)
+                const int64_t cost = int64_t(step_cost) * G::T * rounds * (sps + G::S - 1) +
+                                     (sp > 1 ? kReduceCost : 0) + (form == kWide ? 20 : 0) +
                                      (shared ? 0 : G::T * rounds * sps * (nc - 1) + kRecordCost);
                 if (best < 0 || cost < best) {
                     best = cost;
@@ -1002,12 +1050,15 @@ BgemmShape bgemm_shape(int64_t rows, int64_t cols) {
                     b.nc = nc;
                     b.nsplit = sp;
                     b.sps = sps;
-                    b.shared = shared;
+                    b.form = form;
                     b.cost = cost;
                 }
             }
         }
-    }
+    };
+    consider(Geo<F, kOwn>{}, kOwn);
+    if constexpr (Geo<F, kShared>::kShare) consider(Geo<F, kShared>{}, kShared);
+    if constexpr (Geo<F, kWide>::kShare) consider(Geo<F, kWide>{}, kWide);
     return b;
 }
 
@@ -1015,7 +1066,7 @@ BgemmShape bgemm_shape(int64_t rows, int64_t cols) {
 // bgemm_prep to the workspace.
 template <class F>
 bool shared_records(const BgemmShape &b) {
-    return Geo<F>::kShare && b.nc == 1 && b.shared;
+    return b.form != kOwn;
 }
 
 template <class F>
@@ -1028,14 +1079,29 @@ size_t workspace_for(int64_t rows, int64_t cols) {
 
 // The main kernel in one of its four forms (shared records or not; columns
 // split between workgroups or not).
-template <class F, bool SHARE, bool SPLIT>
-hipError_t launch_main(dim3 grid, hipStream_t st, const uint8_t *W, int64_t row_bytes, int64_t rows, int ns,
-                       int64_t nblk, const uint8_t *rec, const BgemmShape &b, float *Y, int k, int accumulate,
-                       float *partial, uint32_t *tickets, const float *X, int64_t cols) {
-    using G = Geo<F>;
-    hipLaunchKernelGGL((bgemm<F, SHARE, SPLIT>), grid, dim3(64 * G::NW), SHARE ? G::LDS_SH : G::LDS, st, W, row_bytes,
-                       int(rows), ns, int(nblk), rec, b.nc, b.sps, Y, k, accumulate, partial, tickets, X, cols);
+template <class F, int FORM, bool SPLIT>
+hipError_t launch_main(const BgemmShape &b, hipStream_t st, const uint8_t *W, int64_t row_bytes, int64_t rows,
+                       int ns, int64_t nblk, const uint8_t *rec, float *Y, int k, int accumulate, float *partial,
+                       uint32_t *tickets, const float *X, int64_t cols) {
+    using G = Geo<F, FORM>;
+    hipLaunchKernelGGL((bgemm<F, FORM, SPLIT>), dim3(unsigned(b.groups), unsigned(b.nsplit)), dim3(64 * G::NW),
+                       FORM != kOwn ? G::LDS_SH : G::LDS, st, W, row_bytes, int(rows), ns, int(nblk), rec, b.nc,
+                       b.sps, Y, k, accumulate, partial, tickets, X, cols);
     return hipGetLastError();
+}
+
+// More than 64 KB of dynamic LDS: allowed once per kernel (both split
+// variants of one form).
+template <class F, int FORM>
+hipError_t allow_lds() {
+    using G = Geo<F, FORM>;
+    const int bytes = FORM != kOwn ? G::LDS_SH : G::LDS;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&bgemm<F, FORM, false>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&bgemm<F, FORM, true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    return e;
 }
 
 template <class F>
@@ -1053,33 +1119,37 @@ hipError_t run_bgemm(const void *W, int64_t row_bytes, int64_t rows, int64_t col
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
     if (!((done.load(std::memory_order_acquire) >> dev) & 1)) {
-        const auto allow = [](const void *fn, int bytes) {
-            return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-        };
-        hipError_t e = allow(reinterpret_cast<const void *>(&bgemm<F, false, false>), G::LDS);
-        if (e == hipSuccess) e = allow(reinterpret_cast<const void *>(&bgemm<F, false, true>), G::LDS);
-        if constexpr (G::kShare) {
-            if (e == hipSuccess) e = allow(reinterpret_cast<const void *>(&bgemm<F, true, false>), G::LDS_SH);
-            if (e == hipSuccess) e = allow(reinterpret_cast<const void *>(&bgemm<F, true, true>), G::LDS_SH);
+        hipError_t e = allow_lds<F, kOwn>();
+        if constexpr (Geo<F, kShared>::kShare) {
+            if (e == hipSuccess) e = allow_lds<F, kShared>();
+        }
+        if constexpr (Geo<F, kWide>::kShare) {
+            if (e == hipSuccess) e = allow_lds<F, kWide>();
         }
         if (e != hipSuccess) return e;
         done.fetch_or(uint64_t(1) << dev, std::memory_order_release);
     }
-    const dim3 grid(unsigned(b.groups), unsigned(b.nsplit));
     const uint8_t *const w8 = static_cast<const uint8_t *>(W);
-    if constexpr (G::kShare) {
-        if (share)
-            return split ? launch_main<F, true, true>(grid, st, w8, row_bytes, rows, ns, nblk, rec, b, Y, k, accumulate,
-                                                      partial, tickets, X, cols)
-                         : launch_main<F, true, false>(grid, st, w8, row_bytes, rows, ns, nblk, rec, b, Y, k,
-                                                       accumulate, partial, tickets, X, cols);
+    if constexpr (Geo<F, kShared>::kShare) {
+        if (b.form == kShared)
+            return split ? launch_main<F, kShared, true>(b, st, w8, row_bytes, rows, ns, nblk, rec, Y, k, accumulate,
+                                                         partial, tickets, X, cols)
+                         : launch_main<F, kShared, false>(b, st, w8, row_bytes, rows, ns, nblk, rec, Y, k, accumulate,
+                                                          partial, tickets, X, cols);
+    }
+    if constexpr (Geo<F, kWide>::kShare) {
+        if (b.form == kWide)
+            return split ? launch_main<F, kWide, true>(b, st, w8, row_bytes, rows, ns, nblk, rec, Y, k, accumulate,
+                                                       partial, tickets, X, cols)
+                         : launch_main<F, kWide, false>(b, st, w8, row_bytes, rows, ns, nblk, rec, Y, k, accumulate,
+                                                        partial, tickets, X, cols);
     }
     hipLaunchKernelGGL(bgemm_prep<F>, dim3(unsigned(ns)), dim3(256), 0, st, X, cols, k, rec);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    return split ? launch_main<F, false, true>(grid, st, w8, row_bytes, rows, ns, nblk, rec, b, Y, k, accumulate,
-                                               partial, tickets, X, cols)
-                 : launch_main<F, false, false>(grid, st, w8, row_bytes, rows, ns, nblk, rec, b, Y, k, accumulate,
-                                                partial, tickets, X, cols);
+    return split ? launch_main<F, kOwn, true>(b, st, w8, row_bytes, rows, ns, nblk, rec, Y, k, accumulate, partial,
+                                              tickets, X, cols)
+                 : launch_main<F, kOwn, false>(b, st, w8, row_bytes, rows, ns, nblk, rec, Y, k, accumulate, partial,
+                                               tickets, X, cols);
 }
 
 }  // namespace

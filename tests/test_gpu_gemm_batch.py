@@ -105,11 +105,13 @@ def test_gemm_batch_launch_shapes(t, rows, cols, k):
 
 def test_gemm_batch_tall_and_wide_matrices():
     # 40040 rows of 2048 columns (ragged last workgroup, with a partial
-    # 16-row tile; more workgroups than CUs), and 600 rows of 8960 columns
-    # (35 steps split between workgroups: partial sums added by the third
-    # kernel)
+    # 16-row tile; more workgroups than CUs; the K-quants take the
+    # sixteen-wave shared-record form, split three ways), and 600 rows of
+    # 8960 columns (35 steps split between workgroups: partial sums added by
+    # the last wave of each row set)
     _case(O.Q4_K, 40040, 2048, 8, seed=31)
     _case(O.Q6_K, 40040, 2048, 3, seed=33)
+    _case(O.Q5_K, 40040, 2048, 4, seed=34)
     _case(O.Q8_0, 600, 8960, 5, seed=32)
 
 
