@@ -167,9 +167,10 @@ struct BQ80 {
 struct BQ4K {
     static constexpr bool kMin = true;
     static constexpr int kStepBytes = 144, kTiles = 1;   // one tile: LDS room for the record ring
-    // wide form: sixteen waves (four per SIMD), two ring stages, seven record slots
-    static constexpr int kWideWaves = 16, kWideStages = 2;
-    static constexpr int kWideRingSlots = 7, kWideRingAhead = 4, kWideRingReport = 3, kWideCost = 29;
+    static constexpr bool kAligned = true;                // 144-byte blocks
+    // wide form: sixteen waves (four per SIMD), three ring stages (108 KB), five record slots
+    static constexpr int kWideWaves = 16, kWideStages = 3;
+    static constexpr int kWideRingSlots = 5, kWideRingAhead = 3, kWideRingReport = 2, kWideCost = 27;
     struct Raw { u32x4n h; u32x2n q[4]; };
     __host__ __device__ static int elem(int m, int g, int i) { return 32 * (m >> 1) + 8 * g + 4 * (m & 1) + perm4(i); }
     // the eight (m, g) whose values lie in the step's 32-column block jb:
@@ -274,9 +275,10 @@ struct BQ40 {
 struct BQ5K {
     static constexpr bool kMin = true;
     static constexpr int kStepBytes = 176, kTiles = 1;
-    // wide form as for Q6_K
+    static constexpr bool kAligned = true;                // 176-byte blocks
+    // wide form: sixteen waves, two ring stages (88 KB), seven record slots
     static constexpr int kWideWaves = 16, kWideStages = 2;
-    static constexpr int kWideRingSlots = 3, kWideRingAhead = 2, kWideRingReport = 1, kWideCost = 29;
+    static constexpr int kWideRingSlots = 7, kWideRingAhead = 4, kWideRingReport = 3, kWideCost = 29;
     struct Raw { u32x4 h, qh, q0, q1; };
     // lane group g takes code bytes [16g, 16g + 16) and [64 + 16g, 64 + 16g +
     // 16); MFMA m uses word m / 2 of those eight (low nibbles for even m, high
@@ -425,8 +427,10 @@ typedef uint32_t u32x4a __attribute__((ext_vector_type(4)));   // 16-byte aligne
 // step start: they cover the L bytes of the step whatever its offset in the
 // granule, and each copy instruction moves 64 whole granules (1 KB).  Rows
 // sit Lp bytes apart in LDS, an odd number of granules, so the 16 lanes that
-// read one offset of 16 rows hit distinct banks; a tile takes NI whole copy
-// instructions (the lanes past the 16 rows fill padding).
+// read one offset of 16 rows hit distinct banks; a tile takes NI copy
+// instructions (the lanes past the 16 rows fill padding, or, where every
+// step starts 16-byte aligned, are left out of the last one, so a tile takes
+// exactly 16 Lp bytes).
 // Launch forms of the main kernel: 0 = per-wave records (from the record
 // kernel), 1 = shared records formed in LDS, eight waves (two per SIMD) and
 // three weight-ring stages, 2 = shared records with the wide pipeline a
@@ -453,6 +457,17 @@ struct RingOf<F, kWide, std::void_t<decltype(F::kWideRingSlots)>> {
                          cost = F::kWideCost;
 };
 
+// Formats whose 256-column steps all start 16-byte aligned (blocks a
+// multiple of 16 bytes) copy exactly their tile rows (kAligned).
+template <class F, class = void>
+struct AlignedOf {
+    static constexpr bool value = false;
+};
+template <class F>
+struct AlignedOf<F, std::void_t<decltype(F::kAligned)>> {
+    static constexpr bool value = F::kAligned;
+};
+
 // Waves per workgroup and weight-ring stages of a launch form.
 template <class F, int FORM, class = void>
 struct PipeOf {
@@ -472,10 +487,12 @@ struct Geo {
     static constexpr int NW = PipeOf<F, FORM>::waves;            // waves per workgroup
     static_assert(NW % 4 == 0 && NW <= 16 && (S == 2 || S == 3), "launch form");
     static constexpr int L = F::kStepBytes;
-    static constexpr int Lc = (L + 15 + 15) / 16 * 16;
+    static constexpr bool AL = AlignedOf<F>::value;              // every step starts 16-byte aligned
+    static constexpr int Lc = AL ? L : (L + 15 + 15) / 16 * 16;
     static constexpr int Lp = ((Lc / 16) & 1) ? Lc : Lc + 16;
     static constexpr int NI = (16 * Lp + 1023) / 1024;           // copy instructions per tile
-    static constexpr int TB = NI * 1024;                         // LDS bytes of one tile
+    static constexpr int TB = AL ? 16 * Lp : NI * 1024;          // LDS bytes of one tile
+    static constexpr int LAST = AL ? (16 * Lp - 1024 * (NI - 1)) / 16 : 64;   // lanes of the last copy
     static constexpr int WAVE = S * T * TB;                      // LDS bytes of one wave's ring
     static constexpr int LDS = NW * WAVE;
     static constexpr int REC = 8192 + (F::kMin ? 512 : 0) + 32;  // activation record of one step
@@ -769,7 +786,9 @@ __global__ void __launch_bounds__((64 * Geo<F, FORM>::NW), 1) bgemm(const uint8_
             for (int u = 0; u < T; ++u) {
                 const uint32_t dst = lds_addr(ring + (b * T + u) * G::TB);
 #pragma unroll
-                for (int i = 0; i < G::NI; ++i) dma<16>(wbase, min((crel[u][i] + sL) & ~15u, lim), dst + 1024 * i);
+                for (int i = 0; i < G::NI; ++i)
+                    if (i + 1 < G::NI || G::LAST == 64 || lane < G::LAST)
+                        dma<16>(wbase, min((crel[u][i] + sL) & ~15u, lim), dst + 1024 * i);
             }
         };
         uint32_t rlo[T];                                                   // low bits of this lane's row starts
