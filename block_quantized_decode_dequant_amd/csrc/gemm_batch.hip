@@ -107,11 +107,11 @@ __device__ __forceinline__ float ubyte(uint32_t w, int k) { return float((w >> (
 struct BQ80 {
     static constexpr bool kMin = false;
     static constexpr int kStepBytes = 272, kTiles = 1;
-    // 120 KB of weight rings leave room for four record slots; a Q8_0 step
+    // 114 KB of weight rings leave room for five record slots; a Q8_0 step
     // reads its own records cheaply, so forming them costs slightly more
     // (measured at k = 8: 14336 x 4096 25.8 -> 22.1 us shared, 4096 x 14336
     // 25.5 -> 21.1, 128256 x 4096 164-168 -> 170, 4096 x 4096 12.5 either way)
-    static constexpr int kRingSlots = 4, kRingAhead = 3, kRingReport = 2, kShareCost = 21;
+    static constexpr int kRingSlots = 5, kRingAhead = 3, kRingReport = 2, kShareCost = 21;
     struct Raw { u32x3 v[8]; };
     __host__ __device__ static int elem(int m, int g, int i) { return 32 * (m >> 1) + 8 * g + 4 * (m & 1) + perm4(i); }
     __host__ __device__ static void blk(int jb, int e, int &m, int &g, int &o) {   // as for BQ4K
@@ -356,9 +356,9 @@ struct BQ5K {
 struct BQ6K {
     static constexpr bool kMin = false;
     static constexpr int kStepBytes = 210, kTiles = 1;
-    // wide form: sixteen waves, two ring stages, three record slots (128 KB of weight rings)
+    // wide form: sixteen waves, two ring stages (120 KB), four record slots
     static constexpr int kWideWaves = 16, kWideStages = 2;
-    static constexpr int kWideRingSlots = 3, kWideRingAhead = 2, kWideRingReport = 1, kWideCost = 29;
+    static constexpr int kWideRingSlots = 4, kWideRingAhead = 3, kWideRingReport = 2, kWideCost = 29;
     // word pairs at byte offsets 4g + 16j (ql, j < 8), 128 + 4g + 16j (qh,
     // j < 4) from the word-aligned block start; scale words 192..208 (the
     // last also holds d)
@@ -428,9 +428,9 @@ typedef uint32_t u32x4a __attribute__((ext_vector_type(4)));   // 16-byte aligne
 // granule, and each copy instruction moves 64 whole granules (1 KB).  Rows
 // sit Lp bytes apart in LDS, an odd number of granules, so the 16 lanes that
 // read one offset of 16 rows hit distinct banks; a tile takes NI copy
-// instructions (the lanes past the 16 rows fill padding, or, where every
-// step starts 16-byte aligned, are left out of the last one, so a tile takes
-// exactly 16 Lp bytes).
+// instructions, the lanes past the 16 rows left out of the last one, so a
+// tile takes exactly 16 Lp bytes.  Where every step starts 16-byte aligned
+// (kAligned) a row is just the L bytes of the step.
 // Launch forms of the main kernel: 0 = per-wave records (from the record
 // kernel), 1 = shared records formed in LDS, eight waves (two per SIMD) and
 // three weight-ring stages, 2 = shared records with the wide pipeline a
@@ -491,8 +491,8 @@ struct Geo {
     static constexpr int Lc = AL ? L : (L + 15 + 15) / 16 * 16;
     static constexpr int Lp = ((Lc / 16) & 1) ? Lc : Lc + 16;
     static constexpr int NI = (16 * Lp + 1023) / 1024;           // copy instructions per tile
-    static constexpr int TB = AL ? 16 * Lp : NI * 1024;          // LDS bytes of one tile
-    static constexpr int LAST = AL ? (16 * Lp - 1024 * (NI - 1)) / 16 : 64;   // lanes of the last copy
+    static constexpr int TB = 16 * Lp;                           // LDS bytes of one tile
+    static constexpr int LAST = (TB - 1024 * (NI - 1)) / 16;     // lanes of the last copy
     static constexpr int WAVE = S * T * TB;                      // LDS bytes of one wave's ring
     static constexpr int LDS = NW * WAVE;
     static constexpr int REC = 8192 + (F::kMin ? 512 : 0) + 32;  // activation record of one step
@@ -787,7 +787,7 @@ __global__ void __launch_bounds__((64 * Geo<F, FORM>::NW), 1) bgemm(const uint8_
                 const uint32_t dst = lds_addr(ring + (b * T + u) * G::TB);
 #pragma unroll
                 for (int i = 0; i < G::NI; ++i)
-                    if (i + 1 < G::NI || G::LAST == 64 || lane < G::LAST)
+                    if (i + 1 < G::NI || lane < G::LAST)
                         dma<16>(wbase, min((crel[u][i] + sL) & ~15u, lim), dst + 1024 * i);
             }
         };
