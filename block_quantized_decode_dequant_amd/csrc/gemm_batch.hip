@@ -429,7 +429,8 @@ typedef uint32_t u32x4a __attribute__((ext_vector_type(4)));   // 16-byte aligne
 // sit Lp bytes apart in LDS, an odd number of granules, so the 16 lanes that
 // read one offset of 16 rows hit distinct banks; a tile takes NI copy
 // instructions, the lanes past the 16 rows left out of the last one, so a
-// tile takes exactly 16 Lp bytes.  Where every step starts 16-byte aligned
+// tile takes exactly 16 Lp bytes, and the lanes of a row's padding granule
+// (Lp > Lc) copy nothing.  Where every step starts 16-byte aligned
 // (kAligned) a row is just the L bytes of the step.
 // Launch forms of the main kernel: 0 = per-wave records (from the record
 // kernel), 1 = shared records formed in LDS, eight waves (two per SIMD) and
@@ -488,7 +489,9 @@ struct Geo {
     static_assert(NW % 4 == 0 && NW <= 16 && (S == 2 || S == 3), "launch form");
     static constexpr int L = F::kStepBytes;
     static constexpr bool AL = AlignedOf<F>::value;              // every step starts 16-byte aligned
-    static constexpr int Lc = AL ? L : (L + 15 + 15) / 16 * 16;
+    // granules that cover a step: blocks are 2-byte aligned, so a step
+    // starts at most 14 bytes into its first granule
+    static constexpr int Lc = AL ? L : (L + 14 + 15) / 16 * 16;
     static constexpr int Lp = ((Lc / 16) & 1) ? Lc : Lc + 16;
     static constexpr int NI = (16 * Lp + 1023) / 1024;           // copy instructions per tile
     static constexpr int TB = 16 * Lp;                           // LDS bytes of one tile
@@ -772,10 +775,12 @@ __global__ void __launch_bounds__((64 * Geo<F, FORM>::NW), 1) bgemm(const uint8_
         // span at most 32 rows): the copy of step s starts at
         // (crel + s L) & ~15 (base_rel and w are multiples of 16).
         uint32_t crel[T][G::NI];
+        bool cok[G::NI];                                  // a granule of the step, not padding
 #pragma unroll
         for (int i = 0; i < G::NI; ++i) {
             const int P = 1024 * i + 16 * lane, q = min(P / G::Lp, 15);
             const int w = P - q * G::Lp;
+            cok[i] = w < G::Lc;
 #pragma unroll
             for (int u = 0; u < T; ++u) crel[u][i] = uint32_t(min(T0c + 16 * u + q, last) * row_bytes - base_rel) + uint32_t(w);
         }
@@ -787,7 +792,7 @@ __global__ void __launch_bounds__((64 * Geo<F, FORM>::NW), 1) bgemm(const uint8_
                 const uint32_t dst = lds_addr(ring + (b * T + u) * G::TB);
 #pragma unroll
                 for (int i = 0; i < G::NI; ++i)
-                    if (i + 1 < G::NI || lane < G::LAST)
+                    if (G::Lc == G::Lp ? (i + 1 < G::NI || lane < G::LAST) : cok[i])
                         dma<16>(wbase, min((crel[u][i] + sL) & ~15u, lim), dst + 1024 * i);
             }
         };
