@@ -217,7 +217,9 @@ struct BQ4K {
         const f4 cm = mfma(xm, pack(__builtin_amdgcn_perm(0u, mw, 0x0c010c00u), __builtin_amdgcn_perm(0u, mw, 0x0c030c02u)),
                            f4{0.f, 0.f, 0.f, 0.f});
         const float d = h2f(r.h.x) * 16777216.f, dmin = h2f(r.h.x >> 16) * 16777216.f;
-        acc += d * (lo + 0.0625f * hi) - dmin * cm;
+        // as two multiply-adds onto acc (acc - dmin cm first): a separate
+        // "acc +" would cost an add per output even with acc = 0
+        acc = d * (lo + 0.0625f * hi) + (acc - dmin * cm);
     }
 };
 
@@ -339,7 +341,7 @@ struct BQ5K {
         const h4 mb = {_Float16(float(m0)), _Float16(float(m1)), _Float16(float(m2)), _Float16(float(m3))};
         const f4 cm = mfma(xm, mb, f4{0.f, 0.f, 0.f, 0.f});
         const float d = h2f(r.h.x) * 16384.f, dmin = h2f(r.h.x >> 16);
-        acc += d * c - dmin * cm;
+        acc = d * c + (acc - dmin * cm);   // two multiply-adds onto acc
     }
 };
 
