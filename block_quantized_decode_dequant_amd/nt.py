@@ -205,7 +205,10 @@ def nt_gemm_batch_workspace_bytes(qtype: int, rows: int, cols: int) -> int:
 
 def nt_gemm_batch(qtype: int, W, X, Y, rows: int, cols: int, k: int, workspace, accumulate: bool = False,
                   stream=None):
-    """Y[n] (+)= W . X[n] for n < k (X: k x cols, Y: k x rows, fp32, back to back)."""
+    """Y[n] (+)= W . X[n] for n < k (X: k x cols, Y: k x rows, fp32, back to back).
+    workspace: at least nt_gemm_batch_workspace_bytes(qtype, rows, cols) bytes
+    on the device whose first 16384 bytes (the split counters) are zero
+    before its first use, e.g. torch.zeros; every call leaves them zero."""
     rb = row_bytes(qtype, cols)
     need_w = rows * rb if rb > 0 else 0
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
