@@ -106,7 +106,8 @@ def test_gemm_batch_launch_shapes(t, rows, cols, k):
 def test_gemm_batch_tall_and_wide_matrices():
     # 40040 rows of 2048 columns (ragged last workgroup, with a partial
     # 16-row tile; more workgroups than CUs; the K-quants take the
-    # sixteen-wave shared-record form, split three ways), and 600 rows of
+    # sixteen-wave shared-record form, Q5_K and Q6_K split three ways between
+    # workgroups), and 600 rows of
     # 8960 columns (35 steps split between workgroups: partial sums added by
     # the last wave of each row set)
     _case(O.Q4_K, 40040, 2048, 8, seed=31)
@@ -191,6 +192,53 @@ def test_gemm_batch_one_workspace_many_calls():
             for n in range(k):
                 assert_close(got[n], ref[n], what=f"gemm_batch {TID[TYPES.index(t)]} {rows}x{cols} call {rep} vector {n}")
             assert torch.count_nonzero(ws[:16384]).item() == 0, "split counters not back at zero"
+
+
+def test_gemm_batch_graph_replays():
+    """Calls captured in a HIP graph and replayed three times, with eager
+    calls on the same workspace in between: every replay matches the oracle
+    (the split counters reset themselves, so a replay finds them at zero).
+    Shapes: Q6_K 300 x 8192 (records in LDS, 32 splits), Q8_0 3 x 65536
+    (records from the first kernel, splits inside and between workgroups)
+    and Q6_K 40040 x 2048 (sixteen waves, three splits)."""
+    dev = device()
+    cases = [(O.Q6_K, 300, 8192, 5), (O.Q8_0, 3, 65536, 4), (O.Q6_K, 40040, 2048, 3)]
+    nws = max(nt.nt_gemm_batch_workspace_bytes(t, r, c) for t, r, c, _ in cases)
+    ws = torch.zeros(nws, dtype=torch.uint8, device=dev)
+    data = []
+    for i, (t, rows, cols, k) in enumerate(cases):
+        W = O.quantize(t, synth.normal_f32(i, 800 + t, rows * cols, std=0.02))
+        X = np.stack([synth.normal_f32(i, 810 + n, cols) for n in range(k)])
+        Y = torch.full((k * rows,), GUARD, dtype=torch.float32, device=dev)
+        data.append((t, rows, cols, k, to_dev(W), to_dev(X.reshape(-1)), Y, O.gemm_batch(t, W, rows, cols, X)))
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        for t, rows, cols, k, dw, dx, Y, _ in data:        # first use outside capture
+            nt.nt_gemm_batch(t, dw, dx, Y, rows, cols, k, ws)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for t, rows, cols, k, dw, dx, Y, _ in data:
+                nt.nt_gemm_batch(t, dw, dx, Y, rows, cols, k, ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        with torch.cuda.stream(side):
+            for _, _, _, _, _, _, Y, _ in data:
+                Y.fill_(GUARD)
+            g.replay()
+        torch.cuda.synchronize()
+        for t, rows, cols, k, dw, dx, Y, ref in data:
+            got = host(Y).reshape(k, rows)
+            for n in range(k):
+                assert_close(got[n], ref[n], what=f"gemm_batch {TID[TYPES.index(t)]} {rows}x{cols} replay {rep} vector {n}")
+        assert torch.count_nonzero(ws[:16384]).item() == 0, "split counters not back at zero"
+        t, rows, cols, k, dw, dx, Y, ref = data[rep % len(data)]
+        Y2 = torch.empty_like(Y)
+        nt.nt_gemm_batch(t, dw, dx, Y2, rows, cols, k, ws)   # eager call between replays
+        torch.cuda.synchronize()
+        got = host(Y2).reshape(k, rows)
+        for n in range(k):
+            assert_close(got[n], ref[n], what=f"gemm_batch {TID[TYPES.index(t)]} {rows}x{cols} eager {rep} vector {n}")
+    del g
 
 
 def test_gemm_batch_rejects_bad_arguments():
