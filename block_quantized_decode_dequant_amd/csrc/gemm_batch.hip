@@ -585,21 +585,16 @@ __global__ void __launch_bounds__(256) bgemm_prep(const float *__restrict__ X, i
     }
 }
 
-__device__ __forceinline__ void wait_vm(int n) {
-    switch (n) {
-    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4)); break;
-    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5)); break;
-    case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6)); break;
-    case 7: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7)); break;
-    case 8: __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); break;
-    case 10: __builtin_amdgcn_s_waitcnt(vmcnt_imm(10)); break;
-    case 13: __builtin_amdgcn_s_waitcnt(vmcnt_imm(13)); break;
-    case 14: __builtin_amdgcn_s_waitcnt(vmcnt_imm(14)); break;
-    case 15: __builtin_amdgcn_s_waitcnt(vmcnt_imm(15)); break;
-    case 16: __builtin_amdgcn_s_waitcnt(vmcnt_imm(16)); break;
-    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;   // n = 0 (other counts do not occur)
-    }
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N <= 63, "vmcnt holds 0..63");
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
     __builtin_amdgcn_sched_barrier(0);
+}
+// wait until at most N (when more) or no vector-memory operations are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm_or_all(bool more) {
+    if (more) wait_vm<N>(); else wait_vm<0>();
 }
 
 // Step counters of the shared record ring, in LDS: plain workgroup-scope
@@ -872,7 +867,7 @@ __global__ void __launch_bounds__((64 * Geo<F, FORM>::NW), 1) bgemm(const uint8_
             if (mine(kAhead - 1)) issue_x(kAhead - 1);
             if (kWA > 1 && n > 1) issue_w(1, s_lo + 1);
             if (wv < kReport && wv < n) {
-                wait_vm(kWA > 1 && n > 1 ? 2 * kW : kW);        // this wave's activations for record wv
+                if (kWA > 1 && n > 1) wait_vm<2 * kW>(); else wait_vm<kW>();   // this wave's activations for record wv
                 form(wv);
             }
             // the waves of a SIMD (w, w + 4, ...) take turns at the higher issue
@@ -887,7 +882,7 @@ __global__ void __launch_bounds__((64 * Geo<F, FORM>::NW), 1) bgemm(const uint8_
                 // both counters this step waits on, read before the weight wait
                 const uint32_t arrived0 = lds_read_count(&cnt[b]);
                 const uint32_t done0 = lds_read_count(&cnt[G::R + jn % G::R]);
-                wait_vm(t + 1 < n ? (kWA - 1) * kW : 0);          // weights t, activations t + KA - 1 landed
+                wait_vm_or_all<(kWA - 1) * kW>(t + 1 < n);       // weights t, activations t + KA - 1 landed
                 if (mine(t + kReport)) form(t + kReport);
                 lds_wait_count(&cnt[b], kAll * uint32_t(t / G::R + 1), arrived0);
                 const uint8_t *const rc = slot(t);
@@ -915,7 +910,7 @@ __global__ void __launch_bounds__((64 * Geo<F, FORM>::NW), 1) bgemm(const uint8_
         constexpr int kX = 9 + (F::kMin ? 1 : 0);
         XRegs x0, x1, x2;
         const auto step = [&](int t, const XRegs &cur, XRegs &ahead) {
-            wait_vm(t + 1 < n ? kX + kW : 0);
+            wait_vm_or_all<kX + kW>(t + 1 < n);
             if (t + 2 < n) {
                 load_x<F>(rec, s_lo + t + 2, lane, g, ahead);
                 issue_w((t + 2) % G::S, s_lo + t + 2);
