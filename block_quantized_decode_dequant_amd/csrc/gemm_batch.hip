@@ -1040,7 +1040,11 @@ struct BgemmShape {
 // 49.8 us, and lost at 8192 x 8192, where it needs eight splits).
 template <class F>
 BgemmShape bgemm_shape(int64_t rows, int64_t cols) {
-    constexpr int kReduceCost = 20;   // the cross-workgroup sum: about one one-tile step of one wave
+    // the cross-workgroup sum: about one one-tile step of one wave, plus a
+    // fifth of a step per split, for the tickets the splits of a row set take
+    // one after another on the same counter (measured at k = 8: 1024 x 8192
+    // split 32 ways 17.5 us, 16 ways 12.4, 8 ways 10.9, on 64 CUs)
+    constexpr int kReduceCost = 20;
     constexpr int kRecordCost = 40;   // the record kernel of the per-wave-record forms: about two steps
     BgemmShape b{};
     int64_t best = -1;
@@ -1063,7 +1067,7 @@ BgemmShape bgemm_shape(int64_t rows, int64_t cols) {
                 // (the wide form's covers twice the rows per workgroup, and its
                 // start costs one step more)
                 const int64_t cost = int64_t(step_cost) * G::T * rounds * (sps + G::S - 1) +
-                                     (sp > 1 ? kReduceCost : 0) + (form == kWide ? 20 : 0) +
+                                     (sp > 1 ? kReduceCost + 4 * sp : 0) + (form == kWide ? 20 : 0) +
                                      (shared ? 0 : G::T * rounds * sps * (nc - 1) + kRecordCost);
                 if (best < 0 || cost < best) {
                     best = cost;

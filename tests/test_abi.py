@@ -103,9 +103,9 @@ def test_gemm_batch_argument_errors():
                 break
         else:
             raise AssertionError((t, rows, cols, extra))
-    assert wsb(nt.Q8_0, 4096, 4096) == C + 8 * 8 * 4096 * 4   # records in LDS, eight-way split
+    assert wsb(nt.Q8_0, 4096, 4096) == C + 16 * 8224             # records from the first kernel, no split
     assert wsb(nt.Q4_K, 28672, 8192) == C + 2 * 8 * 28672 * 4   # records in LDS, two-way split
-    assert wsb(nt.Q4_K, 1500, 5888) == C + 12 * 8 * 1500 * 4    # records in LDS, twelve-way split
+    assert wsb(nt.Q4_K, 1500, 5888) == C + 8 * 8 * 1500 * 4     # records in LDS, eight-way split
     assert wsb(nt.Q4_K, 3, 65536) > C + 3 * 8 * 4 * 2   # a few rows: split between workgroups
     assert wsb(nt.F32, 4, 256) == 0 and wsb(nt.Q4_K, 4, 100) == 0 and wsb(nt.Q4_K, 4, 65536 + 256) == 0
     assert wsb(nt.Q4_K, -1, 256) == 0
