@@ -742,6 +742,10 @@ __global__ void __launch_bounds__((64 * Geo<F, FORM>::NW), 1) bgemm(const uint8_
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, kept in a scalar register
+    // every argument in a scalar register before any other work: their
+    // loads then go out in one round trip instead of two or three
+    asm volatile("" :: "s"(W), "s"(row_bytes), "s"(rows), "s"(nsteps), "s"(nblk), "s"(rec), "s"(nc), "s"(sps),
+                 "s"(Y), "s"(k), "s"(accumulate), "s"(partial), "s"(tickets), "s"(X), "s"(cols));
     const int wc = wv % nc, nr = G::NW / nc;
     const int s_lo = (blockIdx.y * nc + wc) * sps, n = max(0, min(sps, nsteps - s_lo));
     const int64_t T0 = (int64_t(blockIdx.x) * nr + wv / nc) * 16 * T;  // first row of this wave's tiles

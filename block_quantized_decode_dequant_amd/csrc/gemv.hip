@@ -805,6 +805,10 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, const int b, const 
     // nw waves per row (one per 4096 columns); row groups only with the
     // shared area; wave = grp * nw + cw
     const int nwv = blockDim.x >> 6;
+    // the launch dimensions come from the same argument block as the rest:
+    // asking for them here makes every argument load go out in one round
+    // trip (left alone, the compiler issues these two after the first wait)
+    asm volatile("" :: "s"(nwv), "s"(G));
     const int nw = SHARED ? (a.units + 63) >> 6 : nwv;
     int cw = wave, grp = 0, R = 1;                  // column slice, row group, groups
     if constexpr (SHARED) {
