@@ -418,6 +418,15 @@ __global__ void __launch_bounds__(1024) gemv_generic(const uint8_t *__restrict__
 
 constexpr int kMaxRowsPerWG = 256;           // rows one workgroup reduces (LDS row sums)
 
+// m = ceil(2^16 / d) for 1 <= d <= 8 (d uniform: a scalar select chain in
+// place of a division).  (n * m) >> 16 equals n / d for 0 <= n < 8192: the
+// excess n (m - 2^16 / d) / 2^16 stays below 1/8 <= 1/d, and the fraction of
+// n / d is at most 1 - 1/d
+__device__ __forceinline__ uint32_t small_inv(int d) {
+    return d <= 4 ? (d <= 2 ? (d == 1 ? 65536u : 32768u) : (d == 3 ? 21846u : 16384u))
+                  : (d <= 6 ? (d == 5 ? 13108u : 10923u) : (d == 7 ? 9363u : 8192u));
+}
+
 // Nibble products without a bias term: a 4-bit code in bits 0..3 of an fp16
 // half is the subnormal q * 2^-24, in bits 4..7 the subnormal q * 2^-20, both
 // exact, and v_fma_mix_f32 widens them to fp32 exactly (fp16 denormals are
@@ -805,15 +814,23 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, const int b, const 
     // nw waves per row (one per 4096 columns); row groups only with the
     // shared area; wave = grp * nw + cw
     const int nwv = blockDim.x >> 6;
-    // the launch dimensions come from the same argument block as the rest:
-    // asking for them here makes every argument load go out in one round
-    // trip (left alone, the compiler issues these two after the first wait)
-    asm volatile("" :: "s"(nwv), "s"(G));
+    // every argument (and the launch dimensions, read from the same block)
+    // asked for here, so that all their loads go out in one round trip (left
+    // alone, the compiler issues some after a first wait, where it needs them)
+    asm volatile("" :: "s"(nwv), "s"(G), "s"(a.W[0]), "s"(a.W[1]), "s"(a.W[2]), "s"(a.y[0]), "s"(a.y[1]), "s"(a.y[2]),
+                 "s"(a.seg_end[0]), "s"(a.seg_end[1]), "s"(a.seg_lim[0]), "s"(a.seg_lim[1]), "s"(a.seg_lim[2]),
+                 "s"(a.x), "s"(a.gain), "s"(a.cols), "s"(a.rows), "s"(a.units), "s"(a.row_bytes), "s"(a.accumulate),
+                 "s"(a.swiglu));
     const int nw = SHARED ? (a.units + 63) >> 6 : nwv;
     int cw = wave, grp = 0, R = 1;                  // column slice, row group, groups
+    uint32_t inv_r = 65536u;                        // small_inv(R)
     if constexpr (SHARED) {
-        while (cw >= nw) { cw -= nw; ++grp; }       // at most 7 steps, scalar
-        for (int w = 2 * nw; w <= nwv; w += nw) ++R;
+        // a workgroup holds at most 8 waves, so nw <= 8 and R <= 8
+        const uint32_t inv_nw = small_inv(nw);
+        grp = int((uint32_t(wave) * inv_nw) >> 16);
+        cw = wave - grp * nw;
+        R = int((uint32_t(nwv) * inv_nw) >> 16);
+        inv_r = small_inv(R);
     }
     // LDS: [SHARED: activations nw x 16 KB, gains nw x 16 KB] rings, row sums, norm partials
     uint8_t *const xa = smem;
@@ -832,7 +849,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, const int b, const 
     const bool pairs = a.swiglu != 0;
     const int items = pairs ? a.rows / 2 : a.rows;
     const int nitems = (items - b + G - 1) / G;      // items of this workgroup
-    const int mine = SHARED ? (nitems > grp ? (nitems - grp + R - 1) / R : 0) : nitems;
+    const int mine = SHARED ? (nitems > grp ? int((uint32_t(nitems - grp + R - 1) * inv_r) >> 16) : 0) : nitems;
     const int n = pairs ? 2 * mine : mine;           // rows of this wave, in ring order
 
     const int u = cw * 64 + lane;
@@ -967,7 +984,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, const int b, const 
     if (pairs) {
         float *h = a.y[0];
         for (int t = threadIdx.x; t < nitems; t += blockDim.x) {
-            const int g = t % R, jj = t / R;
+            const int jj = int((uint32_t(t) * inv_r) >> 16), g = t - jj * R;
             const float *pp = part + g * nw * kMaxRowsPerWG + 2 * jj;
             float gs = 0.f, up = 0.f;
             for (int w = 0; w < nw; ++w) {
@@ -978,7 +995,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, const int b, const 
         }
     } else {
         for (int t = threadIdx.x; t < nitems; t += blockDim.x) {
-            const int g = t % R, jj = t / R;
+            const int jj = int((uint32_t(t) * inv_r) >> 16), g = t - jj * R;
             const float *pp = part + g * nw * kMaxRowsPerWG + jj;
             float sum = 0.f;
             for (int w = 0; w < nw; ++w) sum += pp[w * kMaxRowsPerWG];
