@@ -49,6 +49,16 @@ struct GemvArgs {
     uint32_t row_bytes;
     int accumulate;
     int swiglu;
+    // per launch, set where the grid is chosen (integer division is a long
+    // instruction chain on the device): workgroup b of G takes items_q items,
+    // plus one if b < items_r; SHARED layout: `groups` row groups of nw waves,
+    // inv_nw = ceil(2^16 / nw), inv_groups = ceil(2^16 / groups), so that
+    // (n * inv) >> 16 = n / d for the small counts n the kernel divides
+    int items_q;
+    int items_r;
+    int groups;
+    uint32_t inv_nw;
+    uint32_t inv_groups;
 };
 
 GemvArgs gemv_args(nt_qtype t, int nseg, const void *const *W, const int64_t *rows, float *const *y, int64_t cols,
@@ -418,14 +428,6 @@ __global__ void __launch_bounds__(1024) gemv_generic(const uint8_t *__restrict__
 
 constexpr int kMaxRowsPerWG = 256;           // rows one workgroup reduces (LDS row sums)
 
-// m = ceil(2^16 / d) for 1 <= d <= 8 (d uniform: a scalar select chain in
-// place of a division).  (n * m) >> 16 equals n / d for 0 <= n < 8192: the
-// excess n (m - 2^16 / d) / 2^16 stays below 1/8 <= 1/d, and the fraction of
-// n / d is at most 1 - 1/d
-__device__ __forceinline__ uint32_t small_inv(int d) {
-    return d <= 4 ? (d <= 2 ? (d == 1 ? 65536u : 32768u) : (d == 3 ? 21846u : 16384u))
-                  : (d <= 6 ? (d == 5 ? 13108u : 10923u) : (d == 7 ? 9363u : 8192u));
-}
 
 // Nibble products without a bias term: a 4-bit code in bits 0..3 of an fp16
 // half is the subnormal q * 2^-24, in bits 4..7 the subnormal q * 2^-20, both
@@ -820,17 +822,15 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, const int b, const 
     asm volatile("" :: "s"(nwv), "s"(G), "s"(a.W[0]), "s"(a.W[1]), "s"(a.W[2]), "s"(a.y[0]), "s"(a.y[1]), "s"(a.y[2]),
                  "s"(a.seg_end[0]), "s"(a.seg_end[1]), "s"(a.seg_lim[0]), "s"(a.seg_lim[1]), "s"(a.seg_lim[2]),
                  "s"(a.x), "s"(a.gain), "s"(a.cols), "s"(a.rows), "s"(a.units), "s"(a.row_bytes), "s"(a.accumulate),
-                 "s"(a.swiglu));
+                 "s"(a.swiglu), "s"(a.items_q), "s"(a.items_r), "s"(a.groups), "s"(a.inv_nw), "s"(a.inv_groups));
     const int nw = SHARED ? (a.units + 63) >> 6 : nwv;
     int cw = wave, grp = 0, R = 1;                  // column slice, row group, groups
-    uint32_t inv_r = 65536u;                        // small_inv(R)
+    uint32_t inv_r = 65536u;                        // ceil(2^16 / R)
     if constexpr (SHARED) {
-        // a workgroup holds at most 8 waves, so nw <= 8 and R <= 8
-        const uint32_t inv_nw = small_inv(nw);
-        grp = int((uint32_t(wave) * inv_nw) >> 16);
+        grp = int((uint32_t(wave) * a.inv_nw) >> 16);
         cw = wave - grp * nw;
-        R = int((uint32_t(nwv) * inv_nw) >> 16);
-        inv_r = small_inv(R);
+        R = a.groups;
+        inv_r = a.inv_groups;
     }
     // LDS: [SHARED: activations nw x 16 KB, gains nw x 16 KB] rings, row sums, norm partials
     uint8_t *const xa = smem;
@@ -847,8 +847,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, const int b, const 
     // stream one band of neighbouring rows; row group g takes the workgroup's
     // items g, g + R, g + 2R, ...
     const bool pairs = a.swiglu != 0;
-    const int items = pairs ? a.rows / 2 : a.rows;
-    const int nitems = (items - b + G - 1) / G;      // items of this workgroup
+    const int nitems = a.items_q + (b < a.items_r ? 1 : 0);   // items of this workgroup: b, b + G, ...
     const int mine = SHARED ? (nitems > grp ? int((uint32_t(nitems - grp + R - 1) * inv_r) >> 16) : 0) : nitems;
     const int n = pairs ? 2 * mine : mine;           // rows of this wave, in ring order
 
@@ -1154,8 +1153,28 @@ LdsShape lds_shape(int64_t items, int64_t cols, bool pairs, bool norm, bool vec1
     return s;
 }
 
+// ceil(2^16 / d), 1 <= d <= 8: (n * m) >> 16 equals n / d for 0 <= n < 8192
+// (the excess n (m - 2^16 / d) / 2^16 stays below 1/8 <= 1/d, and the
+// fraction of n / d is at most 1 - 1/d); every count divided this way (a
+// wave index, the waves of a workgroup, items per workgroup plus a group
+// index) is below 2^11
+uint32_t small_inv(int d) { return (65535u + uint32_t(d)) / uint32_t(d); }
+
+// The launch constants of one GEMV (or one side of a paired launch) over
+// `grid` workgroups of `groups` row groups of nw waves.
+GemvArgs with_launch(GemvArgs a, int64_t grid, int nw, int groups) {
+    const int64_t items = a.swiglu ? a.rows / 2 : a.rows;
+    a.items_q = int(items / grid);
+    a.items_r = int(items % grid);
+    a.groups = groups;
+    a.inv_nw = nw <= 8 ? small_inv(nw) : 0u;       // used by the shared layout only (nw <= 8 there)
+    a.inv_groups = small_inv(groups);
+    return a;
+}
+
 template <class Tr, int VEC, bool NORM, bool SHARED>
-hipError_t launch_lds_inst(const GemvArgs &a, const LdsShape &s, hipStream_t st) {
+hipError_t launch_lds_inst(const GemvArgs &a0, const LdsShape &s, hipStream_t st) {
+    const GemvArgs a = with_launch(a0, s.grid, s.nw, SHARED ? s.groups : 1);
     // allow the large dynamic LDS areas (a launch that still exceeds the
     // limit fails and is reported by the launch check below)
     static std::atomic<uint64_t> done{0};          // devices this kernel is set up on
@@ -1214,7 +1233,8 @@ hipError_t launch_pair_inst(const GemvArgs &a, const GemvArgs &c, hipStream_t st
     if (gc < 1) gc = 1;
     static std::atomic<uint64_t> done{0};
     allow_full_lds(reinterpret_cast<const void *>(&gemv_pair<TrA, TrB, true>), done);
-    gemv_pair<TrA, TrB, true><<<dim3(unsigned(ga + gc)), dim3(unsigned(64 * nw * groups)), lds, st>>>(a, c, int(ga));
+    gemv_pair<TrA, TrB, true><<<dim3(unsigned(ga + gc)), dim3(unsigned(64 * nw * groups)), lds, st>>>(
+        with_launch(a, ga, nw, groups), with_launch(c, gc, nw, groups), int(ga));
     return hipGetLastError();
     }
 }
